@@ -1,0 +1,272 @@
+"""Plain float64 reference for fused causal grouped-query attention and paged decode.
+
+TEST INFRASTRUCTURE ONLY.  This module is the oracle that the HIP library is
+checked against.  Only the tests, the package smoke check and the benchmark's
+CPU-baseline leg may import it; the library and its binding never do.  It
+shares no code with the GPU path.
+
+What it computes is the unfused ("MATH") attention that the pages describe as
+the fallback that materialises the full S x S score matrix (page "Gemma4 FFPA
+attention backend support for accelerating Gemma4-family training", operator
+table and section Debugging notes; page "Root cause analysis: Gemma4
+sliding-window BF16 cuDNN SDPA NaN on H100", operator table under "Why cuDNN
+SDPA is the affected path"), carried out in float64 as the global FP32 upcast
+of the second page suggests (section Summary, "Proposed fix"), one
+(batch, head) unit at a time with explicit matrix products, exp, max and sum.
+No attention routine of any library is called.
+
+Readings adopted where the pages are silent (each is listed in the design notes):
+* grouped-query heads follow the repeat-KV path of the first page (Debugging
+  notes): query head h reads key/value head h // (Hq // Hkv);
+* a 2D bool padding mask selects the variable-length path (first page,
+  Integration): row b holds len_b valid tokens as a prefix; padded queries do
+  not exist and padded keys are invisible;
+* the sliding window admits key j for query i when i - W < j <= i;
+* a query row with no visible key returns O = 0 and LSE = 0 rather than NaN
+  (fourth page, "What broke correctness and had to be dropped": rows whose
+  mask is all False must stay safe);
+* LSE is the natural-log log-sum-exp of the scaled scores of the visible keys;
+* the paged decode query sits at position ctx_b - 1 and sees every cached
+  token t < ctx_b (fourth page, Architecture notes: PagedKVCache + PageTable).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "visibility", "lengths_from_pad_mask", "lengths_from_cu_seqlens",
+    "unit_forward", "unit_backward", "attention_forward", "attention_backward",
+    "attention_forward_head", "attention_backward_group",
+    "attention_forward_packed", "attention_backward_packed",
+    "gather_pages", "paged_decode", "paged_decode_one",
+]
+
+
+# ---------------------------------------------------------------------------
+# Which keys a query sees
+# ---------------------------------------------------------------------------
+def visibility(n: int, causal: bool, window: int) -> np.ndarray:
+    """(n, n) bool over the valid prefix of one sequence: entry (i, j) is True when query i sees key j.
+
+    Causal keeps j <= i; a window W > 0 keeps j > i - W.  Positions at or past
+    the sequence's length are not part of the block at all: padded queries do
+    not exist and padded keys are invisible.
+    """
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    vis = np.ones((n, n), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window > 0:
+        vis &= j > i - window
+    return vis
+
+
+def lengths_from_pad_mask(mask: np.ndarray) -> np.ndarray:
+    """(B, S) bool/uint8 right-padded mask -> (B,) valid lengths; rejects a mask that is not a prefix."""
+    mask = np.asarray(mask).astype(bool)
+    lengths = mask.sum(axis=1)
+    S = mask.shape[1]
+    expect = np.arange(S)[None, :] < lengths[:, None]
+    if not np.array_equal(mask, expect):
+        raise ValueError("padding mask is not a right-padded prefix mask")
+    return lengths.astype(np.int64)
+
+
+def lengths_from_cu_seqlens(cu: np.ndarray) -> np.ndarray:
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu[0] != 0 or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0 and be non-decreasing")
+    return np.diff(cu)
+
+
+# ---------------------------------------------------------------------------
+# One (batch, head) unit
+# ---------------------------------------------------------------------------
+def unit_forward(q, k, v, scale, vis):
+    """One head: q (n, D), k (n, D), v (n, D) float64 and vis (n, n).
+
+    Returns O (n, D), LSE (n,) and the probabilities P (n, n).  Every key row
+    passed in must be finite: invisible keys get probability exactly 0, which
+    removes a finite value but not a NaN.
+    S = scale * q k^T with invisible entries at -inf; P = row softmax of S;
+    O = P v; LSE = rowmax + ln(sum exp(S - rowmax)).
+    """
+    s = scale * (q @ k.T)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    live = np.isfinite(m)
+    m0 = np.where(live, m, 0.0)
+    e = np.exp(s - m0[:, None])          # exp(-inf) = 0 on invisible entries
+    l = e.sum(axis=1)
+    l_safe = np.where(live, l, 1.0)
+    p = e / l_safe[:, None]
+    o = p @ v
+    lse = np.where(live, m0 + np.log(l_safe), 0.0)
+    return o, lse, p
+
+
+def unit_backward(q, k, v, do, scale, vis):
+    """Gradients of sum(O * dO) for one head; returns dQ, dK, dV (this head's share of dK, dV).
+
+    dP = dO v^T; delta_i = sum_j P_ij dP_ij; dS = P * (dP - delta); dQ = scale dS k;
+    dK = scale dS^T q; dV = P^T dO.
+    """
+    o, _, p = unit_forward(q, k, v, scale, vis)
+    dp = do @ v.T
+    delta = (p * dp).sum(axis=1)
+    ds = p * (dp - delta[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    dv = p.T @ do
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Batched layouts: q, o, dO (B, S, Hq, D); k, v (B, S, Hkv, D); LSE (B, Hq, S)
+# ---------------------------------------------------------------------------
+def _lengths(B, S, lengths):
+    if lengths is None:
+        return np.full(B, S, dtype=np.int64)
+    return np.asarray(lengths, dtype=np.int64)
+
+
+def attention_forward_head(q, k, v, b, h, scale, causal=True, window=0, lengths=None):
+    """O (S, D) and LSE (S,) of one (batch, query-head) unit; rows at or past the length are 0."""
+    B, S, Hq, D = q.shape
+    r = Hq // k.shape[2]
+    n = int(_lengths(B, S, lengths)[b])
+    o = np.zeros((S, D))
+    lse = np.zeros(S)
+    if n > 0:
+        o[:n], lse[:n], _ = unit_forward(q[b, :n, h], k[b, :n, h // r], v[b, :n, h // r], scale,
+                                         visibility(n, causal, window))
+    return o, lse
+
+
+def attention_forward(q, k, v, scale, causal=True, window=0, lengths=None):
+    """Returns O (B, S, Hq, D) float64 and LSE (B, Hq, S) float64."""
+    B, S, Hq, D = q.shape
+    o = np.zeros((B, S, Hq, D))
+    lse = np.zeros((B, Hq, S))
+    for b in range(B):
+        for h in range(Hq):
+            o[b, :, h], lse[b, h] = attention_forward_head(q, k, v, b, h, scale, causal, window, lengths)
+    return o, lse
+
+
+def attention_backward_group(q, k, v, do, b, g, scale, causal=True, window=0, lengths=None):
+    """dQ (S, r, D) for the r query heads of kv-head g, and dK, dV (S, D) summed over them.
+
+    Rows of dQ and keys of dK, dV at or past the sequence length are 0.
+    """
+    B, S, Hq, D = q.shape
+    r = Hq // k.shape[2]
+    n = int(_lengths(B, S, lengths)[b])
+    dq = np.zeros((S, r, D))
+    dk = np.zeros((S, D))
+    dv = np.zeros((S, D))
+    if n == 0:
+        return dq, dk, dv
+    vis = visibility(n, causal, window)
+    for i in range(r):                   # fixed head order
+        h = g * r + i
+        dqh, dkh, dvh = unit_backward(q[b, :n, h], k[b, :n, g], v[b, :n, g], do[b, :n, h], scale, vis)
+        dq[:n, i] = dqh
+        dk[:n] += dkh
+        dv[:n] += dvh
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, scale, causal=True, window=0, lengths=None):
+    """Returns dQ (B, S, Hq, D), dK and dV (B, S, Hkv, D), float64."""
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    r = Hq // Hkv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for g in range(Hkv):
+            gq, gk, gv = attention_backward_group(q, k, v, do, b, g, scale, causal, window, lengths)
+            dq[b, :, g * r:(g + 1) * r] = gq
+            dk[b, :, g] = gk
+            dv[b, :, g] = gv
+    return dq, dk, dv
+
+
+# Packed rows (cu_seqlens): q, o, dO (T, Hq, D); k, v (T, Hkv, D); LSE (Hq, T).
+def attention_forward_packed(q, k, v, cu_seqlens, scale, causal=True, window=0):
+    lengths = lengths_from_cu_seqlens(cu_seqlens)
+    T, Hq, D = q.shape
+    r = Hq // k.shape[1]
+    o = np.zeros(q.shape)
+    lse = np.zeros((Hq, T))
+    for b, n in enumerate(lengths):
+        s0 = int(cu_seqlens[b])
+        n = int(n)
+        if n == 0:
+            continue
+        vis = visibility(n, causal, window)
+        for h in range(Hq):
+            o[s0:s0 + n, h], lse[h, s0:s0 + n], _ = unit_forward(
+                q[s0:s0 + n, h], k[s0:s0 + n, h // r], v[s0:s0 + n, h // r], scale, vis)
+    return o, lse
+
+
+def attention_backward_packed(q, k, v, do, cu_seqlens, scale, causal=True, window=0):
+    lengths = lengths_from_cu_seqlens(cu_seqlens)
+    T, Hq, D = q.shape
+    r = Hq // k.shape[1]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b, n in enumerate(lengths):
+        s0 = int(cu_seqlens[b])
+        n = int(n)
+        if n == 0:
+            continue
+        vis = visibility(n, causal, window)
+        for h in range(Hq):
+            g = h // r
+            a, bk, bv = unit_backward(q[s0:s0 + n, h], k[s0:s0 + n, g], v[s0:s0 + n, g],
+                                      do[s0:s0 + n, h], scale, vis)
+            dq[s0:s0 + n, h] = a
+            dk[s0:s0 + n, g] += bk
+            dv[s0:s0 + n, g] += bv
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Paged decode: q (B, Hq, D); caches (num_pages, page_size, Hkv, D); table (B, max_pages)
+# ---------------------------------------------------------------------------
+def gather_pages(cache, table_row, ctx, page_size):
+    """Logical tokens 0..ctx-1 of one sequence, (ctx, Hkv, D): token t lives in page
+    table_row[t // page_size] at slot t % page_size."""
+    t = np.arange(int(ctx))
+    return cache[np.asarray(table_row)[t // page_size], t % page_size]
+
+
+def paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_size=16):
+    """O (Hq, D) for one sequence's single query token, placed at position ctx_b - 1."""
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k_cache.shape[2]
+    r = Hq // Hkv
+    ctx = int(ctx_lens[b])
+    out = np.zeros((Hq, D))
+    if ctx == 0:
+        return out
+    kk = gather_pages(k_cache, block_table[b], ctx, page_size)
+    vv = gather_pages(v_cache, block_table[b], ctx, page_size)
+    vis = np.ones((1, ctx), dtype=bool)
+    for h in range(Hq):
+        o, _, _ = unit_forward(q[b, h][None, :], kk[:, h // r], vv[:, h // r], scale, vis)
+        out[h] = o[0]
+    return out
+
+
+def paged_decode(q, k_cache, v_cache, block_table, ctx_lens, scale, page_size=16):
+    """O (B, Hq, D) float64."""
+    B = q.shape[0]
+    return np.stack([paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_size)
+                     for b in range(B)])

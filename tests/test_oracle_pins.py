@@ -1,0 +1,366 @@
+"""Pins the oracle to facts that do not come from the oracle itself.
+
+* a causal two-position example worked by hand (tests/golden/hand_worked_two_keys.json);
+* closed forms: K = 0 makes every visible score 0, so LSE_i = ln(count_i) and O_i is the mean
+  of the visible V rows; a single visible key returns that V row exactly; equal keys give the
+  mean of the visible V rows for any Q;
+* invariants: softmax rows sum to 1, grouped-query heads equal multi-head attention on
+  repeated K/V (the repeat-KV path of the page "Gemma4 FFPA attention backend support for
+  accelerating Gemma4-family training", Debugging notes), packed rows equal padded rows;
+* central finite differences of L = sum(O * dO) for every gradient coordinate on tiny shapes;
+* an independent library routine: torch's float64 CPU scaled_dot_product_attention with an
+  explicit boolean mask and autograd, which shares nothing with the oracle;
+* the paged decode equals causal attention's last row on the gathered tokens, and does not
+  depend on which pool pages hold them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import (ATTN_WORKLOADS, DECODE_WORKLOADS, bf16_bits_to_f64, f32_to_bf16_bits,
+                   lengths_to_cu_seqlens, lengths_to_pad_mask, make_attention_inputs,
+                   make_decode_inputs, pack_rows)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _num(x):
+    if isinstance(x, str):
+        table = {"ln3": math.log(3), "2ln3": 2 * math.log(3), "ln4": math.log(4),
+                 "-1.125ln3": -1.125 * math.log(3), "1.125ln3": 1.125 * math.log(3)}
+        return table[x]
+    return float(x)
+
+
+def _arr(rows):
+    return np.array([[_num(x) for x in r] if isinstance(r, list) else _num(r) for r in rows])
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# ---------------------------------------------------------------------------
+# Worked by hand
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [0, 1])
+def test_hand_worked_two_keys(case):
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_two_keys.json")))
+    c = g["cases"][case]
+    q = _arr(c["q"])[None, :, None, :]
+    k = _arr(g["k"])[None, :, None, :]
+    v = _arr(g["v"])[None, :, None, :]
+    do = _arr(g["do"])[None, :, None, :]
+    e = g["expect"]
+    o, lse = oracle.attention_forward(q, k, v, c["scale"], causal=True)
+    np.testing.assert_allclose(o[0, :, 0], _arr(e["o"]), atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], _arr(e["lse"]), atol=1e-14)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, c["scale"], causal=True)
+    np.testing.assert_allclose(dq[0, :, 0], _arr(e["dq_scale1" if case == 0 else "dq_scale_half"]), atol=1e-14)
+    np.testing.assert_allclose(dk[0, :, 0], _arr(e["dk"]), atol=1e-14)
+    np.testing.assert_allclose(dv[0, :, 0], _arr(e["dv"]), atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+def _visible_count(i, n, causal, window):
+    if i >= n:
+        return 0
+    lo = 0
+    hi = i + 1 if causal else n
+    if window > 0:
+        lo = max(lo, i - window + 1)
+    return hi - lo
+
+
+@pytest.mark.parametrize("causal,window,lengths", [
+    (True, 0, None), (True, 5, None), (False, 0, None), (True, 0, [11, 4]), (True, 3, [7, 11]),
+])
+def test_zero_keys_give_log_count(causal, window, lengths):
+    rng = np.random.default_rng(1)
+    B, S, Hq, Hkv, D = 2, 11, 4, 2, 8
+    q = _rand(rng, B, S, Hq, D)
+    k = np.zeros((B, S, Hkv, D))
+    v = _rand(rng, B, S, Hkv, D)
+    o, lse = oracle.attention_forward(q, k, v, 0.3, causal, window, lengths)
+    L = [S] * B if lengths is None else lengths
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                cnt = _visible_count(i, L[b], causal, window)
+                if cnt == 0:
+                    assert lse[b, h, i] == 0.0 and not o[b, i, h].any()
+                    continue
+                assert abs(lse[b, h, i] - math.log(cnt)) < 1e-13
+                hi = i + 1 if causal else L[b]
+                lo = hi - cnt
+                np.testing.assert_allclose(o[b, i, h], v[b, lo:hi, h // 2].mean(axis=0), atol=1e-13)
+
+
+def test_equal_keys_give_mean_of_visible_values():
+    rng = np.random.default_rng(2)
+    B, S, H, D = 1, 9, 2, 6
+    q = _rand(rng, B, S, H, D) * 3
+    k = np.broadcast_to(_rand(rng, 1, 1, H, D), (B, S, H, D)).copy()
+    v = _rand(rng, B, S, H, D)
+    o, _ = oracle.attention_forward(q, k, v, 0.7, causal=True, window=4)
+    for i in range(S):
+        lo = max(0, i - 3)
+        np.testing.assert_allclose(o[0, i], v[0, lo:i + 1].mean(axis=0), atol=1e-13)
+
+
+def test_single_visible_key_returns_value_row_exactly():
+    rng = np.random.default_rng(3)
+    q = _rand(rng, 1, 6, 2, 4)
+    k = _rand(rng, 1, 6, 1, 4)
+    v = _rand(rng, 1, 6, 1, 4)
+    o, _ = oracle.attention_forward(q, k, v, 0.5, causal=True)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0]) and np.array_equal(o[0, 0, 1], v[0, 0, 0])
+    o, _ = oracle.attention_forward(q, k, v, 0.5, causal=True, window=1)   # window 1: only the diagonal
+    assert np.array_equal(o[0, :, 0], v[0, :, 0])
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(4)
+    n = 33
+    for causal, window in [(True, 0), (True, 7), (False, 0)]:
+        _, _, p = oracle.unit_forward(_rand(rng, n, 16) * 3, _rand(rng, n, 16) * 3, _rand(rng, n, 16), 0.25,
+                                      oracle.visibility(n, causal, window))
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+        assert (p >= 0).all()
+        assert not p[~oracle.visibility(n, causal, window)].any()
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    rng = np.random.default_rng(5)
+    B, S, Hq, Hkv, D = 2, 10, 6, 2, 8
+    q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    kr, vr = np.repeat(k, Hq // Hkv, axis=2), np.repeat(v, Hq // Hkv, axis=2)
+    lengths = [10, 6]
+    o1, l1 = oracle.attention_forward(q, k, v, 0.3, True, 4, lengths)
+    o2, l2 = oracle.attention_forward(q, kr, vr, 0.3, True, 4, lengths)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+    g1 = oracle.attention_backward(q, k, v, do, 0.3, True, 4, lengths)
+    g2 = oracle.attention_backward(q, kr, vr, do, 0.3, True, 4, lengths)
+    np.testing.assert_allclose(g1[0], g2[0], atol=1e-12)
+    for a, b in ((g1[1], g2[1]), (g1[2], g2[2])):
+        np.testing.assert_allclose(a, b.reshape(B, S, Hkv, Hq // Hkv, D).sum(axis=3), atol=1e-12)
+
+
+def test_packed_rows_equal_padded_rows():
+    rng = np.random.default_rng(6)
+    B, S, Hq, Hkv, D = 3, 12, 4, 2, 8
+    lengths = np.array([12, 5, 9])
+    q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    cu = lengths_to_cu_seqlens(lengths)
+    o, lse = oracle.attention_forward(q, k, v, 0.4, True, 0, lengths)
+    op, lsep = oracle.attention_forward_packed(pack_rows(q, lengths), pack_rows(k, lengths),
+                                               pack_rows(v, lengths), cu, 0.4, True, 0)
+    np.testing.assert_allclose(op, pack_rows(o, lengths), atol=1e-13)
+    np.testing.assert_allclose(lsep, pack_rows(lse.transpose(0, 2, 1), lengths).T, atol=1e-13)
+    g = oracle.attention_backward(q, k, v, do, 0.4, True, 0, lengths)
+    gp = oracle.attention_backward_packed(pack_rows(q, lengths), pack_rows(k, lengths), pack_rows(v, lengths),
+                                          pack_rows(do, lengths), cu, 0.4, True, 0)
+    for a, b in zip(gp, g):
+        np.testing.assert_allclose(a, pack_rows(b, lengths), atol=1e-12)
+    # padded rows and keys are exactly zero
+    for t in (o, *g):
+        for b in range(B):
+            assert not t[b, lengths[b]:].any()
+
+
+def test_padding_values_never_reach_valid_outputs():
+    rng = np.random.default_rng(7)
+    B, S, Hq, Hkv, D = 2, 9, 2, 1, 4
+    lengths = [9, 5]
+    q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    ref = oracle.attention_forward(q, k, v, 0.5, True, 0, lengths), \
+        oracle.attention_backward(q, k, v, do, 0.5, True, 0, lengths)
+    for t in (q, k, v, do):
+        t[1, 5:] = np.nan
+    got = oracle.attention_forward(q, k, v, 0.5, True, 0, lengths), \
+        oracle.attention_backward(q, k, v, do, 0.5, True, 0, lengths)
+    for a, b in zip(ref[0] + ref[1], got[0] + got[1]):
+        assert np.array_equal(a, b)
+
+
+def test_pad_mask_lengths_and_rejection():
+    m = lengths_to_pad_mask(np.array([3, 0, 5]), 5)
+    assert list(oracle.lengths_from_pad_mask(m)) == [3, 0, 5]
+    bad = m.copy()
+    bad[0, 4] = 1
+    with pytest.raises(ValueError):
+        oracle.lengths_from_pad_mask(bad)
+    assert list(oracle.lengths_from_cu_seqlens(np.array([0, 3, 3, 8]))) == [3, 0, 5]
+
+
+# ---------------------------------------------------------------------------
+# Finite differences: every coordinate of dQ, dK, dV
+# ---------------------------------------------------------------------------
+def test_gradients_match_central_differences():
+    rng = np.random.default_rng(8)
+    B, S, Hq, Hkv, D = 2, 9, 4, 2, 8
+    lengths = [9, 5]
+    scale, causal, window = 0.37, True, 3
+    q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention_forward(q_, k_, v_, scale, causal, window, lengths)
+        return float((o * do).sum())
+
+    grads = oracle.attention_backward(q, k, v, do, scale, causal, window, lengths)
+    eps = 1e-6
+    for which, g in enumerate(grads):
+        base = [q, k, v]
+        num = np.zeros_like(g)
+        t = base[which]
+        for idx in np.ndindex(*t.shape):
+            keep = t[idx]
+            t[idx] = keep + eps
+            lp = loss(*base)
+            t[idx] = keep - eps
+            lm = loss(*base)
+            t[idx] = keep
+            num[idx] = (lp - lm) / (2 * eps)
+        err = np.abs(num - g).max() / max(1.0, np.abs(g).max())
+        assert err < 1e-6, (which, err)
+
+
+# ---------------------------------------------------------------------------
+# Independent library routine: torch float64 CPU SDPA + autograd
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal,window,lengths,Hq,Hkv,D", [
+    (True, 0, None, 4, 1, 64),
+    (True, 16, None, 4, 2, 32),
+    (True, 0, [40, 17, 1], 8, 2, 16),
+    (False, 0, [40, 23, 8], 2, 2, 16),
+])
+def test_matches_torch_float64_sdpa(causal, window, lengths, Hq, Hkv, D):
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(9)
+    B, S = (3 if lengths else 2), 40
+    scale = 1.0 / math.sqrt(D)
+    q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    L = [S] * B if lengths is None else lengths
+    o, lse = oracle.attention_forward(q, k, v, scale, causal, window, lengths)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal, window, lengths)
+
+    mask = np.zeros((B, 1, S, S), dtype=bool)
+    dmask = do.copy()
+    for b in range(B):
+        n = L[b]
+        mask[b, 0, :n, :n] = oracle_free_visibility(n, causal, window)
+        mask[b, 0, n:, 0] = True           # padded query rows: any finite row, then zero its dO
+        dmask[b, n:] = 0.0
+    tq = torch.tensor(q.transpose(0, 2, 1, 3), requires_grad=True)
+    r = Hq // Hkv
+    tk = torch.tensor(np.repeat(k, r, axis=2).transpose(0, 2, 1, 3), requires_grad=True)
+    tv = torch.tensor(np.repeat(v, r, axis=2).transpose(0, 2, 1, 3), requires_grad=True)
+    to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(mask), scale=scale)
+    to.backward(torch.tensor(dmask.transpose(0, 2, 1, 3)))
+    t_o = to.detach().numpy().transpose(0, 2, 1, 3)
+    t_dq = tq.grad.numpy().transpose(0, 2, 1, 3)
+    t_dk = tk.grad.numpy().transpose(0, 2, 1, 3).reshape(B, S, Hkv, r, D).sum(axis=3)
+    t_dv = tv.grad.numpy().transpose(0, 2, 1, 3).reshape(B, S, Hkv, r, D).sum(axis=3)
+    for b in range(B):
+        n = L[b]
+        np.testing.assert_allclose(o[b, :n], t_o[b, :n], atol=1e-12)
+        np.testing.assert_allclose(dq[b, :n], t_dq[b, :n], atol=1e-12)
+        np.testing.assert_allclose(dk[b, :n], t_dk[b, :n], atol=1e-12)
+        np.testing.assert_allclose(dv[b, :n], t_dv[b, :n], atol=1e-12)
+        # LSE against a direct log-sum-exp of torch-computed scores
+        s = torch.einsum("hid,hjd->hij", torch.tensor(q[b, :n].transpose(1, 0, 2)),
+                         torch.tensor(np.repeat(k[b, :n], r, axis=1).transpose(1, 0, 2))) * scale
+        s = s.masked_fill(~torch.tensor(mask[b, 0, :n, :n]), float("-inf"))
+        np.testing.assert_allclose(lse[b, :, :n], torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+def oracle_free_visibility(n, causal, window):
+    """The mask for the torch cross-check, built without the oracle."""
+    m = np.ones((n, n), dtype=bool)
+    if causal:
+        m = np.tril(m)
+    if window > 0:
+        m &= ~np.tril(np.ones((n, n), dtype=bool), -window)
+    return m
+
+
+# ---------------------------------------------------------------------------
+# Paged decode
+# ---------------------------------------------------------------------------
+def test_decode_is_last_row_of_causal_attention_and_table_independent():
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=4, ctx_range=(1, 70))
+    inp = make_decode_inputs(w, seed=3, ctx_lens=np.array([1, 16, 17, 70], dtype=np.int32))
+    q = bf16_bits_to_f64(inp["q"])
+    kc, vc = bf16_bits_to_f64(inp["k_cache"]), bf16_bits_to_f64(inp["v_cache"])
+    table, ctx = inp["block_table"], inp["ctx_lens"]
+    o = oracle.paged_decode(q, kc, vc, table, ctx, w.scale, w.page_size)
+    for b in range(w.B):
+        n = int(ctx[b])
+        kk = np.stack([kc[table[b, t // 16], t % 16] for t in range(n)])[None]
+        vv = np.stack([vc[table[b, t // 16], t % 16] for t in range(n)])[None]
+        qq = np.zeros((1, n, w.Hq, w.D))
+        qq[0, n - 1] = q[b]
+        od, _ = oracle.attention_forward(qq, kk, vv, w.scale, causal=True)
+        np.testing.assert_allclose(o[b], od[0, n - 1], atol=1e-13)
+    # a different physical placement of the same logical tokens gives identical bytes
+    perm = np.random.default_rng(0).permutation(inp["num_pages"])
+    inv = np.argsort(perm)
+    kc2, vc2 = kc[inv], vc[inv]                 # page p moves to slot perm[p]
+    table2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1)
+    o2 = oracle.paged_decode(q, kc2, vc2, table2, ctx, w.scale, w.page_size)
+    assert np.array_equal(o, o2)
+
+
+def test_decode_matches_torch_sdpa_and_ignores_unused_pages():
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=3, ctx_range=(20, 90))
+    inp = make_decode_inputs(w, seed=5)
+    pois = make_decode_inputs(w, seed=5, poison_unused=True)
+    args = [bf16_bits_to_f64(inp[x]) for x in ("q", "k_cache", "v_cache")]
+    o = oracle.paged_decode(*args, inp["block_table"], inp["ctx_lens"], w.scale)
+    argsp = [bf16_bits_to_f64(pois[x]) for x in ("q", "k_cache", "v_cache")]
+    op = oracle.paged_decode(*argsp, pois["block_table"], pois["ctx_lens"], w.scale)
+    assert np.array_equal(o, op) and np.isfinite(o).all()
+    r = w.Hq // w.Hkv
+    for b in range(w.B):
+        n = int(inp["ctx_lens"][b])
+        tok = np.arange(n)
+        kk = args[1][inp["block_table"][b][tok // 16], tok % 16]
+        vv = args[2][inp["block_table"][b][tok // 16], tok % 16]
+        tq = torch.tensor(args[0][b][:, None, :])                        # (Hq, 1, D)
+        tk = torch.tensor(np.repeat(kk, r, axis=1).transpose(1, 0, 2))   # (Hq, n, D)
+        tv = torch.tensor(np.repeat(vv, r, axis=1).transpose(1, 0, 2))
+        ref = F.scaled_dot_product_attention(tq, tk, tv, scale=w.scale).numpy()[:, 0]
+        np.testing.assert_allclose(o[b], ref, atol=1e-12)
+    ctx0 = oracle.paged_decode(*args, inp["block_table"], np.zeros(w.B, dtype=np.int32), w.scale)
+    assert not ctx0.any()
+
+
+# ---------------------------------------------------------------------------
+# Oracle on the generated workloads (small slices): finite everywhere
+# ---------------------------------------------------------------------------
+def test_oracle_finite_on_peaked_window_workload_slice():
+    w = ATTN_WORKLOADS["window_d256"].scaled(B=1, S=300, Hq=2, Hkv=1, window=64)
+    inp = make_attention_inputs(w, seed=0)
+    q, k, v, do = (bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
+    o, lse = oracle.attention_forward(q, k, v, w.scale, True, w.window)
+    g = oracle.attention_backward(q, k, v, do, w.scale, True, w.window)
+    for t in (o, lse, *g):
+        assert np.isfinite(t).all()

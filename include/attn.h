@@ -1,0 +1,180 @@
+/*
+ * libattn: fused causal grouped-query attention for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer named "device" is GPU memory on the current HIP device;
+ * "host" pointers are read during the call only.  The caller owns every buffer:
+ * the library never allocates or frees memory and never copies a layout.  Every
+ * call is asynchronous on the given stream (a hipStream_t passed as void*, NULL
+ * for the default stream) and never synchronises.  On any status other than
+ * ATTN_OK nothing has been launched and no output has been touched.
+ *
+ * Method.  Scaled dot-product attention softmax(scale * Q K^T + mask) V computed
+ * without materialising the score matrix, as the fused full-attention path of
+ * the page "Gemma4 FFPA attention backend support for accelerating Gemma4-family
+ * training" (sections Integration and Debugging notes) does in place of the
+ * unfused path that builds the S x S matrix.  The eligibility gate of that page
+ * (section Integration: head_dim 512, 16-bit floats, no dropout, a given scale)
+ * becomes the argument checks below; unsupported cases return
+ * ATTN_ERR_UNSUPPORTED so that the caller can fall back, as the page does.
+ *
+ * Conventions shared by every call:
+ *   - bf16 tensors: last (head_dim) dimension contiguous; other strides are in
+ *     elements, non-negative multiples of 8; base pointers 16-byte aligned.
+ *   - Grouped-query heads: query head h reads key/value head h / (Hq / Hkv)
+ *     (the repeat-KV mapping of the first page's Debugging notes).
+ *   - Mask: key j is visible from query i when both are inside the sequence
+ *     (i, j < len), j <= i when causal, and j > i - window when window > 0.
+ *   - A query row with no visible key yields O = 0 and LSE = 0, never NaN
+ *     (page "flex_attention + paged KV + CUDA graphs vs vLLM", section "What
+ *     broke correctness and had to be dropped").
+ *   - Padded rows (positions at or past a sequence's length) of O, dQ and LSE,
+ *     and padded keys of dK and dV, are written as exact zeros.
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,  /* null pointer, bad shape, stride or alignment */
+    ATTN_ERR_UNSUPPORTED = 2,  /* head_dim, window without causal, ... : caller falls back */
+    ATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes query */
+    ATTN_ERR_HIP = 4           /* a HIP runtime call failed; see attn_last_hip_error() */
+} attn_status;
+
+/* A bf16 tensor: device pointer plus element strides of the batch, sequence and
+ * head dimensions (the head_dim dimension is contiguous).  For packed
+ * (cu_seqlens) rows stride_b is ignored. */
+typedef struct {
+    void* ptr;
+    int64_t stride_b;
+    int64_t stride_s;
+    int64_t stride_h;
+} attn_tensor;
+
+/* Sizes of one attention call.
+ *   B      batch (number of sequences)
+ *   S      sequence capacity: the padded length for dense and pad_mask inputs,
+ *          the longest sequence for cu_seqlens inputs
+ *   total  packed row count (cu_seqlens[B]); only read with cu_seqlens
+ *   Hq     query heads; Hkv key/value heads; Hq % Hkv == 0
+ *   D      head_dim: 256 or 512 */
+typedef struct {
+    int32_t B, S, total, Hq, Hkv, D;
+} attn_shape;
+
+/*
+ * attn_fwd: O = softmax(scale * Q K^T + mask) V and the row log-sum-exp.
+ *
+ * Layouts: dense or pad_mask inputs are (B, S, H, D); with cu_seqlens they are
+ * packed (total, H, D), sequence b owning rows cu_seqlens[b] .. cu_seqlens[b+1]-1.
+ *   q, o        Hq heads; k, v Hkv heads (o is written)
+ *   lse         device fp32, written: (B, Hq, S) contiguous, or (Hq, total) for
+ *               cu_seqlens; natural-log log-sum-exp of the scaled visible scores
+ *   scale       multiplies Q K^T (must be finite and > 0)
+ *   causal      0 or 1
+ *   window      0 for none; W > 0 keeps keys j > i - W and requires causal
+ *   cu_seqlens  device int32 (B+1), or NULL
+ *   pad_mask    device uint8 (B, S), row-major, 1 = valid; each row must be a
+ *               prefix of ones (right padding); or NULL.  At most one of
+ *               cu_seqlens and pad_mask may be given.  Their contents are not
+ *               checked; lengths are clamped to [0, S] so no access leaves the
+ *               buffers.
+ *   workspace   device scratch of at least attn_fwd_workspace_bytes(shape,
+ *               varlen) bytes (0 for dense inputs), 256-byte aligned
+ * The first page's Results section records that the forward's outputs are kept
+ * for the backward rather than recomputed; attn_bwd takes O and LSE from here.
+ */
+attn_status attn_fwd(const attn_shape* shape,
+                     attn_tensor q, attn_tensor k, attn_tensor v,
+                     float scale, int causal, int window,
+                     const int32_t* cu_seqlens, const uint8_t* pad_mask,
+                     attn_tensor o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd: gradients of sum(O * dO) with respect to Q, K and V.
+ *
+ * q, k, v, scale, causal, window, cu_seqlens, pad_mask and the layouts are as
+ * in attn_fwd, and o and lse must be that call's outputs.  dq (Hq heads), dk
+ * and dv (Hkv heads, summed over the Hq/Hkv query heads that share them) are
+ * written in the same layouts as q, k and v.  The page "Root cause analysis:
+ * Gemma4 sliding-window BF16 cuDNN SDPA NaN on H100" (Debug and validation
+ * results) traces a failure where finite dO produced non-finite dQ/dK/dV; here
+ * every gradient of finite inputs is finite.
+ *   workspace  at least attn_bwd_workspace_bytes(shape, varlen) bytes
+ *              (row statistics, fp32 per query row and head)
+ */
+attn_status attn_bwd(const attn_shape* shape,
+                     attn_tensor q, attn_tensor k, attn_tensor v,
+                     attn_tensor o, const float* lse, attn_tensor dout,
+                     float scale, int causal, int window,
+                     const int32_t* cu_seqlens, const uint8_t* pad_mask,
+                     attn_tensor dq, attn_tensor dk, attn_tensor dv,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sizes of one paged decode call.
+ *   B                 sequences, one query token each
+ *   Hq, Hkv, D        heads and head_dim (D = 128)
+ *   page_size         tokens per cache page (16)
+ *   num_pages         pages in the cache pool
+ *   max_pages_per_seq columns of block_table */
+typedef struct {
+    int32_t B, Hq, Hkv, D, page_size, num_pages, max_pages_per_seq;
+} attn_decode_shape;
+
+/*
+ * paged_decode: one query token per sequence against a paged KV cache
+ * (page "flex_attention + paged KV + CUDA graphs vs vLLM", Architecture notes:
+ * a paged cache plus a page table mapping logical to physical pages; section
+ * "What each option did": the per-block page-table indirection that a random
+ * page placement makes necessary).
+ *
+ *   q            device bf16 (B, Hq, D); element strides q_stride_b, q_stride_h
+ *   k_cache,     device bf16 (num_pages, page_size, Hkv, D); attn_tensor strides
+ *   v_cache      are (page, slot, head) in elements
+ *   block_table  device int32 (B, max_pages_per_seq), row-major: logical page p of
+ *                sequence b lives in physical page block_table[b][p].  Entries a
+ *                sequence does not use are never read.  An entry outside
+ *                [0, num_pages) is clamped into range (no out-of-bounds read).
+ *   ctx_lens     device int32 (B): tokens in each sequence's cache, including the
+ *                current one; the query sits at position ctx_lens[b]-1 and sees
+ *                every token t < ctx_lens[b].  Clamped to
+ *                [0, max_pages_per_seq * page_size]; 0 gives O = 0.
+ *   o            device bf16 (B, Hq, D), written; strides o_stride_b, o_stride_h
+ *   workspace    at least paged_decode_workspace_bytes(shape) bytes
+ */
+attn_status paged_decode(const attn_decode_shape* shape,
+                         const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                         attn_tensor k_cache, attn_tensor v_cache,
+                         const int32_t* block_table, const int32_t* ctx_lens,
+                         float scale,
+                         void* o, int64_t o_stride_b, int64_t o_stride_h,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace sizes in bytes.  varlen: 0 dense, 1 pad_mask, 2 cu_seqlens.
+ * Return 0 for arguments that the matching call would reject. */
+size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen);
+size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen);
+size_t paged_decode_workspace_bytes(const attn_decode_shape* shape);
+
+/* Static string for a status code. */
+const char* attn_status_str(attn_status status);
+
+/* The hipError_t (as int) of the last ATTN_ERR_HIP on this thread, 0 if none. */
+int attn_last_hip_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

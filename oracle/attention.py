@@ -38,7 +38,7 @@ __all__ = [
     "unit_forward", "unit_backward", "attention_forward", "attention_backward",
     "attention_forward_head", "attention_backward_group",
     "attention_forward_packed", "attention_backward_packed",
-    "gather_pages", "paged_decode", "paged_decode_one",
+    "gather_pages", "paged_decode", "paged_decode_one", "attention_rows",
 ]
 
 
@@ -193,6 +193,37 @@ def attention_backward(q, k, v, do, scale, causal=True, window=0, lengths=None):
             dk[b, :, g] = gk
             dv[b, :, g] = gv
     return dq, dk, dv
+
+
+def attention_rows(q, k, v, do, b, h, rows, scale, causal=True, window=0, lengths=None):
+    """O, LSE and dQ of selected query rows of one (batch, head), one row at a time.
+
+    Everything a query row needs is row-local: its visible keys, its softmax, and for
+    the gradient delta_i = sum_j P_ij dP_ij.  Rows at or past the length give zeros.
+    do may be None (then dQ is not computed).  Returns arrays indexed like `rows`.
+    """
+    B, S, Hq, D = q.shape
+    r = Hq // k.shape[2]
+    g = h // r
+    n = int(_lengths(B, S, lengths)[b])
+    rows = np.asarray(rows)
+    o = np.zeros((len(rows), D))
+    lse = np.zeros(len(rows))
+    dq = np.zeros((len(rows), D))
+    for x, i in enumerate(rows):
+        i = int(i)
+        if i >= n:
+            continue
+        vis = visibility(n, causal, window)[i][None, :]
+        kk, vv = k[b, :n, g], v[b, :n, g]
+        oi, li, p = unit_forward(q[b, i, h][None, :], kk, vv, scale, vis)
+        o[x], lse[x] = oi[0], li[0]
+        if do is not None:
+            dp = do[b, i, h][None, :] @ vv.T
+            delta = (p * dp).sum(axis=1)
+            ds = p * (dp - delta[:, None])
+            dq[x] = scale * (ds @ kk)[0]
+    return o, lse, dq
 
 
 # Packed rows (cu_seqlens): q, o, dO (T, Hq, D); k, v (T, Hkv, D); LSE (Hq, T).

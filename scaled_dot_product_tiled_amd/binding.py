@@ -1,0 +1,215 @@
+"""Thin ctypes binding of libattn (include/attn.h): argument marshalling only.
+
+torch supplies device memory and the current stream; every computation runs in the HIP
+kernels behind the C ABI.  There is no fallback: if the library is missing or a call
+returns an error status, a RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK = 0
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_s", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("total", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class AttnDecodeShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32)]
+
+
+_lib = None
+
+EXPORTS = ("attn_fwd", "attn_bwd", "paged_decode", "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes",
+           "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so (built by ``scaled_dot_product_tiled_amd.build``) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libattn.so not found at {path}; build it with "
+                           "`python -m scaled_dot_product_tiled_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [P(AttnShape), AttnTensor, AttnTensor, AttnTensor, ctypes.c_float, ctypes.c_int,
+                             ctypes.c_int, vp, vp, AttnTensor, vp, vp, sz, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [P(AttnShape), AttnTensor, AttnTensor, AttnTensor, AttnTensor, vp, AttnTensor,
+                             ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, vp, AttnTensor, AttnTensor, AttnTensor,
+                             vp, sz, vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.paged_decode.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int64, ctypes.c_int64, AttnTensor, AttnTensor,
+                                 vp, vp, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz, vp]
+    lib.paged_decode.restype = ctypes.c_int
+    lib.attn_fwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
+    lib.attn_fwd_workspace_bytes.restype = sz
+    lib.attn_bwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.paged_decode_workspace_bytes.argtypes = [P(AttnDecodeShape)]
+    lib.paged_decode_workspace_bytes.restype = sz
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = ctypes.c_int
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != ATTN_OK:
+        lib = load_library()
+        msg = lib.attn_status_str(status).decode()
+        hip = lib.attn_last_hip_error()
+        raise RuntimeError(f"{what} failed: status {status} ({msg})" + (f", hip error {hip}" if status == 4 else ""))
+
+
+def _bf16(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 CUDA/HIP tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the head_dim dimension must be contiguous")
+
+
+def _tensor(t: torch.Tensor, packed: bool) -> AttnTensor:
+    if packed:   # (T, H, D)
+        return AttnTensor(t.data_ptr(), 0, t.stride(0), t.stride(1))
+    return AttnTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _shape(q, k, cu_seqlens, pad_mask, max_seqlen):
+    packed = cu_seqlens is not None
+    if packed:
+        T, Hq, D = q.shape
+        B = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        S = int(max_seqlen)
+    else:
+        B, S, Hq, D = q.shape
+        T = 0
+    Hkv = k.shape[-2]
+    return AttnShape(B, S, T, Hq, Hkv, D), packed, (2 if packed else (1 if pad_mask is not None else 0))
+
+
+def _meta_ptrs(cu_seqlens, pad_mask):
+    cu = None
+    pm = None
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
+            raise TypeError("cu_seqlens must be a contiguous int32 device tensor")
+        cu = cu_seqlens.data_ptr()
+    if pad_mask is not None:
+        if pad_mask.dtype not in (torch.bool, torch.uint8) or not pad_mask.is_cuda or not pad_mask.is_contiguous():
+            raise TypeError("pad_mask must be a contiguous bool/uint8 device tensor")
+        pm = pad_mask.data_ptr()
+    return cu, pm
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
+             window: int = 0, cu_seqlens: Optional[torch.Tensor] = None, pad_mask: Optional[torch.Tensor] = None,
+             max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O, LSE of causal grouped-query attention.  q (B,S,Hq,D), k/v (B,S,Hkv,D); with cu_seqlens the
+    rows are packed: q (T,Hq,D), k/v (T,Hkv,D), LSE (Hq,T).  Returns (O, LSE fp32)."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _bf16(t, n)
+    shape, packed, varlen = _shape(q, k, cu_seqlens, pad_mask, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse_shape = (shape.Hq, shape.total) if packed else (shape.B, shape.Hq, shape.S)
+        lse = torch.empty(lse_shape, device=q.device, dtype=torch.float32)
+    cu, pm = _meta_ptrs(cu_seqlens, pad_mask)
+    nbytes = lib.attn_fwd_workspace_bytes(ctypes.byref(shape), varlen)
+    ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    st = lib.attn_fwd(ctypes.byref(shape), _tensor(q, packed), _tensor(k, packed), _tensor(v, packed), float(scale),
+                      int(bool(causal)), int(window), cu, pm, _tensor(out, packed), lse.data_ptr(),
+                      ws.data_ptr() if nbytes else None, nbytes, _stream())
+    _check(st, "attn_fwd")
+    return out, lse
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, scale: Optional[float] = None, causal: bool = True, window: int = 0,
+             cu_seqlens: Optional[torch.Tensor] = None, pad_mask: Optional[torch.Tensor] = None,
+             max_seqlen: Optional[int] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV of sum(O * dO), from attn_fwd's O and LSE."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _bf16(t, n)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    shape, packed, varlen = _shape(q, k, cu_seqlens, pad_mask, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    cu, pm = _meta_ptrs(cu_seqlens, pad_mask)
+    nbytes = lib.attn_bwd_workspace_bytes(ctypes.byref(shape), varlen)
+    ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    st = lib.attn_bwd(ctypes.byref(shape), _tensor(q, packed), _tensor(k, packed), _tensor(v, packed),
+                      _tensor(o, packed), lse.data_ptr(), _tensor(dout, packed), float(scale), int(bool(causal)),
+                      int(window), cu, pm, _tensor(dq, packed), _tensor(dk, packed), _tensor(dv, packed),
+                      ws.data_ptr() if nbytes else None, nbytes, _stream())
+    _check(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 ctx_lens: torch.Tensor, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O (B,Hq,D) of one query token per sequence against a paged cache (num_pages, page_size, Hkv, D)."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _bf16(t, n)
+    for t, n in ((block_table, "block_table"), (ctx_lens, "ctx_lens")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 device tensor")
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, _ = k_cache.shape
+    shape = AttnDecodeShape(B, Hq, Hkv, D, page_size, num_pages, block_table.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    nbytes = lib.paged_decode_workspace_bytes(ctypes.byref(shape))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    st = lib.paged_decode(ctypes.byref(shape), q.data_ptr(), q.stride(0), q.stride(1),
+                          AttnTensor(k_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)),
+                          AttnTensor(v_cache.data_ptr(), v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)),
+                          block_table.data_ptr(), ctx_lens.data_ptr(), float(scale), out.data_ptr(), out.stride(0),
+                          out.stride(1), workspace.data_ptr(), nbytes, _stream())
+    _check(st, "paged_decode")
+    return out

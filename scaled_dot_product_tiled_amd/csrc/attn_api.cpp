@@ -1,0 +1,305 @@
+// C ABI of libattn: argument checks, workspace sizing, launch planning and the kernel
+// launches, all on the caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "kernel_args.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool stride_ok(int64_t s) { return s >= 0 && s % 8 == 0; }
+
+attn_status check_tensor(const attn_tensor& t, bool packed) {
+  if (t.ptr == nullptr || !aligned16(t.ptr)) return ATTN_ERR_INVALID_ARG;
+  if (!stride_ok(t.stride_s) || !stride_ok(t.stride_h)) return ATTN_ERR_INVALID_ARG;
+  if (!packed && !stride_ok(t.stride_b)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// varlen: 0 dense, 1 pad_mask, 2 cu_seqlens
+attn_status check_shape(const attn_shape* s, int varlen) {
+  if (s == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (s->B < 0 || s->S < 0 || s->Hq <= 0 || s->Hkv <= 0 || s->total < 0) return ATTN_ERR_INVALID_ARG;
+  if (s->Hq % s->Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (s->D != 256 && s->D != 512) return ATTN_ERR_UNSUPPORTED;
+  // every row index handled as a 32-bit int inside the kernels
+  const int64_t rows = varlen == 2 ? (int64_t)s->total : (int64_t)s->B * s->S;
+  if (rows * s->Hq >= INT_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+size_t meta_bytes(const attn_shape* s, int varlen) {
+  return varlen ? round_up(2 * sizeof(int32_t) * (size_t)s->B) : 0;
+}
+
+size_t stat_elems(const attn_shape* s, int varlen) {
+  return (size_t)s->Hq * (varlen == 2 ? (size_t)s->total : (size_t)s->B * s->S);
+}
+
+int varlen_kind(const int32_t* cu, const uint8_t* mask) { return cu ? 2 : (mask ? 1 : 0); }
+
+attn_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = (int)e;
+  return ATTN_ERR_HIP;
+}
+
+// Query heads packed per workgroup: the largest power of two dividing r, capped so a
+// tile still spans at least 16 positions.
+int heads_per_tile(int r, int rows) {
+  int hpt = 1;
+  while (hpt * 2 <= 8 && r % (hpt * 2) == 0 && rows / (hpt * 2) >= 16) hpt *= 2;
+  return hpt;
+}
+
+void plan_rows(attn::AttnArgs& a, int rows) {
+  a.hpt = heads_per_tile(a.r, rows);
+  a.mpos = rows / a.hpt;
+  a.nhb = a.r / a.hpt;
+  a.nqt = (a.S + a.mpos - 1) / a.mpos;
+  a.total_items = a.B * a.Hkv * a.nhb * a.nqt;
+  a.per_xcd = (a.total_items + 7) / 8;
+}
+
+void fill_common(attn::AttnArgs& a, const attn_shape* s, int varlen, float scale, int causal, int window,
+                 const int32_t* meta) {
+  a.B = s->B;
+  a.S = s->S;
+  a.Hq = s->Hq;
+  a.Hkv = s->Hkv;
+  a.r = s->Hq / s->Hkv;
+  a.packed = varlen == 2;
+  a.causal = causal ? 1 : 0;
+  a.window = window;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  a.seq_off = varlen ? meta : nullptr;
+  a.seq_len = varlen ? meta + s->B : nullptr;
+  if (a.packed) {
+    a.st_sb = 0;
+    a.st_sh = s->total;
+  } else {
+    a.st_sh = s->S;
+    a.st_sb = (int64_t)s->Hq * s->S;
+  }
+}
+
+void set_tensor(const attn_tensor& t, bool packed, int64_t& sb, int64_t& ss, int64_t& sh) {
+  sb = packed ? 0 : t.stride_b;
+  ss = t.stride_s;
+  sh = t.stride_h;
+}
+
+attn_status check_common(const attn_shape* shape, float scale, int causal, int window, const int32_t* cu,
+                         const uint8_t* mask, size_t ws_bytes, size_t need, const void* ws) {
+  if (cu && mask) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_shape(shape, varlen_kind(cu, mask));
+  if (st != ATTN_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (window < 0) return ATTN_ERR_INVALID_ARG;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (need > 0 && (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))))
+    return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
+bool empty_call(const attn_shape* s, int varlen) {
+  return s->B == 0 || s->S == 0 || (varlen == 2 && s->total == 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen) {
+  if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
+  return meta_bytes(shape, varlen);
+}
+
+size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen) {
+  if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
+  return meta_bytes(shape, varlen) + round_up(sizeof(float) * stat_elems(shape, varlen));
+}
+
+attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, float scale, int causal,
+                     int window, const int32_t* cu_seqlens, const uint8_t* pad_mask, attn_tensor o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const int varlen = varlen_kind(cu_seqlens, pad_mask);
+  attn_status st = check_common(shape, scale, causal, window, cu_seqlens, pad_mask, workspace_bytes,
+                                shape ? attn_fwd_workspace_bytes(shape, varlen) : 0, workspace);
+  if (st != ATTN_OK) return st;
+  const bool packed = varlen == 2;
+  if ((st = check_tensor(q, packed)) || (st = check_tensor(k, packed)) || (st = check_tensor(v, packed)) ||
+      (st = check_tensor(o, packed)))
+    return st;
+  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (empty_call(shape, varlen)) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  int32_t* meta = static_cast<int32_t*>(workspace);
+  if (varlen) {
+    if ((st = hip_status(attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s))))
+      return st;
+  }
+  attn::AttnArgs a = {};
+  fill_common(a, shape, varlen, scale, causal, window, meta);
+  a.q = static_cast<const __bf16*>(q.ptr);
+  a.k = static_cast<const __bf16*>(k.ptr);
+  a.v = static_cast<const __bf16*>(v.ptr);
+  a.out = static_cast<__bf16*>(o.ptr);
+  a.lse = lse;
+  set_tensor(q, packed, a.q_sb, a.q_ss, a.q_sh);
+  set_tensor(k, packed, a.k_sb, a.k_ss, a.k_sh);
+  set_tensor(v, packed, a.v_sb, a.v_ss, a.v_sh);
+  set_tensor(o, packed, a.o_sb, a.o_ss, a.o_sh);
+  plan_rows(a, attn::kFwdRows);
+  return hip_status(attn::launch_fwd(a, shape->D, s));
+}
+
+attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
+                     const float* lse, attn_tensor dout, float scale, int causal, int window,
+                     const int32_t* cu_seqlens, const uint8_t* pad_mask, attn_tensor dq, attn_tensor dk,
+                     attn_tensor dv, void* workspace, size_t workspace_bytes, void* stream) {
+  const int varlen = varlen_kind(cu_seqlens, pad_mask);
+  attn_status st = check_common(shape, scale, causal, window, cu_seqlens, pad_mask, workspace_bytes,
+                                shape ? attn_bwd_workspace_bytes(shape, varlen) : 0, workspace);
+  if (st != ATTN_OK) return st;
+  const bool packed = varlen == 2;
+  if ((st = check_tensor(q, packed)) || (st = check_tensor(k, packed)) || (st = check_tensor(v, packed)) ||
+      (st = check_tensor(o, packed)) || (st = check_tensor(dout, packed)) || (st = check_tensor(dq, packed)) ||
+      (st = check_tensor(dk, packed)) || (st = check_tensor(dv, packed)))
+    return st;
+  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (empty_call(shape, varlen)) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  int32_t* meta = static_cast<int32_t*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(shape, varlen));
+  if (varlen) {
+    if ((st = hip_status(attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s))))
+      return st;
+  }
+  attn::AttnArgs a = {};
+  fill_common(a, shape, varlen, scale, causal, window, meta);
+  a.q = static_cast<const __bf16*>(q.ptr);
+  a.k = static_cast<const __bf16*>(k.ptr);
+  a.v = static_cast<const __bf16*>(v.ptr);
+  a.o = static_cast<const __bf16*>(o.ptr);
+  a.dout = static_cast<const __bf16*>(dout.ptr);
+  a.out = static_cast<__bf16*>(dq.ptr);
+  a.dk = static_cast<__bf16*>(dk.ptr);
+  a.dv = static_cast<__bf16*>(dv.ptr);
+  a.lse = const_cast<float*>(lse);
+  a.delta = delta;
+  set_tensor(q, packed, a.q_sb, a.q_ss, a.q_sh);
+  set_tensor(k, packed, a.k_sb, a.k_ss, a.k_sh);
+  set_tensor(v, packed, a.v_sb, a.v_ss, a.v_sh);
+  set_tensor(o, packed, a.o_sb, a.o_ss, a.o_sh);
+  set_tensor(dout, packed, a.do_sb, a.do_ss, a.do_sh);
+  set_tensor(dq, packed, a.dq_sb, a.dq_ss, a.dq_sh);
+  set_tensor(dk, packed, a.dk_sb, a.dk_ss, a.dk_sh);
+  set_tensor(dv, packed, a.dv_sb, a.dv_ss, a.dv_sh);
+
+  const int rows = packed ? shape->total * shape->Hq : shape->B * shape->S * shape->Hq;
+  if ((st = hip_status(attn::launch_bwd_pre(a, shape->D, rows, s)))) return st;
+
+  attn::AttnArgs kv = a;
+  kv.nkt = (a.S + attn::kDkdvKeys - 1) / attn::kDkdvKeys;
+  kv.total_items = a.B * a.Hkv * kv.nkt;
+  kv.per_xcd = (kv.total_items + 7) / 8;
+  if ((st = hip_status(attn::launch_bwd_dkdv(kv, shape->D, s)))) return st;
+
+  attn::AttnArgs qa = a;
+  plan_rows(qa, attn::kDqRows);
+  return hip_status(attn::launch_bwd_dq(qa, shape->D, s));
+}
+
+size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {
+  if (s == nullptr || s->B < 0 || s->Hq <= 0 || s->Hkv <= 0 || s->D != 128 || s->page_size != 16 ||
+      s->max_pages_per_seq <= 0)
+    return 0;
+  const size_t chunks = ((size_t)s->max_pages_per_seq * s->page_size + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
+  return round_up(sizeof(float) * (size_t)s->B * s->Hq * chunks * (s->D + 2));
+}
+
+attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                         attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
+                         const int32_t* ctx_lens, float scale, void* o, int64_t o_stride_b, int64_t o_stride_h,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (shape == nullptr) return ATTN_ERR_INVALID_ARG;
+  const attn_decode_shape& sh = *shape;
+  if (sh.B < 0 || sh.Hq <= 0 || sh.Hkv <= 0 || sh.num_pages <= 0 || sh.max_pages_per_seq <= 0 || sh.page_size <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (sh.Hq % sh.Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  const int r = sh.Hq / sh.Hkv;
+  if (sh.D != 128 || sh.page_size != 16 || (r != 1 && r != 2 && r != 4 && r != 8)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)sh.max_pages_per_seq * sh.page_size > INT_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (q == nullptr || o == nullptr || !aligned16(q) || !aligned16(o) || block_table == nullptr || ctx_lens == nullptr)
+    return ATTN_ERR_INVALID_ARG;
+  if (!stride_ok(q_stride_b) || !stride_ok(q_stride_h) || !stride_ok(o_stride_b) || !stride_ok(o_stride_h))
+    return ATTN_ERR_INVALID_ARG;
+  attn_status st;
+  if ((st = check_tensor(k_cache, false)) || (st = check_tensor(v_cache, false))) return st;
+  const size_t need = paged_decode_workspace_bytes(shape);
+  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  if (sh.B == 0) return ATTN_OK;
+
+  attn::DecodeArgs a = {};
+  a.q = static_cast<const __bf16*>(q);
+  a.kc = static_cast<const __bf16*>(k_cache.ptr);
+  a.vc = static_cast<const __bf16*>(v_cache.ptr);
+  a.table = block_table;
+  a.ctx = ctx_lens;
+  a.o = static_cast<__bf16*>(o);
+  a.part = static_cast<float*>(workspace);
+  a.q_sb = q_stride_b;
+  a.q_sh = q_stride_h;
+  a.o_sb = o_stride_b;
+  a.o_sh = o_stride_h;
+  a.kc_sp = k_cache.stride_b;
+  a.kc_ss = k_cache.stride_s;
+  a.kc_sh = k_cache.stride_h;
+  a.vc_sp = v_cache.stride_b;
+  a.vc_ss = v_cache.stride_s;
+  a.vc_sh = v_cache.stride_h;
+  a.B = sh.B;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.r = r;
+  a.page_size = sh.page_size;
+  a.num_pages = sh.num_pages;
+  a.max_pages = sh.max_pages_per_seq;
+  a.max_chunks = (sh.max_pages_per_seq * sh.page_size + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
+  a.c = scale * 1.4426950408889634f;
+  return hip_status(attn::launch_decode(a, sh.D, static_cast<hipStream_t>(stream)));
+}
+
+const char* attn_status_str(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument (null pointer, shape, stride or alignment)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, window without causal, sizes)";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+const char* attn_version(void) { return "0.1.0"; }
+
+}  // extern "C"

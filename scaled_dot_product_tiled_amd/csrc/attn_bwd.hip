@@ -1,0 +1,446 @@
+// Fused causal grouped-query attention, backward: gradients of sum(O * dO) with
+// respect to Q, K and V, from the forward's saved O and LSE (the page "Gemma4 FFPA
+// attention backend support for accelerating Gemma4-family training", section Results,
+// keeps the forward's outputs for the backward instead of replaying it).
+//
+// With P = exp(scale Q K^T - LSE) (masked entries 0), dP = dO V^T, delta = rowsum(dO * O)
+// and dS = P * (dP - delta):  dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+// Three kernels run in stream order:
+//   bwd_pre   delta per (query row, head), fp32;
+//   bwd_dkdv  one workgroup per (batch, kv head, 64-key tile): K and V of the tile stay
+//             in registers, every visible 32-row query tile of every query head of the
+//             group streams through LDS, and dK, dV accumulate in registers (no atomics,
+//             one pass over the group's heads, so the grouped-query sum is exact);
+//   bwd_dq    one workgroup per 64 query rows (like the forward): Q and dO stay in
+//             registers and visible 32-key tiles of K and V stream through LDS.
+// Masked entries become exact zeros by selection, never by multiplication, so a
+// non-finite value outside the visible region cannot reach a gradient (the page "Root
+// cause analysis: Gemma4 sliding-window BF16 cuDNN SDPA NaN on H100" traces non-finite
+// dQ/dK/dV from finite dO in a masked sliding-window backward).
+//
+// Inside both gradient kernels the four waves split by role: two "score" waves compute
+// S = Q K^T for one 32-key (or 32-row) block each and two "dP" waves compute dO V^T for
+// the same blocks; dP crosses to the score wave through LDS, the score wave forms P and
+// dS, and every wave then owns a quarter of head_dim for the two gradient products.
+#include "device_common.h"
+#include "kernel_args.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO * O)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, int rows) {
+  constexpr int EPL = D / 64;  // elements per lane
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  int b, pos, h, len;
+  if (a.packed) {
+    // packed rows: batch stride and per-sequence offset are folded into the row index
+    const int t = row / a.Hq;
+    h = row - t * a.Hq;
+    b = 0;
+    pos = t;
+    len = t + 1;
+  } else {
+    h = row % a.Hq;
+    const int bp = row / a.Hq;
+    pos = bp % a.S;
+    b = bp / a.S;
+    len = a.seq_len ? min(max(a.seq_len[b], 0), a.S) : a.S;
+  }
+  const int off = 0;
+  float acc = 0.f;
+  if (pos < len) {
+    const bf16* op = a.o + b * a.o_sb + (int64_t)(off + pos) * a.o_ss + h * a.o_sh + lane * EPL;
+    const bf16* dp = a.dout + b * a.do_sb + (int64_t)(off + pos) * a.do_ss + h * a.do_sh + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc += (float)op[e] * (float)dp[e];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (lane == 0) a.delta[b * a.st_sb + h * a.st_sh + off + pos] = acc;
+}
+
+hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream) {
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (D == 512)
+    hipLaunchKernelGGL(bwd_pre_kernel<512>, grid, block, 0, stream, a, rows);
+  else if (D == 256)
+    hipLaunchKernelGGL(bwd_pre_kernel<256>, grid, block, 0, stream, a, rows);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// Row statistics (LSE * log2 e and delta) of query rows i0 .. i0+31 of head h into LDS:
+// 32 floats of LSE then 32 of delta, one 4-byte DMA lane each.
+__device__ __forceinline__ void dma_stats(float* dst, const float* lse_row0, const float* delta_row0, int i0,
+                                          int imax, int lane) {
+  const int i = min(i0 + (lane & 31), imax);
+  const float* src = (lane < 32 ? lse_row0 : delta_row0) + i;
+  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)dst, 4, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
+  constexpr int NK = kDkdvKeys;   // 64 keys per workgroup
+  constexpr int MQ = kDkdvRows;   // 32 query rows per step
+  constexpr int KS = D / 16;
+  constexpr int DBW = D / 128;    // 32-wide d blocks owned by each wave
+  constexpr int NDMA = dma_rows_per_wave<D, MQ, 4>();
+  static_assert(NK == 64 && MQ == 32, "role split assumes 2 key blocks and one row block");
+  __shared__ __attribute__((aligned(1024))) bf16 Qs[2][MQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 dOs[2][MQ * D];
+  __shared__ __attribute__((aligned(16))) float stat[2][64];
+  __shared__ __attribute__((aligned(16))) float xdp[2][16][64];       // dP of key block kb: [kb][reg][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 pds[2][2][2][64];    // [P|dS][kb][s][lane]
+
+  const int item = xcd_item(a.per_xcd, a.total_items);
+  if (item < 0) return;
+  const int unit = item / a.nkt;
+  const int kt = item - unit * a.nkt;  // low key tiles see the most query rows: first
+  const int g = unit % a.Hkv;
+  const int b = unit / a.Hkv;
+  int len = a.seq_len ? a.seq_len[b] : a.S;
+  len = min(max(len, 0), a.S);
+  const int off = a.seq_off ? a.seq_off[b] : 0;
+  const int j0 = kt * NK;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g2 = lane >> 5, ln = lane & 31;
+  const bool score_wave = wave < 2;
+  const int kb = wave & 1;            // key block of this wave's score / dP product
+  const int dsl = wave * DBW;         // first d block of this wave's gradient slice
+
+  f32x16 dvacc[2][DBW], dkacc[2][DBW];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int d = 0; d < DBW; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dvacc[x][d][r] = dkacc[x][d][r] = 0.f;
+
+  // query range that sees any key of the tile
+  const int qlo = a.causal ? j0 : 0;
+  int qhi = len;
+  if (a.window > 0) qhi = min(qhi, j0 + NK - 1 + a.window);
+  const int tq0 = qlo / MQ;
+  const int nq = (j0 < len && qhi > qlo) ? (qhi + MQ - 1) / MQ - tq0 : 0;
+  const int nsteps = a.r * nq;
+
+  if (nsteps > 0) {
+    // this wave's 32 keys of K (score waves) or V (dP waves) as B operands
+    bf16x8 kv[KS];
+    {
+      const int key = j0 + 32 * kb + ln;
+      const bool ok = key < len;
+      const int krow = min(key, len - 1);
+      const bf16* src = score_wave ? a.k + b * a.k_sb + (int64_t)(off + krow) * a.k_ss + g * a.k_sh
+                                   : a.v + b * a.v_sb + (int64_t)(off + krow) * a.v_ss + g * a.v_sh;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const bf16x8 x = ldg8(src + 16 * t + 8 * g2);
+        kv[t] = ok ? x : zero_bf16x8();
+      }
+    }
+    const RowFrags<D> rowf(lane);
+    const TrFrags<D> trf(lane);
+    const float c = a.c;
+
+    auto issue = [&](int k, int buf) {
+      const int hi = k / nq;
+      const int i0 = (tq0 + (k - hi * nq)) * MQ;
+      const int h = g * a.r + hi;
+      const bf16* qb = a.q + b * a.q_sb + (int64_t)off * a.q_ss + h * a.q_sh;
+      const bf16* db = a.dout + b * a.do_sb + (int64_t)off * a.do_ss + h * a.do_sh;
+      dma_rows<D, MQ, 4>(Qs[buf], qb, a.q_ss, i0, len - 1, wave, lane);
+      dma_rows<D, MQ, 4>(dOs[buf], db, a.do_ss, i0, len - 1, wave, lane);
+      if (wave == 0) {
+        const int64_t so = b * a.st_sb + h * a.st_sh + off;
+        dma_stats(stat[buf], a.lse + so, a.delta + so, i0, len - 1, lane);
+      }
+    };
+    (void)NDMA;
+    issue(0, 0);
+    for (int k = 0; k < nsteps; ++k) {
+      const int buf = k & 1;
+      wait_vmcnt<0>();
+      barrier_lds();  // step k is in LDS; every wave is done with step k-1
+      if (k + 1 < nsteps) issue(k + 1, buf ^ 1);
+      const int hi = k / nq;
+      const int i0 = (tq0 + (k - hi * nq)) * MQ;
+
+      f32x16 sacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      {
+        const bf16* src = score_wave ? Qs[buf] : dOs[buf];
+        bf16x8 f[3];
+        f[0] = rowf.read(src, 0, 0);
+        f[1] = rowf.read(src, 0, 1);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          if (t + 2 < KS) f[(t + 2) % 3] = rowf.read(src, 0, t + 2);
+          sacc = mfma32(f[t % 3], kv[t], sacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // sacc: lane = key j0 + 32 kb + ln, register r = query row i0 + 8 (r/4) + 4 g2 + r%4
+      if (!score_wave) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xdp[kb][r][lane] = sacc[r];
+      }
+      barrier_lds();
+      if (score_wave) {
+        const bool full = (i0 + MQ <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= i0) &&
+                          (a.window <= 0 || j0 > i0 + MQ - 1 - a.window);
+        const int key = j0 + 32 * kb + ln;
+        bf16x8 pb[2], db[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ri = 8 * (r >> 2) + 4 * g2 + (r & 3);
+          const float lse2 = stat[buf][ri] * kLog2e;
+          const float dl = stat[buf][32 + ri];
+          const bool vis = full || key_visible(i0 + ri, key, len, a.causal, a.window);
+          const float p = vis ? fast_exp2(fmaf(sacc[r], c, -lse2)) : 0.f;
+          const float ds = vis ? p * (xdp[kb][r][lane] - dl) : 0.f;
+          pb[r >> 3][r & 7] = (bf16)p;
+          db[r >> 3][r & 7] = (bf16)ds;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          pds[0][kb][s][lane] = pb[s];
+          pds[1][kb][s][lane] = db[s];
+        }
+      }
+      barrier_lds();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 p0 = pds[0][0][s][lane], p1 = pds[0][1][s][lane];
+        const bf16x8 s0 = pds[1][0][s][lane], s1 = pds[1][1][s][lane];
+#pragma unroll
+        for (int d = 0; d < DBW; ++d) {
+          const bf16x8 ado = trf.read(dOs[buf], 16 * s, dsl + d);
+          dvacc[0][d] = mfma32(ado, p0, dvacc[0][d]);
+          dvacc[1][d] = mfma32(ado, p1, dvacc[1][d]);
+          const bf16x8 aq = trf.read(Qs[buf], 16 * s, dsl + d);
+          dkacc[0][d] = mfma32(aq, s0, dkacc[0][d]);
+          dkacc[1][d] = mfma32(aq, s1, dkacc[1][d]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // dV^T / dK^T blocks: lane = key j0 + 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int key = j0 + 32 * x + ln;
+    const bool wr = a.packed ? key < len : key < a.S;
+    if (!wr) continue;
+    bf16* pk = a.dk + b * a.dk_sb + (int64_t)(off + key) * a.dk_ss + g * a.dk_sh + 4 * g2;
+    bf16* pv = a.dv + b * a.dv_sb + (int64_t)(off + key) * a.dv_ss + g * a.dv_sh + 4 * g2;
+    const float sc = a.scale;
+#pragma unroll
+    for (int d = 0; d < DBW; ++d)
+#pragma unroll
+      for (int qa = 0; qa < 4; ++qa) {
+        const int col = 32 * (dsl + d) + 8 * qa;
+        stg4(pk + col, dkacc[x][d][4 * qa] * sc, dkacc[x][d][4 * qa + 1] * sc, dkacc[x][d][4 * qa + 2] * sc,
+             dkacc[x][d][4 * qa + 3] * sc);
+        stg4(pv + col, dvacc[x][d][4 * qa], dvacc[x][d][4 * qa + 1], dvacc[x][d][4 * qa + 2], dvacc[x][d][4 * qa + 3]);
+      }
+  }
+}
+
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
+  const dim3 grid(8 * a.per_xcd), block(256);
+  if (D == 512)
+    hipLaunchKernelGGL(bwd_dkdv_kernel<512>, grid, block, 0, stream, a);
+  else if (D == 256)
+    hipLaunchKernelGGL(bwd_dkdv_kernel<256>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a) {
+  constexpr int M = kDqRows;    // 64 query rows per workgroup
+  constexpr int NK = kDqKeys;   // 32 keys per step
+  constexpr int KS = D / 16;
+  constexpr int DBW = D / 128;
+  static_assert(M == 64 && NK == 32, "role split assumes two row blocks and one key block");
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][NK * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][NK * D];
+  __shared__ __attribute__((aligned(16))) float xdp[2][16][64];      // dP^T of row block qb
+  __shared__ __attribute__((aligned(16))) bf16x8 dsb[2][2][64];      // dS^T: [qb][s][lane]
+
+  const int item = xcd_item(a.per_xcd, a.total_items);
+  if (item < 0) return;
+  const int unit = item / a.nqt;
+  const int qt = a.nqt - 1 - (item - unit * a.nqt);
+  const int hb = unit % a.nhb;
+  const int g = (unit / a.nhb) % a.Hkv;
+  const int b = unit / (a.nhb * a.Hkv);
+  int len = a.seq_len ? a.seq_len[b] : a.S;
+  len = min(max(len, 0), a.S);
+  const int off = a.seq_off ? a.seq_off[b] : 0;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g2 = lane >> 5, ln = lane & 31;
+  const bool score_wave = wave < 2;
+  const int qb = wave & 1;
+  const int dsl = wave * DBW;
+  const int p0 = qt * a.mpos;
+
+  // this lane's query row as the B-operand column of row block qb
+  const int R = 32 * qb + ln;
+  const int hh = R / a.mpos;
+  const int pos = p0 + (R - hh * a.mpos);
+  const int h = g * a.r + hb * a.hpt + hh;
+  const bool row_ok = pos < len;
+  const int prow = min(pos, max(len - 1, 0));
+
+  f32x16 dqacc[2][DBW];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int d = 0; d < DBW; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[x][d][r] = 0.f;
+
+  const int plast = min(p0 + a.mpos, len) - 1;
+  const int jhi = (plast < p0) ? 0 : (a.causal ? plast + 1 : len);
+  const int jlo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
+  const int t_lo = jlo / NK;
+  const int t_hi = jhi > jlo ? (jhi + NK - 1) / NK : t_lo;
+
+  if (t_lo < t_hi) {
+    bf16x8 qd[KS];
+    {
+      const bf16* src = score_wave ? a.q + b * a.q_sb + (int64_t)(off + prow) * a.q_ss + h * a.q_sh
+                                   : a.dout + b * a.do_sb + (int64_t)(off + prow) * a.do_ss + h * a.do_sh;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const bf16x8 x = ldg8(src + 16 * t + 8 * g2);
+        qd[t] = row_ok ? x : zero_bf16x8();
+      }
+    }
+    float lse2 = 0.f, dl = 0.f;
+    if (score_wave && row_ok) {
+      const int64_t si = b * a.st_sb + h * a.st_sh + off + pos;
+      lse2 = a.lse[si] * kLog2e;
+      dl = a.delta[si];
+    }
+    const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh;
+    const bf16* vbase = a.v + b * a.v_sb + (int64_t)off * a.v_ss + g * a.v_sh;
+    const RowFrags<D> rowf(lane);
+    const TrFrags<D> trf(lane);
+    const float c = a.c;
+
+    dma_rows<D, NK, 4>(Ks[0], kbase, a.k_ss, t_lo * NK, len - 1, wave, lane);
+    dma_rows<D, NK, 4>(Vs[0], vbase, a.v_ss, t_lo * NK, len - 1, wave, lane);
+    for (int jt = t_lo; jt < t_hi; ++jt) {
+      const int buf = (jt - t_lo) & 1;
+      const int j0 = jt * NK;
+      wait_vmcnt<0>();
+      barrier_lds();  // tile jt is in LDS; every wave is done with tile jt-1
+      if (jt + 1 < t_hi) {
+        dma_rows<D, NK, 4>(Ks[buf ^ 1], kbase, a.k_ss, j0 + NK, len - 1, wave, lane);
+        dma_rows<D, NK, 4>(Vs[buf ^ 1], vbase, a.v_ss, j0 + NK, len - 1, wave, lane);
+      }
+      f32x16 sacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      {
+        const bf16* src = score_wave ? Ks[buf] : Vs[buf];
+        bf16x8 f[3];
+        f[0] = rowf.read(src, 0, 0);
+        f[1] = rowf.read(src, 0, 1);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          if (t + 2 < KS) f[(t + 2) % 3] = rowf.read(src, 0, t + 2);
+          sacc = mfma32(f[t % 3], qd[t], sacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // sacc: lane = query row R, register r = key j0 + 8 (r/4) + 4 g2 + r%4
+      if (!score_wave) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xdp[qb][r][lane] = sacc[r];
+      }
+      barrier_lds();
+      if (score_wave) {
+        const bool full = (p0 + a.mpos <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= p0) &&
+                          (a.window <= 0 || j0 > plast - a.window);
+        bf16x8 db[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          const bool vis = full || key_visible(pos, key, len, a.causal, a.window);
+          const float p = vis ? fast_exp2(fmaf(sacc[r], c, -lse2)) : 0.f;
+          const float ds = vis ? p * (xdp[qb][r][lane] - dl) : 0.f;
+          db[r >> 3][r & 7] = (bf16)ds;
+        }
+        dsb[qb][0][lane] = db[0];
+        dsb[qb][1][lane] = db[1];
+      }
+      barrier_lds();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 b0 = dsb[0][s][lane], b1 = dsb[1][s][lane];
+#pragma unroll
+        for (int d = 0; d < DBW; ++d) {
+          const bf16x8 ak = trf.read(Ks[buf], 16 * s, dsl + d);
+          dqacc[0][d] = mfma32(ak, b0, dqacc[0][d]);
+          dqacc[1][d] = mfma32(ak, b1, dqacc[1][d]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // dQ^T blocks: lane = row 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int Rx = 32 * x + ln;
+    const int hx = Rx / a.mpos;
+    const int px = p0 + (Rx - hx * a.mpos);
+    const int hq = g * a.r + hb * a.hpt + hx;
+    const bool wr = a.packed ? px < len : px < a.S;
+    if (!wr) continue;
+    bf16* pq = a.out + b * a.dq_sb + (int64_t)(off + px) * a.dq_ss + hq * a.dq_sh + 4 * g2;
+    const float sc = a.scale;
+#pragma unroll
+    for (int d = 0; d < DBW; ++d)
+#pragma unroll
+      for (int qa = 0; qa < 4; ++qa)
+        stg4(pq + 32 * (dsl + d) + 8 * qa, dqacc[x][d][4 * qa] * sc, dqacc[x][d][4 * qa + 1] * sc,
+             dqacc[x][d][4 * qa + 2] * sc, dqacc[x][d][4 * qa + 3] * sc);
+  }
+}
+
+hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream) {
+  const dim3 grid(8 * a.per_xcd), block(256);
+  if (D == 512)
+    hipLaunchKernelGGL(bwd_dq_kernel<512>, grid, block, 0, stream, a);
+  else if (D == 256)
+    hipLaunchKernelGGL(bwd_dq_kernel<256>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace attn

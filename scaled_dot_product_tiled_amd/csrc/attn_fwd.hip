@@ -1,0 +1,262 @@
+// Fused causal grouped-query attention, forward: O = softmax(scale Q K^T + mask) V and
+// the row log-sum-exp, without materialising the score matrix.
+//
+// The computation is the one the page "Gemma4 FFPA attention backend support for
+// accelerating Gemma4-family training" routes head_dim=512 full-attention layers to
+// (section Integration) instead of the unfused path that builds the S x S matrix
+// (operator table, Debugging notes).
+//
+// Workgroup = 4 waves = 128 query rows of one kv-head group: `hpt` query heads of the
+// group times `mpos` consecutive positions, so one K/V tile in LDS serves every head
+// that shares it (grouped-query sharing; the repeat-KV mapping of that page's
+// Debugging notes).  Each wave owns 32 rows:
+//   S^T (N keys x 32 rows) = K Q^T : A = K rows from LDS, B = the wave's Q rows held
+//                                   in registers for the whole key loop;
+//   O^T (D x 32 rows) += V^T P^T   : A = V read transposed from LDS, B = P^T straight
+//                                   from the S^T accumulator registers.
+// Queries sit in lanes, keys and head_dim in registers, so the row max and row sum are
+// in-register reductions plus one swap between the two wave halves.  K and V tiles are
+// copied memory -> LDS asynchronously; the next K tile loads while P V runs and the
+// next V tile while the next Q K^T runs.  Tiles wholly outside the causal / window /
+// length range are never visited; tiles that straddle an edge are masked.
+//
+// Softmax reference.  Exponentials are 2^(s - m) for a per-row reference m (log2
+// units) and the output is normalised by the sum of the same exponentials, which is
+// exact in real arithmetic for any m.  Two policies:
+//  * exact running maximum (head_dim 256): m is the maximum seen so far; when it grows,
+//    the accumulators are scaled by 2^(m_old - m_new).  The largest probability of the
+//    tile holding the row maximum is then exactly 1, so peaked rows (one key dominating)
+//    keep their dominant term exact in bf16.
+//  * fixed reference (head_dim 512): m is fixed from the first tile in which the row
+//    sees a key.  A tile whose row maximum exceeds m by more than kRefSlack would push
+//    the exponentials past 2^kRefSlack; then the whole workgroup raises its references
+//    to the maxima seen so far and restarts its key loop from the first tile.  The
+//    accumulators are never rescaled: at head_dim 512 they fill the matrix-core
+//    accumulator registers and are only ever written by MFMA or cleared.  The dominant
+//    probability is 2^(s_max - m) rounded to bf16, a relative error of at most 2^-9.
+// A row that has seen no key yet uses m = 0 (its exponentials are all 2^-inf = 0).
+#include "device_common.h"
+#include "kernel_args.h"
+
+namespace attn {
+
+constexpr float kRefSlack = 32.0f;
+
+template <int D, int N, bool EXACT>
+__global__ __launch_bounds__(256, 1) void fwd_kernel(AttnArgs a) {
+  constexpr int NKB = N / 32;  // 32-key blocks per tile
+  constexpr int NS = N / 16;   // 16-key steps per tile
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NDMA = dma_rows_per_wave<D, N, 4>();
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[N * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[N * D];
+  __shared__ int restart_flag[2][4];
+
+  const int item = xcd_item(a.per_xcd, a.total_items);
+  if (item < 0) return;
+  const int unit = item / a.nqt;
+  const int qt = a.nqt - 1 - (item - unit * a.nqt);  // longest causal rows first
+  const int hb = unit % a.nhb;
+  const int g = (unit / a.nhb) % a.Hkv;
+  const int b = unit / (a.nhb * a.Hkv);
+  int len = a.seq_len ? a.seq_len[b] : a.S;
+  len = min(max(len, 0), a.S);
+  const int off = a.seq_off ? a.seq_off[b] : 0;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g2 = lane >> 5, ln = lane & 31;
+  const int R = wave * 32 + ln;
+  const int hh = R / a.mpos;
+  const int p0 = qt * a.mpos;
+  const int pos = p0 + (R - hh * a.mpos);
+  const int h = g * a.r + hb * a.hpt + hh;
+
+  bf16x8 qreg[KS];
+  {
+    // Rows past the length read a valid row (never past the tensor) and are zeroed.
+    const int prow = min(pos, max(len - 1, 0));
+    const bf16* qp = a.q + b * a.q_sb + (int64_t)(off + prow) * a.q_ss + h * a.q_sh + 8 * g2;
+    const bool ok = pos < len;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const bf16x8 x = ldg8(qp + 16 * t);
+      qreg[t] = ok ? x : zero_bf16x8();
+    }
+  }
+
+  const int plast = min(p0 + a.mpos, len) - 1;
+  const int jhi = (plast < p0) ? 0 : (a.causal ? plast + 1 : len);
+  const int jlo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
+  const int t_lo = jlo / N;
+  const int t_hi = jhi > jlo ? (jhi + N - 1) / N : t_lo;
+
+  const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh;
+  const bf16* vbase = a.v + b * a.v_sb + (int64_t)off * a.v_ss + g * a.v_sh;
+  const RowFrags<D> rowf(lane);
+  const TrFrags<D> trf(lane);
+  const float c = a.c;
+
+  f32x16 oacc[DB];
+  float m_ref = -INFINITY, l_run = 0.f;
+  bool restart = true;
+  while (restart) {
+    restart = false;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+    l_run = 0.f;
+    if (t_lo < t_hi) {
+      dma_rows<D, N, 4>(Ks, kbase, a.k_ss, t_lo * N, len - 1, wave, lane);
+      dma_rows<D, N, 4>(Vs, vbase, a.v_ss, t_lo * N, len - 1, wave, lane);
+    }
+    for (int jt = t_lo; jt < t_hi; ++jt) {
+      const int j0 = jt * N;
+      const bool has_next = jt + 1 < t_hi;
+      wait_vmcnt<NDMA>();  // K(jt) has landed; V(jt) may still be in flight
+      barrier_lds();
+
+      f32x16 sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      {
+        // K fragments are read two steps ahead of the matrix core; the schedule barrier
+        // keeps the compiler from hoisting every read (and its registers) to the top.
+        bf16x8 kf[3][NKB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = rowf.read(Ks, kb * 32, t);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          if (t + 2 < KS) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kf[(t + 2) % 3][kb] = rowf.read(Ks, kb * 32, t + 2);
+          }
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32(kf[t % 3][kb], qreg[t], sacc[kb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      barrier_lds();  // every wave is done with Ks
+      if (has_next) dma_rows<D, N, 4>(Ks, kbase, a.k_ss, j0 + N, len - 1, wave, lane);
+
+      const bool need_mask = (j0 + N > len) || (p0 + a.mpos > len) || (a.causal && j0 + N - 1 > p0) ||
+                             (a.window > 0 && j0 <= plast - a.window);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+            if (!key_visible(pos, key, len, a.causal, a.window)) sacc[kb][r] = -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      mt = half_swap_max(mt) * c;
+      if constexpr (EXACT) {
+        const float mnew = fmaxf(m_ref, mt);
+        const bool need = mnew > m_ref;
+        if (__any(need)) {
+          const float alpha = need ? fast_exp2(m_ref - mnew) : 1.0f;  // 2^-inf = 0 for a first key
+          m_ref = mnew;
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
+        }
+        if (has_next)
+          wait_vmcnt<NDMA>();  // V(jt) has landed; K(jt+1) may still be in flight
+        else
+          wait_vmcnt<0>();
+        barrier_lds();
+      } else {
+        // A row's first visible keys fix its reference (its accumulators are still zero).
+        if (m_ref == -INFINITY) m_ref = mt;
+        const bool need = mt > m_ref + kRefSlack;
+        const bool wave_need = __any(need);
+        if (lane == 0) restart_flag[jt & 1][wave] = wave_need ? 1 : 0;
+
+        if (has_next)
+          wait_vmcnt<NDMA>();  // V(jt) has landed; K(jt+1) may still be in flight
+        else
+          wait_vmcnt<0>();
+        barrier_lds();
+        if (restart_flag[jt & 1][0] | restart_flag[jt & 1][1] | restart_flag[jt & 1][2] |
+            restart_flag[jt & 1][3]) {
+          m_ref = fmaxf(m_ref, mt);
+          restart = true;
+          wait_vmcnt<0>();
+          barrier_lds();  // no wave still reads Ks / Vs before they are refilled
+          break;
+        }
+      }
+
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[kb][r], c, -m_use));  // masked: 2^-inf = 0
+          sacc[kb][r] = p;
+          rs += p;
+        }
+      l_run += half_swap_sum(rs);
+      {
+        bf16x8 pb[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[s][e] = (bf16)sacc[s >> 1][8 * (s & 1) + e];
+        // V^T fragments in (d block, key step) order, read two ahead of the matrix core.
+        constexpr int NF = DB * NS;
+        bf16x8 vf[3];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) vf[f] = trf.read(Vs, 16 * (f % NS), f / NS);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f + 2 < NF) vf[(f + 2) % 3] = trf.read(Vs, 16 * ((f + 2) % NS), (f + 2) / NS);
+          oacc[f / NS] = mfma32(vf[f % 3], pb[f % NS], oacc[f / NS]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      barrier_lds();  // every wave is done with Vs
+      if (has_next) dma_rows<D, N, 4>(Vs, vbase, a.v_ss, j0 + N, len - 1, wave, lane);
+    }
+  }
+
+  const bool wrow = a.packed ? (pos < len) : (pos < a.S);
+  if (wrow) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    bf16* op = a.out + b * a.o_sb + (int64_t)(off + pos) * a.o_ss + h * a.o_sh + 4 * g2;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int qa = 0; qa < 4; ++qa)
+        stg4(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv, oacc[d][4 * qa + 2] * inv,
+             oacc[d][4 * qa + 3] * inv);
+    if (g2 == 0)
+      a.lse[b * a.st_sb + h * a.st_sh + off + pos] = l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : 0.f;
+  }
+}
+
+hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream) {
+  const dim3 grid(8 * a.per_xcd), block(256);
+  if (D == 512)
+    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false>), grid, block, 0, stream, a);
+  else if (D == 256)
+    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true>), grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,185 @@
+// Device-side building blocks shared by the libattn kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, one wave of 64 lanes):
+//   A operand (32 x 16): lane l holds row (l % 32), 8 consecutive k of group (l / 32)
+//   B operand (16 x 32): lane l holds column (l % 32), the same 8 k of group (l / 32)
+//   C/D (32 x 32, 16 fp32 per lane): register r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+//   column l % 32.
+// Only the C layout matters for correctness below: A and B always take the same
+// (lane group, element) -> k assignment, so any such assignment sums the same products.
+//
+// LDS tiles hold rows of D bf16 with no padding.  The 16-byte chunk c of row r is stored
+// at chunk position c ^ h(r), h(r) = 4 (r & 3) + ((r >> 2) & 3).  With 64 four-byte
+// banks, one pass of a 16-byte-per-lane read serves 16 lanes and one pass of an
+// 8-byte-per-lane read serves 32 lanes; h makes both access patterns used here
+// conflict-free: 16 consecutive rows at one chunk (row fragments), and 4 consecutive
+// rows x 4 consecutive chunks (transposing reads).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+// A running row maximum is only raised when a new score exceeds it by more than
+// this many powers of two; exponentials then stay below 2^8, exact in fp32 and
+// rounded relative to their own size in bf16.  The normaliser uses the same
+// reference value, so the result is unchanged in exact arithmetic.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of this lane's partner in the other half of the wave (lane ^ 32), combined.
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ constexpr int swz_h(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// Element offset of (row, col) in a swizzled tile of D columns.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * D + (((col >> 3) ^ swz_h(row)) << 3) + (col & 7);
+}
+
+// Row fragments for the MFMA operand "row (lane % 32), k chunk 2t + (lane / 32)" of a
+// tile whose row block starts at a multiple of 16: the byte offset is one of eight
+// lane-dependent bases (t & 7) plus a constant, so a fully unrolled loop needs eight
+// address registers and immediate offsets.
+template <int D>
+struct RowFrags {
+  int base[8];
+  __device__ __forceinline__ explicit RowFrags(int lane) {
+    const int ln = lane & 31, g2 = lane >> 5;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) base[q] = ln * D * 2 + 16 * ((2 * q + g2) ^ swz_h(ln));
+  }
+  // rows rblk + lane % 32 (rblk a multiple of 16), k step t (columns 16t .. 16t+15)
+  __device__ __forceinline__ bf16x8 read(const bf16* tile, int rblk, int t) const {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + base[t & 7] +
+                                            rblk * D * 2 + 256 * (t >> 3));
+  }
+};
+
+// Transposing fragments of a row-major tile T (rows = contraction index k): read(kbase,
+// db) returns, for lane l with g = l / 32, T[kbase + 4g + e][32 db + l%32] for e = 0..3
+// and T[kbase + 8 + 4g + e - 4][32 db + l%32] for e = 4..7.  This is the k order in
+// which a C-layout accumulator over the same 16 rows feeds a B operand.  kbase is a
+// multiple of 16.
+template <int D>
+struct TrFrags {
+  int base[8];  // [half][db & 3]
+  __device__ __forceinline__ explicit TrFrags(int lane) {
+    const int G = lane >> 4, i = lane & 15;
+    const int rl = 4 * (G >> 1) + (i >> 2);
+    const int u = 2 * (G & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        base[4 * hf + x] = (rl + 8 * hf) * D * 2 + 16 * ((4 * x + u) ^ swz_h(rl + 8 * hf)) + 8 * (i & 1);
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16* tile, int kbase, int db) const {
+    const char* t = reinterpret_cast<const char*>(tile) + kbase * D * 2 + 256 * (db >> 2);
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(t + base[db & 3]));
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(t + base[4 + (db & 3)]));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+// Asynchronous copy of ROWS rows (row r from g + min(row0 + r, rowmax) * stride elements)
+// into a swizzled LDS tile, straight from memory to LDS.  Each wave-instruction moves 1 KB
+// (64 lanes x 16 bytes) to consecutive LDS; wave `wave` of NW issues instructions wave,
+// wave+NW, ...  The row pointer of an instruction is wave-uniform, so each lane only
+// carries a 32-bit offset.  Nothing is waited for here: the caller waits with wait_vmcnt
+// and a barrier.  `wave` must be wave-uniform, row0 <= rowmax.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(bf16* tile, const bf16* g, int64_t stride, int row0,
+                                         int rowmax, int wave, int lane) {
+  constexpr int CH = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;   // rows per wave-instruction
+  constexpr int NI = ROWS / RPI;
+  static_assert(CH >= 16 && 64 % CH == 0, "row must be 256..1024 bytes");
+  static_assert(NI % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int k = 0; k < NI / NW; ++k) {
+    const int i = wave + k * NW;
+    const int brow = min(row0 + i * RPI, rowmax);                 // wave-uniform
+    const int trow = i * RPI + lane / CH;                         // row within the tile
+    const int lrow = min(row0 + trow, rowmax);
+    const uint32_t voff = (uint32_t)((int64_t)(lrow - brow) * stride * 2) +
+                          (uint32_t)(16 * ((lane % CH) ^ swz_h(trow)));
+    const char* src = reinterpret_cast<const char*>(g + (int64_t)brow * stride) + voff;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(tile + i * RPI * D), 16, 0, 0);
+  }
+}
+
+template <int D, int ROWS, int NW>
+constexpr int dma_rows_per_wave() { return ROWS * D / 512 / NW; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that first retires this wave's outstanding LDS reads, so that a
+// buffer may be refilled by any wave once every wave has passed it.  Global loads in
+// flight are not waited for.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 ldg8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ void stg4(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  v[2] = (bf16)c;
+  v[3] = (bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+
+// Work-item order: consecutive workgroup ids land on consecutive XCDs (id % 8), so
+// the items of one XCD are taken from one contiguous range of the item list; items
+// that share K/V then share that XCD's L2.
+__device__ __forceinline__ int xcd_item(int per_xcd, int total) {
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int item = xcd * per_xcd + slot;
+  return (slot < per_xcd && item < total) ? item : -1;
+}
+
+__device__ __forceinline__ bool key_visible(int i, int j, int len, int causal, int window) {
+  return (i < len) & (j < len) & ((!causal) | (j <= i)) & ((window <= 0) | (j > i - window));
+}
+
+}  // namespace attn

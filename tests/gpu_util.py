@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU parity tests: moving seeded bf16 bit patterns to the device
+and back, the tolerance measures, and one-call wrappers around the library binding."""
+import numpy as np
+import torch
+
+from synth import bf16_bits_to_f64
+
+# Tolerances for floating-point results (bf16 inputs and outputs, fp32 accumulation).
+O_MAX_ABS = 2e-2        # forward output and decode output, max |gpu - oracle| over valid rows
+GRAD_REL_L2 = 5e-2      # dQ, dK, dV: ||gpu - oracle||_2 / ||oracle||_2 over valid rows
+LSE_MAX_ABS = 1e-2      # row log-sum-exp (fp32 output)
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bfloat16 tensor on cuda:0 (same bytes)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to("cuda:0").view(torch.bfloat16)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """bf16 / fp32 device tensor -> float64 numpy (exact)."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f64(host_bits(t))
+    return t.detach().cpu().double().numpy()
+
+
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+
+
+def rel_l2(a, b) -> float:
+    a, b = np.asarray(a), np.asarray(b)
+    den = float(np.linalg.norm(b))
+    return float(np.linalg.norm(a - b)) / den if den > 0 else float(np.linalg.norm(a))
+
+
+def all_finite(*ts) -> bool:
+    for t in ts:
+        if isinstance(t, torch.Tensor):
+            if not bool(torch.isfinite(t.float()).all()):
+                return False
+        elif not np.isfinite(t).all():
+            return False
+    return True

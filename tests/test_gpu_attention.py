@@ -1,0 +1,271 @@
+"""GPU parity of the HIP forward and backward against the float64 oracle, through the C ABI.
+
+Every input is a seeded bf16 draw from `synth`; the same bytes go to the GPU and the oracle.
+Small cases compare every element; the full-size workloads compare sampled query rows (computed
+one by one by the oracle) and one complete (batch, kv-head) unit for dK and dV.  Tolerances:
+O max-abs 2e-2, dQ/dK/dV relative L2 5e-2, LSE max-abs 1e-2; padded rows and keys must be exact
+zeros and every output finite.  Bit-exact properties (masks, indexing, padding) are checked on
+raw output bytes.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import (ATTN_WORKLOADS, AttnWorkload, bf16_bits_to_f64, lengths_to_cu_seqlens, lengths_to_pad_mask,
+                   make_attention_inputs, pack_rows)
+from tests.gpu_util import GRAD_REL_L2, LSE_MAX_ABS, O_MAX_ABS, all_finite, dev, host, host_bits, max_abs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+import scaled_dot_product_tiled_amd as sdpt  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w: AttnWorkload, inp: dict, varlen=None, want_bwd=True):
+    """Runs attn_fwd (+ attn_bwd) on the workload's inputs; returns device tensors."""
+    q, k, v, do = (dev(inp[x]) for x in ("q", "k", "v", "do"))
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window)
+    if varlen == "pad_mask":
+        kw["pad_mask"] = torch.from_numpy(inp["pad_mask"]).to("cuda:0")
+    o, lse = sdpt.attn_fwd(q, k, v, **kw)
+    out = {"q": q, "k": k, "v": v, "do": do, "o": o, "lse": lse}
+    if want_bwd:
+        out["dq"], out["dk"], out["dv"] = sdpt.attn_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_full(w, inp, lengths=None):
+    q, k, v, do = (bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
+    o, lse = oracle.attention_forward(q, k, v, w.scale, w.causal, w.window, lengths)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, w.scale, w.causal, w.window, lengths)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def check_full(w, got, ref, lengths=None):
+    L = [w.S] * w.B if lengths is None else list(lengths)
+    go, gl = host(got["o"]), host(got["lse"])
+    gq, gk, gv = host(got["dq"]), host(got["dk"]), host(got["dv"])
+    assert all_finite(go, gl, gq, gk, gv)
+    valid_o = np.concatenate([go[b, :L[b]] for b in range(w.B)])
+    ref_o = np.concatenate([ref["o"][b, :L[b]] for b in range(w.B)])
+    assert max_abs(valid_o, ref_o) <= O_MAX_ABS, max_abs(valid_o, ref_o)
+    lse_err = max(max_abs(gl[b, :, :L[b]], ref["lse"][b, :, :L[b]]) for b in range(w.B))
+    assert lse_err <= LSE_MAX_ABS, lse_err
+    for name, gt in (("dq", gq), ("dk", gk), ("dv", gv)):
+        a = np.concatenate([gt[b, :L[b]] for b in range(w.B)])
+        r = np.concatenate([ref[name][b, :L[b]] for b in range(w.B)])
+        err = rel_l2(a, r)
+        assert err <= GRAD_REL_L2, (name, err)
+    # padded rows and keys are exact zeros
+    for b in range(w.B):
+        for t in (got["o"], got["dq"], got["dk"], got["dv"]):
+            assert not host_bits(t[b, L[b]:]).any()
+        assert not host_bits(got["lse"][b, :, L[b]:]).any()
+
+
+SMALL = [
+    # name, workload, lengths
+    ("tiny_d512", ATTN_WORKLOADS["tiny_d512"], None),
+    ("d512_gqa8_ragged", AttnWorkload(101, "d512 gqa8 ragged", 2, 300, 16, 2, 512), None),
+    ("d512_mha", AttnWorkload(102, "d512 mha", 1, 200, 2, 2, 512), None),
+    ("d512_noncausal", AttnWorkload(103, "d512 non-causal", 1, 257, 4, 1, 512, causal=False), None),
+    ("d256_window", AttnWorkload(104, "d256 window 200", 2, 700, 4, 2, 256, window=200, qk_std=3.0), None),
+    ("d256_window_gqa", AttnWorkload(105, "d256 window 1024 gqa", 1, 1100, 8, 1, 256, window=1024, qk_std=3.0),
+     None),
+    ("d512_varlen_pad", AttnWorkload(106, "d512 varlen", 3, 333, 8, 2, 512, varlen="pad_mask"), [333, 1, 150]),
+    ("d512_varlen_empty", AttnWorkload(107, "d512 varlen empty", 3, 300, 4, 1, 512, varlen="pad_mask"),
+     [0, 77, 300]),
+    ("d256_varlen_window", AttnWorkload(108, "d256 varlen window", 2, 500, 4, 2, 256, window=64,
+                                        varlen="pad_mask"), [500, 260]),
+]
+
+
+@pytest.mark.parametrize("name,w,lengths", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_match_oracle(name, w, lengths):
+    say(f"[case {name}] B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} causal={w.causal} W={w.window}")
+    inp = make_attention_inputs(w, seed=0)
+    if lengths is not None:
+        inp["lengths"] = np.array(lengths, dtype=np.int32)
+        inp["pad_mask"] = lengths_to_pad_mask(inp["lengths"], w.S)
+    got = run_gpu(w, inp, varlen=w.varlen)
+    ref = oracle_full(w, inp, inp["lengths"] if lengths is not None else None)
+    check_full(w, got, ref, lengths)
+
+
+def test_packed_cu_seqlens_matches_oracle_and_pad_mask():
+    w = AttnWorkload(109, "d512 packed", 3, 333, 8, 2, 512)
+    lengths = np.array([333, 1, 150], dtype=np.int32)
+    say("[case packed cu_seqlens]")
+    inp = make_attention_inputs(w, seed=1)
+    cu = lengths_to_cu_seqlens(lengths)
+    pk = {x: pack_rows(inp[x], lengths) for x in ("q", "k", "v", "do")}
+    q, k, v, do = (dev(pk[x]) for x in ("q", "k", "v", "do"))
+    cu_d = torch.from_numpy(cu).to("cuda:0")
+    kw = dict(scale=w.scale, causal=True, window=0, cu_seqlens=cu_d, max_seqlen=int(lengths.max()))
+    o, lse = sdpt.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = sdpt.attn_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    f = {x: bf16_bits_to_f64(pk[x]) for x in pk}
+    ro, rl = oracle.attention_forward_packed(f["q"], f["k"], f["v"], cu, w.scale, True, 0)
+    rq, rk, rv = oracle.attention_backward_packed(f["q"], f["k"], f["v"], f["do"], cu, w.scale, True, 0)
+    assert all_finite(o, lse, dq, dk, dv)
+    assert max_abs(host(o), ro) <= O_MAX_ABS
+    assert max_abs(host(lse), rl) <= LSE_MAX_ABS
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        assert rel_l2(host(a), r) <= GRAD_REL_L2
+    # the packed layout computes the same bytes as the padded layout with a mask
+    inp["pad_mask"] = lengths_to_pad_mask(lengths, w.S)
+    got = run_gpu(w.scaled(varlen="pad_mask"), inp, varlen="pad_mask")
+    for t_pk, t_pad in ((o, got["o"]), (dq, got["dq"]), (dk, got["dk"]), (dv, got["dv"])):
+        assert np.array_equal(host_bits(t_pk), pack_rows(host_bits(t_pad), lengths))
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: sampled rows + one complete (batch, kv head) unit
+# ---------------------------------------------------------------------------
+def _full_size_check(w, inp, lengths, units, row_samples, seed=0):
+    say(f"[full {w.name}] running GPU")
+    got = run_gpu(w, inp, varlen=w.varlen)
+    assert all_finite(got["o"], got["lse"], got["dq"], got["dk"], got["dv"]), "non-finite output"
+    q, k, v, do = (bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
+    rng = np.random.default_rng(seed)
+    for (b, h) in row_samples:
+        n = w.S if lengths is None else int(lengths[b])
+        rows = np.unique(np.concatenate([[0, 1, n - 1], rng.integers(0, max(n, 1), size=61)]))
+        say(f"[full {w.name}] oracle rows b={b} h={h} ({len(rows)} rows)")
+        ro, rl, rq = oracle.attention_rows(q, k, v, do, b, h, rows, w.scale, w.causal, w.window, lengths)
+        go = host(got["o"][b, rows, h])
+        gl = host(got["lse"][b, h, rows])
+        gq = host(got["dq"][b, rows, h])
+        assert max_abs(go, ro) <= O_MAX_ABS
+        assert max_abs(gl, rl) <= LSE_MAX_ABS
+        assert rel_l2(gq, rq) <= GRAD_REL_L2
+    for (b, g) in units:
+        say(f"[full {w.name}] oracle unit b={b} g={g}")
+        rq, rk, rv = oracle.attention_backward_group(q, k, v, do, b, g, w.scale, w.causal, w.window, lengths)
+        n = w.S if lengths is None else int(lengths[b])
+        r = w.r
+        assert rel_l2(host(got["dq"][b, :n, g * r:(g + 1) * r]), rq[:n]) <= GRAD_REL_L2
+        assert rel_l2(host(got["dk"][b, :n, g]), rk[:n]) <= GRAD_REL_L2
+        assert rel_l2(host(got["dv"][b, :n, g]), rv[:n]) <= GRAD_REL_L2
+        assert not host_bits(got["dk"][b, n:, g]).any() and not host_bits(got["dv"][b, n:, g]).any()
+
+
+def test_full_size_d512_causal_gqa():
+    w = ATTN_WORKLOADS["full_d512"]
+    inp = make_attention_inputs(w, seed=0)
+    _full_size_check(w, inp, None, units=[(1, 3)], row_samples=[(0, 0), (1, 31), (0, 17)])
+
+
+def test_full_size_d256_sliding_window():
+    w = ATTN_WORKLOADS["window_d256"]
+    inp = make_attention_inputs(w, seed=0)
+    _full_size_check(w, inp, None, units=[(0, 5), (1, 15)], row_samples=[(0, 0), (1, 31), (1, 10)])
+
+
+def test_full_size_d512_varlen_pad_mask():
+    w = ATTN_WORKLOADS["varlen_d512"]
+    inp = make_attention_inputs(w, seed=0)
+    L = inp["lengths"]
+    say(f"[full varlen] lengths {L.tolist()}")
+    bshort = int(np.argmin(L))
+    blong = int(np.argmax(L))
+    _full_size_check(w, inp, L, units=[(bshort, 2)], row_samples=[(blong, 5), (bshort, 30)])
+
+
+# ---------------------------------------------------------------------------
+# Bit-exact properties
+# ---------------------------------------------------------------------------
+def test_rows_that_cannot_see_a_key_ignore_it():
+    w = AttnWorkload(110, "row invariance", 1, 260, 4, 2, 512)
+    inp = make_attention_inputs(w, seed=2)
+    base = run_gpu(w, inp, want_bwd=False)
+    j = 130
+    inp2 = {x: (inp[x].copy() if isinstance(inp[x], np.ndarray) else inp[x]) for x in inp}
+    inp2["k"][0, j] ^= np.uint16(0x0040)   # flip a mantissa bit (finite)
+    inp2["v"][0, j] ^= np.uint16(0x0040)
+    pert = run_gpu(w, inp2, want_bwd=False)
+    ob, op = host_bits(base["o"]), host_bits(pert["o"])
+    assert np.array_equal(ob[0, :j], op[0, :j])          # rows before the key: identical bytes
+    assert not np.array_equal(ob[0, j:], op[0, j:])       # rows after it: changed
+    # window: rows i >= j + W cannot see key j either
+    ww = AttnWorkload(111, "row invariance window", 1, 260, 2, 1, 256, window=40)
+    inp = make_attention_inputs(ww, seed=3)
+    base = run_gpu(ww, inp, want_bwd=False)
+    inp["k"][0, j] ^= np.uint16(0x0040)
+    inp["v"][0, j] ^= np.uint16(0x0040)
+    pert = run_gpu(ww, inp, want_bwd=False)
+    ob, op = host_bits(base["o"]), host_bits(pert["o"])
+    assert np.array_equal(ob[0, :j], op[0, :j]) and np.array_equal(ob[0, j + 40:], op[0, j + 40:])
+
+
+def test_padding_poison_never_reaches_valid_outputs():
+    w = AttnWorkload(112, "poison", 3, 300, 8, 2, 512, varlen="pad_mask")
+    lengths = np.array([300, 37, 129], dtype=np.int32)
+    clean = make_attention_inputs(w, seed=4)
+    clean["lengths"] = lengths
+    clean["pad_mask"] = lengths_to_pad_mask(lengths, w.S)
+    pois = {x: (clean[x].copy() if isinstance(clean[x], np.ndarray) else clean[x]) for x in clean}
+    for b, n in enumerate(lengths):
+        for x in ("q", "k", "v", "do"):
+            pois[x][b, n:] = np.uint16(0x7FC0)
+    g1 = run_gpu(w, clean, varlen="pad_mask")
+    g2 = run_gpu(w, pois, varlen="pad_mask")
+    for x in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(host_bits(g1[x]) if g1[x].dtype == torch.bfloat16 else host(g1[x]),
+                              host_bits(g2[x]) if g2[x].dtype == torch.bfloat16 else host(g2[x])), x
+    assert all_finite(g2["o"], g2["lse"], g2["dq"], g2["dk"], g2["dv"])
+
+
+def test_gqa_forward_is_bytewise_mha_on_repeated_kv():
+    w = AttnWorkload(113, "gqa", 1, 256, 8, 2, 512)
+    inp = make_attention_inputs(w, seed=5)
+    g = run_gpu(w, inp, want_bwd=False)
+    wm = w.scaled(Hkv=8)
+    inp_m = dict(inp)
+    inp_m["k"] = np.repeat(inp["k"], 4, axis=2)
+    inp_m["v"] = np.repeat(inp["v"], 4, axis=2)
+    m = run_gpu(wm, inp_m, want_bwd=False)
+    assert np.array_equal(host_bits(g["o"]), host_bits(m["o"]))
+    assert np.array_equal(host(g["lse"]), host(m["lse"]))
+
+
+def test_zero_keys_give_log_visible_count_and_single_key_row_is_exact():
+    for w in (AttnWorkload(114, "k0 causal", 1, 300, 2, 1, 512),
+              AttnWorkload(115, "k0 window", 1, 300, 2, 1, 256, window=50)):
+        inp = make_attention_inputs(w, seed=6)
+        inp["k"][:] = 0
+        got = run_gpu(w, inp, want_bwd=False)
+        lse = host(got["lse"])[0]
+        i = np.arange(w.S)
+        cnt = i + 1 if w.window == 0 else np.minimum(i + 1, w.window)
+        assert np.max(np.abs(lse - np.log(cnt)[None, :])) < 2e-5
+        # causal row 0 sees only key 0: P = 1 exactly, O_0 = V_0 bit for bit
+        assert np.array_equal(host_bits(got["o"])[0, 0, 0], inp["v"][0, 0, 0])
+
+
+def test_outputs_are_deterministic():
+    w = AttnWorkload(116, "determinism", 2, 300, 8, 2, 512)
+    inp = make_attention_inputs(w, seed=7)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp)
+    for x in ("o", "dq", "dk", "dv"):
+        assert np.array_equal(host_bits(a[x]), host_bits(b[x])), x
+
+
+def test_peaked_softmax_with_reference_restarts():
+    # scores far apart (std 3 inputs, window edges with few keys) exercise the reference restart
+    w = AttnWorkload(117, "peaked", 1, 900, 4, 2, 256, window=100, qk_std=6.0)
+    inp = make_attention_inputs(w, seed=8)
+    got = run_gpu(w, inp)
+    ref = oracle_full(w, inp)
+    check_full(w, got, ref)

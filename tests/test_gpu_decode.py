@@ -1,0 +1,80 @@
+"""GPU parity of the paged decode against the float64 oracle, through the C ABI, plus the
+bit-exact page-gather properties: the same logical tokens in different pool pages give the same
+bytes, and unassigned pages or slots past the context (filled with NaN) are never read."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import DECODE_WORKLOADS, bf16_bits_to_f64, make_decode_inputs
+from tests.gpu_util import O_MAX_ABS, all_finite, dev, host, host_bits, max_abs
+
+pytestmark = pytest.mark.gpu
+
+import scaled_dot_product_tiled_amd as sdpt  # noqa: E402
+
+
+def run(inp, scale):
+    q, kc, vc = dev(inp["q"]), dev(inp["k_cache"]), dev(inp["v_cache"])
+    table = torch.from_numpy(inp["block_table"]).to("cuda:0")
+    ctx = torch.from_numpy(inp["ctx_lens"]).to("cuda:0")
+    o = sdpt.paged_decode(q, kc, vc, table, ctx, scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def ref(inp, scale):
+    return oracle.paged_decode(bf16_bits_to_f64(inp["q"]), bf16_bits_to_f64(inp["k_cache"]),
+                               bf16_bits_to_f64(inp["v_cache"]), inp["block_table"], inp["ctx_lens"], scale)
+
+
+def test_full_size_decode_matches_oracle():
+    w = DECODE_WORKLOADS["decode_d128"]
+    inp = make_decode_inputs(w, seed=0)
+    print(f"[decode full] B={w.B} pages={inp['num_pages']}", flush=True)
+    o = run(inp, w.scale)
+    assert all_finite(o)
+    assert max_abs(host(o), ref(inp, w.scale)) <= O_MAX_ABS
+
+
+@pytest.mark.parametrize("ctx", [[1, 15, 16, 17], [255, 256, 257, 4096], [0, 3, 511, 1000]])
+def test_ragged_contexts_match_oracle(ctx):
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=len(ctx))
+    inp = make_decode_inputs(w, seed=1, ctx_lens=np.array(ctx, dtype=np.int32))
+    print(f"[decode ctx {ctx}]", flush=True)
+    o = run(inp, w.scale)
+    r = ref(inp, w.scale)
+    assert all_finite(o)
+    assert max_abs(host(o), r) <= O_MAX_ABS
+    for b, n in enumerate(ctx):
+        if n == 0:
+            assert not host_bits(o[b]).any()
+
+
+def test_page_placement_and_unused_pages_do_not_change_bytes():
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=16)
+    inp = make_decode_inputs(w, seed=2)
+    pois = make_decode_inputs(w, seed=2, poison_unused=True)
+    o1 = host_bits(run(inp, w.scale))
+    o2 = host_bits(run(pois, w.scale))
+    assert np.array_equal(o1, o2)
+    # move every page to another pool slot and rewrite the table accordingly
+    perm = np.random.default_rng(3).permutation(inp["num_pages"])
+    moved = dict(inp)
+    inv = np.argsort(perm)
+    moved["k_cache"] = inp["k_cache"][inv]
+    moved["v_cache"] = inp["v_cache"][inv]
+    t = inp["block_table"]
+    moved["block_table"] = np.where(t >= 0, perm[np.maximum(t, 0)], -1).astype(np.int32)
+    o3 = host_bits(run(moved, w.scale))
+    assert np.array_equal(o1, o3)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (64, 8)])
+def test_other_group_ratios(Hq, Hkv):
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=5, Hq=Hq, Hkv=Hkv, ctx_range=(1, 700))
+    inp = make_decode_inputs(w, seed=4)
+    o = run(inp, w.scale)
+    assert max_abs(host(o), ref(inp, w.scale)) <= O_MAX_ABS

@@ -1,0 +1,106 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/attn.h declares,
+sizes workspaces, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from scaled_dot_product_tiled_amd.binding import AttnDecodeShape, AttnShape, AttnTensor, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    lib = load_library()
+    names = declared_functions()
+    assert {"attn_fwd", "attn_bwd", "paged_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    lib = load_library()
+    for s in range(5):
+        assert lib.attn_status_str(s)
+    assert lib.attn_version() == b"0.1.0"
+    assert lib.attn_last_hip_error() == 0
+
+
+def test_workspace_sizes():
+    lib = load_library()
+    s = AttnShape(2, 4096, 0, 32, 4, 512)
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(s), 0) == 0
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(s), 1) == 256       # 2 x B int32, rounded to 256 bytes
+    # backward: delta, one fp32 per (row, head)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0) == 2 * 4096 * 32 * 4
+    p = AttnShape(3, 100, 250, 8, 2, 256)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 2) == 256 + ((250 * 8 * 4 + 255) // 256) * 256
+    bad = AttnShape(1, 10, 0, 6, 4, 512)      # 6 % 4 != 0
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(bad), 0) == 0
+    d = AttnDecodeShape(64, 32, 8, 128, 16, 1000, 256)
+    assert lib.paged_decode_workspace_bytes(ctypes.byref(d)) == 64 * 32 * 16 * 130 * 4
+
+
+def _t(ptr=0x10000, sb=4096 * 32 * 512, ss=32 * 512, sh=512):
+    return AttnTensor(ptr, sb, ss, sh)
+
+
+def _fwd(lib, shape, q=None, scale=0.05, causal=1, window=0, cu=None, pm=None, lse=0x20000, ws=None, wsb=0):
+    q = q or _t()
+    return lib.attn_fwd(ctypes.byref(shape) if shape is not None else None, q, _t(), _t(), scale, causal, window,
+                        cu, pm, _t(), lse, ws, wsb, None)
+
+
+def test_argument_checks_happen_before_any_launch():
+    lib = load_library()
+    s = AttnShape(2, 64, 0, 8, 2, 512)
+    assert _fwd(lib, None) == INVALID
+    assert _fwd(lib, s, q=_t(ptr=0)) == INVALID                    # null pointer
+    assert _fwd(lib, s, q=_t(ptr=0x10008)) == INVALID              # not 16-byte aligned
+    assert _fwd(lib, s, q=_t(ss=100)) == INVALID                   # stride not a multiple of 8
+    assert _fwd(lib, s, lse=0) == INVALID
+    assert _fwd(lib, s, scale=0.0) == INVALID
+    assert _fwd(lib, s, scale=float("nan")) == INVALID
+    assert _fwd(lib, s, causal=0, window=16) == UNSUPPORTED       # window requires causal
+    assert _fwd(lib, s, window=-1) == INVALID
+    assert _fwd(lib, AttnShape(2, 64, 0, 8, 2, 128)) == UNSUPPORTED   # head_dim 128 is decode-only
+    assert _fwd(lib, AttnShape(2, 64, 0, 8, 3, 512)) == INVALID       # Hq % Hkv
+    assert _fwd(lib, s, cu=0x30000, pm=0x40000) == INVALID            # both varlen forms
+    assert _fwd(lib, s, pm=0x40000) == WORKSPACE                      # varlen needs metadata workspace
+    assert _fwd(lib, s, pm=0x40000, ws=0x50010, wsb=4096) == WORKSPACE  # misaligned workspace
+    assert _fwd(lib, AttnShape(0, 64, 0, 8, 2, 512)) == OK            # empty batch: nothing to do
+    assert lib.attn_last_hip_error() == 0
+
+
+def test_backward_and_decode_checks():
+    lib = load_library()
+    s = AttnShape(2, 64, 0, 8, 2, 512)
+    st = lib.attn_bwd(ctypes.byref(s), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, None, None,
+                      _t(), _t(), _t(), None, 0, None)
+    assert st == WORKSPACE
+    st = lib.attn_bwd(ctypes.byref(s), _t(), _t(), _t(), _t(), 0x20000, _t(ptr=0), 0.05, 1, 0, None, None,
+                      _t(), _t(), _t(), 0x100000, 1 << 20, None)
+    assert st == INVALID
+    d = AttnDecodeShape(4, 32, 8, 128, 16, 100, 8)
+    kc = AttnTensor(0x10000, 16 * 8 * 128, 8 * 128, 128)
+
+    def dec(shape, q=0x1000, table=0x2000, ws=0x100000, wsb=1 << 20):
+        return lib.paged_decode(ctypes.byref(shape), q, 32 * 128, 128, kc, kc, table, 0x3000, 0.1, 0x4000,
+                                32 * 128, 128, ws, wsb, None)
+    assert dec(AttnDecodeShape(4, 32, 8, 64, 16, 100, 8)) == UNSUPPORTED     # head_dim
+    assert dec(AttnDecodeShape(4, 32, 8, 128, 32, 100, 8)) == UNSUPPORTED    # page size
+    assert dec(AttnDecodeShape(4, 24, 8, 128, 16, 100, 8)) == UNSUPPORTED    # group ratio 3
+    assert dec(d, q=0) == INVALID
+    assert dec(d, table=0) == INVALID
+    assert dec(d, wsb=16) == WORKSPACE
+    assert dec(AttnDecodeShape(0, 32, 8, 128, 16, 100, 8)) == OK

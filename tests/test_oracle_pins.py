@@ -364,3 +364,20 @@ def test_oracle_finite_on_peaked_window_workload_slice():
     g = oracle.attention_backward(q, k, v, do, w.scale, True, w.window)
     for t in (o, lse, *g):
         assert np.isfinite(t).all()
+
+
+def test_row_sampled_oracle_equals_full_unit():
+    rng = np.random.default_rng(10)
+    B, S, Hq, Hkv, D = 2, 30, 4, 2, 8
+    q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    lengths = [30, 17]
+    o, lse = oracle.attention_forward(q, k, v, 0.4, True, 5, lengths)
+    dq, _, _ = oracle.attention_backward(q, k, v, do, 0.4, True, 5, lengths)
+    rows = [0, 3, 16, 17, 29]
+    for b in range(B):
+        for h in range(Hq):
+            ro, rl, rdq = oracle.attention_rows(q, k, v, do, b, h, rows, 0.4, True, 5, lengths)
+            np.testing.assert_allclose(ro, o[b, rows, h], atol=1e-13)
+            np.testing.assert_allclose(rl, lse[b, h, rows], atol=1e-13)
+            np.testing.assert_allclose(rdq, dq[b, rows, h], atol=1e-13)

@@ -1,0 +1,231 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+A step is one forward + backward of causal grouped-query attention, head_dim 512 (B=2, S=4096,
+Hq=32, Hkv=4, bf16, seeded N(0,1) inputs already resident in HBM): attn_fwd then attn_bwd through
+the C ABI.  Reported:
+  value     causal-counted TFLOP/s of the step: forward 4 D pairs, backward 2.5x that, where pairs =
+            visible (query, key) pairs summed over batch and heads (exact, not S^2/2);
+  roofline  for the dominant kernel, timed with HIP events on the stream it runs on;
+  decode    paged single-token decode (B=64, Hq=32, Hkv=8, D=128, 16-token pages, contexts
+            U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
+            bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
+  cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores.
+Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def causal_pairs(S, window=0):
+    i = np.arange(S, dtype=np.int64)
+    cnt = i + 1 if window <= 0 else np.minimum(i + 1, window)
+    return int(cnt.sum())
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--decode-steps", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-units", type=int, default=8, help="(batch, kv head) units the oracle times (of 8)")
+    return p.parse_args()
+
+
+def dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+def time_events(fn, iters, stream):
+    """Average milliseconds of fn() over iters calls, timed with HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(units):
+    """Times the float64 oracle (forward + backward of whole (batch, kv head) units) on the host."""
+    import oracle
+    from synth import ATTN_WORKLOADS, bf16_bits_to_f64, make_attention_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = ATTN_WORKLOADS["full_d512"]
+    inp = make_attention_inputs(w, seed=0)
+    q, k, v, do = (bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    for u in range(units):                 # (batch, kv head) units in order
+        b, g = divmod(u, w.Hkv)
+        for hi in range(w.r):
+            oracle.attention_forward_head(q, k, v, b, g * w.r + hi, w.scale, True)
+        oracle.attention_backward_group(q, k, v, do, b, g, w.scale, True)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * 4 * w.D * causal_pairs(w.S) * w.r * units
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{units} of {w.B * w.Hkv} (batch, kv-head) units of the workload (forward + backward of "
+                      f"{w.r} query heads each, causal-counted flops), {dt:.1f} s wall, float64 NumPy/BLAS",
+            "seconds": dt, "cpu_count": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; the attention kernels shard by "
+                                   "(batch, kv head) with no exchange, and multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import scaled_dot_product_tiled_amd as sdpt
+    from synth import ATTN_WORKLOADS, DECODE_WORKLOADS, make_attention_inputs, make_decode_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    w = ATTN_WORKLOADS["full_d512"]
+    inp = make_attention_inputs(w, seed=0)
+    q, k, v, do = (dev(inp[x]) for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), device="cuda:0", dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    kw = dict(scale=w.scale, causal=True, window=0)
+
+    def fwd():
+        sdpt.attn_fwd(q, k, v, out=o, lse=lse, **kw)
+
+    def bwd():
+        sdpt.attn_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, **kw)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    pairs = causal_pairs(w.S) * w.B * w.Hq
+    fwd_flops = 4.0 * w.D * pairs
+    bwd_flops = 2.5 * fwd_flops
+
+    # timed region: exactly `steps` steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = time_events(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps * 1e3
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+
+    # per-call times (HIP events on the launch stream)
+    ms_fwd = time_events(fwd, args.steps, stream)
+    ms_bwd = time_events(bwd, args.steps, stream)
+    fwd_tf = fwd_flops / (ms_fwd * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (ms_bwd * 1e-3) / 1e12
+
+    # per-kernel times: the library records HIP event pairs around each of its launches
+    sdpt.binding.profile(True)
+    for _ in range(args.steps):
+        step()
+    sdpt.binding.profile(False)
+    kt = sdpt.binding.profile_read()
+    per_kernel = {n: {"launches": c, "ms_avg": round(t / c, 4)} for n, (c, t) in kt.items()}
+    # algorithmic flops of each kernel: a contraction is 2 D flops per visible pair; the forward
+    # does two (S, PV), dK/dV four (S, dP, dV, dK), dQ the one the definition adds (dQ)
+    unit = 2.0 * w.D * pairs
+    algo = {"attn_fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["ms_avg"] * per_kernel[n]["launches"])
+    dom_ms = per_kernel[dom]["ms_avg"]
+    dom_tf = algo.get(dom, 0.0) / (dom_ms * 1e-3) / 1e12
+
+    # paged decode, rotating over two independent KV pools
+    dw = DECODE_WORKLOADS["decode_d128"]
+    pools = []
+    for s in (0, 1):
+        di = make_decode_inputs(dw, seed=s)
+        pools.append(dict(q=dev(di["q"]), kc=dev(di["k_cache"]), vc=dev(di["v_cache"]),
+                          table=torch.from_numpy(di["block_table"]).to("cuda:0"),
+                          ctx=torch.from_numpy(di["ctx_lens"]).to("cuda:0"), ctx_host=di["ctx_lens"]))
+    outs = [torch.empty_like(p["q"]) for p in pools]
+    ws = torch.empty(1 << 25, device="cuda:0", dtype=torch.uint8)
+
+    def dbytes(ctx):
+        tok = int(np.sum(ctx))
+        pages = int(np.sum(-(-ctx.astype(np.int64) // dw.page_size)))
+        return tok * dw.Hkv * dw.D * 2 * 2 + 2 * dw.B * dw.Hq * dw.D * 2 + 4 * pages + 4 * dw.B
+
+    it = [0]
+
+    def dec():
+        p = pools[it[0] & 1]
+        sdpt.paged_decode(p["q"], p["kc"], p["vc"], p["table"], p["ctx"], scale=dw.scale, out=outs[it[0] & 1],
+                          workspace=ws)
+        it[0] += 1
+
+    for _ in range(4):
+        dec()
+    torch.cuda.synchronize()
+    n_dec = args.decode_steps - (args.decode_steps % 2)
+    ms_dec = time_events(dec, n_dec, stream)
+    dec_bytes = 0.5 * (dbytes(pools[0]["ctx_host"]) + dbytes(pools[1]["ctx_host"]))
+    dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
+
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "ms_per_launch": dom_ms, "flop_per_launch": algo.get(dom, 0.0)}
+
+    out = {
+        "metric": "causal attn fwd+bwd TFLOP/s @d=512 (% bf16 MFMA peak); decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "seq_len": w.S, "heads_q": w.Hq, "heads_kv": w.Hkv,
+                   "head_dim": w.D, "causal": True, "parallelism": "single GPU"},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(ms_fwd, 4), "tflops": round(fwd_tf, 2), "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(ms_bwd, 4), "tflops": round(bwd_tf, 2), "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "wall_ms_per_step": round(wall, 4),
+        "kernels": per_kernel,
+        "roofline": roof,
+        "decode": {"workload": dw.name, "ms": round(ms_dec, 4), "GB/s": round(dec_gbs, 1),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                                "bytes_per_launch": dec_bytes, "traffic": None}},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_units)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -170,6 +170,22 @@ const char* attn_status_str(attn_status status);
 /* The hipError_t (as int) of the last ATTN_ERR_HIP on this thread, 0 if none. */
 int attn_last_hip_error(void);
 
+/* Kernel timing for benchmarks.  After attn_profile(1), every call made on this thread
+ * records a HIP event pair on its own stream around each kernel it launches; after
+ * attn_profile(0) it stops.  attn_profile_read() waits for the recorded events and
+ * fills up to max_entries records (one per kernel name, in first-launch order) with the
+ * launch count and the summed milliseconds, then forgets them; it returns the number of
+ * records, or -1 after a HIP error.  Events come from a pool of at most 4096 pairs per
+ * thread; launches beyond that are not timed.  Not for use under graph capture. */
+typedef struct {
+    const char* kernel;   /* static string */
+    int launches;
+    double total_ms;
+} attn_kernel_time;
+
+int attn_profile(int on);
+int attn_profile_read(attn_kernel_time* out, int max_entries);
+
 /* Library version, "major.minor.patch". */
 const char* attn_version(void);
 

@@ -29,6 +29,10 @@ class AttnShape(ctypes.Structure):
                 ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32)]
 
 
+class AttnKernelTime(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
 class AttnDecodeShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
@@ -38,7 +42,8 @@ class AttnDecodeShape(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("attn_fwd", "attn_bwd", "paged_decode", "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes",
-           "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version")
+           "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
+           "attn_profile", "attn_profile_read")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -74,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_last_hip_error.restype = ctypes.c_int
     lib.attn_version.argtypes = []
     lib.attn_version.restype = ctypes.c_char_p
+    lib.attn_profile.argtypes = [ctypes.c_int]
+    lib.attn_profile.restype = ctypes.c_int
+    lib.attn_profile_read.argtypes = [P(AttnKernelTime), ctypes.c_int]
+    lib.attn_profile_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -213,3 +222,18 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                           out.stride(1), workspace.data_ptr(), nbytes, _stream())
     _check(st, "paged_decode")
     return out
+
+
+def profile(on: bool) -> None:
+    """Start / stop recording HIP event pairs around every kernel the library launches."""
+    load_library().attn_profile(1 if on else 0)
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} of the launches recorded since the last read."""
+    lib = load_library()
+    arr = (AttnKernelTime * 64)()
+    n = lib.attn_profile_read(arr, 64)
+    if n < 0:
+        raise RuntimeError("attn_profile_read failed")
+    return {arr[i].kernel.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}

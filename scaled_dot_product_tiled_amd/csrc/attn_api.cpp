@@ -5,6 +5,8 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "kernel_args.h"
@@ -52,6 +54,46 @@ attn_status hip_status(hipError_t e) {
   if (e == hipSuccess) return ATTN_OK;
   g_last_hip_error = (int)e;
   return ATTN_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing (attn_profile): HIP event pairs around each launch.
+// ---------------------------------------------------------------------------
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;   // created lazily, reused
+  size_t used = 0;
+  std::vector<TimedLaunch> launches;
+};
+thread_local Profiler g_prof;
+constexpr size_t kMaxTimed = 4096;
+
+hipEvent_t prof_event() {
+  if (g_prof.used == g_prof.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_prof.pool.push_back(e);
+  }
+  return g_prof.pool[g_prof.used++];
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_prof.on || g_prof.launches.size() >= kMaxTimed) return launch();
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (!a || !b) return launch();
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  g_prof.launches.push_back({name, a, b});
+  return hipSuccess;
 }
 
 // Query heads packed per workgroup: the largest power of two dividing r, capped so a
@@ -149,7 +191,9 @@ attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
 
   int32_t* meta = static_cast<int32_t*>(workspace);
   if (varlen) {
-    if ((st = hip_status(attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s))))
+    if ((st = hip_status(timed("varlen_prep", s, [&] {
+           return attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s);
+         }))))
       return st;
   }
   attn::AttnArgs a = {};
@@ -164,7 +208,7 @@ attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   set_tensor(v, packed, a.v_sb, a.v_ss, a.v_sh);
   set_tensor(o, packed, a.o_sb, a.o_ss, a.o_sh);
   plan_rows(a, attn::kFwdRows);
-  return hip_status(attn::launch_fwd(a, shape->D, s));
+  return hip_status(timed("attn_fwd", s, [&] { return attn::launch_fwd(a, shape->D, s); }));
 }
 
 attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
@@ -187,7 +231,9 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   int32_t* meta = static_cast<int32_t*>(workspace);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(shape, varlen));
   if (varlen) {
-    if ((st = hip_status(attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s))))
+    if ((st = hip_status(timed("varlen_prep", s, [&] {
+           return attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s);
+         }))))
       return st;
   }
   attn::AttnArgs a = {};
@@ -212,17 +258,19 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   set_tensor(dv, packed, a.dv_sb, a.dv_ss, a.dv_sh);
 
   const int rows = packed ? shape->total * shape->Hq : shape->B * shape->S * shape->Hq;
-  if ((st = hip_status(attn::launch_bwd_pre(a, shape->D, rows, s)))) return st;
+  if ((st = hip_status(timed("bwd_pre", s, [&] { return attn::launch_bwd_pre(a, shape->D, rows, s); }))))
+    return st;
 
   attn::AttnArgs kv = a;
   kv.nkt = (a.S + attn::kDkdvKeys - 1) / attn::kDkdvKeys;
   kv.total_items = a.B * a.Hkv * kv.nkt;
   kv.per_xcd = (kv.total_items + 7) / 8;
-  if ((st = hip_status(attn::launch_bwd_dkdv(kv, shape->D, s)))) return st;
+  if ((st = hip_status(timed("bwd_dkdv", s, [&] { return attn::launch_bwd_dkdv(kv, shape->D, s); }))))
+    return st;
 
   attn::AttnArgs qa = a;
   plan_rows(qa, attn::kDqRows);
-  return hip_status(attn::launch_bwd_dq(qa, shape->D, s));
+  return hip_status(timed("bwd_dq", s, [&] { return attn::launch_bwd_dq(qa, shape->D, s); }));
 }
 
 size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {
@@ -284,7 +332,8 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   a.max_pages = sh.max_pages_per_seq;
   a.max_chunks = (sh.max_pages_per_seq * sh.page_size + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
   a.c = scale * 1.4426950408889634f;
-  return hip_status(attn::launch_decode(a, sh.D, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("paged_decode", s, [&] { return attn::launch_decode(a, sh.D, s); }));
 }
 
 const char* attn_status_str(attn_status status) {
@@ -299,6 +348,34 @@ const char* attn_status_str(attn_status status) {
 }
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_profile(int on) {
+  g_prof.on = on != 0;
+  return 0;
+}
+
+int attn_profile_read(attn_kernel_time* out, int max_entries) {
+  int n = 0;
+  bool failed = false;
+  for (const TimedLaunch& t : g_prof.launches) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) {
+      failed = true;
+      break;
+    }
+    int i = 0;
+    while (i < n && std::strcmp(out[i].kernel, t.name) != 0) ++i;
+    if (i == n) {
+      if (n == max_entries) continue;
+      out[n++] = {t.name, 0, 0.0};
+    }
+    out[i].launches += 1;
+    out[i].total_ms += ms;
+  }
+  g_prof.launches.clear();
+  g_prof.used = 0;
+  return failed ? -1 : n;
+}
 
 const char* attn_version(void) { return "0.1.0"; }
 

@@ -81,7 +81,7 @@ __device__ __forceinline__ void dma_stats(float* dst, const float* lse_row0, con
                                           int imax, int lane) {
   const int i = min(i0 + (lane & 31), imax);
   const float* src = (lane < 32 ? lse_row0 : delta_row0) + i;
-  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)dst, 4, 0, 0);
+  lds_dma4(dst, src);
 }
 
 // ---------------------------------------------------------------------------
@@ -154,9 +154,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     const TrFrags<D> trf(lane);
     const float c = a.c;
 
+    // Step k = (query tile, head), query tiles from the last one down and heads innermost:
+    // every workgroup of this (batch, kv head) starts at the same tile and advances at the
+    // same pace, so the workgroups sharing an XCD read each Q / dO tile while it is in L2.
+    const int tq_last = tq0 + nq - 1;
+    auto step_rows = [&](int k, int& hi, int& i0) {
+      const int qi = k / a.r;
+      hi = k - qi * a.r;
+      i0 = (tq_last - qi) * MQ;
+    };
     auto issue = [&](int k, int buf) {
-      const int hi = k / nq;
-      const int i0 = (tq0 + (k - hi * nq)) * MQ;
+      int hi, i0;
+      step_rows(k, hi, i0);
       const int h = g * a.r + hi;
       const bf16* qb = a.q + b * a.q_sb + (int64_t)off * a.q_ss + h * a.q_sh;
       const bf16* db = a.dout + b * a.do_sb + (int64_t)off * a.do_ss + h * a.do_sh;
@@ -174,8 +183,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       wait_vmcnt<0>();
       barrier_lds();  // step k is in LDS; every wave is done with step k-1
       if (k + 1 < nsteps) issue(k + 1, buf ^ 1);
-      const int hi = k / nq;
-      const int i0 = (tq0 + (k - hi * nq)) * MQ;
+      int hi, i0;
+      step_rows(k, hi, i0);
+      (void)hi;
 
       f32x16 sacc;
 #pragma unroll

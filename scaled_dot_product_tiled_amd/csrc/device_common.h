@@ -109,6 +109,34 @@ struct TrFrags {
   }
 };
 
+// Memory -> LDS copies (global_load_lds).  They are issued from inline assembly rather
+// than the compiler builtin: with the builtin, the compiler waits for every outstanding
+// LDS read before each later LDS read, which exposes the LDS latency in front of every
+// matrix-core instruction.  Completion is tracked here by hand (wait_vmcnt + barrier).
+// The instruction takes its LDS base from M0, written here just before it with one wait
+// state between the write and the use.  Nothing else in these kernels uses M0 (no LDS
+// DMA builtin, no dynamically indexed register arrays), so no value of it is lost.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+// 16 bytes per lane: lane l writes lds_base + 16 l; its source is sbase + voff, with sbase
+// wave-uniform.
+__device__ __forceinline__ void lds_dma16(void* lds_base, const void* sbase, uint32_t voff) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff),
+               "s"(uniform_ptr(sbase))
+               : "memory");
+}
+// 4 bytes per lane: lane l writes lds_base + 4 l; its source is the per-lane address src.
+__device__ __forceinline__ void lds_dma4(void* lds_base, const void* src) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
+               : "memory");
+}
+
 // Asynchronous copy of ROWS rows (row r from g + min(row0 + r, rowmax) * stride elements)
 // into a swizzled LDS tile, straight from memory to LDS.  Each wave-instruction moves 1 KB
 // (64 lanes x 16 bytes) to consecutive LDS; wave `wave` of NW issues instructions wave,
@@ -131,8 +159,8 @@ __device__ __forceinline__ void dma_rows(bf16* tile, const bf16* g, int64_t stri
     const int lrow = min(row0 + trow, rowmax);
     const uint32_t voff = (uint32_t)((int64_t)(lrow - brow) * stride * 2) +
                           (uint32_t)(16 * ((lane % CH) ^ swz_h(trow)));
-    const char* src = reinterpret_cast<const char*>(g + (int64_t)brow * stride) + voff;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(tile + i * RPI * D), 16, 0, 0);
+    const char* src = reinterpret_cast<const char*>(g + (int64_t)brow * stride);
+    lds_dma16(tile + i * RPI * D, src, voff);
   }
 }
 

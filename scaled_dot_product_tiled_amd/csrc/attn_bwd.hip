@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 Qs[2][MQ * D];
   __shared__ __attribute__((aligned(1024))) bf16 dOs[2][MQ * D];
   __shared__ __attribute__((aligned(16))) float stat[2][64];
-  __shared__ __attribute__((aligned(16))) float xdp[2][16][64];       // dP of key block kb: [kb][reg][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xdp[2][4][64];        // dP of key block kb: [kb][reg/4][lane]
   __shared__ __attribute__((aligned(16))) bf16x8 pds[2][2][2][64];    // [P|dS][kb][s][lane]
 
   const int item = xcd_item(a.per_xcd, a.total_items);
@@ -205,22 +205,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       // sacc: lane = key j0 + 32 kb + ln, register r = query row i0 + 8 (r/4) + 4 g2 + r%4
       if (!score_wave) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xdp[kb][r][lane] = sacc[r];
+        for (int x = 0; x < 4; ++x)
+          xdp[kb][x][lane] = f32x4{sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]};
       }
       barrier_lds();
       if (score_wave) {
         const bool full = (i0 + MQ <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= i0) &&
                           (a.window <= 0 || j0 > i0 + MQ - 1 - a.window);
+        // register r holds query row i0 + 8 (r/4) + 4 g2 + r%4: rows 4-aligned in groups of 4
+        f32x4 lse4[4], dl4[4], dp4[4];
+        const f32x4* st4 = reinterpret_cast<const f32x4*>(stat[buf]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          lse4[x] = st4[2 * x + g2];        // rows 8x + 4 g2 .. +3
+          dl4[x] = st4[8 + 2 * x + g2];
+          dp4[x] = xdp[kb][x][lane];
+        }
         const int key = j0 + 32 * kb + ln;
         bf16x8 pb[2], db[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ri = 8 * (r >> 2) + 4 * g2 + (r & 3);
-          const float lse2 = stat[buf][ri] * kLog2e;
-          const float dl = stat[buf][32 + ri];
-          const bool vis = full || key_visible(i0 + ri, key, len, a.causal, a.window);
-          const float p = vis ? fast_exp2(fmaf(sacc[r], c, -lse2)) : 0.f;
-          const float ds = vis ? p * (xdp[kb][r][lane] - dl) : 0.f;
+          const float e = fast_exp2(fmaf(sacc[r], c, -lse4[r >> 2][r & 3] * kLog2e));
+          bool vis = true;
+          if (!full) {
+            const int qi = i0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+            vis = key_visible(qi, key, len, a.causal, a.window);
+          }
+          const float p = vis ? e : 0.f;
+          const float ds = vis ? p * (dp4[r >> 2][r & 3] - dl4[r >> 2][r & 3]) : 0.f;  // +0 when masked
           pb[r >> 3][r & 7] = (bf16)p;
           db[r >> 3][r & 7] = (bf16)ds;
         }
@@ -293,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a) {
   static_assert(M == 64 && NK == 32, "role split assumes two row blocks and one key block");
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][NK * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][NK * D];
-  __shared__ __attribute__((aligned(16))) float xdp[2][16][64];      // dP^T of row block qb
+  __shared__ __attribute__((aligned(16))) f32x4 xdp[2][4][64];       // dP^T of row block qb
   __shared__ __attribute__((aligned(16))) bf16x8 dsb[2][2][64];      // dS^T: [qb][s][lane]
 
   const int item = xcd_item(a.per_xcd, a.total_items);
@@ -389,20 +401,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a) {
       // sacc: lane = query row R, register r = key j0 + 8 (r/4) + 4 g2 + r%4
       if (!score_wave) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xdp[qb][r][lane] = sacc[r];
+        for (int x = 0; x < 4; ++x)
+          xdp[qb][x][lane] = f32x4{sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]};
       }
       barrier_lds();
       if (score_wave) {
         const bool full = (p0 + a.mpos <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= p0) &&
                           (a.window <= 0 || j0 > plast - a.window);
+        f32x4 dp4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dp4[x] = xdp[qb][x][lane];
         bf16x8 db[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
-          const bool vis = full || key_visible(pos, key, len, a.causal, a.window);
-          const float p = vis ? fast_exp2(fmaf(sacc[r], c, -lse2)) : 0.f;
-          const float ds = vis ? p * (xdp[qb][r][lane] - dl) : 0.f;
-          db[r >> 3][r & 7] = (bf16)ds;
+          const float e = fast_exp2(fmaf(sacc[r], c, -lse2));
+          bool vis = true;
+          if (!full) {
+            const int key = j0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+            vis = key_visible(pos, key, len, a.causal, a.window);
+          }
+          const float p = vis ? e : 0.f;
+          db[r >> 3][r & 7] = (bf16)(vis ? p * (dp4[r >> 2][r & 3] - dl) : 0.f);  // +0 when masked
         }
         dsb[qb][0][lane] = db[0];
         dsb[qb][1][lane] = db[1];

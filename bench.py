@@ -191,6 +191,11 @@ def main():
     ms_dec = time_events(dec, n_dec, stream)
     dec_bytes = 0.5 * (dbytes(pools[0]["ctx_host"]) + dbytes(pools[1]["ctx_host"]))
     dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
+    sdpt.binding.profile(True)
+    for _ in range(n_dec):
+        dec()
+    sdpt.binding.profile(False)
+    dec_kernels = {n: {"launches": c, "ms_avg": round(t / c, 4)} for n, (c, t) in sdpt.binding.profile_read().items()}
 
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
@@ -217,7 +222,7 @@ def main():
         "wall_ms_per_step": round(wall, 4),
         "kernels": per_kernel,
         "roofline": roof,
-        "decode": {"workload": dw.name, "ms": round(ms_dec, 4), "GB/s": round(dec_gbs, 1),
+        "decode": {"workload": dw.name, "ms": round(ms_dec, 4), "GB/s": round(dec_gbs, 1), "kernels": dec_kernels,
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "bytes_per_launch": dec_bytes, "traffic": None}},

@@ -138,7 +138,8 @@ typedef struct {
  *
  *   q            device bf16 (B, Hq, D); element strides q_stride_b, q_stride_h
  *   k_cache,     device bf16 (num_pages, page_size, Hkv, D); attn_tensor strides
- *   v_cache      are (page, slot, head) in elements
+ *   v_cache      are (page, slot, head) in elements; a slot stride of 2^26 elements
+ *                or more returns ATTN_ERR_UNSUPPORTED
  *   block_table  device int32 (B, max_pages_per_seq), row-major: logical page p of
  *                sequence b lives in physical page block_table[b][p].  Entries a
  *                sequence does not use are never read.  An entry outside

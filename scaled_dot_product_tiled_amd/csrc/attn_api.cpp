@@ -300,6 +300,8 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
     return ATTN_ERR_INVALID_ARG;
   attn_status st;
   if ((st = check_tensor(k_cache, false)) || (st = check_tensor(v_cache, false))) return st;
+  // offsets inside one page are 32-bit byte offsets
+  if (k_cache.stride_s > (INT_MAX / 2) / 16 || v_cache.stride_s > (INT_MAX / 2) / 16) return ATTN_ERR_UNSUPPORTED;
   const size_t need = paged_decode_workspace_bytes(shape);
   if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
     return ATTN_ERR_WORKSPACE;
@@ -333,7 +335,9 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   a.max_chunks = (sh.max_pages_per_seq * sh.page_size + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
   a.c = scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(timed("paged_decode", s, [&] { return attn::launch_decode(a, sh.D, s); }));
+  hipError_t e = timed("decode_split", s, [&] { return attn::launch_decode_split(a, sh.D, s); });
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(timed("decode_merge", s, [&] { return attn::launch_decode_merge(a, sh.D, s); }));
 }
 
 const char* attn_status_str(attn_status status) {

@@ -140,28 +140,35 @@ __device__ __forceinline__ void lds_dma4(void* lds_base, const void* src) {
 // Asynchronous copy of ROWS rows (row r from g + min(row0 + r, rowmax) * stride elements)
 // into a swizzled LDS tile, straight from memory to LDS.  Each wave-instruction moves 1 KB
 // (64 lanes x 16 bytes) to consecutive LDS; wave `wave` of NW issues instructions wave,
-// wave+NW, ...  The row pointer of an instruction is wave-uniform, so each lane only
-// carries a 32-bit offset.  Nothing is waited for here: the caller waits with wait_vmcnt
-// and a barrier.  `wave` must be wave-uniform, row0 <= rowmax.
+// wave+NW, ...; dma_rows_one issues this wave's k-th one, so callers can spread a copy
+// over a loop of matrix instructions instead of stalling on a burst of copies.  The row
+// pointer of an instruction is wave-uniform, so each lane only carries a 32-bit offset.
+// Nothing is waited for here: the caller waits with wait_vmcnt and a barrier.  `wave`
+// must be wave-uniform, row0 <= rowmax.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_rows(bf16* tile, const bf16* g, int64_t stride, int row0,
-                                         int rowmax, int wave, int lane) {
+__device__ __forceinline__ void dma_rows_one(bf16* tile, const bf16* g, int64_t stride, int row0, int rowmax,
+                                             int wave, int lane, int k) {
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RPI = 64 / CH;   // rows per wave-instruction
   constexpr int NI = ROWS / RPI;
   static_assert(CH >= 16 && 64 % CH == 0, "row must be 256..1024 bytes");
   static_assert(NI % NW == 0, "tile must split evenly over the waves");
+  const int i = wave + k * NW;
+  const int brow = min(row0 + i * RPI, rowmax);                 // wave-uniform
+  const int trow = i * RPI + lane / CH;                         // row within the tile
+  const int lrow = min(row0 + trow, rowmax);
+  const uint32_t voff = (uint32_t)((int64_t)(lrow - brow) * stride * 2) +
+                        (uint32_t)(16 * ((lane % CH) ^ swz_h(trow)));
+  lds_dma16(tile + i * RPI * D, reinterpret_cast<const char*>(g + (int64_t)brow * stride), voff);
+}
+
+// All of this wave's instructions of one tile copy, back to back.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(bf16* tile, const bf16* g, int64_t stride, int row0,
+                                         int rowmax, int wave, int lane) {
+  constexpr int NK = ROWS * D / 512 / NW;
 #pragma unroll
-  for (int k = 0; k < NI / NW; ++k) {
-    const int i = wave + k * NW;
-    const int brow = min(row0 + i * RPI, rowmax);                 // wave-uniform
-    const int trow = i * RPI + lane / CH;                         // row within the tile
-    const int lrow = min(row0 + trow, rowmax);
-    const uint32_t voff = (uint32_t)((int64_t)(lrow - brow) * stride * 2) +
-                          (uint32_t)(16 * ((lane % CH) ^ swz_h(trow)));
-    const char* src = reinterpret_cast<const char*>(g + (int64_t)brow * stride);
-    lds_dma16(tile + i * RPI * D, src, voff);
-  }
+  for (int k = 0; k < NK; ++k) dma_rows_one<D, ROWS, NW>(tile, g, stride, row0, rowmax, wave, lane, k);
 }
 
 template <int D, int ROWS, int NW>

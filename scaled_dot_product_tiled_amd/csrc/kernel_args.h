@@ -65,7 +65,8 @@ hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream);
+hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream);
 
 // Tile geometry used by the host planner.
 constexpr int kFwdRows = 128;   // query rows per forward workgroup
@@ -74,6 +75,6 @@ constexpr int kDkdvKeys = 64;   // keys per dK/dV workgroup
 constexpr int kDkdvRows = 32;   // query rows per dK/dV step
 constexpr int kDqRows = 64;     // query rows per dQ workgroup
 constexpr int kDqKeys = 32;     // keys per dQ step
-constexpr int kDecodeChunk = 256;  // tokens per decode workgroup
+constexpr int kDecodeChunk = 512;  // tokens per decode workgroup
 
 }  // namespace attn

@@ -48,7 +48,7 @@ def test_workspace_sizes():
     bad = AttnShape(1, 10, 0, 6, 4, 512)      # 6 % 4 != 0
     assert lib.attn_fwd_workspace_bytes(ctypes.byref(bad), 0) == 0
     d = AttnDecodeShape(64, 32, 8, 128, 16, 1000, 256)
-    assert lib.paged_decode_workspace_bytes(ctypes.byref(d)) == 64 * 32 * 16 * 130 * 4
+    assert lib.paged_decode_workspace_bytes(ctypes.byref(d)) == 64 * 32 * 8 * 130 * 4   # 512-token chunks
 
 
 def _t(ptr=0x10000, sb=4096 * 32 * 512, ss=32 * 512, sh=512):

@@ -108,8 +108,11 @@ attn_status attn_fwd(const attn_shape* shape,
  * Gemma4 sliding-window BF16 cuDNN SDPA NaN on H100" (Debug and validation
  * results) traces a failure where finite dO produced non-finite dQ/dK/dV; here
  * every gradient of finite inputs is finite.
- *   workspace  at least attn_bwd_workspace_bytes(shape, varlen) bytes
- *              (row statistics, fp32 per query row and head)
+ *   workspace  at least attn_bwd_workspace_bytes(shape, varlen, causal, window)
+ *              bytes: row statistics (fp32 per query row and head) and dS =
+ *              P * (dP - delta) in bf16 for every visible (query, key) pair, kept
+ *              between the dK/dV pass and the dQ pass (in 32-key x 128-row blocks,
+ *              about B * Hq * S * S bytes for causal attention, less with a window)
  */
 attn_status attn_bwd(const attn_shape* shape,
                      attn_tensor q, attn_tensor k, attn_tensor v,
@@ -159,10 +162,10 @@ attn_status paged_decode(const attn_decode_shape* shape,
                          void* o, int64_t o_stride_b, int64_t o_stride_h,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace sizes in bytes.  varlen: 0 dense, 1 pad_mask, 2 cu_seqlens.
- * Return 0 for arguments that the matching call would reject. */
+/* Workspace sizes in bytes.  varlen: 0 dense, 1 pad_mask, 2 cu_seqlens; causal and
+ * window as in the call.  Return 0 for arguments that the matching call would reject. */
 size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen);
-size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen);
+size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen, int causal, int window);
 size_t paged_decode_workspace_bytes(const attn_decode_shape* shape);
 
 /* Static string for a status code. */

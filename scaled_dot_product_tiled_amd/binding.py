@@ -69,7 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_decode.restype = ctypes.c_int
     lib.attn_fwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
     lib.attn_fwd_workspace_bytes.restype = sz
-    lib.attn_bwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
+    lib.attn_bwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.paged_decode_workspace_bytes.argtypes = [P(AttnDecodeShape)]
     lib.paged_decode_workspace_bytes.restype = sz
@@ -186,7 +186,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     cu, pm = _meta_ptrs(cu_seqlens, pad_mask)
-    nbytes = lib.attn_bwd_workspace_bytes(ctypes.byref(shape), varlen)
+    nbytes = lib.attn_bwd_workspace_bytes(ctypes.byref(shape), varlen, int(bool(causal)), int(window))
     ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
     st = lib.attn_bwd(ctypes.byref(shape), _tensor(q, packed), _tensor(k, packed), _tensor(v, packed),
                       _tensor(o, packed), lse.data_ptr(), _tensor(dout, packed), float(scale), int(bool(causal)),

@@ -2,6 +2,7 @@
 // launches, all on the caller's stream.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -156,6 +157,39 @@ attn_status check_common(const attn_shape* shape, float scale, int causal, int w
   return ATTN_OK;
 }
 
+// dS block layout of the backward (see ds_block_index): triangular for causal attention
+// without a window, else a fixed number of blocks per 128-row query tile.
+struct DsLayout {
+  int tri, cnt;
+  int64_t per_head;  // blocks per (batch, query head)
+};
+
+DsLayout ds_layout(const attn_shape* s, int causal, int window) {
+  const int nqt = (s->S + attn::kDsRows - 1) / attn::kDsRows;
+  const int nkb = (s->S + attn::kDsKeys - 1) / attn::kDsKeys;
+  DsLayout L;
+  if (causal && window <= 0) {
+    L.tri = 1;
+    L.cnt = 0;
+    L.per_head = 2LL * nqt * (nqt + 1);
+  } else {
+    L.tri = 0;
+    L.cnt = causal ? std::min(nkb, (window + attn::kDsRows - 1) / attn::kDsKeys + 6) : nkb;
+    L.per_head = (int64_t)nqt * L.cnt;
+  }
+  return L;
+}
+
+size_t ds_bytes(const attn_shape* s, int causal, int window) {
+  const DsLayout L = ds_layout(s, causal, window);
+  return round_up((size_t)s->B * s->Hq * L.per_head * attn::kDsBlockElems * sizeof(__bf16));
+}
+
+size_t bwd_bytes(const attn_shape* shape, int varlen, int causal, int window) {
+  return meta_bytes(shape, varlen) + round_up(sizeof(float) * stat_elems(shape, varlen)) +
+         ds_bytes(shape, causal, window);
+}
+
 bool empty_call(const attn_shape* s, int varlen) {
   return s->B == 0 || s->S == 0 || (varlen == 2 && s->total == 0);
 }
@@ -164,15 +198,18 @@ bool empty_call(const attn_shape* s, int varlen) {
 
 extern "C" {
 
+size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen, int causal, int window) {
+  if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
+  if ((causal != 0 && causal != 1) || window < 0 || (window > 0 && !causal)) return 0;
+  return bwd_bytes(shape, varlen, causal, window);
+}
+
 size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen) {
   if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
   return meta_bytes(shape, varlen);
 }
 
-size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen) {
-  if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
-  return meta_bytes(shape, varlen) + round_up(sizeof(float) * stat_elems(shape, varlen));
-}
+
 
 attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, float scale, int causal,
                      int window, const int32_t* cu_seqlens, const uint8_t* pad_mask, attn_tensor o, float* lse,
@@ -217,7 +254,7 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
                      attn_tensor dv, void* workspace, size_t workspace_bytes, void* stream) {
   const int varlen = varlen_kind(cu_seqlens, pad_mask);
   attn_status st = check_common(shape, scale, causal, window, cu_seqlens, pad_mask, workspace_bytes,
-                                shape ? attn_bwd_workspace_bytes(shape, varlen) : 0, workspace);
+                                shape ? attn_bwd_workspace_bytes(shape, varlen, causal, window) : 0, workspace);
   if (st != ATTN_OK) return st;
   const bool packed = varlen == 2;
   if ((st = check_tensor(q, packed)) || (st = check_tensor(k, packed)) || (st = check_tensor(v, packed)) ||
@@ -248,6 +285,13 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   a.dv = static_cast<__bf16*>(dv.ptr);
   a.lse = const_cast<float*>(lse);
   a.delta = delta;
+  {
+    const DsLayout L = ds_layout(shape, causal, window);
+    a.dsb = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(delta) + round_up(sizeof(float) * stat_elems(shape, varlen)));
+    a.ds_head = L.per_head;
+    a.ds_tri = L.tri;
+    a.ds_cnt = L.cnt;
+  }
   set_tensor(q, packed, a.q_sb, a.q_ss, a.q_sh);
   set_tensor(k, packed, a.k_sb, a.k_ss, a.k_sh);
   set_tensor(v, packed, a.v_sb, a.v_ss, a.v_sh);
@@ -269,7 +313,9 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
     return st;
 
   attn::AttnArgs qa = a;
-  plan_rows(qa, attn::kDqRows);
+  qa.nqt = (a.S + attn::kDsRows - 1) / attn::kDsRows;
+  qa.total_items = a.B * a.Hkv * qa.nqt * a.r;
+  qa.per_xcd = (qa.total_items + 7) / 8;
   return hip_status(timed("bwd_dq", s, [&] { return attn::launch_bwd_dq(qa, shape->D, s); }));
 }
 

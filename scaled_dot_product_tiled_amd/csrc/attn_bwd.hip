@@ -10,18 +10,20 @@
 //   bwd_dkdv  one workgroup per (batch, kv head, 64-key tile): K and V of the tile stay
 //             in registers, every visible 32-row query tile of every query head of the
 //             group streams through LDS, and dK, dV accumulate in registers (no atomics,
-//             one pass over the group's heads, so the grouped-query sum is exact);
-//   bwd_dq    one workgroup per 64 query rows (like the forward): Q and dO stay in
-//             registers and visible 32-key tiles of K and V stream through LDS.
+//             one pass over the group's heads, so the grouped-query sum is exact).  It
+//             also stores dS (bf16) in blocks, so that dQ needs no second pass over
+//             Q K^T and dO V^T;
+//   bwd_dq    one workgroup per (batch, query head, 128 query rows): dQ = scale dS K as
+//             a plain product over the stored dS blocks and 32-key blocks of K.
 // Masked entries become exact zeros by selection, never by multiplication, so a
 // non-finite value outside the visible region cannot reach a gradient (the page "Root
 // cause analysis: Gemma4 sliding-window BF16 cuDNN SDPA NaN on H100" traces non-finite
 // dQ/dK/dV from finite dO in a masked sliding-window backward).
 //
-// Inside both gradient kernels the four waves split by role: two "score" waves compute
-// S = Q K^T for one 32-key (or 32-row) block each and two "dP" waves compute dO V^T for
-// the same blocks; dP crosses to the score wave through LDS, the score wave forms P and
-// dS, and every wave then owns a quarter of head_dim for the two gradient products.
+// Inside the dK/dV kernel the four waves split by role: two "score" waves compute
+// S = Q K^T for one 32-key block each and two "dP" waves compute dO V^T for the same
+// blocks; dP crosses to the score wave through LDS, the score wave forms P and dS, and
+// every wave then owns a quarter of head_dim for the two gradient products.
 #include "device_common.h"
 #include "kernel_args.h"
 
@@ -185,7 +187,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       if (k + 1 < nsteps) issue(k + 1, buf ^ 1);
       int hi, i0;
       step_rows(k, hi, i0);
-      (void)hi;
 
       f32x16 sacc;
 #pragma unroll
@@ -241,6 +242,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           pds[0][kb][s][lane] = pb[s];
           pds[1][kb][s][lane] = db[s];
         }
+        // dS^T for the dQ product: this lane's key, query rows i0 + 8 x + 4 g2 .. +3
+        const int64_t bi = ds_block_index(i0 / kDsRows, (j0 / kDsKeys) + kb, a.causal, a.window, a.S, a.ds_tri,
+                                          a.ds_cnt);
+        if (bi >= 0) {
+          bf16* dst = a.dsb + ((int64_t)(b * a.Hq + g * a.r + hi) * a.ds_head + bi) * kDsBlockElems +
+                      ln * kDsRows + (i0 & (kDsRows - 1)) + 4 * g2;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const bf16x8 v = db[x >> 1];
+            const int e = 4 * (x & 1);
+            *reinterpret_cast<bf16x4*>(dst + 8 * x) = bf16x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+          }
+        }
       }
       barrier_lds();
 #pragma unroll
@@ -294,170 +308,129 @@ hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ
+// dQ = scale dS K, from the stored dS blocks
 // ---------------------------------------------------------------------------
+// One workgroup per (batch, query head, 128-row query tile).  Each step brings one 32-key
+// block of K and the matching dS^T block into LDS; wave w owns head_dim columns
+// 128 w .. 128 w + 127 (D / 128 blocks of 32) for all 128 rows, so every K fragment it
+// reads serves four products and every dS fragment D / 128.  dQ^T accumulates in
+// registers: A operand K^T and B operand dS^T, both read with transposing LDS reads.
+// Pairs that are not visible are zeroed by selection (blocks on the diagonal or the
+// window edge may hold stale values there).
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a) {
-  constexpr int M = kDqRows;    // 64 query rows per workgroup
-  constexpr int NK = kDqKeys;   // 32 keys per step
-  constexpr int KS = D / 16;
-  constexpr int DBW = D / 128;
-  static_assert(M == 64 && NK == 32, "role split assumes two row blocks and one key block");
+  constexpr int M = kDsRows;    // 128 query rows
+  constexpr int NK = kDsKeys;   // 32 keys per step
+  constexpr int DBW = D / 128;  // 32-wide d blocks per wave
+  constexpr int RB = M / 32;    // 32-row blocks
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][NK * D];
-  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][NK * D];
-  __shared__ __attribute__((aligned(16))) f32x4 xdp[2][4][64];       // dP^T of row block qb
-  __shared__ __attribute__((aligned(16))) bf16x8 dsb[2][2][64];      // dS^T: [qb][s][lane]
+  __shared__ __attribute__((aligned(1024))) bf16 Ss[2][NK * M];
 
   const int item = xcd_item(a.per_xcd, a.total_items);
   if (item < 0) return;
-  const int unit = item / a.nqt;
-  const int qt = a.nqt - 1 - (item - unit * a.nqt);
-  const int hb = unit % a.nhb;
-  const int g = (unit / a.nhb) % a.Hkv;
-  const int b = unit / (a.nhb * a.Hkv);
+  // items: (batch, kv head) units, query tiles from the last one down, heads of the group
+  // innermost, so that the workgroups sharing an XCD read the same K blocks
+  const int per_unit = a.nqt * a.r;
+  const int unit = item / per_unit;
+  const int rem = item - unit * per_unit;
+  const int qt = a.nqt - 1 - rem / a.r;
+  const int g = unit % a.Hkv;
+  const int b = unit / a.Hkv;
+  const int h = g * a.r + rem % a.r;
   int len = a.seq_len ? a.seq_len[b] : a.S;
   len = min(max(len, 0), a.S);
   const int off = a.seq_off ? a.seq_off[b] : 0;
+  const int p0 = qt * M;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g2 = lane >> 5, ln = lane & 31;
-  const bool score_wave = wave < 2;
-  const int qb = wave & 1;
   const int dsl = wave * DBW;
-  const int p0 = qt * a.mpos;
 
-  // this lane's query row as the B-operand column of row block qb
-  const int R = 32 * qb + ln;
-  const int hh = R / a.mpos;
-  const int pos = p0 + (R - hh * a.mpos);
-  const int h = g * a.r + hb * a.hpt + hh;
-  const bool row_ok = pos < len;
-  const int prow = min(pos, max(len - 1, 0));
-
-  f32x16 dqacc[2][DBW];
+  f32x16 acc[RB][DBW];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < RB; ++x)
 #pragma unroll
     for (int d = 0; d < DBW; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dqacc[x][d][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[x][d][r] = 0.f;
 
-  const int plast = min(p0 + a.mpos, len) - 1;
-  const int jhi = (plast < p0) ? 0 : (a.causal ? plast + 1 : len);
-  const int jlo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
-  const int t_lo = jlo / NK;
-  const int t_hi = jhi > jlo ? (jhi + NK - 1) / NK : t_lo;
+  // visible key blocks of the tile's rows
+  const int plast = min(p0 + M, len) - 1;
+  const int kb_first = max(ds_kb_lo(qt, a.causal, a.window), a.window > 0 ? max(0, p0 - a.window + 1) / NK : 0);
+  const int kb_last = plast < p0 ? -1 : (a.causal ? plast / NK : (len - 1) / NK);
 
-  if (t_lo < t_hi) {
-    bf16x8 qd[KS];
-    {
-      const bf16* src = score_wave ? a.q + b * a.q_sb + (int64_t)(off + prow) * a.q_ss + h * a.q_sh
-                                   : a.dout + b * a.do_sb + (int64_t)(off + prow) * a.do_ss + h * a.do_sh;
-#pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const bf16x8 x = ldg8(src + 16 * t + 8 * g2);
-        qd[t] = row_ok ? x : zero_bf16x8();
-      }
-    }
-    float lse2 = 0.f, dl = 0.f;
-    if (score_wave && row_ok) {
-      const int64_t si = b * a.st_sb + h * a.st_sh + off + pos;
-      lse2 = a.lse[si] * kLog2e;
-      dl = a.delta[si];
-    }
+  if (kb_first <= kb_last) {
     const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh;
-    const bf16* vbase = a.v + b * a.v_sb + (int64_t)off * a.v_ss + g * a.v_sh;
-    const RowFrags<D> rowf(lane);
-    const TrFrags<D> trf(lane);
-    const float c = a.c;
+    const bf16* sbase = a.dsb + (int64_t)(b * a.Hq + h) * a.ds_head * kDsBlockElems;
+    auto sblock = [&](int kb) {  // every block in kb_first .. kb_last holds a visible pair, so it is stored
+      const int64_t bi = ds_block_index(qt, kb, a.causal, a.window, a.S, a.ds_tri, a.ds_cnt);
+      return sbase + (bi < 0 ? 0 : bi) * kDsBlockElems;
+    };
+    const TrFrags<D> trk(lane);
+    const TrFrags<M> trs(lane);
+    int klo[DBW], khi[DBW];  // bases of this wave's d blocks
+#pragma unroll
+    for (int d = 0; d < DBW; ++d) trk.pick(dsl + d, klo[d], khi[d]);
 
-    dma_rows<D, NK, 4>(Ks[0], kbase, a.k_ss, t_lo * NK, len - 1, wave, lane);
-    dma_rows<D, NK, 4>(Vs[0], vbase, a.v_ss, t_lo * NK, len - 1, wave, lane);
-    for (int jt = t_lo; jt < t_hi; ++jt) {
-      const int buf = (jt - t_lo) & 1;
-      const int j0 = jt * NK;
+    dma_rows<D, NK, 4>(Ks[0], kbase, a.k_ss, kb_first * NK, len - 1, wave, lane);
+    dma_rows<M, NK, 4>(Ss[0], sblock(kb_first), M, 0, NK - 1, wave, lane);
+    for (int kb = kb_first; kb <= kb_last; ++kb) {
+      const int buf = (kb - kb_first) & 1;
+      const int j0 = kb * NK;
       wait_vmcnt<0>();
-      barrier_lds();  // tile jt is in LDS; every wave is done with tile jt-1
-      if (jt + 1 < t_hi) {
+      barrier_lds();  // block kb is in LDS; every wave is done with block kb-1
+      if (kb < kb_last) {
         dma_rows<D, NK, 4>(Ks[buf ^ 1], kbase, a.k_ss, j0 + NK, len - 1, wave, lane);
-        dma_rows<D, NK, 4>(Vs[buf ^ 1], vbase, a.v_ss, j0 + NK, len - 1, wave, lane);
+        dma_rows<M, NK, 4>(Ss[buf ^ 1], sblock(kb + 1), M, 0, NK - 1, wave, lane);
       }
-      f32x16 sacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-      {
-        const bf16* src = score_wave ? Ks[buf] : Vs[buf];
-        bf16x8 f[3];
-        f[0] = rowf.read(src, 0, 0);
-        f[1] = rowf.read(src, 0, 1);
-#pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          if (t + 2 < KS) f[(t + 2) % 3] = rowf.read(src, 0, t + 2);
-          sacc = mfma32(f[t % 3], qd[t], sacc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // sacc: lane = query row R, register r = key j0 + 8 (r/4) + 4 g2 + r%4
-      if (!score_wave) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          xdp[qb][x][lane] = f32x4{sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]};
-      }
-      barrier_lds();
-      if (score_wave) {
-        const bool full = (p0 + a.mpos <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= p0) &&
-                          (a.window <= 0 || j0 > plast - a.window);
-        f32x4 dp4[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) dp4[x] = xdp[qb][x][lane];
-        bf16x8 db[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(sacc[r], c, -lse2));
-          bool vis = true;
-          if (!full) {
-            const int key = j0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
-            vis = key_visible(pos, key, len, a.causal, a.window);
-          }
-          const float p = vis ? e : 0.f;
-          db[r >> 3][r & 7] = (bf16)(vis ? p * (dp4[r >> 2][r & 3] - dl) : 0.f);  // +0 when masked
-        }
-        dsb[qb][0][lane] = db[0];
-        dsb[qb][1][lane] = db[1];
-      }
-      barrier_lds();
+      const bool full = (p0 + M <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= p0) &&
+                        (a.window <= 0 || j0 > p0 + M - 1 - a.window);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 b0 = dsb[0][s][lane], b1 = dsb[1][s][lane];
+        bf16x8 bs[RB];
+#pragma unroll
+        for (int x = 0; x < RB; ++x) {
+          bs[x] = trs.read(Ss[buf], 16 * s, x);
+          if (!full) {
+            // element e holds key j0 + 16 s + 4 g2 + e (e < 4) or j0 + 16 s + 8 + 4 g2 + e - 4
+            const int row = p0 + 32 * x + ln;
+            uint32_t w[4];
+            __builtin_memcpy(w, &bs[x], 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = j0 + 16 * s + 4 * g2 + (e < 4 ? e : e + 4);
+              const uint32_t keep = key_visible(row, key, len, a.causal, a.window) ? 0xffffu : 0u;
+              w[e >> 1] &= (e & 1) ? (keep << 16) | 0xffffu : keep | 0xffff0000u;
+            }
+            __builtin_memcpy(&bs[x], w, 16);
+          }
+        }
 #pragma unroll
         for (int d = 0; d < DBW; ++d) {
-          const bf16x8 ak = trf.read(Ks[buf], 16 * s, dsl + d);
-          dqacc[0][d] = mfma32(ak, b0, dqacc[0][d]);
-          dqacc[1][d] = mfma32(ak, b1, dqacc[1][d]);
+          const bf16x8 ak = trk.read_with(Ks[buf], 16 * s, dsl + d, klo[d], khi[d]);
+#pragma unroll
+          for (int x = 0; x < RB; ++x) acc[x][d] = mfma32(ak, bs[x], acc[x][d]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   }
 
-  // dQ^T blocks: lane = row 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4
+  // dQ^T blocks: lane = row p0 + 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int Rx = 32 * x + ln;
-    const int hx = Rx / a.mpos;
-    const int px = p0 + (Rx - hx * a.mpos);
-    const int hq = g * a.r + hb * a.hpt + hx;
+  for (int x = 0; x < RB; ++x) {
+    const int px = p0 + 32 * x + ln;
     const bool wr = a.packed ? px < len : px < a.S;
     if (!wr) continue;
-    bf16* pq = a.out + b * a.dq_sb + (int64_t)(off + px) * a.dq_ss + hq * a.dq_sh + 4 * g2;
+    bf16* pq = a.out + b * a.dq_sb + (int64_t)(off + px) * a.dq_ss + h * a.dq_sh + 4 * g2;
     const float sc = a.scale;
 #pragma unroll
     for (int d = 0; d < DBW; ++d)
 #pragma unroll
       for (int qa = 0; qa < 4; ++qa)
-        stg4(pq + 32 * (dsl + d) + 8 * qa, dqacc[x][d][4 * qa] * sc, dqacc[x][d][4 * qa + 1] * sc,
-             dqacc[x][d][4 * qa + 2] * sc, dqacc[x][d][4 * qa + 3] * sc);
+        stg4(pq + 32 * (dsl + d) + 8 * qa, acc[x][d][4 * qa] * sc, acc[x][d][4 * qa + 1] * sc,
+             acc[x][d][4 * qa + 2] * sc, acc[x][d][4 * qa + 3] * sc);
   }
 }
 

@@ -102,10 +102,20 @@ struct TrFrags {
         base[4 * hf + x] = (rl + 8 * hf) * D * 2 + 16 * ((4 * x + u) ^ swz_h(rl + 8 * hf)) + 8 * (i & 1);
   }
   __device__ __forceinline__ bf16x8 read(const bf16* tile, int kbase, int db) const {
+    return read_with(tile, kbase, db, base[db & 3], base[4 + (db & 3)]);
+  }
+  // The two bases of column block db, chosen without indexing the array by a run-time
+  // value (which would put it in scratch memory).
+  __device__ __forceinline__ void pick(int db, int& lo, int& hi) const {
+    const int x = db & 3;
+    lo = x == 0 ? base[0] : x == 1 ? base[1] : x == 2 ? base[2] : base[3];
+    hi = x == 0 ? base[4] : x == 1 ? base[5] : x == 2 ? base[6] : base[7];
+  }
+  __device__ __forceinline__ bf16x8 read_with(const bf16* tile, int kbase, int db, int lo, int hi) const {
     const char* t = reinterpret_cast<const char*>(tile) + kbase * D * 2 + 256 * (db >> 2);
-    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(t + base[db & 3]));
-    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(t + base[4 + (db & 3)]));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    bf16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(t + lo));
+    bf16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(t + hi));
+    return __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
 

@@ -23,6 +23,9 @@ struct AttnArgs {
   __bf16* dv;
   float* lse;   // forward writes, backward reads
   float* delta;  // backward: rowsum(dO * O)
+  __bf16* dsb;   // backward: dS blocks (see ds_block_index)
+  int64_t ds_head;  // dS blocks per (batch, query head)
+  int ds_tri, ds_cnt;  // block layout: triangular, or ds_cnt blocks per query tile
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
@@ -58,6 +61,33 @@ struct DecodeArgs {
   float c;            // scale * log2(e)
 };
 
+// The backward stores dS = P * (dP - delta) (bf16) once, for the dQ product.  It is kept in
+// blocks of kDsKeys keys x kDsRows query rows of one (batch, query head), each block stored
+// transposed (row-major, one row per key, kDsRows query rows per row: 8 KB).  Query tile qt
+// (rows 128 qt ..) keeps key blocks ds_kb_lo(qt) .. ds_kb_hi(qt), the only ones that can
+// hold a visible pair, packed tile after tile.
+constexpr int kDsRows = 128;
+constexpr int kDsKeys = 32;
+constexpr int kDsBlockElems = kDsRows * kDsKeys;
+
+__host__ __device__ inline int ds_kb_lo(int qt, int causal, int window) {
+  if (!causal || window <= 0) return 0;
+  const int lo = qt * kDsRows - window - (kDsRows - 1);  // no visible key below this one
+  return lo <= 0 ? 0 : lo / kDsKeys;
+}
+__host__ __device__ inline int ds_kb_hi(int qt, int causal, int S) {
+  const int nkb = (S + kDsKeys - 1) / kDsKeys;
+  const int hi = causal ? qt * (kDsRows / kDsKeys) + (kDsRows / kDsKeys - 1) : nkb - 1;
+  return hi < nkb - 1 ? hi : nkb - 1;
+}
+// Index of block (qt, kb) among the blocks of one (batch, head); -1 if it is not stored.
+__host__ __device__ inline int64_t ds_block_index(int qt, int kb, int causal, int window, int S, int tri, int cnt) {
+  const int lo = ds_kb_lo(qt, causal, window);
+  if (kb < lo || kb > ds_kb_hi(qt, causal, S) || (!tri && kb - lo >= cnt)) return -1;
+  const int64_t first = tri ? 2LL * qt * (qt + 1) : (int64_t)qt * cnt;
+  return first + (kb - lo);
+}
+
 // Launchers (return the HIP launch status).
 hipError_t launch_varlen_prep(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S,
                               int32_t* seq_off, int32_t* seq_len, hipStream_t stream);
@@ -73,8 +103,6 @@ constexpr int kFwdRows = 128;   // query rows per forward workgroup
 constexpr int kFwdKeys = 32;    // keys per forward step
 constexpr int kDkdvKeys = 64;   // keys per dK/dV workgroup
 constexpr int kDkdvRows = 32;   // query rows per dK/dV step
-constexpr int kDqRows = 64;     // query rows per dQ workgroup
-constexpr int kDqKeys = 32;     // keys per dQ step
 constexpr int kDecodeChunk = 512;  // tokens per decode workgroup
 
 }  // namespace attn

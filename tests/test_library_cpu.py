@@ -41,10 +41,18 @@ def test_workspace_sizes():
     s = AttnShape(2, 4096, 0, 32, 4, 512)
     assert lib.attn_fwd_workspace_bytes(ctypes.byref(s), 0) == 0
     assert lib.attn_fwd_workspace_bytes(ctypes.byref(s), 1) == 256       # 2 x B int32, rounded to 256 bytes
-    # backward: delta, one fp32 per (row, head)
-    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0) == 2 * 4096 * 32 * 4
+    # backward: delta (one fp32 per (row, head)), then dS in 8 KB blocks of 32 keys x 128 rows:
+    # causal keeps key blocks 0 .. 4 qt + 3 of query tile qt (2 nqt (nqt + 1) per head),
+    # non-causal all of them, a window a fixed (window + 127) / 32 + 6 per query tile
+    delta = 2 * 4096 * 32 * 4
+    blk = 32 * 128 * 2
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0, 1, 0) == delta + 64 * (2 * 32 * 33) * blk
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0, 0, 0) == delta + 64 * (32 * 128) * blk
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0, 1, 1024) == delta + 64 * (32 * 41) * blk
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0, 0, 1024) == 0     # window needs causal
     p = AttnShape(3, 100, 250, 8, 2, 256)
-    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 2) == 256 + ((250 * 8 * 4 + 255) // 256) * 256
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 2, 1, 0) == (256 + ((250 * 8 * 4 + 255) // 256) * 256
+                                                                       + 3 * 8 * 4 * blk)
     bad = AttnShape(1, 10, 0, 6, 4, 512)      # 6 % 4 != 0
     assert lib.attn_fwd_workspace_bytes(ctypes.byref(bad), 0) == 0
     d = AttnDecodeShape(64, 32, 8, 128, 16, 1000, 256)

@@ -159,34 +159,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     // Step k = (query tile, head), query tiles from the last one down and heads innermost:
     // every workgroup of this (batch, kv head) starts at the same tile and advances at the
     // same pace, so the workgroups sharing an XCD read each Q / dO tile while it is in L2.
+    // The copies of step k+1 (Q and dO tiles: NDMA row copies each per wave) are spread
+    // over the matrix loop of step k, one every two matrix instructions, so the load path
+    // is busy while the matrix cores are; only the small row-statistics copy is issued
+    // at the top of the step.
     const int tq_last = tq0 + nq - 1;
-    auto step_rows = [&](int k, int& hi, int& i0) {
-      const int qi = k / a.r;
-      hi = k - qi * a.r;
-      i0 = (tq_last - qi) * MQ;
-    };
-    auto issue = [&](int k, int buf) {
-      int hi, i0;
-      step_rows(k, hi, i0);
-      const int h = g * a.r + hi;
-      const bf16* qb = a.q + b * a.q_sb + (int64_t)off * a.q_ss + h * a.q_sh;
-      const bf16* db = a.dout + b * a.do_sb + (int64_t)off * a.do_ss + h * a.do_sh;
-      dma_rows<D, MQ, 4>(Qs[buf], qb, a.q_ss, i0, len - 1, wave, lane);
-      dma_rows<D, MQ, 4>(dOs[buf], db, a.do_ss, i0, len - 1, wave, lane);
+    static_assert(2 * NDMA <= KS / 2, "every copy needs a slot in the S / dP loop");
+    int hi = 0, qi = 0;  // step k
+    auto stats = [&](int hs, int i0s, int buf) {
       if (wave == 0) {
-        const int64_t so = b * a.st_sb + h * a.st_sh + off;
-        dma_stats(stat[buf], a.lse + so, a.delta + so, i0, len - 1, lane);
+        const int64_t so = b * a.st_sb + (g * a.r + hs) * a.st_sh + off;
+        dma_stats(stat[buf], a.lse + so, a.delta + so, i0s, len - 1, lane);
       }
     };
-    (void)NDMA;
-    issue(0, 0);
+    {
+      const int h0 = g * a.r;
+      const int i00 = tq_last * MQ;
+      dma_rows<D, MQ, 4>(Qs[0], a.q + b * a.q_sb + (int64_t)off * a.q_ss + h0 * a.q_sh, a.q_ss, i00, len - 1, wave, lane);
+      dma_rows<D, MQ, 4>(dOs[0], a.dout + b * a.do_sb + (int64_t)off * a.do_ss + h0 * a.do_sh, a.do_ss, i00, len - 1,
+                         wave, lane);
+      stats(0, i00, 0);
+    }
     for (int k = 0; k < nsteps; ++k) {
       const int buf = k & 1;
+      const int i0 = (tq_last - qi) * MQ;
+      const int hn = hi + 1 == a.r ? 0 : hi + 1;          // step k+1
+      const int i0n = hi + 1 == a.r ? i0 - MQ : i0;
+      const bool has_next = k + 1 < nsteps;
+      const bf16* qn = a.q + b * a.q_sb + (int64_t)off * a.q_ss + (g * a.r + hn) * a.q_sh;
+      const bf16* dn = a.dout + b * a.do_sb + (int64_t)off * a.do_ss + (g * a.r + hn) * a.do_sh;
       wait_vmcnt<0>();
       barrier_lds();  // step k is in LDS; every wave is done with step k-1
-      if (k + 1 < nsteps) issue(k + 1, buf ^ 1);
-      int hi, i0;
-      step_rows(k, hi, i0);
+      if (has_next) stats(hn, i0n, buf ^ 1);
 
       f32x16 sacc;
 #pragma unroll
@@ -200,6 +204,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         for (int t = 0; t < KS; ++t) {
           if (t + 2 < KS) f[(t + 2) % 3] = rowf.read(src, 0, t + 2);
           sacc = mfma32(f[t % 3], kv[t], sacc);
+          if (has_next && (t & 1) == 0 && t / 2 < 2 * NDMA) {
+            const int j = t / 2;
+            if (j < NDMA)
+              dma_rows_one<D, MQ, 4>(Qs[buf ^ 1], qn, a.q_ss, i0n, len - 1, wave, lane, j);
+            else
+              dma_rows_one<D, MQ, 4>(dOs[buf ^ 1], dn, a.do_ss, i0n, len - 1, wave, lane, j - NDMA);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -218,24 +229,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         const f32x4* st4 = reinterpret_cast<const f32x4*>(stat[buf]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          lse4[x] = st4[2 * x + g2];        // rows 8x + 4 g2 .. +3
+          lse4[x] = st4[2 * x + g2] * kLog2e;  // rows 8x + 4 g2 .. +3
           dl4[x] = st4[8 + 2 * x + g2];
           dp4[x] = xdp[kb][x][lane];
         }
-        const int key = j0 + 32 * kb + ln;
         bf16x8 pb[2], db[2];
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(sacc[r], c, -lse4[r >> 2][r & 3] * kLog2e));
-          bool vis = true;
-          if (!full) {
-            const int qi = i0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
-            vis = key_visible(qi, key, len, a.causal, a.window);
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sacc[r], c, -lse4[r >> 2][r & 3]));
+            pb[r >> 3][r & 7] = (bf16)p;
+            db[r >> 3][r & 7] = (bf16)(p * (dp4[r >> 2][r & 3] - dl4[r >> 2][r & 3]));
           }
-          const float p = vis ? e : 0.f;
-          const float ds = vis ? p * (dp4[r >> 2][r & 3] - dl4[r >> 2][r & 3]) : 0.f;  // +0 when masked
-          pb[r >> 3][r & 7] = (bf16)p;
-          db[r >> 3][r & 7] = (bf16)ds;
+        } else {
+          // this lane's key is visible from query rows rlo .. rhi-1
+          const int key = j0 + 32 * kb + ln;
+          const int rlo = a.causal ? key : 0;
+          int rhi = key < len ? len : 0;
+          if (a.window > 0) rhi = min(rhi, key + a.window);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+            const bool vis = (row >= rlo) & (row < rhi);
+            const float e = fast_exp2(fmaf(sacc[r], c, -lse4[r >> 2][r & 3]));
+            const float p = vis ? e : 0.f;
+            const float ds = vis ? p * (dp4[r >> 2][r & 3] - dl4[r >> 2][r & 3]) : 0.f;  // +0 when masked
+            pb[r >> 3][r & 7] = (bf16)p;
+            db[r >> 3][r & 7] = (bf16)ds;
+          }
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -272,6 +293,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      qi += hi + 1 == a.r;
+      hi = hn;
     }
   }
 

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 Qs[2][MQ * D];
   __shared__ __attribute__((aligned(1024))) bf16 dOs[2][MQ * D];
   __shared__ __attribute__((aligned(16))) float stat[2][64];
-  __shared__ __attribute__((aligned(16))) f32x4 xdp[2][4][64];        // dP of key block kb: [kb][reg/4][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xdp[2][2][64];        // dP, registers 0..7: [kb][reg/4][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xsc[2][2][64];        // S, registers 8..15: [kb][reg/4 - 2][lane]
   __shared__ __attribute__((aligned(16))) bf16x8 pds[2][2][2][64];    // [P|dS][kb][s][lane]
 
   const int item = xcd_item(a.per_xcd, a.total_items);
@@ -215,31 +216,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         }
       }
       // sacc: lane = key j0 + 32 kb + ln, register r = query row i0 + 8 (r/4) + 4 g2 + r%4
-      if (!score_wave) {
+      // P and dS are formed by all four waves: the score wave of key block kb takes
+      // registers 0..7 (query rows 4 g2 + 0..3 and 8 + 4 g2 + 0..3) and receives their dP, the
+      // dP wave takes registers 8..15 and receives their S.
+      if (score_wave) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 2; x < 4; ++x)
+          xsc[kb][x - 2][lane] = f32x4{sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]};
+      } else {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
           xdp[kb][x][lane] = f32x4{sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]};
       }
       barrier_lds();
-      if (score_wave) {
-        const bool full = (i0 + MQ <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= i0) &&
-                          (a.window <= 0 || j0 > i0 + MQ - 1 - a.window);
-        // register r holds query row i0 + 8 (r/4) + 4 g2 + r%4: rows 4-aligned in groups of 4
-        f32x4 lse4[4], dl4[4], dp4[4];
+      {
+        const int xh = score_wave ? 0 : 2;  // this wave's registers: 4 xh .. 4 xh + 7
+        f32x4 sv[2], dpv[2], lse4[2], dl4[2];
+        if (score_wave) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            sv[u] = f32x4{sacc[4 * u], sacc[4 * u + 1], sacc[4 * u + 2], sacc[4 * u + 3]};
+            dpv[u] = xdp[kb][u][lane];
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            sv[u] = xsc[kb][u][lane];
+            dpv[u] = f32x4{sacc[8 + 4 * u], sacc[9 + 4 * u], sacc[10 + 4 * u], sacc[11 + 4 * u]};
+          }
+        }
+        // register 4 x + e holds query row i0 + 8 x + 4 g2 + e
         const f32x4* st4 = reinterpret_cast<const f32x4*>(stat[buf]);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          lse4[x] = st4[2 * x + g2] * kLog2e;  // rows 8x + 4 g2 .. +3
-          dl4[x] = st4[8 + 2 * x + g2];
-          dp4[x] = xdp[kb][x][lane];
+        for (int u = 0; u < 2; ++u) {
+          lse4[u] = st4[2 * (xh + u) + g2] * kLog2e;
+          dl4[u] = st4[8 + 2 * (xh + u) + g2];
         }
-        bf16x8 pb[2], db[2];
+        const bool full = (i0 + MQ <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= i0) &&
+                          (a.window <= 0 || j0 > i0 + MQ - 1 - a.window);
+        bf16x8 pb, db;
         if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(sacc[r], c, -lse4[r >> 2][r & 3]));
-            pb[r >> 3][r & 7] = (bf16)p;
-            db[r >> 3][r & 7] = (bf16)(p * (dp4[r >> 2][r & 3] - dl4[r >> 2][r & 3]));
+          for (int r = 0; r < 8; ++r) {
+            const float p = fast_exp2(fmaf(sv[r >> 2][r & 3], c, -lse4[r >> 2][r & 3]));
+            pb[r] = (bf16)p;
+            db[r] = (bf16)(p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]));
           }
         } else {
           // this lane's key is visible from query rows rlo .. rhi-1
@@ -248,33 +269,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           int rhi = key < len ? len : 0;
           if (a.window > 0) rhi = min(rhi, key + a.window);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i0 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          for (int r = 0; r < 8; ++r) {
+            const int row = i0 + 8 * (xh + (r >> 2)) + 4 * g2 + (r & 3);
             const bool vis = (row >= rlo) & (row < rhi);
-            const float e = fast_exp2(fmaf(sacc[r], c, -lse4[r >> 2][r & 3]));
+            const float e = fast_exp2(fmaf(sv[r >> 2][r & 3], c, -lse4[r >> 2][r & 3]));
             const float p = vis ? e : 0.f;
-            const float ds = vis ? p * (dp4[r >> 2][r & 3] - dl4[r >> 2][r & 3]) : 0.f;  // +0 when masked
-            pb[r >> 3][r & 7] = (bf16)p;
-            db[r >> 3][r & 7] = (bf16)ds;
+            const float ds = vis ? p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) : 0.f;  // +0 when masked
+            pb[r] = (bf16)p;
+            db[r] = (bf16)ds;
           }
         }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          pds[0][kb][s][lane] = pb[s];
-          pds[1][kb][s][lane] = db[s];
-        }
+        pds[0][kb][xh >> 1][lane] = pb;
+        pds[1][kb][xh >> 1][lane] = db;
         // dS^T for the dQ product: this lane's key, query rows i0 + 8 x + 4 g2 .. +3
         const int64_t bi = ds_block_index(i0 / kDsRows, (j0 / kDsKeys) + kb, a.causal, a.window, a.S, a.ds_tri,
                                           a.ds_cnt);
         if (bi >= 0) {
           bf16* dst = a.dsb + ((int64_t)(b * a.Hq + g * a.r + hi) * a.ds_head + bi) * kDsBlockElems +
-                      ln * kDsRows + (i0 & (kDsRows - 1)) + 4 * g2;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const bf16x8 v = db[x >> 1];
-            const int e = 4 * (x & 1);
-            *reinterpret_cast<bf16x4*>(dst + 8 * x) = bf16x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
-          }
+                      ln * kDsRows + (i0 & (kDsRows - 1)) + 8 * xh + 4 * g2;
+          *reinterpret_cast<bf16x4*>(dst) = bf16x4{db[0], db[1], db[2], db[3]};
+          *reinterpret_cast<bf16x4*>(dst + 8) = bf16x4{db[4], db[5], db[6], db[7]};
         }
       }
       barrier_lds();

@@ -27,6 +27,24 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 
+# HBM traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy)
+# of each kernel on this workload; a record counts only while its kernel source is unchanged.
+TRAFFIC = {
+    "attn_fwd": ("profiles/attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512"),
+    "bwd_dkdv": ("profiles/bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512>"),
+    "bwd_dq": ("profiles/bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<512>"),
+    "decode_split": ("profiles/decode_split_d128_B64_traffic.txt", "decode_split_kernel<4>"),
+}
+
+
+def traffic_bytes(kernel):
+    from scaled_dot_product_tiled_amd.profiling import read_traffic
+    if kernel not in TRAFFIC:
+        return None
+    path, name = TRAFFIC[kernel]
+    rec = read_traffic(os.path.join(ROOT, path), name)
+    return None if rec is None else rec["bytes"]
+
 
 def causal_pairs(S, window=0):
     i = np.arange(S, dtype=np.int64)
@@ -198,7 +216,7 @@ def main():
     dec_kernels = {n: {"launches": c, "ms_avg": round(t / c, 4)} for n, (c, t) in sdpt.binding.profile_read().items()}
 
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_bytes(dom),
             "ms_per_launch": dom_ms, "flop_per_launch": algo.get(dom, 0.0)}
 
     out = {
@@ -225,7 +243,7 @@ def main():
         "decode": {"workload": dw.name, "ms": round(ms_dec, 4), "GB/s": round(dec_gbs, 1), "kernels": dec_kernels,
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                                "bytes_per_launch": dec_bytes, "traffic": None}},
+                                "bytes_per_launch": dec_bytes, "traffic": traffic_bytes("decode_split")}},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_units)

@@ -9,6 +9,8 @@ the C ABI.  Reported:
   decode    paged single-token decode (B=64, Hq=32, Hkv=8, D=128, 16-token pages, contexts
             U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
+  other_workloads  forward / backward TFLOP/s of the sliding-window (D=256, W=1024) and padded
+            varlen (B=8, lengths U{512..8192}, D=512) workloads, not part of the timed step;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores.
 Prints one JSON line.
 """
@@ -52,6 +54,57 @@ def causal_pairs(S, window=0):
     return int(cnt.sum())
 
 
+def other_workload(name, steps, stream):
+    """Forward and backward times of the sliding-window and padded-varlen workloads (device-side
+    seeded draws of the same shapes and distributions; lengths and masks from synth)."""
+    import torch
+    import scaled_dot_product_tiled_amd as sdpt
+    from synth import ATTN_WORKLOADS
+    from synth import draw_lengths, lengths_to_pad_mask
+    w = ATTN_WORKLOADS[name]
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(1234 + w.wid)
+
+    def draw(shape, std):
+        return (torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32) * std).to(torch.bfloat16)
+
+    q = draw((w.B, w.S, w.Hq, w.D), w.qk_std)
+    k = draw((w.B, w.S, w.Hkv, w.D), w.qk_std)
+    v = draw((w.B, w.S, w.Hkv, w.D), 1.0)
+    do = draw((w.B, w.S, w.Hq, w.D), 1.0)
+    lengths = draw_lengths(w, 0)
+    pm = None
+    if lengths is not None:
+        pm = torch.from_numpy(lengths_to_pad_mask(lengths, w.S).astype(np.uint8)).to("cuda:0")
+        pairs = sum(int(n) * (int(n) + 1) // 2 for n in lengths) * w.Hq
+    else:
+        pairs = causal_pairs(w.S, w.window) * w.B * w.Hq
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), device="cuda:0", dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    kw = dict(scale=w.scale, causal=True, window=w.window, pad_mask=pm)
+
+    def fwd():
+        sdpt.attn_fwd(q, k, v, out=o, lse=lse, **kw)
+
+    def bwd():
+        sdpt.attn_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, **kw)
+
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    ms_f = time_events(fwd, steps, stream)
+    ms_b = time_events(bwd, steps, stream)
+    ff = 4.0 * w.D * pairs
+    res = {"workload": w.name, "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+           "fwd_tflops": round(ff / ms_f / 1e9, 2), "bwd_tflops": round(2.5 * ff / ms_b / 1e9, 2),
+           "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2)}
+    res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -60,6 +113,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=8, help="(batch, kv head) units the oracle times (of 8)")
+    p.add_argument("--no-other", action="store_true", help="skip the sliding-window and varlen workloads")
     return p.parse_args()
 
 
@@ -219,6 +273,8 @@ def main():
             "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_bytes(dom),
             "ms_per_launch": dom_ms, "flop_per_launch": algo.get(dom, 0.0)}
 
+    others = {} if args.no_other else {n: other_workload(n, 5, stream) for n in ("window_d256", "varlen_d512")}
+
     out = {
         "metric": "causal attn fwd+bwd TFLOP/s @d=512 (% bf16 MFMA peak); decode HBM GB/s",
         "value": round(value, 2),
@@ -244,6 +300,7 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "bytes_per_launch": dec_bytes, "traffic": traffic_bytes("decode_split")}},
+        "other_workloads": others,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_units)

@@ -128,6 +128,7 @@ void fill_common(attn::AttnArgs& a, const attn_shape* s, int varlen, float scale
   a.c = scale * 1.4426950408889634f;
   a.seq_off = varlen ? meta : nullptr;
   a.seq_len = varlen ? meta + s->B : nullptr;
+  a.balanced = varlen != 0;  // sequences of different lengths: deal work items in rounds
   if (a.packed) {
     a.st_sb = 0;
     a.st_sh = s->total;

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) f32x4 xsc[2][2][64];        // S, registers 8..15: [kb][reg/4 - 2][lane]
   __shared__ __attribute__((aligned(16))) bf16x8 pds[2][2][2][64];    // [P|dS][kb][s][lane]
 
-  const int item = xcd_item(a.per_xcd, a.total_items);
+  const int item = xcd_item(a.per_xcd, a.total_items, a.nkt, a.balanced);
   if (item < 0) return;
   const int unit = item / a.nkt;
   const int kt = item - unit * a.nkt;  // low key tiles see the most query rows: first
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][NK * D];
   __shared__ __attribute__((aligned(1024))) bf16 Ss[2][NK * M];
 
-  const int item = xcd_item(a.per_xcd, a.total_items);
+  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt * a.r, a.balanced);
   if (item < 0) return;
   // items: (batch, kv head) units, query tiles from the last one down, heads of the group
   // innermost, so that the workgroups sharing an XCD read the same K blocks

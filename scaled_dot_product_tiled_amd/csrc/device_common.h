@@ -214,10 +214,22 @@ __device__ __forceinline__ void stg4(bf16* p, float a, float b, float c, float d
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
-// Work-item order: consecutive workgroup ids land on consecutive XCDs (id % 8), so
-// the items of one XCD are taken from one contiguous range of the item list; items
-// that share K/V then share that XCD's L2.
-__device__ __forceinline__ int xcd_item(int per_xcd, int total) {
+// Work-item order.  Items are (unit, w) with W items per unit, w = 0 the heaviest.
+// Consecutive workgroup ids land on consecutive XCDs (id % 8).  When every unit carries the
+// same work (dense inputs), the items of one XCD are taken from one contiguous range of the
+// item list, heaviest first within each unit: the workgroups of a unit then share K/V in
+// that XCD's L2.  When units differ (variable lengths: whole units on one XCD would leave
+// the XCDs with short sequences idle), items are dealt in rounds instead, the heaviest item
+// of every unit first, with the unit order rotated by one each round so that every unit
+// visits every XCD.
+__device__ __forceinline__ int xcd_item(int per_xcd, int total, int W, int balanced) {
+  if (balanced) {
+    const int k = blockIdx.x;
+    if (k >= total) return -1;
+    const int U = total / W;
+    const int round = k / U;
+    return ((k + round) % U) * W + round;
+  }
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int item = xcd * per_xcd + slot;
   return (slot < per_xcd && item < total) ? item : -1;

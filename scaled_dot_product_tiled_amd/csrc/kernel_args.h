@@ -45,6 +45,7 @@ struct AttnArgs {
   float scale;              // multiplies Q K^T
   float c;                  // scale * log2(e)
   int per_xcd, total_items;
+  int balanced;             // deal work items in rounds (see xcd_item)
 };
 
 struct DecodeArgs {

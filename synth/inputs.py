@@ -25,7 +25,7 @@ __all__ = [
     "AttnWorkload", "DecodeWorkload", "ATTN_WORKLOADS", "DECODE_WORKLOADS",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64", "stream",
     "normal_bf16", "make_attention_inputs", "make_decode_inputs",
-    "lengths_to_pad_mask", "lengths_to_cu_seqlens", "pack_rows", "STREAM",
+    "lengths_to_pad_mask", "lengths_to_cu_seqlens", "pack_rows", "draw_lengths", "STREAM",
 ]
 
 # Stream ids inside one workload.
@@ -174,7 +174,8 @@ def pack_rows(x: np.ndarray, lengths: np.ndarray) -> np.ndarray:
     return np.concatenate([x[b, :int(n)] for b, n in enumerate(lengths)], axis=0)
 
 
-def _draw_lengths(w, seed):
+def draw_lengths(w, seed):
+    """The workload's seeded sequence lengths (the ones make_attention_inputs uses), or None."""
     if w.len_range is None:
         return None
     lo, hi = w.len_range
@@ -191,7 +192,7 @@ def make_attention_inputs(w: AttnWorkload, seed: int = 0, poison_padding: bool =
     k = normal_bf16(stream(seed, w.wid, STREAM["k"]), (w.B, w.S, w.Hkv, w.D), w.qk_std)
     v = normal_bf16(stream(seed, w.wid, STREAM["v"]), (w.B, w.S, w.Hkv, w.D), w.vdo_std)
     do = normal_bf16(stream(seed, w.wid, STREAM["do"]), (w.B, w.S, w.Hq, w.D), w.vdo_std)
-    lengths = _draw_lengths(w, seed)
+    lengths = draw_lengths(w, seed)
     out = {"q": q, "k": k, "v": v, "do": do, "lengths": lengths}
     if lengths is not None:
         out["pad_mask"] = lengths_to_pad_mask(lengths, w.S)

@@ -355,7 +355,8 @@ hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
 // Pairs that are not visible are zeroed by selection (blocks on the diagonal or the
 // window edge may hold stale values there).
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a) {
+// Two workgroups per compute unit at head_dim 256 (accumulators in 128 registers).
+__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dq_kernel(AttnArgs a) {
   constexpr int M = kDsRows;    // 128 query rows
   constexpr int NK = kDsKeys;   // 32 keys per step
   constexpr int DBW = D / 128;  // 32-wide d blocks per wave

@@ -43,7 +43,10 @@ namespace attn {
 constexpr float kRefSlack = 32.0f;
 
 template <int D, int N, bool EXACT>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(AttnArgs a) {
+// At head_dim 256 a wave fits in 256 registers, so two workgroups share a compute unit and
+// one's softmax and barriers overlap the other's matrix work; at 512 the accumulators alone
+// take 256 registers.
+__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) {
   constexpr int NKB = N / 32;  // 32-key blocks per tile
   constexpr int NS = N / 16;   // 16-key steps per tile
   constexpr int KS = D / 16;

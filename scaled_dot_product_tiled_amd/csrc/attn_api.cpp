@@ -315,7 +315,7 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
 
   attn::AttnArgs qa = a;
   qa.nqt = (a.S + attn::kDsRows - 1) / attn::kDsRows;
-  qa.total_items = a.B * a.Hkv * qa.nqt * a.r;
+  qa.total_items = a.B * a.Hkv * qa.nqt * a.r * (shape->D == 512 ? attn::kDqSplit512 : 1);
   qa.per_xcd = (qa.total_items + 7) / 8;
   return hip_status(timed("bwd_dq", s, [&] { return attn::launch_bwd_dq(qa, shape->D, s); }));
 }

@@ -347,30 +347,37 @@ hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // dQ = scale dS K, from the stored dS blocks
 // ---------------------------------------------------------------------------
-// One workgroup per (batch, query head, 128-row query tile).  Each step brings one 32-key
-// block of K and the matching dS^T block into LDS; wave w owns head_dim columns
-// 128 w .. 128 w + 127 (D / 128 blocks of 32) for all 128 rows, so every K fragment it
-// reads serves four products and every dS fragment D / 128.  dQ^T accumulates in
-// registers: A operand K^T and B operand dS^T, both read with transposing LDS reads.
-// Pairs that are not visible are zeroed by selection (blocks on the diagonal or the
-// window edge may hold stale values there).
-template <int D>
-// Two workgroups per compute unit at head_dim 256 (accumulators in 128 registers).
-__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dq_kernel(AttnArgs a) {
-  constexpr int M = kDsRows;    // 128 query rows
-  constexpr int NK = kDsKeys;   // 32 keys per step
-  constexpr int DBW = D / 128;  // 32-wide d blocks per wave
-  constexpr int RB = M / 32;    // 32-row blocks
+// One workgroup per (batch, query head, 128-row query tile, head_dim slice of D columns):
+// at head_dim 512 the columns are split in NSPLIT = 2 halves, so that a wave needs only
+// 128 accumulator registers and two workgroups share a compute unit; one's copies and
+// barriers then overlap the other's matrix work (the same dS block is read by both halves,
+// from L2).  Each step brings one 32-key block of K (the workgroup's columns) and the
+// matching dS^T block into LDS; wave w owns columns 32 DBW w .. of the slice for all 128
+// rows, so every K fragment it reads serves four products and every dS fragment DBW.
+// dQ^T accumulates in registers: A operand K^T and B operand dS^T, both read with
+// transposing LDS reads.  Pairs that are not visible are zeroed by selection (blocks on the
+// diagonal or the window edge may hold stale values there).
+template <int D, int NW, int NSPLIT>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
+  // D: head_dim columns of this workgroup (the full head_dim is D * NSPLIT)
+  constexpr int M = kDsRows;          // 128 query rows
+  constexpr int NK = kDsKeys;         // 32 keys per step
+  constexpr int DBW = D / (32 * NW);  // 32-wide d blocks per wave
+  constexpr int RB = M / 32;          // 32-row blocks
+  static_assert(DBW >= 1 && DBW * 32 * NW == D, "head_dim must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][NK * D];
   __shared__ __attribute__((aligned(1024))) bf16 Ss[2][NK * M];
 
-  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt * a.r, a.balanced);
+  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt * a.r * NSPLIT, a.balanced);
   if (item < 0) return;
-  // items: (batch, kv head) units, query tiles from the last one down, heads of the group
-  // innermost, so that the workgroups sharing an XCD read the same K blocks
-  const int per_unit = a.nqt * a.r;
+  // items: (batch, kv head) units, query tiles from the last one down, then the group's
+  // heads and the column slices, so that the workgroups sharing an XCD read the same K
+  // and dS blocks
+  const int per_unit = a.nqt * a.r * NSPLIT;
   const int unit = item / per_unit;
-  const int rem = item - unit * per_unit;
+  const int rem0 = item - unit * per_unit;
+  const int dh = rem0 % NSPLIT;
+  const int rem = rem0 / NSPLIT;
   const int qt = a.nqt - 1 - rem / a.r;
   const int g = unit % a.Hkv;
   const int b = unit / a.Hkv;
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dq_kernel(AttnArgs 
   const int kb_last = plast < p0 ? -1 : (a.causal ? plast / NK : (len - 1) / NK);
 
   if (kb_first <= kb_last) {
-    const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh;
+    const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh + dh * D;
     const bf16* sbase = a.dsb + (int64_t)(b * a.Hq + h) * a.ds_head * kDsBlockElems;
     auto sblock = [&](int kb) {  // every block in kb_first .. kb_last holds a visible pair, so it is stored
       const int64_t bi = ds_block_index(qt, kb, a.causal, a.window, a.S, a.ds_tri, a.ds_cnt);
@@ -411,16 +418,16 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dq_kernel(AttnArgs 
 #pragma unroll
     for (int d = 0; d < DBW; ++d) trk.pick(dsl + d, klo[d], khi[d]);
 
-    dma_rows<D, NK, 4>(Ks[0], kbase, a.k_ss, kb_first * NK, len - 1, wave, lane);
-    dma_rows<M, NK, 4>(Ss[0], sblock(kb_first), M, 0, NK - 1, wave, lane);
+    dma_rows<D, NK, NW>(Ks[0], kbase, a.k_ss, kb_first * NK, len - 1, wave, lane);
+    dma_rows<M, NK, NW>(Ss[0], sblock(kb_first), M, 0, NK - 1, wave, lane);
     for (int kb = kb_first; kb <= kb_last; ++kb) {
       const int buf = (kb - kb_first) & 1;
       const int j0 = kb * NK;
       wait_vmcnt<0>();
       barrier_lds();  // block kb is in LDS; every wave is done with block kb-1
       if (kb < kb_last) {
-        dma_rows<D, NK, 4>(Ks[buf ^ 1], kbase, a.k_ss, j0 + NK, len - 1, wave, lane);
-        dma_rows<M, NK, 4>(Ss[buf ^ 1], sblock(kb + 1), M, 0, NK - 1, wave, lane);
+        dma_rows<D, NK, NW>(Ks[buf ^ 1], kbase, a.k_ss, j0 + NK, len - 1, wave, lane);
+        dma_rows<M, NK, NW>(Ss[buf ^ 1], sblock(kb + 1), M, 0, NK - 1, wave, lane);
       }
       const bool full = (p0 + M <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= p0) &&
                         (a.window <= 0 || j0 > p0 + M - 1 - a.window);
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dq_kernel(AttnArgs 
     const int px = p0 + 32 * x + ln;
     const bool wr = a.packed ? px < len : px < a.S;
     if (!wr) continue;
-    bf16* pq = a.out + b * a.dq_sb + (int64_t)(off + px) * a.dq_ss + h * a.dq_sh + 4 * g2;
+    bf16* pq = a.out + b * a.dq_sb + (int64_t)(off + px) * a.dq_ss + h * a.dq_sh + dh * D + 4 * g2;
     const float sc = a.scale;
 #pragma unroll
     for (int d = 0; d < DBW; ++d)
@@ -473,11 +480,11 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dq_kernel(AttnArgs 
 }
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream) {
-  const dim3 grid(8 * a.per_xcd), block(256);
+  const dim3 grid(8 * a.per_xcd);
   if (D == 512)
-    hipLaunchKernelGGL(bwd_dq_kernel<512>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<512 / kDqSplit512, 4, kDqSplit512>), grid, dim3(256), 0, stream, a);
   else if (D == 256)
-    hipLaunchKernelGGL(bwd_dq_kernel<256>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<256, 4, 1>), grid, dim3(256), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

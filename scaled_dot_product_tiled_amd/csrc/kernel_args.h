@@ -102,6 +102,7 @@ hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream);
 // Tile geometry used by the host planner.
 constexpr int kFwdRows = 128;   // query rows per forward workgroup
 constexpr int kFwdKeys = 32;    // keys per forward step
+constexpr int kDqSplit512 = 2;  // head_dim slices of a dQ query tile at head_dim 512
 constexpr int kDkdvKeys = 64;   // keys per dK/dV workgroup
 constexpr int kDkdvRows = 32;   // query rows per dK/dV step
 constexpr int kDecodeChunk = 512;  // tokens per decode workgroup

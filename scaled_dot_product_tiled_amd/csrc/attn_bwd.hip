@@ -176,9 +176,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     {
       const int h0 = g * a.r;
       const int i00 = tq_last * MQ;
-      dma_rows<D, MQ, 4>(Qs[0], a.q + b * a.q_sb + (int64_t)off * a.q_ss + h0 * a.q_sh, a.q_ss, i00, len - 1, wave, lane);
-      dma_rows<D, MQ, 4>(dOs[0], a.dout + b * a.do_sb + (int64_t)off * a.do_ss + h0 * a.do_sh, a.do_ss, i00, len - 1,
-                         wave, lane);
+      dma_rows<D, MQ, 4>(Qs[0], tile_src<MQ>(a.q + b * a.q_sb + (int64_t)off * a.q_ss + h0 * a.q_sh, a.q_ss, i00,
+                                             len - i00), wave, lane);
+      dma_rows<D, MQ, 4>(dOs[0], tile_src<MQ>(a.dout + b * a.do_sb + (int64_t)off * a.do_ss + h0 * a.do_sh, a.do_ss,
+                                              i00, len - i00), wave, lane);
       stats(0, i00, 0);
     }
     for (int k = 0; k < nsteps; ++k) {
@@ -187,8 +188,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       const int hn = hi + 1 == a.r ? 0 : hi + 1;          // step k+1
       const int i0n = hi + 1 == a.r ? i0 - MQ : i0;
       const bool has_next = k + 1 < nsteps;
-      const bf16* qn = a.q + b * a.q_sb + (int64_t)off * a.q_ss + (g * a.r + hn) * a.q_sh;
-      const bf16* dn = a.dout + b * a.do_sb + (int64_t)off * a.do_ss + (g * a.r + hn) * a.do_sh;
+      // the last step copies nothing real: an empty range reads zeros into the idle buffers
+      const TileSrc qn = tile_src<MQ>(a.q + b * a.q_sb + (int64_t)off * a.q_ss + (g * a.r + hn) * a.q_sh, a.q_ss,
+                                      i0n, has_next ? len - i0n : 0);
+      const TileSrc dn = tile_src<MQ>(a.dout + b * a.do_sb + (int64_t)off * a.do_ss + (g * a.r + hn) * a.do_sh,
+                                      a.do_ss, i0n, has_next ? len - i0n : 0);
       wait_vmcnt<0>();
       barrier_lds();  // step k is in LDS; every wave is done with step k-1
       if (has_next) stats(hn, i0n, buf ^ 1);
@@ -205,12 +209,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         for (int t = 0; t < KS; ++t) {
           if (t + 2 < KS) f[(t + 2) % 3] = rowf.read(src, 0, t + 2);
           sacc = mfma32(f[t % 3], kv[t], sacc);
-          if (has_next && (t & 1) == 0 && t / 2 < 2 * NDMA) {
+          if ((t & 1) == 0 && t / 2 < 2 * NDMA) {
             const int j = t / 2;
             if (j < NDMA)
-              dma_rows_one<D, MQ, 4>(Qs[buf ^ 1], qn, a.q_ss, i0n, len - 1, wave, lane, j);
+              dma_rows_one<D, MQ, 4>(Qs[buf ^ 1], qn, wave, lane, j);
             else
-              dma_rows_one<D, MQ, 4>(dOs[buf ^ 1], dn, a.do_ss, i0n, len - 1, wave, lane, j - NDMA);
+              dma_rows_one<D, MQ, 4>(dOs[buf ^ 1], dn, wave, lane, j - NDMA);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -418,16 +422,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < DBW; ++d) trk.pick(dsl + d, klo[d], khi[d]);
 
-    dma_rows<D, NK, NW>(Ks[0], kbase, a.k_ss, kb_first * NK, len - 1, wave, lane);
-    dma_rows<M, NK, NW>(Ss[0], sblock(kb_first), M, 0, NK - 1, wave, lane);
+    dma_rows<D, NK, NW>(Ks[0], tile_src<NK>(kbase, a.k_ss, kb_first * NK, len - kb_first * NK), wave, lane);
+    dma_rows<M, NK, NW>(Ss[0], tile_src<NK>(sblock(kb_first), M, 0, NK), wave, lane);
     for (int kb = kb_first; kb <= kb_last; ++kb) {
       const int buf = (kb - kb_first) & 1;
       const int j0 = kb * NK;
       wait_vmcnt<0>();
       barrier_lds();  // block kb is in LDS; every wave is done with block kb-1
       if (kb < kb_last) {
-        dma_rows<D, NK, NW>(Ks[buf ^ 1], kbase, a.k_ss, j0 + NK, len - 1, wave, lane);
-        dma_rows<M, NK, NW>(Ss[buf ^ 1], sblock(kb + 1), M, 0, NK - 1, wave, lane);
+        dma_rows<D, NK, NW>(Ks[buf ^ 1], tile_src<NK>(kbase, a.k_ss, j0 + NK, len - j0 - NK), wave, lane);
+        dma_rows<M, NK, NW>(Ss[buf ^ 1], tile_src<NK>(sblock(kb + 1), M, 0, NK), wave, lane);
       }
       const bool full = (p0 + M <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= p0) &&
                         (a.window <= 0 || j0 > p0 + M - 1 - a.window);

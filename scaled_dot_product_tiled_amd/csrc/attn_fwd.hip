@@ -112,8 +112,8 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
       for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
     l_run = 0.f;
     if (t_lo < t_hi) {
-      dma_rows<D, N, 4>(Ks, kbase, a.k_ss, t_lo * N, len - 1, wave, lane);
-      dma_rows<D, N, 4>(Vs, vbase, a.v_ss, t_lo * N, len - 1, wave, lane);
+      dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, t_lo * N, len - t_lo * N), wave, lane);
+      dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, t_lo * N, len - t_lo * N), wave, lane);
     }
     for (int jt = t_lo; jt < t_hi; ++jt) {
       const int j0 = jt * N;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
         }
       }
       barrier_lds();  // every wave is done with Ks
-      if (has_next) dma_rows<D, N, 4>(Ks, kbase, a.k_ss, j0 + N, len - 1, wave, lane);
+      if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, len - j0 - N), wave, lane);
 
       const bool need_mask = (j0 + N > len) || (p0 + a.mpos > len) || (a.causal && j0 + N - 1 > p0) ||
                              (a.window > 0 && j0 <= plast - a.window);
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
         }
       }
       barrier_lds();  // every wave is done with Vs
-      if (has_next) dma_rows<D, N, 4>(Vs, vbase, a.v_ss, j0 + N, len - 1, wave, lane);
+      if (has_next) dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, j0 + N, len - j0 - N), wave, lane);
     }
   }
 

@@ -119,27 +119,13 @@ struct TrFrags {
   }
 };
 
-// Memory -> LDS copies (global_load_lds).  They are issued from inline assembly rather
-// than the compiler builtin: with the builtin, the compiler waits for every outstanding
-// LDS read before each later LDS read, which exposes the LDS latency in front of every
-// matrix-core instruction.  Completion is tracked here by hand (wait_vmcnt + barrier).
-// The instruction takes its LDS base from M0, written here just before it with one wait
-// state between the write and the use.  Nothing else in these kernels uses M0 (no LDS
-// DMA builtin, no dynamically indexed register arrays), so no value of it is lost.
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-// 16 bytes per lane: lane l writes lds_base + 16 l; its source is sbase + voff, with sbase
-// wave-uniform.
-__device__ __forceinline__ void lds_dma16(void* lds_base, const void* sbase, uint32_t voff) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff),
-               "s"(uniform_ptr(sbase))
-               : "memory");
-}
+// Memory -> LDS copies (global_load_lds / buffer_load ... lds).  They are issued from inline
+// assembly rather than the compiler builtins: with the builtin, the compiler waits for
+// every outstanding LDS read before each later LDS read, which exposes the LDS latency in
+// front of every matrix-core instruction.  Completion is tracked here by hand (wait_vmcnt +
+// barrier).  The instructions take their LDS base from M0, written here just before each
+// with one wait state between the write and the use.  Nothing else in these kernels uses
+// M0 (no LDS DMA builtin, no dynamically indexed register arrays), so no value is lost.
 // 4 bytes per lane: lane l writes lds_base + 4 l; its source is the per-lane address src.
 __device__ __forceinline__ void lds_dma4(void* lds_base, const void* src) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
@@ -147,38 +133,59 @@ __device__ __forceinline__ void lds_dma4(void* lds_base, const void* src) {
                : "memory");
 }
 
-// Asynchronous copy of ROWS rows (row r from g + min(row0 + r, rowmax) * stride elements)
-// into a swizzled LDS tile, straight from memory to LDS.  Each wave-instruction moves 1 KB
-// (64 lanes x 16 bytes) to consecutive LDS; wave `wave` of NW issues instructions wave,
-// wave+NW, ...; dma_rows_one issues this wave's k-th one, so callers can spread a copy
-// over a loop of matrix instructions instead of stalling on a burst of copies.  The row
-// pointer of an instruction is wave-uniform, so each lane only carries a 32-bit offset.
-// Nothing is waited for here: the caller waits with wait_vmcnt and a barrier.  `wave`
-// must be wave-uniform, row0 <= rowmax.
+// Asynchronous copy of a tile of ROWS rows into a swizzled LDS tile, straight from memory
+// to LDS with buffer loads (buffer_load_dwordx4 ... lds).  The source is described once per
+// tile (TileSrc: a buffer resource based at the tile's first row whose range covers only its
+// first `nvalid` rows); rows past them read as zeros through the buffer range check, so
+// ragged tiles need no clamping.  Each wave-instruction moves 1 KB (64 lanes x 16 bytes) to
+// consecutive LDS; wave `wave` of NW issues instructions wave, wave+NW, ...; dma_rows_one
+// issues this wave's k-th one, so callers can spread a copy over a loop of matrix
+// instructions.  Per instruction this costs one M0 write and a couple of address
+// instructions, where a global-address copy needed a 64-bit row address computation.
+// Nothing is waited for here: the caller waits with wait_vmcnt and a barrier.  `wave` must
+// be wave-uniform.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+struct TileSrc {
+  i32x4 rsrc;
+  uint32_t row_bytes;
+};
+
+template <int ROWS>
+__device__ __forceinline__ TileSrc tile_src(const bf16* g, int64_t stride, int row0, int nvalid) {
+  nvalid = min(max(nvalid, 0), ROWS);
+  const uint64_t p = (uint64_t)(uintptr_t)(g + (int64_t)row0 * stride);
+  TileSrc t;
+  t.row_bytes = (uint32_t)(stride * 2);
+  t.rsrc[0] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  t.rsrc[1] = (int32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu);  // stride field 0
+  t.rsrc[2] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)nvalid * t.row_bytes);  // bytes in range
+  t.rsrc[3] = 0x00020000;                                                                // raw 32-bit data
+  return t;
+}
+
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_rows_one(bf16* tile, const bf16* g, int64_t stride, int row0, int rowmax,
-                                             int wave, int lane, int k) {
+__device__ __forceinline__ void dma_rows_one(bf16* tile, const TileSrc& src, int wave, int lane, int k) {
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RPI = 64 / CH;   // rows per wave-instruction
   constexpr int NI = ROWS / RPI;
   static_assert(CH >= 16 && 64 % CH == 0, "row must be 256..1024 bytes");
   static_assert(NI % NW == 0, "tile must split evenly over the waves");
   const int i = wave + k * NW;
-  const int brow = min(row0 + i * RPI, rowmax);                 // wave-uniform
-  const int trow = i * RPI + lane / CH;                         // row within the tile
-  const int lrow = min(row0 + trow, rowmax);
-  const uint32_t voff = (uint32_t)((int64_t)(lrow - brow) * stride * 2) +
-                        (uint32_t)(16 * ((lane % CH) ^ swz_h(trow)));
-  lds_dma16(tile + i * RPI * D, reinterpret_cast<const char*>(g + (int64_t)brow * stride), voff);
+  const int trow = i * RPI + lane / CH;  // row within the tile
+  const uint32_t voff = (uint32_t)trow * src.row_bytes + (uint32_t)(16 * ((lane % CH) ^ swz_h(trow)));
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + i * RPI * D));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(src.rsrc)
+               : "memory");
 }
 
 // All of this wave's instructions of one tile copy, back to back.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_rows(bf16* tile, const bf16* g, int64_t stride, int row0,
-                                         int rowmax, int wave, int lane) {
+__device__ __forceinline__ void dma_rows(bf16* tile, const TileSrc& src, int wave, int lane) {
   constexpr int NK = ROWS * D / 512 / NW;
 #pragma unroll
-  for (int k = 0; k < NK; ++k) dma_rows_one<D, ROWS, NW>(tile, g, stride, row0, rowmax, wave, lane, k);
+  for (int k = 0; k < NK; ++k) dma_rows_one<D, ROWS, NW>(tile, src, wave, lane, k);
 }
 
 template <int D, int ROWS, int NW>

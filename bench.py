@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 TRAFFIC = {
     "attn_fwd": ("profiles/attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512"),
     "bwd_dkdv": ("profiles/bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512>"),
-    "bwd_dq": ("profiles/bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<512>"),
+    "bwd_dq": ("profiles/bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2>"),
     "decode_split": ("profiles/decode_split_d128_B64_traffic.txt", "decode_split_kernel<4>"),
 }
 

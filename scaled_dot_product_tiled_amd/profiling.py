@@ -11,6 +11,10 @@
         directories: the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
         by the copy run's bytes per counter unit, with the sha256 of the kernel's source file.
 
+    python -m scaled_dot_product_tiled_amd.profiling summaries OUT
+        writes the profiles/ summaries of the bench.py workloads from OUT/{stats,fetch,write,
+        cfetch,cwrite} (the five rocprofv3 runs listed in each summary).
+
 bench.py reads such records back (read_traffic) and reports the traffic only while the
 source file still has the recorded hash.
 """
@@ -44,7 +48,10 @@ def counter_per_dispatch(d: str, counter: str) -> Dict[str, List[float]]:
 
 
 def _pick(values: Dict[str, List[float]], kernel: str) -> List[float]:
-    names = [n for n in values if kernel in n]
+    """The values of the one kernel whose name contains `kernel` (spaces ignored, so that a
+    template argument list can be written without them)."""
+    key = kernel.replace(" ", "")
+    names = [n for n in values if key in n.replace(" ", "")]
     if len(names) != 1:
         raise KeyError(f"{kernel!r} matches {names}")
     return values[names[0]]
@@ -112,6 +119,75 @@ def stats_table(d: str) -> str:
     return "\n".join(lines)
 
 
+COMMANDS = """Commands (cd /tmp && export TMPDIR=/tmp first; R = repository root, OUT = an output directory):
+  rocprofv3 --kernel-trace --stats -d $OUT/stats --output-format csv -- python3 $R/bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-other
+  rocprofv3 --pmc FETCH_SIZE -d $OUT/fetch --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --decode-steps 4 --no-cpu-baseline --no-other
+  rocprofv3 --pmc WRITE_SIZE -d $OUT/write --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --decode-steps 4 --no-cpu-baseline --no-other
+  rocprofv3 --pmc FETCH_SIZE -d $OUT/cfetch --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
+  rocprofv3 --pmc WRITE_SIZE -d $OUT/cwrite --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
+  python3 -m scaled_dot_product_tiled_amd.profiling summaries $OUT
+"""
+
+# (file, kernel name, source, what, algorithmic bytes) of each traffic summary
+TRAFFIC_SUMMARIES = [
+    ("attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512", "scaled_dot_product_tiled_amd/csrc/attn_fwd.hip",
+     "forward kernel, causal GQA B=2 S=4096 Hq=32 Hkv=4 D=512 (bench.py workload)",
+     "Algorithmic bytes: Q, K, V read once (268 + 33.5 + 33.5 MB) and O, LSE written once (268 + 1 MB).  "
+     "The fetch figure counts every L2 miss sent to the fabric (the 256 MB last-level cache can serve part "
+     "of it); above the algorithmic reads it is the K/V re-reads of the query-row tiles of each head group."),
+    ("bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
+     "dK/dV kernel of the backward, causal GQA B=2 S=4096 Hq=32 Hkv=4 D=512 (bench.py workload)",
+     "Algorithmic bytes: Q, dO read once (268 MB each), K, V (33.5 MB each), LSE and delta (1 MB each); "
+     "writes dK, dV (33.5 MB each) and the stored dS blocks (1.107 GB).  Fetch above the algorithmic reads "
+     "is the Q / dO re-reads of the 64 key tiles of each head group that miss in L2."),
+    ("bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
+     "dQ kernel of the backward (dQ = scale dS K over the stored dS blocks, two head_dim halves), same workload",
+     "Algorithmic bytes: dS blocks read once (1.107 GB), K (33.5 MB); dQ written once (268 MB).  Each dS "
+     "block is read by both head_dim halves; the second read is meant to hit in L2."),
+    ("decode_split_d128_B64_traffic.txt", "decode_split_kernel<4>", "scaled_dot_product_tiled_amd/csrc/attn_decode.hip",
+     "paged decode split kernel, B=64 Hq=32 Hkv=8 D=128, 16-token pages, contexts U{512..4096} "
+     "(bench.py decode workload)",
+     "Algorithmic bytes: K and V of every context token once (619.6 MB per launch, the bench's "
+     "bytes_per_launch); writes the chunk partials (about 5.5 MB)."),
+]
+
+
+def write_summaries(out: str, pdir: str) -> None:
+    import json
+    for fn, k, src, what, note in TRAFFIC_SUMMARIES:
+        rec = traffic_record(k, os.path.join(ROOT, src), os.path.join(out, "fetch"), os.path.join(out, "write"),
+                             os.path.join(out, "cfetch"), os.path.join(out, "cwrite"), 1024)
+        kv = dict(t.split("=", 1) for t in rec[len("record:"):].split())
+        txt = (f"HBM traffic per dispatch: {what}\n\n"
+               "rocprofv3 counters FETCH_SIZE and WRITE_SIZE (one pass each, averaged over the dispatches of the\n"
+               "kernel), scaled by the same counters read for a plain 1 GiB device copy: bytes per counter unit\n"
+               f"{kv['fetch_scale']} (FETCH_SIZE) and {kv['write_scale']} (WRITE_SIZE).\n\n"
+               f"  fetched {int(kv['fetch_bytes']) / 1e9:.3f} GB   written {int(kv['write_bytes']) / 1e9:.3f} GB   "
+               "per dispatch\n\n"
+               f"{note}\n\n{COMMANDS}\n"
+               "bench.py reads the record line below for its roofline \"traffic\" field, as long as the kernel\n"
+               f"source still has the recorded sha256.\n\n{rec}\n")
+        with open(os.path.join(pdir, fn), "w") as fh:
+            fh.write(txt)
+    line = None
+    for f in glob.glob(os.path.join(out, "**", "*.log"), recursive=True) + [os.path.join(out, "bench_stats.log")]:
+        if os.path.exists(f):
+            for ln in open(f):
+                if ln.startswith('{"metric"'):
+                    line = json.loads(ln)
+    txt = ("Kernel times of bench.py on one MI355X: causal GQA forward + backward, B=2 S=4096 Hq=32 Hkv=4\n"
+           "D=512 (10 timed + 3 warm-up steps, plus the per-call and per-kernel passes) and the paged decode\n"
+           "B=64 Hq=32 Hkv=8 D=128.\n\n"
+           f"{COMMANDS}\n{stats_table(os.path.join(out, 'stats'))}\n")
+    if line is not None:
+        txt += "\nbench.py's own HIP-event timings of the same run (ms per launch):\n"
+        for n, v in list(line["kernels"].items()) + list(line["decode"]["kernels"].items()):
+            txt += f"  {n:14s} {v['ms_avg']:.4f}\n"
+        txt += f"\nbench.py line: value {line['value']} TFLOP/s, ms_per_step {line['ms_per_step']}\n"
+    with open(os.path.join(pdir, "bench_d512_B2_S4096_kernel_stats.txt"), "w") as fh:
+        fh.write(txt)
+
+
 def run_copy(mib: int, reps: int) -> None:
     import torch
     a = torch.ones(mib << 20, dtype=torch.uint8, device="cuda:0")
@@ -134,11 +210,16 @@ def main(argv=None) -> int:
     for name in ("kernel", "source", "fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument("--" + name, required=True)
     t.add_argument("--copy-mib", type=int, default=1024)
+    w = sub.add_parser("summaries")
+    w.add_argument("out")
+    w.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     a = p.parse_args(argv)
     if a.cmd == "copy":
         run_copy(a.mib, a.reps)
     elif a.cmd == "stats":
         print(stats_table(a.dir))
+    elif a.cmd == "summaries":
+        write_summaries(a.out, a.profiles)
     else:
         print(traffic_record(a.kernel, a.source, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib))
     return 0

@@ -27,7 +27,10 @@ Readings adopted where the pages are silent (each is listed in the design notes)
   mask is all False must stay safe);
 * LSE is the natural-log log-sum-exp of the scaled scores of the visible keys;
 * the paged decode query sits at position ctx_b - 1 and sees every cached
-  token t < ctx_b (fourth page, Architecture notes: PagedKVCache + PageTable).
+  token t < ctx_b (fourth page, Architecture notes: PagedKVCache + PageTable);
+* a chunk pair of the ring path (first page, Integration) places query i at position
+  q_pos0 + i and key j at k_pos0 + j; a row that sees no key of the chunk has LSE = -inf
+  (the identity of the log-sum-exp merge) and O = 0.
 """
 from __future__ import annotations
 
@@ -39,6 +42,7 @@ __all__ = [
     "attention_forward_head", "attention_backward_group",
     "attention_forward_packed", "attention_backward_packed",
     "gather_pages", "paged_decode", "paged_decode_one", "attention_rows",
+    "chunk_visibility", "attention_forward_chunk", "attention_backward_chunk", "lse_merge",
 ]
 
 
@@ -265,6 +269,92 @@ def attention_backward_packed(q, k, v, do, cu_seqlens, scale, causal=True, windo
             dq[s0:s0 + n, h] = a
             dk[s0:s0 + n, g] += bk
             dv[s0:s0 + n, g] += bv
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Chunks of a sequence: the unit of ring context parallelism.  The first page routes the
+# full-attention chunks of its ring path through the fused kernel (section Integration:
+# dense or varlen per chunk); a chunk pair is a query chunk against one key/value chunk at
+# known positions, and the partial results of a row over its key chunks are combined by
+# their log-sum-exp.
+# ---------------------------------------------------------------------------
+def chunk_visibility(nq: int, nk: int, q_pos0: int, k_pos0: int, causal: bool, window: int) -> np.ndarray:
+    """(nq, nk) bool: query i sits at position q_pos0 + i and key j at k_pos0 + j; the key is
+    visible when k_pos <= q_pos (causal) and k_pos > q_pos - W (window W > 0)."""
+    qp = q_pos0 + np.arange(nq)[:, None]
+    kp = k_pos0 + np.arange(nk)[None, :]
+    vis = np.ones((nq, nk), dtype=bool)
+    if causal:
+        vis &= kp <= qp
+    if window > 0:
+        vis &= kp > qp - window
+    return vis
+
+
+def attention_forward_chunk(q, k, v, scale, causal, window, q_pos0, k_pos0):
+    """Partial attention of a query chunk q (B, Sq, Hq, D) against one key/value chunk k, v
+    (B, Sk, Hkv, D): O (B, Sq, Hq, D) and LSE (B, Hq, Sq) over the chunk's visible keys.  A row
+    that sees no key of the chunk gets O = 0 and LSE = -inf, the identity of lse_merge."""
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    r = Hq // Hkv
+    vis = chunk_visibility(Sq, Sk, q_pos0, k_pos0, causal, window)
+    live = vis.any(axis=1)
+    o = np.zeros((B, Sq, Hq, D))
+    lse = np.full((B, Hq, Sq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            ob, lb, _ = unit_forward(q[b, :, h], k[b, :, h // r], v[b, :, h // r], scale, vis)
+            o[b, :, h] = ob
+            lse[b, h] = np.where(live, lb, -np.inf)
+    return o, lse
+
+
+def lse_merge(o_a, lse_a, o_b, lse_b):
+    """Combine two partial results of the same rows over disjoint key sets:
+    L = ln(e^La + e^Lb), O = e^(La - L) O_a + e^(Lb - L) O_b.  A partial with LSE = -inf adds
+    nothing; two of them give O = 0, LSE = -inf.  o: (B, S, H, D), lse: (B, H, S)."""
+    m = np.maximum(lse_a, lse_b)
+    live = np.isfinite(m)
+    m0 = np.where(live, m, 0.0)
+    wa = np.exp(lse_a - m0)              # exp(-inf) = 0
+    wb = np.exp(lse_b - m0)
+    tot = wa + wb
+    lse = np.where(live, m0 + np.log(np.where(live, tot, 1.0)), -np.inf)
+    tot_safe = np.where(live, tot, 1.0)
+    fa = np.transpose(wa / tot_safe, (0, 2, 1))[..., None]   # (B, S, H, 1)
+    fb = np.transpose(wb / tot_safe, (0, 2, 1))[..., None]
+    return fa * o_a + fb * o_b, lse
+
+
+def attention_backward_chunk(q, k, v, o, lse, do, scale, causal, window, q_pos0, k_pos0):
+    """Gradient contributions of one (query chunk, key chunk) pair, given the rows' final O
+    (B, Sq, Hq, D) and LSE (B, Hq, Sq) over all their keys: P = exp(scale q k^T - LSE) on the
+    chunk's visible entries, delta = rowsum(dO * O), dS = P (dP - delta), dQ = scale dS k,
+    dK = scale dS^T q and dV = P^T dO (dK, dV summed over the group's query heads).  Summing
+    dQ over a row's key chunks, and dK, dV over a key chunk's query chunks, gives the full
+    gradients."""
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    r = Hq // Hkv
+    vis = chunk_visibility(Sq, Sk, q_pos0, k_pos0, causal, window)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // r
+            s = scale * (q[b, :, h] @ k[b, :, g].T)
+            live = np.isfinite(lse[b, h])[:, None]       # a row that sees no key has no gradient
+            arg = np.where(vis & live, s - np.where(live, lse[b, h][:, None], 0.0), -np.inf)
+            p = np.exp(arg)
+            dp = do[b, :, h] @ v[b, :, g].T
+            delta = (do[b, :, h] * o[b, :, h]).sum(axis=1)
+            ds = p * (dp - delta[:, None])
+            dq[b, :, h] = scale * (ds @ k[b, :, g])
+            dk[b, :, g] += scale * (ds.T @ q[b, :, h])
+            dv[b, :, g] += p.T @ do[b, :, h]
     return dq, dk, dv
 
 

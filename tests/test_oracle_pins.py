@@ -11,7 +11,9 @@
 * an independent library routine: torch's float64 CPU scaled_dot_product_attention with an
   explicit boolean mask and autograd, which shares nothing with the oracle;
 * the paged decode equals causal attention's last row on the gathered tokens, and does not
-  depend on which pool pages hold them.
+  depend on which pool pages hold them;
+* chunk pairs (ring context parallelism) merge, by log-sum-exp, to the full attention, and
+  their gradient parts sum to the full gradients.
 """
 import json
 import math
@@ -381,3 +383,75 @@ def test_row_sampled_oracle_equals_full_unit():
             np.testing.assert_allclose(ro, o[b, rows, h], atol=1e-13)
             np.testing.assert_allclose(rl, lse[b, h, rows], atol=1e-13)
             np.testing.assert_allclose(rdq, dq[b, rows, h], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Chunks of a sequence (ring context parallelism): pinned to the full oracle by the
+# decomposition identity -- a row's attention over all keys is the log-sum-exp merge of its
+# attention over disjoint key chunks, and the gradients are sums of per-chunk-pair parts.
+# ---------------------------------------------------------------------------
+def _chunk_inputs(seed, B=2, S=24, Hq=4, Hkv=2, D=8):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for H in (Hq, Hkv, Hkv, Hq))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("causal,window,C", [(True, 0, 8), (True, 5, 8), (False, 0, 6), (True, 11, 6)])
+def test_chunked_forward_merges_to_full_attention(causal, window, C):
+    q, k, v, _ = _chunk_inputs(1)
+    S = q.shape[1]
+    scale = 0.37
+    fo, fl = oracle.attention_forward(q, k, v, scale, causal, window)
+    for q0 in range(0, S, C):
+        o = np.zeros_like(q[:, q0:q0 + C])
+        lse = np.full((q.shape[0], q.shape[2], C), -np.inf)
+        for k0 in range(0, S, C):   # every key chunk, fully masked ones included
+            po, pl = oracle.attention_forward_chunk(q[:, q0:q0 + C], k[:, k0:k0 + C], v[:, k0:k0 + C], scale,
+                                                    causal, window, q0, k0)
+            o, lse = oracle.lse_merge(o, lse, po, pl)
+        np.testing.assert_allclose(o, fo[:, q0:q0 + C], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, fl[:, :, q0:q0 + C], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,window,C", [(True, 0, 8), (True, 7, 12), (False, 0, 8)])
+def test_chunked_backward_sums_to_full_gradients(causal, window, C):
+    q, k, v, do = _chunk_inputs(2)
+    S = q.shape[1]
+    scale = 0.29
+    fo, fl = oracle.attention_forward(q, k, v, scale, causal, window)
+    fq, fk, fv = oracle.attention_backward(q, k, v, do, scale, causal, window)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for q0 in range(0, S, C):
+        for k0 in range(0, S, C):
+            a, b_, c_ = oracle.attention_backward_chunk(q[:, q0:q0 + C], k[:, k0:k0 + C], v[:, k0:k0 + C],
+                                                        fo[:, q0:q0 + C], fl[:, :, q0:q0 + C], do[:, q0:q0 + C],
+                                                        scale, causal, window, q0, k0)
+            dq[:, q0:q0 + C] += a
+            dk[:, k0:k0 + C] += b_
+            dv[:, k0:k0 + C] += c_
+    for got, ref in ((dq, fq), (dk, fk), (dv, fv)):
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
+def test_chunk_rows_without_keys_and_merge_identity():
+    q, k, v, _ = _chunk_inputs(3, S=8)
+    # a key chunk entirely after the query chunk: causal rows see nothing of it
+    o, lse = oracle.attention_forward_chunk(q, k, v, 0.5, True, 0, 0, 8)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+    # merging with that empty partial returns the other partial unchanged
+    po, pl = oracle.attention_forward_chunk(q, k, v, 0.5, True, 0, 0, 0)
+    mo, ml = oracle.lse_merge(po, pl, o, lse)
+    np.testing.assert_array_equal(mo, po)
+    np.testing.assert_array_equal(ml, pl)
+    # the merge is symmetric and agrees with the closed form for two keys, one per chunk
+    s1, s2 = 0.3, -1.1
+    oa = np.full((1, 1, 1, 1), 2.0)
+    ob = np.full((1, 1, 1, 1), -5.0)
+    mo, ml = oracle.lse_merge(oa, np.full((1, 1, 1), s1), ob, np.full((1, 1, 1), s2))
+    mo2, ml2 = oracle.lse_merge(ob, np.full((1, 1, 1), s2), oa, np.full((1, 1, 1), s1))
+    w1 = math.exp(s1) / (math.exp(s1) + math.exp(s2))
+    assert abs(float(mo[0, 0, 0, 0]) - (2.0 * w1 - 5.0 * (1 - w1))) < 1e-14
+    assert abs(float(ml[0, 0, 0]) - math.log(math.exp(s1) + math.exp(s2))) < 1e-14
+    assert np.array_equal(mo, mo2) and np.array_equal(ml, ml2)

@@ -48,6 +48,9 @@ typedef enum {
     ATTN_ERR_HIP = 4           /* a HIP runtime call failed; see attn_last_hip_error() */
 } attn_status;
 
+/* Element type of an output that can be kept in either precision. */
+enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_F32 = 1 };
+
 /* A bf16 tensor: device pointer plus element strides of the batch, sequence and
  * head dimensions (the head_dim dimension is contiguous).  For packed
  * (cu_seqlens) rows stride_b is ignored. */
@@ -122,6 +125,86 @@ attn_status attn_bwd(const attn_shape* shape,
                      attn_tensor dq, attn_tensor dk, attn_tensor dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sizes of one chunk pair of a sequence split into chunks (ring context parallelism).
+ *   B       batch
+ *   Sq      query rows of the query chunk; Sk key/value rows of the key/value chunk
+ *           (each below 2^28)
+ *   Hq, Hkv, D as in attn_shape */
+typedef struct {
+    int32_t B, Sq, Sk, Hq, Hkv, D;
+} attn_chunk_shape;
+
+/*
+ * attn_fwd_chunk: partial attention of one query chunk against one key/value chunk of
+ * the same sequences.  The ring path of the page "Gemma4 FFPA attention backend support
+ * for accelerating Gemma4-family training" (section Integration) runs the fused kernel on
+ * full-attention chunks; a rank holds one query chunk, sees the key/value chunks one ring
+ * step at a time, and combines the partial results with attn_lse_merge.
+ *
+ * Query row i of the chunk sits at sequence position q_pos0 + i and key row j at
+ * k_pos0 + j (both >= 0); the mask compares positions: key visible when k_pos <= q_pos
+ * (causal) and k_pos > q_pos - window (window > 0, requires causal).
+ *   q      dense bf16 (B, Sq, Hq, D); k, v dense bf16 (B, Sk, Hkv, D)
+ *   o      (B, Sq, Hq, D), written, element type o_dtype: ATTN_DTYPE_F32 for a partial
+ *          that attn_lse_merge will combine (the row is then rounded to bf16 once, at
+ *          the last merge), ATTN_DTYPE_BF16 for a pair that is the row's only one
+ *   lse    device fp32 (B, Hq, Sq) contiguous, written: natural-log log-sum-exp of the
+ *          row's scaled visible scores in this chunk, or -inf for a row that sees no
+ *          key of the chunk (its O is 0); -inf is the identity of attn_lse_merge
+ * No workspace.  Other conventions as attn_fwd.
+ */
+attn_status attn_fwd_chunk(const attn_chunk_shape* shape,
+                           attn_tensor q, attn_tensor k, attn_tensor v,
+                           float scale, int causal, int window,
+                           int64_t q_pos0, int64_t k_pos0,
+                           attn_tensor o, int o_dtype, float* lse, void* stream);
+
+/*
+ * attn_bwd_chunk: the gradient parts of one chunk pair.  o and lse are the query rows'
+ * final results, merged over every key chunk the rows attend to (not this pair's
+ * partial), and dout is the gradient of the loss with respect to that final O.  With
+ * P = exp(scale Q K^T - lse) on the pair's visible entries (0 elsewhere) and
+ * dS = P * (dO V^T - rowsum(dO * o)), it writes
+ *   dq  (B, Sq, Hq, D):  scale dS K,
+ *   dk, dv (B, Sk, Hkv, D):  scale dS^T Q and P^T dO, summed over each kv head's
+ *       query heads.
+ * Summed over the key chunks of a query chunk (dq) and over the query chunks of a key
+ * chunk (dk, dv), the parts are the gradients of attention over the whole sequence.  The
+ * parts are written, not accumulated, in bf16; the caller sums them (in fp32 for the
+ * best accuracy).  A row that sees no key of the pair gets dq = 0; a key that no row of
+ * the pair sees gets dk = dv = 0.
+ *   workspace  at least attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0,
+ *              k_pos0) bytes, 256-byte aligned (row statistics and dS blocks, as attn_bwd)
+ * Other conventions as attn_bwd.
+ */
+attn_status attn_bwd_chunk(const attn_chunk_shape* shape,
+                           attn_tensor q, attn_tensor k, attn_tensor v,
+                           attn_tensor o, const float* lse, attn_tensor dout,
+                           float scale, int causal, int window,
+                           int64_t q_pos0, int64_t k_pos0,
+                           attn_tensor dq, attn_tensor dk, attn_tensor dv,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_lse_merge: combine two partial results of the same query rows over disjoint key
+ * sets (the ring path's per-step results, first page, section Integration), in place:
+ *   L = ln(e^lse + e^lse_part),  o = e^(lse - L) o + e^(lse_part - L) o_part,  lse = L.
+ * A partial with LSE = -inf contributes nothing (its O is not read into the result);
+ * two such partials give o = 0 and lse = -inf.
+ *   o, o_part       fp32 (B, S, H, D) with attn_tensor strides (element strides,
+ *                   multiples of 8, 16-byte aligned); o is updated; the two must not
+ *                   overlap
+ *   lse, lse_part   device fp32 (B, H, S) contiguous; lse is updated
+ *   out             bf16 (B, S, H, D): if out.ptr is not NULL, the merged o rounded to
+ *                   bf16 (round to nearest even) is also written there, for the last
+ *                   merge of a row
+ *   D               128, 256 or 512
+ */
+attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D,
+                           attn_tensor o, float* lse,
+                           attn_tensor o_part, const float* lse_part,
+                           attn_tensor out, void* stream);
+
 /* Sizes of one paged decode call.
  *   B                 sequences, one query token each
  *   Hq, Hkv, D        heads and head_dim (D = 128)
@@ -167,6 +250,9 @@ attn_status paged_decode(const attn_decode_shape* shape,
 size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen);
 size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen, int causal, int window);
 size_t paged_decode_workspace_bytes(const attn_decode_shape* shape);
+/* For attn_bwd_chunk; 0 for arguments that it would reject. */
+size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal, int window,
+                                      int64_t q_pos0, int64_t k_pos0);
 
 /* Static string for a status code. */
 const char* attn_status_str(attn_status status);

@@ -29,6 +29,11 @@ class AttnShape(ctypes.Structure):
                 ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32)]
 
 
+class AttnChunkShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
 class AttnKernelTime(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_char_p), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
 
@@ -41,7 +46,8 @@ class AttnDecodeShape(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ("attn_fwd", "attn_bwd", "paged_decode", "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes",
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "paged_decode",
+           "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read")
 
@@ -64,6 +70,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, vp, AttnTensor, AttnTensor, AttnTensor,
                              vp, sz, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.attn_fwd_chunk.argtypes = [P(AttnChunkShape), AttnTensor, AttnTensor, AttnTensor, ctypes.c_float, ctypes.c_int,
+                                   ctypes.c_int, i64, i64, AttnTensor, ctypes.c_int, vp, vp]
+    lib.attn_fwd_chunk.restype = ctypes.c_int
+    lib.attn_bwd_chunk.argtypes = [P(AttnChunkShape), AttnTensor, AttnTensor, AttnTensor, AttnTensor, vp, AttnTensor,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, i64, i64, AttnTensor, AttnTensor,
+                                   AttnTensor, vp, sz, vp]
+    lib.attn_bwd_chunk.restype = ctypes.c_int
+    lib.attn_bwd_chunk_workspace_bytes.argtypes = [P(AttnChunkShape), ctypes.c_int, ctypes.c_int, i64, i64]
+    lib.attn_bwd_chunk_workspace_bytes.restype = sz
+    lib.attn_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, AttnTensor, vp,
+                                   AttnTensor, vp, AttnTensor, vp]
+    lib.attn_lse_merge.restype = ctypes.c_int
     lib.paged_decode.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int64, ctypes.c_int64, AttnTensor, AttnTensor,
                                  vp, vp, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz, vp]
     lib.paged_decode.restype = ctypes.c_int
@@ -102,6 +121,37 @@ def _bf16(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name}: the head_dim dimension must be contiguous")
 
 
+def _expect(t: torch.Tensor, shape, name: str) -> None:
+    """Every tensor's sizes are checked against the call's shape; the library reads each tensor
+    through its own strides, so a mismatched tensor would be read past its end."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != torch.device("cuda", torch.cuda.current_device()):
+        raise ValueError(f"{name} must live on the current device")
+
+
+def _check_attn_shapes(shape, packed, q, k, v, lse=None, o=None, **grads) -> None:
+    """q, o, dout, dq: (B,S,Hq,D) or packed (T,Hq,D); k, v, dk, dv: (B,S,Hkv,D) or (T,Hkv,D)."""
+    if packed:
+        qs, ks = (shape.total, shape.Hq, shape.D), (shape.total, shape.Hkv, shape.D)
+        ls = (shape.Hq, shape.total)
+    else:
+        qs, ks = (shape.B, shape.S, shape.Hq, shape.D), (shape.B, shape.S, shape.Hkv, shape.D)
+        ls = (shape.B, shape.Hq, shape.S)
+    _expect(k, ks, "k")
+    _expect(v, ks, "v")
+    for n, t in (("o", o), ("dout", grads.get("dout")), ("dq", grads.get("dq"))):
+        if t is not None:
+            _expect(t, qs, n)
+    for n, t in (("dk", grads.get("dk")), ("dv", grads.get("dv"))):
+        if t is not None:
+            _expect(t, ks, n)
+    if lse is not None:
+        _expect(lse, ls, "lse")
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise TypeError("lse must be a contiguous float32 tensor")
+
+
 def _tensor(t: torch.Tensor, packed: bool) -> AttnTensor:
     if packed:   # (T, H, D)
         return AttnTensor(t.data_ptr(), 0, t.stride(0), t.stride(1))
@@ -124,6 +174,8 @@ def _shape(q, k, cu_seqlens, pad_mask, max_seqlen):
         B, S, Hq, D = q.shape
         T = 0
     Hkv = k.shape[-2]
+    if pad_mask is not None and tuple(pad_mask.shape) != (B, S):
+        raise ValueError(f"pad_mask must be (B, S) = {(B, S)}, got {tuple(pad_mask.shape)}")
     return AttnShape(B, S, T, Hq, Hkv, D), packed, (2 if packed else (1 if pad_mask is not None else 0))
 
 
@@ -158,6 +210,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
     if lse is None:
         lse_shape = (shape.Hq, shape.total) if packed else (shape.B, shape.Hq, shape.S)
         lse = torch.empty(lse_shape, device=q.device, dtype=torch.float32)
+    _check_attn_shapes(shape, packed, q, k, v, lse=lse, o=out)
     cu, pm = _meta_ptrs(cu_seqlens, pad_mask)
     nbytes = lib.attn_fwd_workspace_bytes(ctypes.byref(shape), varlen)
     ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
@@ -185,6 +238,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_attn_shapes(shape, packed, q, k, v, lse=lse, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
     cu, pm = _meta_ptrs(cu_seqlens, pad_mask)
     nbytes = lib.attn_bwd_workspace_bytes(ctypes.byref(shape), varlen, int(bool(causal)), int(window))
     ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
@@ -194,6 +248,109 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                       ws.data_ptr() if nbytes else None, nbytes, _stream())
     _check(st, "attn_bwd")
     return dq, dk, dv
+
+
+def _chunk_shape(q, k):
+    B, Sq, Hq, D = q.shape
+    return AttnChunkShape(B, Sq, k.shape[1], Hq, k.shape[2], D)
+
+
+def _check_chunk_shapes(shape, q, k, v, lse=None, o=None, **grads) -> None:
+    """q, o, dout, dq: (B,Sq,Hq,D); k, v, dk, dv: (B,Sk,Hkv,D); lse (B,Hq,Sq)."""
+    qs = (shape.B, shape.Sq, shape.Hq, shape.D)
+    ks = (shape.B, shape.Sk, shape.Hkv, shape.D)
+    _expect(q, qs, "q")
+    for n, t in (("k", k), ("v", v), ("dk", grads.get("dk")), ("dv", grads.get("dv"))):
+        if t is not None:
+            _expect(t, ks, n)
+    for n, t in (("o", o), ("dout", grads.get("dout")), ("dq", grads.get("dq"))):
+        if t is not None:
+            _expect(t, qs, n)
+    if lse is not None:
+        _expect(lse, (shape.B, shape.Hq, shape.Sq), "lse")
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise TypeError("lse must be a contiguous float32 tensor")
+
+
+def attn_fwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos0: int, k_pos0: int,
+                   scale: Optional[float] = None, causal: bool = True, window: int = 0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.float32) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Partial O, LSE of a query chunk q (B,Sq,Hq,D) at positions q_pos0.. against one key/value chunk
+    k/v (B,Sk,Hkv,D) at positions k_pos0..; rows that see no key get O = 0, LSE = -inf.  O is fp32
+    (a partial for attn_lse_merge) unless out_dtype is bfloat16."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _bf16(t, n)
+    shape = _chunk_shape(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.D)
+    if out is None:
+        out = torch.empty(tuple(q.shape), device=q.device, dtype=out_dtype)
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(-1) != 1 or not out.is_cuda:
+        raise TypeError("out must be a float32 or bfloat16 device tensor with a contiguous last dimension")
+    if lse is None:
+        lse = torch.empty((shape.B, shape.Hq, shape.Sq), device=q.device, dtype=torch.float32)
+    _check_chunk_shapes(shape, q, k, v, lse=lse, o=out)
+    st = lib.attn_fwd_chunk(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
+                            float(scale), int(bool(causal)), int(window), int(q_pos0), int(k_pos0),
+                            _tensor(out, False), 1 if out.dtype == torch.float32 else 0, lse.data_ptr(), _stream())
+    _check(st, "attn_fwd_chunk")
+    return out, lse
+
+
+def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                   dout: torch.Tensor, q_pos0: int, k_pos0: int, scale: Optional[float] = None,
+                   causal: bool = True, window: int = 0, dq: Optional[torch.Tensor] = None,
+                   dk: Optional[torch.Tensor] = None,
+                   dv: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradient parts dQ (B,Sq,Hq,D), dK, dV (B,Sk,Hkv,D) of one chunk pair, from the rows' final O and
+    LSE (merged over all their key chunks) and dO."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _bf16(t, n)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    shape = _chunk_shape(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_chunk_shapes(shape, q, k, v, lse=lse, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
+    c, w = int(bool(causal)), int(window)
+    nbytes = lib.attn_bwd_chunk_workspace_bytes(ctypes.byref(shape), c, w, int(q_pos0), int(k_pos0))
+    ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    st = lib.attn_bwd_chunk(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
+                            _tensor(o, False), lse.data_ptr(), _tensor(dout, False), float(scale), c, w,
+                            int(q_pos0), int(k_pos0), _tensor(dq, False), _tensor(dk, False), _tensor(dv, False),
+                            ws.data_ptr() if nbytes else None, nbytes, _stream())
+    _check(st, "attn_bwd_chunk")
+    return dq, dk, dv
+
+
+def attn_lse_merge(o: torch.Tensor, lse: torch.Tensor, o_part: torch.Tensor, lse_part: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> None:
+    """In place: (o, lse) <- log-sum-exp merge of (o, lse) and (o_part, lse_part); o, o_part (B,S,H,D) fp32,
+    lse, lse_part (B,H,S).  With out (B,S,H,D) bf16, the merged O rounded to bf16 is written there too."""
+    lib = load_library()
+    for t, n in ((o, "o"), (o_part, "o_part")):
+        if t.dtype != torch.float32 or not t.is_cuda or t.stride(-1) != 1:
+            raise TypeError(f"{n} must be a float32 device tensor with a contiguous last dimension")
+    for t, n in ((lse, "lse"), (lse_part, "lse_part")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise TypeError(f"{n} must be a contiguous float32 device tensor")
+    B, S, H, D = o.shape
+    _expect(o_part, (B, S, H, D), "o_part")
+    _expect(lse, (B, H, S), "lse")
+    _expect(lse_part, (B, H, S), "lse_part")
+    if out is not None:
+        _bf16(out, "out")
+        _expect(out, (B, S, H, D), "out")
+    st = lib.attn_lse_merge(B, S, H, D, _tensor(o, False), lse.data_ptr(), _tensor(o_part, False),
+                            lse_part.data_ptr(), _tensor(out, False) if out is not None else AttnTensor(None, 0, 0, 0),
+                            _stream())
+    _check(st, "attn_lse_merge")
 
 
 def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
@@ -212,6 +369,13 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = torch.empty_like(q) if out is None else out
+    _expect(v_cache, tuple(k_cache.shape), "v_cache")
+    _expect(out, (B, Hq, D), "out")
+    _expect(ctx_lens, (B,), "ctx_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be (B, max_pages_per_seq), got {tuple(block_table.shape)}")
+    if k_cache.shape[3] != D:
+        raise ValueError("k_cache head_dim differs from q's")
     nbytes = lib.paged_decode_workspace_bytes(ctypes.byref(shape))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)

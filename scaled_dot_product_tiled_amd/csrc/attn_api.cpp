@@ -41,13 +41,7 @@ attn_status check_shape(const attn_shape* s, int varlen) {
   return ATTN_OK;
 }
 
-size_t meta_bytes(const attn_shape* s, int varlen) {
-  return varlen ? round_up(2 * sizeof(int32_t) * (size_t)s->B) : 0;
-}
-
-size_t stat_elems(const attn_shape* s, int varlen) {
-  return (size_t)s->Hq * (varlen == 2 ? (size_t)s->total : (size_t)s->B * s->S);
-}
+size_t meta_bytes(int B, int varlen) { return varlen ? round_up(2 * sizeof(int32_t) * (size_t)B) : 0; }
 
 int varlen_kind(const int32_t* cu, const uint8_t* mask) { return cu ? 2 : (mask ? 1 : 0); }
 
@@ -114,27 +108,70 @@ void plan_rows(attn::AttnArgs& a, int rows) {
   a.per_xcd = (a.total_items + 7) / 8;
 }
 
-void fill_common(attn::AttnArgs& a, const attn_shape* s, int varlen, float scale, int causal, int window,
-                 const int32_t* meta) {
-  a.B = s->B;
-  a.S = s->S;
-  a.Hq = s->Hq;
-  a.Hkv = s->Hkv;
-  a.r = s->Hq / s->Hkv;
-  a.packed = varlen == 2;
-  a.causal = causal ? 1 : 0;
-  a.window = window;
+// One forward or backward call, whole sequences or a chunk pair, after argument checks.
+struct Call {
+  int B, S, Sk, total, Hq, Hkv, D;
+  int varlen;          // 0 dense, 1 pad_mask, 2 cu_seqlens
+  int causal, window;  // window normalised (see normalise_offsets)
+  int shift;           // query position offset of the chunk pair; 0 for whole sequences
+  int empty_lse_ninf;  // chunk pairs: a row with no visible key has LSE = -inf
+};
+
+// Visibility of (query i, key j) depends only on d = i + delta - j, the distance of their
+// positions, over i < S and j < Sk: visible when d >= 0 (causal) and d < window (window > 0).
+// This rewrites (delta, window) into an equivalent pair with delta in [-S, Sk] and window in
+// [0, S + Sk - 1], so that every position sum inside the kernels fits in 32 bits.
+void normalise_offsets(Call& c, int64_t delta) {
+  if (!c.causal) {  // every pair is visible; positions do not matter
+    c.shift = 0;
+    c.window = 0;
+    return;
+  }
+  const int64_t dmax = delta + c.S - 1, dmin = delta - (c.Sk - 1);
+  int64_t w = c.window;
+  if (dmax < 0 || (w > 0 && dmin >= w)) {  // no visible pair: every query sits before every key
+    c.shift = -c.S;
+    c.window = 0;
+    return;
+  }
+  if (w > dmax) w = 0;  // the window never binds
+  if (w == 0) {
+    c.shift = (int)std::min<int64_t>(delta, c.Sk);  // delta >= 1 - S here
+    c.window = 0;
+  } else if (delta >= c.Sk - 1) {
+    // the causal bound never binds; only delta - window matters
+    const int64_t e = delta - w;  // in [1 - S, Sk - 2]
+    c.shift = c.Sk;
+    c.window = (int)(c.Sk - e);
+  } else {
+    c.shift = (int)delta;  // in [1 - S, Sk - 2]
+    c.window = (int)w;     // at most dmax < S + Sk
+  }
+}
+
+void fill_common(attn::AttnArgs& a, const Call& c, float scale, const int32_t* meta) {
+  a.B = c.B;
+  a.S = c.S;
+  a.Sk = c.Sk;
+  a.q_shift = c.shift;
+  a.empty_lse_ninf = c.empty_lse_ninf;
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.r = c.Hq / c.Hkv;
+  a.packed = c.varlen == 2;
+  a.causal = c.causal;
+  a.window = c.window;
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
-  a.seq_off = varlen ? meta : nullptr;
-  a.seq_len = varlen ? meta + s->B : nullptr;
-  a.balanced = varlen != 0;  // sequences of different lengths: deal work items in rounds
+  a.seq_off = c.varlen ? meta : nullptr;
+  a.seq_len = c.varlen ? meta + c.B : nullptr;
+  a.balanced = c.varlen != 0;  // sequences of different lengths: deal work items in rounds
   if (a.packed) {
     a.st_sb = 0;
-    a.st_sh = s->total;
+    a.st_sh = c.total;
   } else {
-    a.st_sh = s->S;
-    a.st_sb = (int64_t)s->Hq * s->S;
+    a.st_sh = c.S;
+    a.st_sb = (int64_t)c.Hq * c.S;
   }
 }
 
@@ -159,41 +196,189 @@ attn_status check_common(const attn_shape* shape, float scale, int causal, int w
 }
 
 // dS block layout of the backward (see ds_block_index): triangular for causal attention
-// without a window, else a fixed number of blocks per 128-row query tile.
+// of whole sequences without a window, else a fixed number of blocks per 128-row query tile
+// (every key block for a chunk pair without a window).
 struct DsLayout {
   int tri, cnt;
   int64_t per_head;  // blocks per (batch, query head)
 };
 
-DsLayout ds_layout(const attn_shape* s, int causal, int window) {
-  const int nqt = (s->S + attn::kDsRows - 1) / attn::kDsRows;
-  const int nkb = (s->S + attn::kDsKeys - 1) / attn::kDsKeys;
+DsLayout ds_layout(const Call& c) {
+  const int nqt = (c.S + attn::kDsRows - 1) / attn::kDsRows;
+  const int nkb = (c.Sk + attn::kDsKeys - 1) / attn::kDsKeys;
   DsLayout L;
-  if (causal && window <= 0) {
+  if (c.causal && c.shift <= -c.S) {  // no visible pair (see normalise_offsets)
+    L.tri = 0;
+    L.cnt = 0;
+    L.per_head = 0;
+  } else if (c.causal && c.window <= 0 && c.shift == 0 && c.Sk == c.S) {
     L.tri = 1;
     L.cnt = 0;
     L.per_head = 2LL * nqt * (nqt + 1);
   } else {
+    // a tile's visible key blocks span at most (window + 254) / 32 + 2 <= (window + 127) / 32 + 6 blocks
     L.tri = 0;
-    L.cnt = causal ? std::min(nkb, (window + attn::kDsRows - 1) / attn::kDsKeys + 6) : nkb;
+    L.cnt = (c.causal && c.window > 0) ? std::min(nkb, (c.window + attn::kDsRows - 1) / attn::kDsKeys + 6) : nkb;
     L.per_head = (int64_t)nqt * L.cnt;
   }
   return L;
 }
 
-size_t ds_bytes(const attn_shape* s, int causal, int window) {
-  const DsLayout L = ds_layout(s, causal, window);
-  return round_up((size_t)s->B * s->Hq * L.per_head * attn::kDsBlockElems * sizeof(__bf16));
+size_t ds_bytes(const Call& c) {
+  const DsLayout L = ds_layout(c);
+  return round_up((size_t)c.B * c.Hq * L.per_head * attn::kDsBlockElems * sizeof(__bf16));
 }
 
-size_t bwd_bytes(const attn_shape* shape, int varlen, int causal, int window) {
-  return meta_bytes(shape, varlen) + round_up(sizeof(float) * stat_elems(shape, varlen)) +
-         ds_bytes(shape, causal, window);
+size_t stat_bytes(const Call& c) {
+  return round_up(sizeof(float) * (size_t)c.Hq * (c.varlen == 2 ? (size_t)c.total : (size_t)c.B * c.S));
 }
 
-bool empty_call(const attn_shape* s, int varlen) {
-  return s->B == 0 || s->S == 0 || (varlen == 2 && s->total == 0);
+size_t bwd_bytes(const Call& c) {
+  return meta_bytes(c.B, c.varlen) + stat_bytes(c) + ds_bytes(c);
 }
+
+Call whole_call(const attn_shape* s, int varlen, int causal, int window) {
+  Call c = {};
+  c.B = s->B;
+  c.S = s->S;
+  c.Sk = s->S;
+  c.total = s->total;
+  c.Hq = s->Hq;
+  c.Hkv = s->Hkv;
+  c.D = s->D;
+  c.varlen = varlen;
+  c.causal = causal ? 1 : 0;
+  c.window = window;
+  normalise_offsets(c, 0);
+  return c;
+}
+
+// Chunk pairs: dense (B, Sq | Sk, H, D) tensors.
+attn_status check_chunk(const attn_chunk_shape* s, int causal, int window, int64_t q_pos0, int64_t k_pos0) {
+  if (s == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (s->B < 0 || s->Sq < 0 || s->Sk < 0 || s->Hq <= 0 || s->Hkv <= 0) return ATTN_ERR_INVALID_ARG;
+  if (s->Hq % s->Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (window < 0 || q_pos0 < 0 || k_pos0 < 0 || q_pos0 > (INT64_MAX >> 2) || k_pos0 > (INT64_MAX >> 2))
+    return ATTN_ERR_INVALID_ARG;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (s->D != 256 && s->D != 512) return ATTN_ERR_UNSUPPORTED;
+  if (s->Sq >= (1 << 28) || s->Sk >= (1 << 28)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)s->B * s->Sq * s->Hq >= INT_MAX / 2 || (int64_t)s->B * s->Sk * s->Hkv >= INT_MAX / 2)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+Call chunk_call(const attn_chunk_shape* s, int causal, int window, int64_t q_pos0, int64_t k_pos0) {
+  Call c = {};
+  c.B = s->B;
+  c.S = s->Sq;
+  c.Sk = s->Sk;
+  c.total = 0;
+  c.Hq = s->Hq;
+  c.Hkv = s->Hkv;
+  c.D = s->D;
+  c.varlen = 0;
+  c.causal = causal ? 1 : 0;
+  c.window = window;
+  c.empty_lse_ninf = 1;
+  normalise_offsets(c, q_pos0 - k_pos0);
+  return c;
+}
+
+// Launches one kernel unless its grid is empty.
+template <class F>
+attn_status launch(const char* name, hipStream_t s, int items, F&& f) {
+  if (items <= 0) return ATTN_OK;
+  return hip_status(timed(name, s, f));
+}
+
+struct Tensors {
+  attn_tensor q, k, v, o, dout, dq, dk, dv;
+};
+
+void set_tensors(attn::AttnArgs& a, const Tensors& t, bool packed, bool bwd) {
+  a.q = static_cast<const __bf16*>(t.q.ptr);
+  a.k = static_cast<const __bf16*>(t.k.ptr);
+  a.v = static_cast<const __bf16*>(t.v.ptr);
+  set_tensor(t.q, packed, a.q_sb, a.q_ss, a.q_sh);
+  set_tensor(t.k, packed, a.k_sb, a.k_ss, a.k_sh);
+  set_tensor(t.v, packed, a.v_sb, a.v_ss, a.v_sh);
+  set_tensor(t.o, packed, a.o_sb, a.o_ss, a.o_sh);
+  if (!bwd) {
+    a.out = static_cast<__bf16*>(t.o.ptr);
+    return;
+  }
+  a.o = static_cast<const __bf16*>(t.o.ptr);
+  a.dout = static_cast<const __bf16*>(t.dout.ptr);
+  a.out = static_cast<__bf16*>(t.dq.ptr);
+  a.dk = static_cast<__bf16*>(t.dk.ptr);
+  a.dv = static_cast<__bf16*>(t.dv.ptr);
+  set_tensor(t.dout, packed, a.do_sb, a.do_ss, a.do_sh);
+  set_tensor(t.dq, packed, a.dq_sb, a.dq_ss, a.dq_sh);
+  set_tensor(t.dk, packed, a.dk_sb, a.dk_ss, a.dk_sh);
+  set_tensor(t.dv, packed, a.dv_sb, a.dv_ss, a.dv_sh);
+}
+
+attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, const int32_t* cu_seqlens,
+                    const uint8_t* pad_mask, void* workspace, hipStream_t s, bool o_f32 = false) {
+  int32_t* meta = static_cast<int32_t*>(workspace);
+  attn_status st;
+  if (c.varlen && (st = launch("varlen_prep", s, c.B, [&] {
+                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, meta, meta + c.B, s);
+                   })))
+    return st;
+  attn::AttnArgs a = {};
+  fill_common(a, c, scale, meta);
+  set_tensors(a, t, c.varlen == 2, false);
+  if (o_f32) {
+    a.out = nullptr;
+    a.out_f32 = static_cast<float*>(t.o.ptr);
+  }
+  a.lse = lse;
+  plan_rows(a, attn::kFwdRows);
+  return launch("attn_fwd", s, a.total_items, [&] { return attn::launch_fwd(a, c.D, s); });
+}
+
+attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* lse, const int32_t* cu_seqlens,
+                    const uint8_t* pad_mask, void* workspace, hipStream_t s) {
+  int32_t* meta = static_cast<int32_t*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(c.B, c.varlen));
+  attn_status st;
+  if (c.varlen && (st = launch("varlen_prep", s, c.B, [&] {
+                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, meta, meta + c.B, s);
+                   })))
+    return st;
+  attn::AttnArgs a = {};
+  fill_common(a, c, scale, meta);
+  set_tensors(a, t, c.varlen == 2, true);
+  a.lse = const_cast<float*>(lse);
+  a.delta = delta;
+  {
+    const DsLayout L = ds_layout(c);
+    a.dsb = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(delta) + stat_bytes(c));
+    a.ds_head = L.per_head;
+    a.ds_tri = L.tri;
+    a.ds_cnt = L.cnt;
+  }
+
+  const int rows = (c.varlen == 2 ? c.total : c.B * c.S) * c.Hq;
+  if ((st = launch("bwd_pre", s, rows, [&] { return attn::launch_bwd_pre(a, c.D, rows, s); }))) return st;
+
+  attn::AttnArgs kv = a;
+  kv.nkt = (c.Sk + attn::kDkdvKeys - 1) / attn::kDkdvKeys;
+  kv.total_items = c.B * c.Hkv * kv.nkt;
+  kv.per_xcd = (kv.total_items + 7) / 8;
+  if ((st = launch("bwd_dkdv", s, kv.total_items, [&] { return attn::launch_bwd_dkdv(kv, c.D, s); }))) return st;
+
+  attn::AttnArgs qa = a;
+  qa.nqt = (c.S + attn::kDsRows - 1) / attn::kDsRows;
+  qa.total_items = c.B * c.Hkv * qa.nqt * qa.r * (c.D == 512 ? attn::kDqSplit512 : 1);
+  qa.per_xcd = (qa.total_items + 7) / 8;
+  return launch("bwd_dq", s, qa.total_items, [&] { return attn::launch_bwd_dq(qa, c.D, s); });
+}
+
+bool lse_ok(const float* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 }  // namespace
 
@@ -202,15 +387,13 @@ extern "C" {
 size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen, int causal, int window) {
   if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
   if ((causal != 0 && causal != 1) || window < 0 || (window > 0 && !causal)) return 0;
-  return bwd_bytes(shape, varlen, causal, window);
+  return bwd_bytes(whole_call(shape, varlen, causal, window));
 }
 
 size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen) {
   if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
-  return meta_bytes(shape, varlen);
+  return meta_bytes(shape->B, varlen);
 }
-
-
 
 attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, float scale, int causal,
                      int window, const int32_t* cu_seqlens, const uint8_t* pad_mask, attn_tensor o, float* lse,
@@ -223,30 +406,11 @@ attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   if ((st = check_tensor(q, packed)) || (st = check_tensor(k, packed)) || (st = check_tensor(v, packed)) ||
       (st = check_tensor(o, packed)))
     return st;
-  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARG;
-  if (empty_call(shape, varlen)) return ATTN_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  int32_t* meta = static_cast<int32_t*>(workspace);
-  if (varlen) {
-    if ((st = hip_status(timed("varlen_prep", s, [&] {
-           return attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s);
-         }))))
-      return st;
-  }
-  attn::AttnArgs a = {};
-  fill_common(a, shape, varlen, scale, causal, window, meta);
-  a.q = static_cast<const __bf16*>(q.ptr);
-  a.k = static_cast<const __bf16*>(k.ptr);
-  a.v = static_cast<const __bf16*>(v.ptr);
-  a.out = static_cast<__bf16*>(o.ptr);
-  a.lse = lse;
-  set_tensor(q, packed, a.q_sb, a.q_ss, a.q_sh);
-  set_tensor(k, packed, a.k_sb, a.k_ss, a.k_sh);
-  set_tensor(v, packed, a.v_sb, a.v_ss, a.v_sh);
-  set_tensor(o, packed, a.o_sb, a.o_ss, a.o_sh);
-  plan_rows(a, attn::kFwdRows);
-  return hip_status(timed("attn_fwd", s, [&] { return attn::launch_fwd(a, shape->D, s); }));
+  if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
+  if (shape->B == 0 || shape->S == 0 || (packed && shape->total == 0)) return ATTN_OK;
+  const Tensors t = {q, k, v, o, {}, {}, {}, {}};
+  return run_fwd(whole_call(shape, varlen, causal, window), t, scale, lse, cu_seqlens, pad_mask, workspace,
+                 static_cast<hipStream_t>(stream));
 }
 
 attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
@@ -262,62 +426,89 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
       (st = check_tensor(o, packed)) || (st = check_tensor(dout, packed)) || (st = check_tensor(dq, packed)) ||
       (st = check_tensor(dk, packed)) || (st = check_tensor(dv, packed)))
     return st;
-  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARG;
-  if (empty_call(shape, varlen)) return ATTN_OK;
+  if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
+  if (shape->B == 0 || shape->S == 0 || (packed && shape->total == 0)) return ATTN_OK;
+  const Tensors t = {q, k, v, o, dout, dq, dk, dv};
+  return run_bwd(whole_call(shape, varlen, causal, window), t, scale, lse, cu_seqlens, pad_mask, workspace,
+                 static_cast<hipStream_t>(stream));
+}
+
+size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal, int window, int64_t q_pos0,
+                                      int64_t k_pos0) {
+  if (check_chunk(shape, causal, window, q_pos0, k_pos0) != ATTN_OK) return 0;
+  return bwd_bytes(chunk_call(shape, causal, window, q_pos0, k_pos0));
+}
+
+attn_status attn_fwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, float scale,
+                           int causal, int window, int64_t q_pos0, int64_t k_pos0, attn_tensor o, int o_dtype,
+                           float* lse, void* stream) {
+  attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
+  if (st != ATTN_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (o_dtype != ATTN_DTYPE_BF16 && o_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
+  if ((st = check_tensor(q, false)) || (st = check_tensor(k, false)) || (st = check_tensor(v, false)) ||
+      (st = check_tensor(o, false)))
+    return st;
+  if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
+  if (shape->B == 0 || shape->Sq == 0) return ATTN_OK;
+  const Tensors t = {q, k, v, o, {}, {}, {}, {}};
+  return run_fwd(chunk_call(shape, causal, window, q_pos0, k_pos0), t, scale, lse, nullptr, nullptr, nullptr,
+                 static_cast<hipStream_t>(stream), o_dtype == ATTN_DTYPE_F32);
+}
+
+attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
+                           const float* lse, attn_tensor dout, float scale, int causal, int window, int64_t q_pos0,
+                           int64_t k_pos0, attn_tensor dq, attn_tensor dk, attn_tensor dv, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
+  if (st != ATTN_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0, k_pos0);
+  if (need > 0 &&
+      (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))))
+    return ATTN_ERR_WORKSPACE;
+  if ((st = check_tensor(q, false)) || (st = check_tensor(k, false)) || (st = check_tensor(v, false)) ||
+      (st = check_tensor(o, false)) || (st = check_tensor(dout, false)) || (st = check_tensor(dq, false)) ||
+      (st = check_tensor(dk, false)) || (st = check_tensor(dv, false)))
+    return st;
+  if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
+  if (shape->B == 0 || (shape->Sq == 0 && shape->Sk == 0)) return ATTN_OK;
+  const Tensors t = {q, k, v, o, dout, dq, dk, dv};
+  return run_bwd(chunk_call(shape, causal, window, q_pos0, k_pos0), t, scale, lse, nullptr, nullptr, workspace,
+                 static_cast<hipStream_t>(stream));
+}
+
+attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D, attn_tensor o, float* lse,
+                           attn_tensor o_part, const float* lse_part, attn_tensor out, void* stream) {
+  if (B < 0 || S < 0 || H <= 0) return ATTN_ERR_INVALID_ARG;
+  if (D != 128 && D != 256 && D != 512) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * S * H >= INT_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  attn_status st;
+  if ((st = check_tensor(o, false)) || (st = check_tensor(o_part, false))) return st;
+  if (out.ptr != nullptr && (st = check_tensor(out, false))) return st;
+  if (!lse_ok(lse) || !lse_ok(lse_part)) return ATTN_ERR_INVALID_ARG;
+  if (B == 0 || S == 0) return ATTN_OK;
+  attn::MergeArgs a = {};
+  a.o = static_cast<float*>(o.ptr);
+  a.lse = lse;
+  a.o_part = static_cast<const float*>(o_part.ptr);
+  a.lse_part = lse_part;
+  a.out = static_cast<__bf16*>(out.ptr);
+  a.o_sb = o.stride_b;
+  a.o_ss = o.stride_s;
+  a.o_sh = o.stride_h;
+  a.p_sb = o_part.stride_b;
+  a.p_ss = o_part.stride_s;
+  a.p_sh = o_part.stride_h;
+  a.r_sb = out.stride_b;
+  a.r_ss = out.stride_s;
+  a.r_sh = out.stride_h;
+  a.B = B;
+  a.S = S;
+  a.H = H;
+  a.rows = B * S * H;
   hipStream_t s = static_cast<hipStream_t>(stream);
-
-  int32_t* meta = static_cast<int32_t*>(workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(shape, varlen));
-  if (varlen) {
-    if ((st = hip_status(timed("varlen_prep", s, [&] {
-           return attn::launch_varlen_prep(pad_mask, cu_seqlens, shape->B, shape->S, meta, meta + shape->B, s);
-         }))))
-      return st;
-  }
-  attn::AttnArgs a = {};
-  fill_common(a, shape, varlen, scale, causal, window, meta);
-  a.q = static_cast<const __bf16*>(q.ptr);
-  a.k = static_cast<const __bf16*>(k.ptr);
-  a.v = static_cast<const __bf16*>(v.ptr);
-  a.o = static_cast<const __bf16*>(o.ptr);
-  a.dout = static_cast<const __bf16*>(dout.ptr);
-  a.out = static_cast<__bf16*>(dq.ptr);
-  a.dk = static_cast<__bf16*>(dk.ptr);
-  a.dv = static_cast<__bf16*>(dv.ptr);
-  a.lse = const_cast<float*>(lse);
-  a.delta = delta;
-  {
-    const DsLayout L = ds_layout(shape, causal, window);
-    a.dsb = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(delta) + round_up(sizeof(float) * stat_elems(shape, varlen)));
-    a.ds_head = L.per_head;
-    a.ds_tri = L.tri;
-    a.ds_cnt = L.cnt;
-  }
-  set_tensor(q, packed, a.q_sb, a.q_ss, a.q_sh);
-  set_tensor(k, packed, a.k_sb, a.k_ss, a.k_sh);
-  set_tensor(v, packed, a.v_sb, a.v_ss, a.v_sh);
-  set_tensor(o, packed, a.o_sb, a.o_ss, a.o_sh);
-  set_tensor(dout, packed, a.do_sb, a.do_ss, a.do_sh);
-  set_tensor(dq, packed, a.dq_sb, a.dq_ss, a.dq_sh);
-  set_tensor(dk, packed, a.dk_sb, a.dk_ss, a.dk_sh);
-  set_tensor(dv, packed, a.dv_sb, a.dv_ss, a.dv_sh);
-
-  const int rows = packed ? shape->total * shape->Hq : shape->B * shape->S * shape->Hq;
-  if ((st = hip_status(timed("bwd_pre", s, [&] { return attn::launch_bwd_pre(a, shape->D, rows, s); }))))
-    return st;
-
-  attn::AttnArgs kv = a;
-  kv.nkt = (a.S + attn::kDkdvKeys - 1) / attn::kDkdvKeys;
-  kv.total_items = a.B * a.Hkv * kv.nkt;
-  kv.per_xcd = (kv.total_items + 7) / 8;
-  if ((st = hip_status(timed("bwd_dkdv", s, [&] { return attn::launch_bwd_dkdv(kv, shape->D, s); }))))
-    return st;
-
-  attn::AttnArgs qa = a;
-  qa.nqt = (a.S + attn::kDsRows - 1) / attn::kDsRows;
-  qa.total_items = a.B * a.Hkv * qa.nqt * a.r * (shape->D == 512 ? attn::kDqSplit512 : 1);
-  qa.per_xcd = (qa.total_items + 7) / 8;
-  return hip_status(timed("bwd_dq", s, [&] { return attn::launch_bwd_dq(qa, shape->D, s); }));
+  return launch("lse_merge", s, a.rows, [&] { return attn::launch_lse_merge(a, D, s); });
 }
 
 size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {

@@ -112,6 +112,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   const int b = unit / a.Hkv;
   int len = a.seq_len ? a.seq_len[b] : a.S;
   len = min(max(len, 0), a.S);
+  const int lenk = a.seq_len ? len : a.Sk;  // key rows
+  const int dlt = a.q_shift;
   const int off = a.seq_off ? a.seq_off[b] : 0;
   const int j0 = kt * NK;
 
@@ -131,11 +133,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) dvacc[x][d][r] = dkacc[x][d][r] = 0.f;
 
   // query range that sees any key of the tile
-  const int qlo = a.causal ? j0 : 0;
+  const int qlo = a.causal ? max(j0 - dlt, 0) : 0;
   int qhi = len;
-  if (a.window > 0) qhi = min(qhi, j0 + NK - 1 + a.window);
+  if (a.window > 0) qhi = min(qhi, j0 + NK - 1 + a.window - dlt);
   const int tq0 = qlo / MQ;
-  const int nq = (j0 < len && qhi > qlo) ? (qhi + MQ - 1) / MQ - tq0 : 0;
+  const int nq = (j0 < lenk && qhi > qlo) ? (qhi + MQ - 1) / MQ - tq0 : 0;
   const int nsteps = a.r * nq;
 
   if (nsteps > 0) {
@@ -143,8 +145,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     bf16x8 kv[KS];
     {
       const int key = j0 + 32 * kb + ln;
-      const bool ok = key < len;
-      const int krow = min(key, len - 1);
+      const bool ok = key < lenk;
+      const int krow = min(key, lenk - 1);
       const bf16* src = score_wave ? a.k + b * a.k_sb + (int64_t)(off + krow) * a.k_ss + g * a.k_sh
                                    : a.v + b * a.v_sb + (int64_t)(off + krow) * a.v_ss + g * a.v_sh;
 #pragma unroll
@@ -256,8 +258,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           lse4[u] = st4[2 * (xh + u) + g2] * kLog2e;
           dl4[u] = st4[8 + 2 * (xh + u) + g2];
         }
-        const bool full = (i0 + MQ <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= i0) &&
-                          (a.window <= 0 || j0 > i0 + MQ - 1 - a.window);
+        const bool full = (i0 + MQ <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= i0 + dlt) &&
+                          (a.window <= 0 || j0 > i0 + MQ - 1 + dlt - a.window);
         bf16x8 pb, db;
         if (full) {
 #pragma unroll
@@ -269,9 +271,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         } else {
           // this lane's key is visible from query rows rlo .. rhi-1
           const int key = j0 + 32 * kb + ln;
-          const int rlo = a.causal ? key : 0;
-          int rhi = key < len ? len : 0;
-          if (a.window > 0) rhi = min(rhi, key + a.window);
+          const int rlo = a.causal ? key - dlt : 0;
+          int rhi = key < lenk ? len : 0;
+          if (a.window > 0) rhi = min(rhi, key + a.window - dlt);
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
             const int row = i0 + 8 * (xh + (r >> 2)) + 4 * g2 + (r & 3);
@@ -286,8 +288,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         pds[0][kb][xh >> 1][lane] = pb;
         pds[1][kb][xh >> 1][lane] = db;
         // dS^T for the dQ product: this lane's key, query rows i0 + 8 x + 4 g2 .. +3
-        const int64_t bi = ds_block_index(i0 / kDsRows, (j0 / kDsKeys) + kb, a.causal, a.window, a.S, a.ds_tri,
-                                          a.ds_cnt);
+        const int64_t bi = ds_block_index(i0 / kDsRows, (j0 / kDsKeys) + kb, a.causal, a.window, dlt, lenk,
+                                          a.ds_tri, a.ds_cnt);
         if (bi >= 0) {
           bf16* dst = a.dsb + ((int64_t)(b * a.Hq + g * a.r + hi) * a.ds_head + bi) * kDsBlockElems +
                       ln * kDsRows + (i0 & (kDsRows - 1)) + 8 * xh + 4 * g2;
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int key = j0 + 32 * x + ln;
-    const bool wr = a.packed ? key < len : key < a.S;
+    const bool wr = a.packed ? key < len : key < a.Sk;
     if (!wr) continue;
     bf16* pk = a.dk + b * a.dk_sb + (int64_t)(off + key) * a.dk_ss + g * a.dk_sh + 4 * g2;
     bf16* pv = a.dv + b * a.dv_sb + (int64_t)(off + key) * a.dv_ss + g * a.dv_sh + 4 * g2;
@@ -388,6 +390,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
   const int h = g * a.r + rem % a.r;
   int len = a.seq_len ? a.seq_len[b] : a.S;
   len = min(max(len, 0), a.S);
+  const int lenk = a.seq_len ? len : a.Sk;  // key rows
+  const int dlt = a.q_shift;
   const int off = a.seq_off ? a.seq_off[b] : 0;
   const int p0 = qt * M;
 
@@ -406,14 +410,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
 
   // visible key blocks of the tile's rows
   const int plast = min(p0 + M, len) - 1;
-  const int kb_first = max(ds_kb_lo(qt, a.causal, a.window), a.window > 0 ? max(0, p0 - a.window + 1) / NK : 0);
-  const int kb_last = plast < p0 ? -1 : (a.causal ? plast / NK : (len - 1) / NK);
+  const int kb_first =
+      max(ds_kb_lo(qt, a.causal, a.window, dlt), a.window > 0 ? max(0, p0 + dlt - a.window + 1) / NK : 0);
+  const int jmax = a.causal ? min(plast + dlt, lenk - 1) : lenk - 1;  // the tile's largest visible key
+  const int kb_last = (plast < p0 || jmax < 0) ? -1 : jmax / NK;
 
   if (kb_first <= kb_last) {
     const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh + dh * D;
     const bf16* sbase = a.dsb + (int64_t)(b * a.Hq + h) * a.ds_head * kDsBlockElems;
     auto sblock = [&](int kb) {  // every block in kb_first .. kb_last holds a visible pair, so it is stored
-      const int64_t bi = ds_block_index(qt, kb, a.causal, a.window, a.S, a.ds_tri, a.ds_cnt);
+      const int64_t bi = ds_block_index(qt, kb, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
       return sbase + (bi < 0 ? 0 : bi) * kDsBlockElems;
     };
     const TrFrags<D> trk(lane);
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < DBW; ++d) trk.pick(dsl + d, klo[d], khi[d]);
 
-    dma_rows<D, NK, NW>(Ks[0], tile_src<NK>(kbase, a.k_ss, kb_first * NK, len - kb_first * NK), wave, lane);
+    dma_rows<D, NK, NW>(Ks[0], tile_src<NK>(kbase, a.k_ss, kb_first * NK, lenk - kb_first * NK), wave, lane);
     dma_rows<M, NK, NW>(Ss[0], tile_src<NK>(sblock(kb_first), M, 0, NK), wave, lane);
     for (int kb = kb_first; kb <= kb_last; ++kb) {
       const int buf = (kb - kb_first) & 1;
@@ -430,11 +436,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
       wait_vmcnt<0>();
       barrier_lds();  // block kb is in LDS; every wave is done with block kb-1
       if (kb < kb_last) {
-        dma_rows<D, NK, NW>(Ks[buf ^ 1], tile_src<NK>(kbase, a.k_ss, j0 + NK, len - j0 - NK), wave, lane);
+        dma_rows<D, NK, NW>(Ks[buf ^ 1], tile_src<NK>(kbase, a.k_ss, j0 + NK, lenk - j0 - NK), wave, lane);
         dma_rows<M, NK, NW>(Ss[buf ^ 1], tile_src<NK>(sblock(kb + 1), M, 0, NK), wave, lane);
       }
-      const bool full = (p0 + M <= len) && (j0 + NK <= len) && (!a.causal || j0 + NK - 1 <= p0) &&
-                        (a.window <= 0 || j0 > p0 + M - 1 - a.window);
+      const bool full = (p0 + M <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= p0 + dlt) &&
+                        (a.window <= 0 || j0 > p0 + M - 1 + dlt - a.window);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         bf16x8 bs[RB];
@@ -449,7 +455,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int key = j0 + 16 * s + 4 * g2 + (e < 4 ? e : e + 4);
-              const uint32_t keep = key_visible(row, key, len, a.causal, a.window) ? 0xffffu : 0u;
+              const uint32_t keep = key_visible(row, key, len, lenk, dlt, a.causal, a.window) ? 0xffffu : 0u;
               w[e >> 1] &= (e & 1) ? (keep << 16) | 0xffffu : keep | 0xffff0000u;
             }
             __builtin_memcpy(&bs[x], w, 16);

@@ -65,6 +65,8 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
   const int b = unit / (a.nhb * a.Hkv);
   int len = a.seq_len ? a.seq_len[b] : a.S;
   len = min(max(len, 0), a.S);
+  const int lenk = a.seq_len ? len : a.Sk;  // key rows
+  const int dlt = a.q_shift;
   const int off = a.seq_off ? a.seq_off[b] : 0;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
   }
 
   const int plast = min(p0 + a.mpos, len) - 1;
-  const int jhi = (plast < p0) ? 0 : (a.causal ? plast + 1 : len);
-  const int jlo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
+  const int jhi = (plast < p0) ? 0 : (a.causal ? min(plast + dlt + 1, lenk) : lenk);
+  const int jlo = a.window > 0 ? max(0, p0 + dlt - a.window + 1) : 0;
   const int t_lo = jlo / N;
   const int t_hi = jhi > jlo ? (jhi + N - 1) / N : t_lo;
 
@@ -112,8 +114,8 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
       for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
     l_run = 0.f;
     if (t_lo < t_hi) {
-      dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, t_lo * N, len - t_lo * N), wave, lane);
-      dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, t_lo * N, len - t_lo * N), wave, lane);
+      dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, t_lo * N, lenk - t_lo * N), wave, lane);
+      dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, t_lo * N, lenk - t_lo * N), wave, lane);
     }
     for (int jt = t_lo; jt < t_hi; ++jt) {
       const int j0 = jt * N;
@@ -146,17 +148,25 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
         }
       }
       barrier_lds();  // every wave is done with Ks
-      if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, len - j0 - N), wave, lane);
+      if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
 
-      const bool need_mask = (j0 + N > len) || (p0 + a.mpos > len) || (a.causal && j0 + N - 1 > p0) ||
-                             (a.window > 0 && j0 <= plast - a.window);
+      const bool need_mask = (j0 + N > lenk) || (p0 + a.mpos > len) || (a.causal && j0 + N - 1 > p0 + dlt) ||
+                             (a.window > 0 && j0 <= plast + dlt - a.window);
       if (need_mask) {
+        // this row sees keys klo < key <= khi; register r of block kb holds key
+        // j0 + 4 g2 + 32 kb + 8 (r / 4) + r % 4, so compare the constant part with the
+        // row's bounds shifted by j0 + 4 g2
+        const int ip = pos + dlt;
+        int khi = a.causal ? min(ip, lenk - 1) : lenk - 1;
+        if (pos >= len) khi = -1;
+        const int klo = a.window > 0 ? ip - a.window : -1;
+        const int rhi = khi - j0 - 4 * g2, rlo = klo - j0 - 4 * g2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-            if (!key_visible(pos, key, len, a.causal, a.window)) sacc[kb][r] = -INFINITY;
+            const int kr = 32 * kb + 8 * (r >> 2) + (r & 3);
+            if (kr > rhi || kr <= rlo) sacc[kb][r] = -INFINITY;
           }
       }
       float mt = -INFINITY;
@@ -232,22 +242,29 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
         }
       }
       barrier_lds();  // every wave is done with Vs
-      if (has_next) dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, j0 + N, len - j0 - N), wave, lane);
+      if (has_next) dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, j0 + N, lenk - j0 - N), wave, lane);
     }
   }
 
   const bool wrow = a.packed ? (pos < len) : (pos < a.S);
   if (wrow) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    bf16* op = a.out + b * a.o_sb + (int64_t)(off + pos) * a.o_ss + h * a.o_sh + 4 * g2;
+    const int64_t oo = b * a.o_sb + (int64_t)(off + pos) * a.o_ss + h * a.o_sh + 4 * g2;
+    auto store = [&](auto* op) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+      for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int qa = 0; qa < 4; ++qa)
-        stg4(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv, oacc[d][4 * qa + 2] * inv,
-             oacc[d][4 * qa + 3] * inv);
+        for (int qa = 0; qa < 4; ++qa)
+          stg4(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv, oacc[d][4 * qa + 2] * inv,
+               oacc[d][4 * qa + 3] * inv);
+    };
+    if (a.out_f32)
+      store(a.out_f32 + oo);  // a partial over one key chunk: rounded once, when the partials are merged
+    else
+      store(a.out + oo);
     if (g2 == 0)
-      a.lse[b * a.st_sb + h * a.st_sh + off + pos] = l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : 0.f;
+      a.lse[b * a.st_sb + h * a.st_sh + off + pos] =
+          l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : (a.empty_lse_ninf ? -INFINITY : 0.f);
   }
 }
 

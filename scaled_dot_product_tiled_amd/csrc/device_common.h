@@ -221,6 +221,10 @@ __device__ __forceinline__ void stg4(bf16* p, float a, float b, float c, float d
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
+__device__ __forceinline__ void stg4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
 // Work-item order.  Items are (unit, w) with W items per unit, w = 0 the heaviest.
 // Consecutive workgroup ids land on consecutive XCDs (id % 8).  When every unit carries the
 // same work (dense inputs), the items of one XCD are taken from one contiguous range of the
@@ -242,8 +246,10 @@ __device__ __forceinline__ int xcd_item(int per_xcd, int total, int W, int balan
   return (slot < per_xcd && item < total) ? item : -1;
 }
 
-__device__ __forceinline__ bool key_visible(int i, int j, int len, int causal, int window) {
-  return (i < len) & (j < len) & ((!causal) | (j <= i)) & ((window <= 0) | (j > i - window));
+// Query row i (of lenq) sees key row j (of lenk); query i sits at position i + delta.
+__device__ __forceinline__ bool key_visible(int i, int j, int lenq, int lenk, int delta, int causal, int window) {
+  const int ip = i + delta;
+  return (i < lenq) & (j < lenk) & ((!causal) | (j <= ip)) & ((window <= 0) | (j > ip - window));
 }
 
 }  // namespace attn

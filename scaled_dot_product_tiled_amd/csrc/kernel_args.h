@@ -12,6 +12,12 @@ namespace attn {
 // X_sb = 0 and seq_off from cu_seqlens, dense inputs pass seq_off = seq_len = NULL.
 // Row statistics (LSE, delta) of (b, h, pos) live at st + b * st_sb + h * st_sh +
 // seq_off[b] + pos.
+//
+// Query row i sits at position i + q_shift and key row j at position j, so query i sees
+// key j when j <= i + q_shift (causal) and j > i + q_shift - window (window > 0).  Whole
+// sequences have q_shift = 0 and Sk = S; a chunk pair of a sequence split into chunks has
+// S query rows, Sk key rows and q_shift = (position of its first query) - (position of its
+// first key).  The host keeps q_shift in [-S, Sk] and window in [0, S + Sk].
 struct AttnArgs {
   const __bf16* q;
   const __bf16* k;
@@ -19,6 +25,7 @@ struct AttnArgs {
   const __bf16* o;
   const __bf16* dout;
   __bf16* out;  // forward: O; backward: dQ
+  float* out_f32;  // forward: O in fp32 instead of out (chunk partials); NULL otherwise
   __bf16* dk;
   __bf16* dv;
   float* lse;   // forward writes, backward reads
@@ -38,6 +45,9 @@ struct AttnArgs {
   const int32_t* seq_off;  // NULL: 0
   const int32_t* seq_len;  // NULL: S
   int B, S, Hq, Hkv, r;
+  int Sk;                   // key rows (dense); S for whole sequences
+  int q_shift;              // query position offset (see above)
+  int empty_lse_ninf;       // a query row with no visible key stores LSE = -inf (else 0)
   int hpt, mpos, nhb, nqt;  // heads per tile, positions per tile, head blocks, q tiles
   int nkt;                  // key tiles (dK/dV kernel)
   int packed;               // rows past a sequence's length do not exist
@@ -62,29 +72,48 @@ struct DecodeArgs {
   float c;            // scale * log2(e)
 };
 
+// In-place log-sum-exp merge of a partial result (o_part, lse_part) into (o, lse), rows
+// (b, s, h) of fp32 O (B, S, H, D) with element strides and fp32 LSE (B, H, S) contiguous;
+// optionally also the merged O rounded to bf16 into out (strides r_*).
+struct MergeArgs {
+  float* o;
+  float* lse;
+  const float* o_part;
+  const float* lse_part;
+  __bf16* out;  // NULL: not written
+  int64_t o_sb, o_ss, o_sh;
+  int64_t p_sb, p_ss, p_sh;
+  int64_t r_sb, r_ss, r_sh;
+  int B, S, H, rows;
+};
+
 // The backward stores dS = P * (dP - delta) (bf16) once, for the dQ product.  It is kept in
 // blocks of kDsKeys keys x kDsRows query rows of one (batch, query head), each block stored
 // transposed (row-major, one row per key, kDsRows query rows per row: 8 KB).  Query tile qt
 // (rows 128 qt ..) keeps key blocks ds_kb_lo(qt) .. ds_kb_hi(qt), the only ones that can
-// hold a visible pair, packed tile after tile.
+// hold a visible pair, packed tile after tile: 4 (qt + 1) blocks for causal attention of a
+// whole sequence (tri), else a fixed count cnt per tile.
 constexpr int kDsRows = 128;
 constexpr int kDsKeys = 32;
 constexpr int kDsBlockElems = kDsRows * kDsKeys;
 
-__host__ __device__ inline int ds_kb_lo(int qt, int causal, int window) {
+__host__ __device__ inline int ds_kb_lo(int qt, int causal, int window, int delta) {
   if (!causal || window <= 0) return 0;
-  const int lo = qt * kDsRows - window - (kDsRows - 1);  // no visible key below this one
+  const int lo = qt * kDsRows + delta - window - (kDsRows - 1);  // no visible key below this one
   return lo <= 0 ? 0 : lo / kDsKeys;
 }
-__host__ __device__ inline int ds_kb_hi(int qt, int causal, int S) {
-  const int nkb = (S + kDsKeys - 1) / kDsKeys;
-  const int hi = causal ? qt * (kDsRows / kDsKeys) + (kDsRows / kDsKeys - 1) : nkb - 1;
+__host__ __device__ inline int ds_kb_hi(int qt, int causal, int Sk, int delta) {
+  const int nkb = (Sk + kDsKeys - 1) / kDsKeys;
+  if (!causal) return nkb - 1;
+  const int last = qt * kDsRows + (kDsRows - 1) + delta;  // the tile's largest visible key
+  const int hi = last < 0 ? -1 : last / kDsKeys;
   return hi < nkb - 1 ? hi : nkb - 1;
 }
 // Index of block (qt, kb) among the blocks of one (batch, head); -1 if it is not stored.
-__host__ __device__ inline int64_t ds_block_index(int qt, int kb, int causal, int window, int S, int tri, int cnt) {
-  const int lo = ds_kb_lo(qt, causal, window);
-  if (kb < lo || kb > ds_kb_hi(qt, causal, S) || (!tri && kb - lo >= cnt)) return -1;
+__host__ __device__ inline int64_t ds_block_index(int qt, int kb, int causal, int window, int delta, int Sk,
+                                                  int tri, int cnt) {
+  const int lo = ds_kb_lo(qt, causal, window, delta);
+  if (kb < lo || kb > ds_kb_hi(qt, causal, Sk, delta) || (!tri && kb - lo >= cnt)) return -1;
   const int64_t first = tri ? 2LL * qt * (qt + 1) : (int64_t)qt * cnt;
   return first + (kb - lo);
 }
@@ -98,6 +127,7 @@ hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeArgs& a, int D, hipStream_t stream);
 
 // Tile geometry used by the host planner.
 constexpr int kFwdRows = 128;   // query rows per forward workgroup

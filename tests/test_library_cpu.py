@@ -6,7 +6,8 @@ import re
 
 import pytest
 
-from scaled_dot_product_tiled_amd.binding import AttnDecodeShape, AttnShape, AttnTensor, load_library
+from scaled_dot_product_tiled_amd.binding import (AttnChunkShape, AttnDecodeShape, AttnShape, AttnTensor,
+                                                  load_library)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
@@ -112,3 +113,60 @@ def test_backward_and_decode_checks():
     assert dec(d, table=0) == INVALID
     assert dec(d, wsb=16) == WORKSPACE
     assert dec(AttnDecodeShape(0, 32, 8, 128, 16, 100, 8)) == OK
+
+
+def test_chunk_workspace_sizes():
+    """Chunk pairs of a sequence cut into 2048-row chunks (head_dim 512, 32 query heads): the
+    diagonal pair keeps the triangular dS layout, a pair wholly in the past keeps every key block,
+    a pair wholly in the future stores nothing, and a window keeps (window + 128) / 32 + 6 blocks
+    per 128-row query tile."""
+    lib = load_library()
+    c = AttnChunkShape(1, 2048, 2048, 32, 4, 512)
+    delta = 2048 * 32 * 4
+    blk = 32 * 128 * 2
+
+    def ws(causal, window, qp, kp, shape=c):
+        return lib.attn_bwd_chunk_workspace_bytes(ctypes.byref(shape), causal, window, qp, kp)
+    assert ws(1, 0, 2048, 2048) == delta + 32 * (2 * 16 * 17) * blk
+    assert ws(1, 0, 4096, 0) == delta + 32 * (16 * 64) * blk
+    assert ws(0, 0, 0, 4096) == delta + 32 * (16 * 64) * blk      # non-causal: positions do not matter
+    assert ws(1, 0, 0, 2048) == delta                               # every key after every query
+    assert ws(1, 1024, 2048, 2048) == delta + 32 * (16 * 41) * blk
+    assert ws(1, 1024, 8192, 0) == delta                            # every key beyond the window
+    assert ws(1, 0, -1, 0) == 0                                     # positions are >= 0
+    assert ws(0, 16, 0, 0) == 0                                     # window needs causal
+    assert ws(1, 0, 0, 0, AttnChunkShape(1, 64, 64, 8, 2, 128)) == 0   # head_dim
+    assert ws(1, 0, 0, 0, AttnChunkShape(1, 1 << 28, 64, 8, 2, 512)) == 0
+
+
+def test_chunk_and_merge_checks():
+    lib = load_library()
+    c = AttnChunkShape(2, 64, 96, 8, 2, 512)
+
+    def fwd(shape=c, causal=1, window=0, qp=0, kp=0, lse=0x20000, q=None, odt=1):
+        return lib.attn_fwd_chunk(ctypes.byref(shape), q or _t(), _t(), _t(), 0.05, causal, window, qp, kp, _t(),
+                                  odt, lse, None)
+    assert fwd(causal=0, window=8) == UNSUPPORTED
+    assert fwd(qp=-5) == INVALID
+    assert fwd(lse=0) == INVALID
+    assert fwd(q=_t(ptr=0x10008)) == INVALID
+    assert fwd(shape=AttnChunkShape(2, 64, 96, 8, 3, 512)) == INVALID
+    assert fwd(odt=2) == INVALID                                        # O is bf16 or fp32
+    assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512)) == OK       # empty batch
+    assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512), odt=0) == OK
+    assert fwd(shape=AttnChunkShape(2, 0, 96, 8, 2, 512)) == OK        # no query rows
+    st = lib.attn_bwd_chunk(ctypes.byref(c), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, 64, 0,
+                            _t(), _t(), _t(), None, 0, None)
+    assert st == WORKSPACE
+
+    def merge(B=2, S=64, H=8, D=512, lse=0x20000, part=0x30000, o=None, out=None):
+        return lib.attn_lse_merge(B, S, H, D, o or _t(), lse, _t(), part, out or AttnTensor(None, 0, 0, 0), None)
+    assert merge(D=64) == UNSUPPORTED
+    assert merge(H=0) == INVALID
+    assert merge(lse=0) == INVALID
+    assert merge(part=0x30002) == INVALID                               # fp32 alignment
+    assert merge(o=_t(ptr=0)) == INVALID
+    assert merge(out=_t(ptr=0x10008)) == INVALID                        # the bf16 output is optional, but aligned
+    assert merge(B=0) == OK
+    assert merge(B=0, out=_t()) == OK
+    assert lib.attn_last_hip_error() == 0

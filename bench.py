@@ -10,7 +10,8 @@ the C ABI.  Reported:
             U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
   other_workloads  forward / backward TFLOP/s of the sliding-window (D=256, W=1024) and padded
-            varlen (B=8, lengths U{512..8192}, D=512) workloads, not part of the timed step;
+            varlen (B=8, lengths U{512..8192}, D=512) workloads, and of one context-parallel rank's
+            chunk pairs (16k tokens in 8 chunks, D=512), not part of the timed step;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores.
 Prints one JSON line.
 """
@@ -101,6 +102,74 @@ def other_workload(name, steps, stream):
            "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2)}
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
     del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
+def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
+    """One context-parallel rank's share of causal attention at 16k tokens (8 chunks of 2048
+    positions, D=512, GQA 32/4): the last rank's query chunk against every key/value chunk
+    that it sees (7 whole chunks and its own diagonal one).  Forward = one attn_fwd_chunk per
+    pair into fp32 partials and an attn_lse_merge after each (the last one writes bf16 O);
+    backward = one attn_bwd_chunk per pair adding into fp32 dQ, dK, dV.  Device-side N(0,1)
+    draws."""
+    import torch
+    import scaled_dot_product_tiled_amd as sdpt
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(4321)
+
+    def draw(shape):
+        return torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
+
+    rank = n_chunks - 1
+    q, do = draw((1, chunk, Hq, D)), draw((1, chunk, Hq, D))
+    k, v = draw((1, n_chunks * chunk, Hkv, D)), draw((1, n_chunks * chunk, Hkv, D))
+    q0 = rank * chunk
+    scale = 1.0 / math.sqrt(D)
+    acc_o = torch.empty((1, chunk, Hq, D), device="cuda:0", dtype=torch.float32)
+    part = torch.empty_like(acc_o)
+    acc_l = torch.empty((1, Hq, chunk), device="cuda:0", dtype=torch.float32)
+    part_l = torch.empty_like(acc_l)
+    o = torch.empty_like(q)
+    dq = torch.zeros((1, chunk, Hq, D), device="cuda:0", dtype=torch.float32)
+    dk = torch.zeros((1, n_chunks * chunk, Hkv, D), device="cuda:0", dtype=torch.float32)
+    dv = torch.zeros_like(dk)
+    ks = [(c * chunk, (c + 1) * chunk) for c in range(rank + 1)]
+    nws = max(sdpt.binding.attn_bwd_chunk_workspace_bytes(q, k[:, k0:k1], q0, k0) for k0, k1 in ks)
+    ws = torch.empty(nws, device="cuda:0", dtype=torch.uint8)
+
+    def fwd():
+        for i, (k0, k1) in enumerate(ks):
+            dst = (acc_o, acc_l) if i == 0 else (part, part_l)
+            sdpt.attn_fwd_chunk(q, k[:, k0:k1], v[:, k0:k1], q0, k0, scale=scale, out=dst[0], lse=dst[1])
+            if i > 0:
+                sdpt.attn_lse_merge(acc_o, acc_l, part, part_l, out=o if i == len(ks) - 1 else None)
+
+    def bwd():
+        for k0, k1 in ks:
+            sdpt.attn_bwd_chunk(q, k[:, k0:k1], v[:, k0:k1], o, acc_l, do, q0, k0, scale=scale, dq=dq,
+                                dk=dk[:, k0:k1], dv=dv[:, k0:k1], accumulate=True, workspace=ws)
+
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    ms_f = time_events(fwd, steps, stream)
+    ms_b = time_events(bwd, steps, stream)
+    sdpt.binding.profile(True)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    sdpt.binding.profile(False)
+    kern = {n: {"launches": c, "ms_avg": round(t / c, 4)} for n, (c, t) in sdpt.binding.profile_read().items()}
+    pairs = (rank * chunk * chunk + chunk * (chunk + 1) // 2) * Hq
+    ff = 4.0 * D * pairs
+    res = {"workload": f"ring context-parallel rank share, causal GQA d{D} (chunk {chunk} of {n_chunks}, "
+                       f"Hq{Hq} Hkv{Hkv}, last rank: {rank + 1} chunk pairs)",
+           "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+           "fwd_tflops": round(ff / ms_f / 1e9, 2), "bwd_tflops": round(2.5 * ff / ms_b / 1e9, 2),
+           "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2), "kernels": kern}
+    res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
+    del q, do, k, v, acc_o, part, acc_l, part_l, o, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return res
 
@@ -274,6 +343,8 @@ def main():
             "ms_per_launch": dom_ms, "flop_per_launch": algo.get(dom, 0.0)}
 
     others = {} if args.no_other else {n: other_workload(n, 5, stream) for n in ("window_d256", "varlen_d512")}
+    if not args.no_other:
+        others["ring_cp8_d512"] = ring_workload(5, stream)
 
     out = {
         "metric": "causal attn fwd+bwd TFLOP/s @d=512 (% bf16 MFMA peak); decode HBM GB/s",

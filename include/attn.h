@@ -169,10 +169,13 @@ attn_status attn_fwd_chunk(const attn_chunk_shape* shape,
  *   dk, dv (B, Sk, Hkv, D):  scale dS^T Q and P^T dO, summed over each kv head's
  *       query heads.
  * Summed over the key chunks of a query chunk (dq) and over the query chunks of a key
- * chunk (dk, dv), the parts are the gradients of attention over the whole sequence.  The
- * parts are written, not accumulated, in bf16; the caller sums them (in fp32 for the
- * best accuracy).  A row that sees no key of the pair gets dq = 0; a key that no row of
- * the pair sees gets dk = dv = 0.
+ * chunk (dk, dv), the parts are the gradients of attention over the whole sequence.
+ *   grad_dtype  ATTN_DTYPE_F32: dq, dk, dv are fp32 accumulators (zeroed by the caller
+ *               before a chunk's first pair) and the pair's parts are added to them, so a
+ *               ring step needs no separate sum; a pair with no visible (query, key) pair
+ *               launches nothing.  ATTN_DTYPE_BF16: the parts are written in bf16, not
+ *               accumulated; a row that sees no key of the pair gets dq = 0 and a key that
+ *               no row of the pair sees gets dk = dv = 0.
  *   workspace  at least attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0,
  *              k_pos0) bytes, 256-byte aligned (row statistics and dS blocks, as attn_bwd)
  * Other conventions as attn_bwd.
@@ -182,7 +185,7 @@ attn_status attn_bwd_chunk(const attn_chunk_shape* shape,
                            attn_tensor o, const float* lse, attn_tensor dout,
                            float scale, int causal, int window,
                            int64_t q_pos0, int64_t k_pos0,
-                           attn_tensor dq, attn_tensor dk, attn_tensor dv,
+                           attn_tensor dq, attn_tensor dk, attn_tensor dv, int grad_dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*

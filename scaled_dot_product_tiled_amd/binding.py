@@ -76,7 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_chunk.restype = ctypes.c_int
     lib.attn_bwd_chunk.argtypes = [P(AttnChunkShape), AttnTensor, AttnTensor, AttnTensor, AttnTensor, vp, AttnTensor,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, i64, i64, AttnTensor, AttnTensor,
-                                   AttnTensor, vp, sz, vp]
+                                   AttnTensor, ctypes.c_int, vp, sz, vp]
     lib.attn_bwd_chunk.restype = ctypes.c_int
     lib.attn_bwd_chunk_workspace_bytes.argtypes = [P(AttnChunkShape), ctypes.c_int, ctypes.c_int, i64, i64]
     lib.attn_bwd_chunk_workspace_bytes.restype = sz
@@ -299,13 +299,23 @@ def attn_fwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos0: in
     return out, lse
 
 
+def attn_bwd_chunk_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_pos0: int, k_pos0: int, causal: bool = True,
+                                   window: int = 0) -> int:
+    """Workspace bytes attn_bwd_chunk needs for this chunk pair (q (B,Sq,Hq,D), k (B,Sk,Hkv,D))."""
+    shape = _chunk_shape(q, k)
+    return int(load_library().attn_bwd_chunk_workspace_bytes(ctypes.byref(shape), int(bool(causal)), int(window),
+                                                             int(q_pos0), int(k_pos0)))
+
+
 def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
                    dout: torch.Tensor, q_pos0: int, k_pos0: int, scale: Optional[float] = None,
                    causal: bool = True, window: int = 0, dq: Optional[torch.Tensor] = None,
-                   dk: Optional[torch.Tensor] = None,
-                   dv: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+                   dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                   accumulate: bool = False,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Gradient parts dQ (B,Sq,Hq,D), dK, dV (B,Sk,Hkv,D) of one chunk pair, from the rows' final O and
-    LSE (merged over all their key chunks) and dO."""
+    LSE (merged over all their key chunks) and dO.  accumulate=False writes the parts in bf16 (new
+    tensors unless given); accumulate=True adds them to the given fp32 dq, dk, dv."""
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _bf16(t, n)
@@ -314,17 +324,27 @@ def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
     shape = _chunk_shape(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(shape.D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    if accumulate:
+        if dq is None or dk is None or dv is None:
+            raise ValueError("accumulate=True needs the fp32 accumulators dq, dk, dv")
+        for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            if t.dtype != torch.float32 or not t.is_cuda or t.stride(-1) != 1:
+                raise TypeError(f"{n} must be a float32 device tensor with a contiguous last dimension")
+    else:
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            _bf16(t, n)
     _check_chunk_shapes(shape, q, k, v, lse=lse, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
     c, w = int(bool(causal)), int(window)
     nbytes = lib.attn_bwd_chunk_workspace_bytes(ctypes.byref(shape), c, w, int(q_pos0), int(k_pos0))
-    ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
     st = lib.attn_bwd_chunk(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
                             _tensor(o, False), lse.data_ptr(), _tensor(dout, False), float(scale), c, w,
                             int(q_pos0), int(k_pos0), _tensor(dq, False), _tensor(dk, False), _tensor(dv, False),
-                            ws.data_ptr() if nbytes else None, nbytes, _stream())
+                            1 if accumulate else 0, workspace.data_ptr() if nbytes else None, nbytes, _stream())
     _check(st, "attn_bwd_chunk")
     return dq, dk, dv
 

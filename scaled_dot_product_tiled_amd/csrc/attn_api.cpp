@@ -341,7 +341,9 @@ attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, co
 }
 
 attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* lse, const int32_t* cu_seqlens,
-                    const uint8_t* pad_mask, void* workspace, hipStream_t s) {
+                    const uint8_t* pad_mask, void* workspace, hipStream_t s, bool grad_f32 = false) {
+  // adding the parts of a pair that has no visible (query, key) pair changes nothing
+  if (grad_f32 && c.causal && c.shift <= -c.S) return ATTN_OK;
   int32_t* meta = static_cast<int32_t*>(workspace);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(c.B, c.varlen));
   attn_status st;
@@ -352,6 +354,12 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
   attn::AttnArgs a = {};
   fill_common(a, c, scale, meta);
   set_tensors(a, t, c.varlen == 2, true);
+  if (grad_f32) {
+    a.out = a.dk = a.dv = nullptr;
+    a.dq_f32 = static_cast<float*>(t.dq.ptr);
+    a.dk_f32 = static_cast<float*>(t.dk.ptr);
+    a.dv_f32 = static_cast<float*>(t.dv.ptr);
+  }
   a.lse = const_cast<float*>(lse);
   a.delta = delta;
   {
@@ -458,11 +466,12 @@ attn_status attn_fwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
 
 attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
                            const float* lse, attn_tensor dout, float scale, int causal, int window, int64_t q_pos0,
-                           int64_t k_pos0, attn_tensor dq, attn_tensor dk, attn_tensor dv, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           int64_t k_pos0, attn_tensor dq, attn_tensor dk, attn_tensor dv, int grad_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
   if (st != ATTN_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (grad_dtype != ATTN_DTYPE_BF16 && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0, k_pos0);
   if (need > 0 &&
       (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))))
@@ -475,7 +484,7 @@ attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
   if (shape->B == 0 || (shape->Sq == 0 && shape->Sk == 0)) return ATTN_OK;
   const Tensors t = {q, k, v, o, dout, dq, dk, dv};
   return run_bwd(chunk_call(shape, causal, window, q_pos0, k_pos0), t, scale, lse, nullptr, nullptr, workspace,
-                 static_cast<hipStream_t>(stream));
+                 static_cast<hipStream_t>(stream), grad_dtype == ATTN_DTYPE_F32);
 }
 
 attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D, attn_tensor o, float* lse,

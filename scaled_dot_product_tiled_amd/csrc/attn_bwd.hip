@@ -319,6 +319,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   }
 
   // dV^T / dK^T blocks: lane = key j0 + 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4
+  if (a.dk_f32 != nullptr) {
+    // accumulate a chunk pair's parts; a tile that no query row of the pair sees adds nothing
+    if (nsteps == 0) return;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int key = j0 + 32 * x + ln;
+      if (key >= a.Sk) continue;
+      float* pk = a.dk_f32 + b * a.dk_sb + (int64_t)key * a.dk_ss + g * a.dk_sh + 4 * g2;
+      float* pv = a.dv_f32 + b * a.dv_sb + (int64_t)key * a.dv_ss + g * a.dv_sh + 4 * g2;
+      const float sc = a.scale;
+#pragma unroll
+      for (int d = 0; d < DBW; ++d)
+#pragma unroll
+        for (int qa = 0; qa < 4; ++qa) {
+          const int col = 32 * (dsl + d) + 8 * qa;
+          add4(pk + col, dkacc[x][d][4 * qa] * sc, dkacc[x][d][4 * qa + 1] * sc, dkacc[x][d][4 * qa + 2] * sc,
+               dkacc[x][d][4 * qa + 3] * sc);
+          add4(pv + col, dvacc[x][d][4 * qa], dvacc[x][d][4 * qa + 1], dvacc[x][d][4 * qa + 2],
+               dvacc[x][d][4 * qa + 3]);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int key = j0 + 32 * x + ln;
@@ -473,6 +496,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
   }
 
   // dQ^T blocks: lane = row p0 + 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4
+  if (a.dq_f32 != nullptr) {
+    // accumulate a chunk pair's part; rows that see no key of the pair add nothing
+    if (kb_first > kb_last) return;
+#pragma unroll
+    for (int x = 0; x < RB; ++x) {
+      const int px = p0 + 32 * x + ln;
+      if (px >= a.S) continue;
+      float* pq = a.dq_f32 + b * a.dq_sb + (int64_t)px * a.dq_ss + h * a.dq_sh + dh * D + 4 * g2;
+      const float sc = a.scale;
+#pragma unroll
+      for (int d = 0; d < DBW; ++d)
+#pragma unroll
+        for (int qa = 0; qa < 4; ++qa)
+          add4(pq + 32 * (dsl + d) + 8 * qa, acc[x][d][4 * qa] * sc, acc[x][d][4 * qa + 1] * sc,
+               acc[x][d][4 * qa + 2] * sc, acc[x][d][4 * qa + 3] * sc);
+    }
+    return;
+  }
 #pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int px = p0 + 32 * x + ln;

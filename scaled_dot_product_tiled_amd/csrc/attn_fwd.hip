@@ -153,20 +153,15 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
       const bool need_mask = (j0 + N > lenk) || (p0 + a.mpos > len) || (a.causal && j0 + N - 1 > p0 + dlt) ||
                              (a.window > 0 && j0 <= plast + dlt - a.window);
       if (need_mask) {
-        // this row sees keys klo < key <= khi; register r of block kb holds key
-        // j0 + 4 g2 + 32 kb + 8 (r / 4) + r % 4, so compare the constant part with the
-        // row's bounds shifted by j0 + 4 g2
-        const int ip = pos + dlt;
-        int khi = a.causal ? min(ip, lenk - 1) : lenk - 1;
-        if (pos >= len) khi = -1;
-        const int klo = a.window > 0 ? ip - a.window : -1;
-        const int rhi = khi - j0 - 4 * g2, rlo = klo - j0 - 4 * g2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kr = 32 * kb + 8 * (r >> 2) + (r & 3);
-            if (kr > rhi || kr <= rlo) sacc[kb][r] = -INFINITY;
+            // the key's position relative to the rows' (query row i sits at i + q_shift):
+            // the offset goes to the key side, a scalar per tile, so that only the row
+            // index stays in a vector register across the key loop
+            const int keyq = j0 - dlt + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+            if (!key_visible(pos, keyq, len, lenk - dlt, 0, a.causal, a.window)) sacc[kb][r] = -INFINITY;
           }
       }
       float mt = -INFINITY;

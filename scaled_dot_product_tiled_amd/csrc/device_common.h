@@ -225,6 +225,16 @@ __device__ __forceinline__ void stg4(float* p, float a, float b, float c, float 
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
+// p[0..3] += (a, b, c, d) in fp32; p is owned by this lane alone.
+__device__ __forceinline__ void add4(float* p, float a, float b, float c, float d) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  v.x += a;
+  v.y += b;
+  v.z += c;
+  v.w += d;
+  *reinterpret_cast<float4*>(p) = v;
+}
+
 // Work-item order.  Items are (unit, w) with W items per unit, w = 0 the heaviest.
 // Consecutive workgroup ids land on consecutive XCDs (id % 8).  When every unit carries the
 // same work (dense inputs), the items of one XCD are taken from one contiguous range of the

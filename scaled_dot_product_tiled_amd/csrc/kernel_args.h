@@ -28,6 +28,11 @@ struct AttnArgs {
   float* out_f32;  // forward: O in fp32 instead of out (chunk partials); NULL otherwise
   __bf16* dk;
   __bf16* dv;
+  // backward of a chunk pair: when set, the pair's dQ, dK, dV are added to these fp32
+  // accumulators (same strides as dq, dk, dv) instead of written in bf16
+  float* dq_f32;
+  float* dk_f32;
+  float* dv_f32;
   float* lse;   // forward writes, backward reads
   float* delta;  // backward: rowsum(dO * O)
   __bf16* dsb;   // backward: dS blocks (see ds_block_index)

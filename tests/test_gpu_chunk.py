@@ -55,7 +55,8 @@ def ring_forward(q, k, v, bounds, scale, causal, window):
 
 
 def ring_backward(q, k, v, do, merged, bounds, scale, causal, window):
-    """Gradient parts of every pair from the merged (final) O and LSE; the sums in fp32."""
+    """Per query chunk and key chunk: the pair's gradient parts written in bf16, and the same
+    parts added by the kernels into fp32 accumulators dQ, dK, dV (the ring's running sums)."""
     dq = torch.zeros(q.shape, device=q.device, dtype=torch.float32)
     dk = torch.zeros(k.shape, device=q.device, dtype=torch.float32)
     dv = torch.zeros(v.shape, device=q.device, dtype=torch.float32)
@@ -65,12 +66,10 @@ def ring_backward(q, k, v, do, merged, bounds, scale, causal, window):
         o, lse = merged[a]
         for c in range(len(bounds) - 1):
             k0, k1 = bounds[c], bounds[c + 1]
-            gq, gk, gv = sdpt.attn_bwd_chunk(q[:, q0:q1], k[:, k0:k1], v[:, k0:k1], o, lse, do[:, q0:q1], q0, k0,
-                                             scale=scale, causal=causal, window=window)
-            parts[a, c] = (gq, gk, gv)
-            dq[:, q0:q1] += gq.float()
-            dk[:, k0:k1] += gk.float()
-            dv[:, k0:k1] += gv.float()
+            args = (q[:, q0:q1], k[:, k0:k1], v[:, k0:k1], o, lse, do[:, q0:q1], q0, k0)
+            kw = dict(scale=scale, causal=causal, window=window)
+            parts[a, c] = sdpt.attn_bwd_chunk(*args, **kw)
+            sdpt.attn_bwd_chunk(*args, dq=dq[:, q0:q1], dk=dk[:, k0:k1], dv=dv[:, k0:k1], accumulate=True, **kw)
     torch.cuda.synchronize()
     return parts, (dq, dk, dv)
 
@@ -128,7 +127,8 @@ def test_ring_chunks_match_oracle(name, w, bounds):
         assert max_abs(host(o), ro[:, q0:q1]) <= O_MAX_ABS, a
         assert max_abs(host(lse), rl[:, :, q0:q1]) <= LSE_MAX_ABS, a
 
-    # gradients: parts against the oracle's chunk backward, sums against the whole backward
+    # gradients: parts against the oracle's chunk backward, the kernels' fp32 sums against the
+    # whole backward
     gparts, (dq, dk, dv) = ring_backward(q, k, v, do, merged, bounds, w.scale, w.causal, w.window)
     for (a, c), (gq, gk, gv) in gparts.items():
         q0, q1, k0, k1 = bounds[a], bounds[a + 1], bounds[c], bounds[c + 1]
@@ -165,6 +165,12 @@ def test_pairs_without_visible_keys_and_far_positions():
         torch.cuda.synchronize()
         for t in (gq, gk, gv):
             assert not host_bits(t).any(), (qp, kp, win)
+    # accumulating the parts of a pair without visible keys leaves the accumulators as they were
+    acc = [torch.full(t.shape, 1.5, device="cuda:0", dtype=torch.float32) for t in (qc, kc, vc)]
+    sdpt.attn_bwd_chunk(qc, kc, vc, o_ref, l_ref, dc, 0, 128, scale=w.scale, dq=acc[0], dk=acc[1], dv=acc[2],
+                        accumulate=True)
+    torch.cuda.synchronize()
+    assert all(bool((t == 1.5).all()) for t in acc)
     # distances decide visibility: shifting both chunks by 2^40 changes no byte
     big = 1 << 40
     for (qp, kp, win) in ((512, 0, 0), (300, 256, 0), (700, 600, 150), (128, 128, 64)):

@@ -155,9 +155,12 @@ def test_chunk_and_merge_checks():
     assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512)) == OK       # empty batch
     assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512), odt=0) == OK
     assert fwd(shape=AttnChunkShape(2, 0, 96, 8, 2, 512)) == OK        # no query rows
-    st = lib.attn_bwd_chunk(ctypes.byref(c), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, 64, 0,
-                            _t(), _t(), _t(), None, 0, None)
-    assert st == WORKSPACE
+    def bwd(gdt=0, ws=None, wsb=0):
+        return lib.attn_bwd_chunk(ctypes.byref(c), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, 64, 0,
+                                  _t(), _t(), _t(), gdt, ws, wsb, None)
+    assert bwd() == WORKSPACE
+    assert bwd(gdt=1) == WORKSPACE
+    assert bwd(gdt=3, ws=0x100000, wsb=1 << 30) == INVALID             # parts are bf16 or fp32
 
     def merge(B=2, S=64, H=8, D=512, lse=0x20000, part=0x30000, o=None, out=None):
         return lib.attn_lse_merge(B, S, H, D, o or _t(), lse, _t(), part, out or AttnTensor(None, 0, 0, 0), None)

@@ -102,7 +102,6 @@ def other_workload(name, steps, stream):
            "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2)}
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
     del q, k, v, do, o, lse, dq, dk, dv
-    torch.cuda.empty_cache()
     return res
 
 
@@ -170,7 +169,6 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
            "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2), "kernels": kern}
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
     del q, do, k, v, acc_o, part, acc_l, part_l, o, dq, dk, dv, ws
-    torch.cuda.empty_cache()
     return res
 
 

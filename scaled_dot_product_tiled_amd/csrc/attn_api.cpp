@@ -233,8 +233,27 @@ size_t stat_bytes(const Call& c) {
   return round_up(sizeof(float) * (size_t)c.Hq * (c.varlen == 2 ? (size_t)c.total : (size_t)c.B * c.S));
 }
 
+// The dK/dV pass has one workgroup per 64-key tile of each (batch, kv head); with fewer tiles
+// than compute units (short dense sequences, chunk pairs of a ring) each tile's query heads are
+// split over 2 or 4 workgroups, whose fp32 partial sums a reduction adds in a fixed order.
+constexpr int kComputeUnits = 256;  // MI355X
+
+int kv_split_for(const Call& c) {
+  if (c.varlen != 0) return 1;
+  const int64_t items = (int64_t)c.B * c.Hkv * ((c.Sk + attn::kDkdvKeys - 1) / attn::kDkdvKeys);
+  const int r = c.Hq / c.Hkv;
+  int split = 1;
+  while (split < 4 && items * split < kComputeUnits && r % (2 * split) == 0) split *= 2;
+  return split;
+}
+
+size_t kv_part_bytes(const Call& c) {
+  const int split = kv_split_for(c);
+  return split > 1 ? round_up(sizeof(float) * 2 * split * (size_t)c.B * c.Sk * c.Hkv * c.D) : 0;
+}
+
 size_t bwd_bytes(const Call& c) {
-  return meta_bytes(c.B, c.varlen) + stat_bytes(c) + ds_bytes(c);
+  return meta_bytes(c.B, c.varlen) + stat_bytes(c) + ds_bytes(c) + kv_part_bytes(c);
 }
 
 Call whole_call(const attn_shape* s, int varlen, int causal, int window) {
@@ -375,9 +394,14 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
 
   attn::AttnArgs kv = a;
   kv.nkt = (c.Sk + attn::kDkdvKeys - 1) / attn::kDkdvKeys;
-  kv.total_items = c.B * c.Hkv * kv.nkt;
+  kv.kv_split = kv_split_for(c);
+  kv.kv_part = kv.kv_split > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(a.dsb) + ds_bytes(c)) : nullptr;
+  kv.total_items = c.B * c.Hkv * kv.nkt * kv.kv_split;
   kv.per_xcd = (kv.total_items + 7) / 8;
   if ((st = launch("bwd_dkdv", s, kv.total_items, [&] { return attn::launch_bwd_dkdv(kv, c.D, s); }))) return st;
+  if (kv.kv_split > 1 &&
+      (st = launch("bwd_kv_reduce", s, c.B * c.Sk, [&] { return attn::launch_bwd_kv_reduce(kv, c.D, s); })))
+    return st;
 
   attn::AttnArgs qa = a;
   qa.nqt = (c.S + attn::kDsRows - 1) / attn::kDsRows;

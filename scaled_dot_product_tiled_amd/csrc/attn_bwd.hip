@@ -104,11 +104,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) f32x4 xsc[2][2][64];        // S, registers 8..15: [kb][reg/4 - 2][lane]
   __shared__ __attribute__((aligned(16))) bf16x8 pds[2][2][2][64];    // [P|dS][kb][s][lane]
 
-  const int item = xcd_item(a.per_xcd, a.total_items, a.nkt, a.balanced);
+  const int item = xcd_item(a.per_xcd, a.total_items, a.nkt * a.kv_split, a.balanced);
   if (item < 0) return;
-  const int unit = item / a.nkt;
-  const int kt = item - unit * a.nkt;  // low key tiles see the most query rows: first
+  const int unit = item / (a.nkt * a.kv_split);
+  const int rem = item - unit * (a.nkt * a.kv_split);
+  const int kt = rem / a.kv_split;  // low key tiles see the most query rows: first
+  const int part = rem - kt * a.kv_split;
   const int g = unit % a.Hkv;
+  // the query heads of the group this workgroup visits: all of them, or one of kv_split
+  // equal parts (then its dK, dV are partial sums, added by a separate reduction)
+  const int rs = a.r / a.kv_split;
+  const int hb0 = g * a.r + part * rs;
   const int b = unit / a.Hkv;
   int len = a.seq_len ? a.seq_len[b] : a.S;
   len = min(max(len, 0), a.S);
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   if (a.window > 0) qhi = min(qhi, j0 + NK - 1 + a.window - dlt);
   const int tq0 = qlo / MQ;
   const int nq = (j0 < lenk && qhi > qlo) ? (qhi + MQ - 1) / MQ - tq0 : 0;
-  const int nsteps = a.r * nq;
+  const int nsteps = rs * nq;
 
   if (nsteps > 0) {
     // this wave's 32 keys of K (score waves) or V (dP waves) as B operands
@@ -171,12 +177,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     int hi = 0, qi = 0;  // step k
     auto stats = [&](int hs, int i0s, int buf) {
       if (wave == 0) {
-        const int64_t so = b * a.st_sb + (g * a.r + hs) * a.st_sh + off;
+        const int64_t so = b * a.st_sb + (hb0 + hs) * a.st_sh + off;
         dma_stats(stat[buf], a.lse + so, a.delta + so, i0s, len - 1, lane);
       }
     };
     {
-      const int h0 = g * a.r;
+      const int h0 = hb0;
       const int i00 = tq_last * MQ;
       dma_rows<D, MQ, 4>(Qs[0], tile_src<MQ>(a.q + b * a.q_sb + (int64_t)off * a.q_ss + h0 * a.q_sh, a.q_ss, i00,
                                              len - i00), wave, lane);
@@ -187,13 +193,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     for (int k = 0; k < nsteps; ++k) {
       const int buf = k & 1;
       const int i0 = (tq_last - qi) * MQ;
-      const int hn = hi + 1 == a.r ? 0 : hi + 1;          // step k+1
-      const int i0n = hi + 1 == a.r ? i0 - MQ : i0;
+      const int hn = hi + 1 == rs ? 0 : hi + 1;          // step k+1
+      const int i0n = hi + 1 == rs ? i0 - MQ : i0;
       const bool has_next = k + 1 < nsteps;
       // the last step copies nothing real: an empty range reads zeros into the idle buffers
-      const TileSrc qn = tile_src<MQ>(a.q + b * a.q_sb + (int64_t)off * a.q_ss + (g * a.r + hn) * a.q_sh, a.q_ss,
+      const TileSrc qn = tile_src<MQ>(a.q + b * a.q_sb + (int64_t)off * a.q_ss + (hb0 + hn) * a.q_sh, a.q_ss,
                                       i0n, has_next ? len - i0n : 0);
-      const TileSrc dn = tile_src<MQ>(a.dout + b * a.do_sb + (int64_t)off * a.do_ss + (g * a.r + hn) * a.do_sh,
+      const TileSrc dn = tile_src<MQ>(a.dout + b * a.do_sb + (int64_t)off * a.do_ss + (hb0 + hn) * a.do_sh,
                                       a.do_ss, i0n, has_next ? len - i0n : 0);
       wait_vmcnt<0>();
       barrier_lds();  // step k is in LDS; every wave is done with step k-1
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         const int64_t bi = ds_block_index(i0 / kDsRows, (j0 / kDsKeys) + kb, a.causal, a.window, dlt, lenk,
                                           a.ds_tri, a.ds_cnt);
         if (bi >= 0) {
-          bf16* dst = a.dsb + ((int64_t)(b * a.Hq + g * a.r + hi) * a.ds_head + bi) * kDsBlockElems +
+          bf16* dst = a.dsb + ((int64_t)(b * a.Hq + hb0 + hi) * a.ds_head + bi) * kDsBlockElems +
                       ln * kDsRows + (i0 & (kDsRows - 1)) + 8 * xh + 4 * g2;
           *reinterpret_cast<bf16x4*>(dst) = bf16x4{db[0], db[1], db[2], db[3]};
           *reinterpret_cast<bf16x4*>(dst + 8) = bf16x4{db[4], db[5], db[6], db[7]};
@@ -313,12 +319,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      qi += hi + 1 == a.r;
+      qi += hi + 1 == rs;
       hi = hn;
     }
   }
 
   // dV^T / dK^T blocks: lane = key j0 + 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4
+  if (a.kv_split > 1) {
+    // partial sums over this workgroup's heads, every key of the tile (zeros where no row
+    // of these heads sees it), reduced by bwd_kv_reduce in part order
+    const int64_t plane = (int64_t)a.B * a.Sk * a.Hkv * D;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int key = j0 + 32 * x + ln;
+      if (key >= a.Sk) continue;
+      const int64_t row = (((int64_t)b * a.Sk + key) * a.Hkv + g) * D + 4 * g2;
+      float* pk = a.kv_part + (2 * part) * plane + row;
+      float* pv = a.kv_part + (2 * part + 1) * plane + row;
+      const float sc = a.scale;
+#pragma unroll
+      for (int d = 0; d < DBW; ++d)
+#pragma unroll
+        for (int qa = 0; qa < 4; ++qa) {
+          const int col = 32 * (dsl + d) + 8 * qa;
+          stg4(pk + col, dkacc[x][d][4 * qa] * sc, dkacc[x][d][4 * qa + 1] * sc, dkacc[x][d][4 * qa + 2] * sc,
+               dkacc[x][d][4 * qa + 3] * sc);
+          stg4(pv + col, dvacc[x][d][4 * qa], dvacc[x][d][4 * qa + 1], dvacc[x][d][4 * qa + 2],
+               dvacc[x][d][4 * qa + 3]);
+        }
+    }
+    return;
+  }
   if (a.dk_f32 != nullptr) {
     // accumulate a chunk pair's parts; a tile that no query row of the pair sees adds nothing
     if (nsteps == 0) return;
@@ -360,6 +391,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         stg4(pv + col, dvacc[x][d][4 * qa], dvacc[x][d][4 * qa + 1], dvacc[x][d][4 * qa + 2], dvacc[x][d][4 * qa + 3]);
       }
   }
+}
+
+// dK, dV of workgroups that split a group's query heads: the sum of the parts in part order
+// (deterministic), written in bf16 or added to the fp32 accumulators.  Elementwise: 8
+// consecutive head_dim elements per thread.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(AttnArgs a) {
+  constexpr int TPR = D / 8;
+  const int64_t rows = (int64_t)a.B * a.Sk * a.Hkv;
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gi / TPR;
+  if (row >= rows) return;
+  const int c0 = 8 * (int)(gi - row * TPR);
+  const int g = (int)(row % a.Hkv);
+  const int64_t bk = row / a.Hkv;
+  const int key = (int)(bk % a.Sk);
+  const int b = (int)(bk / a.Sk);
+  const int64_t plane = rows * D;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    for (int p = 0; p < a.kv_split; ++p) {
+      const float* src = a.kv_part + (2 * p + which) * plane + row * D + c0;
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+      v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+    }
+    if (a.dk_f32 != nullptr) {
+      float* acc = (which ? a.dv_f32 + b * a.dv_sb + (int64_t)key * a.dv_ss + g * a.dv_sh
+                          : a.dk_f32 + b * a.dk_sb + (int64_t)key * a.dk_ss + g * a.dk_sh) + c0;
+      add4(acc, v[0], v[1], v[2], v[3]);
+      add4(acc + 4, v[4], v[5], v[6], v[7]);
+    } else {
+      bf16* out = (which ? a.dv + b * a.dv_sb + (int64_t)key * a.dv_ss + g * a.dv_sh
+                         : a.dk + b * a.dk_sb + (int64_t)key * a.dk_ss + g * a.dk_sh) + c0;
+      stg4(out, v[0], v[1], v[2], v[3]);
+      stg4(out + 4, v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+hipError_t launch_bwd_kv_reduce(const AttnArgs& a, int D, hipStream_t stream) {
+  const int64_t threads = (int64_t)a.B * a.Sk * a.Hkv * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (D == 512)
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel<512>, grid, block, 0, stream, a);
+  else if (D == 256)
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel<256>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {

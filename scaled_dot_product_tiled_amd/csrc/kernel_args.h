@@ -55,6 +55,8 @@ struct AttnArgs {
   int empty_lse_ninf;       // a query row with no visible key stores LSE = -inf (else 0)
   int hpt, mpos, nhb, nqt;  // heads per tile, positions per tile, head blocks, q tiles
   int nkt;                  // key tiles (dK/dV kernel)
+  int kv_split;             // dK/dV: workgroups sharing one key tile's query heads (1, 2 or 4)
+  float* kv_part;           // kv_split > 1: fp32 partial dK, dV, [part][dK|dV][B][Sk][Hkv][D]
   int packed;               // rows past a sequence's length do not exist
   int causal, window;
   float scale;              // multiplies Q K^T
@@ -130,6 +132,7 @@ hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd_kv_reduce(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, int D, hipStream_t stream);

@@ -98,7 +98,7 @@ def test_backward_and_decode_checks():
                       _t(), _t(), _t(), None, 0, None)
     assert st == WORKSPACE
     st = lib.attn_bwd(ctypes.byref(s), _t(), _t(), _t(), _t(), 0x20000, _t(ptr=0), 0.05, 1, 0, None, None,
-                      _t(), _t(), _t(), 0x100000, 1 << 20, None)
+                      _t(), _t(), _t(), 0x100000, 1 << 24, None)
     assert st == INVALID
     d = AttnDecodeShape(4, 32, 8, 128, 16, 100, 8)
     kc = AttnTensor(0x10000, 16 * 8 * 128, 8 * 128, 128)
@@ -119,10 +119,13 @@ def test_chunk_workspace_sizes():
     """Chunk pairs of a sequence cut into 2048-row chunks (head_dim 512, 32 query heads): the
     diagonal pair keeps the triangular dS layout, a pair wholly in the past keeps every key block,
     a pair wholly in the future stores nothing, and a window keeps (window + 128) / 32 + 6 blocks
-    per 128-row query tile."""
+    per 128-row query tile.  128 key tiles (4 kv heads x 32) are fewer than the 256 compute
+    units, so each tile's 8 query heads are split over 2 workgroups whose fp32 partial dK, dV
+    (2 parts x 2 tensors x 2048 x 4 x 512) take space too."""
     lib = load_library()
     c = AttnChunkShape(1, 2048, 2048, 32, 4, 512)
-    delta = 2048 * 32 * 4
+    kvp = 2 * 2 * 2048 * 4 * 512 * 4
+    delta = 2048 * 32 * 4 + kvp
     blk = 32 * 128 * 2
 
     def ws(causal, window, qp, kp, shape=c):

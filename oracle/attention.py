@@ -30,7 +30,10 @@ Readings adopted where the pages are silent (each is listed in the design notes)
   token t < ctx_b (fourth page, Architecture notes: PagedKVCache + PageTable);
 * a chunk pair of the ring path (first page, Integration) places query i at position
   q_pos0 + i and key j at k_pos0 + j; a row that sees no key of the chunk has LSE = -inf
-  (the identity of the log-sum-exp merge) and O = 0.
+  (the identity of the log-sum-exp merge) and O = 0;
+* the softcap that the first page's gate sends to the eager path (Integration) is the tanh
+  soft-capping of the scaled scores, s -> cap * tanh(s / cap), applied before masking;
+  cap <= 0 means none.
 """
 from __future__ import annotations
 
@@ -38,7 +41,7 @@ import numpy as np
 
 __all__ = [
     "visibility", "lengths_from_pad_mask", "lengths_from_cu_seqlens",
-    "unit_forward", "unit_backward", "attention_forward", "attention_backward",
+    "scores", "unit_forward", "unit_backward", "attention_forward", "attention_backward",
     "attention_forward_head", "attention_backward_group",
     "attention_forward_packed", "attention_backward_packed",
     "gather_pages", "paged_decode", "paged_decode_one", "attention_rows",
@@ -87,16 +90,27 @@ def lengths_from_cu_seqlens(cu: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # One (batch, head) unit
 # ---------------------------------------------------------------------------
-def unit_forward(q, k, v, scale, vis):
+def scores(q, k, scale, softcap=0.0):
+    """Scaled scores scale * q k^T, soft-capped to cap * tanh(s / cap) when cap = softcap > 0.
+    Returns the scores and their derivative with respect to the uncapped scaled score
+    (1 - tanh^2, or 1 without a cap)."""
+    s = scale * (q @ k.T)
+    if softcap > 0:
+        t = np.tanh(s / softcap)
+        return softcap * t, 1.0 - t * t
+    return s, np.ones_like(s)
+
+
+def unit_forward(q, k, v, scale, vis, softcap=0.0):
     """One head: q (n, D), k (n, D), v (n, D) float64 and vis (n, n).
 
     Returns O (n, D), LSE (n,) and the probabilities P (n, n).  Every key row
     passed in must be finite: invisible keys get probability exactly 0, which
     removes a finite value but not a NaN.
-    S = scale * q k^T with invisible entries at -inf; P = row softmax of S;
-    O = P v; LSE = rowmax + ln(sum exp(S - rowmax)).
+    S = scale * q k^T (soft-capped when softcap > 0) with invisible entries at -inf;
+    P = row softmax of S; O = P v; LSE = rowmax + ln(sum exp(S - rowmax)).
     """
-    s = scale * (q @ k.T)
+    s, _ = scores(q, k, scale, softcap)
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)
     live = np.isfinite(m)
@@ -110,16 +124,17 @@ def unit_forward(q, k, v, scale, vis):
     return o, lse, p
 
 
-def unit_backward(q, k, v, do, scale, vis):
+def unit_backward(q, k, v, do, scale, vis, softcap=0.0):
     """Gradients of sum(O * dO) for one head; returns dQ, dK, dV (this head's share of dK, dV).
 
-    dP = dO v^T; delta_i = sum_j P_ij dP_ij; dS = P * (dP - delta); dQ = scale dS k;
-    dK = scale dS^T q; dV = P^T dO.
+    dP = dO v^T; delta_i = sum_j P_ij dP_ij; dS = P * (dP - delta), times the cap's
+    derivative 1 - tanh^2 under a softcap; dQ = scale dS k; dK = scale dS^T q; dV = P^T dO.
     """
-    o, _, p = unit_forward(q, k, v, scale, vis)
+    o, _, p = unit_forward(q, k, v, scale, vis, softcap)
+    _, deriv = scores(q, k, scale, softcap)
     dp = do @ v.T
     delta = (p * dp).sum(axis=1)
-    ds = p * (dp - delta[:, None])
+    ds = p * (dp - delta[:, None]) * deriv
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     dv = p.T @ do
@@ -135,7 +150,7 @@ def _lengths(B, S, lengths):
     return np.asarray(lengths, dtype=np.int64)
 
 
-def attention_forward_head(q, k, v, b, h, scale, causal=True, window=0, lengths=None):
+def attention_forward_head(q, k, v, b, h, scale, causal=True, window=0, lengths=None, softcap=0.0):
     """O (S, D) and LSE (S,) of one (batch, query-head) unit; rows at or past the length are 0."""
     B, S, Hq, D = q.shape
     r = Hq // k.shape[2]
@@ -144,22 +159,23 @@ def attention_forward_head(q, k, v, b, h, scale, causal=True, window=0, lengths=
     lse = np.zeros(S)
     if n > 0:
         o[:n], lse[:n], _ = unit_forward(q[b, :n, h], k[b, :n, h // r], v[b, :n, h // r], scale,
-                                         visibility(n, causal, window))
+                                         visibility(n, causal, window), softcap)
     return o, lse
 
 
-def attention_forward(q, k, v, scale, causal=True, window=0, lengths=None):
+def attention_forward(q, k, v, scale, causal=True, window=0, lengths=None, softcap=0.0):
     """Returns O (B, S, Hq, D) float64 and LSE (B, Hq, S) float64."""
     B, S, Hq, D = q.shape
     o = np.zeros((B, S, Hq, D))
     lse = np.zeros((B, Hq, S))
     for b in range(B):
         for h in range(Hq):
-            o[b, :, h], lse[b, h] = attention_forward_head(q, k, v, b, h, scale, causal, window, lengths)
+            o[b, :, h], lse[b, h] = attention_forward_head(q, k, v, b, h, scale, causal, window, lengths,
+                                                           softcap)
     return o, lse
 
 
-def attention_backward_group(q, k, v, do, b, g, scale, causal=True, window=0, lengths=None):
+def attention_backward_group(q, k, v, do, b, g, scale, causal=True, window=0, lengths=None, softcap=0.0):
     """dQ (S, r, D) for the r query heads of kv-head g, and dK, dV (S, D) summed over them.
 
     Rows of dQ and keys of dK, dV at or past the sequence length are 0.
@@ -175,14 +191,14 @@ def attention_backward_group(q, k, v, do, b, g, scale, causal=True, window=0, le
     vis = visibility(n, causal, window)
     for i in range(r):                   # fixed head order
         h = g * r + i
-        dqh, dkh, dvh = unit_backward(q[b, :n, h], k[b, :n, g], v[b, :n, g], do[b, :n, h], scale, vis)
+        dqh, dkh, dvh = unit_backward(q[b, :n, h], k[b, :n, g], v[b, :n, g], do[b, :n, h], scale, vis, softcap)
         dq[:n, i] = dqh
         dk[:n] += dkh
         dv[:n] += dvh
     return dq, dk, dv
 
 
-def attention_backward(q, k, v, do, scale, causal=True, window=0, lengths=None):
+def attention_backward(q, k, v, do, scale, causal=True, window=0, lengths=None, softcap=0.0):
     """Returns dQ (B, S, Hq, D), dK and dV (B, S, Hkv, D), float64."""
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -192,14 +208,14 @@ def attention_backward(q, k, v, do, scale, causal=True, window=0, lengths=None):
     dv = np.zeros(v.shape)
     for b in range(B):
         for g in range(Hkv):
-            gq, gk, gv = attention_backward_group(q, k, v, do, b, g, scale, causal, window, lengths)
+            gq, gk, gv = attention_backward_group(q, k, v, do, b, g, scale, causal, window, lengths, softcap)
             dq[b, :, g * r:(g + 1) * r] = gq
             dk[b, :, g] = gk
             dv[b, :, g] = gv
     return dq, dk, dv
 
 
-def attention_rows(q, k, v, do, b, h, rows, scale, causal=True, window=0, lengths=None):
+def attention_rows(q, k, v, do, b, h, rows, scale, causal=True, window=0, lengths=None, softcap=0.0):
     """O, LSE and dQ of selected query rows of one (batch, head), one row at a time.
 
     Everything a query row needs is row-local: its visible keys, its softmax, and for
@@ -220,18 +236,19 @@ def attention_rows(q, k, v, do, b, h, rows, scale, causal=True, window=0, length
             continue
         vis = visibility(n, causal, window)[i][None, :]
         kk, vv = k[b, :n, g], v[b, :n, g]
-        oi, li, p = unit_forward(q[b, i, h][None, :], kk, vv, scale, vis)
+        oi, li, p = unit_forward(q[b, i, h][None, :], kk, vv, scale, vis, softcap)
         o[x], lse[x] = oi[0], li[0]
         if do is not None:
+            _, deriv = scores(q[b, i, h][None, :], kk, scale, softcap)
             dp = do[b, i, h][None, :] @ vv.T
             delta = (p * dp).sum(axis=1)
-            ds = p * (dp - delta[:, None])
+            ds = p * (dp - delta[:, None]) * deriv
             dq[x] = scale * (ds @ kk)[0]
     return o, lse, dq
 
 
 # Packed rows (cu_seqlens): q, o, dO (T, Hq, D); k, v (T, Hkv, D); LSE (Hq, T).
-def attention_forward_packed(q, k, v, cu_seqlens, scale, causal=True, window=0):
+def attention_forward_packed(q, k, v, cu_seqlens, scale, causal=True, window=0, softcap=0.0):
     lengths = lengths_from_cu_seqlens(cu_seqlens)
     T, Hq, D = q.shape
     r = Hq // k.shape[1]
@@ -245,11 +262,11 @@ def attention_forward_packed(q, k, v, cu_seqlens, scale, causal=True, window=0):
         vis = visibility(n, causal, window)
         for h in range(Hq):
             o[s0:s0 + n, h], lse[h, s0:s0 + n], _ = unit_forward(
-                q[s0:s0 + n, h], k[s0:s0 + n, h // r], v[s0:s0 + n, h // r], scale, vis)
+                q[s0:s0 + n, h], k[s0:s0 + n, h // r], v[s0:s0 + n, h // r], scale, vis, softcap)
     return o, lse
 
 
-def attention_backward_packed(q, k, v, do, cu_seqlens, scale, causal=True, window=0):
+def attention_backward_packed(q, k, v, do, cu_seqlens, scale, causal=True, window=0, softcap=0.0):
     lengths = lengths_from_cu_seqlens(cu_seqlens)
     T, Hq, D = q.shape
     r = Hq // k.shape[1]
@@ -265,7 +282,7 @@ def attention_backward_packed(q, k, v, do, cu_seqlens, scale, causal=True, windo
         for h in range(Hq):
             g = h // r
             a, bk, bv = unit_backward(q[s0:s0 + n, h], k[s0:s0 + n, g], v[s0:s0 + n, g],
-                                      do[s0:s0 + n, h], scale, vis)
+                                      do[s0:s0 + n, h], scale, vis, softcap)
             dq[s0:s0 + n, h] = a
             dk[s0:s0 + n, g] += bk
             dv[s0:s0 + n, g] += bv
@@ -292,7 +309,7 @@ def chunk_visibility(nq: int, nk: int, q_pos0: int, k_pos0: int, causal: bool, w
     return vis
 
 
-def attention_forward_chunk(q, k, v, scale, causal, window, q_pos0, k_pos0):
+def attention_forward_chunk(q, k, v, scale, causal, window, q_pos0, k_pos0, softcap=0.0):
     """Partial attention of a query chunk q (B, Sq, Hq, D) against one key/value chunk k, v
     (B, Sk, Hkv, D): O (B, Sq, Hq, D) and LSE (B, Hq, Sq) over the chunk's visible keys.  A row
     that sees no key of the chunk gets O = 0 and LSE = -inf, the identity of lse_merge."""
@@ -305,7 +322,7 @@ def attention_forward_chunk(q, k, v, scale, causal, window, q_pos0, k_pos0):
     lse = np.full((B, Hq, Sq), -np.inf)
     for b in range(B):
         for h in range(Hq):
-            ob, lb, _ = unit_forward(q[b, :, h], k[b, :, h // r], v[b, :, h // r], scale, vis)
+            ob, lb, _ = unit_forward(q[b, :, h], k[b, :, h // r], v[b, :, h // r], scale, vis, softcap)
             o[b, :, h] = ob
             lse[b, h] = np.where(live, lb, -np.inf)
     return o, lse
@@ -328,7 +345,7 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
     return fa * o_a + fb * o_b, lse
 
 
-def attention_backward_chunk(q, k, v, o, lse, do, scale, causal, window, q_pos0, k_pos0):
+def attention_backward_chunk(q, k, v, o, lse, do, scale, causal, window, q_pos0, k_pos0, softcap=0.0):
     """Gradient contributions of one (query chunk, key chunk) pair, given the rows' final O
     (B, Sq, Hq, D) and LSE (B, Hq, Sq) over all their keys: P = exp(scale q k^T - LSE) on the
     chunk's visible entries, delta = rowsum(dO * O), dS = P (dP - delta), dQ = scale dS k,
@@ -345,13 +362,13 @@ def attention_backward_chunk(q, k, v, o, lse, do, scale, causal, window, q_pos0,
     for b in range(B):
         for h in range(Hq):
             g = h // r
-            s = scale * (q[b, :, h] @ k[b, :, g].T)
+            s, deriv = scores(q[b, :, h], k[b, :, g], scale, softcap)
             live = np.isfinite(lse[b, h])[:, None]       # a row that sees no key has no gradient
             arg = np.where(vis & live, s - np.where(live, lse[b, h][:, None], 0.0), -np.inf)
             p = np.exp(arg)
             dp = do[b, :, h] @ v[b, :, g].T
             delta = (do[b, :, h] * o[b, :, h]).sum(axis=1)
-            ds = p * (dp - delta[:, None])
+            ds = p * (dp - delta[:, None]) * deriv
             dq[b, :, h] = scale * (ds @ k[b, :, g])
             dk[b, :, g] += scale * (ds.T @ q[b, :, h])
             dv[b, :, g] += p.T @ do[b, :, h]

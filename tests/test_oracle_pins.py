@@ -13,7 +13,9 @@
 * the paged decode equals causal attention's last row on the gathered tokens, and does not
   depend on which pool pages hold them;
 * chunk pairs (ring context parallelism) merge, by log-sum-exp, to the full attention, and
-  their gradient parts sum to the full gradients.
+  their gradient parts sum to the full gradients;
+* the tanh softcap: central differences, torch autograd through explicit tanh / softmax
+  tensor ops, and its limits (a huge cap is no cap; equal scores stay equal).
 """
 import json
 import math
@@ -211,19 +213,22 @@ def test_pad_mask_lengths_and_rejection():
 # ---------------------------------------------------------------------------
 # Finite differences: every coordinate of dQ, dK, dV
 # ---------------------------------------------------------------------------
-def test_gradients_match_central_differences():
+@pytest.mark.parametrize("softcap", [0.0, 1.3])
+def test_gradients_match_central_differences(softcap):
     rng = np.random.default_rng(8)
     B, S, Hq, Hkv, D = 2, 9, 4, 2, 8
     lengths = [9, 5]
     scale, causal, window = 0.37, True, 3
     q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
     k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    if softcap:
+        q *= 2.0                            # scores of a few units: the cap bends them
 
     def loss(q_, k_, v_):
-        o, _ = oracle.attention_forward(q_, k_, v_, scale, causal, window, lengths)
+        o, _ = oracle.attention_forward(q_, k_, v_, scale, causal, window, lengths, softcap)
         return float((o * do).sum())
 
-    grads = oracle.attention_backward(q, k, v, do, scale, causal, window, lengths)
+    grads = oracle.attention_backward(q, k, v, do, scale, causal, window, lengths, softcap)
     eps = 1e-6
     for which, g in enumerate(grads):
         base = [q, k, v]
@@ -290,6 +295,60 @@ def test_matches_torch_float64_sdpa(causal, window, lengths, Hq, Hkv, D):
                          torch.tensor(np.repeat(k[b, :n], r, axis=1).transpose(1, 0, 2))) * scale
         s = s.masked_fill(~torch.tensor(mask[b, 0, :n, :n]), float("-inf"))
         np.testing.assert_allclose(lse[b, :, :n], torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,window,lengths,softcap", [
+    (True, 0, None, 2.0),
+    (True, 9, [40, 13], 0.7),
+    (False, 0, [40, 31], 5.0),
+])
+def test_softcap_matches_torch_autograd(causal, window, lengths, softcap):
+    """Soft-capped attention written with torch's float64 CPU tensor ops (tanh, masked softmax,
+    matmul) and differentiated by torch's autograd: a second, independent route to the same
+    numbers.  Masked entries are excluded after the cap, so tanh never sees -inf."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    B, S, Hq, Hkv, D = 2, 40, 4, 2, 16
+    scale = 1.0 / math.sqrt(D)
+    q, do = 3.0 * _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    L = [S] * B if lengths is None else lengths
+    o, lse = oracle.attention_forward(q, k, v, scale, causal, window, lengths, softcap)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal, window, lengths, softcap)
+    r = Hq // Hkv
+    for b in range(B):
+        n = L[b]
+        vis = torch.tensor(oracle_free_visibility(n, causal, window))
+        tq = torch.tensor(q[b, :n].transpose(1, 0, 2), requires_grad=True)
+        tk = torch.tensor(k[b, :n].transpose(1, 0, 2), requires_grad=True)
+        tv = torch.tensor(v[b, :n].transpose(1, 0, 2), requires_grad=True)
+        kk = tk.repeat_interleave(r, dim=0)
+        vv = tv.repeat_interleave(r, dim=0)
+        sc = softcap * torch.tanh(scale * torch.matmul(tq, kk.transpose(1, 2)) / softcap)
+        sc = sc.masked_fill(~vis, float("-inf"))
+        to = torch.matmul(torch.softmax(sc, dim=-1), vv)
+        to.backward(torch.tensor(do[b, :n].transpose(1, 0, 2)))
+        np.testing.assert_allclose(o[b, :n], to.detach().numpy().transpose(1, 0, 2), atol=1e-12)
+        np.testing.assert_allclose(lse[b, :, :n], torch.logsumexp(sc, dim=-1).detach().numpy(), atol=1e-12)
+        np.testing.assert_allclose(dq[b, :n], tq.grad.numpy().transpose(1, 0, 2), atol=1e-12)
+        np.testing.assert_allclose(dk[b, :n], tk.grad.numpy().transpose(1, 0, 2), atol=1e-12)
+        np.testing.assert_allclose(dv[b, :n], tv.grad.numpy().transpose(1, 0, 2), atol=1e-12)
+
+
+def test_softcap_limits():
+    """A cap far above every score changes nothing (tanh(x) = x + O(x^3)); equal scores stay
+    equal under the cap, so K = 0 still gives LSE = ln(visible count)."""
+    rng = np.random.default_rng(22)
+    B, S, Hq, Hkv, D = 1, 17, 2, 1, 8
+    q, k, v, do = (_rand(rng, B, S, h, D) for h in (Hq, Hkv, Hkv, Hq))
+    plain = oracle.attention_forward(q, k, v, 0.4, True, 5) + oracle.attention_backward(q, k, v, do, 0.4, True, 5)
+    capped = (oracle.attention_forward(q, k, v, 0.4, True, 5, None, 1e7)
+              + oracle.attention_backward(q, k, v, do, 0.4, True, 5, None, 1e7))
+    for a, b in zip(plain, capped):
+        np.testing.assert_allclose(a, b, atol=1e-10)
+    _, lse = oracle.attention_forward(q, np.zeros_like(k), v, 0.4, True, 5, None, 0.3)
+    cnt = np.minimum(np.arange(S) + 1, 5)
+    np.testing.assert_allclose(lse[0], np.broadcast_to(np.log(cnt), (Hq, S)), atol=1e-14)
 
 
 def oracle_free_visibility(n, causal, window):

@@ -83,6 +83,10 @@ typedef struct {
  *   scale       multiplies Q K^T (must be finite and > 0)
  *   causal      0 or 1
  *   window      0 for none; W > 0 keeps keys j > i - W and requires causal
+ *   softcap     0 for none; cap > 0 replaces every scaled score s by
+ *               cap * tanh(s / cap) before the mask (the tanh soft-capping that
+ *               the first page's gate sends to the eager path, section
+ *               Integration); must be finite and >= 0
  *   cu_seqlens  device int32 (B+1), or NULL
  *   pad_mask    device uint8 (B, S), row-major, 1 = valid; each row must be a
  *               prefix of ones (right padding); or NULL.  At most one of
@@ -96,7 +100,7 @@ typedef struct {
  */
 attn_status attn_fwd(const attn_shape* shape,
                      attn_tensor q, attn_tensor k, attn_tensor v,
-                     float scale, int causal, int window,
+                     float scale, int causal, int window, float softcap,
                      const int32_t* cu_seqlens, const uint8_t* pad_mask,
                      attn_tensor o, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream);
@@ -104,8 +108,9 @@ attn_status attn_fwd(const attn_shape* shape,
 /*
  * attn_bwd: gradients of sum(O * dO) with respect to Q, K and V.
  *
- * q, k, v, scale, causal, window, cu_seqlens, pad_mask and the layouts are as
- * in attn_fwd, and o and lse must be that call's outputs.  dq (Hq heads), dk
+ * q, k, v, scale, causal, window, softcap, cu_seqlens, pad_mask and the layouts
+ * are as in attn_fwd, and o and lse must be that call's outputs.  Under a softcap
+ * the stored dS and the gradients include the cap's derivative 1 - tanh^2.  dq (Hq heads), dk
  * and dv (Hkv heads, summed over the Hq/Hkv query heads that share them) are
  * written in the same layouts as q, k and v.  The page "Root cause analysis:
  * Gemma4 sliding-window BF16 cuDNN SDPA NaN on H100" (Debug and validation
@@ -120,7 +125,7 @@ attn_status attn_fwd(const attn_shape* shape,
 attn_status attn_bwd(const attn_shape* shape,
                      attn_tensor q, attn_tensor k, attn_tensor v,
                      attn_tensor o, const float* lse, attn_tensor dout,
-                     float scale, int causal, int window,
+                     float scale, int causal, int window, float softcap,
                      const int32_t* cu_seqlens, const uint8_t* pad_mask,
                      attn_tensor dq, attn_tensor dk, attn_tensor dv,
                      void* workspace, size_t workspace_bytes, void* stream);
@@ -155,7 +160,7 @@ typedef struct {
  */
 attn_status attn_fwd_chunk(const attn_chunk_shape* shape,
                            attn_tensor q, attn_tensor k, attn_tensor v,
-                           float scale, int causal, int window,
+                           float scale, int causal, int window, float softcap,
                            int64_t q_pos0, int64_t k_pos0,
                            attn_tensor o, int o_dtype, float* lse, void* stream);
 
@@ -183,7 +188,7 @@ attn_status attn_fwd_chunk(const attn_chunk_shape* shape,
 attn_status attn_bwd_chunk(const attn_chunk_shape* shape,
                            attn_tensor q, attn_tensor k, attn_tensor v,
                            attn_tensor o, const float* lse, attn_tensor dout,
-                           float scale, int causal, int window,
+                           float scale, int causal, int window, float softcap,
                            int64_t q_pos0, int64_t k_pos0,
                            attn_tensor dq, attn_tensor dk, attn_tensor dv, int grad_dtype,
                            void* workspace, size_t workspace_bytes, void* stream);

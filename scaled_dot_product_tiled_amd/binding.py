@@ -64,19 +64,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.POINTER
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.attn_fwd.argtypes = [P(AttnShape), AttnTensor, AttnTensor, AttnTensor, ctypes.c_float, ctypes.c_int,
-                             ctypes.c_int, vp, vp, AttnTensor, vp, vp, sz, vp]
+                             ctypes.c_int, ctypes.c_float, vp, vp, AttnTensor, vp, vp, sz, vp]
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [P(AttnShape), AttnTensor, AttnTensor, AttnTensor, AttnTensor, vp, AttnTensor,
-                             ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, vp, AttnTensor, AttnTensor, AttnTensor,
-                             vp, sz, vp]
+                             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, AttnTensor,
+                             AttnTensor, AttnTensor, vp, sz, vp]
     lib.attn_bwd.restype = ctypes.c_int
     i64 = ctypes.c_int64
     lib.attn_fwd_chunk.argtypes = [P(AttnChunkShape), AttnTensor, AttnTensor, AttnTensor, ctypes.c_float, ctypes.c_int,
-                                   ctypes.c_int, i64, i64, AttnTensor, ctypes.c_int, vp, vp]
+                                   ctypes.c_int, ctypes.c_float, i64, i64, AttnTensor, ctypes.c_int, vp, vp]
     lib.attn_fwd_chunk.restype = ctypes.c_int
     lib.attn_bwd_chunk.argtypes = [P(AttnChunkShape), AttnTensor, AttnTensor, AttnTensor, AttnTensor, vp, AttnTensor,
-                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, i64, i64, AttnTensor, AttnTensor,
-                                   AttnTensor, ctypes.c_int, vp, sz, vp]
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_float, i64, i64, AttnTensor,
+                                   AttnTensor, AttnTensor, ctypes.c_int, vp, sz, vp]
     lib.attn_bwd_chunk.restype = ctypes.c_int
     lib.attn_bwd_chunk_workspace_bytes.argtypes = [P(AttnChunkShape), ctypes.c_int, ctypes.c_int, i64, i64]
     lib.attn_bwd_chunk_workspace_bytes.restype = sz
@@ -196,7 +196,7 @@ def _meta_ptrs(cu_seqlens, pad_mask):
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
              window: int = 0, cu_seqlens: Optional[torch.Tensor] = None, pad_mask: Optional[torch.Tensor] = None,
              max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+             lse: Optional[torch.Tensor] = None, softcap: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor]:
     """O, LSE of causal grouped-query attention.  q (B,S,Hq,D), k/v (B,S,Hkv,D); with cu_seqlens the
     rows are packed: q (T,Hq,D), k/v (T,Hkv,D), LSE (Hq,T).  Returns (O, LSE fp32)."""
     lib = load_library()
@@ -215,7 +215,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
     nbytes = lib.attn_fwd_workspace_bytes(ctypes.byref(shape), varlen)
     ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
     st = lib.attn_fwd(ctypes.byref(shape), _tensor(q, packed), _tensor(k, packed), _tensor(v, packed), float(scale),
-                      int(bool(causal)), int(window), cu, pm, _tensor(out, packed), lse.data_ptr(),
+                      int(bool(causal)), int(window), float(softcap), cu, pm, _tensor(out, packed), lse.data_ptr(),
                       ws.data_ptr() if nbytes else None, nbytes, _stream())
     _check(st, "attn_fwd")
     return out, lse
@@ -225,7 +225,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              dout: torch.Tensor, scale: Optional[float] = None, causal: bool = True, window: int = 0,
              cu_seqlens: Optional[torch.Tensor] = None, pad_mask: Optional[torch.Tensor] = None,
              max_seqlen: Optional[int] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             dv: Optional[torch.Tensor] = None, softcap: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV of sum(O * dO), from attn_fwd's O and LSE."""
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
@@ -244,7 +244,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     ws = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
     st = lib.attn_bwd(ctypes.byref(shape), _tensor(q, packed), _tensor(k, packed), _tensor(v, packed),
                       _tensor(o, packed), lse.data_ptr(), _tensor(dout, packed), float(scale), int(bool(causal)),
-                      int(window), cu, pm, _tensor(dq, packed), _tensor(dk, packed), _tensor(dv, packed),
+                      int(window), float(softcap), cu, pm, _tensor(dq, packed), _tensor(dk, packed), _tensor(dv, packed),
                       ws.data_ptr() if nbytes else None, nbytes, _stream())
     _check(st, "attn_bwd")
     return dq, dk, dv
@@ -275,7 +275,7 @@ def _check_chunk_shapes(shape, q, k, v, lse=None, o=None, **grads) -> None:
 def attn_fwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos0: int, k_pos0: int,
                    scale: Optional[float] = None, causal: bool = True, window: int = 0,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   out_dtype: torch.dtype = torch.float32) -> Tuple[torch.Tensor, torch.Tensor]:
+                   out_dtype: torch.dtype = torch.float32, softcap: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Partial O, LSE of a query chunk q (B,Sq,Hq,D) at positions q_pos0.. against one key/value chunk
     k/v (B,Sk,Hkv,D) at positions k_pos0..; rows that see no key get O = 0, LSE = -inf.  O is fp32
     (a partial for attn_lse_merge) unless out_dtype is bfloat16."""
@@ -293,7 +293,7 @@ def attn_fwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos0: in
         lse = torch.empty((shape.B, shape.Hq, shape.Sq), device=q.device, dtype=torch.float32)
     _check_chunk_shapes(shape, q, k, v, lse=lse, o=out)
     st = lib.attn_fwd_chunk(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
-                            float(scale), int(bool(causal)), int(window), int(q_pos0), int(k_pos0),
+                            float(scale), int(bool(causal)), int(window), float(softcap), int(q_pos0), int(k_pos0),
                             _tensor(out, False), 1 if out.dtype == torch.float32 else 0, lse.data_ptr(), _stream())
     _check(st, "attn_fwd_chunk")
     return out, lse
@@ -311,8 +311,8 @@ def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
                    dout: torch.Tensor, q_pos0: int, k_pos0: int, scale: Optional[float] = None,
                    causal: bool = True, window: int = 0, dq: Optional[torch.Tensor] = None,
                    dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-                   accumulate: bool = False,
-                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+                   accumulate: bool = False, workspace: Optional[torch.Tensor] = None,
+                   softcap: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Gradient parts dQ (B,Sq,Hq,D), dK, dV (B,Sk,Hkv,D) of one chunk pair, from the rows' final O and
     LSE (merged over all their key chunks) and dO.  accumulate=False writes the parts in bf16 (new
     tensors unless given); accumulate=True adds them to the given fp32 dq, dk, dv."""
@@ -343,7 +343,7 @@ def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
         workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
     st = lib.attn_bwd_chunk(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
                             _tensor(o, False), lse.data_ptr(), _tensor(dout, False), float(scale), c, w,
-                            int(q_pos0), int(k_pos0), _tensor(dq, False), _tensor(dk, False), _tensor(dv, False),
+                            float(softcap), int(q_pos0), int(k_pos0), _tensor(dq, False), _tensor(dk, False), _tensor(dv, False),
                             1 if accumulate else 0, workspace.data_ptr() if nbytes else None, nbytes, _stream())
     _check(st, "attn_bwd_chunk")
     return dq, dk, dv

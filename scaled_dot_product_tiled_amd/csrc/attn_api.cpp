@@ -115,6 +115,7 @@ struct Call {
   int causal, window;  // window normalised (see normalise_offsets)
   int shift;           // query position offset of the chunk pair; 0 for whole sequences
   int empty_lse_ninf;  // chunk pairs: a row with no visible key has LSE = -inf
+  float softcap;       // tanh cap of the scaled scores; 0: none
 };
 
 // Visibility of (query i, key j) depends only on d = i + delta - j, the distance of their
@@ -163,6 +164,9 @@ void fill_common(attn::AttnArgs& a, const Call& c, float scale, const int32_t* m
   a.window = c.window;
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
+  a.softcap = c.softcap;
+  a.sc_in = c.softcap > 0.f ? scale / c.softcap : 0.f;
+  a.sc_out = c.softcap > 0.f ? c.softcap / scale : 0.f;
   a.seq_off = c.varlen ? meta : nullptr;
   a.seq_len = c.varlen ? meta + c.B : nullptr;
   a.balanced = c.varlen != 0;  // sequences of different lengths: deal work items in rounds
@@ -412,6 +416,14 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
 
 bool lse_ok(const float* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// softcap: 0 (none) or a finite positive cap
+bool softcap_ok(float x) { return std::isfinite(x) && x >= 0.f; }
+
+Call with_softcap(Call c, float softcap) {
+  c.softcap = softcap;
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -428,12 +440,13 @@ size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen) {
 }
 
 attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, float scale, int causal,
-                     int window, const int32_t* cu_seqlens, const uint8_t* pad_mask, attn_tensor o, float* lse,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int window, float softcap, const int32_t* cu_seqlens, const uint8_t* pad_mask, attn_tensor o,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   const int varlen = varlen_kind(cu_seqlens, pad_mask);
   attn_status st = check_common(shape, scale, causal, window, cu_seqlens, pad_mask, workspace_bytes,
                                 shape ? attn_fwd_workspace_bytes(shape, varlen) : 0, workspace);
   if (st != ATTN_OK) return st;
+  if (!softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
   const bool packed = varlen == 2;
   if ((st = check_tensor(q, packed)) || (st = check_tensor(k, packed)) || (st = check_tensor(v, packed)) ||
       (st = check_tensor(o, packed)))
@@ -441,18 +454,19 @@ attn_status attn_fwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
   if (shape->B == 0 || shape->S == 0 || (packed && shape->total == 0)) return ATTN_OK;
   const Tensors t = {q, k, v, o, {}, {}, {}, {}};
-  return run_fwd(whole_call(shape, varlen, causal, window), t, scale, lse, cu_seqlens, pad_mask, workspace,
-                 static_cast<hipStream_t>(stream));
+  return run_fwd(with_softcap(whole_call(shape, varlen, causal, window), softcap), t, scale, lse, cu_seqlens,
+                 pad_mask, workspace, static_cast<hipStream_t>(stream));
 }
 
 attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
-                     const float* lse, attn_tensor dout, float scale, int causal, int window,
+                     const float* lse, attn_tensor dout, float scale, int causal, int window, float softcap,
                      const int32_t* cu_seqlens, const uint8_t* pad_mask, attn_tensor dq, attn_tensor dk,
                      attn_tensor dv, void* workspace, size_t workspace_bytes, void* stream) {
   const int varlen = varlen_kind(cu_seqlens, pad_mask);
   attn_status st = check_common(shape, scale, causal, window, cu_seqlens, pad_mask, workspace_bytes,
                                 shape ? attn_bwd_workspace_bytes(shape, varlen, causal, window) : 0, workspace);
   if (st != ATTN_OK) return st;
+  if (!softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
   const bool packed = varlen == 2;
   if ((st = check_tensor(q, packed)) || (st = check_tensor(k, packed)) || (st = check_tensor(v, packed)) ||
       (st = check_tensor(o, packed)) || (st = check_tensor(dout, packed)) || (st = check_tensor(dq, packed)) ||
@@ -461,8 +475,8 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
   if (shape->B == 0 || shape->S == 0 || (packed && shape->total == 0)) return ATTN_OK;
   const Tensors t = {q, k, v, o, dout, dq, dk, dv};
-  return run_bwd(whole_call(shape, varlen, causal, window), t, scale, lse, cu_seqlens, pad_mask, workspace,
-                 static_cast<hipStream_t>(stream));
+  return run_bwd(with_softcap(whole_call(shape, varlen, causal, window), softcap), t, scale, lse, cu_seqlens,
+                 pad_mask, workspace, static_cast<hipStream_t>(stream));
 }
 
 size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal, int window, int64_t q_pos0,
@@ -472,11 +486,11 @@ size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal,
 }
 
 attn_status attn_fwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, float scale,
-                           int causal, int window, int64_t q_pos0, int64_t k_pos0, attn_tensor o, int o_dtype,
-                           float* lse, void* stream) {
+                           int causal, int window, float softcap, int64_t q_pos0, int64_t k_pos0, attn_tensor o,
+                           int o_dtype, float* lse, void* stream) {
   attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
   if (st != ATTN_OK) return st;
-  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
   if (o_dtype != ATTN_DTYPE_BF16 && o_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
   if ((st = check_tensor(q, false)) || (st = check_tensor(k, false)) || (st = check_tensor(v, false)) ||
       (st = check_tensor(o, false)))
@@ -484,17 +498,17 @@ attn_status attn_fwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
   if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
   if (shape->B == 0 || shape->Sq == 0) return ATTN_OK;
   const Tensors t = {q, k, v, o, {}, {}, {}, {}};
-  return run_fwd(chunk_call(shape, causal, window, q_pos0, k_pos0), t, scale, lse, nullptr, nullptr, nullptr,
-                 static_cast<hipStream_t>(stream), o_dtype == ATTN_DTYPE_F32);
+  return run_fwd(with_softcap(chunk_call(shape, causal, window, q_pos0, k_pos0), softcap), t, scale, lse, nullptr,
+                 nullptr, nullptr, static_cast<hipStream_t>(stream), o_dtype == ATTN_DTYPE_F32);
 }
 
 attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
-                           const float* lse, attn_tensor dout, float scale, int causal, int window, int64_t q_pos0,
-                           int64_t k_pos0, attn_tensor dq, attn_tensor dk, attn_tensor dv, int grad_dtype,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           const float* lse, attn_tensor dout, float scale, int causal, int window, float softcap,
+                           int64_t q_pos0, int64_t k_pos0, attn_tensor dq, attn_tensor dk, attn_tensor dv,
+                           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
   if (st != ATTN_OK) return st;
-  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
   if (grad_dtype != ATTN_DTYPE_BF16 && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0, k_pos0);
   if (need > 0 &&
@@ -507,8 +521,8 @@ attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
   if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
   if (shape->B == 0 || (shape->Sq == 0 && shape->Sk == 0)) return ATTN_OK;
   const Tensors t = {q, k, v, o, dout, dq, dk, dv};
-  return run_bwd(chunk_call(shape, causal, window, q_pos0, k_pos0), t, scale, lse, nullptr, nullptr, workspace,
-                 static_cast<hipStream_t>(stream), grad_dtype == ATTN_DTYPE_F32);
+  return run_bwd(with_softcap(chunk_call(shape, causal, window, q_pos0, k_pos0), softcap), t, scale, lse, nullptr,
+                 nullptr, workspace, static_cast<hipStream_t>(stream), grad_dtype == ATTN_DTYPE_F32);
 }
 
 attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D, attn_tensor o, float* lse,

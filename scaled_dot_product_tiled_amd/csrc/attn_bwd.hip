@@ -89,7 +89,7 @@ __device__ __forceinline__ void dma_stats(float* dst, const float* lse_row0, con
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NK = kDkdvKeys;   // 64 keys per workgroup
   constexpr int MQ = kDkdvRows;   // 32 query rows per step
@@ -267,12 +267,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         const bool full = (i0 + MQ <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= i0 + dlt) &&
                           (a.window <= 0 || j0 > i0 + MQ - 1 + dlt - a.window);
         bf16x8 pb, db;
+        // under a softcap the score is capped before the exponential and dS takes the cap's
+        // derivative 1 - tanh^2 (the stored dS is then the gradient of the uncapped score)
+        auto capped = [&](float x, float& der) {
+          if constexpr (SOFTCAP) {
+            const float t = tanh_from_exp(x * a.sc_in);
+            der = 1.0f - t * t;
+            return a.sc_out * t;
+          } else {
+            der = 1.0f;
+            return x;
+          }
+        };
         if (full) {
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            const float p = fast_exp2(fmaf(sv[r >> 2][r & 3], c, -lse4[r >> 2][r & 3]));
+            float der;
+            const float sx = capped(sv[r >> 2][r & 3], der);
+            const float p = fast_exp2(fmaf(sx, c, -lse4[r >> 2][r & 3]));
             pb[r] = (bf16)p;
-            db[r] = (bf16)(p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]));
+            db[r] = (bf16)(p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) * der);
           }
         } else {
           // this lane's key is visible from query rows rlo .. rhi-1
@@ -284,9 +298,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           for (int r = 0; r < 8; ++r) {
             const int row = i0 + 8 * (xh + (r >> 2)) + 4 * g2 + (r & 3);
             const bool vis = (row >= rlo) & (row < rhi);
-            const float e = fast_exp2(fmaf(sv[r >> 2][r & 3], c, -lse4[r >> 2][r & 3]));
+            float der;
+            const float sx = capped(sv[r >> 2][r & 3], der);
+            const float e = fast_exp2(fmaf(sx, c, -lse4[r >> 2][r & 3]));
             const float p = vis ? e : 0.f;
-            const float ds = vis ? p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) : 0.f;  // +0 when masked
+            const float ds = vis ? p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) * der : 0.f;  // +0 when masked
             pb[r] = (bf16)p;
             db[r] = (bf16)ds;
           }
@@ -449,10 +465,15 @@ hipError_t launch_bwd_kv_reduce(const AttnArgs& a, int D, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
   const dim3 grid(8 * a.per_xcd), block(256);
-  if (D == 512)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<512>, grid, block, 0, stream, a);
+  const bool sc = a.softcap > 0.f;
+  if (D == 512 && !sc)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<512, false>), grid, block, 0, stream, a);
+  else if (D == 512)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<512, true>), grid, block, 0, stream, a);
+  else if (D == 256 && !sc)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<256, false>), grid, block, 0, stream, a);
   else if (D == 256)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<256>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<256, true>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -42,7 +42,7 @@ namespace attn {
 
 constexpr float kRefSlack = 32.0f;
 
-template <int D, int N, bool EXACT>
+template <int D, int N, bool EXACT, bool SOFTCAP>
 // At head_dim 256 a wave fits in 256 registers, so two workgroups share a compute unit and
 // one's softmax and barriers overlap the other's matrix work; at 512 the accumulators alone
 // take 256 registers.
@@ -150,6 +150,13 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
       barrier_lds();  // every wave is done with Ks
       if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
 
+      if constexpr (SOFTCAP) {
+        // the cap applies to every score before the mask (masked entries become -inf below)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = a.sc_out * tanh_from_exp(sacc[kb][r] * a.sc_in);
+      }
       const bool need_mask = (j0 + N > lenk) || (p0 + a.mpos > len) || (a.causal && j0 + N - 1 > p0 + dlt) ||
                              (a.window > 0 && j0 <= plast + dlt - a.window);
       if (need_mask) {
@@ -265,10 +272,15 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
 
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream) {
   const dim3 grid(8 * a.per_xcd), block(256);
-  if (D == 512)
-    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false>), grid, block, 0, stream, a);
+  const bool sc = a.softcap > 0.f;
+  if (D == 512 && !sc)
+    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, false>), grid, block, 0, stream, a);
+  else if (D == 512)
+    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, true>), grid, block, 0, stream, a);
+  else if (D == 256 && !sc)
+    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, false>), grid, block, 0, stream, a);
   else if (D == 256)
-    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, true>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

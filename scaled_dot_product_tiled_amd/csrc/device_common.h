@@ -43,6 +43,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// tanh(x).  For |x| >= 1/8 from the exponential, tanh(x) = sign(x) (1 - 2 / (e^(2|x|) + 1))
+// with e^(2|x|) = 2^(2 log2(e) |x|) (for large |x| the exponential overflows to inf and the
+// result is +-1 exactly).  Below 1/8 that difference would cancel to a few ulps of 1, so the
+// Taylor series x (1 - x^2/3 + 2x^4/15 - 17x^6/315) is used instead (next term 62x^9/2835:
+// relative error below 2e-9).
+__device__ __forceinline__ float tanh_from_exp(float x) {
+  const float ax = fabsf(x);
+  const float e = fast_exp2(2.8853900817779268f * ax);
+  const float big = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  const float x2 = ax * ax;
+  const float small = ax * fmaf(x2, fmaf(x2, fmaf(x2, -0.053968253968253971f, 0.13333333333333333f),
+                                         -0.33333333333333333f), 1.0f);
+  return copysignf(ax < 0.125f ? small : big, x);
+}
+
 // Value of this lane's partner in the other half of the wave (lane ^ 32), combined.
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

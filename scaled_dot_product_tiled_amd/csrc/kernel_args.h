@@ -59,7 +59,11 @@ struct AttnArgs {
   float* kv_part;           // kv_split > 1: fp32 partial dK, dV, [part][dK|dV][B][Sk][Hkv][D]
   int packed;               // rows past a sequence's length do not exist
   int causal, window;
-  float scale;              // multiplies Q K^T
+  float scale;
+  // tanh softcap of the scaled scores s -> cap tanh(s / cap) (cap = softcap > 0), applied to
+  // raw scores x (s = scale x) as x -> sc_out tanh(sc_in x) with sc_in = scale / cap and
+  // sc_out = cap / scale, so the rest of the arithmetic is unchanged
+  float softcap, sc_in, sc_out;              // multiplies Q K^T
   float c;                  // scale * log2(e)
   int per_xcd, total_items;
   int balanced;             // deal work items in rounds (see xcd_item)

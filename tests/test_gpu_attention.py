@@ -29,10 +29,10 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w: AttnWorkload, inp: dict, varlen=None, want_bwd=True):
+def run_gpu(w: AttnWorkload, inp: dict, varlen=None, want_bwd=True, softcap=0.0):
     """Runs attn_fwd (+ attn_bwd) on the workload's inputs; returns device tensors."""
     q, k, v, do = (dev(inp[x]) for x in ("q", "k", "v", "do"))
-    kw = dict(scale=w.scale, causal=w.causal, window=w.window)
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, softcap=softcap)
     if varlen == "pad_mask":
         kw["pad_mask"] = torch.from_numpy(inp["pad_mask"]).to("cuda:0")
     o, lse = sdpt.attn_fwd(q, k, v, **kw)
@@ -43,10 +43,10 @@ def run_gpu(w: AttnWorkload, inp: dict, varlen=None, want_bwd=True):
     return out
 
 
-def oracle_full(w, inp, lengths=None):
+def oracle_full(w, inp, lengths=None, softcap=0.0):
     q, k, v, do = (bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
-    o, lse = oracle.attention_forward(q, k, v, w.scale, w.causal, w.window, lengths)
-    dq, dk, dv = oracle.attention_backward(q, k, v, do, w.scale, w.causal, w.window, lengths)
+    o, lse = oracle.attention_forward(q, k, v, w.scale, w.causal, w.window, lengths, softcap)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, w.scale, w.causal, w.window, lengths, softcap)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
@@ -99,6 +99,42 @@ def test_small_cases_match_oracle(name, w, lengths):
     got = run_gpu(w, inp, varlen=w.varlen)
     ref = oracle_full(w, inp, inp["lengths"] if lengths is not None else None)
     check_full(w, got, ref, lengths)
+
+
+SOFTCAP = [
+    # name, workload, lengths, cap (scaled scores of the std-3 draws reach ~9 at head_dim 256, so
+    # the caps bend them strongly)
+    ("d512_gqa_cap", AttnWorkload(120, "d512 gqa softcap", 2, 300, 16, 2, 512, qk_std=2.0), None, 3.0),
+    ("d256_window_cap", AttnWorkload(121, "d256 window softcap", 2, 700, 4, 2, 256, window=200, qk_std=3.0), None,
+     5.0),
+    ("d512_varlen_cap", AttnWorkload(122, "d512 varlen softcap", 3, 333, 8, 2, 512, varlen="pad_mask"),
+     [333, 1, 150], 1.5),
+    ("d512_noncausal_cap", AttnWorkload(123, "d512 non-causal softcap", 1, 257, 4, 1, 512, causal=False,
+                                        qk_std=2.0), None, 2.0),
+]
+
+
+@pytest.mark.parametrize("name,w,lengths,cap", SOFTCAP, ids=[c[0] for c in SOFTCAP])
+def test_softcap_matches_oracle(name, w, lengths, cap):
+    say(f"[softcap {name}] B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} W={w.window} cap={cap}")
+    inp = make_attention_inputs(w, seed=0)
+    if lengths is not None:
+        inp["lengths"] = np.array(lengths, dtype=np.int32)
+        inp["pad_mask"] = lengths_to_pad_mask(inp["lengths"], w.S)
+    got = run_gpu(w, inp, varlen=w.varlen, softcap=cap)
+    ref = oracle_full(w, inp, inp["lengths"] if lengths is not None else None, softcap=cap)
+    check_full(w, got, ref, lengths)
+
+
+def test_huge_softcap_is_no_cap():
+    """A cap far above every score leaves the result within rounding of the uncapped one."""
+    w = AttnWorkload(124, "huge cap", 1, 300, 8, 2, 512)
+    inp = make_attention_inputs(w, seed=3)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp, softcap=1e6)
+    assert max_abs(host(a["o"]), host(b["o"])) <= 1e-2
+    for x in ("dq", "dk", "dv"):
+        assert rel_l2(host(b[x]), host(a[x])) <= 1e-2, x
 
 
 def test_packed_cu_seqlens_matches_oracle_and_pad_mask():

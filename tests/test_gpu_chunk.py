@@ -31,7 +31,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def ring_forward(q, k, v, bounds, scale, causal, window):
+def ring_forward(q, k, v, bounds, scale, causal, window, softcap=0.0):
     """Partials (fp32 O) of every (query chunk, key chunk) pair, and per query chunk their merge:
     the bf16 O written by the last merge and the merged LSE."""
     parts, merged = {}, []
@@ -43,7 +43,7 @@ def ring_forward(q, k, v, bounds, scale, causal, window):
         for c in range(n):
             k0, k1 = bounds[c], bounds[c + 1]
             o, lse = sdpt.attn_fwd_chunk(q[:, q0:q1], k[:, k0:k1], v[:, k0:k1], q0, k0, scale=scale, causal=causal,
-                                         window=window)
+                                         window=window, softcap=softcap)
             parts[a, c] = (o.clone(), lse.clone())
             if acc_o is None:
                 acc_o, acc_l = o, lse
@@ -54,7 +54,7 @@ def ring_forward(q, k, v, bounds, scale, causal, window):
     return parts, merged
 
 
-def ring_backward(q, k, v, do, merged, bounds, scale, causal, window):
+def ring_backward(q, k, v, do, merged, bounds, scale, causal, window, softcap=0.0):
     """Per query chunk and key chunk: the pair's gradient parts written in bf16, and the same
     parts added by the kernels into fp32 accumulators dQ, dK, dV (the ring's running sums)."""
     dq = torch.zeros(q.shape, device=q.device, dtype=torch.float32)
@@ -67,7 +67,7 @@ def ring_backward(q, k, v, do, merged, bounds, scale, causal, window):
         for c in range(len(bounds) - 1):
             k0, k1 = bounds[c], bounds[c + 1]
             args = (q[:, q0:q1], k[:, k0:k1], v[:, k0:k1], o, lse, do[:, q0:q1], q0, k0)
-            kw = dict(scale=scale, causal=causal, window=window)
+            kw = dict(scale=scale, causal=causal, window=window, softcap=softcap)
             parts[a, c] = sdpt.attn_bwd_chunk(*args, **kw)
             sdpt.attn_bwd_chunk(*args, dq=dq[:, q0:q1], dk=dk[:, k0:k1], dv=dv[:, k0:k1], accumulate=True, **kw)
     torch.cuda.synchronize()
@@ -83,7 +83,7 @@ def check_grad_part(got, ref, name):
 
 
 RING = [
-    # name, workload, chunk bounds
+    # name, workload, chunk bounds[, softcap]
     ("d512_gqa_ragged", AttnWorkload(201, "ring d512 gqa", 2, 600, 8, 2, 512), [0, 256, 512, 600]),
     ("d512_unaligned", AttnWorkload(202, "ring d512 unaligned", 1, 500, 4, 1, 512), [0, 130, 390, 500]),
     ("d256_window", AttnWorkload(203, "ring d256 window 200", 2, 700, 4, 2, 256, window=200, qk_std=3.0),
@@ -91,23 +91,26 @@ RING = [
     ("d256_window_wide", AttnWorkload(204, "ring d256 window 500", 1, 900, 4, 1, 256, window=500, qk_std=3.0),
      [0, 200, 450, 700, 900]),
     ("d512_noncausal", AttnWorkload(205, "ring d512 non-causal", 1, 300, 4, 2, 512, causal=False), [0, 100, 300]),
+    ("d512_softcap", AttnWorkload(210, "ring d512 softcap", 1, 520, 8, 2, 512, qk_std=2.0), [0, 200, 520], 2.5),
 ]
 
 
-@pytest.mark.parametrize("name,w,bounds", RING, ids=[c[0] for c in RING])
-def test_ring_chunks_match_oracle(name, w, bounds):
+@pytest.mark.parametrize("case", RING, ids=[c[0] for c in RING])
+def test_ring_chunks_match_oracle(case):
+    name, w, bounds = case[:3]
+    cap = case[3] if len(case) > 3 else 0.0
     say(f"[ring {name}] B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} causal={w.causal} W={w.window} "
-        f"chunks={bounds}")
+        f"chunks={bounds} cap={cap}")
     inp = make_attention_inputs(w, seed=0)
     q, k, v, do = (dev(inp[x]) for x in ("q", "k", "v", "do"))
     f = {x: bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do")}
-    parts, merged = ring_forward(q, k, v, bounds, w.scale, w.causal, w.window)
+    parts, merged = ring_forward(q, k, v, bounds, w.scale, w.causal, w.window, cap)
 
     # pair partials against the oracle's chunk forward
     for (a, c), (o, lse) in parts.items():
         q0, q1, k0, k1 = bounds[a], bounds[a + 1], bounds[c], bounds[c + 1]
         ro, rl = oracle.attention_forward_chunk(f["q"][:, q0:q1], f["k"][:, k0:k1], f["v"][:, k0:k1], w.scale,
-                                                w.causal, w.window, q0, k0)
+                                                w.causal, w.window, q0, k0, cap)
         go, gl = host(o), host(lse)
         live = np.isfinite(rl)                               # (B, Hq, Sq)
         assert np.array_equal(np.isfinite(gl), live), (a, c)
@@ -120,7 +123,7 @@ def test_ring_chunks_match_oracle(name, w, bounds):
             assert max_abs(go[lrow], ro[lrow]) <= O_MAX_ABS, (a, c)
 
     # merged partials against the whole-sequence oracle
-    ro, rl = oracle.attention_forward(f["q"], f["k"], f["v"], w.scale, w.causal, w.window)
+    ro, rl = oracle.attention_forward(f["q"], f["k"], f["v"], w.scale, w.causal, w.window, None, cap)
     for a, (o, lse) in enumerate(merged):
         q0, q1 = bounds[a], bounds[a + 1]
         assert all_finite(o, lse)
@@ -129,17 +132,17 @@ def test_ring_chunks_match_oracle(name, w, bounds):
 
     # gradients: parts against the oracle's chunk backward, the kernels' fp32 sums against the
     # whole backward
-    gparts, (dq, dk, dv) = ring_backward(q, k, v, do, merged, bounds, w.scale, w.causal, w.window)
+    gparts, (dq, dk, dv) = ring_backward(q, k, v, do, merged, bounds, w.scale, w.causal, w.window, cap)
     for (a, c), (gq, gk, gv) in gparts.items():
         q0, q1, k0, k1 = bounds[a], bounds[a + 1], bounds[c], bounds[c + 1]
         rq, rk, rv = oracle.attention_backward_chunk(f["q"][:, q0:q1], f["k"][:, k0:k1], f["v"][:, k0:k1],
                                                      ro[:, q0:q1], rl[:, :, q0:q1], f["do"][:, q0:q1], w.scale,
-                                                     w.causal, w.window, q0, k0)
+                                                     w.causal, w.window, q0, k0, cap)
         assert all_finite(gq, gk, gv)
         check_grad_part(gq, rq, f"dq{a}{c}")
         check_grad_part(gk, rk, f"dk{a}{c}")
         check_grad_part(gv, rv, f"dv{a}{c}")
-    rq, rk, rv = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], w.scale, w.causal, w.window)
+    rq, rk, rv = oracle.attention_backward(f["q"], f["k"], f["v"], f["do"], w.scale, w.causal, w.window, None, cap)
     for name_, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         err = rel_l2(host(got), ref)
         assert err <= GRAD_REL_L2, (name_, err)

@@ -64,10 +64,11 @@ def _t(ptr=0x10000, sb=4096 * 32 * 512, ss=32 * 512, sh=512):
     return AttnTensor(ptr, sb, ss, sh)
 
 
-def _fwd(lib, shape, q=None, scale=0.05, causal=1, window=0, cu=None, pm=None, lse=0x20000, ws=None, wsb=0):
+def _fwd(lib, shape, q=None, scale=0.05, causal=1, window=0, cu=None, pm=None, lse=0x20000, ws=None, wsb=0,
+         softcap=0.0):
     q = q or _t()
     return lib.attn_fwd(ctypes.byref(shape) if shape is not None else None, q, _t(), _t(), scale, causal, window,
-                        cu, pm, _t(), lse, ws, wsb, None)
+                        softcap, cu, pm, _t(), lse, ws, wsb, None)
 
 
 def test_argument_checks_happen_before_any_launch():
@@ -82,6 +83,9 @@ def test_argument_checks_happen_before_any_launch():
     assert _fwd(lib, s, scale=float("nan")) == INVALID
     assert _fwd(lib, s, causal=0, window=16) == UNSUPPORTED       # window requires causal
     assert _fwd(lib, s, window=-1) == INVALID
+    assert _fwd(lib, s, softcap=-1.0) == INVALID                   # softcap: 0 (none) or a positive cap
+    assert _fwd(lib, s, softcap=float("inf")) == INVALID
+    assert _fwd(lib, s, softcap=float("nan")) == INVALID
     assert _fwd(lib, AttnShape(2, 64, 0, 8, 2, 128)) == UNSUPPORTED   # head_dim 128 is decode-only
     assert _fwd(lib, AttnShape(2, 64, 0, 8, 3, 512)) == INVALID       # Hq % Hkv
     assert _fwd(lib, s, cu=0x30000, pm=0x40000) == INVALID            # both varlen forms
@@ -94,10 +98,10 @@ def test_argument_checks_happen_before_any_launch():
 def test_backward_and_decode_checks():
     lib = load_library()
     s = AttnShape(2, 64, 0, 8, 2, 512)
-    st = lib.attn_bwd(ctypes.byref(s), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, None, None,
+    st = lib.attn_bwd(ctypes.byref(s), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, 0.0, None, None,
                       _t(), _t(), _t(), None, 0, None)
     assert st == WORKSPACE
-    st = lib.attn_bwd(ctypes.byref(s), _t(), _t(), _t(), _t(), 0x20000, _t(ptr=0), 0.05, 1, 0, None, None,
+    st = lib.attn_bwd(ctypes.byref(s), _t(), _t(), _t(), _t(), 0x20000, _t(ptr=0), 0.05, 1, 0, 0.0, None, None,
                       _t(), _t(), _t(), 0x100000, 1 << 24, None)
     assert st == INVALID
     d = AttnDecodeShape(4, 32, 8, 128, 16, 100, 8)
@@ -146,20 +150,21 @@ def test_chunk_and_merge_checks():
     lib = load_library()
     c = AttnChunkShape(2, 64, 96, 8, 2, 512)
 
-    def fwd(shape=c, causal=1, window=0, qp=0, kp=0, lse=0x20000, q=None, odt=1):
-        return lib.attn_fwd_chunk(ctypes.byref(shape), q or _t(), _t(), _t(), 0.05, causal, window, qp, kp, _t(),
-                                  odt, lse, None)
+    def fwd(shape=c, causal=1, window=0, qp=0, kp=0, lse=0x20000, q=None, odt=1, cap=0.0):
+        return lib.attn_fwd_chunk(ctypes.byref(shape), q or _t(), _t(), _t(), 0.05, causal, window, cap, qp, kp,
+                                  _t(), odt, lse, None)
     assert fwd(causal=0, window=8) == UNSUPPORTED
     assert fwd(qp=-5) == INVALID
     assert fwd(lse=0) == INVALID
     assert fwd(q=_t(ptr=0x10008)) == INVALID
     assert fwd(shape=AttnChunkShape(2, 64, 96, 8, 3, 512)) == INVALID
     assert fwd(odt=2) == INVALID                                        # O is bf16 or fp32
+    assert fwd(cap=-2.0) == INVALID
     assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512)) == OK       # empty batch
     assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512), odt=0) == OK
     assert fwd(shape=AttnChunkShape(2, 0, 96, 8, 2, 512)) == OK        # no query rows
     def bwd(gdt=0, ws=None, wsb=0):
-        return lib.attn_bwd_chunk(ctypes.byref(c), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, 64, 0,
+        return lib.attn_bwd_chunk(ctypes.byref(c), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, 0.0, 64, 0,
                                   _t(), _t(), _t(), gdt, ws, wsb, None)
     assert bwd() == WORKSPACE
     assert bwd(gdt=1) == WORKSPACE

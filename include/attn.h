@@ -48,8 +48,10 @@ typedef enum {
     ATTN_ERR_HIP = 4           /* a HIP runtime call failed; see attn_last_hip_error() */
 } attn_status;
 
-/* Element type of an output that can be kept in either precision. */
-enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_F32 = 1 };
+/* Element types.  Attention tensors (Q, K, V, O, dO, dQ, dK, dV, caches) are 16-bit:
+ * bfloat16 or IEEE half, both admitted by the first page's gate (section Integration);
+ * some outputs can also be kept in fp32. */
+enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_F32 = 1, ATTN_DTYPE_F16 = 2 };
 
 /* A bf16 tensor: device pointer plus element strides of the batch, sequence and
  * head dimensions (the head_dim dimension is contiguous).  For packed
@@ -67,9 +69,11 @@ typedef struct {
  *          the longest sequence for cu_seqlens inputs
  *   total  packed row count (cu_seqlens[B]); only read with cu_seqlens
  *   Hq     query heads; Hkv key/value heads; Hq % Hkv == 0
- *   D      head_dim: 256 or 512 */
+ *   D      head_dim: 256 or 512
+ *   dtype  element type of every tensor of the call: ATTN_DTYPE_BF16 or
+ *          ATTN_DTYPE_F16 (products accumulate in fp32 either way) */
 typedef struct {
-    int32_t B, S, total, Hq, Hkv, D;
+    int32_t B, S, total, Hq, Hkv, D, dtype;
 } attn_shape;
 
 /*
@@ -134,9 +138,9 @@ attn_status attn_bwd(const attn_shape* shape,
  *   B       batch
  *   Sq      query rows of the query chunk; Sk key/value rows of the key/value chunk
  *           (each below 2^28)
- *   Hq, Hkv, D as in attn_shape */
+ *   Hq, Hkv, D, dtype as in attn_shape */
 typedef struct {
-    int32_t B, Sq, Sk, Hq, Hkv, D;
+    int32_t B, Sq, Sk, Hq, Hkv, D, dtype;
 } attn_chunk_shape;
 
 /*
@@ -151,8 +155,8 @@ typedef struct {
  * (causal) and k_pos > q_pos - window (window > 0, requires causal).
  *   q      dense bf16 (B, Sq, Hq, D); k, v dense bf16 (B, Sk, Hkv, D)
  *   o      (B, Sq, Hq, D), written, element type o_dtype: ATTN_DTYPE_F32 for a partial
- *          that attn_lse_merge will combine (the row is then rounded to bf16 once, at
- *          the last merge), ATTN_DTYPE_BF16 for a pair that is the row's only one
+ *          that attn_lse_merge will combine (the row is then rounded to 16 bits once,
+ *          at the last merge), or the inputs' dtype for a pair that is the row's only one
  *   lse    device fp32 (B, Hq, Sq) contiguous, written: natural-log log-sum-exp of the
  *          row's scaled visible scores in this chunk, or -inf for a row that sees no
  *          key of the chunk (its O is 0); -inf is the identity of attn_lse_merge
@@ -178,7 +182,7 @@ attn_status attn_fwd_chunk(const attn_chunk_shape* shape,
  *   grad_dtype  ATTN_DTYPE_F32: dq, dk, dv are fp32 accumulators (zeroed by the caller
  *               before a chunk's first pair) and the pair's parts are added to them, so a
  *               ring step needs no separate sum; a pair with no visible (query, key) pair
- *               launches nothing.  ATTN_DTYPE_BF16: the parts are written in bf16, not
+ *               launches nothing.  The inputs' dtype: the parts are written in it, not
  *               accumulated; a row that sees no key of the pair gets dq = 0 and a key that
  *               no row of the pair sees gets dk = dv = 0.
  *   workspace  at least attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0,
@@ -203,15 +207,15 @@ attn_status attn_bwd_chunk(const attn_chunk_shape* shape,
  *                   multiples of 8, 16-byte aligned); o is updated; the two must not
  *                   overlap
  *   lse, lse_part   device fp32 (B, H, S) contiguous; lse is updated
- *   out             bf16 (B, S, H, D): if out.ptr is not NULL, the merged o rounded to
- *                   bf16 (round to nearest even) is also written there, for the last
- *                   merge of a row
+ *   out             (B, S, H, D) of type out_dtype (ATTN_DTYPE_BF16 or ATTN_DTYPE_F16):
+ *                   if out.ptr is not NULL, the merged o rounded to it (round to nearest
+ *                   even) is also written there, for the last merge of a row
  *   D               128, 256 or 512
  */
 attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D,
                            attn_tensor o, float* lse,
                            attn_tensor o_part, const float* lse_part,
-                           attn_tensor out, void* stream);
+                           attn_tensor out, int out_dtype, void* stream);
 
 /* Sizes of one paged decode call.
  *   B                 sequences, one query token each
@@ -221,6 +225,7 @@ attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D,
  *   max_pages_per_seq columns of block_table */
 typedef struct {
     int32_t B, Hq, Hkv, D, page_size, num_pages, max_pages_per_seq;
+    int32_t dtype;  /* q, caches and o: ATTN_DTYPE_BF16 or ATTN_DTYPE_F16 */
 } attn_decode_shape;
 
 /*

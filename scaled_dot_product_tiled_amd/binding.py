@@ -24,14 +24,19 @@ class AttnTensor(ctypes.Structure):
                 ("stride_h", ctypes.c_int64)]
 
 
+# element type codes of include/attn.h
+DTYPE_BF16, DTYPE_F32, DTYPE_F16 = 0, 1, 2
+_DT16 = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+
+
 class AttnShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("total", ctypes.c_int32), ("Hq", ctypes.c_int32),
-                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32)]
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class AttnChunkShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("Hq", ctypes.c_int32),
-                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32)]
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class AttnKernelTime(ctypes.Structure):
@@ -41,7 +46,7 @@ class AttnKernelTime(ctypes.Structure):
 class AttnDecodeShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("max_pages_per_seq", ctypes.c_int32)]
+                ("max_pages_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,7 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_chunk_workspace_bytes.argtypes = [P(AttnChunkShape), ctypes.c_int, ctypes.c_int, i64, i64]
     lib.attn_bwd_chunk_workspace_bytes.restype = sz
     lib.attn_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, AttnTensor, vp,
-                                   AttnTensor, vp, AttnTensor, vp]
+                                   AttnTensor, vp, AttnTensor, ctypes.c_int, vp]
     lib.attn_lse_merge.restype = ctypes.c_int
     lib.paged_decode.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int64, ctypes.c_int64, AttnTensor, AttnTensor,
                                  vp, vp, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz, vp]
@@ -114,9 +119,13 @@ def _check(status: int, what: str) -> None:
         raise RuntimeError(f"{what} failed: status {status} ({msg})" + (f", hip error {hip}" if status == 4 else ""))
 
 
-def _bf16(t: torch.Tensor, name: str) -> None:
-    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
-        raise TypeError(f"{name} must be a bfloat16 CUDA/HIP tensor")
+def _half(t: torch.Tensor, name: str, like: Optional[torch.dtype] = None) -> None:
+    """A 16-bit (bfloat16 or float16) device tensor with a contiguous last dimension, of the
+    same type as the call's other tensors (like)."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in _DT16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 or float16 CUDA/HIP tensor")
+    if like is not None and t.dtype != like:
+        raise TypeError(f"{name} is {t.dtype}, the call's tensors are {like}")
     if t.stride(-1) != 1:
         raise ValueError(f"{name}: the head_dim dimension must be contiguous")
 
@@ -143,9 +152,11 @@ def _check_attn_shapes(shape, packed, q, k, v, lse=None, o=None, **grads) -> Non
     for n, t in (("o", o), ("dout", grads.get("dout")), ("dq", grads.get("dq"))):
         if t is not None:
             _expect(t, qs, n)
+            _half(t, n, q.dtype)
     for n, t in (("dk", grads.get("dk")), ("dv", grads.get("dv"))):
         if t is not None:
             _expect(t, ks, n)
+            _half(t, n, q.dtype)
     if lse is not None:
         _expect(lse, ls, "lse")
         if lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -176,7 +187,7 @@ def _shape(q, k, cu_seqlens, pad_mask, max_seqlen):
     Hkv = k.shape[-2]
     if pad_mask is not None and tuple(pad_mask.shape) != (B, S):
         raise ValueError(f"pad_mask must be (B, S) = {(B, S)}, got {tuple(pad_mask.shape)}")
-    return AttnShape(B, S, T, Hq, Hkv, D), packed, (2 if packed else (1 if pad_mask is not None else 0))
+    return AttnShape(B, S, T, Hq, Hkv, D, _DT16[q.dtype]), packed, (2 if packed else (1 if pad_mask is not None else 0))
 
 
 def _meta_ptrs(cu_seqlens, pad_mask):
@@ -201,7 +212,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
     rows are packed: q (T,Hq,D), k/v (T,Hkv,D), LSE (Hq,T).  Returns (O, LSE fp32)."""
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _bf16(t, n)
+        _half(t, n, q.dtype)
     shape, packed, varlen = _shape(q, k, cu_seqlens, pad_mask, max_seqlen)
     if scale is None:
         scale = 1.0 / math.sqrt(shape.D)
@@ -229,7 +240,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     """dQ, dK, dV of sum(O * dO), from attn_fwd's O and LSE."""
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _bf16(t, n)
+        _half(t, n, q.dtype)
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise TypeError("lse must be a contiguous float32 tensor")
     shape, packed, varlen = _shape(q, k, cu_seqlens, pad_mask, max_seqlen)
@@ -252,7 +263,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 
 def _chunk_shape(q, k):
     B, Sq, Hq, D = q.shape
-    return AttnChunkShape(B, Sq, k.shape[1], Hq, k.shape[2], D)
+    return AttnChunkShape(B, Sq, k.shape[1], Hq, k.shape[2], D, _DT16[q.dtype])
 
 
 def _check_chunk_shapes(shape, q, k, v, lse=None, o=None, **grads) -> None:
@@ -278,23 +289,24 @@ def attn_fwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos0: in
                    out_dtype: torch.dtype = torch.float32, softcap: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Partial O, LSE of a query chunk q (B,Sq,Hq,D) at positions q_pos0.. against one key/value chunk
     k/v (B,Sk,Hkv,D) at positions k_pos0..; rows that see no key get O = 0, LSE = -inf.  O is fp32
-    (a partial for attn_lse_merge) unless out_dtype is bfloat16."""
+    (a partial for attn_lse_merge) unless out_dtype is the inputs' 16-bit type."""
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _bf16(t, n)
+        _half(t, n, q.dtype)
     shape = _chunk_shape(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(shape.D)
     if out is None:
         out = torch.empty(tuple(q.shape), device=q.device, dtype=out_dtype)
-    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(-1) != 1 or not out.is_cuda:
-        raise TypeError("out must be a float32 or bfloat16 device tensor with a contiguous last dimension")
+    if out.dtype not in (torch.float32, q.dtype) or out.stride(-1) != 1 or not out.is_cuda:
+        raise TypeError(f"out must be a float32 or {q.dtype} device tensor with a contiguous last dimension")
     if lse is None:
         lse = torch.empty((shape.B, shape.Hq, shape.Sq), device=q.device, dtype=torch.float32)
     _check_chunk_shapes(shape, q, k, v, lse=lse, o=out)
     st = lib.attn_fwd_chunk(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
                             float(scale), int(bool(causal)), int(window), float(softcap), int(q_pos0), int(k_pos0),
-                            _tensor(out, False), 1 if out.dtype == torch.float32 else 0, lse.data_ptr(), _stream())
+                            _tensor(out, False), DTYPE_F32 if out.dtype == torch.float32 else _DT16[out.dtype],
+                            lse.data_ptr(), _stream())
     _check(st, "attn_fwd_chunk")
     return out, lse
 
@@ -314,11 +326,11 @@ def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
                    accumulate: bool = False, workspace: Optional[torch.Tensor] = None,
                    softcap: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Gradient parts dQ (B,Sq,Hq,D), dK, dV (B,Sk,Hkv,D) of one chunk pair, from the rows' final O and
-    LSE (merged over all their key chunks) and dO.  accumulate=False writes the parts in bf16 (new
-    tensors unless given); accumulate=True adds them to the given fp32 dq, dk, dv."""
+    LSE (merged over all their key chunks) and dO.  accumulate=False writes the parts in the inputs'
+    16-bit type (new tensors unless given); accumulate=True adds them to the given fp32 dq, dk, dv."""
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _bf16(t, n)
+        _half(t, n, q.dtype)
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise TypeError("lse must be a contiguous float32 tensor")
     shape = _chunk_shape(q, k)
@@ -335,7 +347,7 @@ def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
         dk = torch.empty_like(k) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv
         for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-            _bf16(t, n)
+            _half(t, n, q.dtype)
     _check_chunk_shapes(shape, q, k, v, lse=lse, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
     c, w = int(bool(causal)), int(window)
     nbytes = lib.attn_bwd_chunk_workspace_bytes(ctypes.byref(shape), c, w, int(q_pos0), int(k_pos0))
@@ -344,7 +356,8 @@ def attn_bwd_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
     st = lib.attn_bwd_chunk(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
                             _tensor(o, False), lse.data_ptr(), _tensor(dout, False), float(scale), c, w,
                             float(softcap), int(q_pos0), int(k_pos0), _tensor(dq, False), _tensor(dk, False), _tensor(dv, False),
-                            1 if accumulate else 0, workspace.data_ptr() if nbytes else None, nbytes, _stream())
+                            DTYPE_F32 if accumulate else _DT16[q.dtype], workspace.data_ptr() if nbytes else None,
+                            nbytes, _stream())
     _check(st, "attn_bwd_chunk")
     return dq, dk, dv
 
@@ -365,11 +378,11 @@ def attn_lse_merge(o: torch.Tensor, lse: torch.Tensor, o_part: torch.Tensor, lse
     _expect(lse, (B, H, S), "lse")
     _expect(lse_part, (B, H, S), "lse_part")
     if out is not None:
-        _bf16(out, "out")
+        _half(out, "out")
         _expect(out, (B, S, H, D), "out")
     st = lib.attn_lse_merge(B, S, H, D, _tensor(o, False), lse.data_ptr(), _tensor(o_part, False),
                             lse_part.data_ptr(), _tensor(out, False) if out is not None else AttnTensor(None, 0, 0, 0),
-                            _stream())
+                            _DT16[out.dtype] if out is not None else DTYPE_BF16, _stream())
     _check(st, "attn_lse_merge")
 
 
@@ -379,13 +392,13 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     """O (B,Hq,D) of one query token per sequence against a paged cache (num_pages, page_size, Hkv, D)."""
     lib = load_library()
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _bf16(t, n)
+        _half(t, n, q.dtype)
     for t, n in ((block_table, "block_table"), (ctx_lens, "ctx_lens")):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise TypeError(f"{n} must be a contiguous int32 device tensor")
     B, Hq, D = q.shape
     num_pages, page_size, Hkv, _ = k_cache.shape
-    shape = AttnDecodeShape(B, Hq, Hkv, D, page_size, num_pages, block_table.shape[1])
+    shape = AttnDecodeShape(B, Hq, Hkv, D, page_size, num_pages, block_table.shape[1], _DT16[q.dtype])
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = torch.empty_like(q) if out is None else out

@@ -29,12 +29,16 @@ attn_status check_tensor(const attn_tensor& t, bool packed) {
   return ATTN_OK;
 }
 
+// 16-bit tensor types
+bool dtype16_ok(int dt) { return dt == ATTN_DTYPE_BF16 || dt == ATTN_DTYPE_F16; }
+
 // varlen: 0 dense, 1 pad_mask, 2 cu_seqlens
 attn_status check_shape(const attn_shape* s, int varlen) {
   if (s == nullptr) return ATTN_ERR_INVALID_ARG;
   if (s->B < 0 || s->S < 0 || s->Hq <= 0 || s->Hkv <= 0 || s->total < 0) return ATTN_ERR_INVALID_ARG;
   if (s->Hq % s->Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (s->D != 256 && s->D != 512) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype16_ok(s->dtype)) return ATTN_ERR_UNSUPPORTED;
   // every row index handled as a 32-bit int inside the kernels
   const int64_t rows = varlen == 2 ? (int64_t)s->total : (int64_t)s->B * s->S;
   if (rows * s->Hq >= INT_MAX / 2) return ATTN_ERR_UNSUPPORTED;
@@ -112,6 +116,7 @@ void plan_rows(attn::AttnArgs& a, int rows) {
 struct Call {
   int B, S, Sk, total, Hq, Hkv, D;
   int varlen;          // 0 dense, 1 pad_mask, 2 cu_seqlens
+  int f16;             // 16-bit tensors are IEEE half
   int causal, window;  // window normalised (see normalise_offsets)
   int shift;           // query position offset of the chunk pair; 0 for whole sequences
   int empty_lse_ninf;  // chunk pairs: a row with no visible key has LSE = -inf
@@ -160,6 +165,7 @@ void fill_common(attn::AttnArgs& a, const Call& c, float scale, const int32_t* m
   a.Hkv = c.Hkv;
   a.r = c.Hq / c.Hkv;
   a.packed = c.varlen == 2;
+  a.f16 = c.f16;
   a.causal = c.causal;
   a.window = c.window;
   a.scale = scale;
@@ -270,6 +276,7 @@ Call whole_call(const attn_shape* s, int varlen, int causal, int window) {
   c.Hkv = s->Hkv;
   c.D = s->D;
   c.varlen = varlen;
+  c.f16 = s->dtype == ATTN_DTYPE_F16;
   c.causal = causal ? 1 : 0;
   c.window = window;
   normalise_offsets(c, 0);
@@ -286,6 +293,7 @@ attn_status check_chunk(const attn_chunk_shape* s, int causal, int window, int64
     return ATTN_ERR_INVALID_ARG;
   if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
   if (s->D != 256 && s->D != 512) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype16_ok(s->dtype)) return ATTN_ERR_UNSUPPORTED;
   if (s->Sq >= (1 << 28) || s->Sk >= (1 << 28)) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)s->B * s->Sq * s->Hq >= INT_MAX / 2 || (int64_t)s->B * s->Sk * s->Hkv >= INT_MAX / 2)
     return ATTN_ERR_UNSUPPORTED;
@@ -302,6 +310,7 @@ Call chunk_call(const attn_chunk_shape* s, int causal, int window, int64_t q_pos
   c.Hkv = s->Hkv;
   c.D = s->D;
   c.varlen = 0;
+  c.f16 = s->dtype == ATTN_DTYPE_F16;
   c.causal = causal ? 1 : 0;
   c.window = window;
   c.empty_lse_ninf = 1;
@@ -491,7 +500,7 @@ attn_status attn_fwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
   attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
   if (st != ATTN_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
-  if (o_dtype != ATTN_DTYPE_BF16 && o_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
+  if (o_dtype != shape->dtype && o_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
   if ((st = check_tensor(q, false)) || (st = check_tensor(k, false)) || (st = check_tensor(v, false)) ||
       (st = check_tensor(o, false)))
     return st;
@@ -509,7 +518,7 @@ attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
   attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
   if (st != ATTN_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
-  if (grad_dtype != ATTN_DTYPE_BF16 && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
+  if (grad_dtype != shape->dtype && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0, k_pos0);
   if (need > 0 &&
       (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))))
@@ -526,9 +535,10 @@ attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
 }
 
 attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D, attn_tensor o, float* lse,
-                           attn_tensor o_part, const float* lse_part, attn_tensor out, void* stream) {
+                           attn_tensor o_part, const float* lse_part, attn_tensor out, int out_dtype, void* stream) {
   if (B < 0 || S < 0 || H <= 0) return ATTN_ERR_INVALID_ARG;
   if (D != 128 && D != 256 && D != 512) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype16_ok(out_dtype)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * S * H >= INT_MAX / 2) return ATTN_ERR_UNSUPPORTED;
   attn_status st;
   if ((st = check_tensor(o, false)) || (st = check_tensor(o_part, false))) return st;
@@ -554,13 +564,14 @@ attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D, attn_tens
   a.S = S;
   a.H = H;
   a.rows = B * S * H;
+  a.out_f16 = out_dtype == ATTN_DTYPE_F16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launch("lse_merge", s, a.rows, [&] { return attn::launch_lse_merge(a, D, s); });
 }
 
 size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {
   if (s == nullptr || s->B < 0 || s->Hq <= 0 || s->Hkv <= 0 || s->D != 128 || s->page_size != 16 ||
-      s->max_pages_per_seq <= 0)
+      s->max_pages_per_seq <= 0 || !dtype16_ok(s->dtype))
     return 0;
   const size_t chunks = ((size_t)s->max_pages_per_seq * s->page_size + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
   return round_up(sizeof(float) * (size_t)s->B * s->Hq * chunks * (s->D + 2));
@@ -577,6 +588,7 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   if (sh.Hq % sh.Hkv != 0) return ATTN_ERR_INVALID_ARG;
   const int r = sh.Hq / sh.Hkv;
   if (sh.D != 128 || sh.page_size != 16 || (r != 1 && r != 2 && r != 4 && r != 8)) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype16_ok(sh.dtype)) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)sh.max_pages_per_seq * sh.page_size > INT_MAX / 2) return ATTN_ERR_UNSUPPORTED;
   if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (q == nullptr || o == nullptr || !aligned16(q) || !aligned16(o) || block_table == nullptr || ctx_lens == nullptr)
@@ -600,6 +612,7 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   a.ctx = ctx_lens;
   a.o = static_cast<__bf16*>(o);
   a.part = static_cast<float*>(workspace);
+  a.f16 = sh.dtype == ATTN_DTYPE_F16;
   a.q_sb = q_stride_b;
   a.q_sh = q_stride_h;
   a.o_sb = o_stride_b;

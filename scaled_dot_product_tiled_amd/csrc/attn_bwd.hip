@@ -32,7 +32,7 @@ namespace attn {
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O)
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, int rows) {
   constexpr int EPL = D / 64;  // elements per lane
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -59,22 +59,27 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, int rows) {
     const bf16* op = a.o + b * a.o_sb + (int64_t)(off + pos) * a.o_ss + h * a.o_sh + lane * EPL;
     const bf16* dp = a.dout + b * a.do_sb + (int64_t)(off + pos) * a.do_ss + h * a.do_sh + lane * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc += (float)op[e] * (float)dp[e];
+    for (int e = 0; e < EPL; ++e) acc += E16<F16>::to_float(op[e]) * E16<F16>::to_float(dp[e]);
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (lane == 0) a.delta[b * a.st_sb + h * a.st_sh + off + pos] = acc;
 }
 
-hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream) {
+template <bool F16>
+hipError_t launch_bwd_pre_t(const AttnArgs& a, int D, int rows, hipStream_t stream) {
   const dim3 grid((rows + 3) / 4), block(256);
   if (D == 512)
-    hipLaunchKernelGGL(bwd_pre_kernel<512>, grid, block, 0, stream, a, rows);
+    hipLaunchKernelGGL((bwd_pre_kernel<512, F16>), grid, block, 0, stream, a, rows);
   else if (D == 256)
-    hipLaunchKernelGGL(bwd_pre_kernel<256>, grid, block, 0, stream, a, rows);
+    hipLaunchKernelGGL((bwd_pre_kernel<256, F16>), grid, block, 0, stream, a, rows);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream) {
+  return a.f16 ? launch_bwd_pre_t<true>(a, D, rows, stream) : launch_bwd_pre_t<false>(a, D, rows, stream);
 }
 
 // Row statistics (LSE * log2 e and delta) of query rows i0 .. i0+31 of head h into LDS:
@@ -89,7 +94,7 @@ __device__ __forceinline__ void dma_stats(float* dst, const float* lse_row0, con
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool F16>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NK = kDkdvKeys;   // 64 keys per workgroup
   constexpr int MQ = kDkdvRows;   // 32 query rows per step
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
           if (t + 2 < KS) f[(t + 2) % 3] = rowf.read(src, 0, t + 2);
-          sacc = mfma32(f[t % 3], kv[t], sacc);
+          sacc = E16<F16>::mma32(f[t % 3], kv[t], sacc);
           if ((t & 1) == 0 && t / 2 < 2 * NDMA) {
             const int j = t / 2;
             if (j < NDMA)
@@ -285,8 +290,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
             float der;
             const float sx = capped(sv[r >> 2][r & 3], der);
             const float p = fast_exp2(fmaf(sx, c, -lse4[r >> 2][r & 3]));
-            pb[r] = (bf16)p;
-            db[r] = (bf16)(p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) * der);
+            pb[r] = E16<F16>::from_float(p);
+            db[r] = E16<F16>::from_float(p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) * der);
           }
         } else {
           // this lane's key is visible from query rows rlo .. rhi-1
@@ -303,8 +308,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
             const float e = fast_exp2(fmaf(sx, c, -lse4[r >> 2][r & 3]));
             const float p = vis ? e : 0.f;
             const float ds = vis ? p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) * der : 0.f;  // +0 when masked
-            pb[r] = (bf16)p;
-            db[r] = (bf16)ds;
+            pb[r] = E16<F16>::from_float(p);
+            db[r] = E16<F16>::from_float(ds);
           }
         }
         pds[0][kb][xh >> 1][lane] = pb;
@@ -327,11 +332,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
         for (int d = 0; d < DBW; ++d) {
           const bf16x8 ado = trf.read(dOs[buf], 16 * s, dsl + d);
-          dvacc[0][d] = mfma32(ado, p0, dvacc[0][d]);
-          dvacc[1][d] = mfma32(ado, p1, dvacc[1][d]);
+          dvacc[0][d] = E16<F16>::mma32(ado, p0, dvacc[0][d]);
+          dvacc[1][d] = E16<F16>::mma32(ado, p1, dvacc[1][d]);
           const bf16x8 aq = trf.read(Qs[buf], 16 * s, dsl + d);
-          dkacc[0][d] = mfma32(aq, s0, dkacc[0][d]);
-          dkacc[1][d] = mfma32(aq, s1, dkacc[1][d]);
+          dkacc[0][d] = E16<F16>::mma32(aq, s0, dkacc[0][d]);
+          dkacc[1][d] = E16<F16>::mma32(aq, s1, dkacc[1][d]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -402,9 +407,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
       for (int qa = 0; qa < 4; ++qa) {
         const int col = 32 * (dsl + d) + 8 * qa;
-        stg4(pk + col, dkacc[x][d][4 * qa] * sc, dkacc[x][d][4 * qa + 1] * sc, dkacc[x][d][4 * qa + 2] * sc,
-             dkacc[x][d][4 * qa + 3] * sc);
-        stg4(pv + col, dvacc[x][d][4 * qa], dvacc[x][d][4 * qa + 1], dvacc[x][d][4 * qa + 2], dvacc[x][d][4 * qa + 3]);
+        stg4e<F16>(pk + col, dkacc[x][d][4 * qa] * sc, dkacc[x][d][4 * qa + 1] * sc, dkacc[x][d][4 * qa + 2] * sc,
+                   dkacc[x][d][4 * qa + 3] * sc);
+        stg4e<F16>(pv + col, dvacc[x][d][4 * qa], dvacc[x][d][4 * qa + 1], dvacc[x][d][4 * qa + 2],
+                   dvacc[x][d][4 * qa + 3]);
       }
   }
 }
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
 // dK, dV of workgroups that split a group's query heads: the sum of the parts in part order
 // (deterministic), written in bf16 or added to the fp32 accumulators.  Elementwise: 8
 // consecutive head_dim elements per thread.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(AttnArgs a) {
   constexpr int TPR = D / 8;
   const int64_t rows = (int64_t)a.B * a.Sk * a.Hkv;
@@ -445,38 +451,48 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(AttnArgs a) {
     } else {
       bf16* out = (which ? a.dv + b * a.dv_sb + (int64_t)key * a.dv_ss + g * a.dv_sh
                          : a.dk + b * a.dk_sb + (int64_t)key * a.dk_ss + g * a.dk_sh) + c0;
-      stg4(out, v[0], v[1], v[2], v[3]);
-      stg4(out + 4, v[4], v[5], v[6], v[7]);
+      stg4e<F16>(out, v[0], v[1], v[2], v[3]);
+      stg4e<F16>(out + 4, v[4], v[5], v[6], v[7]);
     }
   }
 }
 
-hipError_t launch_bwd_kv_reduce(const AttnArgs& a, int D, hipStream_t stream) {
+template <bool F16>
+hipError_t launch_bwd_kv_reduce_t(const AttnArgs& a, int D, hipStream_t stream) {
   const int64_t threads = (int64_t)a.B * a.Sk * a.Hkv * (D / 8);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   if (D == 512)
-    hipLaunchKernelGGL(bwd_kv_reduce_kernel<512>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((bwd_kv_reduce_kernel<512, F16>), grid, block, 0, stream, a);
   else if (D == 256)
-    hipLaunchKernelGGL(bwd_kv_reduce_kernel<256>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((bwd_kv_reduce_kernel<256, F16>), grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv_reduce(const AttnArgs& a, int D, hipStream_t stream) {
+  return a.f16 ? launch_bwd_kv_reduce_t<true>(a, D, stream) : launch_bwd_kv_reduce_t<false>(a, D, stream);
+}
+
+template <bool F16>
+hipError_t launch_bwd_dkdv_t(const AttnArgs& a, int D, hipStream_t stream) {
+  const dim3 grid(8 * a.per_xcd), block(256);
+  const bool sc = a.softcap > 0.f;
+  if (D == 512 && !sc)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<512, false, F16>), grid, block, 0, stream, a);
+  else if (D == 512)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<512, true, F16>), grid, block, 0, stream, a);
+  else if (D == 256 && !sc)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<256, false, F16>), grid, block, 0, stream, a);
+  else if (D == 256)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<256, true, F16>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
-  const dim3 grid(8 * a.per_xcd), block(256);
-  const bool sc = a.softcap > 0.f;
-  if (D == 512 && !sc)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<512, false>), grid, block, 0, stream, a);
-  else if (D == 512)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<512, true>), grid, block, 0, stream, a);
-  else if (D == 256 && !sc)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<256, false>), grid, block, 0, stream, a);
-  else if (D == 256)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<256, true>), grid, block, 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  return a.f16 ? launch_bwd_dkdv_t<true>(a, D, stream) : launch_bwd_dkdv_t<false>(a, D, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -492,7 +508,7 @@ hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
 // dQ^T accumulates in registers: A operand K^T and B operand dS^T, both read with
 // transposing LDS reads.  Pairs that are not visible are zeroed by selection (blocks on the
 // diagonal or the window edge may hold stale values there).
-template <int D, int NW, int NSPLIT>
+template <int D, int NW, int NSPLIT, bool F16>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
   // D: head_dim columns of this workgroup (the full head_dim is D * NSPLIT)
   constexpr int M = kDsRows;          // 128 query rows
@@ -594,7 +610,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
         for (int d = 0; d < DBW; ++d) {
           const bf16x8 ak = trk.read_with(Ks[buf], 16 * s, dsl + d, klo[d], khi[d]);
 #pragma unroll
-          for (int x = 0; x < RB; ++x) acc[x][d] = mfma32(ak, bs[x], acc[x][d]);
+          for (int x = 0; x < RB; ++x) acc[x][d] = E16<F16>::mma32(ak, bs[x], acc[x][d]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -631,20 +647,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
     for (int d = 0; d < DBW; ++d)
 #pragma unroll
       for (int qa = 0; qa < 4; ++qa)
-        stg4(pq + 32 * (dsl + d) + 8 * qa, acc[x][d][4 * qa] * sc, acc[x][d][4 * qa + 1] * sc,
+        stg4e<F16>(pq + 32 * (dsl + d) + 8 * qa, acc[x][d][4 * qa] * sc, acc[x][d][4 * qa + 1] * sc,
              acc[x][d][4 * qa + 2] * sc, acc[x][d][4 * qa + 3] * sc);
   }
 }
 
-hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream) {
+template <bool F16>
+hipError_t launch_bwd_dq_t(const AttnArgs& a, int D, hipStream_t stream) {
   const dim3 grid(8 * a.per_xcd);
   if (D == 512)
-    hipLaunchKernelGGL((bwd_dq_kernel<512 / kDqSplit512, 4, kDqSplit512>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<512 / kDqSplit512, 4, kDqSplit512, F16>), grid, dim3(256), 0, stream, a);
   else if (D == 256)
-    hipLaunchKernelGGL((bwd_dq_kernel<256, 4, 1>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<256, 4, 1, F16>), grid, dim3(256), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream) {
+  return a.f16 ? launch_bwd_dq_t<true>(a, D, stream) : launch_bwd_dq_t<false>(a, D, stream);
 }
 
 }  // namespace attn

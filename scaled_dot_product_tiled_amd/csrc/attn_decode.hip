@@ -31,10 +31,6 @@ namespace attn {
 
 constexpr int kDecD = 128;
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 // Value of this lane's partner at lane ^ 16, combined.
 __device__ __forceinline__ float row_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -45,7 +41,7 @@ __device__ __forceinline__ float row_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int R>
+template <int R, bool F16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int D = kDecD;
   constexpr int CH = kDecodeChunk;      // tokens per workgroup
@@ -141,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + pg * PAGE_B + li * 256 + 16 * ((4 * kk + grp) ^ li));
-        st[pg] = mfma16(kf, qf[kk], st[pg]);
+        st[pg] = E16<F16>::mma16(kf, qf[kk], st[pg]);
       }
     }
     // lane: head li, tokens 4 grp + i of each page
@@ -170,14 +166,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(t[pg][i] - m);
         l += p;
-        pb[4 * pg + i] = (bf16)p;
+        pb[4 * pg + i] = E16<F16>::from_float(p);
       }
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const int off = rd_base + 32 * (blk ^ rd_x);
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vb + off));
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vb + PAGE_B + off));
-      acc[blk] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, acc[blk]);
+      acc[blk] = E16<F16>::mma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, acc[blk]);
     }
   };
 
@@ -232,6 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
 // One pass over the chunk partials of a (sequence, query head): the loads of up to U
 // chunks are issued together, and a running maximum rescales what was summed before.
+template <bool F16>
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
   constexpr int D = kDecD;
   constexpr int U = 8;
@@ -268,25 +265,33 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
     M = Mn;
   }
   const float out = den > 0.f ? acc / den : 0.f;
-  a.o[b * a.o_sb + h * a.o_sh + d] = (bf16)out;
+  a.o[b * a.o_sb + h * a.o_sh + d] = E16<F16>::from_float(out);
 }
 
-hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream) {
-  if (D != kDecD) return hipErrorInvalidValue;
+template <bool F16>
+hipError_t launch_decode_split_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 g1(a.B * a.Hkv * a.max_chunks), b1(256);
   switch (a.r) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, g1, b1, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, g1, b1, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, g1, b1, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(decode_split_kernel<8>, g1, b1, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<1, F16>), g1, b1, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<2, F16>), g1, b1, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<4, F16>), g1, b1, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_split_kernel<8, F16>), g1, b1, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream) {
+  if (D != kDecD) return hipErrorInvalidValue;
+  return a.f16 ? launch_decode_split_t<true>(a, stream) : launch_decode_split_t<false>(a, stream);
+}
+
 hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream) {
   if (D != kDecD) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.B * a.Hq), dim3(kDecD), 0, stream, a);
+  if (a.f16)
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(a.B * a.Hq), dim3(kDecD), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(a.B * a.Hq), dim3(kDecD), 0, stream, a);
   return hipGetLastError();
 }
 

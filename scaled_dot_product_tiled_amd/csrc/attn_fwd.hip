@@ -40,9 +40,12 @@
 
 namespace attn {
 
+// Largest exponent (log2 units) an exponential may reach above the fixed reference: P is
+// rounded to the 16-bit type before the P V product, and IEEE half ends at 65504 < 2^16.
 constexpr float kRefSlack = 32.0f;
+constexpr float kRefSlackF16 = 15.0f;
 
-template <int D, int N, bool EXACT, bool SOFTCAP>
+template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
 // At head_dim 256 a wave fits in 256 registers, so two workgroups share a compute unit and
 // one's softmax and barriers overlap the other's matrix work; at 512 the accumulators alone
 // take 256 registers.
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
             for (int kb = 0; kb < NKB; ++kb) kf[(t + 2) % 3][kb] = rowf.read(Ks, kb * 32, t + 2);
           }
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32(kf[t % 3][kb], qreg[t], sacc[kb]);
+          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = E16<F16>::mma32(kf[t % 3][kb], qreg[t], sacc[kb]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
       } else {
         // A row's first visible keys fix its reference (its accumulators are still zero).
         if (m_ref == -INFINITY) m_ref = mt;
-        const bool need = mt > m_ref + kRefSlack;
+        const bool need = mt > m_ref + (F16 ? kRefSlackF16 : kRefSlack);
         const bool wave_need = __any(need);
         if (lane == 0) restart_flag[jt & 1][wave] = wave_need ? 1 : 0;
 
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pb[s][e] = (bf16)sacc[s >> 1][8 * (s & 1) + e];
+          for (int e = 0; e < 8; ++e) pb[s][e] = E16<F16>::from_float(sacc[s >> 1][8 * (s & 1) + e]);
         // V^T fragments in (d block, key step) order, read two ahead of the matrix core.
         constexpr int NF = DB * NS;
         bf16x8 vf[3];
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           if (f + 2 < NF) vf[(f + 2) % 3] = trf.read(Vs, 16 * ((f + 2) % NS), (f + 2) / NS);
-          oacc[f / NS] = mfma32(vf[f % 3], pb[f % NS], oacc[f / NS]);
+          oacc[f / NS] = E16<F16>::mma32(vf[f % 3], pb[f % NS], oacc[f / NS]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
       for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int qa = 0; qa < 4; ++qa)
-          stg4(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv, oacc[d][4 * qa + 2] * inv,
+          st4<F16>(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv, oacc[d][4 * qa + 2] * inv,
                oacc[d][4 * qa + 3] * inv);
     };
     if (a.out_f32)
@@ -270,20 +273,25 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
   }
 }
 
-hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream) {
+template <bool F16>
+hipError_t launch_fwd_t(const AttnArgs& a, int D, hipStream_t stream) {
   const dim3 grid(8 * a.per_xcd), block(256);
   const bool sc = a.softcap > 0.f;
   if (D == 512 && !sc)
-    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, false, F16>), grid, block, 0, stream, a);
   else if (D == 512)
-    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, true, F16>), grid, block, 0, stream, a);
   else if (D == 256 && !sc)
-    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, false, F16>), grid, block, 0, stream, a);
   else if (D == 256)
-    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, true, F16>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream) {
+  return a.f16 ? launch_fwd_t<true>(a, D, stream) : launch_fwd_t<false>(a, D, stream);
 }
 
 }  // namespace attn

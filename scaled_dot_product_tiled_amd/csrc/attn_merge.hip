@@ -23,7 +23,7 @@
 
 namespace attn {
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   constexpr int TPR = D / 8;      // lanes per row
   constexpr int RPB = 256 / TPR;  // rows per workgroup
@@ -67,24 +67,29 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   stg4(o1 + 4, y[4], y[5], y[6], y[7]);
   if (a.out) {
     bf16* r = a.out + b * a.r_sb + (int64_t)s * a.r_ss + h * a.r_sh + 8 * t;
-    stg4(r, y[0], y[1], y[2], y[3]);
-    stg4(r + 4, y[4], y[5], y[6], y[7]);
+    stg4e<F16>(r, y[0], y[1], y[2], y[3]);
+    stg4e<F16>(r + 4, y[4], y[5], y[6], y[7]);
   }
   if (t == 0) a.lse[li] = lse;
 }
 
-hipError_t launch_lse_merge(const MergeArgs& a, int D, hipStream_t stream) {
+template <bool F16>
+hipError_t launch_lse_merge_t(const MergeArgs& a, int D, hipStream_t stream) {
   const int rpb = 256 / (D / 8);
   const dim3 grid((a.rows + rpb - 1) / rpb), block(256);
   if (D == 512)
-    hipLaunchKernelGGL(lse_merge_kernel<512>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<512, F16>), grid, block, 0, stream, a);
   else if (D == 256)
-    hipLaunchKernelGGL(lse_merge_kernel<256>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<256, F16>), grid, block, 0, stream, a);
   else if (D == 128)
-    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<128, F16>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const MergeArgs& a, int D, hipStream_t stream) {
+  return a.out_f16 ? launch_lse_merge_t<true>(a, D, stream) : launch_lse_merge_t<false>(a, D, stream);
 }
 
 }  // namespace attn

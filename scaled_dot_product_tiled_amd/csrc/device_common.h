@@ -37,9 +37,42 @@ constexpr float kLn2 = 0.69314718055994531f;
 // reference value, so the result is unchanged in exact arithmetic.
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+// 16-bit element types: bfloat16 (F16 = false) or IEEE half (F16 = true).  Tensors, LDS
+// tiles and matrix operands are moved as 16-bit patterns in the bf16 storage type; only the
+// matrix instruction and the conversions to and from fp32 (round to nearest even) depend on
+// the type.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <bool F16>
+struct E16;
+
+template <>
+struct E16<false> {
+  static __device__ __forceinline__ bf16 from_float(float x) { return (bf16)x; }
+  static __device__ __forceinline__ float to_float(bf16 x) { return (float)x; }
+  static __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct E16<true> {
+  static __device__ __forceinline__ bf16 from_float(float x) { return __builtin_bit_cast(bf16, (_Float16)x); }
+  static __device__ __forceinline__ float to_float(bf16 x) { return (float)__builtin_bit_cast(_Float16, x); }
+  static __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  }
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) { return E16<false>::mma32(a, b, c); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -236,9 +269,26 @@ __device__ __forceinline__ void stg4(bf16* p, float a, float b, float c, float d
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
+// Four fp32 values rounded to the 16-bit type F16 selects.
+template <bool F16>
+__device__ __forceinline__ void stg4e(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = E16<F16>::from_float(a);
+  v[1] = E16<F16>::from_float(b);
+  v[2] = E16<F16>::from_float(c);
+  v[3] = E16<F16>::from_float(d);
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+
 __device__ __forceinline__ void stg4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
+
+// Store to an output that is either the 16-bit type F16 selects or fp32.
+template <bool F16>
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) { stg4e<F16>(p, a, b, c, d); }
+template <bool F16>
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) { stg4(p, a, b, c, d); }
 
 // p[0..3] += (a, b, c, d) in fp32; p is owned by this lane alone.
 __device__ __forceinline__ void add4(float* p, float a, float b, float c, float d) {

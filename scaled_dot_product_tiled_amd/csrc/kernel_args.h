@@ -57,6 +57,7 @@ struct AttnArgs {
   int nkt;                  // key tiles (dK/dV kernel)
   int kv_split;             // dK/dV: workgroups sharing one key tile's query heads (1, 2 or 4)
   float* kv_part;           // kv_split > 1: fp32 partial dK, dV, [part][dK|dV][B][Sk][Hkv][D]
+  int f16;                  // 16-bit tensors are IEEE half (else bfloat16)
   int packed;               // rows past a sequence's length do not exist
   int causal, window;
   float scale;
@@ -81,6 +82,7 @@ struct DecodeArgs {
   int64_t kc_sp, kc_ss, kc_sh, vc_sp, vc_ss, vc_sh;
   int B, Hq, Hkv, r, page_size, num_pages, max_pages, max_chunks;
   float c;            // scale * log2(e)
+  int f16;            // 16-bit tensors are IEEE half (else bfloat16)
 };
 
 // In-place log-sum-exp merge of a partial result (o_part, lse_part) into (o, lse), rows
@@ -96,6 +98,7 @@ struct MergeArgs {
   int64_t p_sb, p_ss, p_sh;
   int64_t r_sb, r_ss, r_sh;
   int B, S, H, rows;
+  int out_f16;  // out is IEEE half (else bfloat16)
 };
 
 // The backward stores dS = P * (dP - delta) (bf16) once, for the dQ product.  It is kept in

@@ -23,8 +23,8 @@ import numpy as np
 
 __all__ = [
     "AttnWorkload", "DecodeWorkload", "ATTN_WORKLOADS", "DECODE_WORKLOADS",
-    "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64", "stream",
-    "normal_bf16", "make_attention_inputs", "make_decode_inputs",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64", "f32_to_f16_bits", "f16_bits_to_f64",
+    "bits_to_f64", "NAN_BITS", "stream", "normal_bf16", "normal_16", "make_attention_inputs", "make_decode_inputs",
     "lengths_to_pad_mask", "lengths_to_cu_seqlens", "pack_rows", "draw_lengths", "STREAM",
 ]
 
@@ -61,12 +61,38 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(b).astype(np.float64)
 
 
+# ----------------------------------------------------------------------------
+# IEEE half bit handling (numpy's float32 -> float16 conversion rounds to nearest, ties to even)
+# ----------------------------------------------------------------------------
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE half (nearest, ties to even); returns uint16 bit patterns."""
+    with np.errstate(over="ignore"):  # past the largest half: +-inf, as rounding defines
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact widening of IEEE half bit patterns to float64."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bits_to_f64(b: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Exact widening of 16-bit patterns of the given type ("bf16" or "f16") to float64."""
+    return f16_bits_to_f64(b) if dtype == "f16" else bf16_bits_to_f64(b)
+
+
+# quiet NaN bit pattern of each 16-bit type
+NAN_BITS = {"bf16": np.uint16(0x7FC0), "f16": np.uint16(0x7E00)}
+
+
 def stream(seed: int, workload_id: int, stream_id: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([seed, workload_id, stream_id]))
 
 
-def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0, chunk: int = 1 << 26) -> np.ndarray:
-    """N(0, std^2) draws in float32, rounded to bfloat16 bit patterns, drawn in bounded chunks."""
+def normal_16(rng: np.random.Generator, shape, std: float = 1.0, dtype: str = "bf16",
+              chunk: int = 1 << 26) -> np.ndarray:
+    """N(0, std^2) draws in float32, rounded to 16-bit patterns ("bf16" or "f16"), drawn in
+    bounded chunks."""
+    conv = f32_to_f16_bits if dtype == "f16" else f32_to_bf16_bits
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
     for s in range(0, n, chunk):
@@ -74,8 +100,13 @@ def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0, chunk: int = 
         x = rng.standard_normal(e - s, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
-        out[s:e] = f32_to_bf16_bits(x)
+        out[s:e] = conv(x)
     return out.reshape(shape)
+
+
+def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0, chunk: int = 1 << 26) -> np.ndarray:
+    """N(0, std^2) draws in float32, rounded to bfloat16 bit patterns, drawn in bounded chunks."""
+    return normal_16(rng, shape, std, "bf16", chunk)
 
 
 # ----------------------------------------------------------------------------
@@ -97,6 +128,7 @@ class AttnWorkload:
     vdo_std: float = 1.0         # std of the V and dO draws
     varlen: Optional[str] = None  # None, "pad_mask" (right padded to S) or "cu_seqlens" (packed rows)
     len_range: Optional[tuple] = None  # inclusive uniform range of valid lengths
+    dtype: str = "bf16"          # 16-bit element type of every tensor: "bf16" or "f16"
 
     @property
     def scale(self) -> float:
@@ -125,6 +157,7 @@ class DecodeWorkload:
     page_size: int = 16
     ctx_range: tuple = (512, 4096)   # inclusive uniform range of context lengths
     pool_factor: float = 1.5         # page pool = ceil(pool_factor * pages actually used)
+    dtype: str = "bf16"              # 16-bit element type of q, caches and o: "bf16" or "f16"
 
     @property
     def scale(self) -> float:
@@ -183,22 +216,23 @@ def draw_lengths(w, seed):
 
 
 def make_attention_inputs(w: AttnWorkload, seed: int = 0, poison_padding: bool = False) -> dict:
-    """Seeded bf16 Q, K, V, dO (uint16 bit patterns, shape (B, S, H, D)) plus varlen metadata.
+    """Seeded 16-bit Q, K, V, dO (uint16 bit patterns of w.dtype, shape (B, S, H, D)) plus varlen
+    metadata.
 
     Padding positions hold ordinary draws; with ``poison_padding`` they hold NaN, which a correct
     varlen path must never let reach a valid output.
     """
-    q = normal_bf16(stream(seed, w.wid, STREAM["q"]), (w.B, w.S, w.Hq, w.D), w.qk_std)
-    k = normal_bf16(stream(seed, w.wid, STREAM["k"]), (w.B, w.S, w.Hkv, w.D), w.qk_std)
-    v = normal_bf16(stream(seed, w.wid, STREAM["v"]), (w.B, w.S, w.Hkv, w.D), w.vdo_std)
-    do = normal_bf16(stream(seed, w.wid, STREAM["do"]), (w.B, w.S, w.Hq, w.D), w.vdo_std)
+    q = normal_16(stream(seed, w.wid, STREAM["q"]), (w.B, w.S, w.Hq, w.D), w.qk_std, w.dtype)
+    k = normal_16(stream(seed, w.wid, STREAM["k"]), (w.B, w.S, w.Hkv, w.D), w.qk_std, w.dtype)
+    v = normal_16(stream(seed, w.wid, STREAM["v"]), (w.B, w.S, w.Hkv, w.D), w.vdo_std, w.dtype)
+    do = normal_16(stream(seed, w.wid, STREAM["do"]), (w.B, w.S, w.Hq, w.D), w.vdo_std, w.dtype)
     lengths = draw_lengths(w, seed)
     out = {"q": q, "k": k, "v": v, "do": do, "lengths": lengths}
     if lengths is not None:
         out["pad_mask"] = lengths_to_pad_mask(lengths, w.S)
         out["cu_seqlens"] = lengths_to_cu_seqlens(lengths)
         if poison_padding:
-            nan = np.uint16(0x7FC0)
+            nan = NAN_BITS[w.dtype]
             for b, n in enumerate(lengths):
                 for t in (q, k, v, do):
                     t[b, n:] = nan
@@ -230,11 +264,11 @@ def make_decode_inputs(w: DecodeWorkload, seed: int = 0, poison_unused: bool = F
         n = int(pages[b])
         table[b, :n] = perm[off:off + n]
         off += n
-    q = normal_bf16(stream(seed, w.wid, STREAM["q"]), (w.B, w.Hq, w.D))
-    kc = normal_bf16(stream(seed, w.wid, STREAM["k"]), (pool, ps, w.Hkv, w.D))
-    vc = normal_bf16(stream(seed, w.wid, STREAM["v"]), (pool, ps, w.Hkv, w.D))
+    q = normal_16(stream(seed, w.wid, STREAM["q"]), (w.B, w.Hq, w.D), 1.0, w.dtype)
+    kc = normal_16(stream(seed, w.wid, STREAM["k"]), (pool, ps, w.Hkv, w.D), 1.0, w.dtype)
+    vc = normal_16(stream(seed, w.wid, STREAM["v"]), (pool, ps, w.Hkv, w.D), 1.0, w.dtype)
     if poison_unused:
-        nan = np.uint16(0x7FC0)
+        nan = NAN_BITS[w.dtype]
         used = np.zeros(pool, dtype=bool)
         for b in range(w.B):
             n = int(pages[b])

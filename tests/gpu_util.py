@@ -3,7 +3,7 @@ and back, the tolerance measures, and one-call wrappers around the library bindi
 import numpy as np
 import torch
 
-from synth import bf16_bits_to_f64
+from synth import bits_to_f64
 
 # Tolerances for floating-point results (bf16 inputs and outputs, fp32 accumulation).
 O_MAX_ABS = 2e-2        # forward output and decode output, max |gpu - oracle| over valid rows
@@ -11,10 +11,13 @@ GRAD_REL_L2 = 5e-2      # dQ, dK, dV: ||gpu - oracle||_2 / ||oracle||_2 over val
 LSE_MAX_ABS = 1e-2      # row log-sum-exp (fp32 output)
 
 
-def dev(bits: np.ndarray) -> torch.Tensor:
-    """uint16 bf16 bit patterns -> bfloat16 tensor on cuda:0 (same bytes)."""
+TORCH16 = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def dev(bits: np.ndarray, dtype: str = "bf16") -> torch.Tensor:
+    """uint16 bit patterns of a 16-bit type -> tensor of that type on cuda:0 (same bytes)."""
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
-    return t.to("cuda:0").view(torch.bfloat16)
+    return t.to("cuda:0").view(TORCH16[dtype])
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:
@@ -22,9 +25,11 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def host(t: torch.Tensor) -> np.ndarray:
-    """bf16 / fp32 device tensor -> float64 numpy (exact)."""
+    """bf16 / fp16 / fp32 device tensor -> float64 numpy (exact)."""
     if t.dtype == torch.bfloat16:
-        return bf16_bits_to_f64(host_bits(t))
+        return bits_to_f64(host_bits(t), "bf16")
+    if t.dtype == torch.float16:
+        return bits_to_f64(host_bits(t), "f16")
     return t.detach().cpu().double().numpy()
 
 

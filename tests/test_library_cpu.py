@@ -88,6 +88,8 @@ def test_argument_checks_happen_before_any_launch():
     assert _fwd(lib, s, softcap=float("nan")) == INVALID
     assert _fwd(lib, AttnShape(2, 64, 0, 8, 2, 128)) == UNSUPPORTED   # head_dim 128 is decode-only
     assert _fwd(lib, AttnShape(2, 64, 0, 8, 3, 512)) == INVALID       # Hq % Hkv
+    assert _fwd(lib, AttnShape(2, 64, 0, 8, 2, 512, 1)) == UNSUPPORTED  # tensors are bf16 or fp16, not fp32
+    assert _fwd(lib, AttnShape(0, 64, 0, 8, 2, 512, 2)) == OK            # fp16
     assert _fwd(lib, s, cu=0x30000, pm=0x40000) == INVALID            # both varlen forms
     assert _fwd(lib, s, pm=0x40000) == WORKSPACE                      # varlen needs metadata workspace
     assert _fwd(lib, s, pm=0x40000, ws=0x50010, wsb=4096) == WORKSPACE  # misaligned workspace
@@ -158,7 +160,8 @@ def test_chunk_and_merge_checks():
     assert fwd(lse=0) == INVALID
     assert fwd(q=_t(ptr=0x10008)) == INVALID
     assert fwd(shape=AttnChunkShape(2, 64, 96, 8, 3, 512)) == INVALID
-    assert fwd(odt=2) == INVALID                                        # O is bf16 or fp32
+    assert fwd(odt=2) == INVALID                                        # O is fp32 or the inputs' type (bf16)
+    assert fwd(odt=3) == INVALID
     assert fwd(cap=-2.0) == INVALID
     assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512)) == OK       # empty batch
     assert fwd(shape=AttnChunkShape(0, 64, 96, 8, 2, 512), odt=0) == OK
@@ -170,8 +173,9 @@ def test_chunk_and_merge_checks():
     assert bwd(gdt=1) == WORKSPACE
     assert bwd(gdt=3, ws=0x100000, wsb=1 << 30) == INVALID             # parts are bf16 or fp32
 
-    def merge(B=2, S=64, H=8, D=512, lse=0x20000, part=0x30000, o=None, out=None):
-        return lib.attn_lse_merge(B, S, H, D, o or _t(), lse, _t(), part, out or AttnTensor(None, 0, 0, 0), None)
+    def merge(B=2, S=64, H=8, D=512, lse=0x20000, part=0x30000, o=None, out=None, odt=0):
+        return lib.attn_lse_merge(B, S, H, D, o or _t(), lse, _t(), part, out or AttnTensor(None, 0, 0, 0), odt,
+                                  None)
     assert merge(D=64) == UNSUPPORTED
     assert merge(H=0) == INVALID
     assert merge(lse=0) == INVALID
@@ -179,5 +183,7 @@ def test_chunk_and_merge_checks():
     assert merge(o=_t(ptr=0)) == INVALID
     assert merge(out=_t(ptr=0x10008)) == INVALID                        # the bf16 output is optional, but aligned
     assert merge(B=0) == OK
+    assert merge(B=0, odt=2) == OK
+    assert merge(B=0, odt=1) == INVALID                                 # the final output is 16-bit
     assert merge(B=0, out=_t()) == OK
     assert lib.attn_last_hip_error() == 0

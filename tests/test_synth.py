@@ -3,8 +3,8 @@ import hashlib
 
 import numpy as np
 
-from synth import (ATTN_WORKLOADS, DECODE_WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits,
-                   lengths_to_cu_seqlens, lengths_to_pad_mask, make_attention_inputs,
+from synth import (ATTN_WORKLOADS, DECODE_WORKLOADS, bf16_bits_to_f32, f16_bits_to_f64, f32_to_bf16_bits,
+                   f32_to_f16_bits, lengths_to_cu_seqlens, lengths_to_pad_mask, make_attention_inputs,
                    make_decode_inputs, normal_bf16, stream)
 
 
@@ -24,6 +24,21 @@ def test_bf16_rounding_hand_picked_patterns():
     x = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
     back = bf16_bits_to_f32(f32_to_bf16_bits(x))
     assert np.all(np.abs(back - x) <= np.abs(x) * 2 ** -8)
+
+
+def test_f16_rounding_hand_picked_patterns():
+    f = np.array([1.0, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, -2.5, 65504.0, 65520.0, 2.0 ** -24, 2.0 ** -26],
+                 dtype=np.float32)
+    b = f32_to_f16_bits(f)
+    # 1+2^-11 ties between 1 and 1+2^-10 and goes to the even mantissa; 1+3*2^-11 goes up to 1+2^-9
+    assert list(b[:3]) == [0x3C00, 0x3C00, 0x3C02]
+    assert b[3] == 0xC100
+    assert b[4] == 0x7BFF            # largest half
+    assert b[5] == 0x7C00            # halfway past it rounds to +inf
+    assert b[6] == 0x0001            # smallest subnormal
+    assert b[7] == 0x0000            # below half of it: +0
+    x = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
+    assert np.all(np.abs(f16_bits_to_f64(f32_to_f16_bits(x)) - x) <= np.abs(x) * 2 ** -11 + 2 ** -25)
 
 
 def test_generators_are_deterministic_and_streams_independent():

@@ -44,7 +44,7 @@ __all__ = [
     "scores", "unit_forward", "unit_backward", "attention_forward", "attention_backward",
     "attention_forward_head", "attention_backward_group",
     "attention_forward_packed", "attention_backward_packed",
-    "gather_pages", "paged_decode", "paged_decode_one", "attention_rows",
+    "gather_pages", "paged_append", "paged_decode", "paged_decode_one", "attention_rows",
     "chunk_visibility", "attention_forward_chunk", "attention_backward_chunk", "lse_merge",
 ]
 
@@ -383,6 +383,27 @@ def gather_pages(cache, table_row, ctx, page_size):
     table_row[t // page_size] at slot t % page_size."""
     t = np.arange(int(ctx))
     return cache[np.asarray(table_row)[t // page_size], t % page_size]
+
+
+def paged_append(cache, block_table, ctx_lens, new, page_size=16):
+    """A copy of cache (num_pages, page_size, Hkv, D) with the n newest tokens of each sequence
+    written in: new[b, i] (new is (B, n, Hkv, D)) goes to logical position ctx_b - n + i, i.e. to
+    slot (pos % page_size) of page block_table[b][pos // page_size] (the page-table mapping of the
+    fourth page, Architecture notes).  Positions below 0 or at or past the table's end, and table
+    entries outside [0, num_pages), are skipped.  Works on any dtype (it only moves values)."""
+    out = np.array(cache, copy=True)
+    B, n = new.shape[0], new.shape[1]
+    num_pages, table_cols = cache.shape[0], block_table.shape[1]
+    for b in range(B):
+        ctx = int(min(max(int(ctx_lens[b]), 0), table_cols * page_size))
+        for i in range(n):
+            pos = ctx - n + i
+            if pos < 0:
+                continue
+            page = int(block_table[b, pos // page_size])
+            if 0 <= page < num_pages:
+                out[page, pos % page_size] = new[b, i]
+    return out
 
 
 def paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_size=16):

@@ -514,3 +514,55 @@ def test_chunk_rows_without_keys_and_merge_identity():
     assert abs(float(mo[0, 0, 0, 0]) - (2.0 * w1 - 5.0 * (1 - w1))) < 1e-14
     assert abs(float(ml[0, 0, 0]) - math.log(math.exp(s1) + math.exp(s2))) < 1e-14
     assert np.array_equal(mo, mo2) and np.array_equal(ml, ml2)
+
+
+# ---------------------------------------------------------------------------
+# Paged cache append: a hand-placed example and the gather round trip
+# ---------------------------------------------------------------------------
+def test_paged_append_hand_example():
+    # page_size 2; sequence 0 uses pages 3, 1 and holds 3 tokens after the append (its new
+    # token lands at position 2: page 1, slot 0); sequence 1 uses pages 0, 2 and holds 1 token
+    # (position 0: page 0, slot 0); a third sequence with a -1 entry is skipped
+    cache = np.zeros((4, 2, 1, 1))
+    table = np.array([[3, 1], [0, 2], [-1, -1]], dtype=np.int32)
+    new = np.array([[[[7.0]]], [[[9.0]]], [[[5.0]]]])
+    out = oracle.paged_append(cache, table, np.array([3, 1, 1]), new, page_size=2)
+    expect = np.zeros((4, 2, 1, 1))
+    expect[1, 0] = 7.0
+    expect[0, 0] = 9.0
+    assert np.array_equal(out, expect)
+    assert not cache.any()                       # the input is not modified
+
+
+def test_paged_append_then_gather_round_trip():
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=5, ctx_range=(3, 90), Hkv=2)
+    inp = make_decode_inputs(w, seed=6)
+    ctx0 = inp["ctx_lens"]
+    n = 3
+    ctx1 = ctx0 + n
+    table = inp["block_table"]
+    rng = np.random.default_rng(7)
+    new = rng.standard_normal((w.B, n, w.Hkv, w.D))
+    kc = bf16_bits_to_f64(inp["k_cache"])
+    # room for the appended tokens: extend each table row with fresh pool pages where needed
+    pages_needed = -(-ctx1 // w.page_size)
+    used = set(table[table >= 0].tolist())
+    free = [p for p in range(kc.shape[0]) if p not in used]
+    table = np.concatenate([table, np.full((w.B, 2), -1, dtype=np.int32)], axis=1)
+    for b in range(w.B):
+        for p in range(int(pages_needed[b])):
+            if table[b, p] < 0:
+                if not free:
+                    kc = np.concatenate([kc, np.zeros((1,) + kc.shape[1:])])
+                    free.append(kc.shape[0] - 1)
+                table[b, p] = free.pop()
+    out = oracle.paged_append(kc, table, ctx1, new, w.page_size)
+    for b in range(w.B):
+        g = oracle.gather_pages(out, table[b], ctx1[b], w.page_size)
+        assert np.array_equal(g[ctx0[b]:], new[b])                       # the appended tokens
+        assert np.array_equal(g[:ctx0[b]], oracle.gather_pages(kc, table[b], ctx0[b], w.page_size))
+    touched = np.zeros(kc.shape[:2], dtype=bool)
+    for b in range(w.B):
+        for t in range(int(ctx0[b]), int(ctx1[b])):
+            touched[table[b, t // w.page_size], t % w.page_size] = True
+    assert np.array_equal(out[~touched], kc[~touched])                    # nothing else changed

@@ -235,8 +235,9 @@ typedef struct {
  * "What each option did": the per-block page-table indirection that a random
  * page placement makes necessary).
  *
- *   q            device bf16 (B, Hq, D); element strides q_stride_b, q_stride_h
- *   k_cache,     device bf16 (num_pages, page_size, Hkv, D); attn_tensor strides
+ *   q            device 16-bit (shape->dtype) (B, Hq, D); element strides q_stride_b,
+ *                q_stride_h
+ *   k_cache,     device 16-bit (num_pages, page_size, Hkv, D); attn_tensor strides
  *   v_cache      are (page, slot, head) in elements; a slot stride of 2^26 elements
  *                or more returns ATTN_ERR_UNSUPPORTED
  *   block_table  device int32 (B, max_pages_per_seq), row-major: logical page p of
@@ -247,7 +248,7 @@ typedef struct {
  *                current one; the query sits at position ctx_lens[b]-1 and sees
  *                every token t < ctx_lens[b].  Clamped to
  *                [0, max_pages_per_seq * page_size]; 0 gives O = 0.
- *   o            device bf16 (B, Hq, D), written; strides o_stride_b, o_stride_h
+ *   o            device 16-bit (B, Hq, D), written; strides o_stride_b, o_stride_h
  *   workspace    at least paged_decode_workspace_bytes(shape) bytes
  */
 attn_status paged_decode(const attn_decode_shape* shape,
@@ -257,6 +258,40 @@ attn_status paged_decode(const attn_decode_shape* shape,
                          float scale,
                          void* o, int64_t o_stride_b, int64_t o_stride_h,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_kv_append: write the n_tokens newest tokens of each sequence into its cache pages:
+ * token i of sequence b (k_new/v_new row (b, i)) goes to logical position
+ * ctx_lens[b] - n_tokens + i, i.e. ctx_lens counts the appended tokens, as it does for
+ * paged_decode (which takes the current token's K/V from the cache).  Positions below 0 are
+ * skipped, as are positions whose table entry is outside [0, num_pages).
+ *   shape       B, Hkv, D (128, 256 or 512), page_size, num_pages, max_pages_per_seq and
+ *               dtype as for paged_decode (Hq is not used)
+ *   k_new,      device (B, n_tokens, Hkv, D) with attn_tensor strides (batch, token, head)
+ *   v_new
+ *   k_cache,    device (num_pages, page_size, Hkv, D), strides (page, slot, head); written
+ *   v_cache
+ *   block_table, ctx_lens  as for paged_decode (ctx_lens clamped the same way)
+ * Sequences whose positions map to the same page slot race; a table that gives each
+ * sequence its own pages (as a page pool does) has none.
+ */
+attn_status paged_kv_append(const attn_decode_shape* shape, int32_t n_tokens,
+                            attn_tensor k_new, attn_tensor v_new,
+                            attn_tensor k_cache, attn_tensor v_cache,
+                            const int32_t* block_table, const int32_t* ctx_lens, void* stream);
+
+/*
+ * paged_kv_gather: the first n_tokens logical tokens of each sequence's cache, contiguous:
+ * row (b, t) of k_out/v_out is token t of sequence b for t < ctx_lens[b], zeros for
+ * t >= ctx_lens[b] or a table entry outside [0, num_pages).  With attn_fwd_chunk over the
+ * gathered keys (k_pos0 = 0) this is the paged prefill of a chunk of new queries.
+ *   k_out, v_out  device (B, n_tokens, Hkv, D) with attn_tensor strides; written
+ * Other arguments as for paged_kv_append.
+ */
+attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens,
+                            attn_tensor k_cache, attn_tensor v_cache,
+                            const int32_t* block_table, const int32_t* ctx_lens,
+                            attn_tensor k_out, attn_tensor v_out, void* stream);
 
 /* Workspace sizes in bytes.  varlen: 0 dense, 1 pad_mask, 2 cu_seqlens; causal and
  * window as in the call.  Return 0 for arguments that the matching call would reject. */

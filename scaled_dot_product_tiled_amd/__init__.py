@@ -5,7 +5,7 @@ libattn.so by ``scaled_dot_product_tiled_amd.build``); this package only marshal
 torch tensors into those calls.
 """
 from .binding import (attn_bwd, attn_bwd_chunk, attn_fwd, attn_fwd_chunk, attn_lse_merge,  # noqa: F401
-                      load_library, paged_decode)
+                      load_library, paged_decode, paged_kv_append, paged_kv_gather)
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "paged_decode",
-           "load_library"]
+           "paged_kv_append", "paged_kv_gather", "load_library"]

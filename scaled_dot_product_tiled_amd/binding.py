@@ -52,6 +52,7 @@ class AttnDecodeShape(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "paged_decode",
+           "paged_kv_append", "paged_kv_gather",
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read")
@@ -91,6 +92,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_decode.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int64, ctypes.c_int64, AttnTensor, AttnTensor,
                                  vp, vp, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz, vp]
     lib.paged_decode.restype = ctypes.c_int
+    lib.paged_kv_append.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, AttnTensor, AttnTensor,
+                                    vp, vp, vp]
+    lib.paged_kv_append.restype = ctypes.c_int
+    lib.paged_kv_gather.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, vp, vp, AttnTensor,
+                                    AttnTensor, vp]
+    lib.paged_kv_gather.restype = ctypes.c_int
     lib.attn_fwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
     lib.attn_fwd_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -419,6 +426,68 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                           out.stride(1), workspace.data_ptr(), nbytes, _stream())
     _check(st, "paged_decode")
     return out
+
+
+def _paged_shape(k_cache, block_table, B, D, dtype):
+    num_pages, page_size, Hkv, Dc = k_cache.shape
+    if Dc != D:
+        raise ValueError("token rows and cache rows have different head_dim")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be (B, max_pages_per_seq), got {tuple(block_table.shape)}")
+    return AttnDecodeShape(B, Hkv, Hkv, D, page_size, num_pages, block_table.shape[1], _DT16[dtype])
+
+
+def _paged_checks(k_cache, v_cache, block_table, ctx_lens, B):
+    _half(k_cache, "k_cache")
+    _half(v_cache, "v_cache", k_cache.dtype)
+    _expect(v_cache, tuple(k_cache.shape), "v_cache")
+    for t, n in ((block_table, "block_table"), (ctx_lens, "ctx_lens")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 device tensor")
+    _expect(ctx_lens, (B,), "ctx_lens")
+
+
+def paged_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_table: torch.Tensor, ctx_lens: torch.Tensor) -> None:
+    """Writes the n newest tokens k_new/v_new (B, n, Hkv, D) of each sequence into the paged caches
+    (num_pages, page_size, Hkv, D): token i of sequence b goes to position ctx_lens[b] - n + i."""
+    lib = load_library()
+    B, n, Hkv, D = k_new.shape
+    _paged_checks(k_cache, v_cache, block_table, ctx_lens, B)
+    _half(k_new, "k_new", k_cache.dtype)
+    _half(v_new, "v_new", k_cache.dtype)
+    _expect(v_new, tuple(k_new.shape), "v_new")
+    shape = _paged_shape(k_cache, block_table, B, D, k_cache.dtype)
+    if Hkv != shape.Hkv:
+        raise ValueError("token rows and cache rows have different kv head counts")
+    st = lib.paged_kv_append(ctypes.byref(shape), n, _tensor(k_new, False), _tensor(v_new, False),
+                             _tensor(k_cache, False), _tensor(v_cache, False), block_table.data_ptr(),
+                             ctx_lens.data_ptr(), _stream())
+    _check(st, "paged_kv_append")
+
+
+def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                    n_tokens: int, k_out: Optional[torch.Tensor] = None,
+                    v_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The first n_tokens cached tokens of each sequence as contiguous (B, n_tokens, Hkv, D) K and V
+    (zeros past ctx_lens[b])."""
+    lib = load_library()
+    B = block_table.shape[0]
+    _, _, Hkv, D = k_cache.shape
+    _paged_checks(k_cache, v_cache, block_table, ctx_lens, B)
+    if k_out is None:
+        k_out = torch.empty((B, n_tokens, Hkv, D), device=k_cache.device, dtype=k_cache.dtype)
+    if v_out is None:
+        v_out = torch.empty_like(k_out)
+    for t, nm in ((k_out, "k_out"), (v_out, "v_out")):
+        _half(t, nm, k_cache.dtype)
+        _expect(t, (B, n_tokens, Hkv, D), nm)
+    shape = _paged_shape(k_cache, block_table, B, D, k_cache.dtype)
+    st = lib.paged_kv_gather(ctypes.byref(shape), int(n_tokens), _tensor(k_cache, False), _tensor(v_cache, False),
+                             block_table.data_ptr(), ctx_lens.data_ptr(), _tensor(k_out, False),
+                             _tensor(v_out, False), _stream())
+    _check(st, "paged_kv_gather")
+    return k_out, v_out
 
 
 def profile(on: bool) -> None:

@@ -13,7 +13,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_merge.hip", "varlen_prep.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_merge.hip", "paged_kv.hip", "varlen_prep.hip",
+           "attn_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

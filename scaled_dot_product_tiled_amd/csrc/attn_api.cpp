@@ -569,6 +569,54 @@ attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D, attn_tens
   return launch("lse_merge", s, a.rows, [&] { return attn::launch_lse_merge(a, D, s); });
 }
 
+// Shared checks and arguments of paged_kv_append and paged_kv_gather.
+static attn_status paged_copy(const attn_decode_shape* shape, int32_t n, attn_tensor k_tok, attn_tensor v_tok,
+                              attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
+                              const int32_t* ctx_lens, int gather, const char* name, void* stream) {
+  if (shape == nullptr) return ATTN_ERR_INVALID_ARG;
+  const attn_decode_shape& sh = *shape;
+  if (sh.B < 0 || n < 0 || sh.Hkv <= 0 || sh.num_pages <= 0 || sh.max_pages_per_seq <= 0 || sh.page_size <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if ((sh.D != 128 && sh.D != 256 && sh.D != 512) || !dtype16_ok(sh.dtype)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)sh.max_pages_per_seq * sh.page_size > INT_MAX / 2 || (int64_t)sh.B * n * sh.Hkv >= INT_MAX / 4)
+    return ATTN_ERR_UNSUPPORTED;
+  if (block_table == nullptr || ctx_lens == nullptr) return ATTN_ERR_INVALID_ARG;
+  attn_status st;
+  if ((st = check_tensor(k_tok, false)) || (st = check_tensor(v_tok, false)) || (st = check_tensor(k_cache, false)) ||
+      (st = check_tensor(v_cache, false)))
+    return st;
+  if (sh.B == 0 || n == 0) return ATTN_OK;
+  attn::PagedCopyArgs a = {};
+  a.tk = static_cast<__bf16*>(k_tok.ptr);
+  a.tv = static_cast<__bf16*>(v_tok.ptr);
+  a.kc = static_cast<__bf16*>(k_cache.ptr);
+  a.vc = static_cast<__bf16*>(v_cache.ptr);
+  a.table = block_table;
+  a.ctx = ctx_lens;
+  a.tk_sb = k_tok.stride_b;
+  a.tk_ss = k_tok.stride_s;
+  a.tk_sh = k_tok.stride_h;
+  a.tv_sb = v_tok.stride_b;
+  a.tv_ss = v_tok.stride_s;
+  a.tv_sh = v_tok.stride_h;
+  a.kc_sp = k_cache.stride_b;
+  a.kc_ss = k_cache.stride_s;
+  a.kc_sh = k_cache.stride_h;
+  a.vc_sp = v_cache.stride_b;
+  a.vc_ss = v_cache.stride_s;
+  a.vc_sh = v_cache.stride_h;
+  a.B = sh.B;
+  a.n = n;
+  a.Hkv = sh.Hkv;
+  a.D = sh.D;
+  a.page_size = sh.page_size;
+  a.num_pages = sh.num_pages;
+  a.max_pages = sh.max_pages_per_seq;
+  a.gather = gather;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch(name, s, 1, [&] { return attn::launch_paged_kv_copy(a, s); });
+}
+
 size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {
   if (s == nullptr || s->B < 0 || s->Hq <= 0 || s->Hkv <= 0 || s->D != 128 || s->page_size != 16 ||
       s->max_pages_per_seq <= 0 || !dtype16_ok(s->dtype))
@@ -636,6 +684,20 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   hipError_t e = timed("decode_split", s, [&] { return attn::launch_decode_split(a, sh.D, s); });
   if (e != hipSuccess) return hip_status(e);
   return hip_status(timed("decode_merge", s, [&] { return attn::launch_decode_merge(a, sh.D, s); }));
+}
+
+attn_status paged_kv_append(const attn_decode_shape* shape, int32_t n_tokens, attn_tensor k_new, attn_tensor v_new,
+                            attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
+                            const int32_t* ctx_lens, void* stream) {
+  return paged_copy(shape, n_tokens, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, 0, "paged_kv_append",
+                    stream);
+}
+
+attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens, attn_tensor k_cache,
+                            attn_tensor v_cache, const int32_t* block_table, const int32_t* ctx_lens,
+                            attn_tensor k_out, attn_tensor v_out, void* stream) {
+  return paged_copy(shape, n_tokens, k_out, v_out, k_cache, v_cache, block_table, ctx_lens, 1, "paged_kv_gather",
+                    stream);
 }
 
 const char* attn_status_str(attn_status status) {

@@ -85,6 +85,21 @@ struct DecodeArgs {
   int f16;            // 16-bit tensors are IEEE half (else bfloat16)
 };
 
+// Paged KV copies (append: token tensor -> cache pages; gather: cache pages -> token tensor).
+// Token tensors are (B, n, Hkv, D) with element strides; caches (num_pages, page_size, Hkv, D).
+struct PagedCopyArgs {
+  __bf16* tk;  // keys of the n tokens per sequence (read by append, written by gather)
+  __bf16* tv;
+  __bf16* kc;  // caches (written by append, read by gather)
+  __bf16* vc;
+  const int32_t* table;
+  const int32_t* ctx;  // tokens per sequence, the appended ones included
+  int64_t tk_sb, tk_ss, tk_sh, tv_sb, tv_ss, tv_sh;
+  int64_t kc_sp, kc_ss, kc_sh, vc_sp, vc_ss, vc_sh;
+  int B, n, Hkv, D, page_size, num_pages, max_pages;
+  int gather;
+};
+
 // In-place log-sum-exp merge of a partial result (o_part, lse_part) into (o, lse), rows
 // (b, s, h) of fp32 O (B, S, H, D) with element strides and fp32 LSE (B, H, S) contiguous;
 // optionally also the merged O rounded to bf16 into out (strides r_*).
@@ -143,6 +158,7 @@ hipError_t launch_bwd_kv_reduce(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, int D, hipStream_t stream);
+hipError_t launch_paged_kv_copy(const PagedCopyArgs& a, hipStream_t stream);
 
 // Tile geometry used by the host planner.
 constexpr int kFwdRows = 128;   // query rows per forward workgroup

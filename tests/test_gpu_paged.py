@@ -1,0 +1,177 @@
+"""GPU checks of the paged cache calls (paged_kv_append, paged_kv_gather) through the C ABI,
+a decode step captured in a HIP graph and replayed, and a paged prefill (gather + chunk-pair
+forward) against the float64 oracle.
+
+Append and gather move bits, so they are compared bit for bit with the oracle's scatter and
+gather.  The graph replays are compared bit for bit with the same calls made eagerly (same
+kernels, same inputs) and with the oracle within the usual tolerance.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import DECODE_WORKLOADS, bits_to_f64, make_decode_inputs, normal_16, stream
+from tests.gpu_util import LSE_MAX_ABS, O_MAX_ABS, all_finite, dev, host, host_bits, max_abs
+
+pytestmark = pytest.mark.gpu
+
+import scaled_dot_product_tiled_amd as sdpt  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _with_room(inp, w, n):
+    """The decode inputs with every table row extended so that n more tokens fit (fresh pool
+    pages appended at the end of the caches)."""
+    ctx0 = inp["ctx_lens"].astype(np.int64)
+    ctx1 = ctx0 + n
+    table = np.concatenate([inp["block_table"], np.full((w.B, -(-n // w.page_size) + 1), -1, np.int32)], axis=1)
+    kc, vc = inp["k_cache"], inp["v_cache"]
+    pool = kc.shape[0]
+    extra = 0
+    for b in range(w.B):
+        for p in range(int(-(-ctx1[b] // w.page_size))):
+            if table[b, p] < 0:
+                table[b, p] = pool + extra
+                extra += 1
+    fill = normal_16(stream(9, w.wid, 7), (extra,) + kc.shape[1:], 1.0, w.dtype)
+    kc = np.concatenate([kc, fill])
+    vc = np.concatenate([vc, fill[::-1].copy()])
+    return table, kc, vc, ctx1.astype(np.int32)
+
+
+@pytest.mark.parametrize("n,dtype,D", [(1, "bf16", 128), (5, "bf16", 128), (3, "f16", 256), (20, "bf16", 512)])
+def test_append_and_gather_move_exact_bits(n, dtype, D):
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=6, Hkv=2, D=D, ctx_range=(0, 70), dtype=dtype)
+    inp = make_decode_inputs(w, seed=3)
+    table, kc, vc, ctx1 = _with_room(inp, w, n)
+    table[1, :] = -1                                   # a sequence without pages: skipped / zeros
+    table[2, 0] = kc.shape[0] + 5                      # out-of-range page id: skipped / zeros
+    new_k = normal_16(stream(4, w.wid, 0), (w.B, n, w.Hkv, w.D), 1.0, dtype)
+    new_v = normal_16(stream(4, w.wid, 1), (w.B, n, w.Hkv, w.D), 1.0, dtype)
+    say(f"[paged append] n={n} dtype={dtype} D={D} ctx={ctx1.tolist()}")
+    k_d, v_d = dev(kc, dtype), dev(vc, dtype)
+    t_d = torch.from_numpy(table).to("cuda:0")
+    c_d = torch.from_numpy(ctx1).to("cuda:0")
+    sdpt.paged_kv_append(dev(new_k, dtype), dev(new_v, dtype), k_d, v_d, t_d, c_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(k_d), oracle.paged_append(kc, table, ctx1, new_k, w.page_size))
+    assert np.array_equal(host_bits(v_d), oracle.paged_append(vc, table, ctx1, new_v, w.page_size))
+    # gather the first m tokens back: cached tokens where the page exists, zeros elsewhere
+    m = int(ctx1.max()) + 3
+    gk, gv = sdpt.paged_kv_gather(k_d, v_d, t_d, c_d, m)
+    torch.cuda.synchronize()
+    kk, vv = host_bits(k_d), host_bits(v_d)
+    gkb, gvb = host_bits(gk), host_bits(gv)
+    for b in range(w.B):
+        for t in range(m):
+            page = table[b, t // w.page_size] if t < ctx1[b] else -1
+            ok = 0 <= page < kk.shape[0]
+            ek = kk[page, t % w.page_size] if ok else 0
+            ev = vv[page, t % w.page_size] if ok else 0
+            assert np.array_equal(gkb[b, t], np.broadcast_to(ek, (w.Hkv, w.D))), (b, t)
+            assert np.array_equal(gvb[b, t], np.broadcast_to(ev, (w.Hkv, w.D))), (b, t)
+
+
+def test_decode_step_captured_in_a_graph_replays_like_eager_calls():
+    """One decode step = append the current token's K/V, then paged_decode; captured once in a
+    HIP graph (no allocation, no memset inside) and replayed for three steps with new inputs
+    copied into the captured buffers; every replay equals the eager calls bit for bit and the
+    oracle within tolerance."""
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=8, ctx_range=(40, 300))
+    inp = make_decode_inputs(w, seed=8)
+    steps = 3
+    table, kc, vc, _ = _with_room(inp, w, steps)
+    ctx0 = inp["ctx_lens"].astype(np.int32)
+    k_d, v_d = dev(kc), dev(vc)
+    k_eager, v_eager = k_d.clone(), v_d.clone()
+    t_d = torch.from_numpy(table).to("cuda:0")
+    q_s = torch.empty((w.B, w.Hq, w.D), device="cuda:0", dtype=torch.bfloat16)
+    kn_s = torch.empty((w.B, 1, w.Hkv, w.D), device="cuda:0", dtype=torch.bfloat16)
+    vn_s = torch.empty_like(kn_s)
+    ctx_s = torch.empty(w.B, device="cuda:0", dtype=torch.int32)
+    out_s = torch.empty_like(q_s)
+    ws = torch.empty(max(1 << 20, 4 * w.B * w.Hq * 64 * (w.D + 2)), device="cuda:0", dtype=torch.uint8)
+
+    def step(kcache, vcache, out):
+        sdpt.paged_kv_append(kn_s, vn_s, kcache, vcache, t_d, ctx_s)
+        sdpt.paged_decode(q_s, kcache, vcache, t_d, ctx_s, scale=w.scale, out=out, workspace=ws)
+
+    def load(i):
+        q_s.copy_(dev(normal_16(stream(20 + i, w.wid, 0), (w.B, w.Hq, w.D))))
+        kn_s.copy_(dev(normal_16(stream(20 + i, w.wid, 1), (w.B, 1, w.Hkv, w.D))))
+        vn_s.copy_(dev(normal_16(stream(20 + i, w.wid, 2), (w.B, 1, w.Hkv, w.D))))
+        ctx_s.copy_(torch.from_numpy(ctx0 + i + 1).to("cuda:0"))
+
+    load(0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):             # warm-up outside the graph (first launches load code)
+        step(k_d.clone(), v_d.clone(), torch.empty_like(q_s))
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(k_d, v_d, out_s)
+    torch.cuda.synchronize()
+    # the capture ran nothing: restore the caches and replay step by step
+    k_d.copy_(dev(kc))
+    v_d.copy_(dev(vc))
+    kc_ref, vc_ref = bits_to_f64(kc, "bf16"), bits_to_f64(vc, "bf16")
+    for i in range(steps):
+        say(f"[graph decode] replay {i}")
+        load(i)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_s.clone()
+        eager = torch.empty_like(q_s)
+        step(k_eager, v_eager, eager)      # the same step made with eager calls on other caches
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(got), host_bits(eager)), i
+        assert np.array_equal(host_bits(k_d), host_bits(k_eager)) and np.array_equal(host_bits(v_d),
+                                                                                     host_bits(v_eager))
+        ctx = ctx0 + i + 1
+        kc_ref = oracle.paged_append(kc_ref, table, ctx, host(kn_s), w.page_size)
+        vc_ref = oracle.paged_append(vc_ref, table, ctx, host(vn_s), w.page_size)
+        ref = oracle.paged_decode(host(q_s), kc_ref, vc_ref, table, ctx, w.scale, w.page_size)
+        assert all_finite(got)
+        assert max_abs(host(got), ref) <= O_MAX_ABS, i
+
+
+@pytest.mark.parametrize("D,prev,n", [(256, 300, 77), (512, 0, 130), (512, 513, 64)])
+def test_paged_prefill_matches_oracle(D, prev, n):
+    """A chunk of n new query tokens after prev cached ones: append the chunk's K/V to the pages,
+    gather the prev + n tokens, run attn_fwd_chunk at q_pos0 = prev against them; rows equal the
+    last n rows of causal attention over the whole sequence."""
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=1, Hq=8, Hkv=2, D=D, ctx_range=(max(prev, 1), max(prev, 1)))
+    inp = make_decode_inputs(w, seed=10, ctx_lens=np.array([prev], dtype=np.int32))
+    table, kc, vc, ctx1 = _with_room(inp, w, n)
+    q_new = normal_16(stream(11, w.wid, 0), (1, n, w.Hq, D))
+    new_k = normal_16(stream(11, w.wid, 1), (1, n, w.Hkv, D))
+    new_v = normal_16(stream(11, w.wid, 2), (1, n, w.Hkv, D))
+    say(f"[paged prefill] D={D} prev={prev} n={n}")
+    k_d, v_d = dev(kc), dev(vc)
+    t_d = torch.from_numpy(table).to("cuda:0")
+    c_d = torch.from_numpy(ctx1).to("cuda:0")
+    sdpt.paged_kv_append(dev(new_k), dev(new_v), k_d, v_d, t_d, c_d)
+    L = prev + n
+    kg, vg = sdpt.paged_kv_gather(k_d, v_d, t_d, c_d, L)
+    o, lse = sdpt.attn_fwd_chunk(dev(q_new), kg, vg, prev, 0, scale=1.0 / np.sqrt(D), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert all_finite(o, lse)
+    kf = np.concatenate([oracle.gather_pages(bits_to_f64(kc), table[0], prev, w.page_size),
+                         bits_to_f64(new_k)[0]])[None]
+    vf = np.concatenate([oracle.gather_pages(bits_to_f64(vc), table[0], prev, w.page_size),
+                         bits_to_f64(new_v)[0]])[None]
+    qf = np.zeros((1, L, w.Hq, D))
+    qf[0, prev:] = bits_to_f64(q_new)[0]
+    ro, rl = oracle.attention_forward(qf, kf, vf, 1.0 / np.sqrt(D), True, 0)
+    assert max_abs(host(o), ro[:, prev:]) <= O_MAX_ABS
+    assert max_abs(host(lse), rl[:, :, prev:]) <= LSE_MAX_ABS

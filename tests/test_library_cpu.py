@@ -187,3 +187,23 @@ def test_chunk_and_merge_checks():
     assert merge(B=0, odt=1) == INVALID                                 # the final output is 16-bit
     assert merge(B=0, out=_t()) == OK
     assert lib.attn_last_hip_error() == 0
+
+
+def test_paged_cache_call_checks():
+    lib = load_library()
+    d = AttnDecodeShape(4, 32, 8, 128, 16, 100, 8)
+    kc = AttnTensor(0x10000, 16 * 8 * 128, 8 * 128, 128)
+    tok = AttnTensor(0x20000, 8 * 128, 8 * 128, 128)
+
+    def app(shape=d, n=1, table=0x3000, ctx=0x4000, k=None):
+        return lib.paged_kv_append(ctypes.byref(shape), n, k or tok, tok, kc, kc, table, ctx, None)
+
+    def gat(shape=d, n=8, table=0x3000, ctx=0x4000):
+        return lib.paged_kv_gather(ctypes.byref(shape), n, kc, kc, table, ctx, tok, tok, None)
+    assert app(n=-1) == INVALID
+    assert app(table=0) == INVALID and gat(ctx=0) == INVALID
+    assert app(k=AttnTensor(0x20008, 1024, 1024, 128)) == INVALID                  # misaligned
+    assert app(AttnDecodeShape(4, 32, 8, 64, 16, 100, 8)) == UNSUPPORTED           # head_dim
+    assert gat(AttnDecodeShape(4, 32, 8, 128, 16, 100, 8, 1)) == UNSUPPORTED       # fp32 cache
+    assert app(n=0) == OK and gat(AttnDecodeShape(0, 32, 8, 512, 16, 100, 8)) == OK  # nothing to move
+    assert lib.attn_last_hip_error() == 0

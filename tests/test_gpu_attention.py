@@ -165,6 +165,43 @@ def test_packed_cu_seqlens_matches_oracle_and_pad_mask():
         assert np.array_equal(host_bits(t_pk), pack_rows(host_bits(t_pad), lengths))
 
 
+def test_packed_documents_are_document_causal():
+    """Several documents packed into each row of a batch (the packing that the first page's CP
+    path routes to varlen chunks, section Integration): flattening the rows and giving every
+    document its own cu_seqlens entry makes attention document-causal (no token sees another
+    document), which the oracle computes document by document."""
+    rows = [[120, 7, 300], [1, 250, 90, 33]]                 # documents per packed row
+    docs = np.array([n for r in rows for n in r], dtype=np.int32)
+    total = int(docs.sum())
+    w = AttnWorkload(125, "packed documents", 1, total, 8, 2, 512)
+    inp = make_attention_inputs(w, seed=11)
+    cu = lengths_to_cu_seqlens(docs)
+    say(f"[packed documents] {docs.tolist()}")
+    q, k, v, do = (dev(inp[x][0]) for x in ("q", "k", "v", "do"))   # (total, H, D)
+    cu_d = torch.from_numpy(cu).to("cuda:0")
+    kw = dict(scale=w.scale, causal=True, window=0, cu_seqlens=cu_d, max_seqlen=int(docs.max()))
+    o, lse = sdpt.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = sdpt.attn_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    f = {x: bf16_bits_to_f64(inp[x][0]) for x in ("q", "k", "v", "do")}
+    ro, rl = oracle.attention_forward_packed(f["q"], f["k"], f["v"], cu, w.scale, True, 0)
+    rq, rk, rv = oracle.attention_backward_packed(f["q"], f["k"], f["v"], f["do"], cu, w.scale, True, 0)
+    assert all_finite(o, lse, dq, dk, dv)
+    assert max_abs(host(o), ro) <= O_MAX_ABS
+    assert max_abs(host(lse), rl) <= LSE_MAX_ABS
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        assert rel_l2(host(a), r) <= GRAD_REL_L2
+    # a document's rows do not depend on the other documents: change everything else
+    inp2 = {x: inp[x].copy() for x in ("q", "k", "v")}
+    lo, hi = int(cu[4]), int(cu[5])                          # document 4 (250 tokens)
+    for x in ("k", "v"):
+        inp2[x][0, :lo] ^= np.uint16(0x0040)
+        inp2[x][0, hi:] ^= np.uint16(0x0040)
+    o2, _ = sdpt.attn_fwd(*(dev(inp2[x][0]) for x in ("q", "k", "v")), **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(o)[lo:hi], host_bits(o2)[lo:hi])
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads: sampled rows + one complete (batch, kv head) unit
 # ---------------------------------------------------------------------------

@@ -10,8 +10,9 @@ the C ABI.  Reported:
             U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
   other_workloads  forward / backward TFLOP/s of the sliding-window (D=256, W=1024) and padded
-            varlen (B=8, lengths U{512..8192}, D=512) workloads, and of one context-parallel rank's
-            chunk pairs (16k tokens in 8 chunks, D=512), not part of the timed step;
+            varlen (B=8, lengths U{512..8192}, D=512) workloads, of one context-parallel rank's
+            chunk pairs (16k tokens in 8 chunks, D=512) and of the step's workload in IEEE half,
+            not part of the timed step;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores.
 Prints one JSON line.
 """
@@ -33,10 +34,10 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 # HBM traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy)
 # of each kernel on this workload; a record counts only while its kernel source is unchanged.
 TRAFFIC = {
-    "attn_fwd": ("profiles/attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512"),
-    "bwd_dkdv": ("profiles/bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512>"),
-    "bwd_dq": ("profiles/bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2>"),
-    "decode_split": ("profiles/decode_split_d128_B64_traffic.txt", "decode_split_kernel<4>"),
+    "attn_fwd": ("profiles/attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512,32,false,false,false>"),
+    "bwd_dkdv": ("profiles/bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512,false,false>"),
+    "bwd_dq": ("profiles/bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2,false>"),
+    "decode_split": ("profiles/decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false>"),
 }
 
 
@@ -55,19 +56,21 @@ def causal_pairs(S, window=0):
     return int(cnt.sum())
 
 
-def other_workload(name, steps, stream):
-    """Forward and backward times of the sliding-window and padded-varlen workloads (device-side
-    seeded draws of the same shapes and distributions; lengths and masks from synth)."""
+def other_workload(name, steps, stream, **changes):
+    """Forward and backward times of the sliding-window and padded-varlen workloads, or of a workload
+    with some fields changed (device-side seeded draws of the same shapes and distributions;
+    lengths and masks from synth)."""
     import torch
     import scaled_dot_product_tiled_amd as sdpt
     from synth import ATTN_WORKLOADS
     from synth import draw_lengths, lengths_to_pad_mask
-    w = ATTN_WORKLOADS[name]
+    w = ATTN_WORKLOADS[name].scaled(**changes)
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(1234 + w.wid)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
 
     def draw(shape, std):
-        return (torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32) * std).to(torch.bfloat16)
+        return (torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32) * std).to(dt)
 
     q = draw((w.B, w.S, w.Hq, w.D), w.qk_std)
     k = draw((w.B, w.S, w.Hkv, w.D), w.qk_std)
@@ -97,7 +100,7 @@ def other_workload(name, steps, stream):
     ms_f = time_events(fwd, steps, stream)
     ms_b = time_events(bwd, steps, stream)
     ff = 4.0 * w.D * pairs
-    res = {"workload": w.name, "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+    res = {"workload": w.name + ("" if w.dtype == "bf16" else f" {w.dtype}"), "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
            "fwd_tflops": round(ff / ms_f / 1e9, 2), "bwd_tflops": round(2.5 * ff / ms_b / 1e9, 2),
            "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2)}
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
@@ -343,6 +346,7 @@ def main():
     others = {} if args.no_other else {n: other_workload(n, 5, stream) for n in ("window_d256", "varlen_d512")}
     if not args.no_other:
         others["ring_cp8_d512"] = ring_workload(5, stream)
+        others["full_d512_f16"] = other_workload("full_d512", 5, stream, dtype="f16")
 
     out = {
         "metric": "causal attn fwd+bwd TFLOP/s @d=512 (% bf16 MFMA peak); decode HBM GB/s",

@@ -130,21 +130,21 @@ COMMANDS = """Commands (cd /tmp && export TMPDIR=/tmp first; R = repository root
 
 # (file, kernel name, source, what, algorithmic bytes) of each traffic summary
 TRAFFIC_SUMMARIES = [
-    ("attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512", "scaled_dot_product_tiled_amd/csrc/attn_fwd.hip",
+    ("attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512,32,false,false,false>", "scaled_dot_product_tiled_amd/csrc/attn_fwd.hip",
      "forward kernel, causal GQA B=2 S=4096 Hq=32 Hkv=4 D=512 (bench.py workload)",
      "Algorithmic bytes: Q, K, V read once (268 + 33.5 + 33.5 MB) and O, LSE written once (268 + 1 MB).  "
      "The fetch figure counts every L2 miss sent to the fabric (the 256 MB last-level cache can serve part "
      "of it); above the algorithmic reads it is the K/V re-reads of the query-row tiles of each head group."),
-    ("bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
+    ("bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512,false,false>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
      "dK/dV kernel of the backward, causal GQA B=2 S=4096 Hq=32 Hkv=4 D=512 (bench.py workload)",
      "Algorithmic bytes: Q, dO read once (268 MB each), K, V (33.5 MB each), LSE and delta (1 MB each); "
      "writes dK, dV (33.5 MB each) and the stored dS blocks (1.107 GB).  Fetch above the algorithmic reads "
      "is the Q / dO re-reads of the 64 key tiles of each head group that miss in L2."),
-    ("bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
+    ("bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2,false>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
      "dQ kernel of the backward (dQ = scale dS K over the stored dS blocks, two head_dim halves), same workload",
      "Algorithmic bytes: dS blocks read once (1.107 GB), K (33.5 MB); dQ written once (268 MB).  Each dS "
      "block is read by both head_dim halves; the second read is meant to hit in L2."),
-    ("decode_split_d128_B64_traffic.txt", "decode_split_kernel<4>", "scaled_dot_product_tiled_amd/csrc/attn_decode.hip",
+    ("decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false>", "scaled_dot_product_tiled_amd/csrc/attn_decode.hip",
      "paged decode split kernel, B=64 Hq=32 Hkv=8 D=128, 16-token pages, contexts U{512..4096} "
      "(bench.py decode workload)",
      "Algorithmic bytes: K and V of every context token once (619.6 MB per launch, the bench's "

@@ -9,7 +9,7 @@ the C ABI.  Reported:
   decode    paged single-token decode (B=64, Hq=32, Hkv=8, D=128, 16-token pages, contexts
             U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
-  other_workloads  forward / backward TFLOP/s of the sliding-window (D=256, W=1024) and padded
+  other_workloads  (median of per-call HIP-event timings) forward / backward TFLOP/s of the sliding-window (D=256, W=1024) and padded
             varlen (B=8, lengths U{512..8192}, D=512) workloads, of one context-parallel rank's
             chunk pairs (16k tokens in 8 chunks, D=512) and of the step's workload in IEEE half,
             not part of the timed step;
@@ -56,7 +56,7 @@ def causal_pairs(S, window=0):
     return int(cnt.sum())
 
 
-def other_workload(name, steps, stream, **changes):
+def other_workload(name, steps, stream, softcap=0.0, **changes):
     """Forward and backward times of the sliding-window and padded-varlen workloads, or of a workload
     with some fields changed (device-side seeded draws of the same shapes and distributions;
     lengths and masks from synth)."""
@@ -86,7 +86,7 @@ def other_workload(name, steps, stream, **changes):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.S), device="cuda:0", dtype=torch.float32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    kw = dict(scale=w.scale, causal=True, window=w.window, pad_mask=pm)
+    kw = dict(scale=w.scale, causal=True, window=w.window, pad_mask=pm, softcap=softcap)
 
     def fwd():
         sdpt.attn_fwd(q, k, v, out=o, lse=lse, **kw)
@@ -97,10 +97,11 @@ def other_workload(name, steps, stream, **changes):
     fwd()
     bwd()
     torch.cuda.synchronize()
-    ms_f = time_events(fwd, steps, stream)
-    ms_b = time_events(bwd, steps, stream)
+    ms_f = time_median(fwd, steps, stream)
+    ms_b = time_median(bwd, steps, stream)
     ff = 4.0 * w.D * pairs
-    res = {"workload": w.name + ("" if w.dtype == "bf16" else f" {w.dtype}"), "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+    res = {"workload": w.name + ("" if w.dtype == "bf16" else f" {w.dtype}") + (f" softcap {softcap}" if softcap else ""),
+           "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
            "fwd_tflops": round(ff / ms_f / 1e9, 2), "bwd_tflops": round(2.5 * ff / ms_b / 1e9, 2),
            "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2)}
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
@@ -155,8 +156,8 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     fwd()
     bwd()
     torch.cuda.synchronize()
-    ms_f = time_events(fwd, steps, stream)
-    ms_b = time_events(bwd, steps, stream)
+    ms_f = time_median(fwd, steps, stream)
+    ms_b = time_median(bwd, steps, stream)
     sdpt.binding.profile(True)
     for _ in range(steps):
         fwd()
@@ -173,6 +174,52 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
     del q, do, k, v, acc_o, part, acc_l, part_l, o, dq, dk, dv, ws
     return res
+
+
+def paged_prefill_workload(steps, stream, B=1, prev=6144, n=2048, Hq=32, Hkv=4, D=512):
+    """A 2048-token chunk of new queries after 6144 cached tokens (D=512, GQA 32/4, 16-token pages
+    permuted over the pool): append the chunk's K/V to the pages, gather the 8192 tokens, run the
+    chunk-pair forward at q_pos0 = 6144.  TFLOP/s of the attention (causal-counted pairs) over the
+    time of the three calls."""
+    import torch
+    import scaled_dot_product_tiled_amd as sdpt
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(99)
+    L = prev + n
+    pages = -(-L // 16)
+    pool = int(1.5 * pages)
+    kc = torch.randn((pool, 16, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    vc = torch.randn((pool, 16, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    perm = torch.randperm(pool, generator=gen, device="cuda:0")[:pages].to(torch.int32)
+    table = perm.reshape(1, pages).repeat(B, 1).contiguous()
+    ctx = torch.full((B,), L, device="cuda:0", dtype=torch.int32)
+    q = torch.randn((B, n, Hq, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    kn = torch.randn((B, n, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    vn = torch.randn((B, n, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    kg = torch.empty((B, L, Hkv, D), device="cuda:0", dtype=torch.bfloat16)
+    vg = torch.empty_like(kg)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, n), device="cuda:0", dtype=torch.float32)
+    scale = 1.0 / math.sqrt(D)
+
+    def run():
+        sdpt.paged_kv_append(kn, vn, kc, vc, table, ctx)
+        sdpt.paged_kv_gather(kc, vc, table, ctx, L, k_out=kg, v_out=vg)
+        sdpt.attn_fwd_chunk(q, kg, vg, prev, 0, scale=scale, out=o, lse=lse)
+
+    run()
+    torch.cuda.synchronize()
+    ms = time_median(run, steps, stream)
+    sdpt.binding.profile(True)
+    for _ in range(steps):
+        run()
+    sdpt.binding.profile(False)
+    kern = {k: {"launches": c, "ms_avg": round(t / c, 4)} for k, (c, t) in sdpt.binding.profile_read().items()}
+    pairs = (n * prev + n * (n + 1) // 2) * Hq * B
+    ff = 4.0 * D * pairs
+    return {"workload": f"paged prefill d{D}: {n} new tokens after {prev} cached (Hq{Hq} Hkv{Hkv}, 16-token pages)",
+            "pairs": pairs, "ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2),
+            "frac": round(ff / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "kernels": kern}
 
 
 def parse():
@@ -203,6 +250,19 @@ def time_events(fn, iters, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / iters
+
+
+def time_median(fn, iters, stream):
+    """Median milliseconds of one fn() call over iters calls, each timed with its own pair of HIP
+    events on `stream` (robust to a rare stall of the device that one long window would absorb)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    evs[-1][1].synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
 def cpu_baseline(units):
@@ -349,6 +409,8 @@ def main():
         others["ring_cp8_d512"] = ring_workload(5, stream)
         others["window_d256"] = other_workload("window_d256", 5, stream)
         others["full_d512_f16"] = other_workload("full_d512", 5, stream, dtype="f16")
+        others["full_d512_softcap"] = other_workload("full_d512", 5, stream, softcap=30.0)
+        others["paged_prefill_d512"] = paged_prefill_workload(5, stream)
         others["varlen_d512"] = other_workload("varlen_d512", 5, stream)
 
     out = {

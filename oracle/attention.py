@@ -406,7 +406,7 @@ def paged_append(cache, block_table, ctx_lens, new, page_size=16):
     return out
 
 
-def paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_size=16):
+def paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_size=16, softcap=0.0):
     """O (Hq, D) for one sequence's single query token, placed at position ctx_b - 1."""
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k_cache.shape[2]
@@ -419,13 +419,13 @@ def paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_
     vv = gather_pages(v_cache, block_table[b], ctx, page_size)
     vis = np.ones((1, ctx), dtype=bool)
     for h in range(Hq):
-        o, _, _ = unit_forward(q[b, h][None, :], kk[:, h // r], vv[:, h // r], scale, vis)
+        o, _, _ = unit_forward(q[b, h][None, :], kk[:, h // r], vv[:, h // r], scale, vis, softcap)
         out[h] = o[0]
     return out
 
 
-def paged_decode(q, k_cache, v_cache, block_table, ctx_lens, scale, page_size=16):
+def paged_decode(q, k_cache, v_cache, block_table, ctx_lens, scale, page_size=16, softcap=0.0):
     """O (B, Hq, D) float64."""
     B = q.shape[0]
-    return np.stack([paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_size)
+    return np.stack([paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_size, softcap)
                      for b in range(B)])

@@ -566,3 +566,21 @@ def test_paged_append_then_gather_round_trip():
         for t in range(int(ctx0[b]), int(ctx1[b])):
             touched[table[b, t // w.page_size], t % w.page_size] = True
     assert np.array_equal(out[~touched], kc[~touched])                    # nothing else changed
+
+
+def test_decode_softcap_is_last_row_of_capped_causal_attention():
+    """The capped decode equals the last row of capped causal attention over the gathered tokens
+    (the same pin as the uncapped decode, with the cap)."""
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=3, Hq=4, Hkv=2, ctx_range=(1, 40))
+    inp = make_decode_inputs(w, seed=12)
+    q = 3.0 * bf16_bits_to_f64(inp["q"])
+    kc, vc = bf16_bits_to_f64(inp["k_cache"]), bf16_bits_to_f64(inp["v_cache"])
+    o = oracle.paged_decode(q, kc, vc, inp["block_table"], inp["ctx_lens"], w.scale, w.page_size, 2.0)
+    for b in range(w.B):
+        n = int(inp["ctx_lens"][b])
+        kk = oracle.gather_pages(kc, inp["block_table"][b], n, w.page_size)[None]
+        vv = oracle.gather_pages(vc, inp["block_table"][b], n, w.page_size)[None]
+        qq = np.zeros((1, n, w.Hq, w.D))
+        qq[0, n - 1] = q[b]
+        full, _ = oracle.attention_forward(qq, kk, vv, w.scale, True, 0, None, 2.0)
+        np.testing.assert_allclose(o[b], full[0, n - 1], atol=1e-13)

@@ -248,6 +248,7 @@ typedef struct {
  *                current one; the query sits at position ctx_lens[b]-1 and sees
  *                every token t < ctx_lens[b].  Clamped to
  *                [0, max_pages_per_seq * page_size]; 0 gives O = 0.
+ *   softcap      as for attn_fwd (0: none)
  *   o            device 16-bit (B, Hq, D), written; strides o_stride_b, o_stride_h
  *   workspace    at least paged_decode_workspace_bytes(shape) bytes
  */
@@ -255,7 +256,7 @@ attn_status paged_decode(const attn_decode_shape* shape,
                          const void* q, int64_t q_stride_b, int64_t q_stride_h,
                          attn_tensor k_cache, attn_tensor v_cache,
                          const int32_t* block_table, const int32_t* ctx_lens,
-                         float scale,
+                         float scale, float softcap,
                          void* o, int64_t o_stride_b, int64_t o_stride_h,
                          void* workspace, size_t workspace_bytes, void* stream);
 

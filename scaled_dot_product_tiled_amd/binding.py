@@ -90,7 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    AttnTensor, vp, AttnTensor, ctypes.c_int, vp]
     lib.attn_lse_merge.restype = ctypes.c_int
     lib.paged_decode.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int64, ctypes.c_int64, AttnTensor, AttnTensor,
-                                 vp, vp, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz, vp]
+                                 vp, vp, ctypes.c_float, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz,
+                                 vp]
     lib.paged_decode.restype = ctypes.c_int
     lib.paged_kv_append.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, AttnTensor, AttnTensor,
                                     vp, vp, vp]
@@ -395,7 +396,8 @@ def attn_lse_merge(o: torch.Tensor, lse: torch.Tensor, o_part: torch.Tensor, lse
 
 def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                  ctx_lens: torch.Tensor, scale: Optional[float] = None,
-                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 softcap: float = 0.0) -> torch.Tensor:
     """O (B,Hq,D) of one query token per sequence against a paged cache (num_pages, page_size, Hkv, D)."""
     lib = load_library()
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -422,7 +424,8 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     st = lib.paged_decode(ctypes.byref(shape), q.data_ptr(), q.stride(0), q.stride(1),
                           AttnTensor(k_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)),
                           AttnTensor(v_cache.data_ptr(), v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)),
-                          block_table.data_ptr(), ctx_lens.data_ptr(), float(scale), out.data_ptr(), out.stride(0),
+                          block_table.data_ptr(), ctx_lens.data_ptr(), float(scale), float(softcap), out.data_ptr(),
+                          out.stride(0),
                           out.stride(1), workspace.data_ptr(), nbytes, _stream())
     _check(st, "paged_decode")
     return out

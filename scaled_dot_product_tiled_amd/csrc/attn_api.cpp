@@ -627,8 +627,8 @@ size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {
 
 attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t q_stride_b, int64_t q_stride_h,
                          attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
-                         const int32_t* ctx_lens, float scale, void* o, int64_t o_stride_b, int64_t o_stride_h,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         const int32_t* ctx_lens, float scale, float softcap, void* o, int64_t o_stride_b,
+                         int64_t o_stride_h, void* workspace, size_t workspace_bytes, void* stream) {
   if (shape == nullptr) return ATTN_ERR_INVALID_ARG;
   const attn_decode_shape& sh = *shape;
   if (sh.B < 0 || sh.Hq <= 0 || sh.Hkv <= 0 || sh.num_pages <= 0 || sh.max_pages_per_seq <= 0 || sh.page_size <= 0)
@@ -638,7 +638,7 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   if (sh.D != 128 || sh.page_size != 16 || (r != 1 && r != 2 && r != 4 && r != 8)) return ATTN_ERR_UNSUPPORTED;
   if (!dtype16_ok(sh.dtype)) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)sh.max_pages_per_seq * sh.page_size > INT_MAX / 2) return ATTN_ERR_UNSUPPORTED;
-  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
   if (q == nullptr || o == nullptr || !aligned16(q) || !aligned16(o) || block_table == nullptr || ctx_lens == nullptr)
     return ATTN_ERR_INVALID_ARG;
   if (!stride_ok(q_stride_b) || !stride_ok(q_stride_h) || !stride_ok(o_stride_b) || !stride_ok(o_stride_h))
@@ -680,6 +680,8 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   a.max_pages = sh.max_pages_per_seq;
   a.max_chunks = (sh.max_pages_per_seq * sh.page_size + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
   a.c = scale * 1.4426950408889634f;
+  a.sc_in = softcap > 0.f ? scale / softcap : 0.f;
+  a.sc_out = softcap > 0.f ? softcap / scale : 0.f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed("decode_split", s, [&] { return attn::launch_decode_split(a, sh.D, s); });
   if (e != hipSuccess) return hip_status(e);

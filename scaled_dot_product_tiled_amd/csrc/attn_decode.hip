@@ -41,7 +41,7 @@ __device__ __forceinline__ float row_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int R, bool F16>
+template <int R, bool F16, bool SOFTCAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int D = kDecD;
   constexpr int CH = kDecodeChunk;      // tokens per workgroup
@@ -147,7 +147,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        t[pg][i] = (4 * grp + i < nv[pg]) ? st[pg][i] * cs : -INFINITY;
+        float x = st[pg][i];
+        if constexpr (SOFTCAP) x = a.sc_out * tanh_from_exp(x * a.sc_in);  // cap before the mask
+        t[pg][i] = (4 * grp + i < nv[pg]) ? x * cs : -INFINITY;
         lm = fmaxf(lm, t[pg][i]);
       }
     lm = row_swap_max(lm);
@@ -268,14 +270,14 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
   a.o[b * a.o_sb + h * a.o_sh + d] = E16<F16>::from_float(out);
 }
 
-template <bool F16>
+template <bool F16, bool SC>
 hipError_t launch_decode_split_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 g1(a.B * a.Hkv * a.max_chunks), b1(256);
   switch (a.r) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<1, F16>), g1, b1, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<2, F16>), g1, b1, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<4, F16>), g1, b1, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_split_kernel<8, F16>), g1, b1, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<1, F16, SC>), g1, b1, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<2, F16, SC>), g1, b1, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<4, F16, SC>), g1, b1, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_split_kernel<8, F16, SC>), g1, b1, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -283,7 +285,9 @@ hipError_t launch_decode_split_t(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream) {
   if (D != kDecD) return hipErrorInvalidValue;
-  return a.f16 ? launch_decode_split_t<true>(a, stream) : launch_decode_split_t<false>(a, stream);
+  const bool sc = a.sc_in > 0.f;
+  if (a.f16) return sc ? launch_decode_split_t<true, true>(a, stream) : launch_decode_split_t<true, false>(a, stream);
+  return sc ? launch_decode_split_t<false, true>(a, stream) : launch_decode_split_t<false, false>(a, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream) {

@@ -82,6 +82,7 @@ struct DecodeArgs {
   int64_t kc_sp, kc_ss, kc_sh, vc_sp, vc_ss, vc_sh;
   int B, Hq, Hkv, r, page_size, num_pages, max_pages, max_chunks;
   float c;            // scale * log2(e)
+  float sc_in, sc_out;  // softcap (see AttnArgs); unused without a cap
   int f16;            // 16-bit tensors are IEEE half (else bfloat16)
 };
 

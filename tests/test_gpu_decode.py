@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from synth import DECODE_WORKLOADS, bf16_bits_to_f64, make_decode_inputs
+from synth import DECODE_WORKLOADS, bf16_bits_to_f64, f32_to_bf16_bits, make_decode_inputs
 from tests.gpu_util import O_MAX_ABS, all_finite, dev, host, host_bits, max_abs
 
 pytestmark = pytest.mark.gpu
@@ -78,3 +78,21 @@ def test_other_group_ratios(Hq, Hkv):
     inp = make_decode_inputs(w, seed=4)
     o = run(inp, w.scale)
     assert max_abs(host(o), ref(inp, w.scale)) <= O_MAX_ABS
+
+
+@pytest.mark.parametrize("cap", [1.5, 30.0])
+def test_decode_softcap_matches_oracle(cap):
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=6, ctx_range=(1, 1200))
+    inp = make_decode_inputs(w, seed=13)
+    inp["q"] = f32_to_bf16_bits(3.0 * bf16_bits_to_f64(inp["q"]).astype(np.float32))   # scores of a few units
+    print(f"[decode softcap {cap}] ctx {inp['ctx_lens'].tolist()}", flush=True)
+    q, kc, vc = dev(inp["q"]), dev(inp["k_cache"]), dev(inp["v_cache"])
+    table = torch.from_numpy(inp["block_table"]).to("cuda:0")
+    ctx = torch.from_numpy(inp["ctx_lens"]).to("cuda:0")
+    o = sdpt.paged_decode(q, kc, vc, table, ctx, scale=w.scale, softcap=cap)
+    torch.cuda.synchronize()
+    r = oracle.paged_decode(bf16_bits_to_f64(inp["q"]), bf16_bits_to_f64(inp["k_cache"]),
+                            bf16_bits_to_f64(inp["v_cache"]), inp["block_table"], inp["ctx_lens"], w.scale,
+                            w.page_size, cap)
+    assert all_finite(o)
+    assert max_abs(host(o), r) <= O_MAX_ABS

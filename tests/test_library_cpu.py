@@ -109,8 +109,8 @@ def test_backward_and_decode_checks():
     d = AttnDecodeShape(4, 32, 8, 128, 16, 100, 8)
     kc = AttnTensor(0x10000, 16 * 8 * 128, 8 * 128, 128)
 
-    def dec(shape, q=0x1000, table=0x2000, ws=0x100000, wsb=1 << 20):
-        return lib.paged_decode(ctypes.byref(shape), q, 32 * 128, 128, kc, kc, table, 0x3000, 0.1, 0x4000,
+    def dec(shape, q=0x1000, table=0x2000, ws=0x100000, wsb=1 << 20, cap=0.0):
+        return lib.paged_decode(ctypes.byref(shape), q, 32 * 128, 128, kc, kc, table, 0x3000, 0.1, cap, 0x4000,
                                 32 * 128, 128, ws, wsb, None)
     assert dec(AttnDecodeShape(4, 32, 8, 64, 16, 100, 8)) == UNSUPPORTED     # head_dim
     assert dec(AttnDecodeShape(4, 32, 8, 128, 32, 100, 8)) == UNSUPPORTED    # page size
@@ -118,6 +118,7 @@ def test_backward_and_decode_checks():
     assert dec(d, q=0) == INVALID
     assert dec(d, table=0) == INVALID
     assert dec(d, wsb=16) == WORKSPACE
+    assert dec(d, cap=-1.0) == INVALID
     assert dec(AttnDecodeShape(0, 32, 8, 128, 16, 100, 8)) == OK
 
 

@@ -303,6 +303,17 @@ size_t paged_decode_workspace_bytes(const attn_decode_shape* shape);
 size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal, int window,
                                       int64_t q_pos0, int64_t k_pos0);
 
+/* Debug mode: calls that take device-resident metadata (cu_seqlens, pad_mask, block tables,
+ * ctx_lens) first check it on their stream and synchronise; inconsistent metadata (a mask that
+ * is not a prefix, offsets that decrease or do not end at `total`, a length above S, a page id
+ * outside the pool, a context longer than the table) returns ATTN_ERR_INVALID_ARG before any
+ * other launch.  Outside debug mode the metadata is not checked (lengths, offsets and page ids
+ * are clamped so that nothing is accessed outside the buffers).  attn_debug(on) sets the mode
+ * for the process and returns the previous one; its initial value is 1 when the environment
+ * variable ATTN_DEBUG is set to anything but "0".  A check synchronises its stream, so debug
+ * mode is for eager calls, not for calls recorded into a graph. */
+int attn_debug(int on);
+
 /* Static string for a status code. */
 const char* attn_status_str(attn_status status);
 

@@ -52,7 +52,7 @@ class AttnDecodeShape(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "paged_decode",
-           "paged_kv_append", "paged_kv_gather",
+           "paged_kv_append", "paged_kv_gather", "attn_debug",
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read")
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_kv_gather.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, vp, vp, AttnTensor,
                                     AttnTensor, vp]
     lib.paged_kv_gather.restype = ctypes.c_int
+    lib.attn_debug.argtypes = [ctypes.c_int]
+    lib.attn_debug.restype = ctypes.c_int
     lib.attn_fwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
     lib.attn_fwd_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -491,6 +493,11 @@ def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: t
                              _tensor(v_out, False), _stream())
     _check(st, "paged_kv_gather")
     return k_out, v_out
+
+
+def debug(on: bool) -> bool:
+    """Switches the library's metadata checks (debug mode) on or off; returns the previous mode."""
+    return bool(load_library().attn_debug(1 if on else 0))
 
 
 def profile(on: bool) -> None:

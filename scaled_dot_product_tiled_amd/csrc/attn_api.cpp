@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -15,6 +17,23 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Debug mode (attn_debug(1), or ATTN_DEBUG=1 in the environment at the first call): calls with
+// device-resident metadata check it first, synchronously, and return ATTN_ERR_INVALID_ARG
+// instead of launching anything when it is inconsistent.
+std::atomic<int> g_debug{-1};
+
+bool debug_on() {
+  int d = g_debug.load(std::memory_order_relaxed);
+  if (d < 0) {
+    const char* e = std::getenv("ATTN_DEBUG");
+    d = (e != nullptr && e[0] != '\0' && e[0] != '0') ? 1 : 0;
+    int expect = -1;
+    g_debug.compare_exchange_strong(expect, d);
+    d = g_debug.load(std::memory_order_relaxed);
+  }
+  return d > 0;
+}
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -352,12 +371,30 @@ void set_tensors(attn::AttnArgs& a, const Tensors& t, bool packed, bool bwd) {
   set_tensor(t.dv, packed, a.dv_sb, a.dv_ss, a.dv_sh);
 }
 
+attn_status debug_check_varlen(const Call& c, const int32_t* cu_seqlens, const uint8_t* pad_mask, hipStream_t s) {
+  if (!c.varlen || !debug_on()) return ATTN_OK;
+  bool bad = false;
+  attn_status st = hip_status(attn::check_varlen_meta(pad_mask, cu_seqlens, c.B, c.S, c.total, s, bad));
+  if (st != ATTN_OK) return st;
+  return bad ? ATTN_ERR_INVALID_ARG : ATTN_OK;
+}
+
+attn_status debug_check_pages(const attn_decode_shape& sh, const int32_t* table, const int32_t* ctx, hipStream_t s) {
+  if (!debug_on()) return ATTN_OK;
+  bool bad = false;
+  attn_status st = hip_status(
+      attn::check_pages_meta(table, ctx, sh.B, sh.max_pages_per_seq, sh.page_size, sh.num_pages, s, bad));
+  if (st != ATTN_OK) return st;
+  return bad ? ATTN_ERR_INVALID_ARG : ATTN_OK;
+}
+
 attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, const int32_t* cu_seqlens,
                     const uint8_t* pad_mask, void* workspace, hipStream_t s, bool o_f32 = false) {
   int32_t* meta = static_cast<int32_t*>(workspace);
   attn_status st;
+  if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
   if (c.varlen && (st = launch("varlen_prep", s, c.B, [&] {
-                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, meta, meta + c.B, s);
+                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, c.total, meta, meta + c.B, s);
                    })))
     return st;
   attn::AttnArgs a = {};
@@ -379,8 +416,9 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
   int32_t* meta = static_cast<int32_t*>(workspace);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(c.B, c.varlen));
   attn_status st;
+  if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
   if (c.varlen && (st = launch("varlen_prep", s, c.B, [&] {
-                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, meta, meta + c.B, s);
+                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, c.total, meta, meta + c.B, s);
                    })))
     return st;
   attn::AttnArgs a = {};
@@ -586,6 +624,7 @@ static attn_status paged_copy(const attn_decode_shape* shape, int32_t n, attn_te
       (st = check_tensor(v_cache, false)))
     return st;
   if (sh.B == 0 || n == 0) return ATTN_OK;
+  if ((st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream)))) return st;
   attn::PagedCopyArgs a = {};
   a.tk = static_cast<__bf16*>(k_tok.ptr);
   a.tv = static_cast<__bf16*>(v_tok.ptr);
@@ -651,6 +690,7 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
     return ATTN_ERR_WORKSPACE;
   if (sh.B == 0) return ATTN_OK;
+  if ((st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream)))) return st;
 
   attn::DecodeArgs a = {};
   a.q = static_cast<const __bf16*>(q);
@@ -700,6 +740,12 @@ attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens, at
                             attn_tensor k_out, attn_tensor v_out, void* stream) {
   return paged_copy(shape, n_tokens, k_out, v_out, k_cache, v_cache, block_table, ctx_lens, 1, "paged_kv_gather",
                     stream);
+}
+
+int attn_debug(int on) {
+  debug_on();  // the environment's setting is read first, so that this call overrides it
+  const int prev = g_debug.exchange(on ? 1 : 0);
+  return prev > 0;
 }
 
 const char* attn_status_str(attn_status status) {

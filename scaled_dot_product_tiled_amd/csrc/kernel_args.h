@@ -149,8 +149,13 @@ __host__ __device__ inline int64_t ds_block_index(int qt, int kb, int causal, in
 }
 
 // Launchers (return the HIP launch status).
-hipError_t launch_varlen_prep(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S,
+hipError_t launch_varlen_prep(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S, int total,
                               int32_t* seq_off, int32_t* seq_len, hipStream_t stream);
+// Debug-mode metadata checks: synchronise the stream and set bad when the metadata is invalid.
+hipError_t check_varlen_meta(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S, int total,
+                             hipStream_t stream, bool& bad);
+hipError_t check_pages_meta(const int32_t* table, const int32_t* ctx, int B, int max_pages, int page_size,
+                            int num_pages, hipStream_t stream, bool& bad);
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream);

@@ -208,3 +208,14 @@ def test_paged_cache_call_checks():
     assert gat(AttnDecodeShape(4, 32, 8, 128, 16, 100, 8, 1)) == UNSUPPORTED       # fp32 cache
     assert app(n=0) == OK and gat(AttnDecodeShape(0, 32, 8, 512, 16, 100, 8)) == OK  # nothing to move
     assert lib.attn_last_hip_error() == 0
+
+
+def test_debug_mode_switch():
+    """attn_debug sets the process-wide metadata-check mode and returns the previous one (no GPU
+    call is made by the switch itself)."""
+    lib = load_library()
+    first = lib.attn_debug(1)
+    assert first in (0, 1)
+    assert lib.attn_debug(0) == 1
+    assert lib.attn_debug(0) == 0
+    lib.attn_debug(first)

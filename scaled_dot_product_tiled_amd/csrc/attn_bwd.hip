@@ -215,13 +215,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
       {
         const bf16* src = score_wave ? Qs[buf] : dOs[buf];
-        bf16x8 f[3];
+        bf16x8 f[4];
         f[0] = rowf.read(src, 0, 0);
         f[1] = rowf.read(src, 0, 1);
+        f[2] = rowf.read(src, 0, 2);
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-          if (t + 2 < KS) f[(t + 2) % 3] = rowf.read(src, 0, t + 2);
-          sacc = E16<F16>::mma32(f[t % 3], kv[t], sacc);
+          if (t + 3 < KS) f[(t + 3) % 4] = rowf.read(src, 0, t + 3);
+          sacc = E16<F16>::mma32(f[t % 4], kv[t], sacc);
           if ((t & 1) == 0 && t / 2 < 2 * NDMA) {
             const int j = t / 2;
             if (j < NDMA)
@@ -325,19 +326,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         }
       }
       barrier_lds();
+      {
+        // the transposed fragments of (s, d) are read one (s, d) step ahead of their products
+        bf16x8 ado = trf.read(dOs[buf], 0, dsl), aq = trf.read(Qs[buf], 0, dsl);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 p0 = pds[0][0][s][lane], p1 = pds[0][1][s][lane];
-        const bf16x8 s0 = pds[1][0][s][lane], s1 = pds[1][1][s][lane];
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 p0 = pds[0][0][s][lane], p1 = pds[0][1][s][lane];
+          const bf16x8 s0 = pds[1][0][s][lane], s1 = pds[1][1][s][lane];
 #pragma unroll
-        for (int d = 0; d < DBW; ++d) {
-          const bf16x8 ado = trf.read(dOs[buf], 16 * s, dsl + d);
-          dvacc[0][d] = E16<F16>::mma32(ado, p0, dvacc[0][d]);
-          dvacc[1][d] = E16<F16>::mma32(ado, p1, dvacc[1][d]);
-          const bf16x8 aq = trf.read(Qs[buf], 16 * s, dsl + d);
-          dkacc[0][d] = E16<F16>::mma32(aq, s0, dkacc[0][d]);
-          dkacc[1][d] = E16<F16>::mma32(aq, s1, dkacc[1][d]);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int d = 0; d < DBW; ++d) {
+            const int ns = d + 1 == DBW ? s + 1 : s, nd = d + 1 == DBW ? 0 : d + 1;
+            bf16x8 ado_n = ado, aq_n = aq;
+            if (ns < 2) {
+              ado_n = trf.read(dOs[buf], 16 * ns, dsl + nd);
+              aq_n = trf.read(Qs[buf], 16 * ns, dsl + nd);
+            }
+            dvacc[0][d] = E16<F16>::mma32(ado, p0, dvacc[0][d]);
+            dvacc[1][d] = E16<F16>::mma32(ado, p1, dvacc[1][d]);
+            dkacc[0][d] = E16<F16>::mma32(aq, s0, dkacc[0][d]);
+            dkacc[1][d] = E16<F16>::mma32(aq, s1, dkacc[1][d]);
+            ado = ado_n;
+            aq = aq_n;
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
       qi += hi + 1 == rs;
@@ -586,32 +597,51 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
       }
       const bool full = (p0 + M <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= p0 + dlt) &&
                         (a.window <= 0 || j0 > p0 + M - 1 + dlt - a.window);
+      // dS fragments of key step s are read one step ahead and masked when used; the K
+      // fragment of (s, d) is read one (s, d) step ahead of its products
+      auto mask = [&](bf16x8& v, int s, int x) {
+        // element e holds key j0 + 16 s + 4 g2 + e (e < 4) or j0 + 16 s + 8 + 4 g2 + e - 4
+        const int row = p0 + 32 * x + ln;
+        uint32_t w[4];
+        __builtin_memcpy(w, &v, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = j0 + 16 * s + 4 * g2 + (e < 4 ? e : e + 4);
+          const uint32_t keep = key_visible(row, key, len, lenk, dlt, a.causal, a.window) ? 0xffffu : 0u;
+          w[e >> 1] &= (e & 1) ? (keep << 16) | 0xffffu : keep | 0xffff0000u;
+        }
+        __builtin_memcpy(&v, w, 16);
+      };
+      bf16x8 bs[RB], bsn[RB];
+#pragma unroll
+      for (int x = 0; x < RB; ++x) bs[x] = trs.read(Ss[buf], 0, x);
+      bf16x8 ak = trk.read_with(Ks[buf], 0, dsl, klo[0], khi[0]);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        bf16x8 bs[RB];
+        if (!full) {
 #pragma unroll
-        for (int x = 0; x < RB; ++x) {
-          bs[x] = trs.read(Ss[buf], 16 * s, x);
-          if (!full) {
-            // element e holds key j0 + 16 s + 4 g2 + e (e < 4) or j0 + 16 s + 8 + 4 g2 + e - 4
-            const int row = p0 + 32 * x + ln;
-            uint32_t w[4];
-            __builtin_memcpy(w, &bs[x], 16);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int key = j0 + 16 * s + 4 * g2 + (e < 4 ? e : e + 4);
-              const uint32_t keep = key_visible(row, key, len, lenk, dlt, a.causal, a.window) ? 0xffffu : 0u;
-              w[e >> 1] &= (e & 1) ? (keep << 16) | 0xffffu : keep | 0xffff0000u;
-            }
-            __builtin_memcpy(&bs[x], w, 16);
-          }
+          for (int x = 0; x < RB; ++x) mask(bs[x], s, x);
         }
 #pragma unroll
         for (int d = 0; d < DBW; ++d) {
-          const bf16x8 ak = trk.read_with(Ks[buf], 16 * s, dsl + d, klo[d], khi[d]);
+          const bool last_d = d + 1 == DBW;
+          if (last_d && s == 0) {
+#pragma unroll
+            for (int x = 0; x < RB; ++x) bsn[x] = trs.read(Ss[buf], 16, x);
+          }
+          bf16x8 akn = ak;
+          if (!(last_d && s == 1)) {
+            const int ns = last_d ? s + 1 : s, nd = last_d ? 0 : d + 1;
+            akn = trk.read_with(Ks[buf], 16 * ns, dsl + nd, klo[nd], khi[nd]);
+          }
 #pragma unroll
           for (int x = 0; x < RB; ++x) acc[x][d] = E16<F16>::mma32(ak, bs[x], acc[x][d]);
+          ak = akn;
           __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s == 0) {
+#pragma unroll
+          for (int x = 0; x < RB; ++x) bs[x] = bsn[x];
         }
       }
     }

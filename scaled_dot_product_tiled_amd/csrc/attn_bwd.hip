@@ -180,35 +180,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     const int tq_last = tq0 + nq - 1;
     static_assert(2 * NDMA <= KS / 2, "every copy needs a slot in the S / dP loop");
     int hi = 0, qi = 0;  // step k
-    auto stats = [&](int hs, int i0s, int buf) {
-      if (wave == 0) {
-        const int64_t so = b * a.st_sb + (hb0 + hs) * a.st_sh + off;
-        dma_stats(stat[buf], a.lse + so, a.delta + so, i0s, len - 1, lane);
-      }
+    // Addresses of step k: Q and dO at (row i0, head hb0 + hi), the row statistics and the dS
+    // blocks of that head.  A step advances one head, or after the group's last head returns
+    // to head hb0 one query tile lower, so each moves by one of two fixed amounts.
+    const int i00 = tq_last * MQ;
+    const bf16* qrow = a.q + b * a.q_sb + (int64_t)(off + i00) * a.q_ss + hb0 * a.q_sh;
+    const bf16* drow = a.dout + b * a.do_sb + (int64_t)(off + i00) * a.do_ss + hb0 * a.do_sh;
+    int64_t so = b * a.st_sb + hb0 * a.st_sh + off;
+    bf16* dshead = a.dsb + (int64_t)(b * a.Hq + hb0) * a.ds_head * kDsBlockElems;
+    const int64_t q_wrap = -(int64_t)(rs - 1) * a.q_sh - (int64_t)MQ * a.q_ss;
+    const int64_t d_wrap = -(int64_t)(rs - 1) * a.do_sh - (int64_t)MQ * a.do_ss;
+    const int64_t s_wrap = -(int64_t)(rs - 1) * a.st_sh;
+    const int64_t ds_step = (int64_t)a.ds_head * kDsBlockElems;
+    int ds_qt = -1;  // query tile of the dS block index ds_bi (of this wave's key block)
+    int64_t ds_bi = -1;
+    auto stats = [&](int64_t sofs, int i0s, int buf) {
+      if (wave == 0) dma_stats(stat[buf], a.lse + sofs, a.delta + sofs, i0s, len - 1, lane);
     };
-    {
-      const int h0 = hb0;
-      const int i00 = tq_last * MQ;
-      dma_rows<D, MQ, 4>(Qs[0], tile_src<MQ>(a.q + b * a.q_sb + (int64_t)off * a.q_ss + h0 * a.q_sh, a.q_ss, i00,
-                                             len - i00), wave, lane);
-      dma_rows<D, MQ, 4>(dOs[0], tile_src<MQ>(a.dout + b * a.do_sb + (int64_t)off * a.do_ss + h0 * a.do_sh, a.do_ss,
-                                              i00, len - i00), wave, lane);
-      stats(0, i00, 0);
-    }
+    dma_rows<D, MQ, 4>(Qs[0], tile_src_rows<MQ>(qrow, a.q_ss, len - i00), wave, lane);
+    dma_rows<D, MQ, 4>(dOs[0], tile_src_rows<MQ>(drow, a.do_ss, len - i00), wave, lane);
+    stats(so, i00, 0);
     for (int k = 0; k < nsteps; ++k) {
       const int buf = k & 1;
       const int i0 = (tq_last - qi) * MQ;
-      const int hn = hi + 1 == rs ? 0 : hi + 1;          // step k+1
-      const int i0n = hi + 1 == rs ? i0 - MQ : i0;
+      const bool wrap = hi + 1 == rs;                    // step k+1
+      const int hn = wrap ? 0 : hi + 1;
+      const int i0n = wrap ? i0 - MQ : i0;
       const bool has_next = k + 1 < nsteps;
+      const bf16* qrn = qrow + (wrap ? q_wrap : a.q_sh);
+      const bf16* drn = drow + (wrap ? d_wrap : a.do_sh);
+      const int64_t son = so + (wrap ? s_wrap : a.st_sh);
       // the last step copies nothing real: an empty range reads zeros into the idle buffers
-      const TileSrc qn = tile_src<MQ>(a.q + b * a.q_sb + (int64_t)off * a.q_ss + (hb0 + hn) * a.q_sh, a.q_ss,
-                                      i0n, has_next ? len - i0n : 0);
-      const TileSrc dn = tile_src<MQ>(a.dout + b * a.do_sb + (int64_t)off * a.do_ss + (hb0 + hn) * a.do_sh,
-                                      a.do_ss, i0n, has_next ? len - i0n : 0);
+      const TileSrc qn = tile_src_rows<MQ>(qrn, a.q_ss, has_next ? len - i0n : 0);
+      const TileSrc dn = tile_src_rows<MQ>(drn, a.do_ss, has_next ? len - i0n : 0);
       wait_vmcnt<0>();
       barrier_lds();  // step k is in LDS; every wave is done with step k-1
-      if (has_next) stats(hn, i0n, buf ^ 1);
 
       f32x16 sacc;
 #pragma unroll
@@ -315,17 +321,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         }
         pds[0][kb][xh >> 1][lane] = pb;
         pds[1][kb][xh >> 1][lane] = db;
-        // dS^T for the dQ product: this lane's key, query rows i0 + 8 x + 4 g2 .. +3
-        const int64_t bi = ds_block_index(i0 / kDsRows, (j0 / kDsKeys) + kb, a.causal, a.window, dlt, lenk,
-                                          a.ds_tri, a.ds_cnt);
+        // dS for the dQ product, this lane's key.  db holds query rows 8 xh + 4 g2 + (0..3) and
+        // 8 xh + 8 + 4 g2 + (0..3) of the step; lanes l and l + 32 trade four of them so that each
+        // holds 8 consecutive rows (8 xh + 8 g2 ..) and writes them with one 16-byte store.
+        if (i0 / kDsRows != ds_qt) {  // the block changes every kDsRows / MQ query tiles
+          ds_qt = i0 / kDsRows;
+          ds_bi = ds_block_index(ds_qt, (j0 / kDsKeys) + kb, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
+        }
+        const int64_t bi = ds_bi;
         if (bi >= 0) {
-          bf16* dst = a.dsb + ((int64_t)(b * a.Hq + hb0 + hi) * a.ds_head + bi) * kDsBlockElems +
-                      ln * kDsRows + (i0 & (kDsRows - 1)) + 8 * xh + 4 * g2;
-          *reinterpret_cast<bf16x4*>(dst) = bf16x4{db[0], db[1], db[2], db[3]};
-          *reinterpret_cast<bf16x4*>(dst + 8) = bf16x4{db[4], db[5], db[6], db[7]};
+          uint32_t w[4];
+          __builtin_memcpy(w, &db, 16);
+          const uint32_t give0 = g2 ? w[0] : w[2], give1 = g2 ? w[1] : w[3];
+          const auto r0 = __builtin_amdgcn_permlane32_swap(give0, give0, false, false);
+          const auto r1 = __builtin_amdgcn_permlane32_swap(give1, give1, false, false);
+          // r[0] carries the lower half's value to every lane, r[1] the upper half's
+          const uint32_t got0 = g2 ? r0[0] : r0[1], got1 = g2 ? r1[0] : r1[1];
+          const uint32_t o[4] = {g2 ? got0 : w[0], g2 ? got1 : w[1], g2 ? w[2] : got0, g2 ? w[3] : got1};
+          bf16* dst = dshead + bi * kDsBlockElems + ds_elem(i0 & (kDsRows - 1), ln) + 8 * xh + 8 * g2;
+          uint4 v;
+          __builtin_memcpy(&v, o, 16);
+          *reinterpret_cast<uint4*>(dst) = v;
         }
       }
       barrier_lds();
+      if (has_next) stats(son, i0n, buf ^ 1);
       {
         // the transposed fragments of (s, d) are read one (s, d) step ahead of their products
         bf16x8 ado = trf.read(dOs[buf], 0, dsl), aq = trf.read(Qs[buf], 0, dsl);
@@ -351,8 +371,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           }
         }
       }
-      qi += hi + 1 == rs;
+      qi += wrap;
       hi = hn;
+      qrow = qrn;
+      drow = drn;
+      so = son;
+      dshead += wrap ? -(rs - 1) * ds_step : ds_step;
     }
   }
 
@@ -506,6 +530,29 @@ hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream) {
   return a.f16 ? launch_bwd_dkdv_t<true>(a, D, stream) : launch_bwd_dkdv_t<false>(a, D, stream);
 }
 
+// Copy of one stored dS block into a swizzled LDS tile of kDsKeys rows (keys) x kDsRows
+// columns (query rows), as dma_rows does for a row-major tile: LDS chunk p of key row r
+// receives the block's chunk p ^ h(r) of that key, found at its place in the quartered
+// layout (ds_elem).
+template <int NW>
+__device__ __forceinline__ void dma_ds_block(bf16* tile, const TileSrc& src, int wave, int lane) {
+  constexpr int CH = kDsRows / 8;   // 16-byte chunks per key row
+  constexpr int RPI = 64 / CH;      // key rows per wave-instruction
+  constexpr int NI = kDsKeys / RPI;
+  static_assert(NI % NW == 0, "the block must split evenly over the waves");
+#pragma unroll
+  for (int k = 0; k < NI / NW; ++k) {
+    const int i = wave + k * NW;
+    const int key = i * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz_h(key);
+    const uint32_t voff = (uint32_t)(2 * ds_elem(8 * c, key));
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + i * RPI * kDsRows));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+                 "s"(src.rsrc)
+                 : "memory");
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dQ = scale dS K, from the stored dS blocks
 // ---------------------------------------------------------------------------
@@ -585,7 +632,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
     for (int d = 0; d < DBW; ++d) trk.pick(dsl + d, klo[d], khi[d]);
 
     dma_rows<D, NK, NW>(Ks[0], tile_src<NK>(kbase, a.k_ss, kb_first * NK, lenk - kb_first * NK), wave, lane);
-    dma_rows<M, NK, NW>(Ss[0], tile_src<NK>(sblock(kb_first), M, 0, NK), wave, lane);
+    dma_ds_block<NW>(Ss[0], tile_src<NK>(sblock(kb_first), M, 0, NK), wave, lane);
     for (int kb = kb_first; kb <= kb_last; ++kb) {
       const int buf = (kb - kb_first) & 1;
       const int j0 = kb * NK;
@@ -593,7 +640,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
       barrier_lds();  // block kb is in LDS; every wave is done with block kb-1
       if (kb < kb_last) {
         dma_rows<D, NK, NW>(Ks[buf ^ 1], tile_src<NK>(kbase, a.k_ss, j0 + NK, lenk - j0 - NK), wave, lane);
-        dma_rows<M, NK, NW>(Ss[buf ^ 1], tile_src<NK>(sblock(kb + 1), M, 0, NK), wave, lane);
+        dma_ds_block<NW>(Ss[buf ^ 1], tile_src<NK>(sblock(kb + 1), M, 0, NK), wave, lane);
       }
       const bool full = (p0 + M <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= p0 + dlt) &&
                         (a.window <= 0 || j0 > p0 + M - 1 + dlt - a.window);

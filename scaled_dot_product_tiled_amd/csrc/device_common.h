@@ -212,6 +212,12 @@ __device__ __forceinline__ TileSrc tile_src(const bf16* g, int64_t stride, int r
   return t;
 }
 
+// The same for a tile whose first row is at `row0` (rows `stride` elements apart).
+template <int ROWS>
+__device__ __forceinline__ TileSrc tile_src_rows(const bf16* row0, int64_t stride, int nvalid) {
+  return tile_src<ROWS>(row0, stride, 0, nvalid);
+}
+
 template <int D, int ROWS, int NW>
 __device__ __forceinline__ void dma_rows_one(bf16* tile, const TileSrc& src, int wave, int lane, int k) {
   constexpr int CH = D / 8;      // 16-byte chunks per row

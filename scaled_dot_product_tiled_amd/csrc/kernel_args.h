@@ -118,14 +118,20 @@ struct MergeArgs {
 };
 
 // The backward stores dS = P * (dP - delta) (bf16) once, for the dQ product.  It is kept in
-// blocks of kDsKeys keys x kDsRows query rows of one (batch, query head), each block stored
-// transposed (row-major, one row per key, kDsRows query rows per row: 8 KB).  Query tile qt
+// blocks of kDsKeys keys x kDsRows query rows of one (batch, query head), 8 KB each, stored
+// transposed in four quarters of 32 query rows: quarter, then key, then the 32 rows (64
+// bytes per key), so the dK/dV step that produces 32 rows of a block writes whole 16-byte
+// pieces (ds_elem gives the element offset of (row, key) in a block).  Query tile qt
 // (rows 128 qt ..) keeps key blocks ds_kb_lo(qt) .. ds_kb_hi(qt), the only ones that can
 // hold a visible pair, packed tile after tile: 4 (qt + 1) blocks for causal attention of a
 // whole sequence (tri), else a fixed count cnt per tile.
 constexpr int kDsRows = 128;
 constexpr int kDsKeys = 32;
 constexpr int kDsBlockElems = kDsRows * kDsKeys;
+
+__host__ __device__ constexpr int ds_elem(int row, int key) {
+  return (row >> 5) * (32 * kDsKeys) + key * 32 + (row & 31);
+}
 
 __host__ __device__ inline int ds_kb_lo(int qt, int causal, int window, int delta) {
   if (!causal || window <= 0) return 0;

@@ -243,6 +243,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       // P and dS are formed by all four waves: the score wave of key block kb takes
       // registers 0..7 (query rows 4 g2 + 0..3 and 8 + 4 g2 + 0..3) and receives their dP, the
       // dP wave takes registers 8..15 and receives their S.
+      const int xh = score_wave ? 0 : 2;  // this wave's registers: 4 xh .. 4 xh + 7
+      // register 4 x + e holds query row i0 + 8 x + 4 g2 + e; the statistics are read before the
+      // exchange so that their latency overlaps it
+      f32x4 lse4[2], dl4[2];
+      {
+        const f32x4* st4 = reinterpret_cast<const f32x4*>(stat[buf]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          lse4[u] = st4[2 * (xh + u) + g2] * kLog2e;
+          dl4[u] = st4[8 + 2 * (xh + u) + g2];
+        }
+      }
       if (score_wave) {
 #pragma unroll
         for (int x = 2; x < 4; ++x)
@@ -254,8 +266,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       }
       barrier_lds();
       {
-        const int xh = score_wave ? 0 : 2;  // this wave's registers: 4 xh .. 4 xh + 7
-        f32x4 sv[2], dpv[2], lse4[2], dl4[2];
+        f32x4 sv[2], dpv[2];
         if (score_wave) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
@@ -268,13 +279,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
             sv[u] = xsc[kb][u][lane];
             dpv[u] = f32x4{sacc[8 + 4 * u], sacc[9 + 4 * u], sacc[10 + 4 * u], sacc[11 + 4 * u]};
           }
-        }
-        // register 4 x + e holds query row i0 + 8 x + 4 g2 + e
-        const f32x4* st4 = reinterpret_cast<const f32x4*>(stat[buf]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          lse4[u] = st4[2 * (xh + u) + g2] * kLog2e;
-          dl4[u] = st4[8 + 2 * (xh + u) + g2];
         }
         const bool full = (i0 + MQ <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= i0 + dlt) &&
                           (a.window <= 0 || j0 > i0 + MQ - 1 + dlt - a.window);
@@ -349,10 +353,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       {
         // the transposed fragments of (s, d) are read one (s, d) step ahead of their products
         bf16x8 ado = trf.read(dOs[buf], 0, dsl), aq = trf.read(Qs[buf], 0, dsl);
+        // both row halves' P and dS fragments are read before the first products
+        bf16x8 pfr[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 p0 = pds[0][0][s][lane], p1 = pds[0][1][s][lane];
-          const bf16x8 s0 = pds[1][0][s][lane], s1 = pds[1][1][s][lane];
+          pfr[s][0] = pds[0][0][s][lane];
+          pfr[s][1] = pds[0][1][s][lane];
+          pfr[s][2] = pds[1][0][s][lane];
+          pfr[s][3] = pds[1][1][s][lane];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 p0 = pfr[s][0], p1 = pfr[s][1];
+          const bf16x8 s0 = pfr[s][2], s1 = pfr[s][3];
 #pragma unroll
           for (int d = 0; d < DBW; ++d) {
             const int ns = d + 1 == DBW ? s + 1 : s, nd = d + 1 == DBW ? 0 : d + 1;

@@ -37,7 +37,7 @@ TRAFFIC = {
     "attn_fwd": ("profiles/attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512,32,false,false,false>"),
     "bwd_dkdv": ("profiles/bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512,false,false>"),
     "bwd_dq": ("profiles/bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2,false>"),
-    "decode_split": ("profiles/decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false>"),
+    "decode_split": ("profiles/decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false,false>"),
 }
 
 

@@ -144,7 +144,7 @@ TRAFFIC_SUMMARIES = [
      "dQ kernel of the backward (dQ = scale dS K over the stored dS blocks, two head_dim halves), same workload",
      "Algorithmic bytes: dS blocks read once (1.107 GB), K (33.5 MB); dQ written once (268 MB).  Each dS "
      "block is read by both head_dim halves; the second read is meant to hit in L2."),
-    ("decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false>", "scaled_dot_product_tiled_amd/csrc/attn_decode.hip",
+    ("decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false,false>", "scaled_dot_product_tiled_amd/csrc/attn_decode.hip",
      "paged decode split kernel, B=64 Hq=32 Hkv=8 D=128, 16-token pages, contexts U{512..4096} "
      "(bench.py decode workload)",
      "Algorithmic bytes: K and V of every context token once (619.6 MB per launch, the bench's "

@@ -9,6 +9,7 @@ the C ABI.  Reported:
   decode    paged single-token decode (B=64, Hq=32, Hkv=8, D=128, 16-token pages, contexts
             U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
+            pages_in_order is the same decode with each sequence's pages consecutive in the pool;
   other_workloads  (median of per-call HIP-event timings) forward / backward TFLOP/s of the sliding-window (D=256, W=1024) and padded
             varlen (B=8, lengths U{512..8192}, D=512) workloads, of one context-parallel rank's
             chunk pairs (16k tokens in 8 chunks, D=512) and of the step's workload in IEEE half,
@@ -399,6 +400,37 @@ def main():
     sdpt.binding.profile(False)
     dec_kernels = {n: {"launches": c, "ms_avg": round(t / c, 4)} for n, (c, t) in sdpt.binding.profile_read().items()}
 
+    # the same decode with every sequence's pages laid out in order (page table = consecutive
+    # ids): what the per-page table lookup costs against the permuted pool above
+    def in_order(p):
+        tbl = p["table"].cpu().numpy()
+        ctx = p["ctx_host"]
+        order = [int(tbl[b, j]) for b in range(dw.B) for j in range(-(-int(ctx[b]) // dw.page_size))]
+        idx = torch.tensor(order, dtype=torch.long, device="cuda:0")
+        t2 = np.full_like(tbl, -1)
+        k = 0
+        for b in range(dw.B):
+            n = -(-int(ctx[b]) // dw.page_size)
+            t2[b, :n] = np.arange(k, k + n)
+            k += n
+        return dict(q=p["q"], kc=p["kc"][idx].contiguous(), vc=p["vc"][idx].contiguous(),
+                    table=torch.from_numpy(t2).to("cuda:0"), ctx=p["ctx"])
+
+    cpools = [in_order(p) for p in pools]
+    itc = [0]
+
+    def dec_in_order():
+        p = cpools[itc[0] & 1]
+        sdpt.paged_decode(p["q"], p["kc"], p["vc"], p["table"], p["ctx"], scale=dw.scale, out=outs[itc[0] & 1],
+                          workspace=ws)
+        itc[0] += 1
+
+    for _ in range(4):
+        dec_in_order()
+    torch.cuda.synchronize()
+    ms_dec_in_order = time_events(dec_in_order, n_dec, stream)
+    del cpools
+
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_bytes(dom),
             "ms_per_launch": dom_ms, "flop_per_launch": algo.get(dom, 0.0)}
@@ -435,6 +467,8 @@ def main():
         "kernels": per_kernel,
         "roofline": roof,
         "decode": {"workload": dw.name, "ms": round(ms_dec, 4), "GB/s": round(dec_gbs, 1), "kernels": dec_kernels,
+                   "pages_in_order": {"ms": round(ms_dec_in_order, 4),
+                                      "GB/s": round(dec_bytes / (ms_dec_in_order * 1e-3) / 1e9, 1)},
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "bytes_per_launch": dec_bytes, "traffic": traffic_bytes("decode_split")}},

@@ -8,8 +8,9 @@
 // Three kernels run in stream order:
 //   bwd_pre   delta per (query row, head), fp32;
 //   bwd_dkdv  one workgroup per (batch, kv head, 64-key tile): K and V of the tile stay
-//             in registers, every visible 32-row query tile of every query head of the
-//             group streams through LDS, and dK, dV accumulate in registers (no atomics,
+//             in registers, every visible query tile (32 rows; 64 at head_dim 256) of
+//             every query head of the group streams through LDS, and dK, dV accumulate
+//             in registers (no atomics,
 //             one pass over the group's heads, so the grouped-query sum is exact).  It
 //             also stores dS (bf16) in blocks, so that dQ needs no second pass over
 //             Q K^T and dO V^T;
@@ -97,17 +98,21 @@ __device__ __forceinline__ void dma_stats(float* dst, const float* lse_row0, con
 template <int D, bool SOFTCAP, bool F16>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NK = kDkdvKeys;   // 64 keys per workgroup
-  constexpr int MQ = kDkdvRows;   // 32 query rows per step
+  // query rows per step: RB blocks of 32 (two at head_dim 256, so that a step's tiles are as
+  // large as at 512 and the per-step work is the same)
+  constexpr int RB = D == 256 ? 2 : 1;
+  constexpr int MQ = 32 * RB;
   constexpr int KS = D / 16;
   constexpr int DBW = D / 128;    // 32-wide d blocks owned by each wave
   constexpr int NDMA = dma_rows_per_wave<D, MQ, 4>();
-  static_assert(NK == 64 && MQ == 32, "role split assumes 2 key blocks and one row block");
+  static_assert(NK == 64, "role split assumes 2 key blocks");
   __shared__ __attribute__((aligned(1024))) bf16 Qs[2][MQ * D];
   __shared__ __attribute__((aligned(1024))) bf16 dOs[2][MQ * D];
-  __shared__ __attribute__((aligned(16))) float stat[2][64];
-  __shared__ __attribute__((aligned(16))) f32x4 xdp[2][2][64];        // dP, registers 0..7: [kb][reg/4][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 xsc[2][2][64];        // S, registers 8..15: [kb][reg/4 - 2][lane]
-  __shared__ __attribute__((aligned(16))) bf16x8 pds[2][2][2][64];    // [P|dS][kb][s][lane]
+  __shared__ __attribute__((aligned(16))) float stat[2][64 * RB];         // per 32-row block: LSE, delta
+  // S / dP exchange, [rb][kb][0: dP of registers 0..7 for the score wave, 1: S of registers
+  // 8..15 for the dP wave][reg/4 (mod 2)][lane].  Once a wave has read its half it writes its
+  // P and dS fragments over it (P at [0], dS at [1]): only that wave reads that half.
+  __shared__ __attribute__((aligned(16))) f32x4 xch[RB][2][2][2][64];
 
   const int item = xcd_item(a.per_xcd, a.total_items, a.nkt * a.kv_split, a.balanced);
   if (item < 0) return;
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     // is busy while the matrix cores are; only the small row-statistics copy is issued
     // at the top of the step.
     const int tq_last = tq0 + nq - 1;
-    static_assert(2 * NDMA <= KS / 2, "every copy needs a slot in the S / dP loop");
+    static_assert(2 * NDMA <= KS * RB / 2, "every copy needs a slot in the S / dP loop");
     int hi = 0, qi = 0;  // step k
     // Addresses of step k: Q and dO at (row i0, head hb0 + hi), the row statistics and the dS
     // blocks of that head.  A step advances one head, or after the group's last head returns
@@ -195,7 +200,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     int ds_qt = -1;  // query tile of the dS block index ds_bi (of this wave's key block)
     int64_t ds_bi = -1;
     auto stats = [&](int64_t sofs, int i0s, int buf) {
-      if (wave == 0) dma_stats(stat[buf], a.lse + sofs, a.delta + sofs, i0s, len - 1, lane);
+      if (wave == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          dma_stats(stat[buf] + 64 * rb, a.lse + sofs, a.delta + sofs, i0s + 32 * rb, len - 1, lane);
+      }
     };
     dma_rows<D, MQ, 4>(Qs[0], tile_src_rows<MQ>(qrow, a.q_ss, len - i00), wave, lane);
     dma_rows<D, MQ, 4>(dOs[0], tile_src_rows<MQ>(drow, a.do_ss, len - i00), wave, lane);
@@ -216,72 +225,87 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       wait_vmcnt<0>();
       barrier_lds();  // step k is in LDS; every wave is done with step k-1
 
-      f32x16 sacc;
+      f32x16 sacc[RB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
       {
         const bf16* src = score_wave ? Qs[buf] : dOs[buf];
-        bf16x8 f[4];
-        f[0] = rowf.read(src, 0, 0);
-        f[1] = rowf.read(src, 0, 1);
-        f[2] = rowf.read(src, 0, 2);
+        bf16x8 f[RB][4];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int t = 0; t < 3; ++t) f[rb][t] = rowf.read(src, 32 * rb, t);
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-          if (t + 3 < KS) f[(t + 3) % 4] = rowf.read(src, 0, t + 3);
-          sacc = E16<F16>::mma32(f[t % 4], kv[t], sacc);
-          if ((t & 1) == 0 && t / 2 < 2 * NDMA) {
-            const int j = t / 2;
-            if (j < NDMA)
-              dma_rows_one<D, MQ, 4>(Qs[buf ^ 1], qn, wave, lane, j);
-            else
-              dma_rows_one<D, MQ, 4>(dOs[buf ^ 1], dn, wave, lane, j - NDMA);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            if (t + 3 < KS) f[rb][(t + 3) % 4] = rowf.read(src, 32 * rb, t + 3);
+            sacc[rb] = E16<F16>::mma32(f[rb][t % 4], kv[t], sacc[rb]);
+            const int slot = t * RB + rb;
+            if ((slot & 1) == 0 && slot / 2 < 2 * NDMA) {
+              const int j = slot / 2;
+              if (j < NDMA)
+                dma_rows_one<D, MQ, 4>(Qs[buf ^ 1], qn, wave, lane, j);
+              else
+                dma_rows_one<D, MQ, 4>(dOs[buf ^ 1], dn, wave, lane, j - NDMA);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // sacc: lane = key j0 + 32 kb + ln, register r = query row i0 + 8 (r/4) + 4 g2 + r%4
+      // sacc[rb]: lane = key j0 + 32 kb + ln, register r = query row i0 + 32 rb + 8 (r/4) + 4 g2 + r%4
       // P and dS are formed by all four waves: the score wave of key block kb takes
       // registers 0..7 (query rows 4 g2 + 0..3 and 8 + 4 g2 + 0..3) and receives their dP, the
       // dP wave takes registers 8..15 and receives their S.
       const int xh = score_wave ? 0 : 2;  // this wave's registers: 4 xh .. 4 xh + 7
       // register 4 x + e holds query row i0 + 8 x + 4 g2 + e; the statistics are read before the
       // exchange so that their latency overlaps it
-      f32x4 lse4[2], dl4[2];
-      {
-        const f32x4* st4 = reinterpret_cast<const f32x4*>(stat[buf]);
+      f32x4 lse4[RB][2], dl4[RB][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x4* st4 = reinterpret_cast<const f32x4*>(stat[buf] + 64 * rb);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          lse4[u] = st4[2 * (xh + u) + g2] * kLog2e;
-          dl4[u] = st4[8 + 2 * (xh + u) + g2];
+          lse4[rb][u] = st4[2 * (xh + u) + g2] * kLog2e;
+          dl4[rb][u] = st4[8 + 2 * (xh + u) + g2];
         }
       }
-      if (score_wave) {
 #pragma unroll
-        for (int x = 2; x < 4; ++x)
-          xsc[kb][x - 2][lane] = f32x4{sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]};
-      } else {
+      for (int rb = 0; rb < RB; ++rb) {
+        if (score_wave) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-          xdp[kb][x][lane] = f32x4{sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]};
+          for (int x = 2; x < 4; ++x)
+            xch[rb][kb][1][x - 2][lane] =
+                f32x4{sacc[rb][4 * x], sacc[rb][4 * x + 1], sacc[rb][4 * x + 2], sacc[rb][4 * x + 3]};
+        } else {
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+            xch[rb][kb][0][x][lane] =
+                f32x4{sacc[rb][4 * x], sacc[rb][4 * x + 1], sacc[rb][4 * x + 2], sacc[rb][4 * x + 3]};
+        }
       }
       barrier_lds();
-      {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
         f32x4 sv[2], dpv[2];
         if (score_wave) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            sv[u] = f32x4{sacc[4 * u], sacc[4 * u + 1], sacc[4 * u + 2], sacc[4 * u + 3]};
-            dpv[u] = xdp[kb][u][lane];
+            sv[u] = f32x4{sacc[rb][4 * u], sacc[rb][4 * u + 1], sacc[rb][4 * u + 2], sacc[rb][4 * u + 3]};
+            dpv[u] = xch[rb][kb][0][u][lane];
           }
         } else {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            sv[u] = xsc[kb][u][lane];
-            dpv[u] = f32x4{sacc[8 + 4 * u], sacc[9 + 4 * u], sacc[10 + 4 * u], sacc[11 + 4 * u]};
+            sv[u] = xch[rb][kb][1][u][lane];
+            dpv[u] = f32x4{sacc[rb][8 + 4 * u], sacc[rb][9 + 4 * u], sacc[rb][10 + 4 * u], sacc[rb][11 + 4 * u]};
           }
         }
-        const bool full = (i0 + MQ <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= i0 + dlt) &&
-                          (a.window <= 0 || j0 > i0 + MQ - 1 + dlt - a.window);
+        const int ir = i0 + 32 * rb;  // first query row of this block
+        const bool full = (ir + 32 <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= ir + dlt) &&
+                          (a.window <= 0 || j0 > ir + 31 + dlt - a.window);
         bf16x8 pb, db;
         // under a softcap the score is capped before the exponential and dS takes the cap's
         // derivative 1 - tanh^2 (the stored dS is then the gradient of the uncapped score)
@@ -300,9 +324,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           for (int r = 0; r < 8; ++r) {
             float der;
             const float sx = capped(sv[r >> 2][r & 3], der);
-            const float p = fast_exp2(fmaf(sx, c, -lse4[r >> 2][r & 3]));
+            const float p = fast_exp2(fmaf(sx, c, -lse4[rb][r >> 2][r & 3]));
             pb[r] = E16<F16>::from_float(p);
-            db[r] = E16<F16>::from_float(p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) * der);
+            db[r] = E16<F16>::from_float(p * (dpv[r >> 2][r & 3] - dl4[rb][r >> 2][r & 3]) * der);
           }
         } else {
           // this lane's key is visible from query rows rlo .. rhi-1
@@ -312,19 +336,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           if (a.window > 0) rhi = min(rhi, key + a.window - dlt);
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            const int row = i0 + 8 * (xh + (r >> 2)) + 4 * g2 + (r & 3);
+            const int row = ir + 8 * (xh + (r >> 2)) + 4 * g2 + (r & 3);
             const bool vis = (row >= rlo) & (row < rhi);
             float der;
             const float sx = capped(sv[r >> 2][r & 3], der);
-            const float e = fast_exp2(fmaf(sx, c, -lse4[r >> 2][r & 3]));
+            const float e = fast_exp2(fmaf(sx, c, -lse4[rb][r >> 2][r & 3]));
             const float p = vis ? e : 0.f;
-            const float ds = vis ? p * (dpv[r >> 2][r & 3] - dl4[r >> 2][r & 3]) * der : 0.f;  // +0 when masked
+            const float ds = vis ? p * (dpv[r >> 2][r & 3] - dl4[rb][r >> 2][r & 3]) * der : 0.f;  // +0 when masked
             pb[r] = E16<F16>::from_float(p);
             db[r] = E16<F16>::from_float(ds);
           }
         }
-        pds[0][kb][xh >> 1][lane] = pb;
-        pds[1][kb][xh >> 1][lane] = db;
+        // 16-row half 2 rb + (xh / 2) of P and dS, over the exchange half this wave has read
+        bf16x8* mine = reinterpret_cast<bf16x8*>(&xch[rb][kb][xh >> 1][0][0]);
+        mine[lane] = pb;
+        mine[64 + lane] = db;
         // dS for the dQ product, this lane's key.  db holds query rows 8 xh + 4 g2 + (0..3) and
         // 8 xh + 8 + 4 g2 + (0..3) of the step; lanes l and l + 32 trade four of them so that each
         // holds 8 consecutive rows (8 xh + 8 g2 ..) and writes them with one 16-byte store.
@@ -342,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
           // r[0] carries the lower half's value to every lane, r[1] the upper half's
           const uint32_t got0 = g2 ? r0[0] : r0[1], got1 = g2 ? r1[0] : r1[1];
           const uint32_t o[4] = {g2 ? got0 : w[0], g2 ? got1 : w[1], g2 ? w[2] : got0, g2 ? w[3] : got1};
-          bf16* dst = dshead + bi * kDsBlockElems + ds_elem(i0 & (kDsRows - 1), ln) + 8 * xh + 8 * g2;
+          bf16* dst = dshead + bi * kDsBlockElems + ds_elem(ir & (kDsRows - 1), ln) + 8 * xh + 8 * g2;
           uint4 v;
           __builtin_memcpy(&v, o, 16);
           *reinterpret_cast<uint4*>(dst) = v;
@@ -353,24 +379,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       {
         // the transposed fragments of (s, d) are read one (s, d) step ahead of their products
         bf16x8 ado = trf.read(dOs[buf], 0, dsl), aq = trf.read(Qs[buf], 0, dsl);
-        // both row halves' P and dS fragments are read before the first products
-        bf16x8 pfr[2][4];
+        // every 16-row half's P and dS fragments are read before the first products
+        bf16x8 pfr[2 * RB][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          pfr[s][0] = pds[0][0][s][lane];
-          pfr[s][1] = pds[0][1][s][lane];
-          pfr[s][2] = pds[1][0][s][lane];
-          pfr[s][3] = pds[1][1][s][lane];
+        for (int s = 0; s < 2 * RB; ++s) {
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const bf16x8* src = reinterpret_cast<const bf16x8*>(&xch[s >> 1][x][s & 1][0][0]);
+            pfr[s][x] = src[lane];           // P, key block x
+            pfr[s][2 + x] = src[64 + lane];  // dS, key block x
+          }
         }
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < 2 * RB; ++s) {
           const bf16x8 p0 = pfr[s][0], p1 = pfr[s][1];
           const bf16x8 s0 = pfr[s][2], s1 = pfr[s][3];
 #pragma unroll
           for (int d = 0; d < DBW; ++d) {
             const int ns = d + 1 == DBW ? s + 1 : s, nd = d + 1 == DBW ? 0 : d + 1;
             bf16x8 ado_n = ado, aq_n = aq;
-            if (ns < 2) {
+            if (ns < 2 * RB) {
               ado_n = trf.read(dOs[buf], 16 * ns, dsl + nd);
               aq_n = trf.read(Qs[buf], 16 * ns, dsl + nd);
             }

@@ -177,7 +177,6 @@ constexpr int kFwdRows = 128;   // query rows per forward workgroup
 constexpr int kFwdKeys = 32;    // keys per forward step
 constexpr int kDqSplit512 = 2;  // head_dim slices of a dQ query tile at head_dim 512
 constexpr int kDkdvKeys = 64;   // keys per dK/dV workgroup
-constexpr int kDkdvRows = 32;   // query rows per dK/dV step
 constexpr int kDecodeChunk = 512;  // tokens per decode workgroup
 
 }  // namespace attn

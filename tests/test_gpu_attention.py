@@ -86,6 +86,12 @@ SMALL = [
      [0, 77, 300]),
     ("d256_varlen_window", AttnWorkload(108, "d256 varlen window", 2, 500, 4, 2, 256, window=64,
                                         varlen="pad_mask"), [500, 260]),
+    # head_dim 256 steps take 64 query rows: lengths that end inside the second 32-row block of
+    # a step, and a non-causal case where every step is full except the ragged last one
+    ("d256_causal_ragged", AttnWorkload(131, "d256 causal ragged", 2, 333, 4, 2, 256), None),
+    ("d256_noncausal_ragged", AttnWorkload(132, "d256 non-causal ragged", 1, 271, 4, 1, 256, causal=False),
+     None),
+    ("d256_varlen_pad", AttnWorkload(133, "d256 varlen", 3, 400, 4, 2, 256, varlen="pad_mask"), [400, 37, 97]),
 ]
 
 

@@ -4,8 +4,9 @@ The computation lives in HIP kernels behind a C ABI (include/attn.h, built into
 libattn.so by ``scaled_dot_product_tiled_amd.build``); this package only marshals
 torch tensors into those calls.
 """
-from .binding import (attn_bwd, attn_bwd_chunk, attn_fwd, attn_fwd_chunk, attn_lse_merge, debug,  # noqa: F401
-                      load_library, paged_decode, paged_kv_append, paged_kv_gather)
+from .binding import (attn_bwd, attn_bwd_chunk, attn_bwd_chunk_workspace_bytes, attn_fwd, attn_fwd_chunk,  # noqa: F401
+                      attn_lse_merge, debug, load_library, paged_decode, paged_kv_append, paged_kv_gather)
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "paged_decode",
+__all__ = ["attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_bwd_chunk_workspace_bytes",
+           "attn_lse_merge", "paged_decode",
            "paged_kv_append", "paged_kv_gather", "debug", "load_library"]

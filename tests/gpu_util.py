@@ -43,11 +43,19 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b)) / den if den > 0 else float(np.linalg.norm(a))
 
 
+def first_nonfinite(*ts):
+    """(argument position, flat index, value) of the first non-finite element, or None."""
+    for n, t in enumerate(ts):
+        a = t.detach().float().cpu().numpy() if isinstance(t, torch.Tensor) else np.asarray(t, dtype=np.float64)
+        bad = np.flatnonzero(~np.isfinite(a))
+        if bad.size:
+            return n, int(bad[0]), float(a.reshape(-1)[bad[0]])
+    return None
+
+
 def all_finite(*ts) -> bool:
-    for t in ts:
-        if isinstance(t, torch.Tensor):
-            if not bool(torch.isfinite(t.float()).all()):
-                return False
-        elif not np.isfinite(t).all():
-            return False
-    return True
+    """Every element of every tensor is finite; otherwise prints where the first one is not."""
+    nf = first_nonfinite(*ts)
+    if nf is not None:
+        print(f"first non-finite: tensor #{nf[0]} flat index {nf[1]} value {nf[2]}", flush=True)
+    return nf is None

@@ -16,7 +16,7 @@ the pages' datasets and trained weights, which are not used.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Optional
 
 import numpy as np

@@ -7,7 +7,6 @@ O max-abs 2e-2, dQ/dK/dV relative L2 5e-2, LSE max-abs 1e-2; padded rows and key
 zeros and every output finite.  Bit-exact properties (masks, indexing, padding) are checked on
 raw output bytes.
 """
-import math
 import sys
 
 import numpy as np

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from synth import DECODE_WORKLOADS, AttnWorkload, lengths_to_pad_mask, make_attention_inputs, make_decode_inputs
-from tests.gpu_util import dev, host_bits
+from tests.gpu_util import dev
 
 pytestmark = pytest.mark.gpu
 

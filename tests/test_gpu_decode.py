@@ -1,8 +1,6 @@
 """GPU parity of the paged decode against the float64 oracle, through the C ABI, plus the
 bit-exact page-gather properties: the same logical tokens in different pool pages give the same
 bytes, and unassigned pages or slots past the context (filled with NaN) are never read."""
-import sys
-
 import numpy as np
 import pytest
 import torch

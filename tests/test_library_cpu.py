@@ -4,8 +4,6 @@ import ctypes
 import os
 import re
 
-import pytest
-
 from scaled_dot_product_tiled_amd.binding import (AttnChunkShape, AttnDecodeShape, AttnShape, AttnTensor,
                                                   load_library)
 

@@ -25,7 +25,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import (ATTN_WORKLOADS, DECODE_WORKLOADS, bf16_bits_to_f64, f32_to_bf16_bits,
+from synth import (ATTN_WORKLOADS, DECODE_WORKLOADS, bf16_bits_to_f64,
                    lengths_to_cu_seqlens, lengths_to_pad_mask, make_attention_inputs,
                    make_decode_inputs, pack_rows)
 

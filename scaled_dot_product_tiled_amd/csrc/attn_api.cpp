@@ -64,7 +64,14 @@ attn_status check_shape(const attn_shape* s, int varlen) {
   return ATTN_OK;
 }
 
-size_t meta_bytes(int B, int varlen) { return varlen ? round_up(2 * sizeof(int32_t) * (size_t)B) : 0; }
+// varlen metadata: per-sequence offset, length, and the batch order by decreasing length
+size_t meta_bytes(int B, int varlen) { return varlen ? round_up(3 * sizeof(int32_t) * (size_t)B) : 0; }
+
+// Workgroups per XCD for `total` items of W per unit: with a batch order (see xcd_item) each
+// XCD takes whole units, ceil(units / 8) of them.
+int per_xcd_for(const attn::AttnArgs& a, int total, int W) {
+  return a.order != nullptr ? ((total / W + 7) / 8) * W : (total + 7) / 8;
+}
 
 int varlen_kind(const int32_t* cu, const uint8_t* mask) { return cu ? 2 : (mask ? 1 : 0); }
 
@@ -128,7 +135,7 @@ void plan_rows(attn::AttnArgs& a, int rows) {
   a.nhb = a.r / a.hpt;
   a.nqt = (a.S + a.mpos - 1) / a.mpos;
   a.total_items = a.B * a.Hkv * a.nhb * a.nqt;
-  a.per_xcd = (a.total_items + 7) / 8;
+  a.per_xcd = per_xcd_for(a, a.total_items, a.nqt);
 }
 
 // One forward or backward call, whole sequences or a chunk pair, after argument checks.
@@ -194,7 +201,8 @@ void fill_common(attn::AttnArgs& a, const Call& c, float scale, const int32_t* m
   a.sc_out = c.softcap > 0.f ? c.softcap / scale : 0.f;
   a.seq_off = c.varlen ? meta : nullptr;
   a.seq_len = c.varlen ? meta + c.B : nullptr;
-  a.balanced = c.varlen != 0;  // sequences of different lengths: deal work items in rounds
+  a.balanced = c.varlen != 0;  // sequences of different lengths: see xcd_item
+  a.order = (c.varlen && c.B <= attn::kOrderMaxBatch) ? meta + 2 * c.B : nullptr;
   if (a.packed) {
     a.st_sb = 0;
     a.st_sh = c.total;
@@ -388,15 +396,24 @@ attn_status debug_check_pages(const attn_decode_shape& sh, const int32_t* table,
   return bad ? ATTN_ERR_INVALID_ARG : ATTN_OK;
 }
 
+// Per-sequence offsets and lengths, then the batch order the work items are dealt by.
+attn_status varlen_meta(const Call& c, const int32_t* cu_seqlens, const uint8_t* pad_mask, int32_t* meta,
+                        hipStream_t s) {
+  if (!c.varlen) return ATTN_OK;
+  attn_status st = launch("varlen_prep", s, c.B, [&] {
+    return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, c.total, meta, meta + c.B, s);
+  });
+  if (st || c.B > attn::kOrderMaxBatch) return st;
+  return launch("varlen_order", s, c.B,
+                [&] { return attn::launch_varlen_order(meta + c.B, c.B, meta + 2 * c.B, s); });
+}
+
 attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, const int32_t* cu_seqlens,
                     const uint8_t* pad_mask, void* workspace, hipStream_t s, bool o_f32 = false) {
   int32_t* meta = static_cast<int32_t*>(workspace);
   attn_status st;
   if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
-  if (c.varlen && (st = launch("varlen_prep", s, c.B, [&] {
-                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, c.total, meta, meta + c.B, s);
-                   })))
-    return st;
+  if ((st = varlen_meta(c, cu_seqlens, pad_mask, meta, s))) return st;
   attn::AttnArgs a = {};
   fill_common(a, c, scale, meta);
   set_tensors(a, t, c.varlen == 2, false);
@@ -417,10 +434,7 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(c.B, c.varlen));
   attn_status st;
   if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
-  if (c.varlen && (st = launch("varlen_prep", s, c.B, [&] {
-                     return attn::launch_varlen_prep(pad_mask, cu_seqlens, c.B, c.S, c.total, meta, meta + c.B, s);
-                   })))
-    return st;
+  if ((st = varlen_meta(c, cu_seqlens, pad_mask, meta, s))) return st;
   attn::AttnArgs a = {};
   fill_common(a, c, scale, meta);
   set_tensors(a, t, c.varlen == 2, true);
@@ -448,7 +462,7 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
   kv.kv_split = kv_split_for(c);
   kv.kv_part = kv.kv_split > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(a.dsb) + ds_bytes(c)) : nullptr;
   kv.total_items = c.B * c.Hkv * kv.nkt * kv.kv_split;
-  kv.per_xcd = (kv.total_items + 7) / 8;
+  kv.per_xcd = per_xcd_for(kv, kv.total_items, kv.nkt * kv.kv_split);
   if ((st = launch("bwd_dkdv", s, kv.total_items, [&] { return attn::launch_bwd_dkdv(kv, c.D, s); }))) return st;
   if (kv.kv_split > 1 &&
       (st = launch("bwd_kv_reduce", s, c.B * c.Sk, [&] { return attn::launch_bwd_kv_reduce(kv, c.D, s); })))
@@ -457,7 +471,7 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
   attn::AttnArgs qa = a;
   qa.nqt = (c.S + attn::kDsRows - 1) / attn::kDsRows;
   qa.total_items = c.B * c.Hkv * qa.nqt * qa.r * (c.D == 512 ? attn::kDqSplit512 : 1);
-  qa.per_xcd = (qa.total_items + 7) / 8;
+  qa.per_xcd = per_xcd_for(qa, qa.total_items, qa.nqt * qa.r * (c.D == 512 ? attn::kDqSplit512 : 1));
   return launch("bwd_dq", s, qa.total_items, [&] { return attn::launch_bwd_dq(qa, c.D, s); });
 }
 

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   // P and dS fragments over it (P at [0], dS at [1]): only that wave reads that half.
   __shared__ __attribute__((aligned(16))) f32x4 xch[RB][2][2][2][64];
 
-  const int item = xcd_item(a.per_xcd, a.total_items, a.nkt * a.kv_split, a.balanced);
+  const int item = xcd_item(a.per_xcd, a.total_items, a.nkt * a.kv_split, a.balanced, a.order, a.Hkv);
   if (item < 0) return;
   const int unit = item / (a.nkt * a.kv_split);
   const int rem = item - unit * (a.nkt * a.kv_split);
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][NK * D];
   __shared__ __attribute__((aligned(1024))) bf16 Ss[2][NK * M];
 
-  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt * a.r * NSPLIT, a.balanced);
+  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt * a.r * NSPLIT, a.balanced, a.order, a.Hkv);
   if (item < 0) return;
   // items: (batch, kv head) units, query tiles from the last one down, then the group's
   // heads and the column slices, so that the workgroups sharing an XCD read the same K

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
   __shared__ __attribute__((aligned(1024))) bf16 Vs[N * D];
   __shared__ int restart_flag[2][4];
 
-  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt, a.balanced);
+  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt, a.balanced, a.order, a.Hkv * a.nhb);
   if (item < 0) return;
   const int unit = item / a.nqt;
   const int qt = a.nqt - 1 - (item - unit * a.nqt);  // longest causal rows first

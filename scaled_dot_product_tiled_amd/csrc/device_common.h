@@ -310,11 +310,27 @@ __device__ __forceinline__ void add4(float* p, float a, float b, float c, float 
 // Consecutive workgroup ids land on consecutive XCDs (id % 8).  When every unit carries the
 // same work (dense inputs), the items of one XCD are taken from one contiguous range of the
 // item list, heaviest first within each unit: the workgroups of a unit then share K/V in
-// that XCD's L2.  When units differ (variable lengths: whole units on one XCD would leave
-// the XCDs with short sequences idle), items are dealt in rounds instead, the heaviest item
-// of every unit first, with the unit order rotated by one each round so that every unit
-// visits every XCD.
-__device__ __forceinline__ int xcd_item(int per_xcd, int total, int W, int balanced) {
+// that XCD's L2.  When units differ (variable lengths), whole units still stay on one XCD,
+// but they are dealt to the XCDs by decreasing length in a snake order (XCD 0..7, then
+// 7..0, ...), `upb` consecutive units per sequence, which evens out the XCDs' totals; an XCD
+// takes its units one after the other, each unit's items heaviest first, so that the
+// workgroups running together on it stream the same tiles (taking its units' items in rounds
+// instead thrashed its L2).  The grid then holds 8 x ceil(units / 8) x W workgroups.  Without
+// an order (very large batches), items are dealt in rounds over all units, the unit order
+// rotated by one each round so that every unit visits every XCD.
+__device__ __forceinline__ int xcd_item(int per_xcd, int total, int W, int balanced, const int32_t* order,
+                                        int upb) {
+  if (balanced && order != nullptr) {
+    const int U = total / W;
+    const int upx = (U + 7) / 8;  // units per XCD
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int j = slot / W, r = slot - j * W;  // unit-major within the XCD
+    if (j >= upx) return -1;
+    const int rho = 8 * j + ((j & 1) ? 7 - xcd : xcd);  // rank of the unit by decreasing length
+    if (rho >= U) return -1;
+    const int unit = order[rho / upb] * upb + rho % upb;
+    return unit * W + r;
+  }
   if (balanced) {
     const int k = blockIdx.x;
     if (k >= total) return -1;

@@ -68,6 +68,7 @@ struct AttnArgs {
   float c;                  // scale * log2(e)
   int per_xcd, total_items;
   int balanced;             // deal work items in rounds (see xcd_item)
+  const int32_t* order;     // batch indices by decreasing length (varlen), or null
 };
 
 struct DecodeArgs {
@@ -157,6 +158,9 @@ __host__ __device__ inline int64_t ds_block_index(int qt, int kb, int causal, in
 // Launchers (return the HIP launch status).
 hipError_t launch_varlen_prep(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S, int total,
                               int32_t* seq_off, int32_t* seq_len, hipStream_t stream);
+// Batch indices by decreasing length (ties by index), from the lengths varlen_prep wrote.
+constexpr int kOrderMaxBatch = 4096;  // larger batches keep the plain round order
+hipError_t launch_varlen_order(const int32_t* seq_len, int B, int32_t* order, hipStream_t stream);
 // Debug-mode metadata checks: synchronise the stream and set bad when the metadata is invalid.
 hipError_t check_varlen_meta(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S, int total,
                              hipStream_t stream, bool& bad);

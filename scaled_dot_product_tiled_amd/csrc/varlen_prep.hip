@@ -46,6 +46,25 @@ hipError_t launch_varlen_prep(const uint8_t* pad_mask, const int32_t* cu_seqlens
   return hipGetLastError();
 }
 
+// Rank of sequence b among all B by decreasing length, ties by index: the number of sequences
+// that come before it.  O(B^2) reads of B lengths, all from cache; used for B <= kOrderMaxBatch.
+__global__ __launch_bounds__(256) void varlen_order_kernel(const int32_t* seq_len, int B, int32_t* order) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int lb = seq_len[b];
+  int rank = 0;
+  for (int o = 0; o < B; ++o) {
+    const int lo = seq_len[o];
+    rank += (lo > lb) | ((lo == lb) & (o < b));
+  }
+  order[rank] = b;
+}
+
+hipError_t launch_varlen_order(const int32_t* seq_len, int B, int32_t* order, hipStream_t stream) {
+  hipLaunchKernelGGL(varlen_order_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, seq_len, B, order);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Metadata checks (debug mode).  Any thread that finds a violation stores 1 to the error word.
 // ---------------------------------------------------------------------------

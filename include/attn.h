@@ -95,8 +95,8 @@ typedef struct {
  *   pad_mask    device uint8 (B, S), row-major, 1 = valid; each row must be a
  *               prefix of ones (right padding); or NULL.  At most one of
  *               cu_seqlens and pad_mask may be given.  Their contents are not
- *               checked; lengths are clamped to [0, S] so no access leaves the
- *               buffers.
+ *               checked (except in debug mode, see attn_debug); lengths are
+ *               clamped to [0, S] so no access leaves the buffers.
  *   workspace   device scratch of at least attn_fwd_workspace_bytes(shape,
  *               varlen) bytes (0 for dense inputs), 256-byte aligned
  * The first page's Results section records that the forward's outputs are kept

@@ -113,10 +113,11 @@ def other_workload(name, steps, stream, softcap=0.0, **changes):
 def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     """One context-parallel rank's share of causal attention at 16k tokens (8 chunks of 2048
     positions, D=512, GQA 32/4): the last rank's query chunk against every key/value chunk
-    that it sees (7 whole chunks and its own diagonal one).  Forward = one attn_fwd_chunk per
-    pair into fp32 partials and an attn_lse_merge after each (the last one writes bf16 O);
-    backward = one attn_bwd_chunk per pair adding into fp32 dQ, dK, dV.  Device-side N(0,1)
-    draws."""
+    that it sees (7 whole chunks and its own diagonal one).  Forward = attn_fwd_chunk for the
+    first pair into the fp32 running O and LSE, then one attn_fwd_chunk_merge per further pair
+    (the last one writes bf16 O); the two-step form (attn_fwd_chunk into an fp32 partial, then
+    attn_lse_merge) is timed beside it.  Backward = one attn_bwd_chunk per pair adding into fp32
+    dQ, dK, dV.  Device-side N(0,1) draws."""
     import torch
     import scaled_dot_product_tiled_amd as sdpt
     gen = torch.Generator(device="cuda:0")
@@ -144,6 +145,14 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
 
     def fwd():
         for i, (k0, k1) in enumerate(ks):
+            if i == 0:
+                sdpt.attn_fwd_chunk(q, k[:, k0:k1], v[:, k0:k1], q0, k0, scale=scale, out=acc_o, lse=acc_l)
+            else:
+                sdpt.attn_fwd_chunk_merge(q, k[:, k0:k1], v[:, k0:k1], q0, k0, acc_o, acc_l, scale=scale,
+                                          out=o if i == len(ks) - 1 else None)
+
+    def fwd_two_step():
+        for i, (k0, k1) in enumerate(ks):
             dst = (acc_o, acc_l) if i == 0 else (part, part_l)
             sdpt.attn_fwd_chunk(q, k[:, k0:k1], v[:, k0:k1], q0, k0, scale=scale, out=dst[0], lse=dst[1])
             if i > 0:
@@ -157,6 +166,7 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     fwd()
     bwd()
     torch.cuda.synchronize()
+    ms_f2 = time_median(fwd_two_step, steps, stream)
     ms_f = time_median(fwd, steps, stream)
     ms_b = time_median(bwd, steps, stream)
     sdpt.binding.profile(True)
@@ -169,7 +179,7 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     ff = 4.0 * D * pairs
     res = {"workload": f"ring context-parallel rank share, causal GQA d{D} (chunk {chunk} of {n_chunks}, "
                        f"Hq{Hq} Hkv{Hkv}, last rank: {rank + 1} chunk pairs)",
-           "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+           "pairs": pairs, "fwd_ms": round(ms_f, 4), "fwd_ms_two_step": round(ms_f2, 4), "bwd_ms": round(ms_b, 4),
            "fwd_tflops": round(ff / ms_f / 1e9, 2), "bwd_tflops": round(2.5 * ff / ms_b / 1e9, 2),
            "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2), "kernels": kern}
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)

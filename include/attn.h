@@ -217,6 +217,30 @@ attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D,
                            attn_tensor o_part, const float* lse_part,
                            attn_tensor out, int out_dtype, void* stream);
 
+/*
+ * attn_fwd_chunk_merge: attn_fwd_chunk of one chunk pair with its partial merged straight
+ * into a running result, in one pass (the same ring step as attn_fwd_chunk followed by
+ * attn_lse_merge, first page, section Integration, without the fp32 partial going through
+ * memory).  With (O_p, L_p) the pair's partial as attn_fwd_chunk defines it:
+ *   lse' = ln(e^lse + e^L_p),  o' = e^(lse - lse') o + e^(L_p - lse') O_p.
+ * The result equals attn_fwd_chunk (o_dtype ATTN_DTYPE_F32) then attn_lse_merge bit for
+ * bit.  A running row with lse = -inf has weight 0 and its o is not read, so a ring may
+ * start from lse = -inf everywhere and o uninitialised (the first pair's call then writes
+ * its partial exactly).
+ *   q, k, v, shape, scale, causal, window, softcap, q_pos0, k_pos0   as attn_fwd_chunk
+ *   o     fp32 (B, Sq, Hq, D) with attn_tensor strides, read and written
+ *   lse   device fp32 (B, Hq, Sq) contiguous, read and written
+ *   out   (B, Sq, Hq, D) in the inputs' dtype: if out.ptr is not NULL, the merged o rounded
+ *         to it (round to nearest even) is also written there, for the row's last pair; it
+ *         must not overlap o
+ * No workspace.  Each call is one kernel; calls on one stream merge in order.
+ */
+attn_status attn_fwd_chunk_merge(const attn_chunk_shape* shape,
+                                 attn_tensor q, attn_tensor k, attn_tensor v,
+                                 float scale, int causal, int window, float softcap,
+                                 int64_t q_pos0, int64_t k_pos0,
+                                 attn_tensor o, float* lse, attn_tensor out, void* stream);
+
 /* Sizes of one paged decode call.
  *   B                 sequences, one query token each
  *   Hq, Hkv, D        heads and head_dim (D = 128)

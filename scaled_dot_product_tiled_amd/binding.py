@@ -51,8 +51,8 @@ class AttnDecodeShape(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "paged_decode",
-           "paged_kv_append", "paged_kv_gather", "attn_debug",
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "attn_fwd_chunk_merge",
+           "paged_decode", "paged_kv_append", "paged_kv_gather", "attn_debug",
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read")
@@ -89,6 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, AttnTensor, vp,
                                    AttnTensor, vp, AttnTensor, ctypes.c_int, vp]
     lib.attn_lse_merge.restype = ctypes.c_int
+    lib.attn_fwd_chunk_merge.argtypes = [P(AttnChunkShape), AttnTensor, AttnTensor, AttnTensor, ctypes.c_float,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_float, i64, i64, AttnTensor, vp,
+                                         AttnTensor, vp]
+    lib.attn_fwd_chunk_merge.restype = ctypes.c_int
     lib.paged_decode.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int64, ctypes.c_int64, AttnTensor, AttnTensor,
                                  vp, vp, ctypes.c_float, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz,
                                  vp]
@@ -394,6 +398,32 @@ def attn_lse_merge(o: torch.Tensor, lse: torch.Tensor, o_part: torch.Tensor, lse
                             lse_part.data_ptr(), _tensor(out, False) if out is not None else AttnTensor(None, 0, 0, 0),
                             _DT16[out.dtype] if out is not None else DTYPE_BF16, _stream())
     _check(st, "attn_lse_merge")
+
+
+def attn_fwd_chunk_merge(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos0: int, k_pos0: int,
+                         o: torch.Tensor, lse: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
+                         window: int = 0, out: Optional[torch.Tensor] = None, softcap: float = 0.0) -> None:
+    """In place: (o, lse) <- log-sum-exp merge of the running (o, lse) (fp32 (B,Sq,Hq,D), (B,Hq,Sq)) and
+    the partial of the query chunk q at positions q_pos0.. against the key/value chunk k/v at
+    k_pos0.. (attn_fwd_chunk then attn_lse_merge in one kernel).  Rows with lse = -inf take the
+    partial whatever o holds.  With out (B,Sq,Hq,D) in q's dtype, the merged O is rounded into it."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _half(t, n, q.dtype)
+    shape = _chunk_shape(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.D)
+    if o.dtype != torch.float32 or o.stride(-1) != 1 or not o.is_cuda:
+        raise TypeError("o must be a float32 device tensor with a contiguous last dimension")
+    if out is not None:
+        _half(out, "out", q.dtype)
+        _expect(out, tuple(q.shape), "out")
+    _check_chunk_shapes(shape, q, k, v, lse=lse, o=o)
+    st = lib.attn_fwd_chunk_merge(ctypes.byref(shape), _tensor(q, False), _tensor(k, False), _tensor(v, False),
+                                  float(scale), int(bool(causal)), int(window), float(softcap), int(q_pos0),
+                                  int(k_pos0), _tensor(o, False), lse.data_ptr(),
+                                  _tensor(out, False) if out is not None else AttnTensor(None, 0, 0, 0), _stream())
+    _check(st, "attn_fwd_chunk_merge")
 
 
 def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

@@ -408,8 +408,13 @@ attn_status varlen_meta(const Call& c, const int32_t* cu_seqlens, const uint8_t*
                 [&] { return attn::launch_varlen_order(meta + c.B, c.B, meta + 2 * c.B, s); });
 }
 
+// Where the forward puts its result: O in the inputs' 16-bit type, O in fp32 (a chunk partial),
+// or merged into a running fp32 (O, LSE) with an optional 16-bit copy of the merged O.
+enum class FwdOut { half, f32, merge };
+
 attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, const int32_t* cu_seqlens,
-                    const uint8_t* pad_mask, void* workspace, hipStream_t s, bool o_f32 = false) {
+                    const uint8_t* pad_mask, void* workspace, hipStream_t s, FwdOut mode = FwdOut::half,
+                    attn_tensor final16 = {}) {
   int32_t* meta = static_cast<int32_t*>(workspace);
   attn_status st;
   if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
@@ -417,13 +422,19 @@ attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, co
   attn::AttnArgs a = {};
   fill_common(a, c, scale, meta);
   set_tensors(a, t, c.varlen == 2, false);
-  if (o_f32) {
+  if (mode != FwdOut::half) {
     a.out = nullptr;
     a.out_f32 = static_cast<float*>(t.o.ptr);
   }
+  if (mode == FwdOut::merge) {
+    a.merge = 1;
+    a.out = static_cast<__bf16*>(final16.ptr);
+    set_tensor(final16, false, a.r_sb, a.r_ss, a.r_sh);
+  }
   a.lse = lse;
   plan_rows(a, attn::kFwdRows);
-  return launch("attn_fwd", s, a.total_items, [&] { return attn::launch_fwd(a, c.D, s); });
+  return launch(mode == FwdOut::merge ? "attn_fwd_merge" : "attn_fwd", s, a.total_items,
+                [&] { return attn::launch_fwd(a, c.D, s); });
 }
 
 attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* lse, const int32_t* cu_seqlens,
@@ -560,7 +571,25 @@ attn_status attn_fwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
   if (shape->B == 0 || shape->Sq == 0) return ATTN_OK;
   const Tensors t = {q, k, v, o, {}, {}, {}, {}};
   return run_fwd(with_softcap(chunk_call(shape, causal, window, q_pos0, k_pos0), softcap), t, scale, lse, nullptr,
-                 nullptr, nullptr, static_cast<hipStream_t>(stream), o_dtype == ATTN_DTYPE_F32);
+                 nullptr, nullptr, static_cast<hipStream_t>(stream),
+                 o_dtype == ATTN_DTYPE_F32 ? FwdOut::f32 : FwdOut::half);
+}
+
+attn_status attn_fwd_chunk_merge(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v,
+                                 float scale, int causal, int window, float softcap, int64_t q_pos0, int64_t k_pos0,
+                                 attn_tensor o, float* lse, attn_tensor out, void* stream) {
+  attn_status st = check_chunk(shape, causal, window, q_pos0, k_pos0);
+  if (st != ATTN_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
+  if ((st = check_tensor(q, false)) || (st = check_tensor(k, false)) || (st = check_tensor(v, false)) ||
+      (st = check_tensor(o, false)))
+    return st;
+  if (out.ptr != nullptr && (st = check_tensor(out, false))) return st;
+  if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
+  if (shape->B == 0 || shape->Sq == 0) return ATTN_OK;
+  const Tensors t = {q, k, v, o, {}, {}, {}, {}};
+  return run_fwd(with_softcap(chunk_call(shape, causal, window, q_pos0, k_pos0), softcap), t, scale, lse, nullptr,
+                 nullptr, nullptr, static_cast<hipStream_t>(stream), FwdOut::merge, out);
 }
 
 attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,

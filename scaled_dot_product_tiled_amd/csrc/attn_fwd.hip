@@ -45,11 +45,11 @@ namespace attn {
 constexpr float kRefSlack = 32.0f;
 constexpr float kRefSlackF16 = 15.0f;
 
-template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
-// At head_dim 256 a wave fits in 256 registers, so two workgroups share a compute unit and
-// one's softmax and barriers overlap the other's matrix work; at 512 the accumulators alone
-// take 256 registers.
-__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) {
+// MERGE: instead of storing the row's O and LSE, merge them into a running result (fp32 O
+// in out_f32, LSE in lse) by log-sum-exp weighting and optionally round the merged O to the
+// 16-bit out: the chunk-pair forward and the merge of its partial in one pass.
+template <int D, int N, bool EXACT, bool SOFTCAP, bool F16, bool MERGE>
+__device__ __forceinline__ void fwd_body(AttnArgs a) {
   constexpr int NKB = N / 32;  // 32-key blocks per tile
   constexpr int NS = N / 16;   // 16-key steps per tile
   constexpr int KS = D / 16;
@@ -255,36 +255,83 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) 
   if (wrow) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     const int64_t oo = b * a.o_sb + (int64_t)(off + pos) * a.o_ss + h * a.o_sh + 4 * g2;
-    auto store = [&](auto* op) {
+    if constexpr (MERGE) {
+      const int64_t li = b * a.st_sb + h * a.st_sh + off + pos;
+      // Both lanes of the row read its running LSE before the first one stores the merged
+      // value (one wave, loads before the store in program order).  The running O is read
+      // only where it has weight, so the first merge may start from LSE = -inf and any O.
+      const float lp = l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : -INFINITY;
+      const MergeWeights w = lse_merge_weights(a.lse[li], lp);
+      float* ro = a.out_f32 + oo;
+      bf16* r16 = a.out ? a.out + b * a.r_sb + (int64_t)(off + pos) * a.r_ss + h * a.r_sh + 4 * g2 : nullptr;
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int qa = 0; qa < 4; ++qa)
-          st4<F16>(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv, oacc[d][4 * qa + 2] * inv,
-               oacc[d][4 * qa + 3] * inv);
-    };
-    if (a.out_f32)
-      store(a.out_f32 + oo);  // a partial over one key chunk: rounded once, when the partials are merged
-    else
-      store(a.out + oo);
-    if (g2 == 0)
-      a.lse[b * a.st_sb + h * a.st_sh + off + pos] =
-          l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : (a.empty_lse_ninf ? -INFINITY : 0.f);
+        for (int qa = 0; qa < 4; ++qa) {
+          float* p = ro + 32 * d + 8 * qa;
+          float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (w.w1 > 0.f) x = *reinterpret_cast<const float4*>(p);
+          const float y0 = lse_merge_value(w, x.x, oacc[d][4 * qa] * inv);
+          const float y1 = lse_merge_value(w, x.y, oacc[d][4 * qa + 1] * inv);
+          const float y2 = lse_merge_value(w, x.z, oacc[d][4 * qa + 2] * inv);
+          const float y3 = lse_merge_value(w, x.w, oacc[d][4 * qa + 3] * inv);
+          stg4(p, y0, y1, y2, y3);
+          if (r16) stg4e<F16>(r16 + 32 * d + 8 * qa, y0, y1, y2, y3);
+        }
+      if (g2 == 0) a.lse[li] = w.lse;
+    } else {
+      auto store = [&](auto* op) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+          for (int qa = 0; qa < 4; ++qa)
+            st4<F16>(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv,
+                     oacc[d][4 * qa + 2] * inv, oacc[d][4 * qa + 3] * inv);
+      };
+      if (a.out_f32)
+        store(a.out_f32 + oo);  // a partial over one key chunk: rounded once, when the partials are merged
+      else
+        store(a.out + oo);
+      if (g2 == 0)
+        a.lse[b * a.st_sb + h * a.st_sh + off + pos] =
+            l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : (a.empty_lse_ninf ? -INFINITY : 0.f);
+    }
   }
+}
+
+// At head_dim 256 a wave fits in 256 registers, so two workgroups share a compute unit and
+// one's softmax and barriers overlap the other's matrix work; at 512 the accumulators alone
+// take 256 registers.
+template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
+__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) {
+  fwd_body<D, N, EXACT, SOFTCAP, F16, false>(a);
+}
+
+template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
+__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_merge_kernel(AttnArgs a) {
+  fwd_body<D, N, EXACT, SOFTCAP, F16, true>(a);
+}
+
+template <int D, bool EXACT, bool SOFTCAP, bool F16>
+void launch_fwd_one(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid(8 * a.per_xcd), block(256);
+  if (a.merge)
+    hipLaunchKernelGGL((fwd_merge_kernel<D, kFwdKeys, EXACT, SOFTCAP, F16>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, kFwdKeys, EXACT, SOFTCAP, F16>), grid, block, 0, stream, a);
 }
 
 template <bool F16>
 hipError_t launch_fwd_t(const AttnArgs& a, int D, hipStream_t stream) {
-  const dim3 grid(8 * a.per_xcd), block(256);
   const bool sc = a.softcap > 0.f;
   if (D == 512 && !sc)
-    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, false, F16>), grid, block, 0, stream, a);
+    launch_fwd_one<512, false, false, F16>(a, stream);
   else if (D == 512)
-    hipLaunchKernelGGL((fwd_kernel<512, kFwdKeys, false, true, F16>), grid, block, 0, stream, a);
+    launch_fwd_one<512, false, true, F16>(a, stream);
   else if (D == 256 && !sc)
-    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, false, F16>), grid, block, 0, stream, a);
+    launch_fwd_one<256, true, false, F16>(a, stream);
   else if (D == 256)
-    hipLaunchKernelGGL((fwd_kernel<256, kFwdKeys, true, true, F16>), grid, block, 0, stream, a);
+    launch_fwd_one<256, true, true, F16>(a, stream);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

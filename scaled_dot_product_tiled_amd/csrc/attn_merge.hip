@@ -37,18 +37,9 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   const int s = bs % a.S;
   const int b = bs / a.S;
   const int64_t li = ((int64_t)b * a.H + h) * a.S + s;
-  const float l1 = a.lse[li], l2 = a.lse_part[li];
-  const float m = fmaxf(l1, l2);
+  const MergeWeights w = lse_merge_weights(a.lse[li], a.lse_part[li]);
   float* o1 = a.o + b * a.o_sb + (int64_t)s * a.o_ss + h * a.o_sh + 8 * t;
   const float* o2 = a.o_part + b * a.p_sb + (int64_t)s * a.p_ss + h * a.p_sh + 8 * t;
-  float w1 = 0.f, w2 = 0.f, lse = -INFINITY;
-  if (m > -INFINITY) {
-    const float e1 = expf(l1 - m), e2 = expf(l2 - m);  // the larger is exactly 1; e^-inf = 0
-    const float tot = e1 + e2;
-    w1 = e1 / tot;
-    w2 = e2 / tot;
-    lse = m + log1pf(fminf(e1, e2));
-  }
   float y[8];
 #pragma unroll
   for (int hv = 0; hv < 2; ++hv) {
@@ -56,12 +47,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     const float4 x2 = *reinterpret_cast<const float4*>(o2 + 4 * hv);
     const float a1[4] = {x1.x, x1.y, x1.z, x1.w}, a2[4] = {x2.x, x2.y, x2.z, x2.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // a zero weight selects, so a non-finite value in an unused partial cannot leak in
-      const float v1 = w1 > 0.f ? w1 * a1[e] : 0.f;
-      const float v2 = w2 > 0.f ? w2 * a2[e] : 0.f;
-      y[4 * hv + e] = v1 + v2;
-    }
+    for (int e = 0; e < 4; ++e) y[4 * hv + e] = lse_merge_value(w, a1[e], a2[e]);
   }
   stg4(o1, y[0], y[1], y[2], y[3]);
   stg4(o1 + 4, y[4], y[5], y[6], y[7]);
@@ -70,7 +56,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     stg4e<F16>(r, y[0], y[1], y[2], y[3]);
     stg4e<F16>(r + 4, y[4], y[5], y[6], y[7]);
   }
-  if (t == 0) a.lse[li] = lse;
+  if (t == 0) a.lse[li] = w.lse;
 }
 
 template <bool F16>

@@ -296,6 +296,38 @@ __device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d)
 template <bool F16>
 __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) { stg4(p, a, b, c, d); }
 
+// Log-sum-exp merge of two partial results of one query row over disjoint key sets:
+// L = ln(e^l1 + e^l2) and O = e^(l1 - L) O1 + e^(l2 - L) O2.  The larger LSE is the
+// reference, so the two exponentials are 1 and e^-|l1 - l2| and never overflow; a partial
+// with LSE = -inf gets weight 0, and two of them give L = -inf.  The standalone merge
+// kernel and the forward's merging epilogue both use these two functions, with
+// contraction off, so the fused and the two-step paths round identically.
+struct MergeWeights {
+  float w1, w2, lse;
+};
+
+__device__ __forceinline__ MergeWeights lse_merge_weights(float l1, float l2) {
+  MergeWeights w = {0.f, 0.f, -INFINITY};
+  const float m = fmaxf(l1, l2);
+  if (m > -INFINITY) {
+    const float e1 = expf(l1 - m), e2 = expf(l2 - m);  // the larger is exactly 1; e^-inf = 0
+    const float tot = e1 + e2;
+    w.w1 = e1 / tot;
+    w.w2 = e2 / tot;
+    w.lse = m + log1pf(fminf(e1, e2));
+  }
+  return w;
+}
+
+// One merged element.  A zero weight selects, so a non-finite value in a partial that does
+// not contribute cannot leak in.
+__device__ __forceinline__ float lse_merge_value(const MergeWeights& w, float a1, float a2) {
+#pragma clang fp contract(off)
+  const float v1 = w.w1 > 0.f ? w.w1 * a1 : 0.f;
+  const float v2 = w.w2 > 0.f ? w.w2 * a2 : 0.f;
+  return v1 + v2;
+}
+
 // p[0..3] += (a, b, c, d) in fp32; p is owned by this lane alone.
 __device__ __forceinline__ void add4(float* p, float a, float b, float c, float d) {
   float4 v = *reinterpret_cast<const float4*>(p);

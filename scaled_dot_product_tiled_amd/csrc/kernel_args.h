@@ -69,6 +69,10 @@ struct AttnArgs {
   int per_xcd, total_items;
   int balanced;             // deal work items in rounds (see xcd_item)
   const int32_t* order;     // batch indices by decreasing length (varlen), or null
+  // forward, merge: out_f32 and lse hold a running result that the row's O and LSE are
+  // merged into; out (strides r_*), if not NULL, receives the merged O in 16 bits
+  int merge;
+  int64_t r_sb, r_ss, r_sh;
 };
 
 struct DecodeArgs {

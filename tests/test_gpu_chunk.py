@@ -1,11 +1,12 @@
-"""GPU parity of the chunk-pair calls (attn_fwd_chunk, attn_bwd_chunk, attn_lse_merge) against the
-float64 oracle, through the C ABI.
+"""GPU parity of the chunk-pair calls (attn_fwd_chunk, attn_bwd_chunk, attn_lse_merge,
+attn_fwd_chunk_merge) against the float64 oracle, through the C ABI.
 
 A sequence is cut into chunks, as a ring of context-parallel ranks would hold it; every query chunk
 meets every key/value chunk (fully masked pairs included) at its true positions.  Checked:
   * each pair's partial O and LSE against the oracle's chunk forward (rows that see no key of the
     pair: O exactly zero, LSE exactly -inf);
-  * the partials merged with attn_lse_merge against the oracle's whole-sequence forward;
+  * the partials merged with attn_lse_merge against the oracle's whole-sequence forward, and the
+    fused forward-and-merge call bit for bit against the two-step one;
   * each pair's gradient parts against the oracle's chunk backward (fed the oracle's own final O
     and LSE), and the parts summed in fp32 against the oracle's whole-sequence backward.
 Tolerances as for the whole-sequence path: O max-abs 2e-2, LSE max-abs 1e-2, gradients relative
@@ -18,7 +19,7 @@ import pytest
 import torch
 
 import oracle
-from synth import AttnWorkload, bf16_bits_to_f64, make_attention_inputs
+from synth import AttnWorkload, bf16_bits_to_f64, bits_to_f64, make_attention_inputs
 from tests.gpu_util import GRAD_REL_L2, LSE_MAX_ABS, O_MAX_ABS, all_finite, dev, host, host_bits, max_abs, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -146,6 +147,54 @@ def test_ring_chunks_match_oracle(case):
     for name_, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         err = rel_l2(host(got), ref)
         assert err <= GRAD_REL_L2, (name_, err)
+
+
+FUSED = RING + [("f16_d512_ragged", AttnWorkload(211, "ring f16 d512", 1, 600, 8, 2, 512, dtype="f16"),
+                  [0, 256, 512, 600])]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_fused_merge_matches_chunk_then_merge(case):
+    """attn_fwd_chunk_merge, started from LSE = -inf and a NaN-filled running O, against
+    attn_fwd_chunk into an fp32 partial followed by attn_lse_merge, pair by pair in a ring's
+    order (the rank's own chunk first, then the chunks before it, wrapping): the running fp32 O,
+    the LSE and the final 16-bit O equal bit for bit after every pair; the final result also
+    against the whole-sequence oracle."""
+    name, w, bounds = case[:3]
+    cap = case[3] if len(case) > 3 else 0.0
+    say(f"[fused merge {name}] B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} causal={w.causal} W={w.window} "
+        f"chunks={bounds} cap={cap} dtype={w.dtype}")
+    inp = make_attention_inputs(w, seed=0)
+    q, k, v = (dev(inp[x], w.dtype) for x in ("q", "k", "v"))
+    n = len(bounds) - 1
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, softcap=cap)
+    f = {x: bits_to_f64(inp[x], w.dtype) for x in ("q", "k", "v")}
+    ro, rl = oracle.attention_forward(f["q"], f["k"], f["v"], w.scale, w.causal, w.window, None, cap)
+    for a in range(n):
+        q0, q1 = bounds[a], bounds[a + 1]
+        qa = q[:, q0:q1]
+        f_o = torch.full((w.B, q1 - q0, w.Hq, w.D), float("nan"), device="cuda:0")
+        f_l = torch.full((w.B, w.Hq, q1 - q0), -float("inf"), device="cuda:0")
+        f_out, s_out = torch.empty_like(qa), torch.empty_like(qa)
+        s_o = s_l = None
+        order = [(a - i) % n for i in range(n)]
+        for i, c in enumerate(order):
+            k0, k1 = bounds[c], bounds[c + 1]
+            last = i == n - 1
+            sdpt.attn_fwd_chunk_merge(qa, k[:, k0:k1], v[:, k0:k1], q0, k0, f_o, f_l, out=f_out if last else None,
+                                      **kw)
+            po, pl = sdpt.attn_fwd_chunk(qa, k[:, k0:k1], v[:, k0:k1], q0, k0, **kw)
+            if s_o is None:
+                s_o, s_l = po, pl
+            else:
+                sdpt.attn_lse_merge(s_o, s_l, po, pl, out=s_out if last else None)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_bits(f_o), host_bits(s_o)), (a, c)
+            assert np.array_equal(host_bits(f_l), host_bits(s_l)), (a, c)
+        assert np.array_equal(host_bits(f_out), host_bits(s_out)), a
+        assert all_finite(f_out, f_l)
+        assert max_abs(host(f_out), ro[:, q0:q1]) <= O_MAX_ABS, a
+        assert max_abs(host(f_l), rl[:, :, q0:q1]) <= LSE_MAX_ABS, a
 
 
 def test_pairs_without_visible_keys_and_far_positions():

@@ -185,6 +185,19 @@ def test_chunk_and_merge_checks():
     assert merge(B=0, odt=2) == OK
     assert merge(B=0, odt=1) == INVALID                                 # the final output is 16-bit
     assert merge(B=0, out=_t()) == OK
+
+    def fmerge(shape=c, causal=1, window=0, qp=0, kp=0, lse=0x20000, o=None, out=None, cap=0.0, scale=0.05):
+        return lib.attn_fwd_chunk_merge(ctypes.byref(shape), _t(), _t(), _t(), scale, causal, window, cap, qp, kp,
+                                        o or _t(), lse, out or AttnTensor(None, 0, 0, 0), None)
+    assert fmerge(causal=0, window=8) == UNSUPPORTED
+    assert fmerge(qp=-5) == INVALID
+    assert fmerge(lse=0) == INVALID and fmerge(lse=0x20002) == INVALID
+    assert fmerge(o=_t(ptr=0)) == INVALID                               # the running O is required
+    assert fmerge(out=_t(ptr=0x10008)) == INVALID                       # the 16-bit copy is optional, but aligned
+    assert fmerge(scale=0.0) == INVALID and fmerge(cap=-1.0) == INVALID
+    assert fmerge(shape=AttnChunkShape(2, 64, 96, 8, 3, 512)) == INVALID
+    assert fmerge(shape=AttnChunkShape(0, 64, 96, 8, 2, 512)) == OK    # empty batch: no launch
+    assert fmerge(shape=AttnChunkShape(2, 0, 96, 8, 2, 512), out=_t()) == OK
     assert lib.attn_last_hip_error() == 0
 
 

@@ -13,7 +13,7 @@
 
     python -m scaled_dot_product_tiled_amd.profiling summaries OUT
         writes the profiles/ summaries of the bench.py workloads from OUT/{stats,fetch,write,
-        cfetch,cwrite} (the five rocprofv3 runs listed in each summary).
+        cfetch,cwrite} and, if present, OUT/sq (the rocprofv3 runs listed in each summary).
 
 bench.py reads such records back (read_traffic) and reports the traffic only while the
 source file still has the recorded hash.
@@ -125,8 +125,37 @@ COMMANDS = """Commands (cd /tmp && export TMPDIR=/tmp first; R = repository root
   rocprofv3 --pmc WRITE_SIZE -d $OUT/write --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --decode-steps 4 --no-cpu-baseline --no-other
   rocprofv3 --pmc FETCH_SIZE -d $OUT/cfetch --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
   rocprofv3 --pmc WRITE_SIZE -d $OUT/cwrite --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
+  rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_INST_LDS SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE -d $OUT/sq --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --decode-steps 4 --no-cpu-baseline --no-other
   python3 -m scaled_dot_product_tiled_amd.profiling summaries $OUT
 """
+
+SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_VALU_MFMA_BUSY_CYCLES",
+               "SQ_BUSY_CU_CYCLES", "SQ_WAIT_INST_LDS", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_LDS_ADDR_CONFLICT",
+               "GRBM_GUI_ACTIVE")
+SQ_KERNELS = (("attn_fwd", "fwd_kernel<512,32,false,false,false>"), ("bwd_dkdv", "bwd_dkdv_kernel<512,false,false>"),
+              ("bwd_dq", "bwd_dq_kernel<256,4,2,false>"), ("decode_split", "decode_split_kernel<4,false,false>"))
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def sq_table(d: str) -> str:
+    """Matrix-core and LDS use per kernel from one pass of SQ_COUNTERS.  GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs, so one XCD's active cycles (the kernel's duration in shader clocks) are an
+    eighth of it; SQ_VALU_MFMA_BUSY_CYCLES is summed over the 1024 SIMDs, SQ_INSTS_LDS_LOAD_BANDWIDTH
+    counts 64-byte units, SQ_WAIT_INST_LDS counts wave-cycles in units of 4."""
+    vals = {c: counter_per_dispatch(d, c) for c in SQ_COUNTERS}
+    rows = [f"{'kernel':14s} {'cycles':>9s} {'MFMA busy':>9s} {'LDS B/clk/CU':>12s} {'bank confl.':>11s} "
+            f"{'LDS fifo full':>13s} {'wait LDS issue':>14s}"]
+    for label, k in SQ_KERNELS:
+        m = {c: sum(_pick(vals[c], k)) / len(_pick(vals[c], k)) for c in SQ_COUNTERS}
+        cyc = m["GRBM_GUI_ACTIVE"] / N_XCD
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
+        lds = m["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64 / (cyc * N_CU)
+        conf = m["SQ_LDS_BANK_CONFLICT"] / max(m["SQ_LDS_IDX_ACTIVE"], 1.0)
+        fifo = m["SQ_LDS_DATA_FIFO_FULL"] / max(m["SQ_BUSY_CU_CYCLES"], 1.0)
+        wait = 4 * m["SQ_WAIT_INST_LDS"] / max(4 * cyc * N_CU, 1.0)   # per wave slot: 4 waves per CU
+        rows.append(f"{label:14s} {cyc:9.0f} {100 * busy:8.1f}% {lds:12.1f} {100 * conf:10.2f}% {100 * fifo:12.2f}% "
+                    f"{100 * wait:13.1f}%")
+    return "\n".join(rows)
 
 # (file, kernel name, source, what, algorithmic bytes) of each traffic summary
 TRAFFIC_SUMMARIES = [
@@ -186,6 +215,19 @@ def write_summaries(out: str, pdir: str) -> None:
         txt += f"\nbench.py line: value {line['value']} TFLOP/s, ms_per_step {line['ms_per_step']}\n"
     with open(os.path.join(pdir, "bench_d512_B2_S4096_kernel_stats.txt"), "w") as fh:
         fh.write(txt)
+    if os.path.isdir(os.path.join(out, "sq")):
+        txt = ("Matrix-core and LDS use of the bench.py kernels on one MI355X (causal GQA B=2 S=4096 Hq=32 Hkv=4\n"
+               "D=512 forward and backward; paged decode B=64 Hq=32 Hkv=8 D=128), one rocprofv3 pass of SQ\n"
+               "counters, averaged over each kernel's dispatches.\n\n"
+               "  cycles          shader clocks the kernel was active on one XCD (GRBM_GUI_ACTIVE / 8)\n"
+               "  MFMA busy       SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)\n"
+               "  LDS B/clk/CU    bytes read from LDS (SQ_INSTS_LDS_LOAD_BANDWIDTH x 64) / (cycles x 256 CUs)\n"
+               "  bank confl.     SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE\n"
+               "  LDS fifo full   SQ_LDS_DATA_FIFO_FULL / SQ_BUSY_CU_CYCLES\n"
+               "  wait LDS issue  wave-cycles waiting to issue an LDS instruction / wave-cycles of 4 waves per CU\n\n"
+               f"{COMMANDS}\n{sq_table(os.path.join(out, 'sq'))}\n")
+        with open(os.path.join(pdir, "sq_mfma_lds_d512_B2_S4096.txt"), "w") as fh:
+            fh.write(txt)
 
 
 def run_copy(mib: int, reps: int) -> None:

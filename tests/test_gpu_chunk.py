@@ -302,7 +302,9 @@ def test_lse_merge_identity_symmetry_and_poison():
 def test_full_size_ring_d512_two_chunks():
     """Causal GQA d512 (B=1, S=4096, Hq=32, Hkv=4) cut into two 2048-row chunks: the per-rank
     share of context parallelism at its real shape.  Sampled rows of O, LSE and dQ against the
-    oracle row by row; dK and dV of one kv head in full."""
+    oracle row by row; dK and dV of one kv head in full.  The fused forward-and-merge path (first
+    pair by attn_fwd_chunk, the second by attn_fwd_chunk_merge, as the ring benchmark runs it)
+    gives the same bytes as the two-step one."""
     w = AttnWorkload(209, "ring full d512", 1, 4096, 32, 4, 512)
     bounds = [0, 2048, 4096]
     inp = make_attention_inputs(w, seed=0)
@@ -313,6 +315,21 @@ def test_full_size_ring_d512_two_chunks():
     o = torch.cat([m[0] for m in merged], dim=1)
     lse = torch.cat([m[1] for m in merged], dim=2)
     assert all_finite(o, lse, dq, dk, dv)
+    for a in range(2):                    # own chunk first, then the other one
+        qa = q[:, bounds[a]:bounds[a + 1]]
+        own, other = (bounds[a], bounds[a + 1]), (bounds[1 - a], bounds[2 - a])
+        kv = lambda c: (k[:, c[0]:c[1]], v[:, c[0]:c[1]])  # noqa: E731
+        run_o, run_l = sdpt.attn_fwd_chunk(qa, *kv(own), bounds[a], own[0], scale=w.scale)
+        fused = torch.empty_like(qa)
+        sdpt.attn_fwd_chunk_merge(qa, *kv(other), bounds[a], other[0], run_o, run_l, scale=w.scale, out=fused)
+        acc_o, acc_l = sdpt.attn_fwd_chunk(qa, *kv(own), bounds[a], own[0], scale=w.scale)
+        part_o, part_l = sdpt.attn_fwd_chunk(qa, *kv(other), bounds[a], other[0], scale=w.scale)
+        two_step = torch.empty_like(qa)
+        sdpt.attn_lse_merge(acc_o, acc_l, part_o, part_l, out=two_step)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(fused), host_bits(two_step)), a
+        assert np.array_equal(host_bits(run_o), host_bits(acc_o)), a
+        assert np.array_equal(host_bits(run_l), host_bits(acc_l)), a
     f = {x: bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do")}
     rng = np.random.default_rng(3)
     for h in (0, 13, 31):

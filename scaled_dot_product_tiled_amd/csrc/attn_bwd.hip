@@ -35,10 +35,12 @@ namespace attn {
 // ---------------------------------------------------------------------------
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, int rows) {
-  constexpr int EPL = D / 64;  // elements per lane
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // Half a wave per row, 16-byte loads: 8 (head_dim 256) or 16 (512) elements per lane.
+  constexpr int LPR = 32;
+  constexpr int NV = D / (8 * LPR);  // 16-byte vectors per lane and tensor
+  const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
   if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & (LPR - 1);
   int b, pos, h, len;
   if (a.packed) {
     // packed rows: batch stride and per-sequence offset are folded into the row index
@@ -54,22 +56,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, int rows) {
     b = bp / a.S;
     len = a.seq_len ? min(max(a.seq_len[b], 0), a.S) : a.S;
   }
-  const int off = 0;
   float acc = 0.f;
   if (pos < len) {
-    const bf16* op = a.o + b * a.o_sb + (int64_t)(off + pos) * a.o_ss + h * a.o_sh + lane * EPL;
-    const bf16* dp = a.dout + b * a.do_sb + (int64_t)(off + pos) * a.do_ss + h * a.do_sh + lane * EPL;
+    const bf16* op = a.o + b * a.o_sb + (int64_t)pos * a.o_ss + h * a.o_sh + lane * 8 * NV;
+    const bf16* dp = a.dout + b * a.do_sb + (int64_t)pos * a.do_ss + h * a.do_sh + lane * 8 * NV;
+    bf16x8 ov[NV], dv[NV];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc += E16<F16>::to_float(op[e]) * E16<F16>::to_float(dp[e]);
+    for (int v = 0; v < NV; ++v) {
+      ov[v] = ldg8(op + 8 * v);
+      dv[v] = ldg8(dp + 8 * v);
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += E16<F16>::to_float(ov[v][e]) * E16<F16>::to_float(dv[v][e]);
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (lane == 0) a.delta[b * a.st_sb + h * a.st_sh + off + pos] = acc;
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);  // within the row's half-wave
+  if (lane == 0) a.delta[b * a.st_sb + h * a.st_sh + pos] = acc;
 }
 
 template <bool F16>
 hipError_t launch_bwd_pre_t(const AttnArgs& a, int D, int rows, hipStream_t stream) {
-  const dim3 grid((rows + 3) / 4), block(256);
+  const dim3 grid((rows + 7) / 8), block(256);
   if (D == 512)
     hipLaunchKernelGGL((bwd_pre_kernel<512, F16>), grid, block, 0, stream, a, rows);
   else if (D == 256)

@@ -7,6 +7,7 @@ meets every key/value chunk (fully masked pairs included) at its true positions.
     pair: O exactly zero, LSE exactly -inf);
   * the partials merged with attn_lse_merge against the oracle's whole-sequence forward, and the
     fused forward-and-merge call bit for bit against the two-step one;
+  * a rank's forward steps captured in a HIP graph and replayed, bit for bit against eager calls;
   * each pair's gradient parts against the oracle's chunk backward (fed the oracle's own final O
     and LSE), and the parts summed in fp32 against the oracle's whole-sequence backward.
 Tolerances as for the whole-sequence path: O max-abs 2e-2, LSE max-abs 1e-2, gradients relative
@@ -19,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from synth import AttnWorkload, bf16_bits_to_f64, bits_to_f64, make_attention_inputs
+from synth import AttnWorkload, bf16_bits_to_f64, bits_to_f64, make_attention_inputs, normal_16, stream
 from tests.gpu_util import GRAD_REL_L2, LSE_MAX_ABS, O_MAX_ABS, all_finite, dev, host, host_bits, max_abs, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -344,3 +345,56 @@ def test_full_size_ring_d512_two_chunks():
     assert rel_l2(host(dq[0, :, 8:16]), rq) <= GRAD_REL_L2
     assert rel_l2(host(dk[0, :, 1]), rk) <= GRAD_REL_L2
     assert rel_l2(host(dv[0, :, 1]), rv) <= GRAD_REL_L2
+
+
+def test_ring_forward_step_captured_in_a_graph():
+    """One rank's forward over three key chunks (attn_fwd_chunk, then attn_fwd_chunk_merge twice,
+    the last writing the bf16 O) captured once in a HIP graph and replayed with new queries copied
+    into the captured buffer: every replay equals the same calls made eagerly, bit for bit, so
+    the chunk calls allocate nothing and do not synchronise."""
+    w = AttnWorkload(212, "ring graph", 1, 384, 8, 2, 512)
+    bounds = [0, 128, 256, 384]
+    inp = make_attention_inputs(w, seed=2)
+    k, v = dev(inp["k"]), dev(inp["v"])
+    q0 = bounds[2]
+    q_s = torch.empty((1, 128, w.Hq, w.D), device="cuda:0", dtype=torch.bfloat16)
+    run_o = torch.empty((1, 128, w.Hq, w.D), device="cuda:0")
+    run_l = torch.empty((1, w.Hq, 128), device="cuda:0")
+    out_s = torch.empty_like(q_s)
+
+    def rank_forward(qq, ro, rl, out):
+        for i, c in enumerate((2, 1, 0)):
+            k0, k1 = bounds[c], bounds[c + 1]
+            if i == 0:
+                sdpt.attn_fwd_chunk(qq, k[:, k0:k1], v[:, k0:k1], q0, k0, scale=w.scale, out=ro, lse=rl)
+            else:
+                sdpt.attn_fwd_chunk_merge(qq, k[:, k0:k1], v[:, k0:k1], q0, k0, ro, rl, scale=w.scale,
+                                          out=out if i == 2 else None)
+
+    def load(i):
+        q_s.copy_(dev(normal_16(stream(30 + i, w.wid, 0), (1, 128, w.Hq, w.D))))
+
+    load(0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):              # warm-up outside the graph
+        rank_forward(q_s, torch.empty_like(run_o), torch.empty_like(run_l), torch.empty_like(out_s))
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rank_forward(q_s, run_o, run_l, out_s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        say(f"[ring graph] replay {i}")
+        load(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e_o, e_l, e_out = torch.empty_like(run_o), torch.empty_like(run_l), torch.empty_like(out_s)
+        rank_forward(q_s, e_o, e_l, e_out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out_s), host_bits(e_out)), i
+        assert np.array_equal(host_bits(run_l), host_bits(e_l)), i
+        assert np.array_equal(host_bits(run_o), host_bits(e_o)), i
+        assert all_finite(out_s, run_l)

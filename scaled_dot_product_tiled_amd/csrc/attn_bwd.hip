@@ -35,10 +35,10 @@ namespace attn {
 // ---------------------------------------------------------------------------
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, int rows) {
-  // Half a wave per row, 16-byte loads: 8 (head_dim 256) or 16 (512) elements per lane.
-  constexpr int LPR = 32;
+  // A quarter wave per row, 16-byte loads: 16 (head_dim 256) or 32 (512) elements per lane.
+  constexpr int LPR = 16;
   constexpr int NV = D / (8 * LPR);  // 16-byte vectors per lane and tensor
-  const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
   if (row >= rows) return;
   const int lane = threadIdx.x & (LPR - 1);
   int b, pos, h, len;
@@ -72,13 +72,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, int rows) {
       for (int e = 0; e < 8; ++e) acc += E16<F16>::to_float(ov[v][e]) * E16<F16>::to_float(dv[v][e]);
   }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);  // within the row's half-wave
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);  // within the row's 16 lanes
   if (lane == 0) a.delta[b * a.st_sb + h * a.st_sh + pos] = acc;
 }
 
 template <bool F16>
 hipError_t launch_bwd_pre_t(const AttnArgs& a, int D, int rows, hipStream_t stream) {
-  const dim3 grid((rows + 7) / 8), block(256);
+  const dim3 grid((rows + 15) / 16), block(256);
   if (D == 512)
     hipLaunchKernelGGL((bwd_pre_kernel<512, F16>), grid, block, 0, stream, a, rows);
   else if (D == 256)

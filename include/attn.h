@@ -360,6 +360,16 @@ typedef struct {
 int attn_profile(int on);
 int attn_profile_read(attn_kernel_time* out, int max_entries);
 
+/* Softmax-reference restarts, for tests.  At head_dim 512 the forward fixes each row's
+ * softmax reference from the first keys it sees and, when a later score exceeds it by more
+ * than the 16-bit probability range allows, restarts the workgroup's key loop with raised
+ * references (exact in real arithmetic; see the forward kernel).  After
+ * attn_count_restarts(p) with p a device int32, every forward kernel launched from this
+ * thread (attn_fwd, attn_fwd_chunk, attn_fwd_chunk_merge) atomically adds 1 to *p per
+ * restart of one of its workgroups; attn_count_restarts(NULL) stops it.  Returns 0.  The
+ * counter is the caller's memory and must stay valid while such calls run. */
+int attn_count_restarts(int32_t* device_counter);
+
 /* Library version, "major.minor.patch". */
 const char* attn_version(void);
 

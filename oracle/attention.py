@@ -41,8 +41,8 @@ import numpy as np
 
 __all__ = [
     "visibility", "lengths_from_pad_mask", "lengths_from_cu_seqlens",
-    "scores", "unit_forward", "unit_backward", "attention_forward", "attention_backward",
-    "attention_forward_head", "attention_backward_group",
+    "scores", "unit_forward", "unit_backward", "unit_forward_backward",
+    "attention_forward", "attention_backward", "attention_forward_head", "attention_backward_group", "attention_group",
     "attention_forward_packed", "attention_backward_packed",
     "gather_pages", "paged_append", "paged_decode", "paged_decode_one", "attention_rows",
     "chunk_visibility", "attention_forward_chunk", "attention_backward_chunk", "lse_merge",
@@ -124,13 +124,14 @@ def unit_forward(q, k, v, scale, vis, softcap=0.0):
     return o, lse, p
 
 
-def unit_backward(q, k, v, do, scale, vis, softcap=0.0):
-    """Gradients of sum(O * dO) for one head; returns dQ, dK, dV (this head's share of dK, dV).
+def unit_forward_backward(q, k, v, do, scale, vis, softcap=0.0):
+    """Forward and gradients of sum(O * dO) for one head from one evaluation of the softmax:
+    returns O, LSE, dQ, dK, dV (this head's share of dK, dV).
 
     dP = dO v^T; delta_i = sum_j P_ij dP_ij; dS = P * (dP - delta), times the cap's
     derivative 1 - tanh^2 under a softcap; dQ = scale dS k; dK = scale dS^T q; dV = P^T dO.
     """
-    o, _, p = unit_forward(q, k, v, scale, vis, softcap)
+    o, lse, p = unit_forward(q, k, v, scale, vis, softcap)
     _, deriv = scores(q, k, scale, softcap)
     dp = do @ v.T
     delta = (p * dp).sum(axis=1)
@@ -138,7 +139,12 @@ def unit_backward(q, k, v, do, scale, vis, softcap=0.0):
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     dv = p.T @ do
-    return dq, dk, dv
+    return o, lse, dq, dk, dv
+
+
+def unit_backward(q, k, v, do, scale, vis, softcap=0.0):
+    """Gradients of sum(O * dO) for one head; returns dQ, dK, dV (this head's share of dK, dV)."""
+    return unit_forward_backward(q, k, v, do, scale, vis, softcap)[2:]
 
 
 # ---------------------------------------------------------------------------
@@ -196,6 +202,31 @@ def attention_backward_group(q, k, v, do, b, g, scale, causal=True, window=0, le
         dk[:n] += dkh
         dv[:n] += dvh
     return dq, dk, dv
+
+
+def attention_group(q, k, v, do, b, g, scale, causal=True, window=0, lengths=None, softcap=0.0):
+    """Everything one (batch, kv head) unit produces, from one softmax evaluation per query head:
+    O (S, r, D) and LSE (r, S) of the r query heads of kv head g, their dQ (S, r, D), and dK, dV
+    (S, D) summed over them in head order.  Rows and keys at or past the length are 0."""
+    B, S, Hq, D = q.shape
+    r = Hq // k.shape[2]
+    n = int(_lengths(B, S, lengths)[b])
+    o = np.zeros((S, r, D))
+    lse = np.zeros((r, S))
+    dq = np.zeros((S, r, D))
+    dk = np.zeros((S, D))
+    dv = np.zeros((S, D))
+    if n == 0:
+        return o, lse, dq, dk, dv
+    vis = visibility(n, causal, window)
+    for i in range(r):                   # fixed head order
+        h = g * r + i
+        oh, lh, dqh, dkh, dvh = unit_forward_backward(q[b, :n, h], k[b, :n, g], v[b, :n, g], do[b, :n, h], scale,
+                                                      vis, softcap)
+        o[:n, i], lse[i, :n], dq[:n, i] = oh, lh, dqh
+        dk[:n] += dkh
+        dv[:n] += dvh
+    return o, lse, dq, dk, dv
 
 
 def attention_backward(q, k, v, do, scale, causal=True, window=0, lengths=None, softcap=0.0):

@@ -55,7 +55,7 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse
            "paged_decode", "paged_kv_append", "paged_kv_gather", "attn_debug",
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
-           "attn_profile", "attn_profile_read")
+           "attn_profile", "attn_profile_read", "attn_count_restarts")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -117,6 +117,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_last_hip_error.restype = ctypes.c_int
     lib.attn_version.argtypes = []
     lib.attn_version.restype = ctypes.c_char_p
+    lib.attn_count_restarts.argtypes = [vp]
+    lib.attn_count_restarts.restype = ctypes.c_int
     lib.attn_profile.argtypes = [ctypes.c_int]
     lib.attn_profile.restype = ctypes.c_int
     lib.attn_profile_read.argtypes = [P(AttnKernelTime), ctypes.c_int]
@@ -528,6 +530,14 @@ def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: t
 def debug(on: bool) -> bool:
     """Switches the library's metadata checks (debug mode) on or off; returns the previous mode."""
     return bool(load_library().attn_debug(1 if on else 0))
+
+
+def count_restarts(counter: Optional[torch.Tensor]) -> None:
+    """Forward kernels add their softmax-reference restarts to counter (a device int32 tensor of
+    one element) until count_restarts(None)."""
+    if counter is not None and (counter.dtype != torch.int32 or not counter.is_cuda):
+        raise TypeError("counter must be an int32 device tensor")
+    load_library().attn_count_restarts(counter.data_ptr() if counter is not None else None)
 
 
 def profile(on: bool) -> None:

@@ -95,6 +95,9 @@ struct Profiler {
   std::vector<TimedLaunch> launches;
 };
 thread_local Profiler g_prof;
+
+// attn_count_restarts: device counter the forward kernels add their key-loop restarts to.
+thread_local int* g_restarts = nullptr;
 constexpr size_t kMaxTimed = 4096;
 
 hipEvent_t prof_event() {
@@ -432,6 +435,7 @@ attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, co
     set_tensor(final16, false, a.r_sb, a.r_ss, a.r_sh);
   }
   a.lse = lse;
+  a.restarts = g_restarts;
   plan_rows(a, attn::kFwdRows);
   return launch(mode == FwdOut::merge ? "attn_fwd_merge" : "attn_fwd", s, a.total_items,
                 [&] { return attn::launch_fwd(a, c.D, s); });
@@ -707,10 +711,11 @@ size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {
   return round_up(sizeof(float) * (size_t)s->B * s->Hq * chunks * (s->D + 2));
 }
 
-attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t q_stride_b, int64_t q_stride_h,
-                         attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
-                         const int32_t* ctx_lens, float scale, float softcap, void* o, int64_t o_stride_b,
-                         int64_t o_stride_h, void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks of the paged decode, before the workspace.
+static attn_status check_decode(const attn_decode_shape* shape, const void* q, int64_t q_stride_b,
+                                int64_t q_stride_h, attn_tensor k_cache, attn_tensor v_cache,
+                                const int32_t* block_table, const int32_t* ctx_lens, float scale, float softcap,
+                                void* o, int64_t o_stride_b, int64_t o_stride_h) {
   if (shape == nullptr) return ATTN_ERR_INVALID_ARG;
   const attn_decode_shape& sh = *shape;
   if (sh.B < 0 || sh.Hq <= 0 || sh.Hkv <= 0 || sh.num_pages <= 0 || sh.max_pages_per_seq <= 0 || sh.page_size <= 0)
@@ -729,11 +734,17 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   if ((st = check_tensor(k_cache, false)) || (st = check_tensor(v_cache, false))) return st;
   // offsets inside one page are 32-bit byte offsets
   if (k_cache.stride_s > (INT_MAX / 2) / 16 || v_cache.stride_s > (INT_MAX / 2) / 16) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = paged_decode_workspace_bytes(shape);
-  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
-    return ATTN_ERR_WORKSPACE;
-  if (sh.B == 0) return ATTN_OK;
+  return ATTN_OK;
+}
+
+// The decode's two launches, after every check; `workspace` holds the chunk partials.
+static attn_status run_decode(const attn_decode_shape& sh, const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                              attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
+                              const int32_t* ctx_lens, float scale, float softcap, void* o, int64_t o_stride_b,
+                              int64_t o_stride_h, void* workspace, void* stream) {
+  attn_status st;
   if ((st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream)))) return st;
+  const int r = sh.Hq / sh.Hkv;
 
   attn::DecodeArgs a = {};
   a.q = static_cast<const __bf16*>(q);
@@ -771,6 +782,21 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   return hip_status(timed("decode_merge", s, [&] { return attn::launch_decode_merge(a, sh.D, s); }));
 }
 
+attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                         attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
+                         const int32_t* ctx_lens, float scale, float softcap, void* o, int64_t o_stride_b,
+                         int64_t o_stride_h, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_decode(shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale,
+                                softcap, o, o_stride_b, o_stride_h);
+  if (st != ATTN_OK) return st;
+  const size_t need = paged_decode_workspace_bytes(shape);
+  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  if (shape->B == 0) return ATTN_OK;
+  return run_decode(*shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale, softcap, o,
+                    o_stride_b, o_stride_h, workspace, stream);
+}
+
 attn_status paged_kv_append(const attn_decode_shape* shape, int32_t n_tokens, attn_tensor k_new, attn_tensor v_new,
                             attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
                             const int32_t* ctx_lens, void* stream) {
@@ -803,6 +829,11 @@ const char* attn_status_str(attn_status status) {
 }
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_count_restarts(int32_t* device_counter) {
+  g_restarts = reinterpret_cast<int*>(device_counter);
+  return 0;
+}
 
 int attn_profile(int on) {
   g_prof.on = on != 0;

@@ -33,7 +33,9 @@
 //    to the maxima seen so far and restarts its key loop from the first tile.  The
 //    accumulators are never rescaled: at head_dim 512 they fill the matrix-core
 //    accumulator registers and are only ever written by MFMA or cleared.  The dominant
-//    probability is 2^(s_max - m) rounded to bf16, a relative error of at most 2^-9.
+//    probability 2^(s_max - m) is then rounded to the 16-bit type (2^-9 relative in
+//    bf16); the normaliser sums the rounded probabilities, so that rounding divides out
+//    of a row one key dominates.
 // A row that has seen no key yet uses m = 0 (its exponentials are all 2^-inf = 0).
 #include "device_common.h"
 #include "kernel_args.h"
@@ -211,6 +213,7 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
             restart_flag[jt & 1][3]) {
           m_ref = fmaxf(m_ref, mt);
           restart = true;
+          if (a.restarts != nullptr && threadIdx.x == 0) atomicAdd(a.restarts, 1);
           wait_vmcnt<0>();
           barrier_lds();  // no wave still reads Ks / Vs before they are refilled
           break;
@@ -218,22 +221,21 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
       }
 
       const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      // P is rounded to the 16-bit type for the P V product, and the normaliser sums the same
+      // rounded values, so that the weights applied to V sum to exactly one: a dominant term
+      // far above the reference then divides out instead of carrying its rounding into O.
       float rs = 0.f;
+      bf16x8 pb[NS];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[kb][r], c, -m_use));  // masked: 2^-inf = 0
-          sacc[kb][r] = p;
-          rs += p;
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + e], c, -m_use));  // masked: 2^-inf = 0
+          pb[s][e] = E16<F16>::from_float(p);
+          rs += E16<F16>::to_float(pb[s][e]);
         }
       l_run += half_swap_sum(rs);
       {
-        bf16x8 pb[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[s][e] = E16<F16>::from_float(sacc[s >> 1][8 * (s & 1) + e]);
         // V^T fragments in (d block, key step) order, read two ahead of the matrix core.
         constexpr int NF = DB * NS;
         bf16x8 vf[3];

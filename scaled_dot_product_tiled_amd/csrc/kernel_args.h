@@ -73,6 +73,9 @@ struct AttnArgs {
   // merged into; out (strides r_*), if not NULL, receives the merged O in 16 bits
   int merge;
   int64_t r_sb, r_ss, r_sh;
+  // forward: when not NULL, every restart of a workgroup's key loop (head_dim 512 softmax
+  // reference raised) adds 1 here
+  int* restarts;
 };
 
 struct DecodeArgs {

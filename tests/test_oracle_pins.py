@@ -444,6 +444,29 @@ def test_row_sampled_oracle_equals_full_unit():
             np.testing.assert_allclose(rdq, dq[b, rows, h], atol=1e-13)
 
 
+def test_group_evaluation_equals_forward_and_backward():
+    """attention_group (one softmax evaluation per head for the forward and the backward of a
+    (batch, kv head) unit, used by the full-size GPU comparisons) returns exactly what the pinned
+    attention_forward and attention_backward return for that unit."""
+    rng = np.random.default_rng(11)
+    B, S, Hq, Hkv, D = 2, 30, 6, 2, 8
+    q, do = _rand(rng, B, S, Hq, D), _rand(rng, B, S, Hq, D)
+    k, v = _rand(rng, B, S, Hkv, D), _rand(rng, B, S, Hkv, D)
+    lengths = [30, 17]
+    o, lse = oracle.attention_forward(q, k, v, 0.4, True, 5, lengths)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.4, True, 5, lengths)
+    r = Hq // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            go, gl, gq, gk, gv = oracle.attention_group(q, k, v, do, b, g, 0.4, True, 5, lengths)
+            hs = slice(g * r, (g + 1) * r)
+            np.testing.assert_array_equal(go, o[b, :, hs])
+            np.testing.assert_array_equal(gl, lse[b, hs])
+            np.testing.assert_array_equal(gq, dq[b, :, hs])
+            np.testing.assert_array_equal(gk, dk[b, :, g])
+            np.testing.assert_array_equal(gv, dv[b, :, g])
+
+
 # ---------------------------------------------------------------------------
 # Chunks of a sequence (ring context parallelism): pinned to the full oracle by the
 # decomposition identity -- a row's attention over all keys is the log-sum-exp merge of its

@@ -285,6 +285,32 @@ attn_status paged_decode(const attn_decode_shape* shape,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_decode_noalloc: paged_decode for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  It takes no
+ * workspace: the chunk partials live in a fixed device array inside the library, of
+ * paged_decode_noalloc_max_bytes() bytes (16 MiB) on every GPU it runs on, held until the
+ * process ends.  The call allocates nothing and frees nothing.
+ *   Arguments, layouts, results and errors are those of paged_decode without workspace and
+ *   workspace_bytes; the results equal paged_decode's bit for bit.  A shape whose
+ *   paged_decode_workspace_bytes(shape) exceeds the fixed array returns ATTN_ERR_WORKSPACE
+ *   before anything is launched.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *   (other streams, other threads, other processes do not share it) race and give wrong
+ *   results.  Calls on one stream run one after the other and do not.
+ * The first call on each device looks the array's address up (hipGetSymbolAddress), which may
+ * load the library's code object on that device; it launches nothing extra.
+ */
+attn_status paged_decode_noalloc(const attn_decode_shape* shape,
+                                 const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                                 attn_tensor k_cache, attn_tensor v_cache,
+                                 const int32_t* block_table, const int32_t* ctx_lens,
+                                 float scale, float softcap,
+                                 void* o, int64_t o_stride_b, int64_t o_stride_h, void* stream);
+
+/* Size in bytes of paged_decode_noalloc's fixed device array. */
+size_t paged_decode_noalloc_max_bytes(void);
+
+/*
  * paged_kv_append: write the n_tokens newest tokens of each sequence into its cache pages:
  * token i of sequence b (k_new/v_new row (b, i)) goes to logical position
  * ctx_lens[b] - n_tokens + i, i.e. ctx_lens counts the appended tokens, as it does for

@@ -55,7 +55,8 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse
            "paged_decode", "paged_kv_append", "paged_kv_gather", "attn_debug",
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
-           "attn_profile", "attn_profile_read", "attn_count_restarts")
+           "attn_profile", "attn_profile_read", "attn_count_restarts", "paged_decode_noalloc",
+           "paged_decode_noalloc_max_bytes")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -97,6 +98,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  vp, vp, ctypes.c_float, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp, sz,
                                  vp]
     lib.paged_decode.restype = ctypes.c_int
+    lib.paged_decode_noalloc.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int64, ctypes.c_int64, AttnTensor,
+                                         AttnTensor, vp, vp, ctypes.c_float, ctypes.c_float, vp, ctypes.c_int64,
+                                         ctypes.c_int64, vp]
+    lib.paged_decode_noalloc.restype = ctypes.c_int
+    lib.paged_decode_noalloc_max_bytes.argtypes = []
+    lib.paged_decode_noalloc_max_bytes.restype = sz
     lib.paged_kv_append.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, AttnTensor, AttnTensor,
                                     vp, vp, vp]
     lib.paged_kv_append.restype = ctypes.c_int
@@ -426,6 +433,49 @@ def attn_fwd_chunk_merge(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_po
                                   int(k_pos0), _tensor(o, False), lse.data_ptr(),
                                   _tensor(out, False) if out is not None else AttnTensor(None, 0, 0, 0), _stream())
     _check(st, "attn_fwd_chunk_merge")
+
+
+def _decode_args(q, k_cache, v_cache, block_table, ctx_lens, scale, out):
+    """Checks and marshals the arguments paged_decode and paged_decode_noalloc share."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _half(t, n, q.dtype)
+    for t, n in ((block_table, "block_table"), (ctx_lens, "ctx_lens")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 device tensor")
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, _ = k_cache.shape
+    shape = AttnDecodeShape(B, Hq, Hkv, D, page_size, num_pages, block_table.shape[1], _DT16[q.dtype])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        raise ValueError("out is required")
+    _half(out, "out", q.dtype)
+    _expect(v_cache, tuple(k_cache.shape), "v_cache")
+    _expect(out, (B, Hq, D), "out")
+    _expect(ctx_lens, (B,), "ctx_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be (B, max_pages_per_seq), got {tuple(block_table.shape)}")
+    if k_cache.shape[3] != D:
+        raise ValueError("k_cache head_dim differs from q's")
+    return shape, float(scale)
+
+
+def paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                         ctx_lens: torch.Tensor, out: torch.Tensor, scale: Optional[float] = None,
+                         softcap: float = 0.0) -> torch.Tensor:
+    """paged_decode without a workspace (the library's fixed device scratch holds the partials);
+    out (B,Hq,D) is required, so that the call allocates nothing."""
+    lib = load_library()
+    shape, scale = _decode_args(q, k_cache, v_cache, block_table, ctx_lens, scale, out)
+    st = lib.paged_decode_noalloc(ctypes.byref(shape), q.data_ptr(), q.stride(0), q.stride(1),
+                                  AttnTensor(k_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1),
+                                             k_cache.stride(2)),
+                                  AttnTensor(v_cache.data_ptr(), v_cache.stride(0), v_cache.stride(1),
+                                             v_cache.stride(2)),
+                                  block_table.data_ptr(), ctx_lens.data_ptr(), scale, float(softcap), out.data_ptr(),
+                                  out.stride(0), out.stride(1), _stream())
+    _check(st, "paged_decode_noalloc")
+    return out
 
 
 def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

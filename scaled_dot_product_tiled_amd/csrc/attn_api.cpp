@@ -711,7 +711,7 @@ size_t paged_decode_workspace_bytes(const attn_decode_shape* s) {
   return round_up(sizeof(float) * (size_t)s->B * s->Hq * chunks * (s->D + 2));
 }
 
-// Argument checks of the paged decode, before the workspace.
+// Argument checks of paged_decode and paged_decode_noalloc, before the workspace.
 static attn_status check_decode(const attn_decode_shape* shape, const void* q, int64_t q_stride_b,
                                 int64_t q_stride_h, attn_tensor k_cache, attn_tensor v_cache,
                                 const int32_t* block_table, const int32_t* ctx_lens, float scale, float softcap,
@@ -795,6 +795,23 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   if (shape->B == 0) return ATTN_OK;
   return run_decode(*shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale, softcap, o,
                     o_stride_b, o_stride_h, workspace, stream);
+}
+
+size_t paged_decode_noalloc_max_bytes(void) { return attn::kDecodeScratchBytes; }
+
+attn_status paged_decode_noalloc(const attn_decode_shape* shape, const void* q, int64_t q_stride_b,
+                                 int64_t q_stride_h, attn_tensor k_cache, attn_tensor v_cache,
+                                 const int32_t* block_table, const int32_t* ctx_lens, float scale, float softcap,
+                                 void* o, int64_t o_stride_b, int64_t o_stride_h, void* stream) {
+  attn_status st = check_decode(shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale,
+                                softcap, o, o_stride_b, o_stride_h);
+  if (st != ATTN_OK) return st;
+  if (paged_decode_workspace_bytes(shape) > attn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+  if (shape->B == 0) return ATTN_OK;
+  void* scratch = nullptr;
+  if ((st = hip_status(attn::decode_scratch(&scratch)))) return st;
+  return run_decode(*shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale, softcap, o,
+                    o_stride_b, o_stride_h, scratch, stream);
 }
 
 attn_status paged_kv_append(const attn_decode_shape* shape, int32_t n_tokens, attn_tensor k_new, attn_tensor v_new,

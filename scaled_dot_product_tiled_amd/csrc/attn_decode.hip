@@ -24,10 +24,43 @@
 //   merge  one workgroup per (sequence, query head) combines the chunk partials.
 // Tokens at or past ctx_len are masked; their loads are redirected to a valid slot of
 // the same step, so no unused slot or page is ever read.
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "kernel_args.h"
 
 namespace attn {
+
+// Chunk partials of paged_decode_noalloc: a fixed array in device memory instead of a
+// caller-provided workspace, for callers that cannot allocate.  Every GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not the device address: the address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to the kernels.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 constexpr int kDecD = 128;
 

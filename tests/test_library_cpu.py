@@ -119,6 +119,18 @@ def test_backward_and_decode_checks():
     assert dec(d, cap=-1.0) == INVALID
     assert dec(AttnDecodeShape(0, 32, 8, 128, 16, 100, 8)) == OK
 
+    # the allocation-free decode: the same checks, and a shape whose chunk partials exceed the
+    # library's fixed array is refused before anything is launched
+    def dec_na(shape, q=0x1000, table=0x2000):
+        return lib.paged_decode_noalloc(ctypes.byref(shape), q, 32 * 128, 128, kc, kc, table, 0x3000, 0.1, 0.0,
+                                        0x4000, 32 * 128, 128, None)
+    assert lib.paged_decode_noalloc_max_bytes() == 16 << 20
+    assert dec_na(AttnDecodeShape(4, 32, 8, 64, 16, 100, 8)) == UNSUPPORTED
+    assert dec_na(d, q=0) == INVALID
+    assert dec_na(AttnDecodeShape(4, 32, 8, 128, 16, 100, 1 << 16)) == WORKSPACE   # 136 MB of partials
+    assert dec_na(AttnDecodeShape(0, 32, 8, 128, 16, 100, 8)) == OK
+    assert lib.attn_last_hip_error() == 0
+
 
 def test_chunk_workspace_sizes():
     """Chunk pairs of a sequence cut into 2048-row chunks (head_dim 512, 32 query heads): the

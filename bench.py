@@ -3,19 +3,32 @@
 A step is one forward + backward of causal grouped-query attention, head_dim 512 (B=2, S=4096,
 Hq=32, Hkv=4, bf16, seeded N(0,1) inputs already resident in HBM): attn_fwd then attn_bwd through
 the C ABI.  Reported:
-  value     causal-counted TFLOP/s of the step: forward 4 D pairs, backward 2.5x that, where pairs =
-            visible (query, key) pairs summed over batch and heads (exact, not S^2/2);
-  roofline  for the dominant kernel, timed with HIP events on the stream it runs on;
+  value     causal-counted TFLOP/s of the step over the timed region (exactly --steps steps between
+            two synchronisations, a HIP event between consecutive steps): forward 4 D pairs, backward
+            2.5x that, where pairs = visible (query, key) pairs summed over batch and heads (exact,
+            not S^2/2); step_ms gives the median and best of the per-step event times;
+  roofline  for the dominant kernel, timed with HIP event pairs around each of its launches on the
+            stream it runs on (attn_profile), beside the rocprofv3 kernel-trace average of the
+            committed profile of the same workload and their difference;
   decode    paged single-token decode (B=64, Hq=32, Hkv=8, D=128, 16-token pages, contexts
             U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
             pages_in_order is the same decode with each sequence's pages consecutive in the pool;
-  other_workloads  (median of per-call HIP-event timings) forward / backward TFLOP/s of the sliding-window (D=256, W=1024) and padded
-            varlen (B=8, lengths U{512..8192}, D=512) workloads, of one context-parallel rank's
-            chunk pairs (16k tokens in 8 chunks, D=512) and of the step's workload in IEEE half,
-            not part of the timed step;
-  cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores.
+  other_workloads  (median and best of per-call HIP-event timings) forward / backward TFLOP/s of the
+            tiny (B=1 S=128 D=512), sliding-window (D=256, W=1024) and padded varlen (B=8, lengths
+            U{512..8192}, D=512) workloads, of one context-parallel rank's chunk pairs (16k tokens in
+            8 chunks, D=512), of the step's workload in IEEE half and with a softcap, and a paged
+            prefill; not part of the timed step;
+  measured_peaks  what plain kernels reach on this device (attn_peak_probe): independent bf16
+            32x32x16 matrix instructions, a streaming read and a streaming copy;
+  cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores, and
+            per_config samples of the other workloads.
 Prints one JSON line.
+
+    python bench.py --workload NAME   (NAME: tiny_d512, full_d512, window_d256, varlen_d512,
+                                        decode_d128) runs only that workload's forward + backward
+                                        (or decode) steps and prints its per-kernel times; the
+                                        rocprofv3 summaries in profiles/ are taken from such runs.
 """
 import argparse
 import json
@@ -35,11 +48,37 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 # HBM traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy)
 # of each kernel on this workload; a record counts only while its kernel source is unchanged.
 TRAFFIC = {
-    "attn_fwd": ("profiles/attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512,32,false,false,false>"),
-    "bwd_dkdv": ("profiles/bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512,false,false>"),
-    "bwd_dq": ("profiles/bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2,false>"),
-    "decode_split": ("profiles/decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false,false>"),
+    "attn_fwd": ("profiles/full_d512_traffic.txt", "fwd_kernel<512,32,false,false,false>"),
+    "bwd_dkdv": ("profiles/full_d512_traffic.txt", "bwd_dkdv_kernel<512,false,false>"),
+    "bwd_dq": ("profiles/full_d512_traffic.txt", "bwd_dq_kernel<256,4,2,false>"),
+    "decode_split": ("profiles/decode_d128_traffic.txt", "decode_split_kernel<4,false,false>"),
 }
+
+
+# rocprofv3 --kernel-trace --stats summaries of each workload (committed profiles)
+STATS = {
+    "full_d512": "profiles/full_d512_kernel_stats.txt",
+    "tiny_d512": "profiles/tiny_d512_kernel_stats.txt",
+    "window_d256": "profiles/window_d256_kernel_stats.txt",
+    "varlen_d512": "profiles/varlen_d512_kernel_stats.txt",
+    "decode_d128": "profiles/decode_d128_kernel_stats.txt",
+}
+KERNEL_OF = {"attn_fwd": "fwd_kernel<", "bwd_dkdv": "bwd_dkdv_kernel<", "bwd_dq": "bwd_dq_kernel<",
+             "bwd_pre": "bwd_pre_kernel<", "decode_split": "decode_split_kernel<",
+             "decode_merge": "decode_merge_kernel<"}
+
+
+def rocprof_ms(workload, kernel):
+    """(median, mean) duration in ms of `kernel`'s dispatches in the committed rocprofv3 summary of
+    `workload` (its kernel trace, warm-up launches included), or None."""
+    path = os.path.join(ROOT, STATS.get(workload, ""))
+    if not os.path.isfile(path) or kernel not in KERNEL_OF:
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) > 6 and parts[0].isdigit() and KERNEL_OF[kernel] in line.replace(" ", ""):
+            return float(parts[2]) / 1e3, float(parts[1]) / 1e3
+    return None
 
 
 def traffic_bytes(kernel):
@@ -57,37 +96,73 @@ def causal_pairs(S, window=0):
     return int(cnt.sum())
 
 
-def other_workload(name, steps, stream, softcap=0.0, **changes):
-    """Forward and backward times of the sliding-window and padded-varlen workloads, or of a workload
-    with some fields changed (device-side seeded draws of the same shapes and distributions;
-    lengths and masks from synth)."""
+def time_calls(fn, n, stream):
+    """n calls of fn() on `stream` with a HIP event before the first and after each call: the
+    per-call times (ms) and their median, best and mean (the mean is the whole window / n)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        fn()
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    return {"median": float(np.median(per)), "best": float(min(per)), "mean": evs[0].elapsed_time(evs[-1]) / n,
+            "reps": n}
+
+
+def rounded(t, nd=4):
+    return {k: (round(v, nd) if isinstance(v, float) else v) for k, v in t.items()}
+
+
+def kernel_times(fn, n):
+    """Per-kernel HIP-event times (attn_profile: an event pair around every launch, on its stream)
+    over n calls of fn()."""
+    import scaled_dot_product_tiled_amd as sdpt
+    sdpt.binding.profile(True)
+    for _ in range(n):
+        fn()
+    sdpt.binding.profile(False)
+    return {k: {"launches": c, "ms_avg": round(t / c, 4)} for k, (c, t) in sdpt.binding.profile_read().items()}
+
+
+def attn_case(name, softcap=0.0, host_inputs=False, **changes):
+    """Device buffers and fwd / bwd closures of one attention workload.  host_inputs: the seeded
+    CPU draws the tests use (synth.make_attention_inputs); otherwise device-side seeded draws of
+    the same shapes and distributions (lengths and masks from synth)."""
     import torch
     import scaled_dot_product_tiled_amd as sdpt
-    from synth import ATTN_WORKLOADS
-    from synth import draw_lengths, lengths_to_pad_mask
+    from synth import ATTN_WORKLOADS, draw_lengths, lengths_to_pad_mask, make_attention_inputs
     w = ATTN_WORKLOADS[name].scaled(**changes)
-    gen = torch.Generator(device="cuda:0")
-    gen.manual_seed(1234 + w.wid)
     dt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    if host_inputs:
+        inp = make_attention_inputs(w, seed=0)
+        q, k, v, do = (torch.from_numpy(np.ascontiguousarray(inp[x]).view(np.int16)).to("cuda:0").view(dt)
+                       for x in ("q", "k", "v", "do"))
+        lengths = inp["lengths"]
+    else:
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(1234 + w.wid)
 
-    def draw(shape, std):
-        return (torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32) * std).to(dt)
+        def draw(shape, std):
+            return (torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32) * std).to(dt)
 
-    q = draw((w.B, w.S, w.Hq, w.D), w.qk_std)
-    k = draw((w.B, w.S, w.Hkv, w.D), w.qk_std)
-    v = draw((w.B, w.S, w.Hkv, w.D), 1.0)
-    do = draw((w.B, w.S, w.Hq, w.D), 1.0)
-    lengths = draw_lengths(w, 0)
+        q = draw((w.B, w.S, w.Hq, w.D), w.qk_std)
+        k = draw((w.B, w.S, w.Hkv, w.D), w.qk_std)
+        v = draw((w.B, w.S, w.Hkv, w.D), w.vdo_std)
+        do = draw((w.B, w.S, w.Hq, w.D), w.vdo_std)
+        lengths = draw_lengths(w, 0)
     pm = None
     if lengths is not None:
         pm = torch.from_numpy(lengths_to_pad_mask(lengths, w.S).astype(np.uint8)).to("cuda:0")
         pairs = sum(int(n) * (int(n) + 1) // 2 for n in lengths) * w.Hq
     else:
-        pairs = causal_pairs(w.S, w.window) * w.B * w.Hq
+        pairs = causal_pairs(w.S, w.window) * w.B * w.Hq if w.causal else w.S * w.S * w.B * w.Hq
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.S), device="cuda:0", dtype=torch.float32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    kw = dict(scale=w.scale, causal=True, window=w.window, pad_mask=pm, softcap=softcap)
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, pad_mask=pm, softcap=softcap)
+    bufs = [q, k, v, do, o, lse, dq, dk, dv, pm]
 
     def fwd():
         sdpt.attn_fwd(q, k, v, out=o, lse=lse, **kw)
@@ -95,18 +170,29 @@ def other_workload(name, steps, stream, softcap=0.0, **changes):
     def bwd():
         sdpt.attn_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, **kw)
 
-    fwd()
-    bwd()
+    label = w.name + ("" if w.dtype == "bf16" else f" {w.dtype}") + (f" softcap {softcap}" if softcap else "")
+    return {"w": w, "fwd": fwd, "bwd": bwd, "pairs": pairs, "fwd_flops": 4.0 * w.D * pairs, "label": label,
+            "lengths": None if lengths is None else [int(x) for x in lengths], "bufs": bufs}
+
+
+def other_workload(name, steps, stream, softcap=0.0, **changes):
+    """Forward and backward per-call times (median and best of `steps` calls) of a workload."""
+    import torch
+    c = attn_case(name, softcap, **changes)
+    c["fwd"]()
+    c["bwd"]()
     torch.cuda.synchronize()
-    ms_f = time_median(fwd, steps, stream)
-    ms_b = time_median(bwd, steps, stream)
-    ff = 4.0 * w.D * pairs
-    res = {"workload": w.name + ("" if w.dtype == "bf16" else f" {w.dtype}") + (f" softcap {softcap}" if softcap else ""),
-           "pairs": pairs, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
-           "fwd_tflops": round(ff / ms_f / 1e9, 2), "bwd_tflops": round(2.5 * ff / ms_b / 1e9, 2),
-           "step_tflops": round(3.5 * ff / (ms_f + ms_b) / 1e9, 2)}
+    tf = time_calls(c["fwd"], steps, stream)
+    tb = time_calls(c["bwd"], steps, stream)
+    ff = c["fwd_flops"]
+    res = {"workload": c["label"], "pairs": c["pairs"], "reps": steps,
+           "fwd_ms": round(tf["median"], 4), "fwd_ms_best": round(tf["best"], 4),
+           "bwd_ms": round(tb["median"], 4), "bwd_ms_best": round(tb["best"], 4),
+           "fwd_tflops": round(ff / tf["median"] / 1e9, 2), "bwd_tflops": round(2.5 * ff / tb["median"] / 1e9, 2),
+           "step_tflops": round(3.5 * ff / (tf["median"] + tb["median"]) / 1e9, 2)}
     res["step_frac"] = round(res["step_tflops"] / PEAK_BF16_TFLOPS, 4)
-    del q, k, v, do, o, lse, dq, dk, dv
+    del c
+    torch.cuda.empty_cache()
     return res
 
 
@@ -166,9 +252,9 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     fwd()
     bwd()
     torch.cuda.synchronize()
-    ms_f2 = time_median(fwd_two_step, steps, stream)
-    ms_f = time_median(fwd, steps, stream)
-    ms_b = time_median(bwd, steps, stream)
+    ms_f2 = time_calls(fwd_two_step, steps, stream)["median"]
+    ms_f = time_calls(fwd, steps, stream)["median"]
+    ms_b = time_calls(bwd, steps, stream)["median"]
     sdpt.binding.profile(True)
     for _ in range(steps):
         fwd()
@@ -220,7 +306,7 @@ def paged_prefill_workload(steps, stream, B=1, prev=6144, n=2048, Hq=32, Hkv=4, 
 
     run()
     torch.cuda.synchronize()
-    ms = time_median(run, steps, stream)
+    ms = time_calls(run, steps, stream)["median"]
     sdpt.binding.profile(True)
     for _ in range(steps):
         run()
@@ -241,7 +327,9 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=8, help="(batch, kv head) units the oracle times (of 8)")
-    p.add_argument("--no-other", action="store_true", help="skip the sliding-window and varlen workloads")
+    p.add_argument("--no-other", action="store_true", help="skip the other workloads")
+    p.add_argument("--workload", default=None,
+                   help="profile one workload only: tiny_d512, full_d512, window_d256, varlen_d512, decode_d128")
     return p.parse_args()
 
 
@@ -250,56 +338,162 @@ def dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
 
 
-def time_events(fn, iters, stream):
-    """Average milliseconds of fn() over iters calls, timed with HIP events on `stream`."""
-    import torch
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(iters):
-        fn()
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / iters
-
-
-def time_median(fn, iters, stream):
-    """Median milliseconds of one fn() call over iters calls, each timed with its own pair of HIP
-    events on `stream` (robust to a rare stall of the device that one long window would absorb)."""
-    import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    evs[-1][1].synchronize()
-    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+def cpu_info():
+    """Host cores, BLAS library and threads, CPU model."""
+    info = {"cpu_count": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": None, "blas_threads": 1}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                info["blas"] = f"{i.get('internal_api')} {i.get('version')}"
+                info["blas_threads"] = int(i.get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return info
 
 
 def cpu_baseline(units):
-    """Times the float64 oracle (forward + backward of whole (batch, kv head) units) on the host."""
+    """Times the float64 oracle on the host: forward + backward of whole (batch, kv head) units of
+    the step's workload (one process, BLAS threads as the library sets them), and bounded samples
+    of the other workloads."""
     import oracle
-    from synth import ATTN_WORKLOADS, bf16_bits_to_f64, make_attention_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from synth import (ATTN_WORKLOADS, DECODE_WORKLOADS, bf16_bits_to_f64, draw_lengths, make_attention_inputs,
+                       make_decode_inputs)
+    info = cpu_info()
+
+    def attn_units(name, picks):
+        """picks: (batch, kv head) units; the oracle's inputs are the workload's seeded draws, except
+        for the padded varlen workload, whose units are timed on draws of one sequence of the
+        unit's length (the oracle's cost depends on the shapes only)."""
+        w = ATTN_WORKLOADS[name]
+        L = draw_lengths(w, 0)
+        inp = make_attention_inputs(w, seed=0) if L is None else None
+        flops = 0.0
+        t0 = time.perf_counter()
+        for b, g in picks:
+            n = w.S if L is None else int(L[b])
+            src = inp if L is None else make_attention_inputs(w.scaled(B=1, S=n, varlen=None, len_range=None), 0)
+            bb = b if L is None else 0
+            f = {x: bf16_bits_to_f64(src[x][bb:bb + 1]) for x in ("q", "k", "v", "do")}
+            oracle.attention_group(f["q"], f["k"], f["v"], f["do"], 0, g, w.scale, w.causal, w.window, [n])
+            flops += 3.5 * 4 * w.D * causal_pairs(n, w.window) * w.r
+        dt = time.perf_counter() - t0
+        lens = "" if L is None else f" (sequence lengths {[int(L[b]) for b, _ in picks]})"
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "seconds": round(dt, 2),
+                "sample": f"{len(picks)} of {w.B * w.Hkv} (batch, kv-head) units {picks}{lens} of {w.name}, "
+                          f"forward + backward of {w.r} query heads each (causal-counted flops)"}
+
     w = ATTN_WORKLOADS["full_d512"]
-    inp = make_attention_inputs(w, seed=0)
-    q, k, v, do = (bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
+    main = attn_units("full_d512", [divmod(u, w.Hkv) for u in range(units)])
+    per = {"tiny_d512": attn_units("tiny_d512", [(0, 0)]),
+           "window_d256": attn_units("window_d256", [(0, 0), (1, 15)]),
+           "varlen_d512": attn_units("varlen_d512", [(4, 0), (7, 3)])}
+    dw = DECODE_WORKLOADS["decode_d128"]
+    di = make_decode_inputs(dw, seed=0)
+    q, kc, vc = (bf16_bits_to_f64(di[x]) for x in ("q", "k_cache", "v_cache"))
+    nb = 16
     t0 = time.perf_counter()
-    for u in range(units):                 # (batch, kv head) units in order
-        b, g = divmod(u, w.Hkv)
-        for hi in range(w.r):
-            oracle.attention_forward_head(q, k, v, b, g * w.r + hi, w.scale, True)
-        oracle.attention_backward_group(q, k, v, do, b, g, w.scale, True)
+    for b in range(nb):
+        oracle.paged_decode_one(q, kc, vc, di["block_table"], di["ctx_lens"], dw.scale, b)
     dt = time.perf_counter() - t0
-    flops = 3.5 * 4 * w.D * causal_pairs(w.S) * w.r * units
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{units} of {w.B * w.Hkv} (batch, kv-head) units of the workload (forward + backward of "
-                      f"{w.r} query heads each, causal-counted flops), {dt:.1f} s wall, float64 NumPy/BLAS",
-            "seconds": dt, "cpu_count": len(os.sched_getaffinity(0))}
+    tok = int(np.sum(di["ctx_lens"][:nb]))
+    per["decode_d128"] = {"value": tok * dw.Hkv * dw.D * 4 / dt / 1e9, "unit": "GB/s", "seconds": round(dt, 2),
+                          "sample": f"{nb} of {dw.B} sequences of {dw.name} (algorithmic K/V bytes)"}
+    for v in per.values():
+        v["value"] = round(v["value"], 5)
+    return {"value": round(main["value"], 5), "unit": "TFLOP/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": main["sample"] + f", {main['seconds']} s wall, float64 NumPy",
+            "seconds": main["seconds"], "workers": 1, "blas": info["blas"], "blas_threads": info["blas_threads"],
+            "cpu_count": info["cpu_count"], "cpu_model": info["cpu_model"], "per_config": per}
+
+
+def measured_peaks(stream):
+    """Matrix rate, streaming read and copy of plain kernels on this device (attn_peak_probe)."""
+    import torch
+    import scaled_dot_product_tiled_amd as sdpt
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    buf = torch.zeros(cus * 4096, device="cuda:0", dtype=torch.uint8)
+    reps = 4096
+    sdpt.binding.peak_probe(0, buf, reps)
+    t = time_calls(lambda: sdpt.binding.peak_probe(0, buf, reps), 5, stream)
+    flops = 4 * cus * 4 * reps * 8 * 32768.0
+    out["mfma_bf16_tflops"] = round(flops / t["best"] / 1e9, 1)
+    big = torch.zeros(4 << 30, device="cuda:0", dtype=torch.uint8)
+    sdpt.binding.peak_probe(1, big)
+    t = time_calls(lambda: sdpt.binding.peak_probe(1, big), 5, stream)
+    out["hbm_read_gbs"] = round(big.numel() / t["best"] / 1e6, 1)
+    sdpt.binding.peak_probe(2, big)
+    t = time_calls(lambda: sdpt.binding.peak_probe(2, big), 5, stream)
+    out["hbm_copy_gbs"] = round(big.numel() / t["best"] / 1e6, 1)   # bytes read + written
+    out["note"] = ("best of 5 launches: independent bf16 32x32x16 matrix instructions (4 workgroups x 4 waves per "
+                   "CU), a 4 GiB streaming read, a 2 GiB -> 2 GiB streaming copy (read + written bytes)")
+    del buf, big
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_setup(seeds=(0, 1)):
+    """Device copies of the decode workload's seeded pools, one per seed."""
+    import torch
+    from synth import DECODE_WORKLOADS, make_decode_inputs
+    dw = DECODE_WORKLOADS["decode_d128"]
+    pools = []
+    for s in seeds:
+        di = make_decode_inputs(dw, seed=s)
+        pools.append(dict(q=dev(di["q"]), kc=dev(di["k_cache"]), vc=dev(di["v_cache"]),
+                          table=torch.from_numpy(di["block_table"]).to("cuda:0"),
+                          ctx=torch.from_numpy(di["ctx_lens"]).to("cuda:0"), ctx_host=di["ctx_lens"]))
+    return dw, pools
+
+
+def decode_bytes(dw, ctx):
+    tok = int(np.sum(ctx))
+    pages = int(np.sum(-(-ctx.astype(np.int64) // dw.page_size)))
+    return tok * dw.Hkv * dw.D * 2 * 2 + 2 * dw.B * dw.Hq * dw.D * 2 + 4 * pages + 4 * dw.B
+
+
+def profile_workload(args):
+    """--workload: only that workload's steps (for rocprofv3), with its per-kernel event times."""
+    import torch
+    import scaled_dot_product_tiled_amd as sdpt
+    stream = torch.cuda.current_stream()
+    if args.workload == "decode_d128":
+        dw, pools = decode_setup()
+        outs = [torch.empty_like(p["q"]) for p in pools]
+        ws = torch.empty(1 << 25, device="cuda:0", dtype=torch.uint8)
+        it = [0]
+
+        def dec():
+            p = pools[it[0] & 1]
+            sdpt.paged_decode(p["q"], p["kc"], p["vc"], p["table"], p["ctx"], scale=dw.scale, out=outs[it[0] & 1],
+                              workspace=ws)
+            it[0] += 1
+        for _ in range(args.warmup):
+            dec()
+        torch.cuda.synchronize()
+        t = time_calls(dec, args.steps, stream)
+        res = {"workload": dw.name, "ms": rounded(t), "kernels": kernel_times(dec, args.steps)}
+    else:
+        c = attn_case(args.workload, host_inputs=args.workload == "full_d512")
+        for _ in range(args.warmup):
+            c["fwd"]()
+            c["bwd"]()
+        torch.cuda.synchronize()
+        tf = time_calls(c["fwd"], args.steps, stream)
+        tb = time_calls(c["bwd"], args.steps, stream)
+        ff = c["fwd_flops"]
+        res = {"workload": c["label"], "pairs": c["pairs"], "fwd_ms": rounded(tf), "bwd_ms": rounded(tb),
+               "fwd_tflops": round(ff / tf["median"] / 1e9, 2), "bwd_tflops": round(2.5 * ff / tb["median"] / 1e9, 2),
+               "kernels": kernel_times(lambda: (c["fwd"](), c["bwd"]()), args.steps)}
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -312,25 +506,17 @@ def main():
 
     import torch
     import scaled_dot_product_tiled_amd as sdpt
-    from synth import ATTN_WORKLOADS, DECODE_WORKLOADS, make_attention_inputs, make_decode_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.workload is not None:
+        profile_workload(args)
+        return
 
-    w = ATTN_WORKLOADS["full_d512"]
-    inp = make_attention_inputs(w, seed=0)
-    q, k, v, do = (dev(inp[x]) for x in ("q", "k", "v", "do"))
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.S), device="cuda:0", dtype=torch.float32)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    kw = dict(scale=w.scale, causal=True, window=0)
-
-    def fwd():
-        sdpt.attn_fwd(q, k, v, out=o, lse=lse, **kw)
-
-    def bwd():
-        sdpt.attn_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, **kw)
+    c = attn_case("full_d512", host_inputs=True)
+    w = c["w"]
+    fwd, bwd = c["fwd"], c["bwd"]
 
     def step():
         fwd()
@@ -340,55 +526,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    pairs = causal_pairs(w.S) * w.B * w.Hq
-    fwd_flops = 4.0 * w.D * pairs
+    fwd_flops = c["fwd_flops"]
     bwd_flops = 2.5 * fwd_flops
 
-    # timed region: exactly `steps` steps
+    # timed region: exactly `steps` steps between two synchronisations, an event after each
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_step = time_events(step, args.steps, stream)
+    ts = time_calls(step, args.steps, stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps * 1e3
+    ms_step = ts["mean"]
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
     # per-call times (HIP events on the launch stream)
-    ms_fwd = time_events(fwd, args.steps, stream)
-    ms_bwd = time_events(bwd, args.steps, stream)
-    fwd_tf = fwd_flops / (ms_fwd * 1e-3) / 1e12
-    bwd_tf = bwd_flops / (ms_bwd * 1e-3) / 1e12
+    tf = time_calls(fwd, args.steps, stream)
+    tb = time_calls(bwd, args.steps, stream)
+    fwd_tf = fwd_flops / (tf["median"] * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (tb["median"] * 1e-3) / 1e12
 
     # per-kernel times: the library records HIP event pairs around each of its launches
-    sdpt.binding.profile(True)
-    for _ in range(args.steps):
-        step()
-    sdpt.binding.profile(False)
-    kt = sdpt.binding.profile_read()
-    per_kernel = {n: {"launches": c, "ms_avg": round(t / c, 4)} for n, (c, t) in kt.items()}
+    per_kernel = kernel_times(step, args.steps)
     # algorithmic flops of each kernel: a contraction is 2 D flops per visible pair; the forward
     # does two (S, PV), dK/dV four (S, dP, dV, dK), dQ the one the definition adds (dQ)
-    unit = 2.0 * w.D * pairs
+    unit = 2.0 * w.D * c["pairs"]
     algo = {"attn_fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
     dom = max(per_kernel, key=lambda n: per_kernel[n]["ms_avg"] * per_kernel[n]["launches"])
     dom_ms = per_kernel[dom]["ms_avg"]
     dom_tf = algo.get(dom, 0.0) / (dom_ms * 1e-3) / 1e12
+    rp = rocprof_ms("full_d512", dom)
 
     # paged decode, rotating over two independent KV pools
-    dw = DECODE_WORKLOADS["decode_d128"]
-    pools = []
-    for s in (0, 1):
-        di = make_decode_inputs(dw, seed=s)
-        pools.append(dict(q=dev(di["q"]), kc=dev(di["k_cache"]), vc=dev(di["v_cache"]),
-                          table=torch.from_numpy(di["block_table"]).to("cuda:0"),
-                          ctx=torch.from_numpy(di["ctx_lens"]).to("cuda:0"), ctx_host=di["ctx_lens"]))
+    dw, pools = decode_setup()
     outs = [torch.empty_like(p["q"]) for p in pools]
     ws = torch.empty(1 << 25, device="cuda:0", dtype=torch.uint8)
-
-    def dbytes(ctx):
-        tok = int(np.sum(ctx))
-        pages = int(np.sum(-(-ctx.astype(np.int64) // dw.page_size)))
-        return tok * dw.Hkv * dw.D * 2 * 2 + 2 * dw.B * dw.Hq * dw.D * 2 + 4 * pages + 4 * dw.B
-
     it = [0]
 
     def dec():
@@ -401,14 +571,10 @@ def main():
         dec()
     torch.cuda.synchronize()
     n_dec = args.decode_steps - (args.decode_steps % 2)
-    ms_dec = time_events(dec, n_dec, stream)
-    dec_bytes = 0.5 * (dbytes(pools[0]["ctx_host"]) + dbytes(pools[1]["ctx_host"]))
-    dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
-    sdpt.binding.profile(True)
-    for _ in range(n_dec):
-        dec()
-    sdpt.binding.profile(False)
-    dec_kernels = {n: {"launches": c, "ms_avg": round(t / c, 4)} for n, (c, t) in sdpt.binding.profile_read().items()}
+    td = time_calls(dec, n_dec, stream)
+    dec_bytes = 0.5 * (decode_bytes(dw, pools[0]["ctx_host"]) + decode_bytes(dw, pools[1]["ctx_host"]))
+    dec_gbs = dec_bytes / (td["mean"] * 1e-3) / 1e9
+    dec_kernels = kernel_times(dec, n_dec)
 
     # the same decode with every sequence's pages laid out in order (page table = consecutive
     # ids): what the per-page table lookup costs against the permuted pool above
@@ -438,18 +604,28 @@ def main():
     for _ in range(4):
         dec_in_order()
     torch.cuda.synchronize()
-    ms_dec_in_order = time_events(dec_in_order, n_dec, stream)
+    tdo = time_calls(dec_in_order, n_dec, stream)
     del cpools
+    rpd = rocprof_ms("decode_d128", "decode_split")
 
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_bytes(dom),
-            "ms_per_launch": dom_ms, "flop_per_launch": algo.get(dom, 0.0)}
+            "ms_per_launch": dom_ms, "flop_per_launch": algo.get(dom, 0.0),
+            "timing": "HIP event pair around each launch on its stream, averaged over the run's launches",
+            "rocprof_ms_median": None if rp is None else rp[0], "rocprof_ms_mean": None if rp is None else rp[1],
+            "rocprof_source": STATS["full_d512"] if rp is not None else None,
+            "event_vs_rocprof_median": None if rp is None else round(dom_ms / rp[0] - 1.0, 4),
+            "rocprof_frac": None if rp is None else round(algo.get(dom, 0.0) / (rp[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                                          4)}
+
+    peaks = measured_peaks(stream)
 
     others = {}
     if not args.no_other:
+        others["tiny_d512"] = other_workload("tiny_d512", 50, stream)
         # the largest workload last: after its 20 GB of buffers the smaller ones timed slower
         others["ring_cp8_d512"] = ring_workload(5, stream)
-        others["window_d256"] = other_workload("window_d256", 5, stream)
+        others["window_d256"] = other_workload("window_d256", 20, stream)
         others["full_d512_f16"] = other_workload("full_d512", 5, stream, dtype="f16")
         others["full_d512_softcap"] = other_workload("full_d512", 5, stream, softcap=30.0)
         others["paged_prefill_d512"] = paged_prefill_workload(5, stream)
@@ -471,17 +647,27 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "seq_len": w.S, "heads_q": w.Hq, "heads_kv": w.Hkv,
                    "head_dim": w.D, "causal": True, "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"ms": round(ms_fwd, 4), "tflops": round(fwd_tf, 2), "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
-        "bwd": {"ms": round(ms_bwd, 4), "tflops": round(bwd_tf, 2), "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "step_ms": rounded(ts),
+        "step_tflops_median": round((fwd_flops + bwd_flops) / (ts["median"] * 1e-3) / 1e12, 2),
+        "step_tflops_best": round((fwd_flops + bwd_flops) / (ts["best"] * 1e-3) / 1e12, 2),
+        "fwd": {"ms": round(tf["median"], 4), "ms_best": round(tf["best"], 4), "tflops": round(fwd_tf, 2),
+                "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(tb["median"], 4), "ms_best": round(tb["best"], 4), "tflops": round(bwd_tf, 2),
+                "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
         "wall_ms_per_step": round(wall, 4),
         "kernels": per_kernel,
         "roofline": roof,
-        "decode": {"workload": dw.name, "ms": round(ms_dec, 4), "GB/s": round(dec_gbs, 1), "kernels": dec_kernels,
-                   "pages_in_order": {"ms": round(ms_dec_in_order, 4),
-                                      "GB/s": round(dec_bytes / (ms_dec_in_order * 1e-3) / 1e9, 1)},
+        "measured_peaks": peaks,
+        "decode": {"workload": dw.name, "ms": round(td["mean"], 4), "ms_median": round(td["median"], 4),
+                   "ms_best": round(td["best"], 4), "reps": n_dec, "GB/s": round(dec_gbs, 1),
+                   "kernels": dec_kernels,
+                   "pages_in_order": {"ms": round(tdo["mean"], 4), "ms_best": round(tdo["best"], 4),
+                                      "GB/s": round(dec_bytes / (tdo["mean"] * 1e-3) / 1e9, 1)},
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                                "bytes_per_launch": dec_bytes, "traffic": traffic_bytes("decode_split")}},
+                                "bytes_per_launch": dec_bytes, "traffic": traffic_bytes("decode_split"),
+                                "timing": "HIP events around each call (split + merge and the gap between them)",
+                                "rocprof_split_ms_median": None if rpd is None else rpd[0]}},
         "other_workloads": others,
     }
     if not args.no_cpu_baseline:

@@ -124,7 +124,8 @@ attn_status attn_fwd(const attn_shape* shape,
  *              bytes: row statistics (fp32 per query row and head) and dS =
  *              P * (dP - delta) in bf16 for every visible (query, key) pair, kept
  *              between the dK/dV pass and the dQ pass (in 32-key x 128-row blocks,
- *              about B * Hq * S * S bytes for causal attention, less with a window)
+ *              about B * Hq * S * S bytes for causal attention, less with a window or
+ *              with cu_seqlens rows; see the workspace queries below)
  */
 attn_status attn_bwd(const attn_shape* shape,
                      attn_tensor q, attn_tensor k, attn_tensor v,
@@ -345,7 +346,18 @@ attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens,
                             attn_tensor k_out, attn_tensor v_out, void* stream);
 
 /* Workspace sizes in bytes.  varlen: 0 dense, 1 pad_mask, 2 cu_seqlens; causal and
- * window as in the call.  Return 0 for arguments that the matching call would reject. */
+ * window as in the call.  Return 0 for arguments that the matching call would reject.
+ * Each call computes its own requirement and the caller owns the memory, so one
+ * workspace grown to the largest query can serve every call issued on one stream (the
+ * page "[Reland] Add dist GEMM attention and FFN backend", section "Symmetric memory",
+ * sizes its shared workspace the same way: every op states its need, the buffer grows to
+ * the maximum, and serialised calls may reuse the same bytes).
+ * Backward: for cu_seqlens rows each sequence's dS blocks take room for its own length,
+ * bounded from `total` and S (about Hq * total * S bytes for causal attention instead of
+ * B * Hq * S^2); dense and pad_mask rows take B * Hq times the longest sequence's room.  A
+ * backward whose workspace would pass 128 GiB is refused (0 here, ATTN_ERR_UNSUPPORTED
+ * from the call): split such sequences into chunk pairs (attn_bwd_chunk), whose workspace
+ * is bounded by the chunk sizes. */
 size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen);
 size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen, int causal, int window);
 size_t paged_decode_workspace_bytes(const attn_decode_shape* shape);
@@ -364,7 +376,10 @@ size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal,
  * mode is for eager calls, not for calls recorded into a graph. */
 int attn_debug(int on);
 
-/* Static string for a status code. */
+/* Static string for a status code.  The codes follow the eligibility gate of the page
+ * "Gemma4 FFPA attention backend support for accelerating Gemma4-family training" (section
+ * Integration): a case the fused path does not take is reported (ATTN_ERR_UNSUPPORTED) so
+ * that the caller can fall back, rather than computed some other way. */
 const char* attn_status_str(attn_status status);
 
 /* The hipError_t (as int) of the last ATTN_ERR_HIP on this thread, 0 if none. */
@@ -395,6 +410,18 @@ int attn_profile_read(attn_kernel_time* out, int max_entries);
  * restart of one of its workgroups; attn_count_restarts(NULL) stops it.  Returns 0.  The
  * counter is the caller's memory and must stay valid while such calls run. */
 int attn_count_restarts(int32_t* device_counter);
+
+/* Roofline probes for benchmarks (not on the attention path): one launch, asynchronous on
+ * `stream`, of a kernel that shows what a plain kernel reaches on this device, to set beside
+ * the published MI355X peaks (dense bf16 matrix 2.5 PFLOP/s and HBM 8 TB/s, which assume the
+ * peak engine clock).  The caller times it (HIP events on the stream).
+ *   kind 0  matrix rate: 4 workgroups of 4 waves per compute unit, each wave `reps` rounds of
+ *           8 independent v_mfma_f32_32x32x16_bf16 (32768 flop each); writes 1024 bytes per
+ *           workgroup to buf (bytes >= compute units * 4096)
+ *   kind 1  streaming read of the first `bytes` of buf (a multiple of 32, >= 4096)
+ *   kind 2  streaming copy of the first half of buf's `bytes` to the second half
+ * Returns ATTN_ERR_INVALID_ARG for a null or misaligned buf, too few bytes or another kind. */
+attn_status attn_peak_probe(int kind, void* buf, size_t bytes, int reps, void* stream);
 
 /* Library version, "major.minor.patch". */
 const char* attn_version(void);

@@ -56,7 +56,7 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read", "attn_count_restarts", "paged_decode_noalloc",
-           "paged_decode_noalloc_max_bytes")
+           "paged_decode_noalloc_max_bytes", "attn_peak_probe")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -124,6 +124,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_last_hip_error.restype = ctypes.c_int
     lib.attn_version.argtypes = []
     lib.attn_version.restype = ctypes.c_char_p
+    lib.attn_peak_probe.argtypes = [ctypes.c_int, vp, sz, ctypes.c_int, vp]
+    lib.attn_peak_probe.restype = ctypes.c_int
     lib.attn_count_restarts.argtypes = [vp]
     lib.attn_count_restarts.restype = ctypes.c_int
     lib.attn_profile.argtypes = [ctypes.c_int]
@@ -588,6 +590,13 @@ def count_restarts(counter: Optional[torch.Tensor]) -> None:
     if counter is not None and (counter.dtype != torch.int32 or not counter.is_cuda):
         raise TypeError("counter must be an int32 device tensor")
     load_library().attn_count_restarts(counter.data_ptr() if counter is not None else None)
+
+
+def peak_probe(kind: int, buf: torch.Tensor, reps: int = 1) -> None:
+    """Launches roofline probe `kind` (0 matrix rate, 1 streaming read, 2 streaming copy) on the
+    current stream over the device buffer buf (see attn_peak_probe)."""
+    _check(load_library().attn_peak_probe(int(kind), buf.data_ptr(), buf.numel() * buf.element_size(), int(reps),
+                                          _stream()), "attn_peak_probe")
 
 
 def profile(on: bool) -> None:

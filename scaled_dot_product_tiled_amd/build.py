@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_merge.hip", "paged_kv.hip", "varlen_prep.hip",
-           "attn_api.cpp"]
+           "peak_probe.hip", "attn_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

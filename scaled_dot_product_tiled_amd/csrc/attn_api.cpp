@@ -264,10 +264,32 @@ DsLayout ds_layout(const Call& c) {
   return L;
 }
 
-size_t ds_bytes(const Call& c) {
+// Packed rows (cu_seqlens) give each sequence a dS region sized by its own length
+// (ds_head_blocks), placed by a prefix sum on the device; batches past kOrderMaxBatch keep one
+// region of the longest sequence's size per (sequence, head).
+bool ds_per_sequence(const Call& c) { return c.varlen == 2 && c.B <= attn::kOrderMaxBatch; }
+
+size_t ds_seq_bytes(const Call& c) { return ds_per_sequence(c) ? round_up(sizeof(int64_t) * (size_t)c.B) : 0; }
+
+// dS blocks of the whole call.  Per sequence: with n_b = ceil(len_b / 128) query tiles,
+// sum_b n_b <= min(B nqt, floor(total / 128) + B) =: N and n_b <= nqt, so the triangular layout
+// needs at most 2 N (nqt + 1) blocks per head and the others N cnt.
+int64_t ds_blocks(const Call& c) {
   const DsLayout L = ds_layout(c);
-  return round_up((size_t)c.B * c.Hq * L.per_head * attn::kDsBlockElems * sizeof(__bf16));
+  if (!ds_per_sequence(c)) return (int64_t)c.B * c.Hq * L.per_head;
+  const int64_t nqt = (c.S + attn::kDsRows - 1) / attn::kDsRows;
+  const int64_t N = std::min<int64_t>((int64_t)c.B * nqt, c.total / attn::kDsRows + c.B);
+  return (int64_t)c.Hq * (L.tri ? 2 * N * (nqt + 1) : N * L.cnt);
 }
+
+size_t ds_bytes(const Call& c) {
+  return round_up((size_t)ds_blocks(c) * attn::kDsBlockElems * sizeof(__bf16));
+}
+
+// Largest backward workspace: the dS blocks grow with the square of the sequence length (about
+// B Hq S^2 bytes for causal attention).  Past this a whole-sequence backward is refused
+// (ATTN_ERR_UNSUPPORTED); chunk pairs (attn_bwd_chunk) bound the workspace by the chunk sizes.
+constexpr size_t kMaxBwdWorkspace = size_t(1) << 37;  // 128 GiB of the GPU's 288 GB
 
 size_t stat_bytes(const Call& c) {
   return round_up(sizeof(float) * (size_t)c.Hq * (c.varlen == 2 ? (size_t)c.total : (size_t)c.B * c.S));
@@ -293,7 +315,7 @@ size_t kv_part_bytes(const Call& c) {
 }
 
 size_t bwd_bytes(const Call& c) {
-  return meta_bytes(c.B, c.varlen) + stat_bytes(c) + ds_bytes(c) + kv_part_bytes(c);
+  return meta_bytes(c.B, c.varlen) + ds_seq_bytes(c) + stat_bytes(c) + ds_bytes(c) + kv_part_bytes(c);
 }
 
 Call whole_call(const attn_shape* s, int varlen, int causal, int window) {
@@ -446,10 +468,17 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
   // adding the parts of a pair that has no visible (query, key) pair changes nothing
   if (grad_f32 && c.causal && c.shift <= -c.S) return ATTN_OK;
   int32_t* meta = static_cast<int32_t*>(workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + meta_bytes(c.B, c.varlen));
+  int64_t* ds_seq = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + meta_bytes(c.B, c.varlen));
+  float* delta = reinterpret_cast<float*>(reinterpret_cast<char*>(ds_seq) + ds_seq_bytes(c));
   attn_status st;
   if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
   if ((st = varlen_meta(c, cu_seqlens, pad_mask, meta, s))) return st;
+  const DsLayout L = ds_layout(c);
+  if (ds_per_sequence(c) &&
+      (st = launch("ds_seq_base", s, c.B, [&] {
+         return attn::launch_ds_seq_base(meta + c.B, c.B, c.Hq, L.tri, L.cnt, ds_blocks(c), ds_seq, s);
+       })))
+    return st;
   attn::AttnArgs a = {};
   fill_common(a, c, scale, meta);
   set_tensors(a, t, c.varlen == 2, true);
@@ -462,7 +491,7 @@ attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* l
   a.lse = const_cast<float*>(lse);
   a.delta = delta;
   {
-    const DsLayout L = ds_layout(c);
+    a.ds_seq = ds_per_sequence(c) ? ds_seq : nullptr;
     a.dsb = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(delta) + stat_bytes(c));
     a.ds_head = L.per_head;
     a.ds_tri = L.tri;
@@ -507,7 +536,8 @@ extern "C" {
 size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen, int causal, int window) {
   if (varlen < 0 || varlen > 2 || check_shape(shape, varlen) != ATTN_OK) return 0;
   if ((causal != 0 && causal != 1) || window < 0 || (window > 0 && !causal)) return 0;
-  return bwd_bytes(whole_call(shape, varlen, causal, window));
+  const size_t n = bwd_bytes(whole_call(shape, varlen, causal, window));
+  return n > kMaxBwdWorkspace ? 0 : n;
 }
 
 size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen) {
@@ -542,6 +572,7 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
   attn_status st = check_common(shape, scale, causal, window, cu_seqlens, pad_mask, workspace_bytes,
                                 shape ? attn_bwd_workspace_bytes(shape, varlen, causal, window) : 0, workspace);
   if (st != ATTN_OK) return st;
+  if (bwd_bytes(whole_call(shape, varlen, causal, window)) > kMaxBwdWorkspace) return ATTN_ERR_UNSUPPORTED;
   if (!softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
   const bool packed = varlen == 2;
   if ((st = check_tensor(q, packed)) || (st = check_tensor(k, packed)) || (st = check_tensor(v, packed)) ||
@@ -558,7 +589,8 @@ attn_status attn_bwd(const attn_shape* shape, attn_tensor q, attn_tensor k, attn
 size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal, int window, int64_t q_pos0,
                                       int64_t k_pos0) {
   if (check_chunk(shape, causal, window, q_pos0, k_pos0) != ATTN_OK) return 0;
-  return bwd_bytes(chunk_call(shape, causal, window, q_pos0, k_pos0));
+  const size_t n = bwd_bytes(chunk_call(shape, causal, window, q_pos0, k_pos0));
+  return n > kMaxBwdWorkspace ? 0 : n;
 }
 
 attn_status attn_fwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_tensor k, attn_tensor v, float scale,
@@ -604,6 +636,7 @@ attn_status attn_bwd_chunk(const attn_chunk_shape* shape, attn_tensor q, attn_te
   if (st != ATTN_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap)) return ATTN_ERR_INVALID_ARG;
   if (grad_dtype != shape->dtype && grad_dtype != ATTN_DTYPE_F32) return ATTN_ERR_INVALID_ARG;
+  if (bwd_bytes(chunk_call(shape, causal, window, q_pos0, k_pos0)) > kMaxBwdWorkspace) return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_bwd_chunk_workspace_bytes(shape, causal, window, q_pos0, k_pos0);
   if (need > 0 &&
       (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))))
@@ -878,6 +911,19 @@ int attn_profile_read(attn_kernel_time* out, int max_entries) {
   g_prof.launches.clear();
   g_prof.used = 0;
   return failed ? -1 : n;
+}
+
+attn_status attn_peak_probe(int kind, void* buf, size_t bytes, int reps, void* stream) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (buf == nullptr || !aligned16(buf) || cus <= 0) return ATTN_ERR_INVALID_ARG;
+  if (kind == 0 && (reps <= 0 || bytes < (size_t)cus * 4 * 256 * sizeof(float))) return ATTN_ERR_INVALID_ARG;
+  if ((kind == 1 || kind == 2) && (bytes < 4096 || bytes % 32 != 0)) return ATTN_ERR_INVALID_ARG;
+  if (kind < 0 || kind > 2) return ATTN_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(attn::launch_peak_probe(kind, buf, bytes, reps, cus, s));
 }
 
 const char* attn_version(void) { return "0.1.0"; }

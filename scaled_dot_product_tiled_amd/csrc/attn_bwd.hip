@@ -137,6 +137,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
   const int b = unit / a.Hkv;
   int len = a.seq_len ? a.seq_len[b] : a.S;
   len = min(max(len, 0), a.S);
+  // packed rows: this sequence's dS region (a sequence that does not fit is skipped)
+  const int64_t ds_b = a.ds_seq ? a.ds_seq[b] : 0;
+  if (ds_b < 0) len = 0;
   const int lenk = a.seq_len ? len : a.Sk;  // key rows
   const int dlt = a.q_shift;
   const int off = a.seq_off ? a.seq_off[b] : 0;
@@ -201,11 +204,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
     const bf16* qrow = a.q + b * a.q_sb + (int64_t)(off + i00) * a.q_ss + hb0 * a.q_sh;
     const bf16* drow = a.dout + b * a.do_sb + (int64_t)(off + i00) * a.do_ss + hb0 * a.do_sh;
     int64_t so = b * a.st_sb + hb0 * a.st_sh + off;
-    bf16* dshead = a.dsb + (int64_t)(b * a.Hq + hb0) * a.ds_head * kDsBlockElems;
+    const int64_t ds_hb = a.ds_seq ? ds_head_blocks(len, a.ds_tri, a.ds_cnt) : a.ds_head;
+    bf16* dshead = a.dsb + ((a.ds_seq ? ds_b : (int64_t)b * a.Hq * ds_hb) + (int64_t)hb0 * ds_hb) * kDsBlockElems;
     const int64_t q_wrap = -(int64_t)(rs - 1) * a.q_sh - (int64_t)MQ * a.q_ss;
     const int64_t d_wrap = -(int64_t)(rs - 1) * a.do_sh - (int64_t)MQ * a.do_ss;
     const int64_t s_wrap = -(int64_t)(rs - 1) * a.st_sh;
-    const int64_t ds_step = (int64_t)a.ds_head * kDsBlockElems;
+    const int64_t ds_step = ds_hb * kDsBlockElems;
     int ds_qt = -1;  // query tile of the dS block index ds_bi (of this wave's key block)
     int64_t ds_bi = -1;
     auto stats = [&](int64_t sofs, int i0s, int buf) {
@@ -643,6 +647,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
   const int h = g * a.r + rem % a.r;
   int len = a.seq_len ? a.seq_len[b] : a.S;
   len = min(max(len, 0), a.S);
+  const int64_t ds_b = a.ds_seq ? a.ds_seq[b] : 0;
+  if (ds_b < 0) len = 0;  // a sequence that did not fit the workspace (see bwd_dkdv)
   const int lenk = a.seq_len ? len : a.Sk;  // key rows
   const int dlt = a.q_shift;
   const int off = a.seq_off ? a.seq_off[b] : 0;
@@ -670,7 +676,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
 
   if (kb_first <= kb_last) {
     const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh + dh * D;
-    const bf16* sbase = a.dsb + (int64_t)(b * a.Hq + h) * a.ds_head * kDsBlockElems;
+    const int64_t ds_hb = a.ds_seq ? ds_head_blocks(len, a.ds_tri, a.ds_cnt) : a.ds_head;
+    const bf16* sbase = a.dsb + ((a.ds_seq ? ds_b : (int64_t)b * a.Hq * ds_hb) + (int64_t)h * ds_hb) * kDsBlockElems;
     auto sblock = [&](int kb) {  // every block in kb_first .. kb_last holds a visible pair, so it is stored
       const int64_t bi = ds_block_index(qt, kb, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
       return sbase + (bi < 0 ? 0 : bi) * kDsBlockElems;

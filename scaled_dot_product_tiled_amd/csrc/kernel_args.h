@@ -38,6 +38,11 @@ struct AttnArgs {
   __bf16* dsb;   // backward: dS blocks (see ds_block_index)
   int64_t ds_head;  // dS blocks per (batch, query head)
   int ds_tri, ds_cnt;  // block layout: triangular, or ds_cnt blocks per query tile
+  // packed (cu_seqlens) rows: first dS block of each sequence's region, whose heads hold
+  // ds_head_blocks(len) blocks each (sized by the sequence's own length, not the longest);
+  // -1: the sequence does not fit the workspace (inconsistent offsets) and is skipped.
+  // NULL: every (batch, head) holds ds_head blocks.
+  const int64_t* ds_seq;
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
@@ -153,6 +158,11 @@ __host__ __device__ inline int ds_kb_hi(int qt, int causal, int Sk, int delta) {
   const int hi = last < 0 ? -1 : last / kDsKeys;
   return hi < nkb - 1 ? hi : nkb - 1;
 }
+// dS blocks of one query head of a sequence of len rows in the packed layout.
+__host__ __device__ inline int64_t ds_head_blocks(int len, int tri, int cnt) {
+  const int64_t n = (len + kDsRows - 1) / kDsRows;
+  return tri ? 2 * n * (n + 1) : n * cnt;
+}
 // Index of block (qt, kb) among the blocks of one (batch, head); -1 if it is not stored.
 __host__ __device__ inline int64_t ds_block_index(int qt, int kb, int causal, int window, int delta, int Sk,
                                                   int tri, int cnt) {
@@ -168,6 +178,10 @@ hipError_t launch_varlen_prep(const uint8_t* pad_mask, const int32_t* cu_seqlens
 // Batch indices by decreasing length (ties by index), from the lengths varlen_prep wrote.
 constexpr int kOrderMaxBatch = 4096;  // larger batches keep the plain round order
 hipError_t launch_varlen_order(const int32_t* seq_len, int B, int32_t* order, hipStream_t stream);
+// First dS block of each packed sequence (prefix sums of Hq * ds_head_blocks(len)); a sequence
+// whose region would end past `capacity` blocks gets -1.
+hipError_t launch_ds_seq_base(const int32_t* seq_len, int B, int Hq, int tri, int cnt, int64_t capacity,
+                              int64_t* ds_seq, hipStream_t stream);
 // Debug-mode metadata checks: synchronise the stream and set bad when the metadata is invalid.
 hipError_t check_varlen_meta(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S, int total,
                              hipStream_t stream, bool& bad);
@@ -185,6 +199,8 @@ constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_lse_merge(const MergeArgs& a, int D, hipStream_t stream);
 hipError_t launch_paged_kv_copy(const PagedCopyArgs& a, hipStream_t stream);
+// Roofline probes (not on the attention path): 0 matrix rate, 1 streaming read, 2 streaming copy.
+hipError_t launch_peak_probe(int kind, void* buf, size_t bytes, int reps, int cus, hipStream_t stream);
 
 // Tile geometry used by the host planner.
 constexpr int kFwdRows = 128;   // query rows per forward workgroup

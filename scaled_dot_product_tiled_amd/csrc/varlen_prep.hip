@@ -65,6 +65,27 @@ hipError_t launch_varlen_order(const int32_t* seq_len, int B, int32_t* order, hi
   return hipGetLastError();
 }
 
+// Thread b sums the dS blocks of sequences 0 .. b-1 (O(B^2) reads of B lengths, all from cache;
+// used for B <= kOrderMaxBatch).  With consistent offsets the host's capacity bound holds; with
+// overlapping ones the lengths can sum past the packed rows, and a sequence that would not fit
+// is marked -1 so that the backward skips it instead of writing past the workspace.
+__global__ __launch_bounds__(256) void ds_seq_base_kernel(const int32_t* seq_len, int B, int Hq, int tri, int cnt,
+                                                           int64_t capacity, int64_t* ds_seq) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  int64_t base = 0;
+  for (int o = 0; o < b; ++o) base += (int64_t)Hq * ds_head_blocks(seq_len[o], tri, cnt);
+  const int64_t need = (int64_t)Hq * ds_head_blocks(seq_len[b], tri, cnt);
+  ds_seq[b] = base + need <= capacity ? base : -1;
+}
+
+hipError_t launch_ds_seq_base(const int32_t* seq_len, int B, int Hq, int tri, int cnt, int64_t capacity,
+                              int64_t* ds_seq, hipStream_t stream) {
+  hipLaunchKernelGGL(ds_seq_base_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, seq_len, B, Hq, tri, cnt,
+                     capacity, ds_seq);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Metadata checks (debug mode).  Any thread that finds a violation stores 1 to the error word.
 // ---------------------------------------------------------------------------

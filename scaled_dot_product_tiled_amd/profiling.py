@@ -12,8 +12,9 @@
         by the copy run's bytes per counter unit, with the sha256 of the kernel's source file.
 
     python -m scaled_dot_product_tiled_amd.profiling summaries OUT
-        writes the profiles/ summaries of the bench.py workloads from OUT/{stats,fetch,write,
-        cfetch,cwrite} and, if present, OUT/sq (the rocprofv3 runs listed in each summary).
+        writes the profiles/ summaries of every workload W with a directory OUT/W holding the
+        rocprofv3 passes of `bench.py --workload W` (stats, fetch, write, sq; the copy
+        calibration in OUT/cfetch, OUT/cwrite); each summary lists the commands that made it.
 
 bench.py reads such records back (read_traffic) and reports the traffic only while the
 source file still has the recorded hash.
@@ -25,6 +26,8 @@ import hashlib
 import os
 import sys
 from typing import Dict, List, Optional
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -106,35 +109,80 @@ def read_traffic(path: str, kernel: str) -> Optional[dict]:
     return None
 
 
+def trace_durations(d: str) -> Dict[str, List[float]]:
+    """{kernel name: [duration ns per dispatch, in dispatch order]} of a --kernel-trace csv output."""
+    out: Dict[str, List[float]] = {}
+    try:
+        files = _csvs(d, "_kernel_trace.csv")
+    except FileNotFoundError:
+        return out
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
+        out.setdefault(r["Kernel_Name"], []).append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    return out
+
+
 def stats_table(d: str) -> str:
+    """Per-kernel table of a --kernel-trace --stats output: calls, mean, median (from the trace),
+    min, max and share of the total time."""
     rows = []
     for f in _csvs(d, "_kernel_stats.csv"):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    lines = [f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    dur = trace_durations(d)
+    lines = [f"{'calls':>6} {'avg_us':>10} {'med_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
     for r in rows:
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
-                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}  {r['Name']}")
+        med = float(np.median(dur[r["Name"]])) / 1e3 if r["Name"] in dur else float("nan")
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {med:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}  "
+                     f"{r['Name']}")
     return "\n".join(lines)
 
 
-COMMANDS = """Commands (cd /tmp && export TMPDIR=/tmp first; R = repository root, OUT = an output directory):
-  rocprofv3 --kernel-trace --stats -d $OUT/stats --output-format csv -- python3 $R/bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-other
-  rocprofv3 --pmc FETCH_SIZE -d $OUT/fetch --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --decode-steps 4 --no-cpu-baseline --no-other
-  rocprofv3 --pmc WRITE_SIZE -d $OUT/write --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --decode-steps 4 --no-cpu-baseline --no-other
-  rocprofv3 --pmc FETCH_SIZE -d $OUT/cfetch --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
-  rocprofv3 --pmc WRITE_SIZE -d $OUT/cwrite --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
-  rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_INST_LDS SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE -d $OUT/sq --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --decode-steps 4 --no-cpu-baseline --no-other
-  python3 -m scaled_dot_product_tiled_amd.profiling summaries $OUT
-"""
+WORKLOADS = {
+    "tiny_d512": "tiny causal GQA, B=1 S=128 Hq=2 Hkv=1 D=512 (forward + backward)",
+    "full_d512": "causal GQA, B=2 S=4096 Hq=32 Hkv=4 D=512 (forward + backward; the bench.py step)",
+    "window_d256": "causal sliding window 1024, B=2 S=4096 Hq=32 Hkv=16 D=256, Q/K std 3 (forward + backward)",
+    "varlen_d512": "padded varlen causal GQA, B=8 lengths U{512..8192} padded to 8192, Hq=32 Hkv=4 D=512 "
+                   "(forward + backward)",
+    "decode_d128": "paged decode, B=64 Hq=32 Hkv=8 D=128, 16-token pages, contexts U{512..4096} (two pools)",
+}
 
 SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_VALU_MFMA_BUSY_CYCLES",
                "SQ_BUSY_CU_CYCLES", "SQ_WAIT_INST_LDS", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_LDS_ADDR_CONFLICT",
                "GRBM_GUI_ACTIVE")
-SQ_KERNELS = (("attn_fwd", "fwd_kernel<512,32,false,false,false>"), ("bwd_dkdv", "bwd_dkdv_kernel<512,false,false>"),
-              ("bwd_dq", "bwd_dq_kernel<256,4,2,false>"), ("decode_split", "decode_split_kernel<4,false,false>"))
 N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+# source file of each kernel family (for the sha256 a traffic record carries)
+SOURCES = (("fwd_kernel<", "attn_fwd.hip"), ("fwd_merge_kernel<", "attn_fwd.hip"), ("bwd_", "attn_bwd.hip"),
+           ("decode_", "attn_decode.hip"), ("varlen_", "varlen_prep.hip"), ("ds_seq_base", "varlen_prep.hip"),
+           ("lse_merge", "attn_merge.hip"), ("paged_kv", "paged_kv.hip"))
+
+
+def commands(wl: str) -> str:
+    steps = "--steps 10 --warmup 3" if wl != "decode_d128" else "--steps 50 --warmup 4"
+    few = "--steps 2 --warmup 1" if wl != "decode_d128" else "--steps 4 --warmup 2"
+    b = f"python3 $R/bench.py --workload {wl}"
+    return f"""Commands (cd /tmp && export TMPDIR=/tmp first; R = repository root, OUT = an output directory):
+  rocprofv3 --kernel-trace --stats -d $OUT/{wl}/stats --output-format csv -- {b} {steps}
+  rocprofv3 --pmc FETCH_SIZE -d $OUT/{wl}/fetch --output-format csv -- {b} {few}
+  rocprofv3 --pmc WRITE_SIZE -d $OUT/{wl}/write --output-format csv -- {b} {few}
+  rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d $OUT/{wl}/sq --output-format csv -- {b} {few}
+  rocprofv3 --pmc FETCH_SIZE -d $OUT/cfetch --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
+  rocprofv3 --pmc WRITE_SIZE -d $OUT/cwrite --output-format csv -- python3 $R/scaled_dot_product_tiled_amd/profiling.py copy --mib 1024
+  python3 -m scaled_dot_product_tiled_amd.profiling summaries $OUT
+"""
+
+
+def _short(name: str) -> str:
+    """'void attn::fwd_kernel<512, 32, false, false, false>(attn::AttnArgs)' -> 'fwd_kernel<512,32,false,false,false>'"""
+    n = name.replace("void ", "").replace("attn::", "").replace(" ", "")
+    return n.split("(")[0]
 
 
 def sq_table(d: str) -> str:
@@ -143,91 +191,98 @@ def sq_table(d: str) -> str:
     eighth of it; SQ_VALU_MFMA_BUSY_CYCLES is summed over the 1024 SIMDs, SQ_INSTS_LDS_LOAD_BANDWIDTH
     counts 64-byte units, SQ_WAIT_INST_LDS counts wave-cycles in units of 4."""
     vals = {c: counter_per_dispatch(d, c) for c in SQ_COUNTERS}
-    rows = [f"{'kernel':14s} {'cycles':>9s} {'MFMA busy':>9s} {'LDS B/clk/CU':>12s} {'bank confl.':>11s} "
+    rows = [f"{'kernel':42s} {'cycles':>9s} {'MFMA busy':>9s} {'LDS B/clk/CU':>12s} {'bank confl.':>11s} "
             f"{'LDS fifo full':>13s} {'wait LDS issue':>14s}"]
-    for label, k in SQ_KERNELS:
-        m = {c: sum(_pick(vals[c], k)) / len(_pick(vals[c], k)) for c in SQ_COUNTERS}
+    names = sorted(vals["GRBM_GUI_ACTIVE"], key=lambda n: -sum(vals["GRBM_GUI_ACTIVE"][n]))
+    for k in names:
+        if not any(k.replace(" ", "").startswith(p) or ("attn::" + p) in k.replace(" ", "") for p, _ in SOURCES):
+            continue
+        m = {c: sum(vals[c].get(k, [0.0])) / max(len(vals[c].get(k, [1.0])), 1) for c in SQ_COUNTERS}
         cyc = m["GRBM_GUI_ACTIVE"] / N_XCD
+        if cyc <= 0:
+            continue
         busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
         lds = m["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64 / (cyc * N_CU)
         conf = m["SQ_LDS_BANK_CONFLICT"] / max(m["SQ_LDS_IDX_ACTIVE"], 1.0)
         fifo = m["SQ_LDS_DATA_FIFO_FULL"] / max(m["SQ_BUSY_CU_CYCLES"], 1.0)
         wait = 4 * m["SQ_WAIT_INST_LDS"] / max(4 * cyc * N_CU, 1.0)   # per wave slot: 4 waves per CU
-        rows.append(f"{label:14s} {cyc:9.0f} {100 * busy:8.1f}% {lds:12.1f} {100 * conf:10.2f}% {100 * fifo:12.2f}% "
-                    f"{100 * wait:13.1f}%")
+        rows.append(f"{_short(k):42s} {cyc:9.0f} {100 * busy:8.1f}% {lds:12.1f} {100 * conf:10.2f}% "
+                    f"{100 * fifo:12.2f}% {100 * wait:13.1f}%")
     return "\n".join(rows)
 
-# (file, kernel name, source, what, algorithmic bytes) of each traffic summary
-TRAFFIC_SUMMARIES = [
-    ("attn_fwd_d512_B2_S4096_traffic.txt", "fwd_kernel<512,32,false,false,false>", "scaled_dot_product_tiled_amd/csrc/attn_fwd.hip",
-     "forward kernel, causal GQA B=2 S=4096 Hq=32 Hkv=4 D=512 (bench.py workload)",
-     "Algorithmic bytes: Q, K, V read once (268 + 33.5 + 33.5 MB) and O, LSE written once (268 + 1 MB).  "
-     "The fetch figure counts every L2 miss sent to the fabric (the 256 MB last-level cache can serve part "
-     "of it); above the algorithmic reads it is the K/V re-reads of the query-row tiles of each head group."),
-    ("bwd_dkdv_d512_B2_S4096_traffic.txt", "bwd_dkdv_kernel<512,false,false>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
-     "dK/dV kernel of the backward, causal GQA B=2 S=4096 Hq=32 Hkv=4 D=512 (bench.py workload)",
-     "Algorithmic bytes: Q, dO read once (268 MB each), K, V (33.5 MB each), LSE and delta (1 MB each); "
-     "writes dK, dV (33.5 MB each) and the stored dS blocks (1.107 GB).  Fetch above the algorithmic reads "
-     "is the Q / dO re-reads of the 64 key tiles of each head group that miss in L2."),
-    ("bwd_dq_d512_B2_S4096_traffic.txt", "bwd_dq_kernel<256,4,2,false>", "scaled_dot_product_tiled_amd/csrc/attn_bwd.hip",
-     "dQ kernel of the backward (dQ = scale dS K over the stored dS blocks, two head_dim halves), same workload",
-     "Algorithmic bytes: dS blocks read once (1.107 GB), K (33.5 MB); dQ written once (268 MB).  Each dS "
-     "block is read by both head_dim halves; the second read is meant to hit in L2."),
-    ("decode_split_d128_B64_traffic.txt", "decode_split_kernel<4,false,false>", "scaled_dot_product_tiled_amd/csrc/attn_decode.hip",
-     "paged decode split kernel, B=64 Hq=32 Hkv=8 D=128, 16-token pages, contexts U{512..4096} "
-     "(bench.py decode workload)",
-     "Algorithmic bytes: K and V of every context token once (619.6 MB per launch, the bench's "
-     "bytes_per_launch); writes the chunk partials (about 5.5 MB)."),
-]
+
+def traffic_records(d: str, out: str) -> List[str]:
+    """One traffic record per attention kernel of a workload's fetch / write passes."""
+    fetch = counter_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE")
+    recs = []
+    for name in sorted(fetch, key=lambda n: -sum(fetch[n]) / len(fetch[n])):
+        short = _short(name)
+        src = next((f for p, f in SOURCES if short.startswith(p)), None)
+        if src is None:
+            continue
+        recs.append(traffic_record(short, os.path.join(ROOT, "scaled_dot_product_tiled_amd", "csrc", src),
+                                   os.path.join(d, "fetch"), os.path.join(d, "write"), os.path.join(out, "cfetch"),
+                                   os.path.join(out, "cwrite"), 1024))
+    return recs
+
+
+def _bench_line(d: str) -> Optional[dict]:
+    import json
+    line = None
+    for f in glob.glob(os.path.join(d, "*.log")):
+        for ln in open(f):
+            if ln.startswith("{"):
+                try:
+                    line = json.loads(ln)
+                except ValueError:
+                    pass
+    return line
 
 
 def write_summaries(out: str, pdir: str) -> None:
-    import json
-    for fn, k, src, what, note in TRAFFIC_SUMMARIES:
-        rec = traffic_record(k, os.path.join(ROOT, src), os.path.join(out, "fetch"), os.path.join(out, "write"),
-                             os.path.join(out, "cfetch"), os.path.join(out, "cwrite"), 1024)
-        kv = dict(t.split("=", 1) for t in rec[len("record:"):].split())
-        txt = (f"HBM traffic per dispatch: {what}\n\n"
-               "rocprofv3 counters FETCH_SIZE and WRITE_SIZE (one pass each, averaged over the dispatches of the\n"
-               "kernel), scaled by the same counters read for a plain 1 GiB device copy: bytes per counter unit\n"
-               f"{kv['fetch_scale']} (FETCH_SIZE) and {kv['write_scale']} (WRITE_SIZE).\n\n"
-               f"  fetched {int(kv['fetch_bytes']) / 1e9:.3f} GB   written {int(kv['write_bytes']) / 1e9:.3f} GB   "
-               "per dispatch\n\n"
-               f"{note}\n\n{COMMANDS}\n"
-               "bench.py reads the record line below for its roofline \"traffic\" field, as long as the kernel\n"
-               f"source still has the recorded sha256.\n\n{rec}\n")
-        with open(os.path.join(pdir, fn), "w") as fh:
+    """profiles/<workload>_kernel_stats.txt, _traffic.txt and _sq.txt for every workload directory
+    OUT/<workload> that holds the rocprofv3 passes of commands(workload)."""
+    os.makedirs(pdir, exist_ok=True)
+    for wl, what in WORKLOADS.items():
+        d = os.path.join(out, wl)
+        if not os.path.isdir(os.path.join(d, "stats")):
+            continue
+        cmds = commands(wl)
+        txt = f"Kernel times on one MI355X, rocprofv3 kernel trace: {what}.\n\n{cmds}\n{stats_table(os.path.join(d, 'stats'))}\n"
+        line = _bench_line(d)
+        if line is not None and "kernels" in line:
+            txt += "\nbench.py --workload's own HIP-event timings of the same run (ms per launch):\n"
+            for n, v in line["kernels"].items():
+                txt += f"  {n:14s} {v['ms_avg']:.4f}\n"
+        with open(os.path.join(pdir, f"{wl}_kernel_stats.txt"), "w") as fh:
             fh.write(txt)
-    line = None
-    for f in glob.glob(os.path.join(out, "**", "*.log"), recursive=True) + [os.path.join(out, "bench_stats.log")]:
-        if os.path.exists(f):
-            for ln in open(f):
-                if ln.startswith('{"metric"'):
-                    line = json.loads(ln)
-    txt = ("Kernel times of bench.py on one MI355X: causal GQA forward + backward, B=2 S=4096 Hq=32 Hkv=4\n"
-           "D=512 (10 timed + 3 warm-up steps, plus the per-call and per-kernel passes) and the paged decode\n"
-           "B=64 Hq=32 Hkv=8 D=128.\n\n"
-           f"{COMMANDS}\n{stats_table(os.path.join(out, 'stats'))}\n")
-    if line is not None:
-        txt += "\nbench.py's own HIP-event timings of the same run (ms per launch):\n"
-        for n, v in list(line["kernels"].items()) + list(line["decode"]["kernels"].items()):
-            txt += f"  {n:14s} {v['ms_avg']:.4f}\n"
-        txt += f"\nbench.py line: value {line['value']} TFLOP/s, ms_per_step {line['ms_per_step']}\n"
-    with open(os.path.join(pdir, "bench_d512_B2_S4096_kernel_stats.txt"), "w") as fh:
-        fh.write(txt)
-    if os.path.isdir(os.path.join(out, "sq")):
-        txt = ("Matrix-core and LDS use of the bench.py kernels on one MI355X (causal GQA B=2 S=4096 Hq=32 Hkv=4\n"
-               "D=512 forward and backward; paged decode B=64 Hq=32 Hkv=8 D=128), one rocprofv3 pass of SQ\n"
-               "counters, averaged over each kernel's dispatches.\n\n"
-               "  cycles          shader clocks the kernel was active on one XCD (GRBM_GUI_ACTIVE / 8)\n"
-               "  MFMA busy       SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)\n"
-               "  LDS B/clk/CU    bytes read from LDS (SQ_INSTS_LDS_LOAD_BANDWIDTH x 64) / (cycles x 256 CUs)\n"
-               "  bank confl.     SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE\n"
-               "  LDS fifo full   SQ_LDS_DATA_FIFO_FULL / SQ_BUSY_CU_CYCLES\n"
-               "  wait LDS issue  wave-cycles waiting to issue an LDS instruction / wave-cycles of 4 waves per CU\n\n"
-               f"{COMMANDS}\n{sq_table(os.path.join(out, 'sq'))}\n")
-        with open(os.path.join(pdir, "sq_mfma_lds_d512_B2_S4096.txt"), "w") as fh:
-            fh.write(txt)
+        if os.path.isdir(os.path.join(d, "fetch")) and os.path.isdir(os.path.join(d, "write")):
+            recs = traffic_records(d, out)
+            txt = (f"HBM traffic per dispatch on one MI355X: {what}.\n\n"
+                   "rocprofv3 counters FETCH_SIZE and WRITE_SIZE (one pass each, averaged over the dispatches of each\n"
+                   "kernel), scaled by what the same counters read for a plain 1 GiB device copy (bytes per counter\n"
+                   "unit: fetch_scale, write_scale).  FETCH_SIZE counts every L2 miss sent to the fabric, part of\n"
+                   "which the 256 MB last-level cache serves.\n\n")
+            for r in recs:
+                kv = dict(t.split("=", 1) for t in r[len("record:"):].split())
+                txt += (f"  {kv['kernel']:42s} fetched {int(kv['fetch_bytes']) / 1e9:8.4f} GB   written "
+                        f"{int(kv['write_bytes']) / 1e9:8.4f} GB\n")
+            txt += (f"\n{cmds}\nbench.py reads the record lines below for its roofline \"traffic\" fields, as long as\n"
+                    "each kernel's source still has the recorded sha256.\n\n" + "\n".join(recs) + "\n")
+            with open(os.path.join(pdir, f"{wl}_traffic.txt"), "w") as fh:
+                fh.write(txt)
+        if os.path.isdir(os.path.join(d, "sq")):
+            txt = (f"Matrix-core and LDS use on one MI355X: {what}; one rocprofv3 pass of SQ counters,\n"
+                   "averaged over each kernel's dispatches.\n\n"
+                   "  cycles          shader clocks the kernel was active on one XCD (GRBM_GUI_ACTIVE / 8)\n"
+                   "  MFMA busy       SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)\n"
+                   "  LDS B/clk/CU    bytes read from LDS (SQ_INSTS_LDS_LOAD_BANDWIDTH x 64) / (cycles x 256 CUs)\n"
+                   "  bank confl.     SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE\n"
+                   "  LDS fifo full   SQ_LDS_DATA_FIFO_FULL / SQ_BUSY_CU_CYCLES\n"
+                   "  wait LDS issue  wave-cycles waiting to issue an LDS instruction / wave-cycles of 4 waves per CU\n\n"
+                   f"{cmds}\n{sq_table(os.path.join(d, 'sq'))}\n")
+            with open(os.path.join(pdir, f"{wl}_sq.txt"), "w") as fh:
+                fh.write(txt)
 
 
 def run_copy(mib: int, reps: int) -> None:

@@ -170,6 +170,45 @@ def test_packed_cu_seqlens_matches_oracle_and_pad_mask():
         assert np.array_equal(host_bits(t_pk), pack_rows(host_bits(t_pad), lengths))
 
 
+PACKED_MANY = [
+    # name, lengths, causal, window: empty, single-token and tile-edge documents; the dS blocks of
+    # each document sit in a region sized by its own length (prefix sums on the device)
+    ("causal", [0, 1, 127, 128, 129, 300, 5, 0, 256, 77, 640, 31], True, 0),
+    ("window", [129, 0, 700, 1, 64, 255], True, 100),
+    ("noncausal", [40, 300, 0, 129, 2], False, 0),
+]
+
+
+@pytest.mark.parametrize("name,lengths,causal,window", PACKED_MANY, ids=[c[0] for c in PACKED_MANY])
+def test_many_packed_sequences_match_oracle_and_padded_layout(name, lengths, causal, window):
+    lengths = np.array(lengths, dtype=np.int32)
+    S = int(lengths.max())
+    D = 256 if window else 512
+    w = AttnWorkload(126, f"many packed {name}", len(lengths), S, 8, 2, D, causal=causal, window=window)
+    say(f"[packed {name}] lengths {lengths.tolist()}")
+    inp = make_attention_inputs(w, seed=12)
+    cu = lengths_to_cu_seqlens(lengths)
+    pk = {x: pack_rows(inp[x], lengths) for x in ("q", "k", "v", "do")}
+    q, k, v, do = (dev(pk[x]) for x in ("q", "k", "v", "do"))
+    kw = dict(scale=w.scale, causal=causal, window=window, cu_seqlens=torch.from_numpy(cu).to("cuda:0"),
+              max_seqlen=S)
+    o, lse = sdpt.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = sdpt.attn_bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    f = {x: bf16_bits_to_f64(pk[x]) for x in pk}
+    ro, rl = oracle.attention_forward_packed(f["q"], f["k"], f["v"], cu, w.scale, causal, window)
+    rq, rk, rv = oracle.attention_backward_packed(f["q"], f["k"], f["v"], f["do"], cu, w.scale, causal, window)
+    assert all_finite(o, lse, dq, dk, dv)
+    assert max_abs(host(o), ro) <= O_MAX_ABS
+    assert max_abs(host(lse), rl) <= LSE_MAX_ABS
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        assert rel_l2(host(a), r) <= GRAD_REL_L2
+    inp["pad_mask"] = lengths_to_pad_mask(lengths, S)
+    got = run_gpu(w.scaled(varlen="pad_mask"), inp, varlen="pad_mask")
+    for t_pk, t_pad in ((o, got["o"]), (dq, got["dq"]), (dk, got["dk"]), (dv, got["dv"])):
+        assert np.array_equal(host_bits(t_pk), pack_rows(host_bits(t_pad), lengths))
+
+
 def test_packed_documents_are_document_causal():
     """Several documents packed into each row of a batch (the packing that the first page's CP
     path routes to varlen chunks, section Integration): flattening the rows and giving every

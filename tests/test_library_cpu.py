@@ -49,9 +49,32 @@ def test_workspace_sizes():
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0, 0, 0) == delta + 64 * (32 * 128) * blk
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0, 1, 1024) == delta + 64 * (32 * 41) * blk
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0, 0, 1024) == 0     # window needs causal
+    # packed rows: metadata, one int64 dS offset per sequence, delta, and dS regions sized by each
+    # sequence's own length, bounded from the row count: with n_b = ceil(len_b / 128) query tiles,
+    # sum n_b <= min(B nqt, total // 128 + B) =: N, and 2 N (nqt + 1) triangular blocks per head
     p = AttnShape(3, 100, 250, 8, 2, 256)
-    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 2, 1, 0) == (256 + ((250 * 8 * 4 + 255) // 256) * 256
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 2, 1, 0) == (256 + 256 + ((250 * 8 * 4 + 255) // 256) * 256
                                                                        + 3 * 8 * 4 * blk)
+    # 64 documents of at most 8192 tokens packed into 65536 rows (32 query heads): N = 512 + 64
+    # tiles, against 64 x 64 if every document were given the longest one's triangle
+    pk = AttnShape(64, 8192, 65536, 32, 4, 512)
+    N = 65536 // 128 + 64
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(pk), 2, 1, 0) == (
+        256 * 3 + 512 + 65536 * 32 * 4 + 32 * 2 * N * 65 * blk)
+    # a padded mask: the lengths are only known on the device, so every row gets the longest
+    # triangle; for 64 rows of 8192 that is 139.7 GB, past the cap below
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(pk), 1, 1, 0) == 0
+    pm = AttnShape(16, 8192, 0, 32, 4, 512)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(pm), 1, 1, 0) == (
+        256 + 16 * 8192 * 32 * 4 + 16 * 32 * 2 * 64 * 65 * blk)
+    # past 128 GiB (one dense 65536-token sequence, 32 heads: 137.7 GB of dS) the whole-sequence
+    # backward is refused; chunk pairs bound the workspace instead
+    long = AttnShape(1, 65536, 0, 32, 4, 512)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(long), 0, 1, 0) == 0
+    st = lib.attn_bwd(ctypes.byref(long), _t(), _t(), _t(), _t(), 0x20000, _t(), 0.05, 1, 0, 0.0, None, None,
+                      _t(), _t(), _t(), 0x100000, 1 << 40, None)
+    assert st == UNSUPPORTED
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(AttnShape(1, 49152, 0, 32, 4, 512)), 0, 1, 0) > 0
     bad = AttnShape(1, 10, 0, 6, 4, 512)      # 6 % 4 != 0
     assert lib.attn_fwd_workspace_bytes(ctypes.byref(bad), 0) == 0
     d = AttnDecodeShape(64, 32, 8, 128, 16, 1000, 256)

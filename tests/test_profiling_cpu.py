@@ -51,15 +51,16 @@ def test_committed_records_parse():
 def test_sq_table_derives_busy_fraction_and_lds_rate(tmp_path, monkeypatch):
     """One kernel active 1000 clocks on each of the 8 XCDs (GRBM_GUI_ACTIVE summed to 8000): MFMA
     busy 512000 SIMD-cycles of 1024 SIMDs is 50%; 4000 64-byte LDS units over 256 CUs x 1000 clocks
-    is 1 byte per clock per CU; conflicts 10 of 200 active LDS cycles is 5%."""
-    monkeypatch.setattr(profiling, "SQ_KERNELS", (("k", "k<1>"),))
+    is 1 byte per clock per CU; conflicts 10 of 200 active LDS cycles is 5%.  Kernels that are not
+    the library's (here "other") are left out."""
     vals = {"GRBM_GUI_ACTIVE": 8000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 512000.0, "SQ_INSTS_LDS_LOAD_BANDWIDTH": 4000.0,
             "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 200.0, "SQ_LDS_DATA_FIFO_FULL": 0.0,
             "SQ_BUSY_CU_CYCLES": 256000.0, "SQ_WAIT_INST_LDS": 2560.0, "SQ_LDS_ADDR_CONFLICT": 0.0}
-    rows = [("void k<1>(A)", c, v) for c, v in vals.items()] + [("void other(A)", c, 1.0) for c in vals]
+    rows = [("void attn::fwd_kernel<1, 2>(A)", c, v) for c, v in vals.items()] + [("void other(A)", c, 1.0)
+                                                                                  for c in vals]
     _counter_csv(tmp_path / "sq", rows)
     table = profiling.sq_table(str(tmp_path / "sq")).splitlines()
     assert len(table) == 2
     f = table[1].split()
-    assert f[0] == "k" and f[1] == "1000" and f[2] == "50.0%" and f[3] == "1.0" and f[4] == "5.00%"
+    assert f[0] == "fwd_kernel<1,2>" and f[1] == "1000" and f[2] == "50.0%" and f[3] == "1.0" and f[4] == "5.00%"
     assert f[5] == "0.00%" and f[6] == "1.0%"   # 4 x 2560 wave-cycles of 4 x 1000 x 256

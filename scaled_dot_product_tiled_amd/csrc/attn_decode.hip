@@ -199,9 +199,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(t[pg][i] - m);
-        l += p;
-        pb[4 * pg + i] = E16<F16>::from_float(p);
+        // the normaliser sums the rounded probabilities that multiply V
+        pb[4 * pg + i] = E16<F16>::from_float(fast_exp2(t[pg][i] - m));
+        l += E16<F16>::to_float(pb[4 * pg + i]);
       }
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {

@@ -94,3 +94,40 @@ def test_decode_softcap_matches_oracle(cap):
                             w.page_size, cap)
     assert all_finite(o)
     assert max_abs(host(o), r) <= O_MAX_ABS
+
+
+def test_one_workspace_serves_calls_of_different_sizes():
+    """One workspace sized for the largest call serves smaller and larger calls in any order: each
+    result equals the one a fresh workspace gives, bit for bit."""
+    import ctypes
+    from scaled_dot_product_tiled_amd.binding import AttnDecodeShape
+    big = DECODE_WORKLOADS["decode_d128"].scaled(B=12, ctx_range=(1, 2000))
+    small = DECODE_WORKLOADS["decode_d128"].scaled(B=5, ctx_range=(600, 1500))
+    shape = AttnDecodeShape(big.B, big.Hq, big.Hkv, big.D, big.page_size, 1, big.max_pages_per_seq, 0)
+    ws = torch.full((sdpt.load_library().paged_decode_workspace_bytes(ctypes.byref(shape)),), 0x5A,
+                    device="cuda:0", dtype=torch.uint8)
+    for w, seed in ((big, 3), (small, 4), (big, 5)):
+        inp = make_decode_inputs(w, seed=seed)
+        q, kc, vc = dev(inp["q"]), dev(inp["k_cache"]), dev(inp["v_cache"])
+        table = torch.from_numpy(inp["block_table"]).to("cuda:0")
+        ctx = torch.from_numpy(inp["ctx_lens"]).to("cuda:0")
+        fresh = sdpt.paged_decode(q, kc, vc, table, ctx, scale=w.scale)
+        reused = sdpt.paged_decode(q, kc, vc, table, ctx, scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(reused), host_bits(fresh))
+        assert max_abs(host(reused), ref(inp, w.scale)) <= O_MAX_ABS
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (8, 2), (24, 6)])
+def test_chunks_merged_across_xcds(Hq, Hkv):
+    """Long contexts (up to 16 chunks of 512 tokens) with kv-head counts that spread a sequence's
+    chunks over different XCDs, merged in chunk order: repeated calls give the same bytes and every
+    result is within the oracle's tolerance."""
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=24, Hq=Hq, Hkv=Hkv, ctx_range=(1, 8192))
+    inp = make_decode_inputs(w, seed=9)
+    print(f"[decode xcd] Hq={Hq} Hkv={Hkv} ctx {inp['ctx_lens'].tolist()}", flush=True)
+    first = run(inp, w.scale)
+    assert all_finite(first)
+    assert max_abs(host(first), ref(inp, w.scale)) <= O_MAX_ABS
+    for _ in range(3):
+        assert np.array_equal(host_bits(run(inp, w.scale)), host_bits(first))

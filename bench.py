@@ -17,8 +17,10 @@ the C ABI.  Reported:
   other_workloads  (median and best of per-call HIP-event timings) forward / backward TFLOP/s of the
             tiny (B=1 S=128 D=512), sliding-window (D=256, W=1024) and padded varlen (B=8, lengths
             U{512..8192}, D=512) workloads, of one context-parallel rank's chunk pairs (16k tokens in
-            8 chunks, D=512), of the step's workload in IEEE half and with a softcap, and a paged
-            prefill; not part of the timed step;
+            8 chunks, D=512), of the step's workload in IEEE half and with a softcap, and of two
+            paged forwards (attn_fwd_paged): a 2048-token prompt chunk after 6144 cached tokens (beside
+            the gather + chunk-pair path it replaces) and a serving step mixing a 1024-token chunk
+            with 31 decode rows; not part of the timed step;
   measured_peaks  what plain kernels reach on this device (attn_peak_probe): independent bf16
             32x32x16 matrix instructions, a streaming read and a streaming copy;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores, and
@@ -26,8 +28,9 @@ the C ABI.  Reported:
 Prints one JSON line.
 
     python bench.py --workload NAME   (NAME: tiny_d512, full_d512, window_d256, varlen_d512,
-                                        decode_d128) runs only that workload's forward + backward
-                                        (or decode) steps and prints its per-kernel times; the
+                                        decode_d128, paged_prefill_d512, mixed_step_d512) runs only
+                                        that workload's forward + backward (or decode, or paged
+                                        forward) steps and prints its per-kernel times; the
                                         rocprofv3 summaries in profiles/ are taken from such runs.
 """
 import argparse
@@ -273,50 +276,91 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     return res
 
 
-def paged_prefill_workload(steps, stream, B=1, prev=6144, n=2048, Hq=32, Hkv=4, D=512):
-    """A 2048-token chunk of new queries after 6144 cached tokens (D=512, GQA 32/4, 16-token pages
-    permuted over the pool): append the chunk's K/V to the pages, gather the 8192 tokens, run the
-    chunk-pair forward at q_pos0 = 6144.  TFLOP/s of the attention (causal-counted pairs) over the
-    time of the three calls."""
+def prefill_workload(name, steps, stream):
+    """A PREFILL_WORKLOADS step: each sequence's new query rows against its paged cache (16-token
+    pages permuted over a pool 1.5x the pages used), K/V read through the table inside
+    attn_fwd_paged.  Times the attention call alone and with the step's paged_kv_append of the new
+    tokens' K/V; for a single sequence also the gathered path it replaces (append, paged_kv_gather
+    of the whole context, attn_fwd_chunk).  TFLOP/s count the causal-visible (query, key) pairs.
+    Values are drawn on the device (torch's generator, seeded) to keep set-up short."""
     import torch
     import scaled_dot_product_tiled_amd as sdpt
+    from synth import PREFILL_WORKLOADS
+    w = PREFILL_WORKLOADS[name]
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(99)
-    L = prev + n
-    pages = -(-L // 16)
-    pool = int(1.5 * pages)
-    kc = torch.randn((pool, 16, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
-    vc = torch.randn((pool, 16, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
-    perm = torch.randperm(pool, generator=gen, device="cuda:0")[:pages].to(torch.int32)
-    table = perm.reshape(1, pages).repeat(B, 1).contiguous()
-    ctx = torch.full((B,), L, device="cuda:0", dtype=torch.int32)
-    q = torch.randn((B, n, Hq, D), generator=gen, device="cuda:0").to(torch.bfloat16)
-    kn = torch.randn((B, n, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
-    vn = torch.randn((B, n, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
-    kg = torch.empty((B, L, Hkv, D), device="cuda:0", dtype=torch.bfloat16)
-    vg = torch.empty_like(kg)
+    ctx = [int(c) for c in w.ctx]
+    new = [int(n) for n in w.new]
+    npages = [-(-c // 16) for c in ctx]
+    pool = int(1.5 * sum(npages))
+    maxp = max(npages)
+
+    def randn(shape):
+        return torch.randn(shape, generator=gen, device="cuda:0").to(torch.bfloat16)
+    kc, vc = randn((pool, 16, w.Hkv, w.D)), randn((pool, 16, w.Hkv, w.D))
+    perm = torch.randperm(pool, generator=gen, device="cuda:0").to(torch.int32)
+    table = torch.full((w.B, maxp), -1, dtype=torch.int32, device="cuda:0")
+    off = 0
+    for b in range(w.B):
+        table[b, :npages[b]] = perm[off:off + npages[b]]
+        off += npages[b]
+    ctx_d = torch.tensor(ctx, dtype=torch.int32, device="cuda:0")
+    cu = torch.tensor([0] + list(np.cumsum(new)), dtype=torch.int32, device="cuda:0")
+    T, maxq = sum(new), max(new)
+    q = randn((T, w.Hq, w.D))
+    # the step's append: each sequence's new tokens, one paged_kv_append per distinct count
+    groups = []
+    for n in sorted(set(new)):
+        idx = torch.tensor([b for b in range(w.B) if new[b] == n], device="cuda:0")
+        groups.append((table[idx].contiguous(), ctx_d[idx].contiguous(), randn((len(idx), n, w.Hkv, w.D)),
+                       randn((len(idx), n, w.Hkv, w.D))))
     o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, n), device="cuda:0", dtype=torch.float32)
-    scale = 1.0 / math.sqrt(D)
+    lse = torch.empty((w.Hq, T), device="cuda:0", dtype=torch.float32)
 
-    def run():
-        sdpt.paged_kv_append(kn, vn, kc, vc, table, ctx)
-        sdpt.paged_kv_gather(kc, vc, table, ctx, L, k_out=kg, v_out=vg)
-        sdpt.attn_fwd_chunk(q, kg, vg, prev, 0, scale=scale, out=o, lse=lse)
+    def attn():
+        sdpt.attn_fwd_paged(q, kc, vc, table, cu, ctx_d, maxq, scale=w.scale, out=o, lse=lse)
 
-    run()
+    def append():
+        for tg, cg, kn, vn in groups:
+            sdpt.paged_kv_append(kn, vn, kc, vc, tg, cg)
+
+    def step():
+        append()
+        attn()
+
+    for f in (attn, step):
+        f()
     torch.cuda.synchronize()
-    ms = time_calls(run, steps, stream)["median"]
-    sdpt.binding.profile(True)
-    for _ in range(steps):
-        run()
-    sdpt.binding.profile(False)
-    kern = {k: {"launches": c, "ms_avg": round(t / c, 4)} for k, (c, t) in sdpt.binding.profile_read().items()}
-    pairs = (n * prev + n * (n + 1) // 2) * Hq * B
-    ff = 4.0 * D * pairs
-    return {"workload": f"paged prefill d{D}: {n} new tokens after {prev} cached (Hq{Hq} Hkv{Hkv}, 16-token pages)",
-            "pairs": pairs, "ms": round(ms, 4), "tflops": round(ff / ms / 1e9, 2),
-            "frac": round(ff / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "kernels": kern}
+    ta = time_calls(attn, steps, stream)
+    tst = time_calls(step, steps, stream)
+    kern = kernel_times(step, steps)
+    pairs = sum(n * (c - n) + n * (n + 1) // 2 for c, n in zip(ctx, new)) * w.Hq
+    ff = 4.0 * w.D * pairs
+    res = {"workload": w.name, "pairs": pairs, "ms": round(ta["median"], 4), "ms_best": round(ta["best"], 4),
+           "tflops": round(ff / ta["median"] / 1e9, 2), "frac": round(ff / ta["median"] / 1e9 / PEAK_BF16_TFLOPS, 4),
+           "step_ms_with_append": round(tst["median"], 4),
+           "step_tflops_with_append": round(ff / tst["median"] / 1e9, 2), "kernels": kern}
+    if w.B == 1:
+        L, n = ctx[0], new[0]
+        kg = torch.empty((1, L, w.Hkv, w.D), device="cuda:0", dtype=torch.bfloat16)
+        vg = torch.empty_like(kg)
+        q4 = q.view(1, n, w.Hq, w.D)
+        o4 = torch.empty_like(q4)
+        l4 = torch.empty((1, w.Hq, n), device="cuda:0", dtype=torch.float32)
+
+        def gathered():
+            append()
+            sdpt.paged_kv_gather(kc, vc, table, ctx_d, L, k_out=kg, v_out=vg)
+            sdpt.attn_fwd_chunk(q4, kg, vg, L - n, 0, scale=w.scale, out=o4, lse=l4, out_dtype=torch.bfloat16)
+
+        gathered()
+        torch.cuda.synchronize()
+        tg = time_calls(gathered, steps, stream)
+        res["gathered_path"] = {"ms": round(tg["median"], 4), "tflops": round(ff / tg["median"] / 1e9, 2),
+                                "kernels": kernel_times(gathered, steps)}
+        del kg, vg, o4, l4
+    del kc, vc, q, groups, o
+    return res
 
 
 def parse():
@@ -329,7 +373,8 @@ def parse():
     p.add_argument("--cpu-units", type=int, default=8, help="(batch, kv head) units the oracle times (of 8)")
     p.add_argument("--no-other", action="store_true", help="skip the other workloads")
     p.add_argument("--workload", default=None,
-                   help="profile one workload only: tiny_d512, full_d512, window_d256, varlen_d512, decode_d128")
+                   help="profile one workload only: tiny_d512, full_d512, window_d256, varlen_d512, decode_d128, "
+                        "paged_prefill_d512, mixed_step_d512")
     return p.parse_args()
 
 
@@ -465,7 +510,9 @@ def profile_workload(args):
     import torch
     import scaled_dot_product_tiled_amd as sdpt
     stream = torch.cuda.current_stream()
-    if args.workload == "decode_d128":
+    if args.workload in ("paged_prefill_d512", "mixed_step_d512"):
+        res = prefill_workload(args.workload, args.steps, stream)
+    elif args.workload == "decode_d128":
         dw, pools = decode_setup()
         outs = [torch.empty_like(p["q"]) for p in pools]
         ws = torch.empty(1 << 25, device="cuda:0", dtype=torch.uint8)
@@ -628,7 +675,8 @@ def main():
         others["window_d256"] = other_workload("window_d256", 20, stream)
         others["full_d512_f16"] = other_workload("full_d512", 5, stream, dtype="f16")
         others["full_d512_softcap"] = other_workload("full_d512", 5, stream, softcap=30.0)
-        others["paged_prefill_d512"] = paged_prefill_workload(5, stream)
+        others["paged_prefill_d512"] = prefill_workload("paged_prefill_d512", 10, stream)
+        others["mixed_step_d512"] = prefill_workload("mixed_step_d512", 10, stream)
         others["varlen_d512"] = other_workload("varlen_d512", 5, stream)
 
     out = {

@@ -345,6 +345,55 @@ attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens,
                             const int32_t* block_table, const int32_t* ctx_lens,
                             attn_tensor k_out, attn_tensor v_out, void* stream);
 
+/* Sizes of one paged prefill call.
+ *   B                 sequences
+ *   max_q             most new query rows of one sequence
+ *   total_q           packed query rows, cu_q[B]
+ *   Hq, Hkv, D        heads and head_dim (256 or 512)
+ *   dtype             q, caches and o: ATTN_DTYPE_BF16 or ATTN_DTYPE_F16
+ *   page_size         tokens per cache page (16)
+ *   num_pages         pages in the cache pool
+ *   max_pages_per_seq columns of block_table */
+typedef struct {
+    int32_t B, max_q, total_q, Hq, Hkv, D, dtype;
+    int32_t page_size, num_pages, max_pages_per_seq;
+} attn_paged_shape;
+
+/*
+ * attn_fwd_paged: causal attention of each sequence's new query tokens against that sequence's
+ * whole paged K/V cache, the cache read through the block table inside the kernel (no gathered
+ * copy).  A sequence with one new token is a decode row, so one call serves a serving step that
+ * mixes prompt chunks and decode tokens: the interleaving of prefill and decode in one step that
+ * the page "flex_attention + paged KV + CUDA graphs vs vLLM" (section "What's left on the
+ * table", chunked prefill) names as the missing piece, over the paged cache and page table of
+ * its Architecture notes.
+ *   q            device 16-bit, packed (total_q, Hq, D): sequence b's new tokens are rows
+ *                cu_q[b] .. cu_q[b+1]-1 (attn_tensor stride_b is ignored)
+ *   k_cache,     device 16-bit (num_pages, page_size, Hkv, D), strides (page, slot, head) in
+ *   v_cache      elements; they already hold the new tokens' K and V (paged_kv_append).  A slot
+ *                stride of 2^26 elements or more returns ATTN_ERR_UNSUPPORTED.
+ *   block_table  device int32 (B, max_pages_per_seq) as for paged_decode; entries outside
+ *                [0, num_pages) are clamped, entries past a sequence's tokens are not read
+ *   cu_q         device int32 (B+1): query row offsets, non-decreasing, cu_q[B] = total_q;
+ *                n_b = cu_q[b+1] - cu_q[b] is clamped to [0, max_q]
+ *   ctx_lens     device int32 (B): tokens in sequence b's cache, the n_b new ones included,
+ *                clamped to [0, max_pages_per_seq * page_size].  Query row i of sequence b sits
+ *                at position ctx_lens[b] - n_b + i and sees key t when t <= that position and,
+ *                with window > 0, t > position - window.  A row at a negative position
+ *                (ctx_lens[b] < n_b) sees no key.
+ *   scale, softcap  as for attn_fwd; window 0 (none) or > 0
+ *   o            device 16-bit, packed (total_q, Hq, D), written
+ *   lse          device fp32 (Hq, total_q) contiguous, written
+ * No workspace: one kernel launch, which reads cu_q, ctx_lens and the table itself.  Rows with no visible key get O = 0 and LSE = 0, as in attn_fwd.  Every other row's O and
+ * LSE equal those of attn_fwd_chunk over the sequence's cached keys 0 .. ctx_lens[b]-1 laid out
+ * densely, with q_pos0 = ctx_lens[b] - n_b and k_pos0 = 0.
+ */
+attn_status attn_fwd_paged(const attn_paged_shape* shape,
+                           attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                           const int32_t* block_table, const int32_t* cu_q, const int32_t* ctx_lens,
+                           float scale, int window, float softcap,
+                           attn_tensor o, float* lse, void* stream);
+
 /* Workspace sizes in bytes.  varlen: 0 dense, 1 pad_mask, 2 cu_seqlens; causal and
  * window as in the call.  Return 0 for arguments that the matching call would reject.
  * Each call computes its own requirement and the caller owns the memory, so one

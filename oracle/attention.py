@@ -28,6 +28,11 @@ Readings adopted where the pages are silent (each is listed in the design notes)
 * LSE is the natural-log log-sum-exp of the scaled scores of the visible keys;
 * the paged decode query sits at position ctx_b - 1 and sees every cached
   token t < ctx_b (fourth page, Architecture notes: PagedKVCache + PageTable);
+* a paged prefill step (fourth page, "What's left on the table": prefill and decode
+  rows in one step) gives sequence b n_b new query rows, the newest of its ctx_b
+  cached tokens: row i sits at position ctx_b - n_b + i and sees the cached tokens
+  at or before it (and inside the window); a row at a negative position sees none
+  and returns O = 0, LSE = 0;
 * a chunk pair of the ring path (first page, Integration) places query i at position
   q_pos0 + i and key j at k_pos0 + j; a row that sees no key of the chunk has LSE = -inf
   (the identity of the log-sum-exp merge) and O = 0;
@@ -46,6 +51,7 @@ __all__ = [
     "attention_forward_packed", "attention_backward_packed",
     "gather_pages", "paged_append", "paged_decode", "paged_decode_one", "attention_rows",
     "chunk_visibility", "attention_forward_chunk", "attention_backward_chunk", "lse_merge",
+    "paged_prefill",
 ]
 
 
@@ -453,6 +459,29 @@ def paged_decode_one(q, k_cache, v_cache, block_table, ctx_lens, scale, b, page_
         o, _, _ = unit_forward(q[b, h][None, :], kk[:, h // r], vv[:, h // r], scale, vis, softcap)
         out[h] = o[0]
     return out
+
+
+def paged_prefill(q, k_cache, v_cache, block_table, cu_q, ctx_lens, scale, window=0, page_size=16, softcap=0.0):
+    """New query rows of several sequences against their paged caches, causal.  q (T, Hq, D) holds
+    sequence b's n_b = cu_q[b+1] - cu_q[b] rows from cu_q[b] on; they are the newest of the ctx_b
+    tokens in its cache, at positions ctx_b - n_b .. ctx_b - 1.  The sequence's tokens are read
+    through its page-table row (gather_pages) and its rows computed as a chunk pair with the
+    queries from q_pos0 = ctx_b - n_b and the keys from k_pos0 = 0.  Returns O (T, Hq, D) and
+    LSE (Hq, T); a row that sees no token has O = 0 and LSE = 0."""
+    T, Hq, D = q.shape
+    o = np.zeros((T, Hq, D))
+    lse = np.zeros((Hq, T))
+    for b in range(len(cu_q) - 1):
+        lo, hi = int(cu_q[b]), int(cu_q[b + 1])
+        ctx = int(ctx_lens[b])
+        if hi == lo or ctx == 0:
+            continue
+        kk = gather_pages(k_cache, block_table[b], ctx, page_size)[None]
+        vv = gather_pages(v_cache, block_table[b], ctx, page_size)[None]
+        ob, lb = attention_forward_chunk(q[None, lo:hi], kk, vv, scale, True, window, ctx - (hi - lo), 0, softcap)
+        o[lo:hi] = ob[0]
+        lse[:, lo:hi] = np.where(np.isfinite(lb[0]), lb[0], 0.0)
+    return o, lse
 
 
 def paged_decode(q, k_cache, v_cache, block_table, ctx_lens, scale, page_size=16, softcap=0.0):

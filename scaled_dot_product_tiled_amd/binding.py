@@ -49,6 +49,12 @@ class AttnDecodeShape(ctypes.Structure):
                 ("max_pages_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class AttnPagedShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("max_q", ctypes.c_int32), ("total_q", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32)]
+
+
 _lib = None
 
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse_merge", "attn_fwd_chunk_merge",
@@ -56,7 +62,7 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read", "attn_count_restarts", "paged_decode_noalloc",
-           "paged_decode_noalloc_max_bytes", "attn_peak_probe")
+           "paged_decode_noalloc_max_bytes", "attn_peak_probe", "attn_fwd_paged")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -110,6 +116,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_kv_gather.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, vp, vp, AttnTensor,
                                     AttnTensor, vp]
     lib.paged_kv_gather.restype = ctypes.c_int
+    lib.attn_fwd_paged.argtypes = [P(AttnPagedShape), AttnTensor, AttnTensor, AttnTensor, vp, vp, vp, ctypes.c_float,
+                                   ctypes.c_int, ctypes.c_float, AttnTensor, vp, vp]
+    lib.attn_fwd_paged.restype = ctypes.c_int
     lib.attn_debug.argtypes = [ctypes.c_int]
     lib.attn_debug.restype = ctypes.c_int
     lib.attn_fwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
@@ -577,6 +586,45 @@ def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: t
                              _tensor(v_out, False), _stream())
     _check(st, "paged_kv_gather")
     return k_out, v_out
+
+
+def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   cu_q: torch.Tensor, ctx_lens: torch.Tensor, max_q: int, scale: Optional[float] = None,
+                   window: int = 0, softcap: float = 0.0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O (T,Hq,D), LSE (Hq,T) of each sequence's new query rows q (T,Hq,D), packed by cu_q (B+1), against
+    its paged cache (num_pages, page_size, Hkv, D) read through block_table (B, max_pages_per_seq);
+    ctx_lens (B) counts the cached tokens, the new ones included (causal; see attn_fwd_paged)."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _half(t, n, q.dtype)
+    for t, n in ((block_table, "block_table"), (cu_q, "cu_q"), (ctx_lens, "ctx_lens")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 device tensor")
+    T, Hq, D = q.shape
+    B = cu_q.numel() - 1
+    num_pages, page_size, Hkv, Dc = k_cache.shape
+    if Dc != D:
+        raise ValueError("k_cache head_dim differs from q's")
+    _expect(v_cache, tuple(k_cache.shape), "v_cache")
+    _expect(ctx_lens, (B,), "ctx_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be (B, max_pages_per_seq), got {tuple(block_table.shape)}")
+    shape = AttnPagedShape(B, int(max_q), T, Hq, Hkv, D, _DT16[q.dtype], page_size, num_pages, block_table.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, T), device=q.device, dtype=torch.float32) if lse is None else lse
+    _half(out, "out", q.dtype)
+    _expect(out, (T, Hq, D), "out")
+    _expect(lse, (Hq, T), "lse")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    st = lib.attn_fwd_paged(ctypes.byref(shape), _tensor(q, True), _tensor(k_cache, False), _tensor(v_cache, False),
+                            block_table.data_ptr(), cu_q.data_ptr(), ctx_lens.data_ptr(), float(scale), int(window),
+                            float(softcap), _tensor(out, True), lse.data_ptr(), _stream())
+    _check(st, "attn_fwd_paged")
+    return out, lse
 
 
 def debug(on: bool) -> bool:

@@ -68,8 +68,14 @@ attn_status check_shape(const attn_shape* s, int varlen) {
 size_t meta_bytes(int B, int varlen) { return varlen ? round_up(3 * sizeof(int32_t) * (size_t)B) : 0; }
 
 // Workgroups per XCD for `total` items of W per unit: with a batch order (see xcd_item) each
-// XCD takes whole units, ceil(units / 8) of them.
-int per_xcd_for(const attn::AttnArgs& a, int total, int W) {
+// XCD takes whole units, ceil(units / 8) of them.  Fewer than 8 units would leave XCDs idle
+// either that way or dealt by units, so they take the dense mapping instead: each XCD a
+// contiguous run of items, a unit split over neighbouring XCDs.
+int per_xcd_for(attn::AttnArgs& a, int total, int W) {
+  if (a.balanced && total / W < 8) {
+    a.order = nullptr;
+    a.balanced = 0;
+  }
   return a.order != nullptr ? ((total / W + 7) / 8) * W : (total + 7) / 8;
 }
 
@@ -437,13 +443,23 @@ attn_status varlen_meta(const Call& c, const int32_t* cu_seqlens, const uint8_t*
 // or merged into a running fp32 (O, LSE) with an optional 16-bit copy of the merged O.
 enum class FwdOut { half, f32, merge };
 
+// K and V of a paged forward: the caches' page strides and the table that places each
+// sequence's pages (the tensors' own pointers, slot and head strides are in Tensors).
+struct PagedKV {
+  const int32_t* table;
+  const int32_t* kv_len;
+  int64_t k_page, v_page;
+  int max_pages, num_pages;
+};
+
 attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, const int32_t* cu_seqlens,
                     const uint8_t* pad_mask, void* workspace, hipStream_t s, FwdOut mode = FwdOut::half,
-                    attn_tensor final16 = {}) {
+                    attn_tensor final16 = {}, const PagedKV* paged = nullptr) {
   int32_t* meta = static_cast<int32_t*>(workspace);
   attn_status st;
   if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
-  if ((st = varlen_meta(c, cu_seqlens, pad_mask, meta, s))) return st;
+  // the paged forward reads its query offsets (cu_seqlens) directly
+  if (paged == nullptr && (st = varlen_meta(c, cu_seqlens, pad_mask, meta, s))) return st;
   attn::AttnArgs a = {};
   fill_common(a, c, scale, meta);
   set_tensors(a, t, c.varlen == 2, false);
@@ -456,11 +472,26 @@ attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, co
     a.out = static_cast<__bf16*>(final16.ptr);
     set_tensor(final16, false, a.r_sb, a.r_ss, a.r_sh);
   }
+  if (paged != nullptr) {
+    a.seq_off = cu_seqlens;
+    a.seq_len = nullptr;
+    a.total = c.total;
+    // A sequence's cost grows with its cached keys, not its query rows, so its items are dealt
+    // round-robin over all units rather than in a batch order by length (see xcd_item).
+    a.order = nullptr;
+    a.paged = 1;
+    a.table = paged->table;
+    a.kv_len = paged->kv_len;
+    a.k_sb = paged->k_page;
+    a.v_sb = paged->v_page;
+    a.max_pages = paged->max_pages;
+    a.num_pages = paged->num_pages;
+  }
   a.lse = lse;
   a.restarts = g_restarts;
   plan_rows(a, attn::kFwdRows);
-  return launch(mode == FwdOut::merge ? "attn_fwd_merge" : "attn_fwd", s, a.total_items,
-                [&] { return attn::launch_fwd(a, c.D, s); });
+  return launch(paged ? "attn_fwd_paged" : mode == FwdOut::merge ? "attn_fwd_merge" : "attn_fwd", s,
+                a.total_items, [&] { return attn::launch_fwd(a, c.D, s); });
 }
 
 attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* lse, const int32_t* cu_seqlens,
@@ -859,6 +890,61 @@ attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens, at
                             attn_tensor k_out, attn_tensor v_out, void* stream) {
   return paged_copy(shape, n_tokens, k_out, v_out, k_cache, v_cache, block_table, ctx_lens, 1, "paged_kv_gather",
                     stream);
+}
+
+// Paged prefill: packed new query rows (cu_q) against each sequence's paged cache.
+static attn_status check_paged_shape(const attn_paged_shape* s) {
+  if (s == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (s->B < 0 || s->max_q < 0 || s->total_q < 0 || s->Hq <= 0 || s->Hkv <= 0 || s->num_pages <= 0 ||
+      s->max_pages_per_seq <= 0 || s->page_size <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (s->Hq % s->Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if ((s->D != 256 && s->D != 512) || s->page_size != 16 || !dtype16_ok(s->dtype)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)s->max_pages_per_seq * s->page_size > INT_MAX / 2 || (int64_t)s->total_q * s->Hq >= INT_MAX / 2 ||
+      s->max_q >= (1 << 28))
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_paged(const attn_paged_shape* shape, attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                           const int32_t* block_table, const int32_t* cu_q, const int32_t* ctx_lens, float scale,
+                           int window, float softcap, attn_tensor o, float* lse, void* stream) {
+  attn_status st = check_paged_shape(shape);
+  if (st != ATTN_OK) return st;
+  const attn_paged_shape& sh = *shape;
+  if (!(std::isfinite(scale) && scale > 0.f) || !softcap_ok(softcap) || window < 0) return ATTN_ERR_INVALID_ARG;
+  if (block_table == nullptr || cu_q == nullptr || ctx_lens == nullptr) return ATTN_ERR_INVALID_ARG;
+  if ((st = check_tensor(q, true)) || (st = check_tensor(o, true)) || (st = check_tensor(k_cache, false)) ||
+      (st = check_tensor(v_cache, false)))
+    return st;
+  if (!lse_ok(lse)) return ATTN_ERR_INVALID_ARG;
+  // offsets inside one page are 32-bit byte offsets
+  if (k_cache.stride_s > (INT_MAX / 2) / 16 || v_cache.stride_s > (INT_MAX / 2) / 16) return ATTN_ERR_UNSUPPORTED;
+  if (sh.B == 0 || sh.max_q == 0 || sh.total_q == 0) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const attn_decode_shape pages = {sh.B, sh.Hq, sh.Hkv, sh.D, sh.page_size, sh.num_pages, sh.max_pages_per_seq,
+                                   sh.dtype};
+  if ((st = debug_check_pages(pages, block_table, ctx_lens, s))) return st;
+
+  Call c = {};
+  c.B = sh.B;
+  c.S = sh.max_q;
+  c.Sk = sh.max_pages_per_seq * sh.page_size;
+  c.total = sh.total_q;
+  c.Hq = sh.Hq;
+  c.Hkv = sh.Hkv;
+  c.D = sh.D;
+  c.varlen = 2;
+  c.f16 = sh.dtype == ATTN_DTYPE_F16;
+  c.causal = 1;
+  // a query's position is below Sk, so a window of Sk or more never binds; a smaller one keeps
+  // every position difference inside 32 bits
+  c.window = window >= c.Sk ? 0 : window;
+  c.shift = 0;
+  c.softcap = softcap;
+  const Tensors t = {q, k_cache, v_cache, o, {}, {}, {}, {}};
+  const PagedKV pg = {block_table, ctx_lens, k_cache.stride_b, v_cache.stride_b, sh.max_pages_per_seq, sh.num_pages};
+  return run_fwd(c, t, scale, lse, cu_q, nullptr, nullptr, s, FwdOut::half, {}, &pg);
 }
 
 int attn_debug(int on) {

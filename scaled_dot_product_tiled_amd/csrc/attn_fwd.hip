@@ -50,7 +50,8 @@ constexpr float kRefSlackF16 = 15.0f;
 // MERGE: instead of storing the row's O and LSE, merge them into a running result (fp32 O
 // in out_f32, LSE in lse) by log-sum-exp weighting and optionally round the merged O to the
 // 16-bit out: the chunk-pair forward and the merge of its partial in one pass.
-template <int D, int N, bool EXACT, bool SOFTCAP, bool F16, bool MERGE>
+// PAGED: K and V come from a paged cache through the page table (see AttnArgs::paged).
+template <int D, int N, bool EXACT, bool SOFTCAP, bool F16, bool MERGE, bool PAGED>
 __device__ __forceinline__ void fwd_body(AttnArgs a) {
   constexpr int NKB = N / 32;  // 32-key blocks per tile
   constexpr int NS = N / 16;   // 16-key steps per tile
@@ -64,15 +65,32 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
   const int item = xcd_item(a.per_xcd, a.total_items, a.nqt, a.balanced, a.order, a.Hkv * a.nhb);
   if (item < 0) return;
   const int unit = item / a.nqt;
-  const int qt = a.nqt - 1 - (item - unit * a.nqt);  // longest causal rows first
+  int qt = a.nqt - 1 - (item - unit * a.nqt);  // longest causal rows first
   const int hb = unit % a.nhb;
   const int g = (unit / a.nhb) % a.Hkv;
   const int b = unit / (a.nhb * a.Hkv);
-  int len = a.seq_len ? a.seq_len[b] : a.S;
+  int len, off;
+  if constexpr (PAGED) {
+    // query rows straight from the offsets: sequence b owns rows cu[b] .. cu[b+1]-1, clamped into
+    // the packed rows (cu is a.seq_off, B + 1 entries)
+    off = min(max(a.seq_off[b], 0), a.total);
+    len = min(max(a.seq_off[b + 1] - off, 0), a.total - off);
+  } else {
+    len = a.seq_len ? a.seq_len[b] : a.S;
+    off = a.seq_off ? a.seq_off[b] : 0;
+  }
   len = min(max(len, 0), a.S);
-  const int lenk = a.seq_len ? len : a.Sk;  // key rows
-  const int dlt = a.q_shift;
-  const int off = a.seq_off ? a.seq_off[b] : 0;
+  if constexpr (PAGED) {
+    // The unit's r-th item takes the r-th tile counted back from the sequence's last row, so
+    // that every sequence's heaviest tile (its newest queries see the most keys) comes in the
+    // first round of the deal, decode rows included; items past the sequence's rows exit.
+    qt = (len + a.mpos - 1) / a.mpos - 1 - (a.nqt - 1 - qt);
+    if (qt < 0) return;
+  }
+  // key rows; a paged sequence's are its cached keys, clamped to its table row, and its
+  // queries are the newest of them
+  const int lenk = PAGED ? min(max(a.kv_len[b], 0), a.max_pages * 16) : a.seq_len ? len : a.Sk;
+  const int dlt = PAGED ? lenk - len : a.q_shift;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -102,8 +120,11 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
   const int t_lo = jlo / N;
   const int t_hi = jhi > jlo ? (jhi + N - 1) / N : t_lo;
 
-  const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh;
-  const bf16* vbase = a.v + b * a.v_sb + (int64_t)off * a.v_ss + g * a.v_sh;
+  const bf16* kbase = a.k + (PAGED ? 0 : b * a.k_sb + (int64_t)off * a.k_ss) + g * a.k_sh;
+  const bf16* vbase = a.v + (PAGED ? 0 : b * a.v_sb + (int64_t)off * a.v_ss) + g * a.v_sh;
+  [[maybe_unused]] const int32_t* trow = PAGED ? a.table + (int64_t)b * a.max_pages : nullptr;
+  static_assert(!PAGED || N == 32, "a paged tile spans two pages");
+  [[maybe_unused]] int phys[2] = {0, 0};  // physical pages of the tile being copied (paged)
   const RowFrags<D> rowf(lane);
   const TrFrags<D> trf(lane);
   const float c = a.c;
@@ -119,8 +140,16 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
       for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
     l_run = 0.f;
     if (t_lo < t_hi) {
-      dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, t_lo * N, lenk - t_lo * N), wave, lane);
-      dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, t_lo * N, lenk - t_lo * N), wave, lane);
+      if constexpr (PAGED) {
+        table_pages2(phys, trow, t_lo * N, lenk - t_lo * N);
+        dma_rows_paged<D, N, 4>(Ks, paged_tile_src<N>(kbase, a.k_sb, a.k_ss, phys, a.num_pages, lenk - t_lo * N),
+                                wave, lane);
+        dma_rows_paged<D, N, 4>(Vs, paged_tile_src<N>(vbase, a.v_sb, a.v_ss, phys, a.num_pages, lenk - t_lo * N),
+                                wave, lane);
+      } else {
+        dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, t_lo * N, lenk - t_lo * N), wave, lane);
+        dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, t_lo * N, lenk - t_lo * N), wave, lane);
+      }
     }
     for (int jt = t_lo; jt < t_hi; ++jt) {
       const int j0 = jt * N;
@@ -153,7 +182,15 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
         }
       }
       barrier_lds();  // every wave is done with Ks
-      if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
+      if constexpr (PAGED) {
+        if (has_next) {
+          table_pages2(phys, trow, j0 + N, lenk - j0 - N);  // the next tile's pages, for K and V
+          dma_rows_paged<D, N, 4>(Ks, paged_tile_src<N>(kbase, a.k_sb, a.k_ss, phys, a.num_pages, lenk - j0 - N),
+                                  wave, lane);
+        }
+      } else {
+        if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
+      }
 
       if constexpr (SOFTCAP) {
         // the cap applies to every score before the mask (masked entries become -inf below)
@@ -249,7 +286,13 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
         }
       }
       barrier_lds();  // every wave is done with Vs
-      if (has_next) dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, j0 + N, lenk - j0 - N), wave, lane);
+      if constexpr (PAGED) {
+        if (has_next)
+          dma_rows_paged<D, N, 4>(Vs, paged_tile_src<N>(vbase, a.v_sb, a.v_ss, phys, a.num_pages, lenk - j0 - N),
+                                  wave, lane);
+      } else {
+        if (has_next) dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, j0 + N, lenk - j0 - N), wave, lane);
+      }
     }
   }
 
@@ -306,18 +349,25 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
 // take 256 registers.
 template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
 __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_kernel(AttnArgs a) {
-  fwd_body<D, N, EXACT, SOFTCAP, F16, false>(a);
+  fwd_body<D, N, EXACT, SOFTCAP, F16, false, false>(a);
 }
 
 template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
 __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_merge_kernel(AttnArgs a) {
-  fwd_body<D, N, EXACT, SOFTCAP, F16, true>(a);
+  fwd_body<D, N, EXACT, SOFTCAP, F16, true, false>(a);
+}
+
+template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
+__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_paged_kernel(AttnArgs a) {
+  fwd_body<D, N, EXACT, SOFTCAP, F16, false, true>(a);
 }
 
 template <int D, bool EXACT, bool SOFTCAP, bool F16>
 void launch_fwd_one(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(8 * a.per_xcd), block(256);
-  if (a.merge)
+  if (a.paged)
+    hipLaunchKernelGGL((fwd_paged_kernel<D, kFwdKeys, EXACT, SOFTCAP, F16>), grid, block, 0, stream, a);
+  else if (a.merge)
     hipLaunchKernelGGL((fwd_merge_kernel<D, kFwdKeys, EXACT, SOFTCAP, F16>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((fwd_kernel<D, kFwdKeys, EXACT, SOFTCAP, F16>), grid, block, 0, stream, a);

@@ -245,6 +245,83 @@ __device__ __forceinline__ void dma_rows(bf16* tile, const TileSrc& src, int wav
 template <int D, int ROWS, int NW>
 constexpr int dma_rows_per_wave() { return ROWS * D / 512 / NW; }
 
+// A tile of ROWS key / value rows of a paged cache: 16-token pages, rows of one page at a fixed
+// slot stride, the pages anywhere in the pool.  One buffer resource per page; rows past `nvalid`
+// read as zeros.  row0 is a multiple of 16.
+template <int ROWS>
+struct PagedTileSrc {
+  static_assert(ROWS % 16 == 0, "whole pages");
+  TileSrc pg[ROWS / 16];
+};
+
+// The physical page ids of the two pages of a 32-row tile starting at row0 (a multiple of 16),
+// of which nvalid >= 1 rows are valid, from the sequence's page-table row `trow`.  They are read
+// with scalar loads and one wait for those loads alone: the compiler would otherwise emit a
+// vector load whose wait also drains the tile copies still in flight.  The second entry is only
+// read when the second page holds a valid row (else the first entry is read again and the id
+// goes unused).
+__device__ __forceinline__ void table_pages2(int (&phys)[2], const int32_t* trow, int row0, int nvalid) {
+  const uint64_t base = (uint64_t)(uintptr_t)trow;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const uint64_t ub = ((uint64_t)hi << 32) | lo;
+  const uint32_t o0 = __builtin_amdgcn_readfirstlane((uint32_t)(row0 >> 4) * 4u);
+  const uint32_t o1 = __builtin_amdgcn_readfirstlane(o0 + (nvalid > 16 ? 4u : 0u));
+  int p0, p1;
+  asm volatile("s_load_dword %0, %2, %3\n\ts_load_dword %1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(p0), "=&s"(p1)
+               : "s"(ub), "s"(o0), "s"(o1)
+               : "memory");
+  phys[0] = p0;
+  phys[1] = p1;
+}
+
+template <int ROWS>
+__device__ __forceinline__ PagedTileSrc<ROWS> paged_tile_src(const bf16* cache, int64_t page_stride,
+                                                             int64_t slot_stride, const int (&phys)[ROWS / 16],
+                                                             int num_pages, int nvalid) {
+  PagedTileSrc<ROWS> t;
+#pragma unroll
+  for (int p = 0; p < ROWS / 16; ++p) {
+    const int id = min(max(phys[p], 0), num_pages - 1);  // out-of-pool ids are clamped, never followed
+    t.pg[p] = tile_src<16>(cache + (int64_t)id * page_stride, slot_stride, 0, nvalid - 16 * p);
+  }
+  return t;
+}
+
+// dma_rows for a paged tile: wave-instruction i moves tile rows i * RPI .. (all in one page)
+// from that page's resource into the same swizzled LDS positions dma_rows uses.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows_paged(bf16* tile, const PagedTileSrc<ROWS>& src, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int RPI = 64 / CH;
+  constexpr int NI = ROWS / RPI;
+  static_assert(16 % RPI == 0 && NI % NW == 0, "an instruction's rows lie in one page");
+#pragma unroll
+  for (int k = 0; k < NI / NW; ++k) {
+    const int i = wave + k * NW;
+    const int page = (i * RPI) >> 4;  // wave-uniform
+    const int trow = i * RPI + lane / CH;
+    // the page's resource, selected without indexing the array by a run-time value and kept
+    // in scalar registers (the instruction takes it from there)
+    i32x4 rs = src.pg[0].rsrc;
+    uint32_t rb = src.pg[0].row_bytes;
+#pragma unroll
+    for (int p = 1; p < ROWS / 16; ++p)
+      if (page == p) {
+        rs = src.pg[p].rsrc;
+        rb = src.pg[p].row_bytes;
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rs[e] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)rs[e]);
+    const uint32_t voff = (uint32_t)(trow & 15) * rb + (uint32_t)(16 * ((lane % CH) ^ swz_h(trow)));
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + i * RPI * D));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+                 "s"(rs)
+                 : "memory");
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

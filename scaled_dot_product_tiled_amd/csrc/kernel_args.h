@@ -81,6 +81,17 @@ struct AttnArgs {
   // forward: when not NULL, every restart of a workgroup's key loop (head_dim 512 softmax
   // reference raised) adds 1 here
   int* restarts;
+  // forward over a paged cache (paged): K, V are (num_pages, 16, Hkv, D) with k_sb / v_sb the
+  // page stride, k_ss / v_ss the slot stride and k_sh / v_sh the head stride; sequence b's key
+  // j lives in page table[b * max_pages + j / 16], slot j % 16; it holds kv_len[b] keys (its
+  // cached tokens, the new ones included) and its len query rows sit at positions
+  // kv_len[b] - len .. kv_len[b] - 1.  seq_off is then the B + 1 query row offsets (cu_q),
+  // read directly, and total the packed row count
+  int paged;
+  int total;
+  const int32_t* table;
+  const int32_t* kv_len;
+  int max_pages, num_pages;
 };
 
 struct DecodeArgs {

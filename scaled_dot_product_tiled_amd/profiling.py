@@ -151,6 +151,10 @@ WORKLOADS = {
     "varlen_d512": "padded varlen causal GQA, B=8 lengths U{512..8192} padded to 8192, Hq=32 Hkv=4 D=512 "
                    "(forward + backward)",
     "decode_d128": "paged decode, B=64 Hq=32 Hkv=8 D=128, 16-token pages, contexts U{512..4096} (two pools)",
+    "paged_prefill_d512": "paged forward, a 2048-token chunk after 6144 cached tokens, Hq=32 Hkv=4 D=512, 16-token "
+                          "pages (append + attn_fwd_paged; then append + gather + chunk-pair forward)",
+    "mixed_step_d512": "paged forward, a 1024-token chunk after 3072 cached plus 31 decode rows of 512..4096 tokens, "
+                       "Hq=32 Hkv=4 D=512 (append + attn_fwd_paged)",
 }
 
 SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_VALU_MFMA_BUSY_CYCLES",

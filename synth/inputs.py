@@ -26,10 +26,11 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64", "f32_to_f16_bits", "f16_bits_to_f64",
     "bits_to_f64", "NAN_BITS", "stream", "normal_bf16", "normal_16", "make_attention_inputs", "make_decode_inputs",
     "lengths_to_pad_mask", "lengths_to_cu_seqlens", "pack_rows", "draw_lengths", "STREAM",
+    "PrefillWorkload", "PREFILL_WORKLOADS", "make_prefill_inputs",
 ]
 
 # Stream ids inside one workload.
-STREAM = {"q": 0, "k": 1, "v": 2, "do": 3, "lengths": 4, "pages": 5, "fill": 6}
+STREAM = {"q": 0, "k": 1, "v": 2, "do": 3, "lengths": 4, "pages": 5, "fill": 6, "new": 7}
 
 
 # ----------------------------------------------------------------------------
@@ -185,6 +186,61 @@ ATTN_WORKLOADS = {
 DECODE_WORKLOADS = {
     "decode_d128": DecodeWorkload(5, "paged decode d128 (B64 Hq32 Hkv8, 16-token pages)", 64, 32, 8, 128),
 }
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    """New query tokens of several sequences against their paged KV caches in one call: each
+    sequence holds ctx tokens (its new ones included) and has n of them new; n = 1 is a decode
+    row, n = ctx a whole prompt, anything between a prompt chunk after a cached prefix."""
+    wid: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    ctx: tuple                       # per sequence: tokens in the cache after the step
+    new: tuple                       # per sequence: how many of them are new query rows
+    page_size: int = 16
+    pool_factor: float = 1.5
+    dtype: str = "bf16"
+    window: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def scaled(self, **kw) -> "PrefillWorkload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return PrefillWorkload(**d)
+
+
+PREFILL_WORKLOADS = {
+    # a 2048-token prompt chunk after 6144 cached tokens at the full-attention layer's shape
+    "paged_prefill_d512": PrefillWorkload(6, "paged prefill d512: 2048 new tokens after 6144 cached "
+                                             "(Hq32 Hkv4, 16-token pages)", 1, 32, 4, 512, (8192,), (2048,)),
+    # a serving step mixing one prompt chunk with 31 decode rows of 512..4096-token contexts
+    "mixed_step_d512": PrefillWorkload(7, "mixed step d512: a 1024-token chunk after 3072 cached plus 31 decode "
+                                          "rows (Hq32 Hkv4, 16-token pages)", 32, 32, 4, 512,
+                                       (4096,) + tuple(512 + (3584 * i) // 30 for i in range(31)),
+                                       (1024,) + (1,) * 31),
+}
+
+
+def make_prefill_inputs(w: PrefillWorkload, seed: int = 0, poison_unused: bool = False) -> dict:
+    """Seeded paged prefill inputs: the caches and block table of make_decode_inputs for the
+    contexts w.ctx (pages permuted over the pool), plus the packed new query rows q (T, Hq, D)
+    with their offsets cu_q (B+1) and max_q."""
+    dw = DecodeWorkload(w.wid, w.name, w.B, w.Hq, w.Hkv, w.D, w.page_size,
+                        (min(w.ctx), max(w.ctx)), w.pool_factor, w.dtype)
+    out = make_decode_inputs(dw, seed, poison_unused, ctx_lens=np.asarray(w.ctx, dtype=np.int32))
+    n = np.asarray(w.new, dtype=np.int64)
+    cu = lengths_to_cu_seqlens(n)
+    out["q"] = normal_16(stream(seed, w.wid, STREAM["new"]), (int(cu[-1]), w.Hq, w.D), 1.0, w.dtype)
+    out["cu_q"] = cu
+    out["max_q"] = int(n.max()) if len(n) else 0
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from synth import DECODE_WORKLOADS, AttnWorkload, lengths_to_pad_mask, make_attention_inputs, make_decode_inputs
+from synth import (DECODE_WORKLOADS, PREFILL_WORKLOADS, AttnWorkload, lengths_to_pad_mask, make_attention_inputs,
+                   make_decode_inputs, make_prefill_inputs)
 from tests.gpu_util import dev, host_bits
 
 pytestmark = pytest.mark.gpu
@@ -116,5 +117,35 @@ def test_bad_page_metadata_is_rejected(debug_on, fault):
         sdpt.paged_kv_append(new, new, kc, vc, bt, bc)
     with pytest.raises(RuntimeError, match="status 1"):
         sdpt.paged_kv_gather(kc, vc, bt, bc, 8)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), host_bits(ref))   # nothing was launched
+
+
+@pytest.mark.parametrize("fault", ["cu_decreasing", "cu_short_total", "page_id", "ctx_too_long"])
+def test_bad_paged_forward_metadata_is_rejected(debug_on, fault):
+    """attn_fwd_paged checks its query offsets and its pages before its one launch."""
+    w = PREFILL_WORKLOADS["mixed_step_d512"].scaled(B=3, Hq=4, Hkv=2, D=256, ctx=(40, 20, 70), new=(10, 1, 30))
+    inp = make_prefill_inputs(w, seed=3)
+    q, kc, vc = (dev(inp[x]) for x in ("q", "k_cache", "v_cache"))
+    table, ctx, cu = inp["block_table"].copy(), inp["ctx_lens"].copy(), inp["cu_q"].astype(np.int32)
+    say(f"[debug] paged forward {fault}")
+
+    def run(table, ctx, cu, out=None):
+        return sdpt.attn_fwd_paged(q, kc, vc, torch.from_numpy(table).to("cuda:0"), torch.from_numpy(cu).to("cuda:0"),
+                                   torch.from_numpy(ctx).to("cuda:0"), inp["max_q"], scale=w.scale, out=out)
+    ref, _ = run(table, ctx, cu)
+    if fault == "cu_decreasing":
+        cu = cu.copy()
+        cu[1], cu[2] = cu[2], cu[1]
+    elif fault == "cu_short_total":
+        cu = cu.copy()
+        cu[-1] -= 1
+    elif fault == "page_id":
+        table[2, 1] = kc.shape[0]
+    else:
+        ctx[0] = table.shape[1] * w.page_size + 1
+    out = ref.clone()
+    with pytest.raises(RuntimeError, match="status 1"):
+        run(table, ctx, cu, out=out)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), host_bits(ref))   # nothing was launched

@@ -1,6 +1,8 @@
 """GPU checks of the paged cache calls (paged_kv_append, paged_kv_gather) through the C ABI,
-a decode step captured in a HIP graph and replayed, and a paged prefill (gather + chunk-pair
-forward) against the float64 oracle.
+a decode step captured in a HIP graph and replayed, a paged prefill (gather + chunk-pair
+forward) against the float64 oracle, and the in-kernel paged forward attn_fwd_paged (prompt
+chunks, whole prompts and decode rows in one call) against the oracle and, bit for bit,
+against the gather + chunk-pair path.
 
 Append and gather move bits, so they are compared bit for bit with the oracle's scatter and
 gather.  The graph replays are compared bit for bit with the same calls made eagerly (same
@@ -13,7 +15,8 @@ import pytest
 import torch
 
 import oracle
-from synth import DECODE_WORKLOADS, bits_to_f64, make_decode_inputs, normal_16, stream
+from synth import (DECODE_WORKLOADS, PREFILL_WORKLOADS, bits_to_f64, make_decode_inputs, make_prefill_inputs,
+                   normal_16, stream)
 from tests.gpu_util import LSE_MAX_ABS, O_MAX_ABS, all_finite, dev, host, host_bits, max_abs
 
 pytestmark = pytest.mark.gpu
@@ -175,3 +178,134 @@ def test_paged_prefill_matches_oracle(D, prev, n):
     ro, rl = oracle.attention_forward(qf, kf, vf, 1.0 / np.sqrt(D), True, 0)
     assert max_abs(host(o), ro[:, prev:]) <= O_MAX_ABS
     assert max_abs(host(lse), rl[:, :, prev:]) <= LSE_MAX_ABS
+
+
+# ---------------------------------------------------------------------------
+# attn_fwd_paged: K/V read through the block table inside the forward kernel
+# ---------------------------------------------------------------------------
+def _prefill_dev(inp, dtype):
+    return dict(q=dev(inp["q"], dtype), kc=dev(inp["k_cache"], dtype), vc=dev(inp["v_cache"], dtype),
+                table=torch.from_numpy(inp["block_table"]).to("cuda:0"),
+                cu=torch.from_numpy(inp["cu_q"].astype(np.int32)).to("cuda:0"),
+                ctx=torch.from_numpy(inp["ctx_lens"]).to("cuda:0"))
+
+
+def _prefill_oracle(inp, w, softcap=0.0):
+    f = lambda x: bits_to_f64(x, w.dtype)  # noqa: E731
+    return oracle.paged_prefill(f(inp["q"]), f(inp["k_cache"]), f(inp["v_cache"]), inp["block_table"], inp["cu_q"],
+                                inp["ctx_lens"], w.scale, w.window, w.page_size, softcap)
+
+
+MIXED = PREFILL_WORKLOADS["mixed_step_d512"]
+# (D, dtype, window, softcap, contexts, new rows): a prompt chunk after a cached prefix, whole
+# prompts, decode rows (n = 1) with one-token, page-edge and long contexts, a sequence with no
+# new row, and rows before position 0 (more new rows than cached tokens)
+PREFILL_CASES = [
+    (512, "bf16", 0, 0.0, (300, 1, 17, 130, 520, 40, 64), (77, 1, 1, 130, 1, 40, 0)),
+    (256, "bf16", 100, 0.0, (700, 33, 1, 260), (190, 1, 1, 260)),
+    (512, "f16", 0, 0.0, (96, 2, 400), (96, 1, 33)),
+    (256, "bf16", 0, 20.0, (129, 64, 3), (129, 1, 3)),
+    (512, "bf16", 0, 0.0, (3, 10, 0), (40, 40, 5)),
+]
+
+
+@pytest.mark.parametrize("D,dtype,window,softcap,ctx,new", PREFILL_CASES)
+def test_fwd_paged_matches_oracle(D, dtype, window, softcap, ctx, new):
+    w = MIXED.scaled(B=len(ctx), Hq=8, Hkv=2, D=D, dtype=dtype, window=window, ctx=ctx, new=new,
+                     name=f"paged fwd d{D}")
+    inp = make_prefill_inputs(w, seed=31)
+    say(f"[fwd paged] D={D} dtype={dtype} window={window} softcap={softcap} ctx={ctx} new={new}")
+    d = _prefill_dev(inp, dtype)
+    o, lse = sdpt.attn_fwd_paged(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"],
+                                 scale=w.scale, window=window, softcap=softcap)
+    torch.cuda.synchronize()
+    assert all_finite(o, lse)
+    ro, rl = _prefill_oracle(inp, w, softcap)
+    assert max_abs(host(o), ro) <= O_MAX_ABS
+    assert max_abs(host(lse), rl) <= LSE_MAX_ABS
+    # rows before position 0 and sequences without keys: exact zeros
+    cu, c = inp["cu_q"], inp["ctx_lens"]
+    for b in range(w.B):
+        neg = min(max(int(new[b]) - int(c[b]), 0), int(new[b])) if c[b] > 0 else int(new[b])
+        if neg:
+            assert not host(o)[cu[b]:cu[b] + neg].any() and not host(lse)[:, cu[b]:cu[b] + neg].any()
+
+
+@pytest.mark.parametrize("D,dtype,window", [(512, "bf16", 0), (256, "f16", 48)])
+def test_fwd_paged_equals_gather_then_chunk_bit_for_bit(D, dtype, window):
+    """The same kernel arithmetic reads the keys through the table instead of a gathered copy:
+    per sequence, O and LSE equal paged_kv_gather + attn_fwd_chunk at q_pos0 = ctx - n exactly."""
+    ctx, new = (600, 1, 250, 45), (200, 1, 250, 1)
+    w = MIXED.scaled(B=len(ctx), Hq=8, Hkv=2, D=D, dtype=dtype, window=window, ctx=ctx, new=new)
+    inp = make_prefill_inputs(w, seed=32)
+    say(f"[fwd paged vs gather] D={D} dtype={dtype} window={window}")
+    d = _prefill_dev(inp, dtype)
+    o, lse = sdpt.attn_fwd_paged(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"],
+                                 scale=w.scale, window=window)
+    torch.cuda.synchronize()
+    ob, lb = host_bits(o), lse.cpu().numpy()
+    cu = inp["cu_q"]
+    for b in range(w.B):
+        L, n = int(ctx[b]), int(new[b])
+        tb = d["table"][b:b + 1].contiguous()
+        cb = d["ctx"][b:b + 1].contiguous()
+        kg, vg = sdpt.paged_kv_gather(d["kc"], d["vc"], tb, cb, L)
+        qb = d["q"][cu[b]:cu[b + 1]].unsqueeze(0).contiguous()
+        oc, lc = sdpt.attn_fwd_chunk(qb, kg, vg, L - n, 0, scale=w.scale, window=window, out_dtype=qb.dtype)
+        torch.cuda.synchronize()
+        assert np.array_equal(ob[cu[b]:cu[b + 1]], host_bits(oc)[0]), b
+        assert np.array_equal(lb[:, cu[b]:cu[b + 1]], lc.cpu().numpy()[0]), b
+
+
+def test_fwd_paged_never_reads_unused_pages_or_slots():
+    """Pool pages no sequence uses, the slots past each context and the table entries past each
+    sequence's pages hold NaN / out-of-pool ids: the result is finite and equals the clean run's
+    bit for bit."""
+    w = MIXED.scaled(B=4, Hq=8, Hkv=2, D=512, ctx=(70, 1, 33, 300), new=(20, 1, 1, 64))
+    clean = make_prefill_inputs(w, seed=33)
+    pois = make_prefill_inputs(w, seed=33, poison_unused=True)
+    table = pois["block_table"].copy()
+    for b in range(w.B):
+        table[b, -(-int(w.ctx[b]) // 16):] = 1 << 30
+    pois["block_table"] = table
+    say("[fwd paged poisoned]")
+    outs = []
+    for inp in (clean, pois):
+        d = _prefill_dev(inp, "bf16")
+        o, lse = sdpt.attn_fwd_paged(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"],
+                                     scale=w.scale)
+        torch.cuda.synchronize()
+        outs.append((host_bits(o), lse.cpu().numpy()))
+    assert np.isfinite(outs[1][1]).all() and all_finite(torch.from_numpy(outs[1][1]))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_mixed_step_full_size_sampled_rows():
+    """The mixed serving step at its full size (a 1024-token chunk after 3072 cached plus 31 decode
+    rows, 32 query heads, D = 512): every decode row and sampled chunk rows against the oracle,
+    row by row."""
+    w = MIXED
+    inp = make_prefill_inputs(w, seed=0)
+    say("[mixed step full size]")
+    d = _prefill_dev(inp, "bf16")
+    o, lse = sdpt.attn_fwd_paged(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"],
+                                 scale=w.scale)
+    torch.cuda.synchronize()
+    assert all_finite(o, lse)
+    oh, lh = host(o), lse.cpu().numpy()
+    cu = inp["cu_q"]
+    rows = sorted(set([0, 1, 511, 512, 1000, 1023] + list(range(1024, int(cu[-1])))))
+    f = lambda x: bits_to_f64(x, "bf16")  # noqa: E731
+    q, kc, vc = f(inp["q"]), f(inp["k_cache"]), f(inp["v_cache"])
+    worst_o = worst_l = 0.0
+    for t in rows:
+        b = int(np.searchsorted(cu, t, side="right") - 1)
+        L, n = int(w.ctx[b]), int(w.new[b])
+        pos = L - n + (t - int(cu[b]))
+        kk = oracle.gather_pages(kc, inp["block_table"][b], L, w.page_size)[None]
+        vv = oracle.gather_pages(vc, inp["block_table"][b], L, w.page_size)[None]
+        ro, rl = oracle.attention_forward_chunk(q[None, t:t + 1], kk, vv, w.scale, True, 0, pos, 0)
+        worst_o = max(worst_o, max_abs(oh[t], ro[0, 0]))
+        worst_l = max(worst_l, max_abs(lh[:, t], rl[0, :, 0]))
+    say(f"[mixed step full size] rows={len(rows)} O max-abs {worst_o:.3g} LSE max-abs {worst_l:.3g}")
+    assert worst_o <= O_MAX_ABS and worst_l <= LSE_MAX_ABS

@@ -4,8 +4,8 @@ import ctypes
 import os
 import re
 
-from scaled_dot_product_tiled_amd.binding import (AttnChunkShape, AttnDecodeShape, AttnShape, AttnTensor,
-                                                  load_library)
+from scaled_dot_product_tiled_amd.binding import (AttnChunkShape, AttnDecodeShape, AttnPagedShape, AttnShape,
+                                                  AttnTensor, load_library)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
@@ -253,6 +253,31 @@ def test_paged_cache_call_checks():
     assert app(AttnDecodeShape(4, 32, 8, 64, 16, 100, 8)) == UNSUPPORTED           # head_dim
     assert gat(AttnDecodeShape(4, 32, 8, 128, 16, 100, 8, 1)) == UNSUPPORTED       # fp32 cache
     assert app(n=0) == OK and gat(AttnDecodeShape(0, 32, 8, 512, 16, 100, 8)) == OK  # nothing to move
+    assert lib.attn_last_hip_error() == 0
+
+
+def test_paged_prefill_checks():
+    """attn_fwd_paged takes no workspace; bad arguments are refused before any launch."""
+    lib = load_library()
+    sh = AttnPagedShape(32, 1024, 1055, 32, 4, 512, 0, 16, 7000, 256)
+    q = AttnTensor(0x10000, 0, 32 * 512, 512)
+    kc = AttnTensor(0x20000, 16 * 4 * 512, 4 * 512, 512)
+
+    def call(shape=sh, q=q, k=kc, table=0x3000, cu=0x3100, ctx=0x3200, scale=0.05, window=0, softcap=0.0,
+             lse=0x5000):
+        return lib.attn_fwd_paged(ctypes.byref(shape), q, k, k, table, cu, ctx, scale, window, softcap, q, lse, None)
+    assert call(table=0) == INVALID and call(cu=0) == INVALID and call(ctx=0) == INVALID
+    assert call(scale=0.0) == INVALID and call(window=-1) == INVALID and call(softcap=-1.0) == INVALID
+    assert call(lse=0x5002) == INVALID                                   # misaligned lse
+    assert call(q=AttnTensor(0x10008, 0, 32 * 512, 512)) == INVALID      # misaligned rows
+    for bad, st in ((AttnPagedShape(2, 8, 16, 32, 4, 128, 0, 16, 10, 4), UNSUPPORTED),   # head_dim
+                    (AttnPagedShape(2, 8, 16, 32, 4, 512, 0, 32, 10, 4), UNSUPPORTED),   # page size
+                    (AttnPagedShape(2, 8, 16, 32, 4, 512, 1, 16, 10, 4), UNSUPPORTED),   # fp32
+                    (AttnPagedShape(2, 8, 16, 30, 4, 512, 0, 16, 10, 4), INVALID),       # Hq % Hkv
+                    (AttnPagedShape(2, 8, 16, 32, 4, 512, 0, 16, 0, 4), INVALID)):       # empty pool
+        assert call(shape=bad) == st
+    assert call(k=AttnTensor(0x20000, 1 << 31, 1 << 27, 512)) == UNSUPPORTED   # slot stride past 2^26
+    assert call(shape=AttnPagedShape(0, 0, 0, 32, 4, 512, 0, 16, 1, 1)) == OK   # nothing to do
     assert lib.attn_last_hip_error() == 0
 
 

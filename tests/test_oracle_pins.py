@@ -607,3 +607,70 @@ def test_decode_softcap_is_last_row_of_capped_causal_attention():
         qq[0, n - 1] = q[b]
         full, _ = oracle.attention_forward(qq, kk, vv, w.scale, True, 0, None, 2.0)
         np.testing.assert_allclose(o[b], full[0, n - 1], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Paged prefill: the new rows of several sequences against their paged caches
+# ---------------------------------------------------------------------------
+def _paged_sequences(rng, ctx, Hkv, D, ps, pool, maxp):
+    """Each sequence's tokens written into pages of a permuted pool with paged_append (pinned by
+    its hand example); returns the caches, the table and the dense tokens."""
+    B = len(ctx)
+    perm = rng.permutation(pool)
+    table = np.full((B, maxp), -1, np.int32)
+    off = 0
+    for b in range(B):
+        n = -(-int(ctx[b]) // ps)
+        table[b, :n] = perm[off:off + n]
+        off += n
+    kc = rng.standard_normal((pool, ps, Hkv, D))         # unused slots hold other values
+    vc = rng.standard_normal((pool, ps, Hkv, D))
+    toks_k = [rng.standard_normal((int(c), Hkv, D)) for c in ctx]
+    toks_v = [rng.standard_normal((int(c), Hkv, D)) for c in ctx]
+    for b in range(B):
+        if ctx[b] > 0:
+            kc = oracle.paged_append(kc, table[b:b + 1], ctx[b:b + 1], toks_k[b][None], ps)
+            vc = oracle.paged_append(vc, table[b:b + 1], ctx[b:b + 1], toks_v[b][None], ps)
+    return kc, vc, table, toks_k, toks_v
+
+
+@pytest.mark.parametrize("window,softcap", [(0, 0.0), (7, 0.0), (0, 2.0)])
+def test_paged_prefill_rows_are_last_rows_of_causal_attention(window, softcap):
+    """A sequence's n new rows equal the last n rows of whole-sequence causal attention
+    (attention_forward, pinned against torch's float64 SDPA) over its ctx tokens, whatever the
+    page placement; decode rows (n = 1) equal paged_decode; rows at negative positions (n > ctx)
+    see nothing and the others are the sequence's causal rows."""
+    rng = np.random.default_rng(21)
+    Hq, Hkv, D, ps, pool, maxp = 4, 2, 8, 4, 40, 5
+    ctx = np.array([9, 1, 12, 5, 6, 2, 0], dtype=np.int32)
+    new = np.array([3, 1, 12, 1, 0, 4, 2])
+    kc, vc, table, tk, tv = _paged_sequences(rng, ctx, Hkv, D, ps, pool, maxp)
+    cu = np.concatenate([[0], np.cumsum(new)])
+    q = 2.0 * rng.standard_normal((int(cu[-1]), Hq, D))
+    scale = 0.4
+    o, lse = oracle.paged_prefill(q, kc, vc, table, cu, ctx, scale, window, ps, softcap)
+    for b in range(len(ctx)):
+        lo, hi, n, c = int(cu[b]), int(cu[b + 1]), int(new[b]), int(ctx[b])
+        if n == 0:
+            continue
+        neg = max(n - c, 0)                       # rows before position 0
+        assert not o[lo:lo + neg].any() and not lse[:, lo:lo + neg].any()
+        if c == 0:
+            continue
+        qf = np.zeros((1, c, Hq, D))
+        qf[0, c - (n - neg):] = q[lo + neg:hi]
+        full, fl = oracle.attention_forward(qf, tk[b][None], tv[b][None], scale, True, window, None, softcap)
+        np.testing.assert_allclose(o[lo + neg:hi], full[0, c - (n - neg):], atol=1e-13)
+        np.testing.assert_allclose(lse[:, lo + neg:hi], fl[0, :, c - (n - neg):], atol=1e-13)
+        if n == 1 and window == 0:
+            qd = np.zeros((len(ctx), Hq, D))
+            qd[b] = q[lo]
+            od = oracle.paged_decode_one(qd, kc, vc, table, ctx, scale, b, ps, softcap)
+            np.testing.assert_allclose(o[lo], od, atol=1e-13)
+    # another placement of the same tokens gives the same bytes
+    kc2, vc2, table2, _, _ = _paged_sequences(np.random.default_rng(21), ctx, Hkv, D, ps, pool, maxp)
+    perm = np.random.default_rng(5).permutation(pool)
+    inv = np.argsort(perm)
+    table3 = np.where(table2 >= 0, perm[np.maximum(table2, 0)], -1)
+    o3, lse3 = oracle.paged_prefill(q, kc2[inv], vc2[inv], table3, cu, ctx, scale, window, ps, softcap)
+    assert np.array_equal(o3, o) and np.array_equal(lse3, lse)

@@ -13,7 +13,8 @@ the C ABI.  Reported:
   decode    paged single-token decode (B=64, Hq=32, Hkv=8, D=128, 16-token pages, contexts
             U{512..4096}, pages permuted over a 1.5x pool) as achieved HBM GB/s of the algorithmic
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
-            pages_in_order is the same decode with each sequence's pages consecutive in the pool;
+            pages_in_order is the same decode with each sequence's pages consecutive in the pool,
+            through the table and through paged_decode_contiguous (first page per sequence, no table);
   other_workloads  (median and best of per-call HIP-event timings) forward / backward TFLOP/s of the
             tiny (B=1 S=128 D=512), sliding-window (D=256, W=1024) and padded varlen (B=8, lengths
             U{512..8192}, D=512) workloads, of one context-parallel rank's chunk pairs (16k tokens in
@@ -637,7 +638,8 @@ def main():
             t2[b, :n] = np.arange(k, k + n)
             k += n
         return dict(q=p["q"], kc=p["kc"][idx].contiguous(), vc=p["vc"][idx].contiguous(),
-                    table=torch.from_numpy(t2).to("cuda:0"), ctx=p["ctx"])
+                    table=torch.from_numpy(t2).to("cuda:0"), ctx=p["ctx"],
+                    first=torch.from_numpy(np.ascontiguousarray(t2[:, 0])).to("cuda:0"), max_pages=tbl.shape[1])
 
     cpools = [in_order(p) for p in pools]
     itc = [0]
@@ -652,6 +654,18 @@ def main():
         dec_in_order()
     torch.cuda.synchronize()
     tdo = time_calls(dec_in_order, n_dec, stream)
+
+    # the same in-order pools through paged_decode_contiguous: no table, one first page per sequence
+    def dec_contiguous():
+        p = cpools[itc[0] & 1]
+        sdpt.paged_decode_contiguous(p["q"], p["kc"], p["vc"], p["first"], p["ctx"], p["max_pages"], scale=dw.scale,
+                                     out=outs[itc[0] & 1], workspace=ws)
+        itc[0] += 1
+
+    for _ in range(4):
+        dec_contiguous()
+    torch.cuda.synchronize()
+    tdc = time_calls(dec_contiguous, n_dec, stream)
     del cpools
     rpd = rocprof_ms("decode_d128", "decode_split")
 
@@ -710,7 +724,9 @@ def main():
                    "ms_best": round(td["best"], 4), "reps": n_dec, "GB/s": round(dec_gbs, 1),
                    "kernels": dec_kernels,
                    "pages_in_order": {"ms": round(tdo["mean"], 4), "ms_best": round(tdo["best"], 4),
-                                      "GB/s": round(dec_bytes / (tdo["mean"] * 1e-3) / 1e9, 1)},
+                                      "GB/s": round(dec_bytes / (tdo["mean"] * 1e-3) / 1e9, 1),
+                                      "contiguous_call": {"ms": round(tdc["mean"], 4), "ms_best": round(tdc["best"], 4),
+                                                          "GB/s": round(dec_bytes / (tdc["mean"] * 1e-3) / 1e9, 1)}},
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "bytes_per_launch": dec_bytes, "traffic": traffic_bytes("decode_split"),

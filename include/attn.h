@@ -312,6 +312,28 @@ attn_status paged_decode_noalloc(const attn_decode_shape* shape,
 size_t paged_decode_noalloc_max_bytes(void);
 
 /*
+ * paged_decode_contiguous: paged_decode for caches whose every sequence holds consecutive pages
+ * (the BLOCKS_ARE_CONTIGUOUS setting of the page "flex_attention + paged KV + CUDA graphs vs
+ * vLLM", section "What each option did": safe there because a fresh batch reserves its pages in
+ * order, and faster because no per-block page-table lookup is made).  Instead of a block table
+ * it takes
+ *   first_page   device int32 (B): logical page p of sequence b is physical page
+ *                first_page[b] + p.  Ids outside [0, num_pages) are clamped into range.
+ * shape->max_pages_per_seq still bounds ctx_lens (clamped to max_pages_per_seq * page_size)
+ * and sizes the workspace (paged_decode_workspace_bytes).  Other arguments, layouts and
+ * results as paged_decode; the result equals paged_decode's bit for bit when block_table[b][p]
+ * = first_page[b] + p.  In debug mode (attn_debug) a sequence whose pages leave the pool
+ * returns ATTN_ERR_INVALID_ARG.
+ */
+attn_status paged_decode_contiguous(const attn_decode_shape* shape,
+                                    const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                                    attn_tensor k_cache, attn_tensor v_cache,
+                                    const int32_t* first_page, const int32_t* ctx_lens,
+                                    float scale, float softcap,
+                                    void* o, int64_t o_stride_b, int64_t o_stride_h,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_kv_append: write the n_tokens newest tokens of each sequence into its cache pages:
  * token i of sequence b (k_new/v_new row (b, i)) goes to logical position
  * ctx_lens[b] - n_tokens + i, i.e. ctx_lens counts the appended tokens, as it does for

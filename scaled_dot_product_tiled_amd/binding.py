@@ -62,7 +62,7 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read", "attn_count_restarts", "paged_decode_noalloc",
-           "paged_decode_noalloc_max_bytes", "attn_peak_probe", "attn_fwd_paged")
+           "paged_decode_noalloc_max_bytes", "attn_peak_probe", "attn_fwd_paged", "paged_decode_contiguous")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -108,6 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          AttnTensor, vp, vp, ctypes.c_float, ctypes.c_float, vp, ctypes.c_int64,
                                          ctypes.c_int64, vp]
     lib.paged_decode_noalloc.restype = ctypes.c_int
+    lib.paged_decode_contiguous.argtypes = lib.paged_decode.argtypes
+    lib.paged_decode_contiguous.restype = ctypes.c_int
     lib.paged_decode_noalloc_max_bytes.argtypes = []
     lib.paged_decode_noalloc_max_bytes.restype = sz
     lib.paged_kv_append.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, AttnTensor, AttnTensor,
@@ -494,35 +496,39 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                  softcap: float = 0.0) -> torch.Tensor:
     """O (B,Hq,D) of one query token per sequence against a paged cache (num_pages, page_size, Hkv, D)."""
+    return _decode_call("paged_decode", q, k_cache, v_cache, block_table, ctx_lens, scale, out, workspace, softcap)
+
+
+def paged_decode_contiguous(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, first_page: torch.Tensor,
+                            ctx_lens: torch.Tensor, max_pages_per_seq: int, scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            softcap: float = 0.0) -> torch.Tensor:
+    """paged_decode for caches whose sequences hold consecutive pages: logical page p of sequence b is
+    physical page first_page[b] + p (first_page (B,) int32); contexts are bounded by max_pages_per_seq."""
+    if first_page.dim() != 1:
+        raise ValueError("first_page must be (B,)")
+    return _decode_call("paged_decode_contiguous", q, k_cache, v_cache, first_page, ctx_lens, scale, out, workspace,
+                        softcap, max_pages=int(max_pages_per_seq))
+
+
+def _decode_call(fn, q, k_cache, v_cache, table, ctx_lens, scale, out, workspace, softcap, max_pages=None):
     lib = load_library()
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _half(t, n, q.dtype)
-    for t, n in ((block_table, "block_table"), (ctx_lens, "ctx_lens")):
-        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
-            raise TypeError(f"{n} must be a contiguous int32 device tensor")
-    B, Hq, D = q.shape
-    num_pages, page_size, Hkv, _ = k_cache.shape
-    shape = AttnDecodeShape(B, Hq, Hkv, D, page_size, num_pages, block_table.shape[1], _DT16[q.dtype])
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    out = torch.empty_like(q) if out is None else out
-    _expect(v_cache, tuple(k_cache.shape), "v_cache")
-    _expect(out, (B, Hq, D), "out")
-    _expect(ctx_lens, (B,), "ctx_lens")
-    if block_table.dim() != 2 or block_table.shape[0] != B:
-        raise ValueError(f"block_table must be (B, max_pages_per_seq), got {tuple(block_table.shape)}")
-    if k_cache.shape[3] != D:
-        raise ValueError("k_cache head_dim differs from q's")
+    if out is None:
+        out = torch.empty_like(q)
+    if max_pages is None:
+        shape, scale = _decode_args(q, k_cache, v_cache, table, ctx_lens, scale, out)
+    else:   # a (B,) first-page array in place of the table
+        shape, scale = _decode_args(q, k_cache, v_cache, table.view(-1, 1), ctx_lens, scale, out)
+        shape.max_pages_per_seq = max_pages
     nbytes = lib.paged_decode_workspace_bytes(ctypes.byref(shape))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
-    st = lib.paged_decode(ctypes.byref(shape), q.data_ptr(), q.stride(0), q.stride(1),
+    st = getattr(lib, fn)(ctypes.byref(shape), q.data_ptr(), q.stride(0), q.stride(1),
                           AttnTensor(k_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)),
                           AttnTensor(v_cache.data_ptr(), v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)),
-                          block_table.data_ptr(), ctx_lens.data_ptr(), float(scale), float(softcap), out.data_ptr(),
-                          out.stride(0),
+                          table.data_ptr(), ctx_lens.data_ptr(), scale, float(softcap), out.data_ptr(), out.stride(0),
                           out.stride(1), workspace.data_ptr(), nbytes, _stream())
-    _check(st, "paged_decode")
+    _check(st, fn)
     return out
 
 

@@ -418,11 +418,12 @@ attn_status debug_check_varlen(const Call& c, const int32_t* cu_seqlens, const u
   return bad ? ATTN_ERR_INVALID_ARG : ATTN_OK;
 }
 
-attn_status debug_check_pages(const attn_decode_shape& sh, const int32_t* table, const int32_t* ctx, hipStream_t s) {
+attn_status debug_check_pages(const attn_decode_shape& sh, const int32_t* table, const int32_t* ctx, hipStream_t s,
+                              int contiguous = 0) {
   if (!debug_on()) return ATTN_OK;
   bool bad = false;
-  attn_status st = hip_status(
-      attn::check_pages_meta(table, ctx, sh.B, sh.max_pages_per_seq, sh.page_size, sh.num_pages, s, bad));
+  attn_status st = hip_status(attn::check_pages_meta(table, contiguous, ctx, sh.B, sh.max_pages_per_seq, sh.page_size,
+                                                     sh.num_pages, s, bad));
   if (st != ATTN_OK) return st;
   return bad ? ATTN_ERR_INVALID_ARG : ATTN_OK;
 }
@@ -805,9 +806,9 @@ static attn_status check_decode(const attn_decode_shape* shape, const void* q, i
 static attn_status run_decode(const attn_decode_shape& sh, const void* q, int64_t q_stride_b, int64_t q_stride_h,
                               attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
                               const int32_t* ctx_lens, float scale, float softcap, void* o, int64_t o_stride_b,
-                              int64_t o_stride_h, void* workspace, void* stream) {
+                              int64_t o_stride_h, void* workspace, void* stream, int contiguous = 0) {
   attn_status st;
-  if ((st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream)))) return st;
+  if ((st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream), contiguous))) return st;
   const int r = sh.Hq / sh.Hkv;
 
   attn::DecodeArgs a = {};
@@ -819,6 +820,7 @@ static attn_status run_decode(const attn_decode_shape& sh, const void* q, int64_
   a.o = static_cast<__bf16*>(o);
   a.part = static_cast<float*>(workspace);
   a.f16 = sh.dtype == ATTN_DTYPE_F16;
+  a.contiguous = contiguous;
   a.q_sb = q_stride_b;
   a.q_sh = q_stride_h;
   a.o_sb = o_stride_b;
@@ -859,6 +861,22 @@ attn_status paged_decode(const attn_decode_shape* shape, const void* q, int64_t 
   if (shape->B == 0) return ATTN_OK;
   return run_decode(*shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale, softcap, o,
                     o_stride_b, o_stride_h, workspace, stream);
+}
+
+attn_status paged_decode_contiguous(const attn_decode_shape* shape, const void* q, int64_t q_stride_b,
+                                    int64_t q_stride_h, attn_tensor k_cache, attn_tensor v_cache,
+                                    const int32_t* first_page, const int32_t* ctx_lens, float scale, float softcap,
+                                    void* o, int64_t o_stride_b, int64_t o_stride_h, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  attn_status st = check_decode(shape, q, q_stride_b, q_stride_h, k_cache, v_cache, first_page, ctx_lens, scale,
+                                softcap, o, o_stride_b, o_stride_h);
+  if (st != ATTN_OK) return st;
+  const size_t need = paged_decode_workspace_bytes(shape);
+  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  if (shape->B == 0) return ATTN_OK;
+  return run_decode(*shape, q, q_stride_b, q_stride_h, k_cache, v_cache, first_page, ctx_lens, scale, softcap, o,
+                    o_stride_b, o_stride_h, workspace, stream, 1);
 }
 
 size_t paged_decode_noalloc_max_bytes(void) { return attn::kDecodeScratchBytes; }

@@ -116,11 +116,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
   // Physical pages of this wave's steps, fetched once: lane 2 s + pg holds page pg of step s.
   // A page past the context is replaced by the step's first page (its tokens are masked).
+  // Contiguous pages need no table row: page lp is the sequence's first page + lp.
   int tbl = 0;
   if (lane < 2 * nst) {
     const int tok0 = c * CH + (4 * (lane >> 1) + wave) * 32;
     const int lp = (tok0 + 16 * (lane & 1) < ctx) ? (tok0 >> 4) + (lane & 1) : (tok0 >> 4);
-    tbl = min(max(trow[lp], 0), a.num_pages - 1);
+    const int64_t id = a.contiguous ? (int64_t)a.table[b] + lp : (int64_t)trow[lp];
+    tbl = (int)min<int64_t>(max<int64_t>(id, 0), a.num_pages - 1);
   }
 
   // Staged rows are 256 bytes.  K: chunk ch of row r sits at chunk position ch ^ r, so the

@@ -108,6 +108,7 @@ struct DecodeArgs {
   float c;            // scale * log2(e)
   float sc_in, sc_out;  // softcap (see AttnArgs); unused without a cap
   int f16;            // 16-bit tensors are IEEE half (else bfloat16)
+  int contiguous;     // table holds one first page per sequence: logical page p of b is table[b] + p
 };
 
 // Paged KV copies (append: token tensor -> cache pages; gather: cache pages -> token tensor).
@@ -196,8 +197,8 @@ hipError_t launch_ds_seq_base(const int32_t* seq_len, int B, int Hq, int tri, in
 // Debug-mode metadata checks: synchronise the stream and set bad when the metadata is invalid.
 hipError_t check_varlen_meta(const uint8_t* pad_mask, const int32_t* cu_seqlens, int B, int S, int total,
                              hipStream_t stream, bool& bad);
-hipError_t check_pages_meta(const int32_t* table, const int32_t* ctx, int B, int max_pages, int page_size,
-                            int num_pages, hipStream_t stream, bool& bad);
+hipError_t check_pages_meta(const int32_t* table, int contiguous, const int32_t* ctx, int B, int max_pages,
+                            int page_size, int num_pages, hipStream_t stream, bool& bad);
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream);

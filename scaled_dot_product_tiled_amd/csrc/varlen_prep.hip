@@ -117,8 +117,9 @@ __global__ __launch_bounds__(256) void varlen_check_kernel(const uint8_t* pad_ma
   if (bad) g_meta_error = 1;
 }
 
-__global__ __launch_bounds__(256) void pages_check_kernel(const int32_t* table, const int32_t* ctx, int max_pages,
-                                                           int page_size, int num_pages) {
+// contiguous: table holds one first page per sequence, whose pages must lie inside the pool.
+__global__ __launch_bounds__(256) void pages_check_kernel(const int32_t* table, int contiguous, const int32_t* ctx,
+                                                           int max_pages, int page_size, int num_pages) {
   const int b = blockIdx.x;
   const int n = ctx[b];
   if (n < 0 || (int64_t)n > (int64_t)max_pages * page_size) {
@@ -126,6 +127,10 @@ __global__ __launch_bounds__(256) void pages_check_kernel(const int32_t* table, 
     return;
   }
   const int pages = (n + page_size - 1) / page_size;
+  if (contiguous) {
+    if (threadIdx.x == 0 && pages > 0 && (table[b] < 0 || (int64_t)table[b] + pages > num_pages)) g_meta_error = 1;
+    return;
+  }
   bool bad = false;
   for (int p = threadIdx.x; p < pages; p += 256) {
     const int id = table[(int64_t)b * max_pages + p];
@@ -159,11 +164,11 @@ hipError_t check_varlen_meta(const uint8_t* pad_mask, const int32_t* cu_seqlens,
   });
 }
 
-hipError_t check_pages_meta(const int32_t* table, const int32_t* ctx, int B, int max_pages, int page_size,
-                            int num_pages, hipStream_t stream, bool& bad) {
+hipError_t check_pages_meta(const int32_t* table, int contiguous, const int32_t* ctx, int B, int max_pages,
+                            int page_size, int num_pages, hipStream_t stream, bool& bad) {
   return run_check(stream, bad, [&] {
-    hipLaunchKernelGGL(pages_check_kernel, dim3(B), dim3(256), 0, stream, table, ctx, max_pages, page_size,
-                       num_pages);
+    hipLaunchKernelGGL(pages_check_kernel, dim3(B), dim3(256), 0, stream, table, contiguous, ctx, max_pages,
+                       page_size, num_pages);
   });
 }
 

@@ -149,3 +149,22 @@ def test_bad_paged_forward_metadata_is_rejected(debug_on, fault):
         run(table, ctx, cu, out=out)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), host_bits(ref))   # nothing was launched
+
+
+def test_contiguous_pages_leaving_the_pool_are_rejected(debug_on):
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=3, ctx_range=(10, 60))
+    inp = make_decode_inputs(w, seed=4)
+    q, kc, vc = (dev(inp[x]) for x in ("q", "k_cache", "v_cache"))
+    ctx = torch.from_numpy(inp["ctx_lens"]).to("cuda:0")
+    pages = -(-inp["ctx_lens"].astype(np.int64) // 16)
+    first = np.concatenate([[0], np.cumsum(pages)[:-1]]).astype(np.int32)
+    say("[debug] contiguous first pages")
+    mp = inp["block_table"].shape[1]
+    ref = sdpt.paged_decode_contiguous(q, kc, vc, torch.from_numpy(first).to("cuda:0"), ctx, mp, scale=w.scale)
+    bad = first.copy()
+    bad[2] = kc.shape[0] - int(pages[2]) + 1          # its last page is past the pool
+    out = ref.clone()
+    with pytest.raises(RuntimeError, match="status 1"):
+        sdpt.paged_decode_contiguous(q, kc, vc, torch.from_numpy(bad).to("cuda:0"), ctx, mp, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), host_bits(ref))

@@ -131,3 +131,45 @@ def test_chunks_merged_across_xcds(Hq, Hkv):
     assert max_abs(host(first), ref(inp, w.scale)) <= O_MAX_ABS
     for _ in range(3):
         assert np.array_equal(host_bits(run(inp, w.scale)), host_bits(first))
+
+
+def _in_order(inp, w):
+    """The same logical tokens moved so that every sequence's pages are consecutive in a new pool
+    (sequence after sequence, unused pages after them): caches, consecutive table, first pages."""
+    table, ctx = inp["block_table"], inp["ctx_lens"]
+    order, first = [], np.zeros(w.B, dtype=np.int32)
+    t2 = np.full_like(table, -1)
+    for b in range(w.B):
+        n = -(-int(ctx[b]) // w.page_size)
+        first[b] = len(order)
+        t2[b, :n] = np.arange(len(order), len(order) + n)
+        order += [int(p) for p in table[b, :n]]
+    used = set(order)
+    rest = [p for p in range(inp["k_cache"].shape[0]) if p not in used]
+    perm = np.array(order + rest)
+    return dict(inp, k_cache=inp["k_cache"][perm], v_cache=inp["v_cache"][perm], block_table=t2), first
+
+
+@pytest.mark.parametrize("B,ctx_range,softcap", [(64, (512, 4096), 0.0), (7, (1, 300), 0.0), (9, (0, 700), 15.0)])
+def test_contiguous_pages_equal_the_table_path_bit_for_bit(B, ctx_range, softcap):
+    """paged_decode_contiguous on consecutive pages gives the bytes paged_decode gives on the same
+    logical tokens through a permuted table (and through a consecutive one)."""
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=B, ctx_range=ctx_range)
+    inp = make_decode_inputs(w, seed=40)
+    cont, first = _in_order(inp, w)
+    print(f"[decode contiguous] B={B} ctx={ctx_range} softcap={softcap}", flush=True)
+    q = dev(inp["q"])
+    ctx = torch.from_numpy(inp["ctx_lens"]).to("cuda:0")
+    o_perm = sdpt.paged_decode(q, dev(inp["k_cache"]), dev(inp["v_cache"]),
+                               torch.from_numpy(inp["block_table"]).to("cuda:0"), ctx, scale=w.scale, softcap=softcap)
+    kc, vc = dev(cont["k_cache"]), dev(cont["v_cache"])
+    o_tab = sdpt.paged_decode(q, kc, vc, torch.from_numpy(cont["block_table"]).to("cuda:0"), ctx, scale=w.scale,
+                              softcap=softcap)
+    o_con = sdpt.paged_decode_contiguous(q, kc, vc, torch.from_numpy(first).to("cuda:0"), ctx,
+                                         inp["block_table"].shape[1], scale=w.scale, softcap=softcap)
+    torch.cuda.synchronize()
+    assert all_finite(o_con)
+    assert np.array_equal(host_bits(o_con), host_bits(o_perm))
+    assert np.array_equal(host_bits(o_con), host_bits(o_tab))
+    if B == 64:
+        assert max_abs(host(o_con), ref(inp, w.scale)) <= O_MAX_ABS

@@ -15,6 +15,8 @@ the C ABI.  Reported:
             bytes, rotating over two KV pools so the 256 MB last-level cache cannot serve repeats;
             pages_in_order is the same decode with each sequence's pages consecutive in the pool,
             through the table and through paged_decode_contiguous (first page per sequence, no table);
+            graph_replay replays the decode captured per batch bucket (DecodeGraphs) and gives the host
+            time per launch beside that of an eager call;
   other_workloads  (median and best of per-call HIP-event timings) forward / backward TFLOP/s of the
             tiny (B=1 S=128 D=512), sliding-window (D=256, W=1024) and padded varlen (B=8, lengths
             U{512..8192}, D=512) workloads, of one context-parallel rank's chunk pairs (16k tokens in
@@ -667,6 +669,27 @@ def main():
     torch.cuda.synchronize()
     tdc = time_calls(dec_contiguous, n_dec, stream)
     del cpools
+
+    # the decode replayed from captured graphs (one per batch bucket, DecodeGraphs) against eager
+    # calls: GPU time per step, and host time per launch
+    p0 = pools[0]
+    gr = sdpt.DecodeGraphs(p0["q"], p0["kc"], p0["vc"], p0["table"], p0["ctx"], outs[0], [1, 2, 4, 8, 16, 32, 64],
+                           scale=dw.scale)
+    torch.cuda.synchronize()
+    tgr = time_calls(lambda: gr.launch(dw.B), n_dec, stream)
+
+    def host_us(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        return (t1 - t0) / n * 1e6
+    graph_host = host_us(lambda: gr.launch(dw.B), n_dec)
+    eager_host = host_us(lambda: sdpt.paged_decode(p0["q"], p0["kc"], p0["vc"], p0["table"], p0["ctx"],
+                                                    scale=dw.scale, out=outs[0], workspace=ws), n_dec)
+    gr.close()
     rpd = rocprof_ms("decode_d128", "decode_split")
 
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
@@ -727,6 +750,9 @@ def main():
                                       "GB/s": round(dec_bytes / (tdo["mean"] * 1e-3) / 1e9, 1),
                                       "contiguous_call": {"ms": round(tdc["mean"], 4), "ms_best": round(tdc["best"], 4),
                                                           "GB/s": round(dec_bytes / (tdc["mean"] * 1e-3) / 1e9, 1)}},
+                   "graph_replay": {"ms": round(tgr["mean"], 4), "ms_best": round(tgr["best"], 4),
+                                    "host_us_per_launch": round(graph_host, 1),
+                                    "eager_host_us_per_call": round(eager_host, 1)},
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "bytes_per_launch": dec_bytes, "traffic": traffic_bytes("decode_split"),

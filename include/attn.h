@@ -367,6 +367,51 @@ attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens,
                             const int32_t* block_table, const int32_t* ctx_lens,
                             attn_tensor k_out, attn_tensor v_out, void* stream);
 
+/*
+ * Decode-step graphs per batch bucket: one captured HIP graph of a decode step (optionally the
+ * append of the current token's K/V, then paged_decode) for each batch size of a bucket list,
+ * all over the same fixed buffers and one shared workspace, so that a serving loop replays a
+ * graph instead of launching kernels (page "flex_attention + paged KV + CUDA graphs vs vLLM",
+ * Architecture notes: one graph per bucket in [1, 2, 4, 8, ..., max_bs]; section "What each
+ * option did": graph capture took that decode from about 420 to 4279 tokens/s).
+ *
+ * paged_decode_graphs_create
+ *   shape        sizes of the largest bucket: shape->B is the buffers' row count
+ *   buckets      host int32 (n_buckets): increasing batch sizes in [1, shape->B]
+ *   q, k_cache, v_cache, block_table, ctx_lens, scale, softcap, o and strides
+ *                as for paged_decode; the graphs keep these device addresses
+ *   k_new, v_new device (B, 1, Hkv, D) with attn_tensor strides: the current token's K and V,
+ *                appended by each replay before its decode (as paged_kv_append with n_tokens
+ *                = 1); k_new.ptr = v_new.ptr = NULL for a graph of the decode alone
+ *   workspace    at least paged_decode_workspace_bytes(shape) bytes, shared by every graph
+ *   stream       a created stream (not NULL) to capture on; nothing runs during creation
+ *   out          receives the graph set (free it with paged_decode_graphs_destroy)
+ * The graph of bucket n processes rows 0 .. n-1 of the buffers.  In debug mode the metadata is
+ * checked once, here.  Creating graphs allocates host and device memory (hipGraphInstantiate).
+ *
+ * paged_decode_graphs_launch: replays, on `stream`, the graph of the smallest bucket >= B
+ * (0 <= B <= largest bucket; B = 0 launches nothing) and stores that bucket in *bucket if
+ * bucket is not NULL.  Rows B .. bucket-1 are processed too: a caller gives them ctx_lens 0
+ * (their O is then 0 and nothing is appended for them) or ignores them.  The replay reads
+ * whatever the buffers hold when it runs.  Replays of one graph set share its workspace:
+ * overlapping replays (other streams) race.
+ */
+typedef struct attn_decode_graphs attn_decode_graphs;
+
+attn_status paged_decode_graphs_create(const attn_decode_shape* shape,
+                                       const int32_t* buckets, int32_t n_buckets,
+                                       const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                                       attn_tensor k_new, attn_tensor v_new,
+                                       attn_tensor k_cache, attn_tensor v_cache,
+                                       const int32_t* block_table, const int32_t* ctx_lens,
+                                       float scale, float softcap,
+                                       void* o, int64_t o_stride_b, int64_t o_stride_h,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       attn_decode_graphs** out);
+attn_status paged_decode_graphs_launch(const attn_decode_graphs* graphs, int32_t B, void* stream,
+                                       int32_t* bucket);
+void paged_decode_graphs_destroy(attn_decode_graphs* graphs);
+
 /* Sizes of one paged prefill call.
  *   B                 sequences
  *   max_q             most new query rows of one sequence

@@ -62,7 +62,8 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read", "attn_count_restarts", "paged_decode_noalloc",
-           "paged_decode_noalloc_max_bytes", "attn_peak_probe", "attn_fwd_paged", "paged_decode_contiguous")
+           "paged_decode_noalloc_max_bytes", "attn_peak_probe", "attn_fwd_paged", "paged_decode_contiguous",
+           "paged_decode_graphs_create", "paged_decode_graphs_launch", "paged_decode_graphs_destroy")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -110,6 +111,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_decode_noalloc.restype = ctypes.c_int
     lib.paged_decode_contiguous.argtypes = lib.paged_decode.argtypes
     lib.paged_decode_contiguous.restype = ctypes.c_int
+    lib.paged_decode_graphs_create.argtypes = [P(AttnDecodeShape), vp, ctypes.c_int32, vp, ctypes.c_int64,
+                                               ctypes.c_int64, AttnTensor, AttnTensor, AttnTensor, AttnTensor, vp, vp,
+                                               ctypes.c_float, ctypes.c_float, vp, ctypes.c_int64, ctypes.c_int64, vp,
+                                               sz, vp, P(vp)]
+    lib.paged_decode_graphs_create.restype = ctypes.c_int
+    lib.paged_decode_graphs_launch.argtypes = [vp, ctypes.c_int32, vp, P(ctypes.c_int32)]
+    lib.paged_decode_graphs_launch.restype = ctypes.c_int
+    lib.paged_decode_graphs_destroy.argtypes = [vp]
+    lib.paged_decode_graphs_destroy.restype = None
     lib.paged_decode_noalloc_max_bytes.argtypes = []
     lib.paged_decode_noalloc_max_bytes.restype = sz
     lib.paged_kv_append.argtypes = [P(AttnDecodeShape), ctypes.c_int32, AttnTensor, AttnTensor, AttnTensor, AttnTensor,
@@ -530,6 +540,60 @@ def _decode_call(fn, q, k_cache, v_cache, table, ctx_lens, scale, out, workspace
                           out.stride(1), workspace.data_ptr(), nbytes, _stream())
     _check(st, fn)
     return out
+
+
+class DecodeGraphs:
+    """Captured decode steps, one HIP graph per batch bucket (paged_decode_graphs_create), over fixed
+    buffers: q (Bmax,Hq,D), caches, block_table (Bmax, max_pages), ctx_lens (Bmax,), out (Bmax,Hq,D)
+    and, when given, the current token's k_new / v_new (Bmax,1,Hkv,D) appended before each decode.
+    launch(B) replays the smallest bucket >= B on the current stream and returns that bucket.  The
+    tensors are kept referenced so the captured addresses stay valid."""
+
+    def __init__(self, q, k_cache, v_cache, block_table, ctx_lens, out, buckets, scale=None, softcap=0.0,
+                 k_new=None, v_new=None, stream=None):
+        lib = load_library()
+        shape, scale = _decode_args(q, k_cache, v_cache, block_table, ctx_lens, scale, out)
+        if (k_new is None) != (v_new is None):
+            raise ValueError("k_new and v_new go together")
+        if k_new is not None:
+            for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+                _half(t, n, q.dtype)
+                _expect(t, (shape.B, 1, shape.Hkv, shape.D), n)
+        nbytes = lib.paged_decode_workspace_bytes(ctypes.byref(shape))
+        self.workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+        self._keep = (q, k_cache, v_cache, block_table, ctx_lens, out, k_new, v_new)
+        self.buckets = [int(b) for b in buckets]
+        arr = (ctypes.c_int32 * len(self.buckets))(*self.buckets)
+        handle = ctypes.c_void_p()
+        none = AttnTensor(None, 0, 0, 0)
+        s = stream if stream is not None else torch.cuda.Stream()
+        self._stream = s
+        st = lib.paged_decode_graphs_create(
+            ctypes.byref(shape), arr, len(self.buckets), q.data_ptr(), q.stride(0), q.stride(1),
+            _tensor(k_new, False) if k_new is not None else none, _tensor(v_new, False) if v_new is not None else none,
+            AttnTensor(k_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)),
+            AttnTensor(v_cache.data_ptr(), v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)),
+            block_table.data_ptr(), ctx_lens.data_ptr(), scale, float(softcap), out.data_ptr(), out.stride(0),
+            out.stride(1), self.workspace.data_ptr(), nbytes, s.cuda_stream, ctypes.byref(handle))
+        _check(st, "paged_decode_graphs_create")
+        self._handle = handle
+
+    def launch(self, B: int) -> int:
+        bucket = ctypes.c_int32(0)
+        _check(load_library().paged_decode_graphs_launch(self._handle, int(B), _stream(), ctypes.byref(bucket)),
+               "paged_decode_graphs_launch")
+        return bucket.value
+
+    def close(self) -> None:
+        if self._handle is not None and self._handle.value:
+            load_library().paged_decode_graphs_destroy(self._handle)
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _paged_shape(k_cache, block_table, B, D, dtype):

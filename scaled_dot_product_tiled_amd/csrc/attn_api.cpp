@@ -722,7 +722,8 @@ attn_status attn_lse_merge(int32_t B, int32_t S, int32_t H, int32_t D, attn_tens
 // Shared checks and arguments of paged_kv_append and paged_kv_gather.
 static attn_status paged_copy(const attn_decode_shape* shape, int32_t n, attn_tensor k_tok, attn_tensor v_tok,
                               attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
-                              const int32_t* ctx_lens, int gather, const char* name, void* stream) {
+                              const int32_t* ctx_lens, int gather, const char* name, void* stream,
+                              bool meta_check = true) {
   if (shape == nullptr) return ATTN_ERR_INVALID_ARG;
   const attn_decode_shape& sh = *shape;
   if (sh.B < 0 || n < 0 || sh.Hkv <= 0 || sh.num_pages <= 0 || sh.max_pages_per_seq <= 0 || sh.page_size <= 0)
@@ -736,7 +737,7 @@ static attn_status paged_copy(const attn_decode_shape* shape, int32_t n, attn_te
       (st = check_tensor(v_cache, false)))
     return st;
   if (sh.B == 0 || n == 0) return ATTN_OK;
-  if ((st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream)))) return st;
+  if (meta_check && (st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream)))) return st;
   attn::PagedCopyArgs a = {};
   a.tk = static_cast<__bf16*>(k_tok.ptr);
   a.tv = static_cast<__bf16*>(v_tok.ptr);
@@ -806,9 +807,12 @@ static attn_status check_decode(const attn_decode_shape* shape, const void* q, i
 static attn_status run_decode(const attn_decode_shape& sh, const void* q, int64_t q_stride_b, int64_t q_stride_h,
                               attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
                               const int32_t* ctx_lens, float scale, float softcap, void* o, int64_t o_stride_b,
-                              int64_t o_stride_h, void* workspace, void* stream, int contiguous = 0) {
+                              int64_t o_stride_h, void* workspace, void* stream, int contiguous = 0,
+                              bool meta_check = true) {
   attn_status st;
-  if ((st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream), contiguous))) return st;
+  if (meta_check &&
+      (st = debug_check_pages(sh, block_table, ctx_lens, static_cast<hipStream_t>(stream), contiguous)))
+    return st;
   const int r = sh.Hq / sh.Hkv;
 
   attn::DecodeArgs a = {};
@@ -894,6 +898,101 @@ attn_status paged_decode_noalloc(const attn_decode_shape* shape, const void* q, 
   if ((st = hip_status(attn::decode_scratch(&scratch)))) return st;
   return run_decode(*shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale, softcap, o,
                     o_stride_b, o_stride_h, scratch, stream);
+}
+
+}  // extern "C"
+
+// One captured decode step per batch bucket (paged_decode_graphs_*).
+struct attn_decode_graphs {
+  std::vector<int32_t> buckets;
+  std::vector<hipGraph_t> graphs;
+  std::vector<hipGraphExec_t> execs;
+};
+
+namespace {
+
+void destroy_graphs(attn_decode_graphs* g) {
+  for (hipGraphExec_t e : g->execs) (void)hipGraphExecDestroy(e);
+  for (hipGraph_t gr : g->graphs) (void)hipGraphDestroy(gr);
+  delete g;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status paged_decode_graphs_create(const attn_decode_shape* shape, const int32_t* buckets, int32_t n_buckets,
+                                       const void* q, int64_t q_stride_b, int64_t q_stride_h, attn_tensor k_new,
+                                       attn_tensor v_new, attn_tensor k_cache, attn_tensor v_cache,
+                                       const int32_t* block_table, const int32_t* ctx_lens, float scale, float softcap,
+                                       void* o, int64_t o_stride_b, int64_t o_stride_h, void* workspace,
+                                       size_t workspace_bytes, void* stream, attn_decode_graphs** out) {
+  if (out == nullptr) return ATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  attn_status st = check_decode(shape, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale,
+                                softcap, o, o_stride_b, o_stride_h);
+  if (st != ATTN_OK) return st;
+  if (stream == nullptr || buckets == nullptr || n_buckets <= 0 || shape->B <= 0) return ATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < n_buckets; ++i)
+    if (buckets[i] < 1 || buckets[i] > shape->B || (i > 0 && buckets[i] <= buckets[i - 1])) return ATTN_ERR_INVALID_ARG;
+  const bool append = k_new.ptr != nullptr || v_new.ptr != nullptr;
+  if (append && ((st = check_tensor(k_new, false)) || (st = check_tensor(v_new, false)))) return st;
+  const size_t need = paged_decode_workspace_bytes(shape);
+  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // metadata is checked once, here (a check synchronises, which a capture cannot)
+  if ((st = debug_check_pages(*shape, block_table, ctx_lens, s))) return st;
+
+  attn_decode_graphs* g = new attn_decode_graphs();
+  const bool prof = g_prof.on;
+  g_prof.on = false;  // no timing events inside the graphs
+  for (int i = 0; i < n_buckets && st == ATTN_OK; ++i) {
+    attn_decode_shape sb = *shape;
+    sb.B = buckets[i];
+    hipGraph_t graph = nullptr;
+    st = hip_status(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    if (st != ATTN_OK) break;
+    attn_status run = ATTN_OK;
+    if (append)
+      run = paged_copy(&sb, 1, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, 0, "paged_kv_append", stream,
+                       false);
+    if (run == ATTN_OK)
+      run = run_decode(sb, q, q_stride_b, q_stride_h, k_cache, v_cache, block_table, ctx_lens, scale, softcap, o,
+                       o_stride_b, o_stride_h, workspace, stream, 0, false);
+    const hipError_t end = hipStreamEndCapture(s, &graph);
+    st = run != ATTN_OK ? run : hip_status(end);
+    if (graph != nullptr) g->graphs.push_back(graph);
+    if (st != ATTN_OK) break;
+    hipGraphExec_t exec = nullptr;
+    st = hip_status(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+    if (st == ATTN_OK) {
+      g->execs.push_back(exec);
+      g->buckets.push_back(buckets[i]);
+    }
+  }
+  g_prof.on = prof;
+  if (st != ATTN_OK) {
+    destroy_graphs(g);
+    return st;
+  }
+  *out = g;
+  return ATTN_OK;
+}
+
+attn_status paged_decode_graphs_launch(const attn_decode_graphs* graphs, int32_t B, void* stream,
+                                       int32_t* bucket) {
+  if (graphs == nullptr || B < 0 || B > graphs->buckets.back()) return ATTN_ERR_INVALID_ARG;
+  if (bucket != nullptr) *bucket = 0;
+  if (B == 0) return ATTN_OK;
+  size_t i = 0;
+  while (graphs->buckets[i] < B) ++i;
+  if (bucket != nullptr) *bucket = graphs->buckets[i];
+  return hip_status(hipGraphLaunch(graphs->execs[i], static_cast<hipStream_t>(stream)));
+}
+
+void paged_decode_graphs_destroy(attn_decode_graphs* graphs) {
+  if (graphs != nullptr) destroy_graphs(graphs);
 }
 
 attn_status paged_kv_append(const attn_decode_shape* shape, int32_t n_tokens, attn_tensor k_new, attn_tensor v_new,

@@ -309,3 +309,58 @@ def test_mixed_step_full_size_sampled_rows():
         worst_l = max(worst_l, max_abs(lh[:, t], rl[0, :, 0]))
     say(f"[mixed step full size] rows={len(rows)} O max-abs {worst_o:.3g} LSE max-abs {worst_l:.3g}")
     assert worst_o <= O_MAX_ABS and worst_l <= LSE_MAX_ABS
+
+
+def test_decode_graphs_per_bucket_replay_like_eager_calls():
+    """One captured decode step (append the current token's K/V, then decode) per bucket [1, 2, 4,
+    ..., 64], over one set of buffers and one shared workspace (DecodeGraphs).  For a sequence of
+    batch sizes, the smallest bucket >= B is replayed with rows B .. bucket-1 as padding (context
+    0); each replay equals the same step made with eager calls on the B rows bit for bit (output
+    and caches), its padding rows are exact zeros, and the output is within tolerance of the
+    oracle."""
+    w = DECODE_WORKLOADS["decode_d128"].scaled(ctx_range=(20, 700))    # B = 64 rows, shorter contexts
+    inp = make_decode_inputs(w, seed=50)
+    sizes = [1, 3, 8, 17, 64, 40, 3, 64]
+    table, kc, vc, _ = _with_room(inp, w, len(sizes))
+    cur = inp["ctx_lens"].astype(np.int32).copy()
+    k_d, v_d = dev(kc), dev(vc)
+    k_e, v_e = k_d.clone(), v_d.clone()
+    t_d = torch.from_numpy(table).to("cuda:0")
+    q_s = torch.zeros((w.B, w.Hq, w.D), device="cuda:0", dtype=torch.bfloat16)
+    kn_s = torch.zeros((w.B, 1, w.Hkv, w.D), device="cuda:0", dtype=torch.bfloat16)
+    vn_s = torch.zeros_like(kn_s)
+    ctx_s = torch.zeros(w.B, device="cuda:0", dtype=torch.int32)
+    out_s = torch.zeros_like(q_s)
+    buckets = [1, 2, 4, 8, 16, 32, 64]
+    g = sdpt.DecodeGraphs(q_s, k_d, v_d, t_d, ctx_s, out_s, buckets, scale=w.scale, k_new=kn_s, v_new=vn_s)
+    torch.cuda.synchronize()
+    kc_ref, vc_ref = bits_to_f64(kc, "bf16"), bits_to_f64(vc, "bf16")
+    ws = torch.empty(1 << 24, device="cuda:0", dtype=torch.uint8)
+    for i, B in enumerate(sizes):
+        cur[:B] += 1
+        ctx = np.where(np.arange(w.B) < B, cur, 0).astype(np.int32)
+        q_s.copy_(dev(normal_16(stream(60 + i, w.wid, 0), (w.B, w.Hq, w.D))))
+        kn_s.copy_(dev(normal_16(stream(60 + i, w.wid, 1), (w.B, 1, w.Hkv, w.D))))
+        vn_s.copy_(dev(normal_16(stream(60 + i, w.wid, 2), (w.B, 1, w.Hkv, w.D))))
+        ctx_s.copy_(torch.from_numpy(ctx).to("cuda:0"))
+        out_s.fill_(1.0)
+        torch.cuda.synchronize()
+        say(f"[decode graphs] step {i} B={B}")
+        bucket = g.launch(B)
+        assert bucket == min(b for b in buckets if b >= B)
+        torch.cuda.synchronize()
+        got = out_s.clone()
+        # the same step with eager calls on B rows and other caches
+        tb, cb = t_d[:B].contiguous(), ctx_s[:B].contiguous()
+        sdpt.paged_kv_append(kn_s[:B].contiguous(), vn_s[:B].contiguous(), k_e, v_e, tb, cb)
+        eager = sdpt.paged_decode(q_s[:B].contiguous(), k_e, v_e, tb, cb, scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(got[:B]), host_bits(eager)), i
+        assert not host_bits(got[B:bucket]).any(), i                      # padding rows: O = 0
+        assert np.array_equal(host_bits(k_d), host_bits(k_e)) and np.array_equal(host_bits(v_d), host_bits(v_e)), i
+        kc_ref = oracle.paged_append(kc_ref, table[:B], ctx[:B], host(kn_s[:B]), w.page_size)
+        vc_ref = oracle.paged_append(vc_ref, table[:B], ctx[:B], host(vn_s[:B]), w.page_size)
+        ref = oracle.paged_decode(host(q_s[:B]), kc_ref, vc_ref, table[:B], ctx[:B], w.scale, w.page_size)
+        assert all_finite(got[:B])
+        assert max_abs(host(got[:B]), ref) <= O_MAX_ABS, i
+    g.close()

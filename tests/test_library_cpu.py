@@ -281,6 +281,31 @@ def test_paged_prefill_checks():
     assert lib.attn_last_hip_error() == 0
 
 
+def test_decode_graph_checks():
+    """paged_decode_graphs_create refuses bad buckets, a NULL stream and a small workspace before
+    any capture; launch refuses a missing graph set."""
+    lib = load_library()
+    d = AttnDecodeShape(8, 32, 8, 128, 16, 100, 8)
+    kc = AttnTensor(0x10000, 16 * 8 * 128, 8 * 128, 128)
+    none = AttnTensor(None, 0, 0, 0)
+    need = lib.paged_decode_workspace_bytes(ctypes.byref(d))
+
+    def create(buckets=(1, 2, 4, 8), stream=0x1234, ws=0x40000, nbytes=need, out=True):
+        arr = (ctypes.c_int32 * len(buckets))(*buckets)
+        h = ctypes.c_void_p()
+        return lib.paged_decode_graphs_create(ctypes.byref(d), arr, len(buckets), 0x20000, 32 * 128, 128, none, none,
+                                              kc, kc, 0x3000, 0x4000, 0.1, 0.0, 0x50000, 32 * 128, 128, ws, nbytes,
+                                              stream, ctypes.byref(h) if out else None)
+    assert create(out=False) == INVALID
+    assert create(buckets=(2, 1)) == INVALID and create(buckets=(0, 4)) == INVALID and create(buckets=(4, 9)) == INVALID
+    assert create(stream=0) == INVALID
+    assert create(ws=0) == WORKSPACE and create(nbytes=need - 1) == WORKSPACE
+    b = ctypes.c_int32(-1)
+    assert lib.paged_decode_graphs_launch(None, 1, None, ctypes.byref(b)) == INVALID
+    lib.paged_decode_graphs_destroy(None)
+    assert lib.attn_last_hip_error() == 0
+
+
 def test_debug_mode_switch():
     """attn_debug sets the process-wide metadata-check mode and returns the previous one (no GPU
     call is made by the switch itself)."""

@@ -105,11 +105,14 @@ __device__ __forceinline__ void dma_stats(float* dst, const float* lse_row0, con
 // dK, dV
 // ---------------------------------------------------------------------------
 template <int D, bool SOFTCAP, bool F16>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NK = kDkdvKeys;   // 64 keys per workgroup
-  // query rows per step: RB blocks of 32 (two at head_dim 256, so that a step's tiles are as
-  // large as at 512 and the per-step work is the same)
-  constexpr int RB = D == 256 ? 2 : 1;
+  // query rows per step: one block of 32.  At head_dim 256 two workgroups share a compute unit
+  // (LOWREG: 256 registers and 74 KB of LDS each), so that one's softmax, exchange and barriers
+  // overlap the other's matrix work.
+  constexpr int RB = 1;
+  constexpr bool LOWREG = D == 256;
+  constexpr bool DMA_EARLY = false;
   constexpr int MQ = 32 * RB;
   constexpr int KS = D / 16;
   constexpr int DBW = D / 128;    // 32-wide d blocks owned by each wave
@@ -183,8 +186,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
         kv[t] = ok ? x : zero_bf16x8();
       }
     }
-    const RowFrags<D> rowf(lane);
-    const TrFrags<D> trf(lane);
     const float c = a.c;
 
     // Step k = (query tile, head), query tiles from the last one down and heads innermost:
@@ -243,26 +244,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+      // At head_dim 256 the lane index is re-read each step (an opaque copy), so that the LDS
+      // fragment bases and the copies' lane offsets are recomputed in the loop instead of being
+      // kept live across it.
+      int dlane = lane;
+      if constexpr (LOWREG) asm volatile("v_mov_b32 %0, %1" : "=v"(dlane) : "v"(lane));
+      const RowFrags<D> rowf(dlane);
+      const TrFrags<D> trf(dlane);
+      // the transposing-read bases of this wave's d blocks dsl .. dsl + DBW - 1
+      int tlo[DBW], thi[DBW];
+#pragma unroll
+      for (int d = 0; d < DBW; ++d) trf.pick(dsl + d, tlo[d], thi[d]);
       {
         const bf16* src = score_wave ? Qs[buf] : dOs[buf];
-        bf16x8 f[RB][4];
+        // fragments read PF steps ahead (fewer at head_dim 256, whose two workgroups per
+        // compute unit hide each other's LDS latency within half the registers)
+        constexpr int PF = LOWREG ? 1 : 3;
+        bf16x8 f[RB][PF + 1];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int t = 0; t < 3; ++t) f[rb][t] = rowf.read(src, 32 * rb, t);
+          for (int t = 0; t < PF; ++t) f[rb][t] = rowf.read(src, 32 * rb, t);
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            if (t + 3 < KS) f[rb][(t + 3) % 4] = rowf.read(src, 32 * rb, t + 3);
-            sacc[rb] = E16<F16>::mma32(f[rb][t % 4], kv[t], sacc[rb]);
+            if (t + PF < KS) f[rb][(t + PF) % (PF + 1)] = rowf.read(src, 32 * rb, t + PF);
+            sacc[rb] = E16<F16>::mma32(f[rb][t % (PF + 1)], kv[t], sacc[rb]);
+            // copy slots: one every two matrix instructions, or (DMA_EARLY) all at the first ones
             const int slot = t * RB + rb;
-            if ((slot & 1) == 0 && slot / 2 < 2 * NDMA) {
-              const int j = slot / 2;
+            if (DMA_EARLY ? slot < 2 * NDMA : ((slot & 1) == 0 && slot / 2 < 2 * NDMA)) {
+              const int j = DMA_EARLY ? slot : slot / 2;
               if (j < NDMA)
-                dma_rows_one<D, MQ, 4>(Qs[buf ^ 1], qn, wave, lane, j);
+                dma_rows_one<D, MQ, 4>(Qs[buf ^ 1], qn, wave, dlane, j);
               else
-                dma_rows_one<D, MQ, 4>(dOs[buf ^ 1], dn, wave, lane, j - NDMA);
+                dma_rows_one<D, MQ, 4>(dOs[buf ^ 1], dn, wave, dlane, j - NDMA);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -389,9 +405,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
       }
       barrier_lds();
       if (has_next) stats(son, i0n, buf ^ 1);
-      {
+      if constexpr (LOWREG) {
+        // one 16-row half at a time: its P and dS fragments, then per d block the transposed
+        // dO and Q fragments and the four products
+#pragma unroll
+        for (int s = 0; s < 2 * RB; ++s) {
+          bf16x8 pfr[4];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const bf16x8* src = reinterpret_cast<const bf16x8*>(&xch[s >> 1][x][s & 1][0][0]);
+            pfr[x] = src[lane];           // P, key block x
+            pfr[2 + x] = src[64 + lane];  // dS, key block x
+          }
+#pragma unroll
+          for (int d = 0; d < DBW; ++d) {
+            const bf16x8 ado = trf.read_with(dOs[buf], 16 * s, dsl + d, tlo[d], thi[d]);
+            const bf16x8 aq = trf.read_with(Qs[buf], 16 * s, dsl + d, tlo[d], thi[d]);
+            dvacc[0][d] = E16<F16>::mma32(ado, pfr[0], dvacc[0][d]);
+            dvacc[1][d] = E16<F16>::mma32(ado, pfr[1], dvacc[1][d]);
+            dkacc[0][d] = E16<F16>::mma32(aq, pfr[2], dkacc[0][d]);
+            dkacc[1][d] = E16<F16>::mma32(aq, pfr[3], dkacc[1][d]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
         // the transposed fragments of (s, d) are read one (s, d) step ahead of their products
-        bf16x8 ado = trf.read(dOs[buf], 0, dsl), aq = trf.read(Qs[buf], 0, dsl);
+        bf16x8 ado = trf.read_with(dOs[buf], 0, dsl, tlo[0], thi[0]), aq = trf.read_with(Qs[buf], 0, dsl, tlo[0], thi[0]);
         // every 16-row half's P and dS fragments are read before the first products
         bf16x8 pfr[2 * RB][4];
 #pragma unroll
@@ -412,8 +451,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a) {
             const int ns = d + 1 == DBW ? s + 1 : s, nd = d + 1 == DBW ? 0 : d + 1;
             bf16x8 ado_n = ado, aq_n = aq;
             if (ns < 2 * RB) {
-              ado_n = trf.read(dOs[buf], 16 * ns, dsl + nd);
-              aq_n = trf.read(Qs[buf], 16 * ns, dsl + nd);
+              ado_n = trf.read_with(dOs[buf], 16 * ns, dsl + nd, tlo[nd], thi[nd]);
+              aq_n = trf.read_with(Qs[buf], 16 * ns, dsl + nd, tlo[nd], thi[nd]);
             }
             dvacc[0][d] = E16<F16>::mma32(ado, p0, dvacc[0][d]);
             dvacc[1][d] = E16<F16>::mma32(ado, p1, dvacc[1][d]);

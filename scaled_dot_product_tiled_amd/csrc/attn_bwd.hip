@@ -197,18 +197,28 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
     // at the top of the step.
     const int tq_last = tq0 + nq - 1;
     static_assert(2 * NDMA <= KS * RB / 2, "every copy needs a slot in the S / dP loop");
-    int hi = 0, qi = 0;  // step k
+    // Row tiles are visited from the last one down (heads innermost).  With a window every key
+    // tile sees the same number nq of row tiles, each key tile's range two tiles above its
+    // neighbour's, so a plain top-down visit would have the workgroups of a unit read tiles
+    // spread over the whole sequence at every step.  Instead the visit starts at a rotated tile
+    // and wraps from the first tile to the last: step k then reads an absolute tile congruent to
+    // -k/rs modulo nq in every workgroup, a handful of distinct tiles that the XCD's L2 serves.
+    // Without a window every key tile's range ends at the same last tile and the plain visit
+    // already keeps the workgroups together.
+    const int phase = a.window > 0 ? tq_last % nq : 0;
+    int tcur = tq_last - phase;  // row tile of step k
+    int hi = 0;                  // head of step k
     // Addresses of step k: Q and dO at (row i0, head hb0 + hi), the row statistics and the dS
     // blocks of that head.  A step advances one head, or after the group's last head returns
-    // to head hb0 one query tile lower, so each moves by one of two fixed amounts.
-    const int i00 = tq_last * MQ;
+    // to head hb0 one query tile lower (or, at the wrap, to the last tile).
+    const int i00 = tcur * MQ;
     const bf16* qrow = a.q + b * a.q_sb + (int64_t)(off + i00) * a.q_ss + hb0 * a.q_sh;
     const bf16* drow = a.dout + b * a.do_sb + (int64_t)(off + i00) * a.do_ss + hb0 * a.do_sh;
     int64_t so = b * a.st_sb + hb0 * a.st_sh + off;
     const int64_t ds_hb = a.ds_seq ? ds_head_blocks(len, a.ds_tri, a.ds_cnt) : a.ds_head;
     bf16* dshead = a.dsb + ((a.ds_seq ? ds_b : (int64_t)b * a.Hq * ds_hb) + (int64_t)hb0 * ds_hb) * kDsBlockElems;
-    const int64_t q_wrap = -(int64_t)(rs - 1) * a.q_sh - (int64_t)MQ * a.q_ss;
-    const int64_t d_wrap = -(int64_t)(rs - 1) * a.do_sh - (int64_t)MQ * a.do_ss;
+    const int64_t q_back = -(int64_t)(rs - 1) * a.q_sh;  // from the last head back to the first
+    const int64_t d_back = -(int64_t)(rs - 1) * a.do_sh;
     const int64_t s_wrap = -(int64_t)(rs - 1) * a.st_sh;
     const int64_t ds_step = ds_hb * kDsBlockElems;
     int ds_qt = -1;  // query tile of the dS block index ds_bi (of this wave's key block)
@@ -225,13 +235,15 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
     stats(so, i00, 0);
     for (int k = 0; k < nsteps; ++k) {
       const int buf = k & 1;
-      const int i0 = (tq_last - qi) * MQ;
+      const int i0 = tcur * MQ;
       const bool wrap = hi + 1 == rs;                    // step k+1
       const int hn = wrap ? 0 : hi + 1;
-      const int i0n = wrap ? i0 - MQ : i0;
+      const int tn = wrap ? (tcur == tq0 ? tq_last : tcur - 1) : tcur;
+      const int i0n = tn * MQ;
+      const int64_t rmove = (int64_t)(i0n - i0);         // rows moved at a wrap
       const bool has_next = k + 1 < nsteps;
-      const bf16* qrn = qrow + (wrap ? q_wrap : a.q_sh);
-      const bf16* drn = drow + (wrap ? d_wrap : a.do_sh);
+      const bf16* qrn = qrow + (wrap ? q_back + rmove * a.q_ss : a.q_sh);
+      const bf16* drn = drow + (wrap ? d_back + rmove * a.do_ss : a.do_sh);
       const int64_t son = so + (wrap ? s_wrap : a.st_sh);
       // the last step copies nothing real: an empty range reads zeros into the idle buffers
       const TileSrc qn = tile_src_rows<MQ>(qrn, a.q_ss, has_next ? len - i0n : 0);
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
           }
         }
       }
-      qi += wrap;
+      tcur = tn;
       hi = hn;
       qrow = qrn;
       drow = drn;

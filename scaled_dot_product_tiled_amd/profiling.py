@@ -128,7 +128,8 @@ def trace_durations(d: str) -> Dict[str, List[float]]:
 
 def stats_table(d: str) -> str:
     """Per-kernel table of a --kernel-trace --stats output: calls, mean, median (from the trace),
-    min, max and share of the total time."""
+    min, max and share of the total time, for the library's kernels (the run's other kernels,
+    torch's input generation and copies, are summed in one line)."""
     rows = []
     for f in _csvs(d, "_kernel_stats.csv"):
         with open(f) as fh:
@@ -136,11 +137,16 @@ def stats_table(d: str) -> str:
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     dur = trace_durations(d)
     lines = [f"{'calls':>6} {'avg_us':>10} {'med_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    other = [r for r in rows if "attn::" not in r["Name"]]
+    rows = [r for r in rows if "attn::" in r["Name"]]
     for r in rows:
         med = float(np.median(dur[r["Name"]])) / 1e3 if r["Name"] in dur else float("nan")
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {med:10.2f} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}  "
                      f"{r['Name']}")
+    if other:
+        lines.append(f"{sum(int(r['Calls']) for r in other):6d} launches of {len(other)} other kernels (input "
+                     f"generation, copies): {sum(float(r['Percentage']) for r in other):.2f}% of the time")
     return "\n".join(lines)
 
 
@@ -163,7 +169,8 @@ SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FU
 N_XCD, N_CU, N_SIMD = 8, 256, 1024
 
 # source file of each kernel family (for the sha256 a traffic record carries)
-SOURCES = (("fwd_kernel<", "attn_fwd.hip"), ("fwd_merge_kernel<", "attn_fwd.hip"), ("bwd_", "attn_bwd.hip"),
+SOURCES = (("fwd_kernel<", "attn_fwd.hip"), ("fwd_merge_kernel<", "attn_fwd.hip"), ("fwd_paged_kernel<", "attn_fwd.hip"),
+           ("bwd_", "attn_bwd.hip"),
            ("decode_", "attn_decode.hip"), ("varlen_", "varlen_prep.hip"), ("ds_seq_base", "varlen_prep.hip"),
            ("lse_merge", "attn_merge.hip"), ("paged_kv", "paged_kv.hip"))
 

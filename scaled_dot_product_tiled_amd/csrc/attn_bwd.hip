@@ -679,8 +679,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
   constexpr int DBW = D / (32 * NW);  // 32-wide d blocks per wave
   constexpr int RB = M / 32;          // 32-row blocks
   static_assert(DBW >= 1 && DBW * 32 * NW == D, "head_dim must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][NK * D];
-  __shared__ __attribute__((aligned(1024))) bf16 Ss[2][NK * M];
+  // A step's two blocks are copied NBUF - 1 steps ahead: its own matrix work is short against
+  // the memory latency of a dS block (written by the dK/dV pass, read once here).
+  constexpr int NBUF = 3;
+  constexpr int NCOPY = NK * D / 512 / NW + (NK / (64 / (M / 8))) / NW;  // copies per wave and block
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[NBUF][NK * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Ss[NBUF][NK * M];
 
   const int item = xcd_item(a.per_xcd, a.total_items, a.nqt * a.r * NSPLIT, a.balanced, a.order, a.Hkv);
   if (item < 0) return;
@@ -739,17 +743,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < DBW; ++d) trk.pick(dsl + d, klo[d], khi[d]);
 
-    dma_rows<D, NK, NW>(Ks[0], tile_src<NK>(kbase, a.k_ss, kb_first * NK, lenk - kb_first * NK), wave, lane);
-    dma_ds_block<NW>(Ss[0], tile_src<NK>(sblock(kb_first), M, 0, NK), wave, lane);
+    auto copy_block = [&](int kb, int buf) {
+      dma_rows<D, NK, NW>(Ks[buf], tile_src<NK>(kbase, a.k_ss, kb * NK, lenk - kb * NK), wave, lane);
+      dma_ds_block<NW>(Ss[buf], tile_src<NK>(sblock(kb), M, 0, NK), wave, lane);
+    };
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+      if (kb_first + i <= kb_last) copy_block(kb_first + i, i);
+    int buf = 0;
     for (int kb = kb_first; kb <= kb_last; ++kb) {
-      const int buf = (kb - kb_first) & 1;
       const int j0 = kb * NK;
-      wait_vmcnt<0>();
-      barrier_lds();  // block kb is in LDS; every wave is done with block kb-1
-      if (kb < kb_last) {
-        dma_rows<D, NK, NW>(Ks[buf ^ 1], tile_src<NK>(kbase, a.k_ss, j0 + NK, lenk - j0 - NK), wave, lane);
-        dma_ds_block<NW>(Ss[buf ^ 1], tile_src<NK>(sblock(kb + 1), M, 0, NK), wave, lane);
-      }
+      // block kb has landed; the later blocks already issued may still be in flight
+      static_assert(NBUF == 3, "the waits below assume one block in flight beyond the current one");
+      if (kb + 1 <= kb_last)
+        wait_vmcnt<NCOPY>();
+      else
+        wait_vmcnt<0>();
+      barrier_lds();  // block kb is in LDS; every wave is done with block kb-1 (buffer of kb + 2)
+      if (kb + NBUF - 1 <= kb_last) copy_block(kb + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1);
       const bool full = (p0 + M <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= p0 + dlt) &&
                         (a.window <= 0 || j0 > p0 + M - 1 + dlt - a.window);
       // dS fragments of key step s are read one step ahead and masked when used; the K
@@ -799,6 +810,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
           for (int x = 0; x < RB; ++x) bs[x] = bsn[x];
         }
       }
+      buf = buf + 1 == NBUF ? 0 : buf + 1;
     }
   }
 

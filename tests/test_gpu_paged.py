@@ -280,13 +280,15 @@ def test_fwd_paged_never_reads_unused_pages_or_slots():
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
-def test_mixed_step_full_size_sampled_rows():
-    """The mixed serving step at its full size (a 1024-token chunk after 3072 cached plus 31 decode
-    rows, 32 query heads, D = 512): every decode row and sampled chunk rows against the oracle,
-    row by row."""
-    w = MIXED
+@pytest.mark.parametrize("name", ["mixed_step_d512", "paged_prefill_d512"])
+def test_paged_forward_full_size_sampled_rows(name):
+    """The benchmark's paged-forward workloads at their full sizes (a 1024-token chunk after 3072
+    cached plus 31 decode rows; a 2048-token chunk after 6144 cached; 32 query heads, D = 512):
+    every decode row, the chunk's first, last and tile-edge rows and seeded random rows, every
+    head, against the oracle row by row."""
+    w = PREFILL_WORKLOADS[name]
     inp = make_prefill_inputs(w, seed=0)
-    say("[mixed step full size]")
+    say(f"[{name} full size]")
     d = _prefill_dev(inp, "bf16")
     o, lse = sdpt.attn_fwd_paged(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"],
                                  scale=w.scale)
@@ -294,20 +296,25 @@ def test_mixed_step_full_size_sampled_rows():
     assert all_finite(o, lse)
     oh, lh = host(o), lse.cpu().numpy()
     cu = inp["cu_q"]
-    rows = sorted(set([0, 1, 511, 512, 1000, 1023] + list(range(1024, int(cu[-1])))))
+    n0 = int(w.new[0])
+    pick = np.random.default_rng(7).choice(n0, size=min(24, n0), replace=False).tolist()
+    rows = sorted(set([0, 1, 15, 16, 127, 128, n0 // 2, n0 - 2, n0 - 1] + pick + list(range(n0, int(cu[-1])))))
     f = lambda x: bits_to_f64(x, "bf16")  # noqa: E731
     q, kc, vc = f(inp["q"]), f(inp["k_cache"]), f(inp["v_cache"])
     worst_o = worst_l = 0.0
+    gathered = {}
     for t in rows:
         b = int(np.searchsorted(cu, t, side="right") - 1)
         L, n = int(w.ctx[b]), int(w.new[b])
         pos = L - n + (t - int(cu[b]))
-        kk = oracle.gather_pages(kc, inp["block_table"][b], L, w.page_size)[None]
-        vv = oracle.gather_pages(vc, inp["block_table"][b], L, w.page_size)[None]
+        if b not in gathered:
+            gathered = {b: (oracle.gather_pages(kc, inp["block_table"][b], L, w.page_size)[None],
+                            oracle.gather_pages(vc, inp["block_table"][b], L, w.page_size)[None])}
+        kk, vv = gathered[b]
         ro, rl = oracle.attention_forward_chunk(q[None, t:t + 1], kk, vv, w.scale, True, 0, pos, 0)
         worst_o = max(worst_o, max_abs(oh[t], ro[0, 0]))
         worst_l = max(worst_l, max_abs(lh[:, t], rl[0, :, 0]))
-    say(f"[mixed step full size] rows={len(rows)} O max-abs {worst_o:.3g} LSE max-abs {worst_l:.3g}")
+    say(f"[{name} full size] rows={len(rows)} O max-abs {worst_o:.3g} LSE max-abs {worst_l:.3g}")
     assert worst_o <= O_MAX_ABS and worst_l <= LSE_MAX_ABS
 
 

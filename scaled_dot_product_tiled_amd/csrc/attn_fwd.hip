@@ -163,21 +163,24 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
       {
-        // K fragments are read two steps ahead of the matrix core; the schedule barrier
-        // keeps the compiler from hoisting every read (and its registers) to the top.
-        bf16x8 kf[3][NKB];
+        // K fragments are read KPF steps ahead of the matrix core (three at head_dim 512, where
+        // one wave per SIMD must hide the LDS latency alone: 5-6% faster than two; two at 256,
+        // where a third spills); the schedule barrier keeps the compiler from hoisting every
+        // read (and its registers) to the top.
+        constexpr int KPF = D == 512 ? 3 : 2;
+        bf16x8 kf[KPF + 1][NKB];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < KPF; ++t)
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = rowf.read(Ks, kb * 32, t);
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-          if (t + 2 < KS) {
+          if (t + KPF < KS) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kf[(t + 2) % 3][kb] = rowf.read(Ks, kb * 32, t + 2);
+            for (int kb = 0; kb < NKB; ++kb) kf[(t + KPF) % (KPF + 1)][kb] = rowf.read(Ks, kb * 32, t + KPF);
           }
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = E16<F16>::mma32(kf[t % 3][kb], qreg[t], sacc[kb]);
+          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = E16<F16>::mma32(kf[t % (KPF + 1)][kb], qreg[t], sacc[kb]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -273,15 +276,16 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
         }
       l_run += half_swap_sum(rs);
       {
-        // V^T fragments in (d block, key step) order, read two ahead of the matrix core.
+        // V^T fragments in (d block, key step) order, read VPF ahead of the matrix core.
         constexpr int NF = DB * NS;
-        bf16x8 vf[3];
+        constexpr int VPF = D == 512 ? 3 : 2;
+        bf16x8 vf[VPF + 1];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) vf[f] = trf.read(Vs, 16 * (f % NS), f / NS);
+        for (int f = 0; f < VPF; ++f) vf[f] = trf.read(Vs, 16 * (f % NS), f / NS);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          if (f + 2 < NF) vf[(f + 2) % 3] = trf.read(Vs, 16 * ((f + 2) % NS), (f + 2) / NS);
-          oacc[f / NS] = E16<F16>::mma32(vf[f % 3], pb[f % NS], oacc[f / NS]);
+          if (f + VPF < NF) vf[(f + VPF) % (VPF + 1)] = trf.read(Vs, 16 * ((f + VPF) % NS), (f + VPF) / NS);
+          oacc[f / NS] = E16<F16>::mma32(vf[f % (VPF + 1)], pb[f % NS], oacc[f / NS]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

@@ -184,16 +184,19 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      barrier_lds();  // every wave is done with Ks
-      if constexpr (PAGED) {
-        if (has_next) {
-          table_pages2(phys, trow, j0 + N, lenk - j0 - N);  // the next tile's pages, for K and V
-          dma_rows_paged<D, N, 4>(Ks, paged_tile_src<N>(kbase, a.k_sb, a.k_ss, phys, a.num_pages, lenk - j0 - N),
-                                  wave, lane);
+      // The next K tile is copied once every wave is past the barrier below (which every wave
+      // reaches after its S reads of Ks), so that one barrier per tile serves both.
+      auto copy_next_k = [&]() __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+          if (has_next) {
+            table_pages2(phys, trow, j0 + N, lenk - j0 - N);  // the next tile's pages, for K and V
+            dma_rows_paged<D, N, 4>(Ks, paged_tile_src<N>(kbase, a.k_sb, a.k_ss, phys, a.num_pages, lenk - j0 - N),
+                                    wave, lane);
+          }
+        } else {
+          if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
         }
-      } else {
-        if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
-      }
+      };
 
       if constexpr (SOFTCAP) {
         // the cap applies to every score before the mask (masked entries become -inf below)
@@ -232,11 +235,9 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
 #pragma unroll
           for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
         }
-        if (has_next)
-          wait_vmcnt<NDMA>();  // V(jt) has landed; K(jt+1) may still be in flight
-        else
-          wait_vmcnt<0>();
-        barrier_lds();
+        wait_vmcnt<0>();  // V(jt) has landed (K(jt+1) is not issued yet)
+        barrier_lds();     // V(jt) visible to every wave; every wave is done with Ks
+        copy_next_k();
       } else {
         // A row's first visible keys fix its reference (its accumulators are still zero).
         if (m_ref == -INFINITY) m_ref = mt;
@@ -244,11 +245,8 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
         const bool wave_need = __any(need);
         if (lane == 0) restart_flag[jt & 1][wave] = wave_need ? 1 : 0;
 
-        if (has_next)
-          wait_vmcnt<NDMA>();  // V(jt) has landed; K(jt+1) may still be in flight
-        else
-          wait_vmcnt<0>();
-        barrier_lds();
+        wait_vmcnt<0>();  // V(jt) has landed (K(jt+1) is not issued yet)
+        barrier_lds();     // the flags and V(jt) visible to every wave; every wave is done with Ks
         if (restart_flag[jt & 1][0] | restart_flag[jt & 1][1] | restart_flag[jt & 1][2] |
             restart_flag[jt & 1][3]) {
           m_ref = fmaxf(m_ref, mt);
@@ -258,6 +256,7 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
           barrier_lds();  // no wave still reads Ks / Vs before they are refilled
           break;
         }
+        copy_next_k();
       }
 
       const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;

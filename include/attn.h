@@ -275,7 +275,12 @@ typedef struct {
  *                [0, max_pages_per_seq * page_size]; 0 gives O = 0.
  *   softcap      as for attn_fwd (0: none)
  *   o            device 16-bit (B, Hq, D), written; strides o_stride_b, o_stride_h
- *   workspace    at least paged_decode_workspace_bytes(shape) bytes
+ *   workspace    at least paged_decode_workspace_bytes(shape) bytes; used only when the
+ *                call splits contexts into chunks (below), and always checked
+ * Two schedules, same results within rounding: when B * Hkv >= 512 and
+ * max_pages_per_seq * page_size <= 8192, one kernel gives each (sequence, kv head) one
+ * workgroup that covers the whole context and writes o; otherwise a first kernel scores
+ * 512-token chunks into the workspace and a second merges them into o.
  */
 attn_status paged_decode(const attn_decode_shape* shape,
                          const void* q, int64_t q_stride_b, int64_t q_stride_h,

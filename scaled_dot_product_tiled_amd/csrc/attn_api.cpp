@@ -803,7 +803,15 @@ static attn_status check_decode(const attn_decode_shape* shape, const void* q, i
   return ATTN_OK;
 }
 
-// The decode's two launches, after every check; `workspace` holds the chunk partials.
+// Which decode runs: one 8-wave workgroup per (sequence, kv head) over the whole context when
+// the batch alone gives every compute unit at least two workgroups and no context can exceed
+// 8192 tokens (the longest workgroup then stays within the time of the others' two rounds);
+// otherwise 512-token chunks over (kv head, chunk, sequence) and a merge of their partials.
+static bool decode_whole(const attn_decode_shape& sh) {
+  return (int64_t)sh.B * sh.Hkv >= 2 * kComputeUnits && (int64_t)sh.max_pages_per_seq * sh.page_size <= 8192;
+}
+
+// The decode's launches, after every check; `workspace` holds the chunk partials (split path).
 static attn_status run_decode(const attn_decode_shape& sh, const void* q, int64_t q_stride_b, int64_t q_stride_h,
                               attn_tensor k_cache, attn_tensor v_cache, const int32_t* block_table,
                               const int32_t* ctx_lens, float scale, float softcap, void* o, int64_t o_stride_b,
@@ -847,6 +855,8 @@ static attn_status run_decode(const attn_decode_shape& sh, const void* q, int64_
   a.sc_in = softcap > 0.f ? scale / softcap : 0.f;
   a.sc_out = softcap > 0.f ? softcap / scale : 0.f;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (decode_whole(sh))
+    return hip_status(timed("decode_whole", s, [&] { return attn::launch_decode_whole(a, sh.D, s); }));
   hipError_t e = timed("decode_split", s, [&] { return attn::launch_decode_split(a, sh.D, s); });
   if (e != hipSuccess) return hip_status(e);
   return hip_status(timed("decode_merge", s, [&] { return attn::launch_decode_merge(a, sh.D, s); }));

@@ -206,6 +206,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_kv_reduce(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, int D, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int D, hipStream_t stream);
+hipError_t launch_decode_whole(const DecodeArgs& a, int D, hipStream_t stream);
 // Device address of the fixed decode scratch on the current device (looked up once per device).
 constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
 hipError_t decode_scratch(void** ptr);

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from synth import DECODE_WORKLOADS, bf16_bits_to_f64, f32_to_bf16_bits, make_decode_inputs
+from synth import DECODE_WORKLOADS, bf16_bits_to_f64, bits_to_f64, f32_to_bf16_bits, make_decode_inputs
 from tests.gpu_util import O_MAX_ABS, all_finite, dev, host, host_bits, max_abs
 
 pytestmark = pytest.mark.gpu
@@ -173,3 +173,52 @@ def test_contiguous_pages_equal_the_table_path_bit_for_bit(B, ctx_range, softcap
     assert np.array_equal(host_bits(o_con), host_bits(o_tab))
     if B == 64:
         assert max_abs(host(o_con), ref(inp, w.scale)) <= O_MAX_ABS
+
+
+# ---------------------------------------------------------------------------
+# The two decode strategies: one workgroup per (sequence, kv head) over the whole context when
+# the batch fills the chip (B * Hkv >= 512 and contexts of at most 8192 tokens), otherwise
+# 512-token chunks and a merge
+# ---------------------------------------------------------------------------
+def _pad_table(inp, cols):
+    """The same inputs with the block table widened to `cols` columns (unused entries -1): the
+    table's capacity then passes 8192 tokens and the chunked path runs."""
+    t = np.full((inp["block_table"].shape[0], cols), -1, dtype=np.int32)
+    t[:, :inp["block_table"].shape[1]] = inp["block_table"]
+    return dict(inp, block_table=t)
+
+
+def test_whole_and_chunked_decode_agree_with_the_oracle():
+    w = DECODE_WORKLOADS["decode_d128"]
+    ctx = make_decode_inputs(w, seed=41)["ctx_lens"].copy()
+    ctx[[3, 40]] = 0                                   # sequences with no context: O = 0
+    ctx[7] = 1
+    inp = make_decode_inputs(w, seed=41, ctx_lens=ctx)
+    wide = _pad_table(inp, 520)
+    print("[decode whole vs chunked]", flush=True)
+    o_whole, o_chunk = run(inp, w.scale), run(wide, w.scale)
+    r = ref(inp, w.scale)
+    assert all_finite(o_whole, o_chunk)
+    assert max_abs(host(o_whole), r) <= O_MAX_ABS and max_abs(host(o_chunk), r) <= O_MAX_ABS
+    for b in (3, 40):
+        assert not host_bits(o_whole[b]).any() and not host_bits(o_chunk[b]).any()
+
+
+@pytest.mark.parametrize("B,Hq,dtype,cap", [(64, 8, "bf16", 0.0), (64, 16, "bf16", 0.0), (64, 64, "f16", 0.0),
+                                            (80, 32, "bf16", 0.0), (64, 32, "bf16", 20.0)])
+def test_whole_sequence_decode_variants(B, Hq, dtype, cap):
+    """The whole-sequence kernel at group sizes 1, 2, 8 and 4, in fp16, with a softcap, and for a
+    batch above 64 sequences (dealt in index order instead of by decreasing context).  Unused
+    pages and the slots past each context hold NaN, so a read of any of them shows in O."""
+    w = DECODE_WORKLOADS["decode_d128"].scaled(B=B, Hq=Hq, ctx_range=(0, 900), dtype=dtype)
+    inp = make_decode_inputs(w, seed=42, poison_unused=True)
+    print(f"[decode whole] B={B} Hq={Hq} {dtype} cap={cap}", flush=True)
+    q, kc, vc = dev(inp["q"], dtype), dev(inp["k_cache"], dtype), dev(inp["v_cache"], dtype)
+    o = sdpt.paged_decode(q, kc, vc, torch.from_numpy(inp["block_table"]).to("cuda:0"),
+                          torch.from_numpy(inp["ctx_lens"]).to("cuda:0"), scale=w.scale, softcap=cap)
+    torch.cuda.synchronize()
+    f = lambda x: bits_to_f64(x, dtype)  # noqa: E731
+    r = oracle.paged_decode(f(inp["q"]), f(inp["k_cache"]), f(inp["v_cache"]), inp["block_table"], inp["ctx_lens"],
+                            w.scale, w.page_size, cap)
+    assert all_finite(o)
+    assert max_abs(host(o), r) <= O_MAX_ABS

@@ -280,7 +280,9 @@ typedef struct {
  * Two schedules, same results within rounding: when B * Hkv >= 512 and
  * max_pages_per_seq * page_size <= 8192, one kernel gives each (sequence, kv head) one
  * workgroup that covers the whole context and writes o; otherwise a first kernel scores
- * 512-token chunks into the workspace and a second merges them into o.
+ * 512-token chunks into the workspace and a second merges them into o.  A row's result is
+ * deterministic for a given shape, but the same row in calls of different B (or table width)
+ * may differ in its last bits.
  */
 attn_status paged_decode(const attn_decode_shape* shape,
                          const void* q, int64_t q_stride_b, int64_t q_stride_h,
@@ -397,7 +399,8 @@ attn_status paged_kv_gather(const attn_decode_shape* shape, int32_t n_tokens,
  * paged_decode_graphs_launch: replays, on `stream`, the graph of the smallest bucket >= B
  * (0 <= B <= largest bucket; B = 0 launches nothing) and stores that bucket in *bucket if
  * bucket is not NULL.  Rows B .. bucket-1 are processed too: a caller gives them ctx_lens 0
- * (their O is then 0 and nothing is appended for them) or ignores them.  The replay reads
+ * (their O is then 0 and nothing is appended for them) or ignores them.  A replay equals the
+ * eager step on the bucket's rows bit for bit.  The replay reads
  * whatever the buffers hold when it runs.  Replays of one graph set share its workspace:
  * overlapping replays (other streams) race.
  */

@@ -322,9 +322,10 @@ def test_decode_graphs_per_bucket_replay_like_eager_calls():
     """One captured decode step (append the current token's K/V, then decode) per bucket [1, 2, 4,
     ..., 64], over one set of buffers and one shared workspace (DecodeGraphs).  For a sequence of
     batch sizes, the smallest bucket >= B is replayed with rows B .. bucket-1 as padding (context
-    0); each replay equals the same step made with eager calls on the B rows bit for bit (output
-    and caches), its padding rows are exact zeros, and the output is within tolerance of the
-    oracle."""
+    0); each replay equals the same step made with eager calls on the bucket's rows bit for bit
+    (output and caches: the graph of bucket n is the step on rows 0 .. n-1, and the decode's
+    schedule, hence its rounding, depends on the row count), its padding rows are exact zeros,
+    and the B rows are within tolerance of the oracle."""
     w = DECODE_WORKLOADS["decode_d128"].scaled(ctx_range=(20, 700))    # B = 64 rows, shorter contexts
     inp = make_decode_inputs(w, seed=50)
     sizes = [1, 3, 8, 17, 64, 40, 3, 64]
@@ -357,12 +358,12 @@ def test_decode_graphs_per_bucket_replay_like_eager_calls():
         assert bucket == min(b for b in buckets if b >= B)
         torch.cuda.synchronize()
         got = out_s.clone()
-        # the same step with eager calls on B rows and other caches
-        tb, cb = t_d[:B].contiguous(), ctx_s[:B].contiguous()
-        sdpt.paged_kv_append(kn_s[:B].contiguous(), vn_s[:B].contiguous(), k_e, v_e, tb, cb)
-        eager = sdpt.paged_decode(q_s[:B].contiguous(), k_e, v_e, tb, cb, scale=w.scale, workspace=ws)
+        # the same step with eager calls on the bucket's rows (padding included) and other caches
+        tb, cb = t_d[:bucket].contiguous(), ctx_s[:bucket].contiguous()
+        sdpt.paged_kv_append(kn_s[:bucket].contiguous(), vn_s[:bucket].contiguous(), k_e, v_e, tb, cb)
+        eager = sdpt.paged_decode(q_s[:bucket].contiguous(), k_e, v_e, tb, cb, scale=w.scale, workspace=ws)
         torch.cuda.synchronize()
-        assert np.array_equal(host_bits(got[:B]), host_bits(eager)), i
+        assert np.array_equal(host_bits(got[:bucket]), host_bits(eager)), i
         assert not host_bits(got[B:bucket]).any(), i                      # padding rows: O = 0
         assert np.array_equal(host_bits(k_d), host_bits(k_e)) and np.array_equal(host_bits(v_d), host_bits(v_e)), i
         kc_ref = oracle.paged_append(kc_ref, table[:B], ctx[:B], host(kn_s[:B]), w.page_size)

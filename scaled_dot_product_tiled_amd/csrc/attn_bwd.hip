@@ -328,6 +328,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
         }
       }
       barrier_lds();
+      bf16x8 ds_out[RB];  // this lane's dS values of the step, stored during the gradient products
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f32x4 sv[2], dpv[2];
@@ -392,29 +393,38 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
         bf16x8* mine = reinterpret_cast<bf16x8*>(&xch[rb][kb][xh >> 1][0][0]);
         mine[lane] = pb;
         mine[64 + lane] = db;
-        // dS for the dQ product, this lane's key.  db holds query rows 8 xh + 4 g2 + (0..3) and
-        // 8 xh + 8 + 4 g2 + (0..3) of the step; lanes l and l + 32 trade four of them so that each
-        // holds 8 consecutive rows (8 xh + 8 g2 ..) and writes them with one 16-byte store.
+        ds_out[rb] = db;
+      }
+      // dS for the dQ product, this lane's key, issued under the first gradient products at head
+      // dim 512 (its address arithmetic and store then overlap the matrix work).  ds_out holds query rows
+      // 8 xh + 4 g2 + (0..3) and 8 xh + 8 + 4 g2 + (0..3) of the block; lanes l and l + 32 trade
+      // four of them so that each holds 8 consecutive rows (8 xh + 8 g2 ..) and writes them with
+      // one 16-byte store.
+      auto store_ds = [&]() {
         if (i0 / kDsRows != ds_qt) {  // the block changes every kDsRows / MQ query tiles
           ds_qt = i0 / kDsRows;
           ds_bi = ds_block_index(ds_qt, (j0 / kDsKeys) + kb, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
         }
         const int64_t bi = ds_bi;
-        if (bi >= 0) {
+        if (bi < 0) return;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
           uint32_t w[4];
-          __builtin_memcpy(w, &db, 16);
+          __builtin_memcpy(w, &ds_out[rb], 16);
           const uint32_t give0 = g2 ? w[0] : w[2], give1 = g2 ? w[1] : w[3];
           const auto r0 = __builtin_amdgcn_permlane32_swap(give0, give0, false, false);
           const auto r1 = __builtin_amdgcn_permlane32_swap(give1, give1, false, false);
           // r[0] carries the lower half's value to every lane, r[1] the upper half's
           const uint32_t got0 = g2 ? r0[0] : r0[1], got1 = g2 ? r1[0] : r1[1];
           const uint32_t o[4] = {g2 ? got0 : w[0], g2 ? got1 : w[1], g2 ? w[2] : got0, g2 ? w[3] : got1};
-          bf16* dst = dshead + bi * kDsBlockElems + ds_elem(ir & (kDsRows - 1), ln) + 8 * xh + 8 * g2;
+          bf16* dst = dshead + bi * kDsBlockElems + ds_elem((i0 + 32 * rb) & (kDsRows - 1), ln) + 8 * xh + 8 * g2;
           uint4 v;
           __builtin_memcpy(&v, o, 16);
           *reinterpret_cast<uint4*>(dst) = v;
         }
-      }
+      };
+      // (at head_dim 256 the registers to carry the values across the barrier are not there)
+      if constexpr (LOWREG) store_ds();
       barrier_lds();
       if (has_next) stats(son, i0n, buf ^ 1);
       if constexpr (LOWREG) {
@@ -470,6 +480,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
             dvacc[1][d] = E16<F16>::mma32(ado, p1, dvacc[1][d]);
             dkacc[0][d] = E16<F16>::mma32(aq, s0, dkacc[0][d]);
             dkacc[1][d] = E16<F16>::mma32(aq, s1, dkacc[1][d]);
+            if (s == 0 && d == 0) store_ds();
             ado = ado_n;
             aq = aq_n;
             __builtin_amdgcn_sched_barrier(0);
@@ -764,18 +775,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
       const bool full = (p0 + M <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= p0 + dlt) &&
                         (a.window <= 0 || j0 > p0 + M - 1 + dlt - a.window);
       // dS fragments of key step s are read one step ahead and masked when used; the K
-      // fragment of (s, d) is read one (s, d) step ahead of its products
+      // fragment of (s, d) is read one (s, d) step ahead of its products.  On a block that
+      // straddles an edge, a row's visible keys are one interval [lo, hi], held as a 32-bit mask
+      // over the block's keys (bit t: key j0 + t), from which each fragment takes its 8 bits.
+      uint32_t vis[RB];
+      if (!full) {
+#pragma unroll
+        for (int x = 0; x < RB; ++x) {
+          const int row = p0 + 32 * x + ln;
+          const int ip = row + dlt;
+          const int hi = a.causal ? min(lenk - 1, ip) : lenk - 1;
+          const int lo = a.window > 0 ? ip - a.window + 1 : 0;
+          const int nh = min(max(hi - j0 + 1, 0), 32), nl = min(max(lo - j0, 0), 32);
+          const uint32_t mh = (uint32_t)((1ull << nh) - 1), ml = (uint32_t)((1ull << nl) - 1);
+          vis[x] = row < len ? (mh & ~ml) : 0u;
+        }
+      }
       auto mask = [&](bf16x8& v, int s, int x) {
-        // element e holds key j0 + 16 s + 4 g2 + e (e < 4) or j0 + 16 s + 8 + 4 g2 + e - 4
-        const int row = p0 + 32 * x + ln;
+        // element e holds key j0 + 16 s + 4 g2 + e (e < 4) or j0 + 16 s + 8 + 4 g2 + e - 4;
+        // 16-bit halves of dword i hold elements 2 i and 2 i + 1
+        const uint32_t ba = vis[x] >> (16 * s + 4 * g2), bb = ba >> 8;
+        auto halves = [](uint32_t t) { return ((t & 1u) * 0xffffu) | ((t & 2u) * 0x7fff8000u); };
         uint32_t w[4];
         __builtin_memcpy(w, &v, 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = j0 + 16 * s + 4 * g2 + (e < 4 ? e : e + 4);
-          const uint32_t keep = key_visible(row, key, len, lenk, dlt, a.causal, a.window) ? 0xffffu : 0u;
-          w[e >> 1] &= (e & 1) ? (keep << 16) | 0xffffu : keep | 0xffff0000u;
-        }
+        w[0] &= halves(ba);
+        w[1] &= halves(ba >> 2);
+        w[2] &= halves(bb);
+        w[3] &= halves(bb >> 2);
         __builtin_memcpy(&v, w, 16);
       };
       bf16x8 bs[RB], bsn[RB];

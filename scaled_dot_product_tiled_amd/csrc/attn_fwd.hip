@@ -208,16 +208,21 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
       const bool need_mask = (j0 + N > lenk) || (p0 + a.mpos > len) || (a.causal && j0 + N - 1 > p0 + dlt) ||
                              (a.window > 0 && j0 <= plast + dlt - a.window);
       if (need_mask) {
+        // the row's visible keys are one interval [lo, hi]; per 32-key block it becomes a 32-bit
+        // mask (bit t: key j0 + 32 kb + t), and register r tests bit 8 (r/4) + 4 g2 + r%4
+        const int ip = pos + dlt;
+        const int hi = a.causal ? min(lenk - 1, ip) : lenk - 1;
+        const int lo = a.window > 0 ? ip - a.window + 1 : 0;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int jb = j0 + 32 * kb;
+          const int nh = min(max(hi - jb + 1, 0), 32), nl = min(max(lo - jb, 0), 32);
+          const uint32_t mh = (uint32_t)((1ull << nh) - 1), ml = (uint32_t)((1ull << nl) - 1);
+          const uint32_t vis = (pos < len ? (mh & ~ml) : 0u) >> (4 * g2);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // the key's position relative to the rows' (query row i sits at i + q_shift):
-            // the offset goes to the key side, a scalar per tile, so that only the row
-            // index stays in a vector register across the key loop
-            const int keyq = j0 - dlt + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-            if (!key_visible(pos, keyq, len, lenk - dlt, 0, a.causal, a.window)) sacc[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (!((vis >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[kb][r] = -INFINITY;
+        }
       }
       float mt = -INFINITY;
 #pragma unroll

@@ -744,23 +744,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
     const bf16* kbase = a.k + b * a.k_sb + (int64_t)off * a.k_ss + g * a.k_sh + dh * D;
     const int64_t ds_hb = a.ds_seq ? ds_head_blocks(len, a.ds_tri, a.ds_cnt) : a.ds_head;
     const bf16* sbase = a.dsb + ((a.ds_seq ? ds_b : (int64_t)b * a.Hq * ds_hb) + (int64_t)h * ds_hb) * kDsBlockElems;
-    auto sblock = [&](int kb) {  // every block in kb_first .. kb_last holds a visible pair, so it is stored
-      const int64_t bi = ds_block_index(qt, kb, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
-      return sbase + (bi < 0 ? 0 : bi) * kDsBlockElems;
-    };
+    // Every block in kb_first .. kb_last holds a visible pair, so it is stored, and the stored
+    // blocks of a query tile are consecutive: block kb sits (kb - kb_first) blocks after the
+    // first.  The copies walk K and dS with two pointers, one block per copy.
+    const int64_t bi0 = ds_block_index(qt, kb_first, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
+    const bf16* scopy = sbase + (bi0 < 0 ? 0 : bi0) * kDsBlockElems;
+    const bf16* kcopy = kbase + (int64_t)kb_first * NK * a.k_ss;
+    int kbcopy = kb_first;  // block of the next copy
     const TrFrags<D> trk(lane);
     const TrFrags<M> trs(lane);
     int klo[DBW], khi[DBW];  // bases of this wave's d blocks
 #pragma unroll
     for (int d = 0; d < DBW; ++d) trk.pick(dsl + d, klo[d], khi[d]);
 
-    auto copy_block = [&](int kb, int buf) {
-      dma_rows<D, NK, NW>(Ks[buf], tile_src<NK>(kbase, a.k_ss, kb * NK, lenk - kb * NK), wave, lane);
-      dma_ds_block<NW>(Ss[buf], tile_src<NK>(sblock(kb), M, 0, NK), wave, lane);
+    auto copy_block = [&](int buf) {
+      dma_rows<D, NK, NW>(Ks[buf], tile_src<NK>(kcopy, a.k_ss, 0, lenk - kbcopy * NK), wave, lane);
+      dma_ds_block<NW>(Ss[buf], tile_src<NK>(scopy, M, 0, NK), wave, lane);
+      kcopy += (int64_t)NK * a.k_ss;
+      scopy += kDsBlockElems;
+      ++kbcopy;
     };
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i)
-      if (kb_first + i <= kb_last) copy_block(kb_first + i, i);
+      if (kb_first + i <= kb_last) copy_block(i);
     int buf = 0;
     for (int kb = kb_first; kb <= kb_last; ++kb) {
       const int j0 = kb * NK;
@@ -771,7 +777,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(AttnArgs a) {
       else
         wait_vmcnt<0>();
       barrier_lds();  // block kb is in LDS; every wave is done with block kb-1 (buffer of kb + 2)
-      if (kb + NBUF - 1 <= kb_last) copy_block(kb + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1);
+      if (kb + NBUF - 1 <= kb_last) copy_block(buf == 0 ? NBUF - 1 : buf - 1);  // block kb + NBUF - 1
       const bool full = (p0 + M <= len) && (j0 + NK <= lenk) && (!a.causal || j0 + NK - 1 <= p0 + dlt) &&
                         (a.window <= 0 || j0 > p0 + M - 1 + dlt - a.window);
       // dS fragments of key step s are read one step ahead and masked when used; the K

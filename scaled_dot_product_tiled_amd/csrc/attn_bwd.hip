@@ -269,9 +269,10 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
       for (int d = 0; d < DBW; ++d) trf.pick(dsl + d, tlo[d], thi[d]);
       {
         const bf16* src = score_wave ? Qs[buf] : dOs[buf];
-        // fragments read PF steps ahead (fewer at head_dim 256, whose two workgroups per
-        // compute unit hide each other's LDS latency within half the registers)
-        constexpr int PF = LOWREG ? 1 : 3;
+        // fragments read PF steps ahead: three at head_dim 512; two at 256, whose two workgroups
+        // per compute unit hide part of each other's LDS latency within half the registers (one
+        // ahead measured 3.5% slower there, three spilled)
+        constexpr int PF = LOWREG ? 2 : 3;
         bf16x8 f[RB][PF + 1];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -428,8 +429,9 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
       barrier_lds();
       if (has_next) stats(son, i0n, buf ^ 1);
       if constexpr (LOWREG) {
-        // one 16-row half at a time: its P and dS fragments, then per d block the transposed
-        // dO and Q fragments and the four products
+        // one 16-row half at a time: its P and dS fragments, then per d block the four products;
+        // the transposed dO and Q fragments are read one (half, d block) step ahead
+        bf16x8 ado = trf.read_with(dOs[buf], 0, dsl, tlo[0], thi[0]), aq = trf.read_with(Qs[buf], 0, dsl, tlo[0], thi[0]);
 #pragma unroll
         for (int s = 0; s < 2 * RB; ++s) {
           bf16x8 pfr[4];
@@ -441,12 +443,18 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
           }
 #pragma unroll
           for (int d = 0; d < DBW; ++d) {
-            const bf16x8 ado = trf.read_with(dOs[buf], 16 * s, dsl + d, tlo[d], thi[d]);
-            const bf16x8 aq = trf.read_with(Qs[buf], 16 * s, dsl + d, tlo[d], thi[d]);
+            const int ns = d + 1 == DBW ? s + 1 : s, nd = d + 1 == DBW ? 0 : d + 1;
+            bf16x8 ado_n = ado, aq_n = aq;
+            if (ns < 2 * RB) {
+              ado_n = trf.read_with(dOs[buf], 16 * ns, dsl + nd, tlo[nd], thi[nd]);
+              aq_n = trf.read_with(Qs[buf], 16 * ns, dsl + nd, tlo[nd], thi[nd]);
+            }
             dvacc[0][d] = E16<F16>::mma32(ado, pfr[0], dvacc[0][d]);
             dvacc[1][d] = E16<F16>::mma32(ado, pfr[1], dvacc[1][d]);
             dkacc[0][d] = E16<F16>::mma32(aq, pfr[2], dkacc[0][d]);
             dkacc[1][d] = E16<F16>::mma32(aq, pfr[3], dkacc[1][d]);
+            ado = ado_n;
+            aq = aq_n;
             __builtin_amdgcn_sched_barrier(0);
           }
         }

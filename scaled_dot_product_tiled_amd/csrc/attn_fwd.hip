@@ -151,11 +151,25 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
         dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, t_lo * N, lenk - t_lo * N), wave, lane);
       }
     }
+    // Copies after the first tile's (non-paged, head_dim 512): the next K tile's row copies are
+    // spread over this tile's P V products and this tile's V copies over its Q K^T products, one
+    // per two matrix instructions, so that the four waves do not queue their copies on the load
+    // path all at once (issued back to back, a wave's eight copies took about 650 cycles to
+    // leave it; spread: 1.22 -> 1.19 ms on B2 S4096).  The first tile's K and V are copied above,
+    // back to back.  At head_dim 256 the spread copies' registers spill and two workgroups per
+    // compute unit already overlap each other's copies: it stays with the bursts.
+    constexpr bool SPREAD = !PAGED && D == 512;
     for (int jt = t_lo; jt < t_hi; ++jt) {
       const int j0 = jt * N;
       const bool has_next = jt + 1 < t_hi;
-      wait_vmcnt<NDMA>();  // K(jt) has landed; V(jt) may still be in flight
+      if (SPREAD && jt != t_lo)
+        wait_vmcnt<0>();  // K(jt) has landed (V(jt) is copied below)
+      else
+        wait_vmcnt<NDMA>();  // K(jt) has landed; V(jt) may still be in flight
       barrier_lds();
+      TileSrc vsrc{};
+      if constexpr (SPREAD) vsrc = tile_src<N>(vbase, a.v_ss, j0, lenk - j0);
+      const bool copy_v = SPREAD && jt != t_lo;
 
       f32x16 sacc[NKB];
 #pragma unroll
@@ -181,6 +195,7 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
           }
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) sacc[kb] = E16<F16>::mma32(kf[t % (KPF + 1)][kb], qreg[t], sacc[kb]);
+          if (copy_v && (t & 1) == 0 && t / 2 < NDMA) dma_rows_one<D, N, 4>(Vs, vsrc, wave, lane, t / 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -194,8 +209,8 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
                                     wave, lane);
           }
         } else {
-          if (has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
-        }
+          if (!SPREAD && has_next) dma_rows<D, N, 4>(Ks, tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N), wave, lane);
+        }  // (SPREAD: copied during the P V products below)
       };
 
       if constexpr (SOFTCAP) {
@@ -284,12 +299,17 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
         constexpr int NF = DB * NS;
         constexpr int VPF = D == 512 ? 3 : 2;
         bf16x8 vf[VPF + 1];
+        TileSrc ksrc{};  // the next K tile
+        if constexpr (SPREAD) ksrc = tile_src<N>(kbase, a.k_ss, j0 + N, lenk - j0 - N);
+        const bool copy_k = SPREAD && has_next;
+        static_assert(2 * NDMA <= NF && 2 * NDMA <= KS, "every copy needs a slot in the matrix loops");
 #pragma unroll
         for (int f = 0; f < VPF; ++f) vf[f] = trf.read(Vs, 16 * (f % NS), f / NS);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           if (f + VPF < NF) vf[(f + VPF) % (VPF + 1)] = trf.read(Vs, 16 * ((f + VPF) % NS), (f + VPF) / NS);
           oacc[f / NS] = E16<F16>::mma32(vf[f % (VPF + 1)], pb[f % NS], oacc[f / NS]);
+          if (copy_k && (f & 1) == 0 && f / 2 < NDMA) dma_rows_one<D, N, 4>(Ks, ksrc, wave, lane, f / 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -299,7 +319,7 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
           dma_rows_paged<D, N, 4>(Vs, paged_tile_src<N>(vbase, a.v_sb, a.v_ss, phys, a.num_pages, lenk - j0 - N),
                                   wave, lane);
       } else {
-        if (has_next) dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, j0 + N, lenk - j0 - N), wave, lane);
+        if (!SPREAD && has_next) dma_rows<D, N, 4>(Vs, tile_src<N>(vbase, a.v_ss, j0 + N, lenk - j0 - N), wave, lane);
       }
     }
   }

@@ -295,7 +295,8 @@ attn_status paged_decode(const attn_decode_shape* shape,
 /*
  * paged_decode_noalloc: paged_decode for callers that cannot allocate memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation).  It takes no
- * workspace: the chunk partials live in a fixed device array inside the library, of
+ * workspace: the chunk partials (when the call splits contexts into chunks, see paged_decode)
+ * live in a fixed device array inside the library, of
  * paged_decode_noalloc_max_bytes() bytes (16 MiB) on every GPU it runs on, held until the
  * process ends.  The call allocates nothing and frees nothing.
  *   Arguments, layouts, results and errors are those of paged_decode without workspace and

@@ -277,7 +277,7 @@ typedef struct {
  *   o            device 16-bit (B, Hq, D), written; strides o_stride_b, o_stride_h
  *   workspace    at least paged_decode_workspace_bytes(shape) bytes; used only when the
  *                call splits contexts into chunks (below), and always checked
- * Two schedules, same results within rounding: when B * Hkv >= 512 and
+ * Two schedules, same results within rounding: when B * Hkv >= 256 and
  * max_pages_per_seq * page_size <= 8192, one kernel gives each (sequence, kv head) one
  * workgroup that covers the whole context and writes o; otherwise a first kernel scores
  * 512-token chunks into the workspace and a second merges them into o.  A row's result is

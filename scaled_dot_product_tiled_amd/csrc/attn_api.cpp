@@ -804,11 +804,12 @@ static attn_status check_decode(const attn_decode_shape* shape, const void* q, i
 }
 
 // Which decode runs: one 8-wave workgroup per (sequence, kv head) over the whole context when
-// the batch alone gives every compute unit at least two workgroups and no context can exceed
-// 8192 tokens (the longest workgroup then stays within the time of the others' two rounds);
+// the batch alone gives every compute unit a workgroup and no context can exceed 8192 tokens;
 // otherwise 512-token chunks over (kv head, chunk, sequence) and a merge of their partials.
+// Measured on the head_dim-128 decode workload's lengths (Hkv 8): whole against chunked 2.8
+// against 3.3 TB/s at 8 sequences, 3.0 / 3.6 at 16, 4.15 / 4.0 at 32, 4.9 / 4.3 at 48.
 static bool decode_whole(const attn_decode_shape& sh) {
-  return (int64_t)sh.B * sh.Hkv >= 2 * kComputeUnits && (int64_t)sh.max_pages_per_seq * sh.page_size <= 8192;
+  return (int64_t)sh.B * sh.Hkv >= kComputeUnits && (int64_t)sh.max_pages_per_seq * sh.page_size <= 8192;
 }
 
 // The decode's launches, after every check; `workspace` holds the chunk partials (split path).

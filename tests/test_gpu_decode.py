@@ -177,8 +177,8 @@ def test_contiguous_pages_equal_the_table_path_bit_for_bit(B, ctx_range, softcap
 
 # ---------------------------------------------------------------------------
 # The two decode strategies: one workgroup per (sequence, kv head) over the whole context when
-# the batch fills the chip (B * Hkv >= 512 and contexts of at most 8192 tokens), otherwise
-# 512-token chunks and a merge
+# the batch gives every compute unit a workgroup (B * Hkv >= 256 and contexts of at most 8192
+# tokens), otherwise 512-token chunks and a merge
 # ---------------------------------------------------------------------------
 def _pad_table(inp, cols):
     """The same inputs with the block table widened to `cols` columns (unused entries -1): the

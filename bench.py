@@ -690,6 +690,28 @@ def main():
     eager_host = host_us(lambda: sdpt.paged_decode(p0["q"], p0["kc"], p0["vc"], p0["table"], p0["ctx"],
                                                     scale=dw.scale, out=outs[0], workspace=ws), n_dec)
     gr.close()
+
+    # smaller batches of the same pools (their first B sequences): below one workgroup per compute
+    # unit (B * Hkv < 256) the call takes the chunked schedule
+    sweep = {}
+    for bs in (8, 16, 32, 48):
+        its = [0]
+
+        def dec_b():
+            p = pools[its[0] & 1]
+            sdpt.paged_decode(p["q"][:bs], p["kc"], p["vc"], p["table"][:bs], p["ctx"][:bs], scale=dw.scale,
+                              out=outs[its[0] & 1][:bs], workspace=ws)
+            its[0] += 1
+
+        for _ in range(4):
+            dec_b()
+        torch.cuda.synchronize()
+        tb_ = time_calls(dec_b, 20, stream)
+        kb_ = kernel_times(dec_b, 4)
+        dwb = dw.scaled(B=bs)
+        byt = 0.5 * (decode_bytes(dwb, pools[0]["ctx_host"][:bs]) + decode_bytes(dwb, pools[1]["ctx_host"][:bs]))
+        sweep[str(bs)] = {"ms": round(tb_["mean"], 4), "GB/s": round(byt / (tb_["mean"] * 1e-3) / 1e9, 1),
+                          "kernels": sorted(kb_)}
     # the decode workload's batch fills the chip: one launch of the whole-sequence kernel
     dec_kernel = "decode_whole" if "decode_whole" in dec_kernels else "decode_split"
     rpd = rocprof_ms("decode_d128", dec_kernel)
@@ -752,6 +774,7 @@ def main():
                                       "GB/s": round(dec_bytes / (tdo["mean"] * 1e-3) / 1e9, 1),
                                       "contiguous_call": {"ms": round(tdc["mean"], 4), "ms_best": round(tdc["best"], 4),
                                                           "GB/s": round(dec_bytes / (tdc["mean"] * 1e-3) / 1e9, 1)}},
+                   "batch_sweep": sweep,
                    "graph_replay": {"ms": round(tgr["mean"], 4), "ms_best": round(tgr["best"], 4),
                                     "host_us_per_launch": round(graph_host, 1),
                                     "eager_host_us_per_call": round(eager_host, 1)},

@@ -193,8 +193,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
     // same pace, so the workgroups sharing an XCD read each Q / dO tile while it is in L2.
     // The copies of step k+1 (Q and dO tiles: NDMA row copies each per wave) are spread
     // over the matrix loop of step k, one every two matrix instructions, so the load path
-    // is busy while the matrix cores are; only the small row-statistics copy is issued
-    // at the top of the step.
+    // is busy while the matrix cores are, and so is the small row-statistics copy.
     const int tq_last = tq0 + nq - 1;
     static_assert(2 * NDMA <= KS * RB / 2, "every copy needs a slot in the S / dP loop");
     // Row tiles are visited from the last one down (heads innermost).  With a window every key
@@ -233,6 +232,36 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
     dma_rows<D, MQ, 4>(Qs[0], tile_src_rows<MQ>(qrow, a.q_ss, len - i00), wave, lane);
     dma_rows<D, MQ, 4>(dOs[0], tile_src_rows<MQ>(drow, a.do_ss, len - i00), wave, lane);
     stats(so, i00, 0);
+    // dS for the dQ product, this lane's key.  At head_dim 512 the dS of step k is stored at the
+    // top of step k+1, after its wait, so that the wait there is for the tile copies alone and
+    // the store has a whole step to complete.  ds_pend holds query rows 8 xh + 4 g2 + (0..3)
+    // and 8 xh + 8 + 4 g2 + (0..3) of the block; lanes l and l + 32 trade four of them so that
+    // each holds 8 consecutive rows (8 xh + 8 g2 ..) and writes them with one 16-byte store.
+    static_assert(RB == 1, "one 32-row block per step");
+    bf16x8 ds_pend = zero_bf16x8();
+    int pend_i0 = 0;
+    bf16* pend_dsh = dshead;
+    auto store_pending = [&]() {
+      const int xh = score_wave ? 0 : 2;
+      if (pend_i0 / kDsRows != ds_qt) {
+        ds_qt = pend_i0 / kDsRows;
+        ds_bi = ds_block_index(ds_qt, (j0 / kDsKeys) + kb, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
+      }
+      const int64_t bi = ds_bi;
+      if (bi < 0) return;
+      uint32_t w[4];
+      __builtin_memcpy(w, &ds_pend, 16);
+      const uint32_t give0 = g2 ? w[0] : w[2], give1 = g2 ? w[1] : w[3];
+      const auto r0 = __builtin_amdgcn_permlane32_swap(give0, give0, false, false);
+      const auto r1 = __builtin_amdgcn_permlane32_swap(give1, give1, false, false);
+      // r[0] carries the lower half's value to every lane, r[1] the upper half's
+      const uint32_t got0 = g2 ? r0[0] : r0[1], got1 = g2 ? r1[0] : r1[1];
+      const uint32_t o[4] = {g2 ? got0 : w[0], g2 ? got1 : w[1], g2 ? w[2] : got0, g2 ? w[3] : got1};
+      bf16* dst = pend_dsh + bi * kDsBlockElems + ds_elem(pend_i0 & (kDsRows - 1), ln) + 8 * xh + 8 * g2;
+      uint4 v;
+      __builtin_memcpy(&v, o, 16);
+      *reinterpret_cast<uint4*>(dst) = v;
+    };
     for (int k = 0; k < nsteps; ++k) {
       const int buf = k & 1;
       const int i0 = tcur * MQ;
@@ -250,6 +279,9 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
       const TileSrc dn = tile_src_rows<MQ>(drn, a.do_ss, has_next ? len - i0n : 0);
       wait_vmcnt<0>();
       barrier_lds();  // step k is in LDS; every wave is done with step k-1
+      if constexpr (!LOWREG) {
+        if (k > 0) store_pending();
+      }
 
       f32x16 sacc[RB];
 #pragma unroll
@@ -286,6 +318,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
             sacc[rb] = E16<F16>::mma32(f[rb][t % (PF + 1)], kv[t], sacc[rb]);
             // copy slots: one every two matrix instructions, or (DMA_EARLY) all at the first ones
             const int slot = t * RB + rb;
+            if (t == 1 && rb == 0 && has_next) stats(son, i0n, buf ^ 1);
             if (DMA_EARLY ? slot < 2 * NDMA : ((slot & 1) == 0 && slot / 2 < 2 * NDMA)) {
               const int j = DMA_EARLY ? slot : slot / 2;
               if (j < NDMA)
@@ -396,38 +429,13 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
         mine[64 + lane] = db;
         ds_out[rb] = db;
       }
-      // dS for the dQ product, this lane's key, issued under the first gradient products at head
-      // dim 512 (its address arithmetic and store then overlap the matrix work).  ds_out holds query rows
-      // 8 xh + 4 g2 + (0..3) and 8 xh + 8 + 4 g2 + (0..3) of the block; lanes l and l + 32 trade
-      // four of them so that each holds 8 consecutive rows (8 xh + 8 g2 ..) and writes them with
-      // one 16-byte store.
-      auto store_ds = [&]() {
-        if (i0 / kDsRows != ds_qt) {  // the block changes every kDsRows / MQ query tiles
-          ds_qt = i0 / kDsRows;
-          ds_bi = ds_block_index(ds_qt, (j0 / kDsKeys) + kb, a.causal, a.window, dlt, lenk, a.ds_tri, a.ds_cnt);
-        }
-        const int64_t bi = ds_bi;
-        if (bi < 0) return;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          uint32_t w[4];
-          __builtin_memcpy(w, &ds_out[rb], 16);
-          const uint32_t give0 = g2 ? w[0] : w[2], give1 = g2 ? w[1] : w[3];
-          const auto r0 = __builtin_amdgcn_permlane32_swap(give0, give0, false, false);
-          const auto r1 = __builtin_amdgcn_permlane32_swap(give1, give1, false, false);
-          // r[0] carries the lower half's value to every lane, r[1] the upper half's
-          const uint32_t got0 = g2 ? r0[0] : r0[1], got1 = g2 ? r1[0] : r1[1];
-          const uint32_t o[4] = {g2 ? got0 : w[0], g2 ? got1 : w[1], g2 ? w[2] : got0, g2 ? w[3] : got1};
-          bf16* dst = dshead + bi * kDsBlockElems + ds_elem((i0 + 32 * rb) & (kDsRows - 1), ln) + 8 * xh + 8 * g2;
-          uint4 v;
-          __builtin_memcpy(&v, o, 16);
-          *reinterpret_cast<uint4*>(dst) = v;
-        }
-      };
-      // (at head_dim 256 the registers to carry the values across the barrier are not there)
-      if constexpr (LOWREG) store_ds();
+      // the dS of the step: stored now at head_dim 256 (there are no registers to carry it across
+      // the barrier), at the top of the next step at 512
+      ds_pend = ds_out[0];
+      pend_i0 = i0;
+      pend_dsh = dshead;
+      if constexpr (LOWREG) store_pending();
       barrier_lds();
-      if (has_next) stats(son, i0n, buf ^ 1);
       if constexpr (LOWREG) {
         // one 16-row half at a time: its P and dS fragments, then per d block the four products;
         // the transposed dO and Q fragments are read one (half, d block) step ahead
@@ -488,7 +496,6 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
             dvacc[1][d] = E16<F16>::mma32(ado, p1, dvacc[1][d]);
             dkacc[0][d] = E16<F16>::mma32(aq, s0, dkacc[0][d]);
             dkacc[1][d] = E16<F16>::mma32(aq, s1, dkacc[1][d]);
-            if (s == 0 && d == 0) store_ds();
             ado = ado_n;
             aq = aq_n;
             __builtin_amdgcn_sched_barrier(0);
@@ -502,6 +509,8 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void bwd_dkdv_kernel(AttnArg
       so = son;
       dshead += wrap ? -(rs - 1) * ds_step : ds_step;
     }
+    if constexpr (!LOWREG) store_pending();
+    wait_vmcnt<0>();  // no copy into LDS may be in flight when the workgroup ends
   }
 
   // dV^T / dK^T blocks: lane = key j0 + 32 x + ln, register r = d 32 (dsl + d) + 8 (r/4) + 4 g2 + r%4

@@ -313,7 +313,9 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      barrier_lds();  // every wave is done with Vs
+      // Every wave is done with Vs before V(jt+1) is copied: with the copies spread, V(jt+1) is
+      // copied after the next tile's first barrier, which every wave reaches after these reads.
+      if constexpr (!SPREAD) barrier_lds();
       if constexpr (PAGED) {
         if (has_next)
           dma_rows_paged<D, N, 4>(Vs, paged_tile_src<N>(vbase, a.v_sb, a.v_ss, phys, a.num_pages, lenk - j0 - N),

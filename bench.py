@@ -319,9 +319,20 @@ def prefill_workload(name, steps, stream):
                        randn((len(idx), n, w.Hkv, w.D))))
     o = torch.empty_like(q)
     lse = torch.empty((w.Hq, T), device="cuda:0", dtype=torch.float32)
+    # with decode rows beside the chunk, the step runs attn_fwd_paged_split (decode rows split over
+    # several workgroups, one workspace for every call); attn_fwd_paged is timed beside it
+    split = 1 in new
+    ws = torch.empty(sdpt.binding.attn_fwd_paged_workspace_bytes(q, kc, table, cu, maxq), device="cuda:0",
+                     dtype=torch.uint8) if split else None
+
+    def unsplit():
+        sdpt.attn_fwd_paged(q, kc, vc, table, cu, ctx_d, maxq, scale=w.scale, out=o, lse=lse)
 
     def attn():
-        sdpt.attn_fwd_paged(q, kc, vc, table, cu, ctx_d, maxq, scale=w.scale, out=o, lse=lse)
+        if split:
+            sdpt.attn_fwd_paged_split(q, kc, vc, table, cu, ctx_d, maxq, scale=w.scale, out=o, lse=lse, workspace=ws)
+        else:
+            unsplit()
 
     def append():
         for tg, cg, kn, vn in groups:
@@ -343,6 +354,13 @@ def prefill_workload(name, steps, stream):
            "tflops": round(ff / ta["median"] / 1e9, 2), "frac": round(ff / ta["median"] / 1e9 / PEAK_BF16_TFLOPS, 4),
            "step_ms_with_append": round(tst["median"], 4),
            "step_tflops_with_append": round(ff / tst["median"] / 1e9, 2), "kernels": kern}
+    if split:
+        unsplit()
+        torch.cuda.synchronize()
+        tu = time_calls(unsplit, steps, stream)
+        res["call"] = "attn_fwd_paged_split"
+        res["unsplit"] = {"call": "attn_fwd_paged", "ms": round(tu["median"], 4), "ms_best": round(tu["best"], 4),
+                          "tflops": round(ff / tu["median"] / 1e9, 2)}
     if w.B == 1:
         L, n = ctx[0], new[0]
         kg = torch.empty((1, L, w.Hkv, w.D), device="cuda:0", dtype=torch.bfloat16)
@@ -362,7 +380,7 @@ def prefill_workload(name, steps, stream):
         res["gathered_path"] = {"ms": round(tg["median"], 4), "tflops": round(ff / tg["median"] / 1e9, 2),
                                 "kernels": kernel_times(gathered, steps)}
         del kg, vg, o4, l4
-    del kc, vc, q, groups, o
+    del kc, vc, q, groups, o, ws
     return res
 
 

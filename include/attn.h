@@ -470,6 +470,31 @@ attn_status attn_fwd_paged(const attn_paged_shape* shape,
                            float scale, int window, float softcap,
                            attn_tensor o, float* lse, void* stream);
 
+/*
+ * attn_fwd_paged_split: attn_fwd_paged for a serving step whose decode rows sit beside prompt
+ * chunks (the mixed prefill / decode step of the page "flex_attention + paged KV + CUDA graphs
+ * vs vLLM", section "What's left on the table").  A decode row (a sequence with one new token)
+ * whose visible keys span more than 8 tiles of 32 keys is cut into at most 16 pieces of whole
+ * tiles, each computed by its own workgroup into the workspace; a second kernel combines a
+ * row's pieces, in piece order, by log-sum-exp weighting (the combination of partial results
+ * over disjoint key sets, as attn_lse_merge) and writes its O and LSE.  Without the split, a
+ * decode row's one workgroup walks the whole context for 1/16 of a prompt tile's work.
+ * Arguments as attn_fwd_paged, and
+ *   workspace  device, at least attn_fwd_paged_workspace_bytes(shape) bytes, 256-byte aligned
+ *              (fp32 O and LSE per piece: B * Hq * 16 * (D + 1) * 4 bytes, rounded up); its
+ *              contents on return are unspecified; missing or too small: ATTN_ERR_WORKSPACE
+ * Rows that are not split get exactly attn_fwd_paged's O and LSE (bit for bit); a split row's
+ * O is the fp32 combination of its pieces' normalised O rounded once to 16 bits, equal to
+ * attn_fwd_paged's within rounding.  Two launches; calls on one stream that share a workspace
+ * are ordered by the stream.
+ */
+attn_status attn_fwd_paged_split(const attn_paged_shape* shape,
+                                 attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                                 const int32_t* block_table, const int32_t* cu_q, const int32_t* ctx_lens,
+                                 float scale, int window, float softcap,
+                                 attn_tensor o, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace sizes in bytes.  varlen: 0 dense, 1 pad_mask, 2 cu_seqlens; causal and
  * window as in the call.  Return 0 for arguments that the matching call would reject.
  * Each call computes its own requirement and the caller owns the memory, so one
@@ -486,6 +511,8 @@ attn_status attn_fwd_paged(const attn_paged_shape* shape,
 size_t attn_fwd_workspace_bytes(const attn_shape* shape, int varlen);
 size_t attn_bwd_workspace_bytes(const attn_shape* shape, int varlen, int causal, int window);
 size_t paged_decode_workspace_bytes(const attn_decode_shape* shape);
+/* For attn_fwd_paged_split; 0 for a shape that it would reject. */
+size_t attn_fwd_paged_workspace_bytes(const attn_paged_shape* shape);
 /* For attn_bwd_chunk; 0 for arguments that it would reject. */
 size_t attn_bwd_chunk_workspace_bytes(const attn_chunk_shape* shape, int causal, int window,
                                       int64_t q_pos0, int64_t k_pos0);

@@ -62,7 +62,8 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_fwd_chunk", "attn_bwd_chunk", "attn_lse
            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_bwd_chunk_workspace_bytes",
            "paged_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "attn_version",
            "attn_profile", "attn_profile_read", "attn_count_restarts", "paged_decode_noalloc",
-           "paged_decode_noalloc_max_bytes", "attn_peak_probe", "attn_fwd_paged", "paged_decode_contiguous",
+           "paged_decode_noalloc_max_bytes", "attn_peak_probe", "attn_fwd_paged", "attn_fwd_paged_split", "attn_fwd_paged_workspace_bytes",
+           "paged_decode_contiguous",
            "paged_decode_graphs_create", "paged_decode_graphs_launch", "paged_decode_graphs_destroy")
 
 
@@ -131,6 +132,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_paged.argtypes = [P(AttnPagedShape), AttnTensor, AttnTensor, AttnTensor, vp, vp, vp, ctypes.c_float,
                                    ctypes.c_int, ctypes.c_float, AttnTensor, vp, vp]
     lib.attn_fwd_paged.restype = ctypes.c_int
+    lib.attn_fwd_paged_workspace_bytes.argtypes = [P(AttnPagedShape)]
+    lib.attn_fwd_paged_workspace_bytes.restype = sz
+    lib.attn_fwd_paged_split.argtypes = [P(AttnPagedShape), AttnTensor, AttnTensor, AttnTensor, vp, vp, vp,
+                                         ctypes.c_float, ctypes.c_int, ctypes.c_float, AttnTensor, vp, vp, sz, vp]
+    lib.attn_fwd_paged_split.restype = ctypes.c_int
     lib.attn_debug.argtypes = [ctypes.c_int]
     lib.attn_debug.restype = ctypes.c_int
     lib.attn_fwd_workspace_bytes.argtypes = [P(AttnShape), ctypes.c_int]
@@ -658,14 +664,7 @@ def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: t
     return k_out, v_out
 
 
-def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
-                   cu_q: torch.Tensor, ctx_lens: torch.Tensor, max_q: int, scale: Optional[float] = None,
-                   window: int = 0, softcap: float = 0.0, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O (T,Hq,D), LSE (Hq,T) of each sequence's new query rows q (T,Hq,D), packed by cu_q (B+1), against
-    its paged cache (num_pages, page_size, Hkv, D) read through block_table (B, max_pages_per_seq);
-    ctx_lens (B) counts the cached tokens, the new ones included (causal; see attn_fwd_paged)."""
-    lib = load_library()
+def _paged_fwd_args(q, k_cache, v_cache, block_table, cu_q, ctx_lens, max_q, scale, out, lse):
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _half(t, n, q.dtype)
     for t, n in ((block_table, "block_table"), (cu_q, "cu_q"), (ctx_lens, "ctx_lens")):
@@ -690,10 +689,53 @@ def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     _expect(lse, (Hq, T), "lse")
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise TypeError("lse must be a contiguous float32 tensor")
+    return shape, float(scale), out, lse
+
+
+def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   cu_q: torch.Tensor, ctx_lens: torch.Tensor, max_q: int, scale: Optional[float] = None,
+                   window: int = 0, softcap: float = 0.0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O (T,Hq,D), LSE (Hq,T) of each sequence's new query rows q (T,Hq,D), packed by cu_q (B+1), against
+    its paged cache (num_pages, page_size, Hkv, D) read through block_table (B, max_pages_per_seq);
+    ctx_lens (B) counts the cached tokens, the new ones included (causal; see attn_fwd_paged)."""
+    lib = load_library()
+    shape, scale, out, lse = _paged_fwd_args(q, k_cache, v_cache, block_table, cu_q, ctx_lens, max_q, scale, out, lse)
     st = lib.attn_fwd_paged(ctypes.byref(shape), _tensor(q, True), _tensor(k_cache, False), _tensor(v_cache, False),
-                            block_table.data_ptr(), cu_q.data_ptr(), ctx_lens.data_ptr(), float(scale), int(window),
+                            block_table.data_ptr(), cu_q.data_ptr(), ctx_lens.data_ptr(), scale, int(window),
                             float(softcap), _tensor(out, True), lse.data_ptr(), _stream())
     _check(st, "attn_fwd_paged")
+    return out, lse
+
+
+def attn_fwd_paged_workspace_bytes(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+                                   cu_q: torch.Tensor, max_q: int) -> int:
+    """Workspace bytes attn_fwd_paged_split needs for these shapes (0 if it would refuse them)."""
+    T, Hq, D = q.shape
+    num_pages, page_size, Hkv, _ = k_cache.shape
+    shape = AttnPagedShape(cu_q.numel() - 1, int(max_q), T, Hq, Hkv, D, _DT16.get(q.dtype, -1), page_size, num_pages,
+                           block_table.shape[1])
+    return int(load_library().attn_fwd_paged_workspace_bytes(ctypes.byref(shape)))
+
+
+def attn_fwd_paged_split(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                         cu_q: torch.Tensor, ctx_lens: torch.Tensor, max_q: int, scale: Optional[float] = None,
+                         window: int = 0, softcap: float = 0.0, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """attn_fwd_paged with decode rows (sequences of one new token) split over several workgroups
+    whose partial results a second kernel merges; workspace: a uint8 device tensor of at least
+    attn_fwd_paged_workspace_bytes (allocated here when None)."""
+    lib = load_library()
+    shape, scale, out, lse = _paged_fwd_args(q, k_cache, v_cache, block_table, cu_q, ctx_lens, max_q, scale, out, lse)
+    nbytes = int(lib.attn_fwd_paged_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
+    st = lib.attn_fwd_paged_split(ctypes.byref(shape), _tensor(q, True), _tensor(k_cache, False),
+                                  _tensor(v_cache, False), block_table.data_ptr(), cu_q.data_ptr(), ctx_lens.data_ptr(),
+                                  scale, int(window), float(softcap), _tensor(out, True), lse.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "attn_fwd_paged_split")
     return out, lse
 
 

@@ -455,7 +455,7 @@ struct PagedKV {
 
 attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, const int32_t* cu_seqlens,
                     const uint8_t* pad_mask, void* workspace, hipStream_t s, FwdOut mode = FwdOut::half,
-                    attn_tensor final16 = {}, const PagedKV* paged = nullptr) {
+                    attn_tensor final16 = {}, const PagedKV* paged = nullptr, float* split_ws = nullptr) {
   int32_t* meta = static_cast<int32_t*>(workspace);
   attn_status st;
   if ((st = debug_check_varlen(c, cu_seqlens, pad_mask, s))) return st;
@@ -491,8 +491,26 @@ attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, co
   a.lse = lse;
   a.restarts = g_restarts;
   plan_rows(a, attn::kFwdRows);
-  return launch(paged ? "attn_fwd_paged" : mode == FwdOut::merge ? "attn_fwd_merge" : "attn_fwd", s,
-                a.total_items, [&] { return attn::launch_fwd(a, c.D, s); });
+  // Decode rows are split only while the batch's units leave compute units without a workgroup
+  // (with one per compute unit a row's single workgroup already streams its keys at the memory's
+  // pace, and its pieces would add their start-up and a merge), and only when a sequence can have
+  // one new token (it cannot when every sequence has max_q > 1 of them).
+  if (split_ws != nullptr && ((int64_t)a.B * a.Hkv * a.nhb >= kComputeUnits ||
+                              (c.S > 1 && c.total == c.B * c.S)))
+    split_ws = nullptr;
+  if (paged != nullptr && split_ws != nullptr) {
+    // split decode rows: kSplitMax more items per unit, after every query tile's, hold the pieces
+    a.split_slot0 = a.nqt;
+    a.nqt += attn::kSplitMax;
+    a.total_items = a.B * a.Hkv * a.nhb * a.nqt;
+    a.per_xcd = per_xcd_for(a, a.total_items, a.nqt);
+    a.split_o = split_ws;
+    a.split_lse = split_ws + (int64_t)a.B * a.Hq * attn::kSplitMax * c.D;
+  }
+  attn_status st2 = launch(paged ? "attn_fwd_paged" : mode == FwdOut::merge ? "attn_fwd_merge" : "attn_fwd", s,
+                           a.total_items, [&] { return attn::launch_fwd(a, c.D, s); });
+  if (st2 != ATTN_OK || a.split_o == nullptr) return st2;
+  return launch("attn_fwd_split_merge", s, a.B * a.Hq, [&] { return attn::launch_fwd_split_merge(a, c.D, s); });
 }
 
 attn_status run_bwd(const Call& c, const Tensors& t, float scale, const float* lse, const int32_t* cu_seqlens,
@@ -1034,9 +1052,19 @@ static attn_status check_paged_shape(const attn_paged_shape* s) {
   return ATTN_OK;
 }
 
-attn_status attn_fwd_paged(const attn_paged_shape* shape, attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
-                           const int32_t* block_table, const int32_t* cu_q, const int32_t* ctx_lens, float scale,
-                           int window, float softcap, attn_tensor o, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Workspace of the split paged forward: per (sequence, query head) kSplitMax pieces of an fp32
+// O row and an LSE.
+size_t paged_split_bytes(const attn_paged_shape& sh) {
+  return round_up((size_t)sh.B * sh.Hq * attn::kSplitMax * (sh.D + 1) * sizeof(float));
+}
+
+attn_status fwd_paged(const attn_paged_shape* shape, attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                      const int32_t* block_table, const int32_t* cu_q, const int32_t* ctx_lens, float scale,
+                      int window, float softcap, attn_tensor o, float* lse, float* split_ws, void* stream) {
   attn_status st = check_paged_shape(shape);
   if (st != ATTN_OK) return st;
   const attn_paged_shape& sh = *shape;
@@ -1072,7 +1100,36 @@ attn_status attn_fwd_paged(const attn_paged_shape* shape, attn_tensor q, attn_te
   c.softcap = softcap;
   const Tensors t = {q, k_cache, v_cache, o, {}, {}, {}, {}};
   const PagedKV pg = {block_table, ctx_lens, k_cache.stride_b, v_cache.stride_b, sh.max_pages_per_seq, sh.num_pages};
-  return run_fwd(c, t, scale, lse, cu_q, nullptr, nullptr, s, FwdOut::half, {}, &pg);
+  return run_fwd(c, t, scale, lse, cu_q, nullptr, nullptr, s, FwdOut::half, {}, &pg, split_ws);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_paged(const attn_paged_shape* shape, attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                           const int32_t* block_table, const int32_t* cu_q, const int32_t* ctx_lens, float scale,
+                           int window, float softcap, attn_tensor o, float* lse, void* stream) {
+  return fwd_paged(shape, q, k_cache, v_cache, block_table, cu_q, ctx_lens, scale, window, softcap, o, lse, nullptr,
+                   stream);
+}
+
+size_t attn_fwd_paged_workspace_bytes(const attn_paged_shape* shape) {
+  if (check_paged_shape(shape) != ATTN_OK) return 0;
+  return paged_split_bytes(*shape);
+}
+
+attn_status attn_fwd_paged_split(const attn_paged_shape* shape, attn_tensor q, attn_tensor k_cache,
+                                 attn_tensor v_cache, const int32_t* block_table, const int32_t* cu_q,
+                                 const int32_t* ctx_lens, float scale, int window, float softcap, attn_tensor o,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_paged_shape(shape);
+  if (st != ATTN_OK) return st;
+  const size_t need = paged_split_bytes(*shape);
+  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return ATTN_ERR_WORKSPACE;
+  return fwd_paged(shape, q, k_cache, v_cache, block_table, cu_q, ctx_lens, scale, window, softcap, o, lse,
+                   static_cast<float*>(workspace), stream);
 }
 
 int attn_debug(int on) {

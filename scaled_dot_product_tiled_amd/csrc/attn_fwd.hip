@@ -80,17 +80,30 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
     off = a.seq_off ? a.seq_off[b] : 0;
   }
   len = min(max(len, 0), a.S);
-  if constexpr (PAGED) {
-    // The unit's r-th item takes the r-th tile counted back from the sequence's last row, so
-    // that every sequence's heaviest tile (its newest queries see the most keys) comes in the
-    // first round of the deal, decode rows included; items past the sequence's rows exit.
-    qt = (len + a.mpos - 1) / a.mpos - 1 - (a.nqt - 1 - qt);
-    if (qt < 0) return;
-  }
   // key rows; a paged sequence's are its cached keys, clamped to its table row, and its
   // queries are the newest of them
   const int lenk = PAGED ? min(max(a.kv_len[b], 0), a.max_pages * 16) : a.seq_len ? len : a.Sk;
   const int dlt = PAGED ? lenk - len : a.q_shift;
+  [[maybe_unused]] int piece = -1, piece_t0 = 0, piece_ch = 0;  // split decode row: its key tiles
+  if constexpr (PAGED) {
+    // The unit's r-th item takes the r-th tile counted back from the sequence's last row, so
+    // that every sequence's heaviest tile (its newest queries see the most keys) comes in the
+    // first round of the deal, decode rows included; items past the sequence's rows exit.  The
+    // pieces of a split decode row take the unit's items split_slot0 + p, past every sequence's
+    // query tiles, so that they are dealt after the long tiles of the prompt chunks and fill the
+    // compute units those leave.
+    const int slot = a.nqt - 1 - qt;
+    qt = (len + a.mpos - 1) / a.mpos - 1 - slot;
+    if (a.split_o != nullptr && len == 1) {
+      const int np = decode_pieces(lenk, a.window, piece_t0, piece_ch);
+      if (np > 1) {
+        piece = slot - a.split_slot0;
+        if (piece < 0 || piece >= np) return;
+        qt = 0;
+      }
+    }
+    if (qt < 0) return;
+  }
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -117,8 +130,14 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
   const int plast = min(p0 + a.mpos, len) - 1;
   const int jhi = (plast < p0) ? 0 : (a.causal ? min(plast + dlt + 1, lenk) : lenk);
   const int jlo = a.window > 0 ? max(0, p0 + dlt - a.window + 1) : 0;
-  const int t_lo = jlo / N;
-  const int t_hi = jhi > jlo ? (jhi + N - 1) / N : t_lo;
+  int t_lo = jlo / N;
+  int t_hi = jhi > jlo ? (jhi + N - 1) / N : t_lo;
+  if constexpr (PAGED) {
+    if (piece >= 0) {  // the same tiles decode_pieces cut (N = 32)
+      t_lo = piece_t0 + piece * piece_ch;
+      t_hi = min(t_hi, t_lo + piece_ch);
+    }
+  }
 
   const bf16* kbase = a.k + (PAGED ? 0 : b * a.k_sb + (int64_t)off * a.k_ss) + g * a.k_sh;
   const bf16* vbase = a.v + (PAGED ? 0 : b * a.v_sb + (int64_t)off * a.v_ss) + g * a.v_sh;
@@ -363,13 +382,24 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
             st4<F16>(op + 32 * d + 8 * qa, oacc[d][4 * qa] * inv, oacc[d][4 * qa + 1] * inv,
                      oacc[d][4 * qa + 2] * inv, oacc[d][4 * qa + 3] * inv);
       };
-      if (a.out_f32)
-        store(a.out_f32 + oo);  // a partial over one key chunk: rounded once, when the partials are merged
+      float* o32 = a.out_f32 ? a.out_f32 + oo : nullptr;
+      float* lp = a.lse + (b * a.st_sb + h * a.st_sh + off + pos);
+      bool ninf = a.empty_lse_ninf;
+      if constexpr (PAGED) {
+        if (piece >= 0) {
+          // a piece of a split decode row: its normalised O in fp32 and its LSE (-inf without a
+          // visible key), for fwd_split_merge
+          const int64_t pi = ((int64_t)unit * kSplitMax + piece) * a.hpt + hh;
+          o32 = a.split_o + pi * D + 4 * g2;
+          lp = a.split_lse + pi;
+          ninf = true;
+        }
+      }
+      if (o32)
+        store(o32);  // a partial over one key chunk: rounded once, when the partials are merged
       else
         store(a.out + oo);
-      if (g2 == 0)
-        a.lse[b * a.st_sb + h * a.st_sh + off + pos] =
-            l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : (a.empty_lse_ninf ? -INFINITY : 0.f);
+      if (g2 == 0) *lp = l_run > 0.f ? kLn2 * (m_ref + __log2f(l_run)) : (ninf ? -INFINITY : 0.f);
     }
   }
 }
@@ -390,6 +420,75 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_merge_kernel(AttnAr
 template <int D, int N, bool EXACT, bool SOFTCAP, bool F16>
 __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void fwd_paged_kernel(AttnArgs a) {
   fwd_body<D, N, EXACT, SOFTCAP, F16, false, true>(a);
+}
+
+// Merge of the pieces of split decode rows (paged forward).  One wave per (sequence, query head);
+// a row that was not split exits.  Over the row's pieces p, in piece order:
+//   L = ln sum_p e^LSE_p,  O = sum_p e^(LSE_p - L) O_p,
+// the log-sum-exp combination of partial results over disjoint key sets; O is rounded to the
+// 16-bit type.  Every piece holds a visible key, so L is finite for finite scores.
+template <int D, bool F16>
+__global__ __launch_bounds__(256) void fwd_split_merge_kernel(AttnArgs a) {
+  constexpr int E = D / 64;  // elements per lane
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= a.B * a.Hq) return;
+  const int b = w / a.Hq, h = w - b * a.Hq;
+  const int off = min(max(a.seq_off[b], 0), a.total);
+  const int len = min(min(max(a.seq_off[b + 1] - off, 0), a.total - off), a.S);
+  if (len != 1) return;
+  const int lenk = min(max(a.kv_len[b], 0), a.max_pages * 16);
+  int t0, ch;
+  const int np = decode_pieces(lenk, a.window, t0, ch);
+  if (np <= 1) return;
+  const int g = h / a.r, hg = h - g * a.r;
+  const int unit = (b * a.Hkv + g) * a.nhb + hg / a.hpt;
+  const int64_t i0 = (int64_t)unit * kSplitMax * a.hpt + hg % a.hpt;  // piece p: i0 + p hpt
+  // lane p < np holds piece p's LSE and then its weight
+  const float lp = lane < np ? a.split_lse[i0 + lane * a.hpt] : -INFINITY;
+  float m = lp;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
+  const float wl = (lane < np && m > -INFINITY) ? expf(lp - m) : 0.f;
+  float sum = 0.f;
+  for (int p = 0; p < np; ++p) sum += __shfl(wl, p);  // piece order
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const float* src = a.split_o + i0 * D + E * lane;
+#pragma unroll 4
+  for (int p = 0; p < np; ++p) {
+    const float wt = __shfl(wl, p);
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e) {
+      const float4 x = reinterpret_cast<const float4*>(src + (int64_t)p * a.hpt * D)[e];
+      acc[4 * e] += wt * x.x;
+      acc[4 * e + 1] += wt * x.y;
+      acc[4 * e + 2] += wt * x.z;
+      acc[4 * e + 3] += wt * x.w;
+    }
+  }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  auto* op = a.out + b * a.o_sb + (int64_t)off * a.o_ss + h * a.o_sh + E * lane;
+#pragma unroll
+  for (int e = 0; e < E / 4; ++e)
+    st4<F16>(op + 4 * e, acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv, acc[4 * e + 3] * inv);
+  if (lane == 0) a.lse[b * a.st_sb + h * a.st_sh + off] = sum > 0.f ? m + logf(sum) : 0.f;
+}
+
+hipError_t launch_fwd_split_merge(const AttnArgs& a, int D, hipStream_t stream) {
+  const dim3 grid((a.B * a.Hq + 3) / 4), block(256);
+  if (D == 512 && a.f16)
+    hipLaunchKernelGGL((fwd_split_merge_kernel<512, true>), grid, block, 0, stream, a);
+  else if (D == 512)
+    hipLaunchKernelGGL((fwd_split_merge_kernel<512, false>), grid, block, 0, stream, a);
+  else if (D == 256 && a.f16)
+    hipLaunchKernelGGL((fwd_split_merge_kernel<256, true>), grid, block, 0, stream, a);
+  else if (D == 256)
+    hipLaunchKernelGGL((fwd_split_merge_kernel<256, false>), grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 template <int D, bool EXACT, bool SOFTCAP, bool F16>

@@ -92,7 +92,36 @@ struct AttnArgs {
   const int32_t* table;
   const int32_t* kv_len;
   int max_pages, num_pages;
+  // paged forward with split decode rows (split_o not NULL): a sequence with one new token
+  // whose keys span more than kSplitMinTiles tiles is cut into pieces (decode_pieces), each a
+  // workgroup (the unit's item split_slot0 + piece) that writes its normalised fp32 O to split_o[((unit * kSplitMax + piece) * hpt +
+  // head in the tile) * D ..] and its LSE to split_lse[(unit * kSplitMax + piece) * hpt + head
+  // in the tile]; fwd_split_merge combines them
+  float* split_o;
+  float* split_lse;
+  int split_slot0;  // a unit's items split_slot0 .. split_slot0 + kSplitMax - 1 hold the pieces
 };
+
+// Split decode rows of the paged forward: at most kSplitMax pieces of at least kSplitMinTiles
+// 32-key tiles each.
+constexpr int kSplitMax = 16;
+constexpr int kSplitMinTiles = 8;
+
+// Pieces of the decode row of a paged sequence with lenk cached keys (its one query sits at
+// position lenk - 1): its key tiles t_lo .. t_lo + n - 1 are cut into pieces of ch tiles (the
+// last one shorter), every piece holding at least one visible key.  Returns the piece count;
+// 1 means the row is not split.
+__host__ __device__ inline int decode_pieces(int lenk, int window, int& t_lo, int& ch) {
+  const int jlo = window > 0 ? (lenk - window > 0 ? lenk - window : 0) : 0;
+  t_lo = jlo / 32;
+  const int n = lenk > jlo ? (lenk + 31) / 32 - t_lo : 0;
+  int ns = (n + kSplitMinTiles - 1) / kSplitMinTiles;
+  ns = ns < kSplitMax ? ns : kSplitMax;
+  ch = n;
+  if (ns <= 1) return 1;
+  ch = (n + ns - 1) / ns;
+  return (n + ch - 1) / ch;
+}
 
 struct DecodeArgs {
   const __bf16* q;
@@ -200,6 +229,7 @@ hipError_t check_varlen_meta(const uint8_t* pad_mask, const int32_t* cu_seqlens,
 hipError_t check_pages_meta(const int32_t* table, int contiguous, const int32_t* ctx, int B, int max_pages,
                             int page_size, int num_pages, hipStream_t stream, bool& bad);
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream);
+hipError_t launch_fwd_split_merge(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream);

@@ -280,18 +280,68 @@ def test_fwd_paged_never_reads_unused_pages_or_slots():
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.parametrize("name", ["mixed_step_d512", "paged_prefill_d512"])
-def test_paged_forward_full_size_sampled_rows(name):
+# (D, dtype, window, softcap, contexts, new rows) for the split paged forward: decode rows whose
+# keys span 9, 10, 66 and 128 tiles (2, 2, 9 and 16 pieces) beside a prompt chunk; a window that
+# leaves 16 tiles (2 pieces) beside a short prompt; a batch of decode rows only (one item slot per
+# unit without the split) in fp16 with a softcap; decode rows at or under 8 tiles (not split)
+SPLIT_CASES = [
+    (512, "bf16", 0, 0.0, (1000, 4096, 257, 300, 2100, 256), (300, 1, 1, 1, 1, 1)),
+    (256, "bf16", 500, 0.0, (3000, 1200, 40), (1, 64, 1)),
+    (512, "f16", 0, 30.0, (1500, 800, 4000), (1, 1, 1)),
+    (256, "bf16", 0, 0.0, (1030, 33, 700), (1, 1, 20)),
+]
+
+
+@pytest.mark.parametrize("D,dtype,window,softcap,ctx,new", SPLIT_CASES)
+def test_fwd_paged_split_matches_oracle(D, dtype, window, softcap, ctx, new):
+    """attn_fwd_paged_split: every row against the oracle; rows that are not split (every row of a
+    sequence with more than one new token, decode rows of at most 8 key tiles) bit for bit equal to
+    attn_fwd_paged's; split decode rows within the tolerance of attn_fwd_paged's."""
+    w = MIXED.scaled(B=len(ctx), Hq=8, Hkv=2, D=D, dtype=dtype, window=window, ctx=ctx, new=new,
+                     name=f"paged fwd split d{D}")
+    inp = make_prefill_inputs(w, seed=33)
+    say(f"[fwd paged split] D={D} dtype={dtype} window={window} softcap={softcap} ctx={ctx} new={new}")
+    d = _prefill_dev(inp, dtype)
+    kw = dict(scale=w.scale, window=window, softcap=softcap)
+    o, lse = sdpt.attn_fwd_paged_split(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"], **kw)
+    o1, lse1 = sdpt.attn_fwd_paged(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"], **kw)
+    torch.cuda.synchronize()
+    assert all_finite(o, lse)
+    ro, rl = _prefill_oracle(inp, w, softcap)
+    assert max_abs(host(o), ro) <= O_MAX_ABS
+    assert max_abs(host(lse), rl) <= LSE_MAX_ABS
+    ob, ob1, lb, lb1 = host_bits(o), host_bits(o1), lse.cpu().numpy(), lse1.cpu().numpy()
+    cu = inp["cu_q"]
+    n_split = 0
+    for b in range(w.B):
+        L, n = int(ctx[b]), int(new[b])
+        rows = slice(int(cu[b]), int(cu[b + 1]))
+        lo = max(0, L - window) if window > 0 else 0
+        tiles = (L + 31) // 32 - lo // 32 if L > lo else 0
+        if n == 1 and tiles > 8:
+            n_split += 1
+            assert max_abs(host(o)[rows], host(o1)[rows]) <= O_MAX_ABS, b
+            assert max_abs(lb[:, rows], lb1[:, rows]) <= LSE_MAX_ABS, b
+        else:
+            assert np.array_equal(ob[rows], ob1[rows]), b
+            assert np.array_equal(lb[:, rows], lb1[:, rows]), b
+    assert n_split > 0
+    say(f"[fwd paged split] {n_split} of {w.B} sequences split")
+
+
+@pytest.mark.parametrize("name,split", [("mixed_step_d512", False), ("mixed_step_d512", True),
+                                        ("paged_prefill_d512", False)])
+def test_paged_forward_full_size_sampled_rows(name, split):
     """The benchmark's paged-forward workloads at their full sizes (a 1024-token chunk after 3072
     cached plus 31 decode rows; a 2048-token chunk after 6144 cached; 32 query heads, D = 512):
     every decode row, the chunk's first, last and tile-edge rows and seeded random rows, every
-    head, against the oracle row by row."""
+    head, against the oracle row by row; the mixed step also through attn_fwd_paged_split."""
     w = PREFILL_WORKLOADS[name]
     inp = make_prefill_inputs(w, seed=0)
-    say(f"[{name} full size]")
+    say(f"[{name} full size] split={split}")
     d = _prefill_dev(inp, "bf16")
-    o, lse = sdpt.attn_fwd_paged(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"],
-                                 scale=w.scale)
+    fwd = sdpt.attn_fwd_paged_split if split else sdpt.attn_fwd_paged
+    o, lse = fwd(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], inp["max_q"], scale=w.scale)
     torch.cuda.synchronize()
     assert all_finite(o, lse)
     oh, lh = host(o), lse.cpu().numpy()

@@ -281,6 +281,27 @@ def test_paged_prefill_checks():
     assert lib.attn_last_hip_error() == 0
 
 
+def test_paged_prefill_split_workspace():
+    """attn_fwd_paged_split: fp32 O and LSE for 16 pieces per (sequence, query head), rounded up to
+    256 bytes; a missing, small or misaligned workspace is refused before any launch, and so are
+    the arguments attn_fwd_paged refuses."""
+    lib = load_library()
+    sh = AttnPagedShape(32, 1024, 1055, 32, 4, 512, 0, 16, 7000, 256)
+    need = lib.attn_fwd_paged_workspace_bytes(ctypes.byref(sh))
+    assert need == -(-32 * 32 * 16 * 513 * 4 // 256) * 256
+    assert lib.attn_fwd_paged_workspace_bytes(ctypes.byref(AttnPagedShape(2, 8, 16, 32, 4, 128, 0, 16, 10, 4))) == 0
+    q = AttnTensor(0x10000, 0, 32 * 512, 512)
+    kc = AttnTensor(0x20000, 16 * 4 * 512, 4 * 512, 512)
+
+    def call(ws=0x100000, nbytes=need, scale=0.05, shape=sh):
+        return lib.attn_fwd_paged_split(ctypes.byref(shape), q, kc, kc, 0x3000, 0x3100, 0x3200, scale, 0, 0.0, q,
+                                        0x5000, ws, nbytes, None)
+    assert call(ws=0) == WORKSPACE and call(nbytes=need - 1) == WORKSPACE and call(ws=0x100010) == WORKSPACE
+    assert call(scale=0.0) == INVALID
+    assert call(shape=AttnPagedShape(2, 8, 16, 30, 4, 512, 0, 16, 10, 4)) == INVALID
+    assert lib.attn_last_hip_error() == 0
+
+
 def test_decode_graph_checks():
     """paged_decode_graphs_create refuses bad buckets, a NULL stream and a small workspace before
     any capture; launch refuses a missing graph set."""

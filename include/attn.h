@@ -478,11 +478,15 @@ attn_status attn_fwd_paged(const attn_paged_shape* shape,
  * tiles, each computed by its own workgroup into the workspace; a second kernel combines a
  * row's pieces, in piece order, by log-sum-exp weighting (the combination of partial results
  * over disjoint key sets, as attn_lse_merge) and writes its O and LSE.  Without the split, a
- * decode row's one workgroup walks the whole context for 1/16 of a prompt tile's work.
+ * decode row's one workgroup walks the whole context for 1/16 of a prompt tile's work.  The
+ * split applies while the batch's (sequence, kv head) units number fewer than the 256 compute
+ * units and some sequence can have one new token; the tiles are then dealt by the sequences'
+ * work (new rows x cached keys, ranked on the device), heaviest first, and the pieces after them.
  * Arguments as attn_fwd_paged, and
  *   workspace  device, at least attn_fwd_paged_workspace_bytes(shape) bytes, 256-byte aligned
- *              (fp32 O and LSE per piece: B * Hq * 16 * (D + 1) * 4 bytes, rounded up); its
- *              contents on return are unspecified; missing or too small: ATTN_ERR_WORKSPACE
+ *              (fp32 O and LSE per piece, B * Hq * 16 * (D + 1) * 4 bytes, and the sequences'
+ *              order by work, B * 4 bytes, rounded up); its contents on return are unspecified;
+ *              missing or too small: ATTN_ERR_WORKSPACE
  * Rows that are not split get exactly attn_fwd_paged's O and LSE (bit for bit); a split row's
  * O is the fp32 combination of its pieces' normalised O rounded once to 16 bits, equal to
  * attn_fwd_paged's within rounding.  Two launches; calls on one stream that share a workspace

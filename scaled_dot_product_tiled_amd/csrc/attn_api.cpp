@@ -499,13 +499,24 @@ attn_status run_fwd(const Call& c, const Tensors& t, float scale, float* lse, co
                               (c.S > 1 && c.total == c.B * c.S)))
     split_ws = nullptr;
   if (paged != nullptr && split_ws != nullptr) {
-    // split decode rows: kSplitMax more items per unit, after every query tile's, hold the pieces
+    // split decode rows: kSplitMax more items per unit, after every query tile's, hold the pieces;
+    // the sequences are ranked by work on the device for the deal (paged_split_item)
+    const int U = a.B * a.Hkv * a.nhb;
     a.split_slot0 = a.nqt;
     a.nqt += attn::kSplitMax;
-    a.total_items = a.B * a.Hkv * a.nhb * a.nqt;
-    a.per_xcd = per_xcd_for(a, a.total_items, a.nqt);
+    a.total_items = U * a.nqt;
     a.split_o = split_ws;
     a.split_lse = split_ws + (int64_t)a.B * a.Hq * attn::kSplitMax * c.D;
+    int32_t* order = reinterpret_cast<int32_t*>(split_ws + (int64_t)a.B * a.Hq * attn::kSplitMax * (c.D + 1));
+    const int blocks = U * ((a.split_slot0 + 31) / 32);
+    a.split_nA = 8 * ((blocks + 7) / 8) * 32;
+    a.per_xcd = (a.split_nA + U * attn::kSplitMax) / 8;
+    a.balanced = 0;
+    a.order = order;
+    attn_status st1 = launch("paged_rank", s, a.B, [&] {
+      return attn::launch_paged_rank(cu_seqlens, paged->kv_len, a.B, a.total, c.S, paged->max_pages * 16, order, s);
+    });
+    if (st1 != ATTN_OK) return st1;
   }
   attn_status st2 = launch(paged ? "attn_fwd_paged" : mode == FwdOut::merge ? "attn_fwd_merge" : "attn_fwd", s,
                            a.total_items, [&] { return attn::launch_fwd(a, c.D, s); });
@@ -1059,7 +1070,7 @@ namespace {
 // Workspace of the split paged forward: per (sequence, query head) kSplitMax pieces of an fp32
 // O row and an LSE.
 size_t paged_split_bytes(const attn_paged_shape& sh) {
-  return round_up((size_t)sh.B * sh.Hq * attn::kSplitMax * (sh.D + 1) * sizeof(float));
+  return round_up((size_t)sh.B * sh.Hq * attn::kSplitMax * (sh.D + 1) * sizeof(float) + sizeof(int32_t) * sh.B);
 }
 
 attn_status fwd_paged(const attn_paged_shape* shape, attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,

@@ -47,6 +47,31 @@ namespace attn {
 constexpr float kRefSlack = 32.0f;
 constexpr float kRefSlackF16 = 15.0f;
 
+// Deal of the split paged forward.  Phase A (the first split_nA workgroups) holds every unit's
+// query-tile items in blocks of 32, the blocks of the units ranked by decreasing work (order: the
+// sequences by new rows x cached keys) dealt to the XCDs in a snake order (workgroup k runs on XCD
+// k mod 8), so that a long prompt's tiles fill whole XCDs first and each XCD's L2 serves few
+// units' keys; phase B holds the pieces of split decode rows, round-robin over the units, dealt
+// after every tile.  Returns the item (unit * nqt + slot) or -1.
+__device__ __forceinline__ int paged_split_item(const AttnArgs& a) {
+  const int W = a.nqt, W0 = a.split_slot0, U = a.total_items / W;
+  const int k = blockIdx.x;
+  if (k >= a.split_nA) {
+    const int kb = k - a.split_nA;
+    if (kb >= U * kSplitMax) return -1;
+    const int round = kb / U;
+    return ((kb + round) % U) * W + W0 + round;
+  }
+  const int NB = (W0 + 31) / 32;  // blocks per unit
+  const int x = k & 7, p = k >> 3, j = p >> 5, s = p & 31;
+  const int rho = 8 * j + ((j & 1) ? 7 - x : x);
+  if (rho >= U * NB) return -1;
+  const int ur = rho / NB, slot = (rho - ur * NB) * 32 + s;
+  if (slot >= W0) return -1;
+  const int upb = a.Hkv * a.nhb;
+  return (a.order[ur / upb] * upb + ur % upb) * W + slot;
+}
+
 // MERGE: instead of storing the row's O and LSE, merge them into a running result (fp32 O
 // in out_f32, LSE in lse) by log-sum-exp weighting and optionally round the merged O to the
 // 16-bit out: the chunk-pair forward and the merge of its partial in one pass.
@@ -62,7 +87,9 @@ __device__ __forceinline__ void fwd_body(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 Vs[N * D];
   __shared__ int restart_flag[2][4];
 
-  const int item = xcd_item(a.per_xcd, a.total_items, a.nqt, a.balanced, a.order, a.Hkv * a.nhb);
+  const int item = (PAGED && a.split_nA > 0) ? paged_split_item(a)
+                                             : xcd_item(a.per_xcd, a.total_items, a.nqt, a.balanced, a.order,
+                                                        a.Hkv * a.nhb);
   if (item < 0) return;
   const int unit = item / a.nqt;
   int qt = a.nqt - 1 - (item - unit * a.nqt);  // longest causal rows first

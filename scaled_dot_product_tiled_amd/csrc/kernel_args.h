@@ -100,6 +100,8 @@ struct AttnArgs {
   float* split_o;
   float* split_lse;
   int split_slot0;  // a unit's items split_slot0 .. split_slot0 + kSplitMax - 1 hold the pieces
+  // workgroups of the split deal's first phase (paged_split_item), 0 for the other deals
+  int split_nA;
 };
 
 // Split decode rows of the paged forward: at most kSplitMax pieces of at least kSplitMinTiles
@@ -230,6 +232,8 @@ hipError_t check_pages_meta(const int32_t* table, int contiguous, const int32_t*
                             int page_size, int num_pages, hipStream_t stream, bool& bad);
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_fwd_split_merge(const AttnArgs& a, int D, hipStream_t stream);
+hipError_t launch_paged_rank(const int32_t* cu_q, const int32_t* kv_len, int B, int total, int max_q, int max_keys,
+                             int32_t* order, hipStream_t stream);
 hipError_t launch_bwd_pre(const AttnArgs& a, int D, int rows, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t stream);

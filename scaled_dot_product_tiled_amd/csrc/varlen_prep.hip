@@ -65,6 +65,34 @@ hipError_t launch_varlen_order(const int32_t* seq_len, int B, int32_t* order, hi
   return hipGetLastError();
 }
 
+// Rank of paged sequence b by decreasing work, the product of its new query rows and its cached
+// keys (both clamped as the forward clamps them), ties by index: order[rank] = b.  Used for the
+// deal of the split paged forward (B below the compute-unit count there).
+__global__ __launch_bounds__(256) void paged_rank_kernel(const int32_t* cu_q, const int32_t* kv_len, int B, int total,
+                                                          int max_q, int max_keys, int32_t* order) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  auto work = [&](int s) {
+    const int off = min(max(cu_q[s], 0), total);
+    const int n = min(min(max(cu_q[s + 1] - off, 0), total - off), max_q);
+    return (int64_t)n * min(max(kv_len[s], 0), max_keys);
+  };
+  const int64_t wb = work(b);
+  int rank = 0;
+  for (int o = 0; o < B; ++o) {
+    const int64_t wo = work(o);
+    rank += (wo > wb) | ((wo == wb) & (o < b));
+  }
+  order[rank] = b;
+}
+
+hipError_t launch_paged_rank(const int32_t* cu_q, const int32_t* kv_len, int B, int total, int max_q, int max_keys,
+                             int32_t* order, hipStream_t stream) {
+  hipLaunchKernelGGL(paged_rank_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, cu_q, kv_len, B, total, max_q,
+                     max_keys, order);
+  return hipGetLastError();
+}
+
 // Thread b sums the dS blocks of sequences 0 .. b-1 (O(B^2) reads of B lengths, all from cache;
 // used for B <= kOrderMaxBatch).  With consistent offsets the host's capacity bound holds; with
 // overlapping ones the lengths can sum past the packed rows, and a sequence that would not fit

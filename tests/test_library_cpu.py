@@ -282,13 +282,13 @@ def test_paged_prefill_checks():
 
 
 def test_paged_prefill_split_workspace():
-    """attn_fwd_paged_split: fp32 O and LSE for 16 pieces per (sequence, query head), rounded up to
-    256 bytes; a missing, small or misaligned workspace is refused before any launch, and so are
+    """attn_fwd_paged_split: fp32 O and LSE for 16 pieces per (sequence, query head) and one int32
+    per sequence, rounded up to 256 bytes; a missing, small or misaligned workspace is refused before any launch, and so are
     the arguments attn_fwd_paged refuses."""
     lib = load_library()
     sh = AttnPagedShape(32, 1024, 1055, 32, 4, 512, 0, 16, 7000, 256)
     need = lib.attn_fwd_paged_workspace_bytes(ctypes.byref(sh))
-    assert need == -(-32 * 32 * 16 * 513 * 4 // 256) * 256
+    assert need == -(-(32 * 32 * 16 * 513 * 4 + 4 * 32) // 256) * 256   # pieces, then the deal's sequence order
     assert lib.attn_fwd_paged_workspace_bytes(ctypes.byref(AttnPagedShape(2, 8, 16, 32, 4, 128, 0, 16, 10, 4))) == 0
     q = AttnTensor(0x10000, 0, 32 * 512, 512)
     kc = AttnTensor(0x20000, 16 * 4 * 512, 4 * 512, 512)

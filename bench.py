@@ -23,7 +23,8 @@ the C ABI.  Reported:
             8 chunks, D=512), of the step's workload in IEEE half and with a softcap, and of two
             paged forwards (attn_fwd_paged): a 2048-token prompt chunk after 6144 cached tokens (beside
             the gather + chunk-pair path it replaces) and a serving step mixing a 1024-token chunk
-            with 31 decode rows; not part of the timed step;
+            with 31 decode rows (attn_fwd_paged_split, which splits the decode rows, beside
+            attn_fwd_paged); not part of the timed step;
   measured_peaks  what plain kernels reach on this device (attn_peak_probe): independent bf16
             32x32x16 matrix instructions, a streaming read and a streaming copy;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload on the host cores, and
@@ -279,13 +280,15 @@ def ring_workload(steps, stream, n_chunks=8, chunk=2048, Hq=32, Hkv=4, D=512):
     return res
 
 
-def prefill_workload(name, steps, stream):
+def prefill_workload(name, steps, stream, compare=True):
     """A PREFILL_WORKLOADS step: each sequence's new query rows against its paged cache (16-token
     pages permuted over a pool 1.5x the pages used), K/V read through the table inside
     attn_fwd_paged.  Times the attention call alone and with the step's paged_kv_append of the new
     tokens' K/V; for a single sequence also the gathered path it replaces (append, paged_kv_gather
     of the whole context, attn_fwd_chunk).  TFLOP/s count the causal-visible (query, key) pairs.
-    Values are drawn on the device (torch's generator, seeded) to keep set-up short."""
+    Values are drawn on the device (torch's generator, seeded) to keep set-up short.  compare=False
+    (--workload, the profiled runs) skips the unsplit call, whose forward kernel has the split
+    call's name."""
     import torch
     import scaled_dot_product_tiled_amd as sdpt
     from synth import PREFILL_WORKLOADS
@@ -354,7 +357,7 @@ def prefill_workload(name, steps, stream):
            "tflops": round(ff / ta["median"] / 1e9, 2), "frac": round(ff / ta["median"] / 1e9 / PEAK_BF16_TFLOPS, 4),
            "step_ms_with_append": round(tst["median"], 4),
            "step_tflops_with_append": round(ff / tst["median"] / 1e9, 2), "kernels": kern}
-    if split:
+    if split and compare:
         unsplit()
         torch.cuda.synchronize()
         tu = time_calls(unsplit, steps, stream)
@@ -532,7 +535,7 @@ def profile_workload(args):
     import scaled_dot_product_tiled_amd as sdpt
     stream = torch.cuda.current_stream()
     if args.workload in ("paged_prefill_d512", "mixed_step_d512"):
-        res = prefill_workload(args.workload, args.steps, stream)
+        res = prefill_workload(args.workload, args.steps, stream, compare=False)
     elif args.workload == "decode_d128":
         dw, pools = decode_setup()
         outs = [torch.empty_like(p["q"]) for p in pools]

@@ -160,7 +160,8 @@ WORKLOADS = {
     "paged_prefill_d512": "paged forward, a 2048-token chunk after 6144 cached tokens, Hq=32 Hkv=4 D=512, 16-token "
                           "pages (append + attn_fwd_paged; then append + gather + chunk-pair forward)",
     "mixed_step_d512": "paged forward, a 1024-token chunk after 3072 cached plus 31 decode rows of 512..4096 tokens, "
-                       "Hq=32 Hkv=4 D=512 (append + attn_fwd_paged)",
+                       "Hq=32 Hkv=4 D=512 (append + attn_fwd_paged_split: rank, forward, merge; then "
+                       "attn_fwd_paged alone)",
 }
 
 SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_VALU_MFMA_BUSY_CYCLES",
@@ -170,7 +171,7 @@ N_XCD, N_CU, N_SIMD = 8, 256, 1024
 
 # source file of each kernel family (for the sha256 a traffic record carries)
 SOURCES = (("fwd_kernel<", "attn_fwd.hip"), ("fwd_merge_kernel<", "attn_fwd.hip"), ("fwd_paged_kernel<", "attn_fwd.hip"),
-           ("bwd_", "attn_bwd.hip"),
+           ("fwd_split_merge", "attn_fwd.hip"), ("paged_rank", "varlen_prep.hip"), ("bwd_", "attn_bwd.hip"),
            ("decode_", "attn_decode.hip"), ("varlen_", "varlen_prep.hip"), ("ds_seq_base", "varlen_prep.hip"),
            ("lse_merge", "attn_merge.hip"), ("paged_kv", "paged_kv.hip"))
 

@@ -329,6 +329,61 @@ def test_fwd_paged_split_matches_oracle(D, dtype, window, softcap, ctx, new):
     say(f"[fwd paged split] {n_split} of {w.B} sequences split")
 
 
+def test_fwd_paged_split_captured_in_a_graph():
+    """attn_fwd_paged_split (rank, forward, merge) captured once in a HIP graph over fixed buffers
+    and one workspace, then replayed with new query values and new context lengths of the decode
+    rows written into the captured buffers: the pieces a row is cut into are decided on the device
+    at each replay, and every replay equals an eager call on the same inputs bit for bit (and the
+    oracle within tolerance)."""
+    ctx, new = (600, 2000, 300, 1200), (100, 1, 1, 1)
+    w = MIXED.scaled(B=len(ctx), Hq=8, Hkv=2, D=512, dtype="bf16", window=0, ctx=ctx, new=new,
+                     name="paged fwd split graph")
+    inp = make_prefill_inputs(w, seed=34)
+    d = _prefill_dev(inp, "bf16")
+    maxq = inp["max_q"]
+    ws = torch.empty(sdpt.binding.attn_fwd_paged_workspace_bytes(d["q"], d["kc"], d["table"], d["cu"], maxq),
+                     device="cuda:0", dtype=torch.uint8)
+    o, lse = torch.empty_like(d["q"]), torch.empty((w.Hq, d["q"].shape[0]), device="cuda:0", dtype=torch.float32)
+
+    def call(out, l):
+        sdpt.attn_fwd_paged_split(d["q"], d["kc"], d["vc"], d["table"], d["cu"], d["ctx"], maxq, scale=w.scale,
+                                  out=out, lse=l, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up outside the graph
+        call(torch.empty_like(o), torch.empty_like(lse))
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(o, lse)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(35)
+    # decode rows' contexts per replay, never above the pages their table rows hold (the prompt's
+    # stays): 8..63 tiles, so 2..8 pieces, or one decode row not split
+    ctxs = [(600, 2000, 300, 1200), (600, 1500, 257, 256), (600, 290, 299, 1199)]
+    for i, c in enumerate(ctxs):
+        say(f"[paged split graph] replay {i} contexts {c}")
+        d["q"].copy_(torch.randn(d["q"].shape, generator=gen, device="cuda:0").to(torch.bfloat16))
+        d["ctx"].copy_(torch.tensor(c, dtype=torch.int32))
+        g.replay()
+        torch.cuda.synchronize()
+        eo, el = torch.empty_like(o), torch.empty_like(lse)
+        call(eo, el)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(o), host_bits(eo)), i
+        assert np.array_equal(lse.cpu().numpy(), el.cpu().numpy()), i
+        assert all_finite(o, lse)
+    inp2 = dict(inp, q=host_bits(d["q"]), ctx_lens=np.array(ctxs[-1], dtype=np.int32))
+    w2 = MIXED.scaled(B=len(ctx), Hq=8, Hkv=2, D=512, dtype="bf16", window=0, ctx=ctxs[-1], new=new,
+                      name="paged fwd split graph")
+    ro, rl = _prefill_oracle(inp2, w2)
+    assert max_abs(host(o), ro) <= O_MAX_ABS
+    assert max_abs(host(lse), rl) <= LSE_MAX_ABS
+
+
 @pytest.mark.parametrize("name,split", [("mixed_step_d512", False), ("mixed_step_d512", True),
                                         ("paged_prefill_d512", False)])
 def test_paged_forward_full_size_sampled_rows(name, split):

@@ -479,15 +479,16 @@ def test_decode_graphs_per_bucket_replay_like_eager_calls():
     g.close()
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (16, 1)])
-def test_fwd_paged_strided_views_and_group_sizes(Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv,split", [(4, 4, False), (16, 1, False), (4, 4, True), (16, 1, True)])
+def test_fwd_paged_strided_views_and_group_sizes(Hq, Hkv, split):
     """Queries and outputs as strided views (every other head of a wider tensor) and K/V caches as
-    the two halves of one combined (num_pages, 16, 2, Hkv, D) cache, at group sizes 1 and 16: the
-    kernel reads every tensor through its own strides; results as the oracle's."""
-    ctx, new = (200, 1, 77), (64, 1, 77)
+    the two halves of one combined (num_pages, 16, 2, Hkv, D) cache, at group sizes 1 and 16, through
+    attn_fwd_paged and attn_fwd_paged_split (whose decode row of 700 keys is cut into 3 pieces): the
+    kernels read every tensor through its own strides; results as the oracle's."""
+    ctx, new = (200, 700, 77), (64, 1, 77)
     w = MIXED.scaled(B=3, Hq=Hq, Hkv=Hkv, D=256, ctx=ctx, new=new)
     inp = make_prefill_inputs(w, seed=34)
-    say(f"[fwd paged strided] Hq={Hq} Hkv={Hkv}")
+    say(f"[fwd paged strided] Hq={Hq} Hkv={Hkv} split={split}")
     T = int(inp["cu_q"][-1])
     qw = torch.zeros((T, 2 * Hq, w.D), device="cuda:0", dtype=torch.bfloat16)
     qw[:, ::2] = dev(inp["q"])
@@ -498,8 +499,8 @@ def test_fwd_paged_strided_views_and_group_sizes(Hq, Hkv):
     ow = torch.full((T, 2 * Hq, w.D), 7.0, device="cuda:0", dtype=torch.bfloat16)
     o = ow[:, 1::2]
     d = _prefill_dev(inp, "bf16")
-    _, lse = sdpt.attn_fwd_paged(q, kv[:, :, 0], kv[:, :, 1], d["table"], d["cu"], d["ctx"], inp["max_q"],
-                                 scale=w.scale, out=o)
+    fwd = sdpt.attn_fwd_paged_split if split else sdpt.attn_fwd_paged
+    _, lse = fwd(q, kv[:, :, 0], kv[:, :, 1], d["table"], d["cu"], d["ctx"], inp["max_q"], scale=w.scale, out=o)
     torch.cuda.synchronize()
     ro, rl = _prefill_oracle(inp, w)
     assert max_abs(host(o), ro) <= O_MAX_ABS and max_abs(host(lse), rl) <= LSE_MAX_ABS
